@@ -1,0 +1,209 @@
+"""Pins for the oracle's dispatch (bf16 and fp8) and combine, CPU only.
+
+* dispatch bf16: numpy fancy-index scatter (library special case), the
+  adjoint identity <dispatch(x), y> = <x, sum_j y[slot[t,j]]> in fp64, and
+  untouched rows beyond N;
+* dispatch fp8: a hand-worked block (tests/golden/fp8_block_handworked.txt),
+  the pure-Python table-search quantiser, torch's float8_e4m3fn cast on
+  numpy float32 quotients (library special case) and the E4M3 error bound;
+* combine: a hand-worked case, exact rational brute force, the closed form
+  "identity experts + row-normalised weights return x", and the closed form
+  of the scaled-expert workload.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+from combine_ep_layout_04_amd.inputs import (
+    WORKLOADS, expert_outputs_scaled, float32_from_bf16_bits, make_inputs, make_random_case,
+    bf16_bits_from_float32,
+)
+
+from golden_io import read_cases
+
+
+# ---------------------------------------------------------------- dispatch --
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "skewed"])
+def test_dispatch_bf16_is_the_scatter(name):
+    w = WORKLOADS[name]
+    T = w.T if w.T * w.H <= 4096 * 2048 else 1024
+    inp = make_inputs(w, T=T)
+    L = oracle.layout(inp.topk_idx, w.E)
+    recv, rw = oracle.dispatch_bf16(inp.x_bits, L.slot, inp.topk_weights)
+    ref = np.zeros_like(recv)
+    refw = np.zeros(recv.shape[0], np.float32)
+    t, j = np.nonzero(L.slot >= 0)
+    ref[L.slot[t, j]] = inp.x_bits[t]
+    refw[L.slot[t, j]] = inp.topk_weights[t, j]
+    np.testing.assert_array_equal(recv, ref)
+    np.testing.assert_array_equal(rw, refw)
+    assert not recv[L.n:].any()
+
+
+def test_dispatch_bf16_adjoint_identity():
+    # the backward of dispatch is a combine: <D x, y> = <x, D^T y>
+    inp = make_random_case(3, 40, 24, 6, 3, mask_frac=0.2, dup_frac=1.0)
+    L = oracle.layout(inp.topk_idx, 6)
+    recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    rng = np.random.default_rng(9)
+    y = rng.standard_normal(recv.shape)
+    lhs = float((float32_from_bf16_bits(recv).astype(np.float64) * y).sum())
+    x = float32_from_bf16_bits(inp.x_bits).astype(np.float64)
+    back = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(L.slot.shape[1]):
+            r = L.slot[t, j]
+            if r >= 0:
+                back[t] += y[r]
+    rhs = float((x * back).sum())
+    assert math.isclose(lhs, rhs, rel_tol=1e-12, abs_tol=1e-9)
+
+
+def test_fp8_block_handworked():
+    (case,) = read_cases("fp8_block_handworked.txt")
+    H = case["H"][0]
+    xf = np.zeros(H, np.float32)
+    xf[:12] = case["x_block0_first12"]
+    xb = bf16_bits_from_float32(xf)
+    assert np.array_equal(float32_from_bf16_bits(xb), xf)  # every value is a bf16 value
+    slot = np.array([[0]], np.int32)
+    q, sc, _ = oracle.dispatch_fp8(xb[None, :], slot)
+    want = np.zeros(H, np.uint8)
+    want[:12] = case["codes_block0_first12"]
+    np.testing.assert_array_equal(q[0], want)
+    np.testing.assert_array_equal(sc[0], np.array(case["scales"], np.float32))
+
+
+def _fp8_torch_reference(x_bits: np.ndarray):
+    """Library special case: numpy float32 amax/448 and x/scale, torch cast."""
+    T, H = x_bits.shape
+    xf = float32_from_bf16_bits(x_bits).reshape(T, H // 128, 128)
+    amax = np.abs(xf).max(axis=2)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        qf = (xf / scale[:, :, None]).astype(np.float32)
+    q = torch.from_numpy(np.ascontiguousarray(qf)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q = q.reshape(T, H).copy()
+    q[np.repeat(amax == 0, 128, axis=1)] = 0
+    return q, scale
+
+
+@pytest.mark.parametrize("T", [64])
+def test_dispatch_fp8_vs_torch_cast_outlier_workload(T):
+    w = WORKLOADS["fp8"]
+    inp = make_inputs(w, T=T)
+    # include zero blocks and signed zeros to reach those branches
+    xb = inp.x_bits.copy()
+    xb[0, :128] = 0
+    xb[1, 128:256] = 0x8000
+    xb[2, 300] = 0x8000
+    L = oracle.layout(inp.topk_idx, w.E)
+    q, sc, _ = oracle.dispatch_fp8(xb, L.slot)
+    qr, sr = _fp8_torch_reference(xb)
+    t, j = np.nonzero(L.slot >= 0)
+    np.testing.assert_array_equal(q[L.slot[t, j]], qr[t])
+    np.testing.assert_array_equal(sc[L.slot[t, j]], sr[t])
+
+
+def test_dispatch_fp8_vs_bruteforce_rows():
+    inp = make_random_case(17, 6, 256, 4, 2, mask_frac=0.25)
+    xb = inp.x_bits.copy()
+    xb[3, :128] = bf16_bits_from_float32(np.full(128, 1e-30, np.float32))  # subnormal codes
+    L = oracle.layout(inp.topk_idx, 4)
+    q, sc, _ = oracle.dispatch_fp8(xb, L.slot)
+    for t in range(6):
+        bq, bs = brute.fp8_quantize_row(xb[t])
+        for j in range(2):
+            r = L.slot[t, j]
+            if r >= 0:
+                np.testing.assert_array_equal(q[r], bq)
+                np.testing.assert_array_equal(sc[r], bs)
+
+
+def test_dispatch_fp8_error_bound():
+    inp = make_inputs(WORKLOADS["fp8"], T=128)
+    slot = np.arange(128, dtype=np.int32)[:, None]
+    q, sc, _ = oracle.dispatch_fp8(inp.x_bits, slot)
+    x = float32_from_bf16_bits(inp.x_bits).astype(np.float64)
+    dec = np.array([oracle.e4m3_decode(c) for c in range(256)])[q]
+    s = np.repeat(sc.astype(np.float64), 128, axis=1)
+    err = np.abs(x - dec * s)
+    # relative half-step 2^-4 for normals, absolute 2^-10 for subnormals,
+    # plus slack for the fp32 rounding of the scale and the quotient
+    bound = np.maximum(2.0 ** -4 * np.abs(dec) * s, 2.0 ** -10 * s) * (1 + 1e-6) + 1e-30
+    assert np.all(err <= bound)
+    assert np.abs(dec).max() == 448.0
+
+
+# ----------------------------------------------------------------- combine --
+
+def test_combine_handworked():
+    (case,) = read_cases("combine_handworked.txt")
+    T, k, H = case["T"][0], case["k"][0], case["H"][0]
+    y = bf16_bits_from_float32(np.array(case["y"], np.float32).reshape(case["y_rows"][0], H))
+    slot = np.array(case["slot"], np.int32).reshape(T, k)
+    w = np.array(case["weights"], np.float32).reshape(T, k)
+    out = oracle.combine(y, slot, w)
+    np.testing.assert_array_equal(out.reshape(-1), np.array(case["out"], np.uint16))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_combine_vs_exact_rational_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    T, H, E, k = 5, 8, 5, 3
+    inp = make_random_case(seed, T, H, E, k, mask_frac=0.3, dup_frac=1.0)
+    L = oracle.layout(inp.topk_idx, E)
+    # expert outputs with mixed signs and magnitudes (cancellation, ties)
+    y = bf16_bits_from_float32((rng.standard_normal((T * k, H)) *
+                                np.exp2(rng.integers(-8, 8, (T * k, H)))).astype(np.float32))
+    w = inp.topk_weights if seed % 3 else None
+    out = oracle.combine(y, L.slot, w)
+    ref = brute.combine(y, L.slot, w)
+    np.testing.assert_array_equal(out, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "headline", "skewed"])
+def test_combine_identity_experts_return_x(name):
+    # sum_j w_j = 1 up to a few float32 ulps, far from any bf16 tie, so
+    # combine(dispatch(x)) == x for every token with an unmasked slot
+    w = WORKLOADS[name]
+    inp = make_inputs(w, T=min(w.T, 512))
+    L = oracle.layout(inp.topk_idx, w.E)
+    recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    out = oracle.combine(recv, L.slot, inp.topk_weights)
+    has = (L.slot >= 0).any(axis=1)
+    np.testing.assert_array_equal(out[has], inp.x_bits[has])
+    assert not out[~has].any()
+
+
+def test_combine_scaled_experts_closed_form():
+    # y[r] = bf16(x * (e+1)/64): out[t] = x[t] * sum_j w_j (e_j+1)/64 up to
+    # the bf16 rounding of y (at most 2^-8 relative, every term has the sign
+    # of x) and of the result (2^-8)
+    w = WORKLOADS["mid"]
+    inp = make_inputs(w, T=256)
+    L = oracle.layout(inp.topk_idx, w.E)
+    recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    y = expert_outputs_scaled(recv, L.offsets)
+    out = float32_from_bf16_bits(oracle.combine(y, L.slot, inp.topk_weights)).astype(np.float64)
+    x = float32_from_bf16_bits(inp.x_bits).astype(np.float64)
+    f = (inp.topk_weights.astype(np.float64) * (inp.topk_idx + 1) / 64.0).sum(axis=1)
+    ref = x * f[:, None]
+    assert np.all(np.abs(out - ref) <= (2.0 ** -7 + 2.0 ** -15) * np.abs(ref) + 1e-30)
+
+
+def test_combine_unit_weights_all_masked_and_zero_tokens():
+    inp = make_random_case(5, 4, 16, 3, 2, mask_frac=0.0)
+    idx = inp.topk_idx.copy()
+    idx[2, :] = -1
+    L = oracle.layout(idx, 3)
+    recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    out = oracle.combine(recv, L.slot, None)
+    np.testing.assert_array_equal(out, brute.combine(recv, L.slot, None))
+    assert not out[2].any()
