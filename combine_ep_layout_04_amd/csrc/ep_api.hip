@@ -1,0 +1,155 @@
+// ep_api.hip -- the C ABI declared in include/ep.h: argument checks on the
+// host, then stream-ordered launches.  Nothing here allocates, frees or
+// synchronises; every failure is a returned status code (the pages' host
+// library maps CUDA errors to an internal-error code and returns invalid-
+// argument / invalid-usage codes; it never has to exit for bad input here).
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "ep.h"
+#include "ep_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int from_hip(hipError_t err, const char* what)
+{
+    if (err == hipSuccess) return EP_SUCCESS;
+    return fail(EP_RUNTIME_ERROR, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_tokens(int64_t num_tokens, int num_topk)
+{
+    if (num_tokens < 0) return fail(EP_INVALID_ARGUMENT, "num_tokens < 0");
+    if (num_topk < 1 || num_topk > EP_MAX_TOPK)
+        return fail(EP_INVALID_ARGUMENT, "num_topk %d outside [1, %d]", num_topk, EP_MAX_TOPK);
+    if (num_tokens * (int64_t)num_topk >= ((int64_t)1 << 31))
+        return fail(EP_UNSUPPORTED, "num_tokens * num_topk must be < 2^31");
+    return EP_SUCCESS;
+}
+
+int check_hidden(int hidden, int multiple)
+{
+    if (hidden < 1 || hidden > EP_MAX_HIDDEN || hidden % multiple != 0)
+        return fail(EP_INVALID_ARGUMENT, "hidden %d must be a positive multiple of %d, at most %d",
+                    hidden, multiple, EP_MAX_HIDDEN);
+    return EP_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_version(void) { return (1 << 16) | 0; }
+
+const char* ep_status_string(int status)
+{
+    switch (status) {
+    case EP_SUCCESS: return "EP_SUCCESS";
+    case EP_INVALID_ARGUMENT: return "EP_INVALID_ARGUMENT";
+    case EP_UNSUPPORTED: return "EP_UNSUPPORTED";
+    case EP_RUNTIME_ERROR: return "EP_RUNTIME_ERROR";
+    default: return "EP_UNKNOWN_STATUS";
+    }
+}
+
+const char* ep_last_error(void) { return g_last_error; }
+
+size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_experts)
+{
+    if (num_tokens < 0 || num_topk < 1 || num_topk > EP_MAX_TOPK || num_experts < 1 ||
+        num_experts > EP_MAX_EXPERTS || num_tokens * (int64_t)num_topk >= ((int64_t)1 << 31))
+        return 0;
+    return ep::layout_workspace_bytes(num_tokens * (int64_t)num_topk, num_experts);
+}
+
+int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+              int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+              int32_t* num_invalid, void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+        return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
+                    EP_MAX_EXPERTS);
+    if (!counts || !offsets) return fail(EP_INVALID_ARGUMENT, "counts and offsets are required");
+    if (num_tokens > 0 && (!topk_idx || !slot))
+        return fail(EP_INVALID_ARGUMENT, "topk_idx and slot are required");
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(EP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    const size_t need = ep_layout_workspace_size(num_tokens, num_topk, num_experts);
+    if (workspace_bytes < need)
+        return fail(EP_INVALID_ARGUMENT, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(topk_idx) & 7u))
+        return fail(EP_INVALID_ARGUMENT, "topk_idx must be 8-byte aligned");
+    return from_hip(ep::launch_layout(topk_idx, num_tokens, num_topk, num_experts, counts, offsets,
+                                      slot, src, num_invalid, workspace,
+                                      static_cast<hipStream_t>(stream)),
+                    "ep_layout launch");
+}
+
+int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
+                float* recv_scales, float* recv_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    if (out_dtype != EP_OUT_BF16 && out_dtype != EP_OUT_FP8_E4M3)
+        return fail(EP_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
+    const bool fp8 = out_dtype == EP_OUT_FP8_E4M3;
+    st = check_hidden(hidden, fp8 ? 128 : 8);
+    if (st) return st;
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x || !slot || !recv_x) return fail(EP_INVALID_ARGUMENT, "x, slot and recv_x are required");
+    if (!aligned16(x) || !aligned16(recv_x))
+        return fail(EP_INVALID_ARGUMENT, "x and recv_x must be 16-byte aligned");
+    if (recv_weights && !topk_weights)
+        return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
+    if (fp8) {
+        if (!recv_scales) return fail(EP_INVALID_ARGUMENT, "fp8 dispatch needs recv_scales");
+        if (reinterpret_cast<uintptr_t>(recv_scales) & 3u)
+            return fail(EP_INVALID_ARGUMENT, "recv_scales must be 4-byte aligned");
+        return from_hip(ep::launch_dispatch_fp8(x, num_tokens, hidden, num_topk, slot, topk_weights,
+                                                recv_x, recv_scales, recv_weights,
+                                                static_cast<hipStream_t>(stream)),
+                        "ep_dispatch (fp8) launch");
+    }
+    if (recv_scales) return fail(EP_INVALID_ARGUMENT, "recv_scales must be NULL for bf16 output");
+    return from_hip(ep::launch_dispatch_bf16(x, num_tokens, hidden, num_topk, slot, topk_weights,
+                                             recv_x, recv_weights, static_cast<hipStream_t>(stream)),
+                    "ep_dispatch (bf16) launch");
+}
+
+int ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
+               int64_t num_tokens, int hidden, int num_topk, void* out, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 8);
+    if (st) return st;
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!y || !slot || !out) return fail(EP_INVALID_ARGUMENT, "y, slot and out are required");
+    if (!aligned16(y) || !aligned16(out))
+        return fail(EP_INVALID_ARGUMENT, "y and out must be 16-byte aligned");
+    return from_hip(ep::launch_combine(y, slot, topk_weights, num_tokens, hidden, num_topk, out,
+                                       static_cast<hipStream_t>(stream)),
+                    "ep_combine launch");
+}
+
+}  // extern "C"

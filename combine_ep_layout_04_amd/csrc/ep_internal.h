@@ -1,0 +1,37 @@
+// ep_internal.h -- launchers shared between the C ABI (ep_api.hip) and the
+// kernel files.  Host-side declarations only; every launcher assumes the
+// arguments were validated by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Layout: pairs are processed in chunks of kLayoutChunk flat indices; one
+// workgroup of kLayoutThreads owns a chunk in both passes.
+constexpr int kLayoutThreads = 256;
+constexpr int kLayoutChunk = 1024;
+
+int64_t layout_num_chunks(int64_t pairs);
+size_t layout_workspace_bytes(int64_t pairs, int num_experts);
+
+hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                         int num_experts, int32_t* counts, int32_t* offsets, int32_t* slot,
+                         int32_t* src, int32_t* num_invalid, void* workspace,
+                         hipStream_t stream);
+
+hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                                const int32_t* slot, const float* topk_weights, void* recv_x,
+                                float* recv_weights, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                               const int32_t* slot, const float* topk_weights, void* recv_q,
+                               float* recv_scales, float* recv_weights, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_weights,
+                          int64_t num_tokens, int hidden, int num_topk, void* out,
+                          hipStream_t stream);
+
+}  // namespace ep

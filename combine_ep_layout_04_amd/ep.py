@@ -1,0 +1,236 @@
+"""Python binding of libep.so (the C ABI in include/ep.h).
+
+Argument marshalling only: every step of layout, dispatch and combine runs
+in the HIP kernels behind the C ABI.  PyTorch provides device memory and
+the stream.  There is no fallback: if the library is missing or a call
+fails, an exception is raised.
+
+Two levels, with the C names:
+
+* ``lib()`` returns the raw ``ctypes`` handle whose functions take integer
+  device addresses (``tensor.data_ptr()``) and a stream handle;
+* ``ep_layout``, ``ep_dispatch``, ``ep_combine`` take torch tensors, check
+  dtype / shape / device, allocate outputs with torch when not given, and
+  launch on ``stream`` (default: torch's current stream).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep.so")
+
+EP_SUCCESS = 0
+EP_INVALID_ARGUMENT = 1
+EP_UNSUPPORTED = 2
+EP_RUNTIME_ERROR = 3
+EP_OUT_BF16 = 0
+EP_OUT_FP8_E4M3 = 1
+EP_MAX_EXPERTS = 1024
+EP_MAX_TOPK = 64
+EP_MAX_HIDDEN = 65536
+
+# every symbol include/ep.h declares
+SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspace_size",
+           "ep_layout", "ep_dispatch", "ep_combine")
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {message}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libep.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m combine_ep_layout_04_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.ep_version.argtypes = []
+        L.ep_version.restype = i32
+        L.ep_status_string.argtypes = [i32]
+        L.ep_status_string.restype = ctypes.c_char_p
+        L.ep_last_error.argtypes = []
+        L.ep_last_error.restype = ctypes.c_char_p
+        L.ep_layout_workspace_size.argtypes = [i64, i32, i32]
+        L.ep_layout_workspace_size.restype = sz
+        L.ep_layout.argtypes = [P, i64, i32, i32, P, P, P, P, P, P, sz, P]
+        L.ep_layout.restype = i32
+        L.ep_dispatch.argtypes = [P, i64, i32, i32, P, P, i32, P, P, P, P]
+        L.ep_dispatch.restype = i32
+        L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
+        L.ep_combine.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ep_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().ep_last_error().decode()
+
+
+def version() -> int:
+    return int(lib().ep_version())
+
+
+def layout_workspace_size(num_tokens: int, num_topk: int, num_experts: int) -> int:
+    return int(lib().ep_layout_workspace_size(int(num_tokens), int(num_topk), int(num_experts)))
+
+
+def _check(status: int, where: str) -> None:
+    if status != EP_SUCCESS:
+        raise EpError(status, where, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+
+
+# ------------------------------------------------------------------ layout --
+
+def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, counts=None, offsets=None, slot=None,
+              src=None, num_invalid=None, workspace=None, want_src: bool = True,
+              want_invalid: bool = True, stream=None):
+    """Routing layout of ``topk_idx`` (int64 [T, k], -1 = masked).
+
+    Returns (counts int32 [E], offsets int32 [E+1], slot int32 [T, k],
+    src int32 [T*k] or None, num_invalid int32 [1] or None).
+    """
+    _need(topk_idx, "topk_idx", torch.int64)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be 2-D [num_tokens, num_topk]")
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    dev = topk_idx.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = torch.empty(E, **i32) if counts is None else counts
+    offsets = torch.empty(E + 1, **i32) if offsets is None else offsets
+    slot = torch.empty((T, k), **i32) if slot is None else slot
+    if want_src and src is None:
+        src = torch.empty(T * k, **i32)
+    if want_invalid and num_invalid is None:
+        num_invalid = torch.empty(1, **i32)
+    need = layout_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(counts, "counts", torch.int32, E)
+    _need(offsets, "offsets", torch.int32, E + 1)
+    _need(slot, "slot", torch.int32, T * k)
+    if src is not None:
+        _need(src, "src", torch.int32, T * k)
+    if num_invalid is not None:
+        _need(num_invalid, "num_invalid", torch.int32, 1)
+    _need(workspace, "workspace", torch.uint8)
+    st = lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot),
+                         _ptr(src), _ptr(num_invalid), _ptr(workspace), workspace.numel(),
+                         _stream(stream))
+    _check(st, "ep_layout")
+    return counts, offsets, slot, src, num_invalid
+
+
+# ---------------------------------------------------------------- dispatch --
+
+def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                *, fp8: bool = False, recv_x=None, recv_scales=None, recv_weights=None,
+                want_weights: bool = False, trust_slots: bool = False, stream=None):
+    """Permute (bf16) or cast (fp8 e4m3 + per-128 fp32 scales) the rows of
+    ``x`` (bf16 [T, H]) into the expert-grouped buffer named by ``slot``.
+
+    Returns (recv_x, recv_scales or None, recv_weights or None); recv_x is
+    bf16 [T*k, H] or uint8 [T*k, H].  Output buffers given by the caller
+    must hold T*k rows (the worst case), unless ``trust_slots`` says the
+    caller knows every slot is below the rows it passed.
+    """
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [num_tokens, hidden]")
+    T, H = x.shape
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or slot.shape[0] != T:
+        raise ValueError("slot must be 2-D [num_tokens, num_topk]")
+    k = slot.shape[1]
+    R = T * k
+    dev = x.device
+    if recv_x is None:
+        recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    if fp8 and recv_scales is None:
+        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    cap = 0 if trust_slots else R
+    _need(recv_x, "recv_x", torch.uint8 if fp8 else torch.bfloat16, cap * H)
+    if recv_x.shape[-1] != H:
+        raise ValueError("recv_x rows must have hidden elements")
+    if recv_scales is not None:
+        _need(recv_scales, "recv_scales", torch.float32, cap * (H // 128))
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, cap)
+    st = lib().ep_dispatch(_ptr(x), T, H, k, _ptr(slot), _ptr(topk_weights),
+                           EP_OUT_FP8_E4M3 if fp8 else EP_OUT_BF16, _ptr(recv_x),
+                           _ptr(recv_scales), _ptr(recv_weights), _stream(stream))
+    _check(st, "ep_dispatch")
+    return recv_x, recv_scales, recv_weights
+
+
+# ----------------------------------------------------------------- combine --
+
+def ep_combine(y: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor],
+               *, out=None, trust_slots: bool = False, stream=None) -> torch.Tensor:
+    """out[t] = bf16(sum_j w[t,j] * y[slot[t,j]]) for y bf16 [rows, H] and
+    slot int32 [T, k]; ``topk_weights`` None means unit weights.  y must
+    hold T*k rows unless ``trust_slots`` says every slot is below its rows."""
+    _need(y, "y", torch.bfloat16)
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or y.dim() != 2:
+        raise ValueError("slot must be [num_tokens, num_topk] and y [rows, hidden]")
+    T, k = slot.shape
+    H = y.shape[-1]
+    if not trust_slots and y.shape[0] < T * k:
+        raise ValueError(f"y has {y.shape[0]} rows, needs num_tokens * num_topk = {T * k}")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, T * H)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    st = lib().ep_combine(_ptr(y), _ptr(slot), _ptr(topk_weights), T, H, k, _ptr(out),
+                          _stream(stream))
+    _check(st, "ep_combine")
+    return out

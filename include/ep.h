@@ -1,0 +1,183 @@
+/*
+ * ep.h -- C ABI of the MoE token layout / dispatch / combine library
+ * (libep.so, HIP kernels for AMD Instinct MI355X, gfx950).
+ *
+ * One device's share of expert-parallel token routing, with every buffer in
+ * that device's memory:
+ *
+ *   ep_layout    topk_idx [T,k]  ->  per-expert counts, exclusive offsets,
+ *                stable destination row ("slot") of every (token, k) pair,
+ *                and the source token of every destination row;
+ *   ep_dispatch  copy (bf16) or cast (OCP E4M3 with one fp32 scale per 128
+ *                channels) every token row into the expert-grouped buffer;
+ *   ep_combine   gather the expert-output rows back and reduce them per
+ *                token, weighted by topk_weights, in fp32, in top-k order.
+ *
+ * The operations follow the pages' problem statement:
+ *   - NCCL EP (nccl_ep.cc): ncclEpCreateHandle (topk_idx is a 2-D int64
+ *     tensor; "Step 3" metadata preprocessing gives per-expert counts),
+ *     ncclEpDispatch (bf16 tokens with hidden a multiple of 8 elements; fp8
+ *     scales of hidden/128 fp32 per token), ncclEpCombine (low-latency
+ *     branch: reduction weighted by topk_weights [T,k] fp32; high-throughput
+ *     forward: unweighted);
+ *   - DeepEP ElasticBuffer dispatch() / combine() and EPHandle's prefix sums
+ *     ("Prefix Sum Interpretation for Expert Token Counts": expert i owns
+ *     rows [psum[i-1], psum[i]) of the expanded, one-slot-per-token-per-
+ *     expert receive buffer);
+ *   - NeMo fused_a2a HybridEPDispatch: topk_idx uses -1 for an unused slot;
+ *     the dispatched rows are grouped by expert.
+ *
+ * Conventions shared by every call
+ *   - All array arguments are device pointers (memory the GPU can read and
+ *     write: hipMalloc'd, or torch CUDA tensors).  The caller owns them; the
+ *     library never frees, keeps or allocates memory and holds no state
+ *     between calls, so the layout outputs themselves are the "handle" that
+ *     dispatch and combine take.
+ *   - bf16 / fp8 / fp32 row buffers must be 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Arguments are checked on the host before anything is
+ *     launched; a failed check returns EP_INVALID_ARGUMENT (or
+ *     EP_UNSUPPORTED) and launches nothing.  A HIP launch error returns
+ *     EP_RUNTIME_ERROR.  The library never aborts or exits.
+ *   - Data-dependent problems cannot be reported synchronously: a topk_idx
+ *     entry outside [-1, E) is treated as masked and counted in
+ *     *num_invalid.
+ *   - ep_last_error() returns a message for the last failed call on the
+ *     calling thread.
+ */
+#ifndef EP_H_
+#define EP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_SUCCESS = 0,
+    EP_INVALID_ARGUMENT = 1,
+    EP_UNSUPPORTED = 2,
+    EP_RUNTIME_ERROR = 3
+} ep_status_t;
+
+typedef enum {
+    EP_OUT_BF16 = 0,      /* recv_x is bf16 [rows, hidden]                  */
+    EP_OUT_FP8_E4M3 = 1   /* recv_x is OCP E4M3 bytes [rows, hidden] plus
+                             recv_scales fp32 [rows, hidden/128]            */
+} ep_out_dtype_t;
+
+/* Limits checked by every call. */
+#define EP_MAX_EXPERTS 1024
+#define EP_MAX_TOPK 64
+#define EP_MAX_HIDDEN 65536
+
+/* Library version, (major << 16) | minor. */
+int ep_version(void);
+
+/* Static text for a status code. */
+const char *ep_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *ep_last_error(void);
+
+/*
+ * Bytes of device scratch ep_layout needs for this shape (a multiple of
+ * 256).  Pure host arithmetic; returns 0 for an invalid shape.
+ */
+size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_experts);
+
+/*
+ * ep_layout -- routing layout of one device's tokens.
+ *
+ * Passages: NCCL EP page, nccl_ep.cc, ncclEpCreateHandle (int64 topk_idx
+ * [T,k]; "Step 3" preprocessing yields per-expert token counts and the
+ * received-token total); DeepEP page, dispatch() do_expand and "Prefix Sum
+ * Interpretation for Expert Token Counts"; NeMo fused_a2a page,
+ * HybridEPDispatch topk_idx with -1 for unused slots.
+ *
+ * In:  topk_idx     int64 [num_tokens, num_topk] row-major; -1 = masked,
+ *                   anything else outside [0, num_experts) is invalid and
+ *                   treated as masked.
+ * Out: counts       int32 [num_experts]: unmasked pairs per expert.
+ *      offsets      int32 [num_experts + 1]: exclusive prefix sum of counts;
+ *                   offsets[E] = N, the number of dispatched rows.
+ *      slot         int32 [num_tokens * num_topk]: destination row of pair
+ *                   (t, j) at index t*k + j, or -1 if masked.  Rows of one
+ *                   expert are handed out in increasing t*k + j order
+ *                   (a stable counting sort), so the result is
+ *                   deterministic.
+ *      src          int32 [num_tokens * num_topk] or NULL: src[r] = source
+ *                   token of row r for r < N; entries >= N are not written.
+ *      num_invalid  int32 [1] or NULL: number of invalid entries.
+ * Scratch: workspace of at least ep_layout_workspace_size(...) bytes,
+ *      256-byte aligned; contents need not be initialised and are
+ *      clobbered.
+ * num_tokens may be 0 (then counts and offsets are zero-filled).
+ * Requires num_tokens * num_topk < 2^31, 1 <= num_topk <= EP_MAX_TOPK,
+ * 1 <= num_experts <= EP_MAX_EXPERTS.
+ */
+int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+              int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
+              int32_t *num_invalid, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ep_dispatch -- permute (and optionally cast) token rows into the
+ * expert-grouped receive buffer.
+ *
+ * Passages: NCCL EP page, nccl_ep.cc, ncclEpDispatch (x bf16 [T, hidden]
+ * with 16-byte rows; fp8 output with hidden/128 fp32 scales per row) and
+ * the dense-to-sparse weight step that returns recv_topk_weights; DeepEP
+ * page, dispatch() (returns recv_x and recv_topk_weights; FP8 data comes
+ * with its scale factors).
+ *
+ * In:  x             bf16 [num_tokens, hidden] row-major.
+ *      slot          int32 [num_tokens * num_topk] from ep_layout.
+ *      topk_weights  fp32 [num_tokens * num_topk] or NULL.
+ * Out: recv_x        EP_OUT_BF16: bf16 [rows, hidden], row slot[t,j] =
+ *                    x[t] bit for bit.
+ *                    EP_OUT_FP8_E4M3: bytes [rows, hidden]; per token and
+ *                    128-channel block b, amax = max |x|, scale =
+ *                    amax / 448 (fp32, correctly rounded), code = OCP E4M3
+ *                    of x / scale (fp32 quotient, correctly rounded) with
+ *                    round-to-nearest-even and saturation to +-448; a block
+ *                    with amax == 0 gets scale 0 and zero codes.
+ *      recv_scales   fp32 [rows, hidden/128]; required for FP8, else NULL.
+ *      recv_weights  fp32 [rows] or NULL: recv_weights[slot[t,j]] =
+ *                    topk_weights[t,j] (needs topk_weights).
+ * Only rows named by slot are written; rows = num_tokens * num_topk is
+ * always enough.  hidden must be a positive multiple of 8 (of 128 for FP8),
+ * at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                const int32_t *slot, const float *topk_weights, int out_dtype,
+                void *recv_x, float *recv_scales, float *recv_weights, void *stream);
+
+/*
+ * ep_combine -- weighted reduction of expert outputs back to token order.
+ *
+ * Passages: NCCL EP page, nccl_ep.cc, ncclEpCombine (low-latency branch:
+ * bf16 expert outputs reduced into [T, hidden] bf16 with topk_weights
+ * [T, k] fp32; high-throughput forward combine: tokens only, no weights);
+ * DeepEP page, combine().
+ *
+ * In:  y             bf16 [rows, hidden]: expert outputs, row r belongs to
+ *                    the pair whose slot is r.
+ *      slot          int32 [num_tokens * num_topk] from ep_layout.
+ *      topk_weights  fp32 [num_tokens * num_topk] or NULL (all ones).
+ * Out: out           bf16 [num_tokens, hidden]:
+ *                    out[t] = bf16_rne( sum over j = 0..k-1 with slot >= 0
+ *                    of w[t,j] * y[slot[t,j]] ), accumulated in fp32 with
+ *                    one fused multiply-add per term in increasing j;
+ *                    a token whose slots are all masked gets +0.
+ * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
+ */
+int ep_combine(const void *y, const int32_t *slot, const float *topk_weights,
+               int64_t num_tokens, int hidden, int num_topk, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H_ */

@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+include/ep.h declares, and rejects bad arguments on the host before
+launching anything (these calls fail validation, so no HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_ep_layout_04_amd import ep
+from combine_ep_layout_04_amd.build import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ep.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(ep.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(ep.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings():
+    assert ep.version() >> 16 == 1
+    assert ep.status_string(0) == "EP_SUCCESS"
+    assert ep.status_string(1) == "EP_INVALID_ARGUMENT"
+    assert ep.status_string(2) == "EP_UNSUPPORTED"
+    assert ep.status_string(3) == "EP_RUNTIME_ERROR"
+    assert ep.status_string(99) == "EP_UNKNOWN_STATUS"
+
+
+def test_workspace_size():
+    # one int32 per (chunk of 1024 pairs, expert) plus one per chunk, 256-aligned
+    assert ep.layout_workspace_size(8192, 8, 256) == 64 * 257 * 4
+    assert ep.layout_workspace_size(0, 8, 256) == ((257 * 4 + 255) // 256) * 256
+    assert ep.layout_workspace_size(1000, 3, 7) == ((3 * 8 * 4 + 255) // 256) * 256
+    assert ep.layout_workspace_size(10, 0, 8) == 0
+    assert ep.layout_workspace_size(10, 2, 0) == 0
+    assert ep.layout_workspace_size(10, 2, 1025) == 0
+    assert ep.layout_workspace_size(1 << 28, 8, 8) == 0  # pairs >= 2^31
+
+
+FAKE = 0x100000  # 16- and 256-byte aligned, never dereferenced by these calls
+
+
+@pytest.mark.parametrize("args,code", [
+    # (topk_idx, T, k, E, counts, offsets, slot, src, invalid, ws, ws_bytes)
+    ((FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),       # E < 1
+    ((FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),    # E too large
+    ((FAKE, 4, 0, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),       # k < 1
+    ((FAKE, 4, 65, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),      # k too large
+    ((FAKE, -1, 2, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),      # T < 0
+    ((FAKE, 1 << 28, 8, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40), 2),  # pairs >= 2^31
+    ((None, 4, 2, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),       # no topk_idx
+    ((FAKE, 4, 2, 8, None, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),       # no counts
+    ((FAKE, 4, 2, 8, FAKE, FAKE, None, None, None, FAKE, 1 << 20), 1),       # no slot
+    ((FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, None, None, 1 << 20), 1),       # no workspace
+    ((FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, None, FAKE + 16, 1 << 20), 1),  # ws misaligned
+    ((FAKE, 4, 2, 8, FAKE, FAKE, FAKE, None, None, FAKE, 16), 1),            # ws too small
+    ((FAKE + 4, 4, 2, 8, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),   # idx misaligned
+])
+def test_layout_rejects(args, code):
+    st = ep.lib().ep_layout(*args, None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    # (x, T, H, k, slot, w, out_dtype, recv_x, recv_scales, recv_w)
+    ((FAKE, 4, 7, 2, FAKE, None, 0, FAKE, None, None), 1),          # H % 8
+    ((FAKE, 4, 0, 2, FAKE, None, 0, FAKE, None, None), 1),          # H < 1
+    ((FAKE, 4, 65544, 2, FAKE, None, 0, FAKE, None, None), 1),      # H too large
+    ((FAKE, 4, 136, 2, FAKE, None, 1, FAKE, FAKE, None), 1),        # fp8 needs H % 128
+    ((FAKE, 4, 256, 2, FAKE, None, 1, FAKE, None, None), 1),        # fp8 needs scales
+    ((FAKE, 4, 256, 2, FAKE, None, 0, FAKE, FAKE, None), 1),        # bf16 with scales
+    ((FAKE, 4, 256, 2, FAKE, None, 2, FAKE, None, None), 1),        # unknown dtype
+    ((FAKE, 4, 256, 0, FAKE, None, 0, FAKE, None, None), 1),        # k < 1
+    ((None, 4, 256, 2, FAKE, None, 0, FAKE, None, None), 1),        # no x
+    ((FAKE, 4, 256, 2, None, None, 0, FAKE, None, None), 1),        # no slot
+    ((FAKE, 4, 256, 2, FAKE, None, 0, None, None, None), 1),        # no recv_x
+    ((FAKE + 8, 4, 256, 2, FAKE, None, 0, FAKE, None, None), 1),    # x misaligned
+    ((FAKE, 4, 256, 2, FAKE, None, 0, FAKE + 2, None, None), 1),    # recv misaligned
+    ((FAKE, 4, 256, 2, FAKE, None, 0, FAKE, None, FAKE), 1),        # recv_w without w
+    ((FAKE, 1 << 28, 256, 8, FAKE, None, 0, FAKE, None, None), 2),  # pairs >= 2^31
+])
+def test_dispatch_rejects(args, code):
+    st = ep.lib().ep_dispatch(*args, None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_dispatch_and_combine_zero_tokens_are_noops():
+    assert ep.lib().ep_dispatch(None, 0, 256, 2, None, None, 0, None, None, None, None) == 0
+    assert ep.lib().ep_combine(None, None, None, 0, 256, 2, None, None) == 0
+    assert ep.last_error() == ""
+
+
+@pytest.mark.parametrize("args,code", [
+    # (y, slot, w, T, H, k, out)
+    ((FAKE, FAKE, None, 4, 12, 2, FAKE), 1),        # H % 8
+    ((FAKE, FAKE, None, 4, 256, 65, FAKE), 1),      # k too large
+    ((FAKE, FAKE, None, -3, 256, 2, FAKE), 1),      # T < 0
+    ((None, FAKE, None, 4, 256, 2, FAKE), 1),       # no y
+    ((FAKE, None, None, 4, 256, 2, FAKE), 1),       # no slot
+    ((FAKE, FAKE, None, 4, 256, 2, None), 1),       # no out
+    ((FAKE + 4, FAKE, None, 4, 256, 2, FAKE), 1),   # y misaligned
+    ((FAKE, FAKE, None, 4, 256, 2, FAKE + 8), 1),   # out misaligned
+])
+def test_combine_rejects(args, code):
+    st = ep.lib().ep_combine(*args, None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ep, "_lib", None)
+    monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ep.lib()

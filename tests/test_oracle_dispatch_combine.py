@@ -171,14 +171,16 @@ def test_combine_vs_exact_rational_bruteforce(seed):
 @pytest.mark.parametrize("name", ["tiny", "headline", "skewed"])
 def test_combine_identity_experts_return_x(name):
     # sum_j w_j = 1 up to a few float32 ulps, far from any bf16 tie, so
-    # combine(dispatch(x)) == x for every token with an unmasked slot
+    # combine(dispatch(x)) == x (as values; -0 comes back as +0) for every
+    # token with an unmasked slot
     w = WORKLOADS[name]
     inp = make_inputs(w, T=min(w.T, 512))
     L = oracle.layout(inp.topk_idx, w.E)
     recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
     out = oracle.combine(recv, L.slot, inp.topk_weights)
     has = (L.slot >= 0).any(axis=1)
-    np.testing.assert_array_equal(out[has], inp.x_bits[has])
+    np.testing.assert_array_equal(float32_from_bf16_bits(out[has]),
+                                  float32_from_bf16_bits(inp.x_bits[has]))
     assert not out[~has].any()
 
 
