@@ -12,12 +12,15 @@
 // starting from +0; the bf16 rounding is done once at the end.
 //
 // Design (HBM-bound): one workgroup per token; each lane owns 16-byte
-// column vectors of the row.  For a vector the k source rows are loaded
-// back to back (k independent 16-byte loads in flight per lane before the
-// first is consumed), then reduced in j order.  Each loaded byte is used
-// once by the lane that loaded it, so the gather goes straight to
-// registers; an LDS round trip would add traffic without reuse.  k is a
-// template parameter for k <= 8 so the loads are fully unrolled.
+// column vectors of the row.  For U column vectors at a time the k source
+// rows are loaded back to back (U*k independent 16-byte loads in flight per
+// lane before the first is consumed), then reduced in j order.  Each loaded
+// byte is used once by the lane that loaded it, so the gather goes straight
+// to registers; an LDS round trip would add traffic without reuse.  The
+// loads carry the non-temporal hint: the expert outputs are read exactly
+// once, and streaming them past the caches measured ~12% faster than
+// cached loads on MI355X.  k is a template parameter for k <= 8 so the
+// loads are fully unrolled.
 
 #include "ep_internal.h"
 
@@ -68,15 +71,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint4* y, int32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(base), (short)0, bytes, 0x00020000);
 }
 
+// Cache-policy bits of a gfx950 buffer instruction: bit 1 is "nt"
+// (non-temporal, streaming).
+constexpr int kLoadNT = 2;
+
+// 16 bytes at vector v of the resource; past the resource's end it reads 0.
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int v)
 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, kLoadNT));
 }
 
-// K > 0: exactly K = k slots, unrolled.  K == 0: any k (runtime loop).
+// K > 0: exactly K = k slots, unrolled, U column vectors per lane per
+// iteration.  K == 0: any k (runtime loop, one vector per iteration).
 // Lane j of every wavefront holds slot[t, j] and w[t, j] (k <= 64); they are
 // read back as wavefront-uniform values with readlane.
-template <int NT, int K>
+template <int NT, int U, int K>
 __global__ __launch_bounds__(NT)
 void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slot,
                     const float* __restrict__ w, int nvec, int k, uint4* __restrict__ out)
@@ -93,6 +102,7 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
         // A masked slot reads zeros through an empty resource and gets
         // weight 0, so its term fma(0, 0, acc) leaves acc's value unchanged
         // (at most an accumulated -0 turns into +0) and no branch is needed.
+        // Vectors past the row end also read zeros and are not stored.
         __amdgpu_buffer_rsrc_t rs[K];
         float g[K];
 #pragma unroll
@@ -102,14 +112,19 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
             g[j] = r >= 0 ? wj : 0.0f;
         }
-        for (int v = tid; v < nvec; v += NT) {
-            uint4 d[K];
+        for (int v0 = tid; v0 < nvec; v0 += NT * U) {
+            uint4 d[U][K];
 #pragma unroll
-            for (int j = 0; j < K; ++j) d[j] = load16(rs[j], v);
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int j = 0; j < K; ++j) fma8(acc, g[j], d[j]);
-            o[v] = pack8(acc);
+                for (int j = 0; j < K; ++j) d[u][j] = load16(rs[j], v0 + u * NT);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < K; ++j) fma8(acc, g[j], d[u][j]);
+                if (v0 + u * NT < nvec) o[v0 + u * NT] = pack8(acc);
+            }
         }
     } else {
         for (int v = tid; v < nvec; v += NT) {
@@ -125,21 +140,25 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
     }
 }
 
-template <int NT>
-void launch_nt(dim3 grid, hipStream_t stream, const uint4* y, const int32_t* slot,
-               const float* w, int nvec, int k, uint4* out)
+template <int NT, int U>
+void launch_shape(dim3 grid, hipStream_t stream, const uint4* y, const int32_t* slot,
+                  const float* w, int nvec, int k, uint4* out)
 {
+#define EP_COMBINE_K(KV)                                                                       \
+    hipLaunchKernelGGL((combine_kernel<NT, U, KV>), grid, dim3(NT), 0, stream, y, slot, w, nvec, \
+                       k, out)
     switch (k) {
-    case 1: hipLaunchKernelGGL((combine_kernel<NT, 1>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 2: hipLaunchKernelGGL((combine_kernel<NT, 2>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 3: hipLaunchKernelGGL((combine_kernel<NT, 3>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 4: hipLaunchKernelGGL((combine_kernel<NT, 4>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 5: hipLaunchKernelGGL((combine_kernel<NT, 5>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 6: hipLaunchKernelGGL((combine_kernel<NT, 6>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 7: hipLaunchKernelGGL((combine_kernel<NT, 7>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    case 8: hipLaunchKernelGGL((combine_kernel<NT, 8>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
-    default: hipLaunchKernelGGL((combine_kernel<NT, 0>), grid, dim3(NT), 0, stream, y, slot, w, nvec, k, out); break;
+    case 1: EP_COMBINE_K(1); break;
+    case 2: EP_COMBINE_K(2); break;
+    case 3: EP_COMBINE_K(3); break;
+    case 4: EP_COMBINE_K(4); break;
+    case 5: EP_COMBINE_K(5); break;
+    case 6: EP_COMBINE_K(6); break;
+    case 7: EP_COMBINE_K(7); break;
+    case 8: EP_COMBINE_K(8); break;
+    default: EP_COMBINE_K(0); break;
     }
+#undef EP_COMBINE_K
 }
 
 }  // namespace
@@ -153,10 +172,14 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
     const dim3 grid((unsigned)num_tokens);
     const uint4* yy = static_cast<const uint4*>(y);
     uint4* oo = static_cast<uint4*>(out);
+    // 256 lanes x 2 vectors for long rows (hidden >= 4096: 896 vectors at
+    // 7168 take two iterations); smaller workgroups for short rows
     if (nvec <= 64)
-        launch_nt<64>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+        launch_shape<64, 1>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+    else if (nvec < 512)
+        launch_shape<128, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
     else
-        launch_nt<128>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+        launch_shape<256, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
     return hipGetLastError();
 }
 

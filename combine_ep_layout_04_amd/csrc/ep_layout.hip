@@ -17,9 +17,10 @@
 //
 //   1. count:   one workgroup per chunk of kLayoutChunk pairs builds the
 //               chunk's expert histogram in LDS -> hist[c][e].
-//   2. scan:    one workgroup turns hist into per-(chunk, expert) starting
-//               rows in place (column running sums over chunks plus the
-//               exclusive scan over experts) and writes counts / offsets.
+//   2. scan:    one workgroup of 1024 threads turns hist into per-(chunk,
+//               expert) starting rows in place (column running sums over
+//               chunks plus the exclusive scan over experts) and writes
+//               counts / offsets.
 //   3. scatter: each chunk again, in batches of 256 pairs.  Inside a batch
 //               every pair sets its bit in an LDS bit-matrix row of its
 //               expert (256 bits = 8 words per expert); its rank among
@@ -94,41 +95,88 @@ void layout_count_kernel(const int64_t* __restrict__ idx, int64_t pairs, int E,
     if (tid == 0) bad[blockIdx.x] = nbad;
 }
 
+// hist is C rows (chunks) x E columns (experts).  The 1024 threads tile it:
+// epad = E rounded up to a power of two columns, tpc = 1024 / epad threads
+// per column, each owning a contiguous slab of rows.  Loads are batched
+// kBatch at a time so a thread has one memory round trip per batch, not one
+// per row.
+constexpr int kBatch = 16;
+
 __global__ __launch_bounds__(kScanThreads)
 void layout_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
-                        int num_chunks, int E, int32_t* __restrict__ counts,
+                        int num_chunks, int E, int epad, int32_t* __restrict__ counts,
                         int32_t* __restrict__ offsets, int32_t* __restrict__ num_invalid)
 {
+    __shared__ int32_t part_sum[kScanThreads];
+    __shared__ int32_t col_start[kMaxExperts];
     __shared__ int32_t waves[kScanThreads / 64];
     __shared__ int32_t nbad;
-    const int e = threadIdx.x;
-    if (e == 0) nbad = 0;
+    const int tid = threadIdx.x;
+    const int tpc = kScanThreads / epad;
+    const int col = tid & (epad - 1);
+    const int part = tid / epad;
+    const int rows = (num_chunks + tpc - 1) / tpc;
+    const int r0 = min(part * rows, num_chunks);
+    const int r1 = min(r0 + rows, num_chunks);
+    const bool live = col < E;
+    if (tid == 0) nbad = 0;
 
-    // column running sum over chunks: hist[c][e] <- rows of e in chunks < c
-    int32_t tot = 0;
-    if (e < E) {
-        for (int c = 0; c < num_chunks; ++c) {
-            int32_t* p = hist + (int64_t)c * E + e;
-            const int32_t h = *p;
-            *p = tot;
-            tot += h;
+    // 1. sum of this thread's slab of its column
+    int32_t mine = 0;
+    if (live) {
+        for (int r = r0; r < r1; r += kBatch) {
+            int32_t h[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                h[b] = (r + b < r1) ? hist[(int64_t)(r + b) * E + col] : 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) mine += h[b];
         }
     }
-    int32_t n = 0;
-    const int32_t start = block_exclusive_scan(tot, waves, &n);
-    if (e < E) {
-        counts[e] = tot;
-        offsets[e] = start;
-        for (int c = 0; c < num_chunks; ++c) hist[(int64_t)c * E + e] += start;
+    part_sum[tid] = mine;
+    __syncthreads();
+
+    // 2. column total, and the rows of this column in earlier slabs
+    int32_t before = 0, tot = 0;
+    for (int q = 0; q < tpc; ++q) {
+        const int32_t v = part_sum[col + q * epad];
+        before += (q < part) ? v : 0;
+        tot += v;
     }
-    if (e == 0) offsets[E] = n;
+    // 3. exclusive scan of column totals over experts: the part-0 threads
+    // are tids 0..epad-1, in column order, and everyone else adds 0
+    int32_t n = 0;
+    const int32_t start = block_exclusive_scan((part == 0 && live) ? tot : 0, waves, &n);
+    if (part == 0) col_start[col] = start;
+    __syncthreads();
+
+    // 4. rewrite the slab in place with each (chunk, expert)'s first row
+    if (live) {
+        int32_t run = col_start[col] + before;
+        for (int r = r0; r < r1; r += kBatch) {
+            int32_t h[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b)
+                h[b] = (r + b < r1) ? hist[(int64_t)(r + b) * E + col] : 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (r + b < r1) hist[(int64_t)(r + b) * E + col] = run;
+                run += h[b];
+            }
+        }
+        if (part == 0) {
+            counts[col] = tot;
+            offsets[col] = start;
+        }
+    }
+    if (tid == 0) offsets[E] = n;
 
     if (num_invalid) {
         int32_t b = 0;
-        for (int c = threadIdx.x; c < num_chunks; c += kScanThreads) b += bad[c];
+        for (int c = tid; c < num_chunks; c += kScanThreads) b += bad[c];
         if (b) atomicAdd(&nbad, b);
         __syncthreads();
-        if (threadIdx.x == 0) *num_invalid = nbad;
+        if (tid == 0) *num_invalid = nbad;
     }
 }
 
@@ -216,8 +264,10 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_to
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
+    int epad = 1;
+    while (epad < num_experts) epad <<= 1;
     hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                       hist, bad, (int)C, num_experts, counts, offsets, num_invalid);
+                       hist, bad, (int)C, num_experts, epad, counts, offsets, num_invalid);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
