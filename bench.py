@@ -40,14 +40,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+# the source file of each kernel bench.py reports (plus the shared internal
+# header and the build flags)
+KERNEL_SOURCES = {
+    "dispatch_bf16": "ep_dispatch.hip", "dispatch_fp8": "ep_dispatch.hip",
+    "combine": "ep_combine.hip", "layout_count": "ep_layout.hip",
+    "layout_scatter": "ep_layout.hip",
+}
+
+
+def source_digest(kernel_key: str) -> str:
+    """Digest of what a kernel's counters depend on: its source file, the
+    internal header and the hipcc flags."""
+    from combine_ep_layout_04_amd.build import HIPCC_FLAGS
+
+    csrc = os.path.join(ROOT, "combine_ep_layout_04_amd", "csrc")
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "combine_ep_layout_04_amd", "csrc", "*")))
-    files.append(os.path.join(ROOT, "include", "ep.h"))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+    for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    h.update(" ".join(HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -68,23 +80,19 @@ def bytes_model(T, H, k, n):
 def read_traffic(kernel_key: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE,
     scaled by a plain copy's counters; None when the measurement is missing
-    or was taken on different kernel sources."""
+    or was taken on a different version of that kernel."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    rec = {}
     for line in open(TRAFFIC_FILE):
         line = line.strip()
-        if line.startswith("#") or "=" not in line:
+        if line.startswith("#") or not line.startswith("kernel="):
             continue
-        fields = dict(kv.split("=", 1) for kv in line.split())
-        if "kernel" in fields:
-            rec[fields["kernel"]] = fields
-        elif "source_digest" in fields:
-            rec["_digest"] = fields["source_digest"]
-    if rec.get("_digest") != source_digest() or kernel_key not in rec:
-        return None
-    r = rec[kernel_key]
-    return float(r["hbm_bytes_per_launch"])
+        fields = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+        if fields.get("kernel") == kernel_key:
+            if fields.get("source_digest") != source_digest(kernel_key):
+                return None
+            return float(fields["hbm_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(inp, E, nbytes):

@@ -201,7 +201,13 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, fl
         const float sc = amax / 448.0f;
         scale = sc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c[i] = amax == 0.0f ? 0u : e4m3_rne_sat(f[i] / sc);
+        for (int i = 0; i < 16; ++i) {
+            const float q = f[i] / sc;
+            // a NaN quotient (NaN x, or infinite x over an infinite scale)
+            // is S.1111.111 with the sign of x, whatever NaN the divide made
+            const uint32_t sx = (__float_as_uint(f[i]) >> 24) & 0x80u;
+            c[i] = amax == 0.0f ? 0u : (q != q ? (0x7Fu | sx) : e4m3_rne_sat(q));
+        }
     }
     uint4 q;
     q.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);

@@ -9,11 +9,15 @@
 
 namespace ep {
 
-// Layout: pairs are processed in chunks of kLayoutChunk flat indices; one
-// workgroup of kLayoutThreads owns a chunk in both passes.
+// Layout: pairs are processed in chunks of flat indices, one workgroup of
+// kLayoutThreads per chunk in both launches.  A chunk holds at least
+// kLayoutMinChunk pairs and the chunk count never exceeds kLayoutMaxChunks,
+// so the per-workgroup histogram pass stays bounded for any input size.
 constexpr int kLayoutThreads = 256;
-constexpr int kLayoutChunk = 1024;
+constexpr int64_t kLayoutMinChunk = 1024;
+constexpr int64_t kLayoutMaxChunks = 256;
 
+int64_t layout_chunk_pairs(int64_t pairs);
 int64_t layout_num_chunks(int64_t pairs);
 size_t layout_workspace_bytes(int64_t pairs, int num_experts);
 

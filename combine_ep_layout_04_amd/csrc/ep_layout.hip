@@ -13,22 +13,26 @@
 //
 // The pages' preprocessing counts with atomics; here atomics only ever
 // produce counts, never positions, so the result is a deterministic stable
-// counting sort.  Three launches, each linear in the number of pairs:
+// counting sort.  Two launches, each linear in the number of pairs:
 //
-//   1. count:   one workgroup per chunk of kLayoutChunk pairs builds the
-//               chunk's expert histogram in LDS -> hist[c][e].
-//   2. scan:    one workgroup of 1024 threads turns hist into per-(chunk,
-//               expert) starting rows in place (column running sums over
-//               chunks plus the exclusive scan over experts) and writes
-//               counts / offsets.
-//   3. scatter: each chunk again, in batches of 256 pairs.  Inside a batch
-//               every pair sets its bit in an LDS bit-matrix row of its
-//               expert (256 bits = 8 words per expert); its rank among
+//   1. count:   one workgroup per chunk of pairs (1024, or more once there
+//               would be over 256 chunks) builds the
+//               chunk's expert histogram in LDS and writes it transposed,
+//               hist[e][c], with the chunk count padded to a multiple of 4
+//               (padding chunks are empty and write zeros).
+//   2. scatter: each workgroup first derives what it needs from the whole
+//               histogram -- every expert's total (for offsets) and its rows
+//               in earlier chunks -- reading each expert's chunk counts as
+//               16-byte vectors; workgroup 0 also writes counts, offsets and
+//               num_invalid.  Then it walks its chunk in batches of 256
+//               pairs: every pair sets its bit in an LDS bit-matrix row of
+//               its expert (256 bits = 8 words per expert); its rank among
 //               earlier pairs of the same expert is a popcount of the bits
-//               below its own, so no ordering depends on atomic timing.
+//               below its own, so no position depends on atomic timing.
 //
-// The workspace holds hist (C*E int32, rewritten in place by the scan) and
-// one invalid-entry count per chunk.
+// The workspace holds hist (E * Cp int32) and one invalid-entry count per
+// chunk.  Folding the scan into the scatter saves a launch: at 64 chunks the
+// redundant per-workgroup reads are 64 KiB from L2 each.
 
 #include "ep_internal.h"
 
@@ -37,9 +41,8 @@ namespace {
 
 constexpr int kMaxExperts = 1024;                 // EP_MAX_EXPERTS
 constexpr int kWords = kLayoutThreads / 32;       // bit words per expert per batch
-constexpr int kScanThreads = 1024;
 
-static_assert(kLayoutChunk % kLayoutThreads == 0, "chunk must be whole batches");
+static_assert(kLayoutMinChunk % kLayoutThreads == 0, "chunk must be whole batches");
 
 // Exclusive scan of one int per thread over the workgroup (blockDim a
 // multiple of 64).  `waves` is LDS scratch of blockDim/64 ints.  Returns the
@@ -68,8 +71,8 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t* waves, int32_t* tota
 }
 
 __global__ __launch_bounds__(kLayoutThreads)
-void layout_count_kernel(const int64_t* __restrict__ idx, int64_t pairs, int E,
-                         int32_t* __restrict__ hist, int32_t* __restrict__ bad)
+void layout_count_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64_t chunk, int E,
+                         int cpad, int32_t* __restrict__ hist, int32_t* __restrict__ bad)
 {
     __shared__ int32_t cnt[kMaxExperts];
     __shared__ int32_t nbad;
@@ -78,8 +81,8 @@ void layout_count_kernel(const int64_t* __restrict__ idx, int64_t pairs, int E,
     if (tid == 0) nbad = 0;
     __syncthreads();
 
-    const int64_t begin = (int64_t)blockIdx.x * kLayoutChunk;
-    const int64_t end = min(begin + (int64_t)kLayoutChunk, pairs);
+    const int64_t begin = (int64_t)blockIdx.x * chunk;
+    const int64_t end = min(begin + chunk, pairs);
 #pragma unroll 4
     for (int64_t i = begin + tid; i < end; i += kLayoutThreads) {
         const int64_t e = idx[i];
@@ -90,113 +93,94 @@ void layout_count_kernel(const int64_t* __restrict__ idx, int64_t pairs, int E,
     }
     __syncthreads();
 
-    int32_t* h = hist + (int64_t)blockIdx.x * E;
-    for (int e = tid; e < E; e += kLayoutThreads) h[e] = cnt[e];
+    for (int e = tid; e < E; e += kLayoutThreads) hist[(int64_t)e * cpad + blockIdx.x] = cnt[e];
     if (tid == 0) bad[blockIdx.x] = nbad;
 }
 
-// hist is C rows (chunks) x E columns (experts).  The 1024 threads tile it:
-// epad = E rounded up to a power of two columns, tpc = 1024 / epad threads
-// per column, each owning a contiguous slab of rows.  Loads are batched
-// kBatch at a time so a thread has one memory round trip per batch, not one
-// per row.
-constexpr int kBatch = 16;
-
-__global__ __launch_bounds__(kScanThreads)
-void layout_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
-                        int num_chunks, int E, int epad, int32_t* __restrict__ counts,
-                        int32_t* __restrict__ offsets, int32_t* __restrict__ num_invalid)
+// Sum of n int32 at p (16-byte aligned, n a multiple of 4), and the sum of
+// the first `upto` of them.
+__device__ __forceinline__ void sum_row(const int32_t* p, int n, int upto, int32_t& all,
+                                        int32_t& before)
 {
-    __shared__ int32_t part_sum[kScanThreads];
-    __shared__ int32_t col_start[kMaxExperts];
-    __shared__ int32_t waves[kScanThreads / 64];
-    __shared__ int32_t nbad;
-    const int tid = threadIdx.x;
-    const int tpc = kScanThreads / epad;
-    const int col = tid & (epad - 1);
-    const int part = tid / epad;
-    const int rows = (num_chunks + tpc - 1) / tpc;
-    const int r0 = min(part * rows, num_chunks);
-    const int r1 = min(r0 + rows, num_chunks);
-    const bool live = col < E;
-    if (tid == 0) nbad = 0;
-
-    // 1. sum of this thread's slab of its column
-    int32_t mine = 0;
-    if (live) {
-        for (int r = r0; r < r1; r += kBatch) {
-            int32_t h[kBatch];
+    const int4* v = reinterpret_cast<const int4*>(p);
+    int32_t a = 0, b = 0;
+    for (int i0 = 0; i0 < n / 4; i0 += 8) {
+        int4 q[8];
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b)
-                h[b] = (r + b < r1) ? hist[(int64_t)(r + b) * E + col] : 0;
+        for (int u = 0; u < 8; ++u) q[u] = (i0 + u < n / 4) ? v[i0 + u] : make_int4(0, 0, 0, 0);
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) mine += h[b];
+        for (int u = 0; u < 8; ++u) {
+            const int c = 4 * (i0 + u);
+            a += q[u].x + q[u].y + q[u].z + q[u].w;
+            b += (c < upto ? q[u].x : 0) + (c + 1 < upto ? q[u].y : 0) +
+                 (c + 2 < upto ? q[u].z : 0) + (c + 3 < upto ? q[u].w : 0);
         }
     }
-    part_sum[tid] = mine;
-    __syncthreads();
-
-    // 2. column total, and the rows of this column in earlier slabs
-    int32_t before = 0, tot = 0;
-    for (int q = 0; q < tpc; ++q) {
-        const int32_t v = part_sum[col + q * epad];
-        before += (q < part) ? v : 0;
-        tot += v;
-    }
-    // 3. exclusive scan of column totals over experts: the part-0 threads
-    // are tids 0..epad-1, in column order, and everyone else adds 0
-    int32_t n = 0;
-    const int32_t start = block_exclusive_scan((part == 0 && live) ? tot : 0, waves, &n);
-    if (part == 0) col_start[col] = start;
-    __syncthreads();
-
-    // 4. rewrite the slab in place with each (chunk, expert)'s first row
-    if (live) {
-        int32_t run = col_start[col] + before;
-        for (int r = r0; r < r1; r += kBatch) {
-            int32_t h[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b)
-                h[b] = (r + b < r1) ? hist[(int64_t)(r + b) * E + col] : 0;
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                if (r + b < r1) hist[(int64_t)(r + b) * E + col] = run;
-                run += h[b];
-            }
-        }
-        if (part == 0) {
-            counts[col] = tot;
-            offsets[col] = start;
-        }
-    }
-    if (tid == 0) offsets[E] = n;
-
-    if (num_invalid) {
-        int32_t b = 0;
-        for (int c = tid; c < num_chunks; c += kScanThreads) b += bad[c];
-        if (b) atomicAdd(&nbad, b);
-        __syncthreads();
-        if (tid == 0) *num_invalid = nbad;
-    }
+    all = a;
+    before = b;
 }
 
 __global__ __launch_bounds__(kLayoutThreads)
-void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int k, int E,
-                           const int32_t* __restrict__ start, int32_t* __restrict__ slot,
-                           int32_t* __restrict__ src)
+void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64_t chunk, int k,
+                           int E, int cpad, int num_chunks, const int32_t* __restrict__ hist,
+                           const int32_t* __restrict__ bad, int32_t* __restrict__ counts,
+                           int32_t* __restrict__ offsets, int32_t* __restrict__ slot,
+                           int32_t* __restrict__ src, int32_t* __restrict__ num_invalid)
 {
     __shared__ int32_t base[kMaxExperts];
+    __shared__ int32_t total[kMaxExperts];
     __shared__ uint32_t bits[kMaxExperts * kWords];
+    __shared__ int32_t waves[kLayoutThreads / 64];
+    __shared__ int32_t nbad;
     const int tid = threadIdx.x;
     const int64_t c = blockIdx.x;
 
-    const int32_t* s = start + c * E;
-    for (int e = tid; e < E; e += kLayoutThreads) base[e] = s[e];
+    // 1. every expert's total and its rows in chunks before this one
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        int32_t all, before;
+        sum_row(hist + (int64_t)e * cpad, cpad, (int)c, all, before);
+        total[e] = all;
+        base[e] = before;
+    }
     for (int w = tid; w < E * kWords; w += kLayoutThreads) bits[w] = 0;
+    if (tid == 0) nbad = 0;
     __syncthreads();
 
-    const int64_t begin = c * kLayoutChunk;
-    const int64_t end = min(begin + (int64_t)kLayoutChunk, pairs);
+    // 2. exclusive scan of the totals over experts: thread t owns the
+    // contiguous experts [t*per, t*per + per)
+    const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
+    int32_t local = 0;
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        if (e < E) local += total[e];
+    }
+    int32_t n = 0;
+    int32_t run = block_exclusive_scan(local, waves, &n);
+    for (int q = 0; q < per; ++q) {
+        const int e = tid * per + q;
+        if (e < E) {
+            const int32_t tot = total[e];
+            base[e] += run;
+            if (c == 0) {
+                counts[e] = tot;
+                offsets[e] = run;
+            }
+            run += tot;
+        }
+    }
+    if (c == 0) {
+        if (tid == 0) offsets[E] = n;
+        if (num_invalid) {
+            int32_t b = 0;
+            for (int cc = tid; cc < num_chunks; cc += kLayoutThreads) b += bad[cc];
+            if (b) atomicAdd(&nbad, b);
+        }
+    }
+    __syncthreads();
+    if (c == 0 && num_invalid && tid == 0) *num_invalid = nbad;
+
+    const int64_t begin = c * chunk;
+    const int64_t end = min(begin + chunk, pairs);
     const int word = tid >> 5;
     const uint32_t bit = 1u << (tid & 31);
 
@@ -237,15 +221,29 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int k
 
 }  // namespace
 
+int64_t layout_chunk_pairs(int64_t pairs)
+{
+    // at least kLayoutMinChunk, a whole number of 256-pair batches, and few
+    // enough chunks that C <= kLayoutMaxChunks
+    const int64_t need = (pairs + kLayoutMaxChunks - 1) / kLayoutMaxChunks;
+    const int64_t c = (need + kLayoutThreads - 1) / kLayoutThreads * kLayoutThreads;
+    return c < kLayoutMinChunk ? kLayoutMinChunk : c;
+}
+
 int64_t layout_num_chunks(int64_t pairs)
 {
-    return pairs <= 0 ? 1 : (pairs + kLayoutChunk - 1) / kLayoutChunk;
+    const int64_t chunk = layout_chunk_pairs(pairs);
+    return pairs <= 0 ? 1 : (pairs + chunk - 1) / chunk;
 }
+
+// chunks padded to a multiple of 4 so each expert's row of the histogram is
+// a whole number of 16-byte vectors
+static int64_t padded_chunks(int64_t pairs) { return (layout_num_chunks(pairs) + 3) & ~(int64_t)3; }
 
 size_t layout_workspace_bytes(int64_t pairs, int num_experts)
 {
-    const int64_t C = layout_num_chunks(pairs);
-    const size_t bytes = (size_t)(C * (int64_t)num_experts + C) * sizeof(int32_t);
+    const int64_t Cp = padded_chunks(pairs);
+    const size_t bytes = (size_t)(Cp * (int64_t)num_experts + Cp) * sizeof(int32_t);
     return (bytes + 255) & ~(size_t)255;
 }
 
@@ -255,25 +253,21 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_to
                          hipStream_t stream)
 {
     const int64_t pairs = num_tokens * (int64_t)num_topk;
+    const int64_t chunk = layout_chunk_pairs(pairs);
     const int64_t C = layout_num_chunks(pairs);
+    const int64_t Cp = padded_chunks(pairs);
     int32_t* hist = static_cast<int32_t*>(workspace);
-    int32_t* bad = hist + C * num_experts;
+    int32_t* bad = hist + Cp * num_experts;
 
-    hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)C), dim3(kLayoutThreads), 0, stream,
-                       topk_idx, pairs, num_experts, hist, bad);
+    // Cp workgroups: the padding chunks start past the end and write zeros
+    hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)Cp), dim3(kLayoutThreads), 0, stream,
+                       topk_idx, pairs, chunk, num_experts, (int)Cp, hist, bad);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    int epad = 1;
-    while (epad < num_experts) epad <<= 1;
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                       hist, bad, (int)C, num_experts, epad, counts, offsets, num_invalid);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
-    if (pairs == 0) return hipSuccess;
     hipLaunchKernelGGL(layout_scatter_kernel, dim3((unsigned)C), dim3(kLayoutThreads), 0, stream,
-                       topk_idx, pairs, num_topk, num_experts, hist, slot, src);
+                       topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C, hist, bad, counts,
+                       offsets, slot, src, num_invalid);
     return hipGetLastError();
 }
 

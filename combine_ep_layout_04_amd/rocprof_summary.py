@@ -2,10 +2,17 @@
 
     python -m combine_ep_layout_04_amd.rocprof_summary stats DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary pmc DIR --cmd "..." > profiles/X.md
+    python -m combine_ep_layout_04_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
+        --cmd "..." --out profiles/hbm_traffic_headline.txt
 
 ``stats`` reads ``*_kernel_stats.csv`` (from ``--kernel-trace --stats``);
 ``pmc`` reads ``*_counter_collection.csv`` (from ``--pmc``) and reports the
-mean counter value per dispatch for each kernel.
+mean counter value per dispatch for each kernel; ``traffic`` takes one
+FETCH_SIZE run and one WRITE_SIZE run of ``bench.py --copy-calibration``,
+scales each counter by what it reads for the plain 1 GiB elementwise copy
+(torch.neg on int32: 1 GiB read, 1 GiB written) and writes HBM bytes per
+launch for each library kernel, tagged with the digest of the kernel
+sources the counters were taken on.
 """
 
 from __future__ import annotations
@@ -56,13 +63,67 @@ def pmc(d: str):
     return out
 
 
+def _counter_means(d: str):
+    vals = defaultdict(list)
+    for f in _find(d, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName")
+                vals[name].append(float(r.get("Counter_Value") or r.get("Counter-Value")))
+    return {k: statistics.fmean(v) for k, v in vals.items()}
+
+
+# library kernels by the key bench.py reports them under
+KERNEL_KEYS = {"dispatch_bf16": "dispatch_bf16_kernel", "dispatch_fp8": "dispatch_fp8_kernel",
+               "combine": "combine_kernel", "layout_count": "layout_count_kernel",
+               "layout_scatter": "layout_scatter_kernel"}
+COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
+
+
+def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
+    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+
+    def pick(table, needle):
+        hits = [v for k, v in table.items() if needle in k]
+        if len(hits) != 1:
+            sys.exit(f"expected one kernel matching {needle!r}, found {len(hits)}")
+        return hits[0]
+
+    f_scale = COPY_KIB / pick(fetch, "neg_kernel")
+    w_scale = COPY_KIB / pick(write, "neg_kernel")
+    lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+             "# each scaled by the same counter on a plain 1 GiB elementwise copy (torch.neg,",
+             "# int32): scale = 1048576 KiB / counter.  Commands:",
+             *[f"#   {c}" for c in cmd.split(" ;; ")],
+             "# source_digest: the kernel's source file, internal header and hipcc flags",
+             f"copy_scale fetch={f_scale:.4f} write={w_scale:.4f}"]
+    for key, needle in KERNEL_KEYS.items():
+        fk, wk = pick(fetch, needle), pick(write, needle)
+        b = (fk * f_scale + wk * w_scale) * 1024.0
+        lines.append(f"kernel={key} fetch_kib={fk:.1f} write_kib={wk:.1f} "
+                     f"hbm_bytes_per_launch={b:.0f} source_digest={digest(key)}")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc"])
+    ap.add_argument("kind", choices=["stats", "pmc", "traffic"])
     ap.add_argument("dir")
-    ap.add_argument("--cmd", required=True, help="the command that produced the data")
+    ap.add_argument("dir2", nargs="?")
+    ap.add_argument("--cmd", required=True, help="the command(s) that produced the data")
     ap.add_argument("--title", default="")
+    ap.add_argument("--out")
     a = ap.parse_args()
+    if a.kind == "traffic":
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        sys.path.insert(0, root)
+        from bench import source_digest
+        text = "\n".join(traffic(a.dir, a.dir2, source_digest, a.cmd)) + "\n"
+        if a.out:
+            with open(a.out, "w") as fh:
+                fh.write(text)
+        print(text, end="")
+        return
     lines = [f"# {a.title or a.kind}", "", "Command:", "", "```", a.cmd, "```", ""]
     lines += stats(a.dir) if a.kind == "stats" else pmc(a.dir)
     print("\n".join(lines))

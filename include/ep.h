@@ -142,7 +142,10 @@ int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num
  *                    amax / 448 (fp32, correctly rounded), code = OCP E4M3
  *                    of x / scale (fp32 quotient, correctly rounded) with
  *                    round-to-nearest-even and saturation to +-448; a block
- *                    with amax == 0 gets scale 0 and zero codes.
+ *                    with amax == 0 gets scale 0 and zero codes.  amax
+ *                    ignores NaN; a NaN quotient (NaN x, or infinite x in
+ *                    a block whose amax is infinite) gives 0x7F with the
+ *                    sign of x.
  *      recv_scales   fp32 [rows, hidden/128]; required for FP8, else NULL.
  *      recv_weights  fp32 [rows] or NULL: recv_weights[slot[t,j]] =
  *                    topk_weights[t,j] (needs topk_weights).

@@ -151,22 +151,37 @@ def layout(topk_idx: np.ndarray, E: int):
 # ---------------------------------------------------------------- dispatch --
 
 def fp8_quantize_row(x_bits: np.ndarray):
-    """Per 128-channel block: amax (exact), scale = float32(amax / 448),
-    code = nearest E4M3 of float32(x / scale).  Returns (codes, scales)."""
+    """Per 128-channel block: amax (exact, NaN ignored), scale =
+    float32(amax / 448), code = nearest E4M3 of float32(x / scale); a NaN
+    quotient gives S.1111.111 with the sign of x.  Returns (codes, scales)."""
     H = x_bits.shape[0]
-    xs = [float(bf16_value(int(b))) for b in x_bits]
+    xs = [_bf16_float(int(b)) for b in x_bits]
     codes, scales = [], []
     for b in range(H // 128):
         blk = xs[b * 128:(b + 1) * 128]
-        amax = np.float32(max(abs(v) for v in blk))
+        amax = np.float32(max((abs(v) for v in blk if v == v), default=0.0))
         scale = np.float32(amax / np.float32(448.0))
         scales.append(float(scale))
         for v in blk:
             if amax == 0:
                 codes.append(0)
+                continue
+            with np.errstate(invalid="ignore"):
+                q = np.float32(np.float32(v) / scale)
+            if q != q:   # NaN quotient: S.1111.111 with the sign of x
+                codes.append(0x7F | (0x80 if np.signbit(np.float32(v)) else 0))
             else:
-                codes.append(e4m3_encode(float(np.float32(np.float32(v) / scale))))
+                codes.append(e4m3_encode(float(q)))
     return np.array(codes, np.uint8), np.array(scales, np.float32)
+
+
+def _bf16_float(code: int) -> float:
+    """bf16 code -> Python float, including infinities and NaN."""
+    if (code & 0x7F80) == 0x7F80:
+        if code & 0x7F:
+            return float("nan") if not code & 0x8000 else -float("nan")
+        return -float("inf") if code & 0x8000 else float("inf")
+    return float(bf16_value(code))
 
 
 # ----------------------------------------------------------------- combine --

@@ -202,9 +202,9 @@ void oracle_dispatch_bf16(const uint16_t *x, int64_t T, int H, int k,
         }
 }
 
-/* Per token t and channel block b of 128: amax = max |x|, scale =
- * fl32(amax/448), q = e4m3(fl32(x/scale)); amax == 0 gives scale 0 and
- * all-zero codes.  The same codes and scales go to every unmasked row of t:
+/* Per token t and channel block b of 128: amax = max |x| (NaN ignored),
+ * scale = fl32(amax/448), q = e4m3(fl32(x/scale)); amax == 0 gives scale 0
+ * and all-zero codes; a NaN quotient gives 0x7F with the sign of x.  The same codes and scales go to every unmasked row of t:
  * recv_q [N, H] bytes, recv_scales [N, H/128] fp32. */
 void oracle_dispatch_fp8(const uint16_t *x, int64_t T, int H, int k,
                          const int32_t *slot, const float *topk_weights,
@@ -230,7 +230,11 @@ void oracle_dispatch_fp8(const uint16_t *x, int64_t T, int H, int k,
                     row_q[b * 128 + c] = 0x00;
                 } else {
                     float v = (float)oracle_bf16_to_double(xr[b * 128 + c]);
-                    row_q[b * 128 + c] = oracle_e4m3_encode(v / scale);
+                    float q = v / scale;
+                    /* a NaN quotient (NaN x, or infinite x over an infinite
+                     * scale) is S.1111.111 with the sign of x */
+                    row_q[b * 128 + c] = isnan(q) ? (uint8_t)(0x7F | (signbit(v) ? 0x80 : 0))
+                                                  : oracle_e4m3_encode(q);
                 }
             }
         }

@@ -129,6 +129,8 @@ def check_case(idx, x_bits, w, E, seed=0, use_weights=True, stream=None):
     (64, 64, 64, 128),     # k = EP_MAX_TOPK
     (2048, 4, 1024, 256),  # E = EP_MAX_EXPERTS
     (16, 2, 8, 65536),     # hidden = EP_MAX_HIDDEN
+    (40000, 8, 1024, 8),   # 320000 pairs: 1280-pair chunks, 250 of them
+    (65537, 8, 256, 8),    # 524296 pairs: 2304-pair chunks, a ragged last one
 ])
 def test_shapes(T, k, E, H):
     inp = make_random_case(T * 31 + k, T, H, E, k, mask_frac=0.1, dup_frac=0.0 if k <= E else 1.0)
@@ -166,7 +168,8 @@ def test_unit_weights():
 
 
 def test_fp8_special_blocks():
-    # zero blocks, negative zeros, subnormal-range values and huge outliers
+    # zero blocks, negative zeros, subnormal-range values, huge outliers,
+    # both sides of the fast-quotient threshold, infinities and NaNs
     inp = make_random_case(11, 40, 512, 8, 2)
     x = float32_from_bf16_bits(inp.x_bits).copy()
     x[0, :128] = 0.0
@@ -179,7 +182,19 @@ def test_fp8_special_blocks():
     x[6, :128] = 0.0
     x[6, 3] = 1e-38        # a block whose amax is an fp32 denormal
     x[6, 9] = -2e-39
+    # either side of the fast-quotient threshold amax = 2^-80
+    x[7, :128] = np.float32(2.0 ** -83) * x[7, :128] / np.abs(x[7, :128]).max()
+    x[7, 5] = 2.0 ** -80
+    x[7, 128:256] = np.float32(2.0 ** -84) * x[7, 128:256] / np.abs(x[7, 128:256]).max()
+    x[7, 130] = -(2.0 ** -80) * (1 - 2.0 ** -8)
+    # non-finite blocks: infinities (amax = inf) and NaNs (ignored by amax)
+    x[8, 3] = np.inf
+    x[8, 4] = -np.inf
+    x[8, 260] = np.nan
+    x[9, :128] = np.nan
+    x[9, 200] = -np.inf
     xb = bf16_bits_from_float32(x)
+    xb[8, 261] = 0xFFC0    # a negative NaN
     check_case(inp.topk_idx, xb, inp.topk_weights, 8)
 
 

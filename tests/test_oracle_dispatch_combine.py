@@ -126,6 +126,29 @@ def test_dispatch_fp8_vs_bruteforce_rows():
                 np.testing.assert_array_equal(sc[r], bs)
 
 
+def test_dispatch_fp8_nonfinite_vs_bruteforce():
+    # amax ignores NaN; an infinite amax makes finite x encode to signed
+    # zero and infinite x to NaN; a NaN quotient is 0x7F with the sign of x
+    inp = make_random_case(21, 4, 256, 4, 1)
+    x = float32_from_bf16_bits(inp.x_bits).copy()
+    x[0, 3], x[0, 4] = np.inf, -np.inf
+    x[1, 130] = np.nan
+    x[2, :128] = np.nan
+    x[2, 7] = -np.inf
+    xb = bf16_bits_from_float32(x)
+    xb[1, 130] = 0x7FC0    # NaNs with either sign bit (torch's cast makes 0xFFFF)
+    xb[1, 131] = 0xFFC0
+    slot = np.arange(4, dtype=np.int32)[:, None]
+    q, sc, _ = oracle.dispatch_fp8(xb, slot)
+    for t in range(4):
+        bq, bs = brute.fp8_quantize_row(xb[t])
+        np.testing.assert_array_equal(q[t], bq)
+        np.testing.assert_array_equal(sc[t], bs)
+    assert q[0, 3] == 0x7F and q[0, 4] == 0xFF and q[0, 5] in (0x00, 0x80)
+    assert q[1, 130] == 0x7F and q[1, 131] == 0xFF
+    assert np.isinf(sc[0, 0]) and np.isfinite(sc[1, 1])
+
+
 def test_dispatch_fp8_error_bound():
     inp = make_inputs(WORKLOADS["fp8"], T=128)
     slot = np.arange(128, dtype=np.int32)[:, None]
