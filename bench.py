@@ -44,7 +44,8 @@ def log(*a):
 # header and the build flags)
 KERNEL_SOURCES = {
     "dispatch_bf16": "ep_dispatch.hip", "dispatch_fp8": "ep_dispatch.hip",
-    "combine": "ep_combine.hip", "layout_count": "ep_layout.hip",
+    "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
+    "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
 }
 
@@ -72,6 +73,12 @@ def bytes_model(T, H, k, n):
         "dispatch_fp8": T * H * 2 + n * H + n * (H // 128) * 4 + T * k * 4,
         # read every dispatched row once, write out once, read slot and weights
         "combine": n * H * 2 + T * H * 2 + T * k * 4 + T * k * 4,
+        # read g and every expert row once, write every row gradient once,
+        # read slot and weights, write the weight gradients
+        "combine_backward": T * H * 2 + 2 * n * H * 2 + T * k * 12,
+        # read every row gradient once, write grad_x, read slot, gather the
+        # row weight gradients into [T, k]
+        "dispatch_backward": n * H * 2 + T * H * 2 + T * k * 4 + n * 4 + T * k * 4,
         # read topk_idx, write slot and src
         "layout": T * k * 8 + T * k * 4 + n * 4,
     }
@@ -241,6 +248,60 @@ def main():
     stream.synchronize()
     f8 = [e[0].elapsed_time(e[1]) for e in fev]
 
+    # ---- backward passes on the headline layout (identity experts: y is
+    # the dispatched rows; g and the row weight gradients are seeded N(0,1))
+    from combine_ep_layout_04_amd.inputs import make_gradient
+    with torch.cuda.stream(stream):
+        gout = torch.from_numpy(make_gradient(T, H, 7).view(np.int16)).view(torch.bfloat16).to(dev)
+        grad_y = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+        grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        grw = torch.randn(P, generator=torch.Generator().manual_seed(8)).to(dev)
+    stream.synchronize()
+    check(L.ep_layout(p["idx"], T, k, E, p["counts"], p["offsets"], p["slot"], p["src"],
+                      p["inval"], p["ws"], ws_bytes, s), "ep_layout")
+    check(L.ep_dispatch(p["x"], T, H, k, p["slot"], None, 0, p["recv"], None, None, s),
+          "ep_dispatch")
+
+    def time_call(fn, reps):
+        evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(-args.warmup, reps):
+            if i >= 0:
+                evl[i][0].record(stream)
+            fn()
+            if i >= 0:
+                evl[i][1].record(stream)
+        stream.synchronize()
+        return us([e[0].elapsed_time(e[1]) for e in evl])
+
+    cb_us = time_call(lambda: check(L.ep_combine_backward(
+        gout.data_ptr(), p["recv"], p["slot"], p["wt"], T, H, k, grad_y.data_ptr(),
+        grad_w.data_ptr(), s), "ep_combine_backward"), args.steps)
+    db_us = time_call(lambda: check(L.ep_dispatch_backward(
+        p["recv"], grw.data_ptr(), p["slot"], T, H, k, p["out"], grad_w.data_ptr(), s),
+        "ep_dispatch_backward"), args.steps)
+    del grad_y
+
+    # ---- layout variants on the headline routing: segment starts aligned
+    # to 128 rows, and a fixed 320 rows per expert (1.25x the mean load)
+    def time_layout(alignment, capacity, reps):
+        rows = ep.layout_max_rows(T, k, E, alignment, capacity)
+        src_x = torch.empty(rows, **i32)
+        drop = torch.empty(1, **i32)
+        evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(-args.warmup, reps):
+            if i >= 0:
+                evl[i][0].record(stream)
+            check(L.ep_layout_ex(p["idx"], T, k, E, alignment, capacity, p["counts"],
+                                 p["offsets"], p["slot"], src_x.data_ptr(), p["inval"],
+                                 drop.data_ptr(), p["ws"], ws_bytes, s), "ep_layout_ex")
+            if i >= 0:
+                evl[i][1].record(stream)
+        stream.synchronize()
+        return us([e[0].elapsed_time(e[1]) for e in evl]), int(drop.item())
+
+    lay_a128, _ = time_layout(128, 0, args.steps)
+    lay_cap, dropped_cap = time_layout(1, 320, args.steps)
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly 1 GiB each
         a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
@@ -257,6 +318,10 @@ def main():
         "combine": {"us": round(us(com), 2), "bytes": bm["combine"]},
         "dispatch_fp8": {"us": round(us(f8), 2), "bytes": bmf["dispatch_fp8"],
                          "workload": "fp8: headline shape, 1% of rows x100"},
+        "combine_backward": {"us": round(cb_us, 2), "bytes": bm["combine_backward"]},
+        "dispatch_backward": {"us": round(db_us, 2), "bytes": bm["dispatch_backward"]},
+        "layout_aligned128": {"us": round(lay_a128, 2)},
+        "layout_capacity320": {"us": round(lay_cap, 2), "dropped_pairs": dropped_cap},
     }
     for key, v in per_kernel.items():
         if "bytes" in v:

@@ -76,9 +76,25 @@ size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_expert
     return ep::layout_workspace_bytes(num_tokens * (int64_t)num_topk, num_experts);
 }
 
-int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-              int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
-              int32_t* num_invalid, void* workspace, size_t workspace_bytes, void* stream)
+int64_t ep_layout_max_rows(int64_t num_tokens, int num_topk, int num_experts, int alignment,
+                           int64_t expert_capacity)
+{
+    if (num_tokens < 0 || num_topk < 1 || num_topk > EP_MAX_TOPK || num_experts < 1 ||
+        num_experts > EP_MAX_EXPERTS || alignment < 1 || alignment > EP_MAX_ALIGNMENT ||
+        expert_capacity < 0 || (expert_capacity > 0 && expert_capacity % alignment != 0) ||
+        num_tokens * (int64_t)num_topk >= ((int64_t)1 << 31))
+        return -1;
+    const int64_t pairs = num_tokens * (int64_t)num_topk;
+    if (expert_capacity > 0) return (int64_t)num_experts * expert_capacity;
+    // every expert with at least one pair may add up to alignment-1 rows
+    const int64_t touched = pairs < num_experts ? pairs : num_experts;
+    return pairs + touched * (alignment - 1);
+}
+
+int ep_layout_ex(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                 int alignment, int64_t expert_capacity, int32_t* counts, int32_t* offsets,
+                 int32_t* slot, int32_t* src, int32_t* num_invalid, int32_t* num_dropped,
+                 void* workspace, size_t workspace_bytes, void* stream)
 {
     g_last_error[0] = '\0';
     int st = check_tokens(num_tokens, num_topk);
@@ -86,6 +102,18 @@ int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
         return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
                     EP_MAX_EXPERTS);
+    if (alignment < 1 || alignment > EP_MAX_ALIGNMENT)
+        return fail(EP_INVALID_ARGUMENT, "alignment %d outside [1, %d]", alignment,
+                    EP_MAX_ALIGNMENT);
+    if (expert_capacity < 0 || (expert_capacity > 0 && expert_capacity % alignment != 0))
+        return fail(EP_INVALID_ARGUMENT,
+                    "expert_capacity %lld must be 0 or a positive multiple of alignment %d",
+                    (long long)expert_capacity, alignment);
+    const int64_t rows = ep_layout_max_rows(num_tokens, num_topk, num_experts, alignment,
+                                            expert_capacity);
+    if (rows < 0 || rows >= ((int64_t)1 << 31))
+        return fail(EP_UNSUPPORTED, "the layout could need %lld rows; rows must stay below 2^31",
+                    (long long)rows);
     if (!counts || !offsets) return fail(EP_INVALID_ARGUMENT, "counts and offsets are required");
     if (num_tokens > 0 && (!topk_idx || !slot))
         return fail(EP_INVALID_ARGUMENT, "topk_idx and slot are required");
@@ -96,10 +124,19 @@ int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num
         return fail(EP_INVALID_ARGUMENT, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if ((reinterpret_cast<uintptr_t>(topk_idx) & 7u))
         return fail(EP_INVALID_ARGUMENT, "topk_idx must be 8-byte aligned");
-    return from_hip(ep::launch_layout(topk_idx, num_tokens, num_topk, num_experts, counts, offsets,
-                                      slot, src, num_invalid, workspace,
+    return from_hip(ep::launch_layout(topk_idx, num_tokens, num_topk, num_experts, alignment,
+                                      (int)expert_capacity, counts, offsets, slot, src,
+                                      num_invalid, num_dropped, workspace,
                                       static_cast<hipStream_t>(stream)),
                     "ep_layout launch");
+}
+
+int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+              int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+              int32_t* num_invalid, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets, slot,
+                        src, num_invalid, nullptr, workspace, workspace_bytes, stream);
 }
 
 int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
@@ -148,8 +185,53 @@ int ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
     if (!aligned16(y) || !aligned16(out))
         return fail(EP_INVALID_ARGUMENT, "y and out must be 16-byte aligned");
     return from_hip(ep::launch_combine(y, slot, topk_weights, num_tokens, hidden, num_topk, out,
-                                       static_cast<hipStream_t>(stream)),
+                                       nullptr, nullptr, static_cast<hipStream_t>(stream)),
                     "ep_combine launch");
+}
+
+int ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                        const float* topk_weights, int64_t num_tokens, int hidden, int num_topk,
+                        void* grad_y, float* grad_topk_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 8);
+    if (st) return st;
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!grad_out || !slot || !grad_y)
+        return fail(EP_INVALID_ARGUMENT, "grad_out, slot and grad_y are required");
+    if (grad_topk_weights && !y)
+        return fail(EP_INVALID_ARGUMENT, "grad_topk_weights needs the expert outputs y");
+    if (!aligned16(grad_out) || !aligned16(grad_y) || (y && !aligned16(y)))
+        return fail(EP_INVALID_ARGUMENT, "grad_out, y and grad_y must be 16-byte aligned");
+    return from_hip(ep::launch_combine_backward(grad_out, y, slot, topk_weights, num_tokens, hidden,
+                                                num_topk, grad_y, grad_topk_weights,
+                                                static_cast<hipStream_t>(stream)),
+                    "ep_combine_backward launch");
+}
+
+int ep_dispatch_backward(const void* grad_recv, const float* grad_recv_weights,
+                         const int32_t* slot, int64_t num_tokens, int hidden, int num_topk,
+                         void* grad_x, float* grad_topk_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 8);
+    if (st) return st;
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!grad_recv || !slot || !grad_x)
+        return fail(EP_INVALID_ARGUMENT, "grad_recv, slot and grad_x are required");
+    if ((grad_topk_weights == nullptr) != (grad_recv_weights == nullptr))
+        return fail(EP_INVALID_ARGUMENT,
+                    "grad_recv_weights and grad_topk_weights are given together or not at all");
+    if (!aligned16(grad_recv) || !aligned16(grad_x))
+        return fail(EP_INVALID_ARGUMENT, "grad_recv and grad_x must be 16-byte aligned");
+    return from_hip(ep::launch_combine(grad_recv, slot, nullptr, num_tokens, hidden, num_topk,
+                                       grad_x, grad_recv_weights, grad_topk_weights,
+                                       static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_backward launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,217 @@
+// ep_backward.hip -- backward of the weighted combine.
+//
+// Passages: DeepEP page, "MoE Dispatch and Combine for Training/Inference
+// with ElasticBuffer" (the backward of combine is a dispatch, the backward of
+// dispatch is a combine that also returns the reduced weight gradients);
+// NeMo fused_a2a page, HybridEPCombine.backward (redispatch the combined-
+// output gradients through the saved layout); NCCL EP page, ncclEpCombine
+// high-throughput branch (backward combine carries tokens and topk weight
+// gradients).
+//
+// With out[t] = sum_j w[t,j] * y[slot[t,j]] and upstream gradient g [T, H]:
+//   grad_y[slot[t,j]] = bf16( w[t,j] * g[t] )       one rounding of the exact
+//                                                   product
+//   grad_w[t,j]       = sum_c g[t,c] * y[slot[t,j], c]   fp32 accumulation
+//
+// Design (HBM-bound): one 128-lane workgroup per token reads g[t] once into
+// registers (VPT 16-byte vectors per lane).  For each slot it streams the
+// expert row y[slot] (when grad_w is wanted), accumulates the per-lane dot
+// product with fp32 FMAs and writes the scaled gradient row with
+// non-temporal 16-byte stores; the per-slot partial dots are reduced across
+// the workgroup at the end (8 slots at a time).  The bf16 rounding of
+// w * g uses the exact product error e = fma(w, g, -p) of p = fl32(w * g):
+// p is on the same side of every bf16 rounding boundary as the exact product
+// unless p is itself a boundary (a bf16 midpoint), where the sign of e
+// decides; this is exact whenever w * g is not an fp32 subnormal.
+
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// bf16 round-to-nearest-even of the exact product w * g.
+__device__ __forceinline__ uint32_t bf16_of_product(float w, float g)
+{
+    const float p = w * g;
+    const float e = __builtin_fmaf(w, g, -p);
+    const uint32_t u = __float_as_uint(p);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
+    if ((u & 0xFFFFu) == 0x8000u && e != 0.0f) {
+        // p is a bf16 midpoint; the exact product lies beyond it (away from
+        // zero) when e has p's sign
+        const bool away = (e > 0.0f) == (p > 0.0f);
+        return (u >> 16) + (away ? 1u : 0u);
+    }
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint4 scale_row8(float w, const uint4& g)
+{
+    uint4 o;
+    o.x = bf16_of_product(w, bf16_lo(g.x)) | (bf16_of_product(w, bf16_hi(g.x)) << 16);
+    o.y = bf16_of_product(w, bf16_lo(g.y)) | (bf16_of_product(w, bf16_hi(g.y)) << 16);
+    o.z = bf16_of_product(w, bf16_lo(g.z)) | (bf16_of_product(w, bf16_hi(g.z)) << 16);
+    o.w = bf16_of_product(w, bf16_lo(g.w)) | (bf16_of_product(w, bf16_hi(g.w)) << 16);
+    return o;
+}
+
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc)
+{
+    acc = __builtin_fmaf(bf16_lo(a.x), bf16_lo(b.x), acc);
+    acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(b.x), acc);
+    acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(b.y), acc);
+    acc = __builtin_fmaf(bf16_hi(a.y), bf16_hi(b.y), acc);
+    acc = __builtin_fmaf(bf16_lo(a.z), bf16_lo(b.z), acc);
+    acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(b.z), acc);
+    acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(b.w), acc);
+    acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(b.w), acc);
+    return acc;
+}
+
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+__device__ __forceinline__ void keep(uint4& v)
+{
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+constexpr int kGroup = 8;   // slots whose partial dots are carried together
+
+// A pass covers NT*VPT vectors of the row; lanes past the row end hold
+// zeros and store nothing.
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT)
+void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restrict__ y,
+                             const int32_t* __restrict__ slot, const float* __restrict__ w,
+                             int nvec, int k, uint4* __restrict__ grad_y,
+                             float* __restrict__ grad_w)
+{
+    __shared__ float red[NT / 64][kGroup];
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int32_t sl = lane < k ? slot[t * k + lane] : -1;
+    const float wl = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
+    const uint4* gr = g + t * nvec;
+    const bool want_dot = grad_w != nullptr;
+    constexpr int kPass = NT * VPT;
+
+    for (int jg = 0; jg < k; jg += kGroup) {
+        const int jn = min(kGroup, k - jg);
+        float acc[kGroup];
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q) acc[q] = 0.0f;
+
+        for (int p0 = 0; p0 < nvec; p0 += kPass) {
+            uint4 gv[VPT];
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) {
+                const int v = p0 + tid + u * NT;
+                gv[u] = v < nvec ? gr[v] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) keep(gv[u]);
+#pragma unroll
+            for (int q = 0; q < kGroup; ++q) {
+                if (q >= jn) break;
+                const int32_t r = __builtin_amdgcn_readlane(sl, jg + q);
+                if (r < 0) continue;
+                const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jg + q));
+                const uint4* yr = y + (int64_t)r * nvec;
+                uint4* dst = grad_y + (int64_t)r * nvec;
+                if (want_dot) {
+                    uint4 yv[VPT];
+#pragma unroll
+                    for (int u = 0; u < VPT; ++u) {
+                        const int v = p0 + tid + u * NT;
+                        yv[u] = v < nvec ? yr[v] : make_uint4(0u, 0u, 0u, 0u);
+                    }
+#pragma unroll
+                    for (int u = 0; u < VPT; ++u) acc[q] = dot8(gv[u], yv[u], acc[q]);
+                }
+#pragma unroll
+                for (int u = 0; u < VPT; ++u) {
+                    const int v = p0 + tid + u * NT;
+                    if (v < nvec) store_nt(dst + v, scale_row8(wj, gv[u]));
+                }
+            }
+        }
+
+        if (want_dot) {
+            // reduce each slot's partial dot over the workgroup
+#pragma unroll
+            for (int q = 0; q < kGroup; ++q) {
+                float v = acc[q];
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+                if (lane == 0) red[wave][q] = v;
+            }
+            __syncthreads();
+            if (tid < jn) {
+                float s = 0.0f;
+#pragma unroll
+                for (int wv = 0; wv < NT / 64; ++wv) s += red[wv][tid];
+                const int j = jg + tid;
+                const int32_t rj = slot[t * k + j];
+                grad_w[t * k + j] = rj >= 0 ? s : 0.0f;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                                   const float* topk_weights, int64_t num_tokens, int hidden,
+                                   int num_topk, void* grad_y, float* grad_topk_weights,
+                                   hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const dim3 grid((unsigned)num_tokens);
+    const uint4* gg = static_cast<const uint4*>(grad_out);
+    const uint4* yy = static_cast<const uint4*>(y);
+    uint4* gy = static_cast<uint4*>(grad_y);
+    // 64 lanes for short rows; else 128 lanes with the largest VPT <= 8
+    // whose pass divides the row (896 = 128*7 at hidden 7168)
+    if (nvec <= 64) {
+        hipLaunchKernelGGL((combine_backward_kernel<64, 1>), grid, dim3(64), 0, stream, gg, yy,
+                           slot, topk_weights, nvec, num_topk, gy, grad_topk_weights);
+        return hipGetLastError();
+    }
+    const int fit = nvec / 128;
+    int vpt = fit < 1 ? 1 : (fit > 8 ? 8 : fit);
+    for (int v = 8; v >= 1; --v) {
+        if (nvec % (128 * v) == 0) {
+            vpt = v;
+            break;
+        }
+    }
+#define EP_CB(V)                                                                             \
+    hipLaunchKernelGGL((combine_backward_kernel<128, V>), grid, dim3(128), 0, stream, gg, yy, \
+                       slot, topk_weights, nvec, num_topk, gy, grad_topk_weights)
+    switch (vpt) {
+    case 1: EP_CB(1); break;
+    case 2: EP_CB(2); break;
+    case 3: EP_CB(3); break;
+    case 4: EP_CB(4); break;
+    case 5: EP_CB(5); break;
+    case 6: EP_CB(6); break;
+    case 7: EP_CB(7); break;
+    default: EP_CB(8); break;
+    }
+#undef EP_CB
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -85,10 +85,15 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, int v)
 // iteration.  K == 0: any k (runtime loop, one vector per iteration).
 // Lane j of every wavefront holds slot[t, j] and w[t, j] (k <= 64); they are
 // read back as wavefront-uniform values with readlane.
+//
+// row_w / out_w (both or neither): the backward of dispatch also gathers the
+// per-row weight gradients back to the pairs, out_w[t, j] = row_w[slot[t, j]]
+// (0 for a masked pair).
 template <int NT, int U, int K>
 __global__ __launch_bounds__(NT)
 void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slot,
-                    const float* __restrict__ w, int nvec, int k, uint4* __restrict__ out)
+                    const float* __restrict__ w, int nvec, int k, uint4* __restrict__ out,
+                    const float* __restrict__ row_w, float* __restrict__ out_w)
 {
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -97,6 +102,7 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
     const int32_t sl = lane < kk ? slot[t * kk + lane] : -1;
     const float wl = lane < kk ? (w ? w[t * kk + lane] : 1.0f) : 0.0f;
     uint4* o = out + t * nvec;
+    if (out_w != nullptr && tid < kk) out_w[t * kk + tid] = sl >= 0 ? row_w[sl] : 0.0f;
 
     if constexpr (K > 0) {
         // A masked slot reads zeros through an empty resource and gets
@@ -142,11 +148,11 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
 
 template <int NT, int U>
 void launch_shape(dim3 grid, hipStream_t stream, const uint4* y, const int32_t* slot,
-                  const float* w, int nvec, int k, uint4* out)
+                  const float* w, int nvec, int k, uint4* out, const float* row_w, float* out_w)
 {
 #define EP_COMBINE_K(KV)                                                                       \
     hipLaunchKernelGGL((combine_kernel<NT, U, KV>), grid, dim3(NT), 0, stream, y, slot, w, nvec, \
-                       k, out)
+                       k, out, row_w, out_w)
     switch (k) {
     case 1: EP_COMBINE_K(1); break;
     case 2: EP_COMBINE_K(2); break;
@@ -165,7 +171,7 @@ void launch_shape(dim3 grid, hipStream_t stream, const uint4* y, const int32_t* 
 
 hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_weights,
                           int64_t num_tokens, int hidden, int num_topk, void* out,
-                          hipStream_t stream)
+                          const float* row_w, float* out_w, hipStream_t stream)
 {
     if (num_tokens == 0) return hipSuccess;
     const int nvec = hidden / 8;
@@ -175,11 +181,11 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
     // 256 lanes x 2 vectors for long rows (hidden >= 4096: 896 vectors at
     // 7168 take two iterations); smaller workgroups for short rows
     if (nvec <= 64)
-        launch_shape<64, 1>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+        launch_shape<64, 1>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo, row_w, out_w);
     else if (nvec < 512)
-        launch_shape<128, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+        launch_shape<128, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo, row_w, out_w);
     else
-        launch_shape<256, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo);
+        launch_shape<256, 2>(grid, stream, yy, slot, topk_weights, nvec, num_topk, oo, row_w, out_w);
     return hipGetLastError();
 }
 

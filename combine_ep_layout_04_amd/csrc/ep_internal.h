@@ -22,9 +22,9 @@ int64_t layout_num_chunks(int64_t pairs);
 size_t layout_workspace_bytes(int64_t pairs, int num_experts);
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
-                         int num_experts, int32_t* counts, int32_t* offsets, int32_t* slot,
-                         int32_t* src, int32_t* num_invalid, void* workspace,
-                         hipStream_t stream);
+                         int num_experts, int alignment, int capacity, int32_t* counts,
+                         int32_t* offsets, int32_t* slot, int32_t* src, int32_t* num_invalid,
+                         int32_t* num_dropped, void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, int num_topk,
                                 const int32_t* slot, const float* topk_weights, void* recv_x,
@@ -34,8 +34,15 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
                                const int32_t* slot, const float* topk_weights, void* recv_q,
                                float* recv_scales, float* recv_weights, hipStream_t stream);
 
+// row_w / out_w: optional gather out_w[t,j] = row_w[slot[t,j]] (dispatch
+// backward); both NULL for a plain combine.
 hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_weights,
                           int64_t num_tokens, int hidden, int num_topk, void* out,
-                          hipStream_t stream);
+                          const float* row_w, float* out_w, hipStream_t stream);
+
+hipError_t launch_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                                   const float* topk_weights, int64_t num_tokens, int hidden,
+                                   int num_topk, void* grad_y, float* grad_topk_weights,
+                                   hipStream_t stream);
 
 }  // namespace ep

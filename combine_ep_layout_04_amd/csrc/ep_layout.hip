@@ -30,6 +30,16 @@
 //               earlier pairs of the same expert is a popcount of the bits
 //               below its own, so no position depends on atomic timing.
 //
+// Segment placement (DeepEP page, "Prefix Sum Interpretation for Expert
+// Token Counts": in expand mode an expert's rows start at
+// align(psum[i-1], expert_alignment); NeMo page, HybridEP pad_multiple; NCCL
+// EP page, ncclEpDispatch low-latency branch: recv_x [experts, capacity,
+// hidden] with per-expert receive counts):
+//   packed       start[e] = sum_{e'<e} align_up(count[e'], alignment)
+//   fixed stride start[e] = e * capacity; pairs whose rank within their
+//                expert reaches the capacity are dropped (slot -1) and
+//                counted, so nothing is ever written past the buffer.
+//
 // The workspace holds hist (E * Cp int32) and one invalid-entry count per
 // chunk.  Folding the scan into the scatter saves a launch: at 64 chunks the
 // redundant per-workgroup reads are 64 KiB from L2 each.
@@ -122,13 +132,16 @@ __device__ __forceinline__ void sum_row(const int32_t* p, int n, int upto, int32
 
 __global__ __launch_bounds__(kLayoutThreads)
 void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64_t chunk, int k,
-                           int E, int cpad, int num_chunks, const int32_t* __restrict__ hist,
-                           const int32_t* __restrict__ bad, int32_t* __restrict__ counts,
-                           int32_t* __restrict__ offsets, int32_t* __restrict__ slot,
-                           int32_t* __restrict__ src, int32_t* __restrict__ num_invalid)
+                           int E, int cpad, int num_chunks, int alignment, int capacity,
+                           const int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
+                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ slot, int32_t* __restrict__ src,
+                           int32_t* __restrict__ num_invalid, int32_t* __restrict__ num_dropped)
 {
     __shared__ int32_t base[kMaxExperts];
     __shared__ int32_t total[kMaxExperts];
+    __shared__ int32_t seg[kMaxExperts];
+    __shared__ int32_t ndrop;
     __shared__ uint32_t bits[kMaxExperts * kWords];
     __shared__ int32_t waves[kLayoutThreads / 64];
     __shared__ int32_t nbad;
@@ -146,30 +159,36 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
     if (tid == 0) nbad = 0;
     __syncthreads();
 
-    // 2. exclusive scan of the totals over experts: thread t owns the
-    // contiguous experts [t*per, t*per + per)
+    // 2. segment starts: packed segments are an exclusive scan of the counts
+    // rounded up to the alignment (thread t owns the contiguous experts
+    // [t*per, t*per + per)); fixed-stride segments start at e * capacity
     const int per = (E + kLayoutThreads - 1) / kLayoutThreads;
     int32_t local = 0;
     for (int q = 0; q < per; ++q) {
         const int e = tid * per + q;
-        if (e < E) local += total[e];
+        if (e < E) local += (total[e] + alignment - 1) / alignment * alignment;
     }
     int32_t n = 0;
     int32_t run = block_exclusive_scan(local, waves, &n);
+    if (tid == 0) ndrop = 0;
+    int32_t drop = 0;
     for (int q = 0; q < per; ++q) {
         const int e = tid * per + q;
         if (e < E) {
             const int32_t tot = total[e];
-            base[e] += run;
+            const int32_t start = capacity > 0 ? e * capacity : run;
+            seg[e] = start;
+            base[e] += start;
             if (c == 0) {
-                counts[e] = tot;
-                offsets[e] = run;
+                counts[e] = capacity > 0 ? min(tot, capacity) : tot;
+                offsets[e] = start;
             }
-            run += tot;
+            if (capacity > 0 && tot > capacity) drop += tot - capacity;
+            run += (tot + alignment - 1) / alignment * alignment;
         }
     }
     if (c == 0) {
-        if (tid == 0) offsets[E] = n;
+        if (tid == 0) offsets[E] = capacity > 0 ? E * capacity : n;
         if (num_invalid) {
             int32_t b = 0;
             for (int cc = tid; cc < num_chunks; cc += kLayoutThreads) b += bad[cc];
@@ -177,7 +196,12 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
         }
     }
     __syncthreads();
-    if (c == 0 && num_invalid && tid == 0) *num_invalid = nbad;
+    if (c == 0 && num_dropped && drop) atomicAdd(&ndrop, drop);
+    __syncthreads();
+    if (c == 0 && tid == 0) {
+        if (num_invalid) *num_invalid = nbad;
+        if (num_dropped) *num_dropped = ndrop;
+    }
 
     const int64_t begin = c * chunk;
     const int64_t end = min(begin + chunk, pairs);
@@ -204,8 +228,12 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
                 rank += (q < word) ? pc : (q == word ? __popc(m & (bit - 1u)) : 0);
             }
             const int32_t r = base[e] + rank;
-            slot[i] = r;
-            if (src) src[r] = (int32_t)i / k;
+            if (capacity > 0 && r - seg[e] >= capacity) {
+                slot[i] = -1;                       // past the expert's capacity
+            } else {
+                slot[i] = r;
+                if (src) src[r] = (int32_t)i / k;
+            }
         } else if (live) {
             slot[i] = -1;
         }
@@ -248,9 +276,9 @@ size_t layout_workspace_bytes(int64_t pairs, int num_experts)
 }
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
-                         int num_experts, int32_t* counts, int32_t* offsets, int32_t* slot,
-                         int32_t* src, int32_t* num_invalid, void* workspace,
-                         hipStream_t stream)
+                         int num_experts, int alignment, int capacity, int32_t* counts,
+                         int32_t* offsets, int32_t* slot, int32_t* src, int32_t* num_invalid,
+                         int32_t* num_dropped, void* workspace, hipStream_t stream)
 {
     const int64_t pairs = num_tokens * (int64_t)num_topk;
     const int64_t chunk = layout_chunk_pairs(pairs);
@@ -266,8 +294,8 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_to
     if (err != hipSuccess) return err;
 
     hipLaunchKernelGGL(layout_scatter_kernel, dim3((unsigned)C), dim3(kLayoutThreads), 0, stream,
-                       topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C, hist, bad, counts,
-                       offsets, slot, src, num_invalid);
+                       topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C, alignment,
+                       capacity, hist, bad, counts, offsets, slot, src, num_invalid, num_dropped);
     return hipGetLastError();
 }
 

@@ -34,10 +34,12 @@ EP_OUT_FP8_E4M3 = 1
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 EP_MAX_HIDDEN = 65536
+EP_MAX_ALIGNMENT = 4096
 
 # every symbol include/ep.h declares
 SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspace_size",
-           "ep_layout", "ep_dispatch", "ep_combine")
+           "ep_layout", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_combine",
+           "ep_combine_backward", "ep_dispatch_backward")
 
 
 class EpError(RuntimeError):
@@ -68,10 +70,18 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_workspace_size.restype = sz
         L.ep_layout.argtypes = [P, i64, i32, i32, P, P, P, P, P, P, sz, P]
         L.ep_layout.restype = i32
+        L.ep_layout_ex.argtypes = [P, i64, i32, i32, i32, i64, P, P, P, P, P, P, P, sz, P]
+        L.ep_layout_ex.restype = i32
+        L.ep_layout_max_rows.argtypes = [i64, i32, i32, i32, i64]
+        L.ep_layout_max_rows.restype = i64
         L.ep_dispatch.argtypes = [P, i64, i32, i32, P, P, i32, P, P, P, P]
         L.ep_dispatch.restype = i32
         L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
         L.ep_combine.restype = i32
+        L.ep_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, P, P, P]
+        L.ep_combine_backward.restype = i32
+        L.ep_dispatch_backward.argtypes = [P, P, P, i64, i32, i32, P, P, P]
+        L.ep_dispatch_backward.restype = i32
         _lib = L
     return _lib
 
@@ -90,6 +100,14 @@ def version() -> int:
 
 def layout_workspace_size(num_tokens: int, num_topk: int, num_experts: int) -> int:
     return int(lib().ep_layout_workspace_size(int(num_tokens), int(num_topk), int(num_experts)))
+
+
+def layout_max_rows(num_tokens: int, num_topk: int, num_experts: int, alignment: int = 1,
+                    capacity: int = 0) -> int:
+    """Rows a receive buffer needs for any routing of this shape (-1 if the
+    arguments are invalid)."""
+    return int(lib().ep_layout_max_rows(int(num_tokens), int(num_topk), int(num_experts),
+                                        int(alignment), int(capacity)))
 
 
 def _check(status: int, where: str) -> None:
@@ -124,26 +142,36 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, numel: Optional[int] =
 
 # ------------------------------------------------------------------ layout --
 
-def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, counts=None, offsets=None, slot=None,
-              src=None, num_invalid=None, workspace=None, want_src: bool = True,
+def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, alignment: int = 1, capacity: int = 0,
+              counts=None, offsets=None, slot=None, src=None, num_invalid=None,
+              num_dropped=None, workspace=None, want_src: bool = True,
               want_invalid: bool = True, stream=None):
     """Routing layout of ``topk_idx`` (int64 [T, k], -1 = masked).
 
+    ``alignment`` / ``capacity`` select ep_layout_ex's segment placement
+    (packed segments starting on multiples of ``alignment``, or a fixed
+    ``capacity`` rows per expert with overflow dropped).
+
     Returns (counts int32 [E], offsets int32 [E+1], slot int32 [T, k],
-    src int32 [T*k] or None, num_invalid int32 [1] or None).
+    src int32 [rows] or None, num_invalid int32 [1] or None); with a
+    capacity, ``num_dropped`` (int32 [1]) is filled when given.  ``rows`` is
+    layout_max_rows(...).
     """
     _need(topk_idx, "topk_idx", torch.int64)
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be 2-D [num_tokens, num_topk]")
     T, k = topk_idx.shape
     E = int(num_experts)
+    rows = layout_max_rows(T, k, E, alignment, capacity)
+    if rows < 0:
+        raise ValueError("invalid layout shape, alignment or capacity")
     dev = topk_idx.device
     i32 = dict(dtype=torch.int32, device=dev)
     counts = torch.empty(E, **i32) if counts is None else counts
     offsets = torch.empty(E + 1, **i32) if offsets is None else offsets
     slot = torch.empty((T, k), **i32) if slot is None else slot
     if want_src and src is None:
-        src = torch.empty(T * k, **i32)
+        src = torch.empty(max(rows, 1), **i32)
     if want_invalid and num_invalid is None:
         num_invalid = torch.empty(1, **i32)
     need = layout_workspace_size(T, k, E)
@@ -153,13 +181,21 @@ def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, counts=None, offsets=
     _need(offsets, "offsets", torch.int32, E + 1)
     _need(slot, "slot", torch.int32, T * k)
     if src is not None:
-        _need(src, "src", torch.int32, T * k)
+        _need(src, "src", torch.int32, rows)
     if num_invalid is not None:
         _need(num_invalid, "num_invalid", torch.int32, 1)
+    if num_dropped is not None:
+        _need(num_dropped, "num_dropped", torch.int32, 1)
     _need(workspace, "workspace", torch.uint8)
-    st = lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot),
-                         _ptr(src), _ptr(num_invalid), _ptr(workspace), workspace.numel(),
-                         _stream(stream))
+    if alignment == 1 and capacity == 0 and num_dropped is None:
+        st = lib().ep_layout(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot),
+                             _ptr(src), _ptr(num_invalid), _ptr(workspace), workspace.numel(),
+                             _stream(stream))
+    else:
+        st = lib().ep_layout_ex(_ptr(topk_idx), T, k, E, int(alignment), int(capacity),
+                                _ptr(counts), _ptr(offsets), _ptr(slot), _ptr(src),
+                                _ptr(num_invalid), _ptr(num_dropped), _ptr(workspace),
+                                workspace.numel(), _stream(stream))
     _check(st, "ep_layout")
     return counts, offsets, slot, src, num_invalid
 
@@ -168,13 +204,15 @@ def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, counts=None, offsets=
 
 def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
                 *, fp8: bool = False, recv_x=None, recv_scales=None, recv_weights=None,
-                want_weights: bool = False, trust_slots: bool = False, stream=None):
+                want_weights: bool = False, rows: Optional[int] = None,
+                trust_slots: bool = False, stream=None):
     """Permute (bf16) or cast (fp8 e4m3 + per-128 fp32 scales) the rows of
     ``x`` (bf16 [T, H]) into the expert-grouped buffer named by ``slot``.
 
     Returns (recv_x, recv_scales or None, recv_weights or None); recv_x is
-    bf16 [T*k, H] or uint8 [T*k, H].  Output buffers given by the caller
-    must hold T*k rows (the worst case), unless ``trust_slots`` says the
+    bf16 [rows, H] or uint8 [rows, H].  ``rows`` is the layout's row bound
+    (layout_max_rows; T*k for the compact layout) and output buffers given
+    by the caller must hold that many, unless ``trust_slots`` says the
     caller knows every slot is below the rows it passed.
     """
     _need(x, "x", torch.bfloat16)
@@ -185,7 +223,7 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
     if slot.dim() != 2 or slot.shape[0] != T:
         raise ValueError("slot must be 2-D [num_tokens, num_topk]")
     k = slot.shape[1]
-    R = T * k
+    R = T * k if rows is None else int(rows)
     dev = x.device
     if recv_x is None:
         recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
@@ -213,18 +251,21 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
 # ----------------------------------------------------------------- combine --
 
 def ep_combine(y: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor],
-               *, out=None, trust_slots: bool = False, stream=None) -> torch.Tensor:
+               *, out=None, rows: Optional[int] = None, trust_slots: bool = False,
+               stream=None) -> torch.Tensor:
     """out[t] = bf16(sum_j w[t,j] * y[slot[t,j]]) for y bf16 [rows, H] and
     slot int32 [T, k]; ``topk_weights`` None means unit weights.  y must
-    hold T*k rows unless ``trust_slots`` says every slot is below its rows."""
+    hold ``rows`` rows (the layout's bound, T*k by default) unless
+    ``trust_slots`` says every slot is below its rows."""
     _need(y, "y", torch.bfloat16)
     _need(slot, "slot", torch.int32)
     if slot.dim() != 2 or y.dim() != 2:
         raise ValueError("slot must be [num_tokens, num_topk] and y [rows, hidden]")
     T, k = slot.shape
     H = y.shape[-1]
-    if not trust_slots and y.shape[0] < T * k:
-        raise ValueError(f"y has {y.shape[0]} rows, needs num_tokens * num_topk = {T * k}")
+    R = T * k if rows is None else int(rows)
+    if not trust_slots and y.shape[0] < R:
+        raise ValueError(f"y has {y.shape[0]} rows, the layout may use {R}")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _need(out, "out", torch.bfloat16, T * H)
@@ -234,3 +275,63 @@ def ep_combine(y: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch
                           _stream(stream))
     _check(st, "ep_combine")
     return out
+
+
+# ---------------------------------------------------------------- backward --
+
+def ep_combine_backward(grad_out: torch.Tensor, y: Optional[torch.Tensor], slot: torch.Tensor,
+                        topk_weights: Optional[torch.Tensor], *, grad_y=None,
+                        grad_topk_weights=None, want_weight_grad: bool = True,
+                        rows: Optional[int] = None, stream=None):
+    """Gradients of ep_combine: returns (grad_y bf16 [rows, H],
+    grad_topk_weights fp32 [T, k] or None).  The weight gradient needs y."""
+    _need(grad_out, "grad_out", torch.bfloat16)
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or grad_out.dim() != 2 or slot.shape[0] != grad_out.shape[0]:
+        raise ValueError("grad_out must be [T, H] and slot [T, k]")
+    T, H = grad_out.shape
+    k = slot.shape[1]
+    R = T * k if rows is None else int(rows)
+    if grad_y is None:
+        grad_y = torch.empty((R, H), dtype=torch.bfloat16, device=grad_out.device)
+    _need(grad_y, "grad_y", torch.bfloat16, R * H)
+    if y is not None:
+        _need(y, "y", torch.bfloat16, R * H)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    if want_weight_grad and y is not None and grad_topk_weights is None:
+        grad_topk_weights = torch.empty((T, k), dtype=torch.float32, device=grad_out.device)
+    if grad_topk_weights is not None:
+        _need(grad_topk_weights, "grad_topk_weights", torch.float32, T * k)
+    st = lib().ep_combine_backward(_ptr(grad_out), _ptr(y), _ptr(slot), _ptr(topk_weights), T, H, k,
+                                   _ptr(grad_y), _ptr(grad_topk_weights), _stream(stream))
+    _check(st, "ep_combine_backward")
+    return grad_y, grad_topk_weights
+
+
+def ep_dispatch_backward(grad_recv: torch.Tensor, grad_recv_weights: Optional[torch.Tensor],
+                         slot: torch.Tensor, *, grad_x=None, grad_topk_weights=None,
+                         rows: Optional[int] = None, stream=None):
+    """Gradients of ep_dispatch: returns (grad_x bf16 [T, H],
+    grad_topk_weights fp32 [T, k] or None)."""
+    _need(grad_recv, "grad_recv", torch.bfloat16)
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or grad_recv.dim() != 2:
+        raise ValueError("slot must be [T, k] and grad_recv [rows, H]")
+    T, k = slot.shape
+    H = grad_recv.shape[1]
+    R = T * k if rows is None else int(rows)
+    if grad_recv.shape[0] < R:
+        raise ValueError(f"grad_recv has {grad_recv.shape[0]} rows, the layout may use {R}")
+    if grad_x is None:
+        grad_x = torch.empty((T, H), dtype=torch.bfloat16, device=grad_recv.device)
+    _need(grad_x, "grad_x", torch.bfloat16, T * H)
+    if grad_recv_weights is not None:
+        _need(grad_recv_weights, "grad_recv_weights", torch.float32, R)
+        if grad_topk_weights is None:
+            grad_topk_weights = torch.empty((T, k), dtype=torch.float32, device=grad_recv.device)
+        _need(grad_topk_weights, "grad_topk_weights", torch.float32, T * k)
+    st = lib().ep_dispatch_backward(_ptr(grad_recv), _ptr(grad_recv_weights), _ptr(slot), T, H, k,
+                                    _ptr(grad_x), _ptr(grad_topk_weights), _stream(stream))
+    _check(st, "ep_dispatch_backward")
+    return grad_x, grad_topk_weights

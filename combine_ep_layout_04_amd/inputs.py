@@ -46,6 +46,7 @@ __all__ = [
     "expert_ids_of_rows",
     "expert_outputs_scaled",
     "expert_outputs_dequant",
+    "make_gradient",
 ]
 
 
@@ -216,3 +217,9 @@ def expert_outputs_dequant(q: np.ndarray, scales: np.ndarray, n: int) -> np.ndar
     prod = (qt.view(n, nb, 128) * st.view(n, nb, 1)).view(n, H)
     y[:n] = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     return y
+
+
+def make_gradient(rows: int, H: int, seed: int = 1) -> np.ndarray:
+    """A seeded upstream gradient: N(0,1) float32 [rows, H] rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits_from_float32(rng.standard_normal((rows, H), dtype=np.float32))

@@ -73,9 +73,12 @@ def _counter_means(d: str):
     return {k: statistics.fmean(v) for k, v in vals.items()}
 
 
-# library kernels by the key bench.py reports them under
+# library kernels by the key bench.py reports them under (the combine line
+# also averages the dispatch-backward launches, which run the same kernel
+# over the same bytes plus a [T, k] gather)
 KERNEL_KEYS = {"dispatch_bf16": "dispatch_bf16_kernel", "dispatch_fp8": "dispatch_fp8_kernel",
-               "combine": "combine_kernel", "layout_count": "layout_count_kernel",
+               "combine": "combine_kernel", "combine_backward": "combine_backward_kernel",
+               "layout_count": "layout_count_kernel",
                "layout_scatter": "layout_scatter_kernel"}
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
 

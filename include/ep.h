@@ -72,6 +72,7 @@ typedef enum {
 #define EP_MAX_EXPERTS 1024
 #define EP_MAX_TOPK 64
 #define EP_MAX_HIDDEN 65536
+#define EP_MAX_ALIGNMENT 4096
 
 /* Library version, (major << 16) | minor. */
 int ep_version(void);
@@ -110,6 +111,7 @@ size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_expert
  *                   deterministic.
  *      src          int32 [num_tokens * num_topk] or NULL: src[r] = source
  *                   token of row r for r < N; entries >= N are not written.
+ *                   (With ep_layout_ex, src needs ep_layout_max_rows rows.)
  *      num_invalid  int32 [1] or NULL: number of invalid entries.
  * Scratch: workspace of at least ep_layout_workspace_size(...) bytes,
  *      256-byte aligned; contents need not be initialised and are
@@ -121,6 +123,48 @@ size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_expert
 int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
               int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
               int32_t *num_invalid, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ep_layout_ex -- ep_layout with the segment placements the pages' expanded
+ * layouts offer.  ep_layout is ep_layout_ex(alignment 1, capacity 0).
+ *
+ * Passages: DeepEP page, dispatch() expert_alignment and "Prefix Sum
+ * Interpretation for Expert Token Counts" (in expand mode expert i's rows
+ * start at align(psum[i-1], expert_alignment) and end at psum[i]); NeMo
+ * fused_a2a page, HybridEPDispatch pad_multiple; NCCL EP page,
+ * ncclEpDispatch low-latency branch (recv_x [num_local_experts, capacity,
+ * hidden] with a per-expert receive count).
+ *
+ *   alignment        1..EP_MAX_ALIGNMENT.  With expert_capacity == 0 the
+ *                    segments are packed: expert e starts at
+ *                    offsets[e] = sum_{e'<e} round_up(counts[e'], alignment),
+ *                    and offsets[E] is the padded total; DeepEP's
+ *                    psum[e] = offsets[e] + counts[e].
+ *   expert_capacity  0, or a positive multiple of alignment: fixed stride,
+ *                    expert e owns rows [e*cap, (e+1)*cap), offsets[e] =
+ *                    e*cap, offsets[E] = E*cap.  Pairs whose rank within
+ *                    their expert (in flat order) reaches cap are dropped:
+ *                    slot -1, counted in *num_dropped; counts[e] is the
+ *                    number of rows placed, at most cap.
+ *   num_dropped      int32 [1] or NULL.
+ * Padding rows are never written by ep_layout (src) or by ep_dispatch.
+ * A receive buffer of ep_layout_max_rows(...) rows is always enough.
+ * Other arguments, errors and requirements as ep_layout; additionally the
+ * layout's row count bound must be below 2^31 (else EP_UNSUPPORTED).
+ */
+int ep_layout_ex(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                 int alignment, int64_t expert_capacity, int32_t *counts, int32_t *offsets,
+                 int32_t *slot, int32_t *src, int32_t *num_invalid, int32_t *num_dropped,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Rows a receive buffer needs for any routing of this shape and placement:
+ * E * expert_capacity with a capacity, else T*k + min(E, T*k)*(alignment-1)
+ * (each expert holding a pair pads by less than one alignment).  Pure host
+ * arithmetic; -1 for invalid arguments.
+ */
+int64_t ep_layout_max_rows(int64_t num_tokens, int num_topk, int num_experts, int alignment,
+                           int64_t expert_capacity);
 
 /*
  * ep_dispatch -- permute (and optionally cast) token rows into the
@@ -178,6 +222,55 @@ int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
  */
 int ep_combine(const void *y, const int32_t *slot, const float *topk_weights,
                int64_t num_tokens, int hidden, int num_topk, void *out, void *stream);
+
+/*
+ * ep_combine_backward -- gradients of ep_combine.
+ *
+ * Passages: DeepEP page, "MoE Dispatch and Combine for Training/Inference
+ * with ElasticBuffer" (the backward of combine is a dispatch); NeMo
+ * fused_a2a page, HybridEPCombine.backward (redispatch the combined-output
+ * gradients through the saved layout); NCCL EP page, ncclEpCombine
+ * high-throughput branch (backward combine with topk weight gradients).
+ *
+ * With out[t] = sum_j w[t,j] * y[slot[t,j]] and grad_out g:
+ * In:  grad_out          bf16 [num_tokens, hidden].
+ *      y                 bf16 [rows, hidden], the forward's expert outputs;
+ *                        may be NULL when grad_topk_weights is NULL.
+ *      slot              int32 [num_tokens * num_topk] from ep_layout.
+ *      topk_weights      fp32 [num_tokens * num_topk] or NULL (all ones).
+ * Out: grad_y            bf16 [rows, hidden]: grad_y[slot[t,j]] =
+ *                        bf16_rne(w[t,j] * g[t]), one rounding of the exact
+ *                        product (exact for products that are not fp32
+ *                        subnormals); rows nothing maps to are not written.
+ *      grad_topk_weights fp32 [num_tokens * num_topk] or NULL:
+ *                        sum_c g[t,c] * y[slot[t,j],c] accumulated in fp32
+ *                        (in an unspecified order), 0 for a masked pair.
+ */
+int ep_combine_backward(const void *grad_out, const void *y, const int32_t *slot,
+                        const float *topk_weights, int64_t num_tokens, int hidden, int num_topk,
+                        void *grad_y, float *grad_topk_weights, void *stream);
+
+/*
+ * ep_dispatch_backward -- gradients of ep_dispatch.
+ *
+ * Passages: DeepEP page, "MoE Dispatch and Combine for Training/Inference
+ * with ElasticBuffer" (the backward of dispatch is a combine that also
+ * reduces the weight gradients); NeMo fused_a2a page,
+ * HybridEPDispatch.backward.
+ *
+ * In:  grad_recv          bf16 [rows, hidden]: gradient of recv_x.
+ *      grad_recv_weights  fp32 [rows] or NULL: gradient of recv_weights.
+ *      slot               int32 [num_tokens * num_topk] from ep_layout.
+ * Out: grad_x             bf16 [num_tokens, hidden]: bf16_rne of the fp32 sum
+ *                         over unmasked j (ascending) of grad_recv[slot[t,j]]
+ *                         -- ep_combine with unit weights.
+ *      grad_topk_weights  fp32 [num_tokens * num_topk] or NULL (exactly when
+ *                         grad_recv_weights is NULL): grad_recv_weights[slot],
+ *                         0 for a masked pair.
+ */
+int ep_dispatch_backward(const void *grad_recv, const float *grad_recv_weights,
+                         const int32_t *slot, int64_t num_tokens, int hidden, int num_topk,
+                         void *grad_x, float *grad_topk_weights, void *stream);
 
 #ifdef __cplusplus
 }

@@ -63,12 +63,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
         L.oracle_layout.argtypes = [P, i64, i32, i32, P, P, P, P, P]
         L.oracle_layout.restype = None
+        L.oracle_layout_ex.argtypes = [P, i64, i32, i32, i32, i64, P, P, P, P, P, P]
+        L.oracle_layout_ex.restype = None
         L.oracle_dispatch_bf16.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.oracle_dispatch_bf16.restype = None
         L.oracle_dispatch_fp8.argtypes = [P, i64, i32, i32, P, P, P, P, P]
         L.oracle_dispatch_fp8.restype = None
         L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
         L.oracle_combine.restype = None
+        L.oracle_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, P, P]
+        L.oracle_combine_backward.restype = None
+        L.oracle_dispatch_backward.argtypes = [P, P, P, i64, i32, i32, P, P]
+        L.oracle_dispatch_backward.restype = None
         _lib = L
     return _lib
 
@@ -103,31 +109,47 @@ def e4m3_encode(v: float) -> int:
 
 class Layout:
     """Result of :func:`layout`: counts [E], offsets [E+1], slot [T,k],
-    src [T*k] (rows >= N hold -1) and the invalid-index count."""
+    src [rows] (rows nothing maps to hold -1), and the invalid-index and
+    dropped-pair counts."""
 
-    def __init__(self, counts, offsets, slot, src, num_invalid):
+    def __init__(self, counts, offsets, slot, src, num_invalid, num_dropped=0):
         self.counts = counts
         self.offsets = offsets
         self.slot = slot
         self.src = src
         self.num_invalid = num_invalid
+        self.num_dropped = num_dropped
 
     @property
     def n(self) -> int:
+        """Rows of the layout (padding included): offsets[E]."""
         return int(self.offsets[-1])
 
 
-def layout(topk_idx: np.ndarray, num_experts: int) -> Layout:
+def max_rows(T: int, k: int, E: int, alignment: int = 1, capacity: int = 0) -> int:
+    """Rows a receive buffer needs for any routing of this shape."""
+    if capacity > 0:
+        return E * capacity
+    return T * k + min(E, T * k) * (alignment - 1)
+
+
+def layout(topk_idx: np.ndarray, num_experts: int, alignment: int = 1, capacity: int = 0) -> Layout:
     idx = _c(topk_idx, np.int64)
     T, k = idx.shape
     E = int(num_experts)
     counts = np.zeros(E, np.int32)
     offsets = np.zeros(E + 1, np.int32)
     slot = np.zeros((T, k), np.int32)
-    src = np.full(T * k, -1, np.int32)
+    src = np.full(max(max_rows(T, k, E, alignment, capacity), T * k), -1, np.int32)
     bad = np.zeros(1, np.int32)
-    lib().oracle_layout(_ptr(idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot), _ptr(src), _ptr(bad))
-    return Layout(counts, offsets, slot, src, int(bad[0]))
+    dropped = np.zeros(1, np.int32)
+    if alignment == 1 and capacity == 0:
+        lib().oracle_layout(_ptr(idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot), _ptr(src),
+                            _ptr(bad))
+    else:
+        lib().oracle_layout_ex(_ptr(idx), T, k, E, int(alignment), int(capacity), _ptr(counts),
+                               _ptr(offsets), _ptr(slot), _ptr(src), _ptr(bad), _ptr(dropped))
+    return Layout(counts, offsets, slot, src, int(bad[0]), int(dropped[0]))
 
 
 # ---------------------------------------------------------------- dispatch --
@@ -141,6 +163,8 @@ def dispatch_bf16(x_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[n
     T, H = x.shape
     k = s.shape[1]
     R = T * k if rows is None else int(rows)
+    if s.size and s.max() >= R:
+        raise ValueError("a slot is beyond the receive buffer")
     recv = np.zeros((R, H), np.uint16)
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     rw = None if w is None else np.zeros(R, np.float32)
@@ -159,6 +183,8 @@ def dispatch_fp8(x_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[np
         raise ValueError("fp8 dispatch needs hidden % 128 == 0")
     k = s.shape[1]
     R = T * k if rows is None else int(rows)
+    if s.size and s.max() >= R:
+        raise ValueError("a slot is beyond the receive buffer")
     q = np.zeros((R, H), np.uint8)
     sc = np.zeros((R, H // 128), np.float32)
     w = None if topk_weights is None else _c(topk_weights, np.float32)
@@ -175,7 +201,46 @@ def combine(y_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[np.ndar
     s = _c(slot, np.int32)
     T, k = s.shape
     H = y.shape[1]
+    if s.size and s.max() >= y.shape[0]:
+        raise ValueError("a slot is beyond the expert outputs")
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     out = np.zeros((T, H), np.uint16)
     lib().oracle_combine(_ptr(y), _ptr(s), _ptr(w), T, H, k, _ptr(out))
     return out
+
+
+# ---------------------------------------------------------------- backward --
+
+def combine_backward(g_bits: np.ndarray, y_bits: Optional[np.ndarray], slot: np.ndarray,
+                     topk_weights: Optional[np.ndarray], rows: Optional[int] = None):
+    """Return (grad_y uint16 [rows, H], grad_w float32 [T, k] or None).
+    grad_w is computed when y is given.  Rows nothing maps to stay 0."""
+    g = _c(g_bits, np.uint16)
+    s = _c(slot, np.int32)
+    T, H = g.shape
+    k = s.shape[1]
+    R = T * k if rows is None else int(rows)
+    if s.size and s.max() >= R:
+        raise ValueError("a slot is beyond the expert outputs")
+    y = None if y_bits is None else _c(y_bits, np.uint16)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    gy = np.zeros((R, H), np.uint16)
+    gw = None if y is None else np.zeros((T, k), np.float32)
+    lib().oracle_combine_backward(_ptr(g), _ptr(y), _ptr(s), _ptr(w), T, H, k, _ptr(gy), _ptr(gw))
+    return gy, gw
+
+
+def dispatch_backward(grad_recv_bits: np.ndarray, grad_recv_w: Optional[np.ndarray],
+                      slot: np.ndarray, T: int):
+    """Return (grad_x uint16 [T, H], grad_w float32 [T, k] or None)."""
+    gr = _c(grad_recv_bits, np.uint16)
+    s = _c(slot, np.int32)
+    k = s.shape[1]
+    H = gr.shape[1]
+    if s.size and s.max() >= gr.shape[0]:
+        raise ValueError("a slot is beyond the row gradients")
+    grw = None if grad_recv_w is None else _c(grad_recv_w, np.float32)
+    gx = np.zeros((T, H), np.uint16)
+    gw = None if grw is None else np.zeros((T, k), np.float32)
+    lib().oracle_dispatch_backward(_ptr(gr), _ptr(grw), _ptr(s), T, H, k, _ptr(gx), _ptr(gw))
+    return gx, gw

@@ -121,31 +121,45 @@ def bf16_round(q: Fraction, negative_zero: bool = False) -> int:
 
 # ------------------------------------------------------------------ layout --
 
-def layout(topk_idx: np.ndarray, E: int):
+def layout(topk_idx: np.ndarray, E: int, alignment: int = 1, capacity: int = 0):
     """Expanded, expert-grouped, stable layout straight from its definition:
-    slot(i) = start(e) + #{i' < i : key(i') == e}, start(e) = sum of the
-    counts of experts below e.  Returns (counts, offsets, slot, src, invalid)."""
+    slot(i) = start(e) + #{i' < i : key(i') == e}.  Packed: start(e) is the
+    sum over experts below e of their counts rounded up to `alignment`.
+    Fixed stride: start(e) = e * capacity and a pair whose rank reaches the
+    capacity is dropped.  Returns (counts, offsets, slot, src, invalid,
+    dropped)."""
     idx = [int(v) for v in np.asarray(topk_idx).reshape(-1)]
     T, k = np.asarray(topk_idx).shape
     valid = [0 <= e < E for e in idx]
-    counts = [sum(1 for e, ok in zip(idx, valid) if ok and e == x) for x in range(E)]
-    offsets = [0]
-    for x in range(E):
-        offsets.append(offsets[-1] + counts[x])
-    slot = []
+    raw = [sum(1 for e, ok in zip(idx, valid) if ok and e == x) for x in range(E)]
+    if capacity > 0:
+        starts = [x * capacity for x in range(E)]
+        counts = [min(c, capacity) for c in raw]
+        total = E * capacity
+    else:
+        starts, total = [], 0
+        for x in range(E):
+            starts.append(total)
+            total += -(-raw[x] // alignment) * alignment
+        counts = raw
+    slot, dropped = [], 0
     for i, (e, ok) in enumerate(zip(idx, valid)):
         if not ok:
             slot.append(-1)
             continue
         earlier = sum(1 for i2 in range(i) if valid[i2] and idx[i2] == e)
-        slot.append(offsets[e] + earlier)
-    src = [-1] * (T * k)
+        if capacity > 0 and earlier >= capacity:
+            slot.append(-1)
+            dropped += 1
+            continue
+        slot.append(starts[e] + earlier)
+    src = [-1] * max(total, T * k)
     for i, r in enumerate(slot):
         if r >= 0:
             src[r] = i // k
     invalid = sum(1 for e in idx if not (e == -1 or 0 <= e < E))
-    return (np.array(counts, np.int32), np.array(offsets, np.int32),
-            np.array(slot, np.int32).reshape(T, k), np.array(src, np.int32), invalid)
+    return (np.array(counts, np.int32), np.array(starts + [total], np.int32),
+            np.array(slot, np.int32).reshape(T, k), np.array(src, np.int32), invalid, dropped)
 
 
 # ---------------------------------------------------------------- dispatch --

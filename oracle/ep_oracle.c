@@ -135,42 +135,74 @@ uint8_t oracle_e4m3_encode(float v)
 
 /* ------------------------------------------------------------- layout -- */
 
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
 /*
- * Stable counting sort of the pairs i = t*k + j by expert e = topk_idx[i].
+ * Stable counting sort of the pairs i = t*k + j by expert e = topk_idx[i],
+ * with the segment placement options of the pages' expanded layouts:
+ *
+ *  - packed (expert_capacity == 0): expert e's rows start at
+ *      start[e] = sum_{e' < e} align_up(count[e'], alignment),
+ *    i.e. every segment starts on a multiple of `alignment` (DeepEP page,
+ *    "Prefix Sum Interpretation for Expert Token Counts": in expand mode
+ *    start = align(psum[i-1], expert_alignment), end = psum[i]; NeMo page,
+ *    HybridEP pad_multiple).  alignment == 1 is the compact layout.
+ *  - fixed stride (expert_capacity > 0): expert e owns rows
+ *    [e * cap, (e + 1) * cap) (NCCL EP page, ncclEpDispatch low-latency
+ *    branch: recv_x [num_local_experts, capacity, hidden] with a per-expert
+ *    recv_count).  Pairs past an expert's capacity, in flat order, are
+ *    dropped: slot -1, counted in *num_dropped.
+ *
  * e == -1 is a masked slot; any e outside [-1, E) is counted in
  * *num_invalid and also treated as masked.  Outputs:
- *   counts[e]      number of unmasked pairs routed to e
- *   offsets[e]     exclusive prefix sum of counts, offsets[E] = N
- *   slot[i]        destination row of pair i in [0, N), or -1 if masked;
+ *   counts[e]      rows of expert e that were placed
+ *   offsets[e]     first row of expert e; offsets[E] = total rows of the
+ *                  layout (padding included)
+ *   slot[i]        destination row of pair i, or -1 (masked / dropped);
  *                  pairs of one expert keep their flat order
- *   src[r]         source token of destination row r < N (may be NULL)
+ *   src[r]         source token of every placed row r (may be NULL); rows
+ *                  nothing maps to are not written
  */
-void oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E,
-                   int32_t *counts, int32_t *offsets, int32_t *slot,
-                   int32_t *src, int32_t *num_invalid)
+void oracle_layout_ex(const int64_t *topk_idx, int64_t T, int k, int E, int alignment,
+                      int64_t expert_capacity, int32_t *counts, int32_t *offsets,
+                      int32_t *slot, int32_t *src, int32_t *num_invalid, int32_t *num_dropped)
 {
     int64_t P = T * (int64_t)k;
-    int32_t bad = 0;
-    for (int e = 0; e < E; ++e)
-        counts[e] = 0;
+    int32_t bad = 0, dropped = 0;
+    int64_t *raw = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    int64_t *start = (int64_t *)malloc((size_t)E * sizeof(int64_t));
+    int64_t *cursor = (int64_t *)calloc((size_t)E, sizeof(int64_t));
     for (int64_t i = 0; i < P; ++i) {
         int64_t e = topk_idx[i];
         if (e >= 0 && e < E)
-            counts[e] += 1;
+            raw[e] += 1;
         else if (e != -1)
             bad += 1;
     }
-    offsets[0] = 0;
-    for (int e = 0; e < E; ++e)
-        offsets[e + 1] = offsets[e] + counts[e];
+    int64_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+        if (expert_capacity > 0) {
+            start[e] = (int64_t)e * expert_capacity;
+            counts[e] = (int32_t)(raw[e] < expert_capacity ? raw[e] : expert_capacity);
+        } else {
+            start[e] = acc;
+            acc += align_up(raw[e], alignment);
+            counts[e] = (int32_t)raw[e];
+        }
+        offsets[e] = (int32_t)start[e];
+    }
+    offsets[E] = (int32_t)(expert_capacity > 0 ? (int64_t)E * expert_capacity : acc);
     /* second pass: hand out rows in increasing flat order per expert */
-    int32_t *cursor = (int32_t *)malloc((size_t)E * sizeof(int32_t));
-    for (int e = 0; e < E; ++e)
-        cursor[e] = offsets[e];
     for (int64_t i = 0; i < P; ++i) {
         int64_t e = topk_idx[i];
         if (e >= 0 && e < E) {
-            int32_t r = cursor[e]++;
+            int64_t local = cursor[e]++;
+            if (expert_capacity > 0 && local >= expert_capacity) {
+                slot[i] = -1;
+                dropped += 1;
+                continue;
+            }
+            int32_t r = (int32_t)(start[e] + local);
             slot[i] = r;
             if (src)
                 src[r] = (int32_t)(i / k);
@@ -178,9 +210,21 @@ void oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E,
             slot[i] = -1;
         }
     }
+    free(raw);
+    free(start);
     free(cursor);
     if (num_invalid)
         *num_invalid = bad;
+    if (num_dropped)
+        *num_dropped = dropped;
+}
+
+/* The compact layout: alignment 1, no capacity. */
+void oracle_layout(const int64_t *topk_idx, int64_t T, int k, int E,
+                   int32_t *counts, int32_t *offsets, int32_t *slot,
+                   int32_t *src, int32_t *num_invalid)
+{
+    oracle_layout_ex(topk_idx, T, k, E, 1, 0, counts, offsets, slot, src, num_invalid, NULL);
 }
 
 /* ----------------------------------------------------------- dispatch -- */
@@ -272,4 +316,60 @@ void oracle_combine(const uint16_t *y, const int32_t *slot, const float *topk_we
             }
             out[t * H + c] = oracle_bf16_from_double(acc);
         }
+}
+
+/* ----------------------------------------------------------- backward -- */
+
+/*
+ * Backward of the weighted combine (DeepEP page, "MoE Dispatch and Combine
+ * for Training/Inference with ElasticBuffer": the backward of combine is a
+ * dispatch; NeMo page, HybridEPCombine.backward redispatches the combined-
+ * output gradients through the saved layout).  With out[t] = sum_j
+ * w[t,j] * y[slot[t,j]]:
+ *   grad_y[slot[t,j], c] = bf16( w[t,j] * g[t,c] )   (exact product in fp64,
+ *                                                     one rounding)
+ *   grad_w[t,j] = fl32( sum_c g[t,c] * y[slot[t,j], c] )   (fp64 sum)
+ * Masked pairs write no row and get grad_w 0.  w == NULL means unit
+ * weights; grad_w may be NULL (then y is not read).
+ */
+void oracle_combine_backward(const uint16_t *g, const uint16_t *y, const int32_t *slot,
+                             const float *topk_weights, int64_t T, int H, int k,
+                             uint16_t *grad_y, float *grad_w)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[t * k + j];
+            if (r < 0) {
+                if (grad_w)
+                    grad_w[t * k + j] = 0.0f;
+                continue;
+            }
+            double w = topk_weights ? (double)topk_weights[t * k + j] : 1.0;
+            double dot = 0.0;
+            for (int c = 0; c < H; ++c) {
+                double gv = oracle_bf16_to_double(g[t * H + c]);
+                grad_y[(int64_t)r * H + c] = oracle_bf16_from_double(w * gv);
+                if (grad_w)
+                    dot += gv * oracle_bf16_to_double(y[(int64_t)r * H + c]);
+            }
+            if (grad_w)
+                grad_w[t * k + j] = (float)dot;
+        }
+}
+
+/*
+ * Backward of dispatch (DeepEP page, same section: the backward of dispatch
+ * is a combine, which also returns the reduced weight gradients):
+ *   grad_x[t] = bf16( sum_j grad_recv[slot[t,j]] )          (unit weights)
+ *   grad_w[t,j] = grad_recv_w[slot[t,j]], 0 if masked
+ * grad_recv_w / grad_w may be NULL.
+ */
+void oracle_dispatch_backward(const uint16_t *grad_recv, const float *grad_recv_w,
+                              const int32_t *slot, int64_t T, int H, int k, uint16_t *grad_x,
+                              float *grad_w)
+{
+    oracle_combine(grad_recv, slot, NULL, T, H, k, grad_x);
+    if (grad_w && grad_recv_w)
+        for (int64_t i = 0; i < T * (int64_t)k; ++i)
+            grad_w[i] = slot[i] >= 0 ? grad_recv_w[slot[i]] : 0.0f;
 }

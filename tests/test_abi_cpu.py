@@ -59,7 +59,15 @@ def test_workspace_size():
 
 FAKE = 0x100000  # 16- and 256-byte aligned, never dereferenced by these calls
 
+# The calls below hand the library fake device pointers and expect a host-side
+# rejection.  Should a case ever pass validation by mistake it would launch a
+# kernel on them, so they run only where no GPU is visible.
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="fake pointers must never reach a launch on a real GPU")
 
+
+@no_gpu
 @pytest.mark.parametrize("args,code", [
     # (topk_idx, T, k, E, counts, offsets, slot, src, invalid, ws, ws_bytes)
     ((FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20), 1),       # E < 1
@@ -82,6 +90,7 @@ def test_layout_rejects(args, code):
     assert ep.last_error()
 
 
+@no_gpu
 @pytest.mark.parametrize("args,code", [
     # (x, T, H, k, slot, w, out_dtype, recv_x, recv_scales, recv_w)
     ((FAKE, 4, 7, 2, FAKE, None, 0, FAKE, None, None), 1),          # H % 8
@@ -112,6 +121,7 @@ def test_dispatch_and_combine_zero_tokens_are_noops():
     assert ep.last_error() == ""
 
 
+@no_gpu
 @pytest.mark.parametrize("args,code", [
     # (y, slot, w, T, H, k, out)
     ((FAKE, FAKE, None, 4, 12, 2, FAKE), 1),        # H % 8
@@ -134,3 +144,30 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ep, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ep.lib()
+
+
+def test_layout_max_rows():
+    assert ep.layout_max_rows(8192, 8, 256) == 65536
+    assert ep.layout_max_rows(8192, 8, 256, 128) == 65536 + 256 * 127
+    assert ep.layout_max_rows(3, 1, 256, 128) == 3 + 3 * 127       # only 3 experts can be hit
+    assert ep.layout_max_rows(8192, 8, 256, 1, 512) == 256 * 512
+    assert ep.layout_max_rows(8192, 8, 256, 128, 512) == 256 * 512
+    assert ep.layout_max_rows(8192, 8, 256, 128, 500) == -1          # capacity % alignment
+    assert ep.layout_max_rows(8192, 8, 256, 0) == -1
+    assert ep.layout_max_rows(8192, 8, 256, 4097) == -1
+    assert ep.layout_max_rows(8192, 8, 256, 1, -1) == -1
+
+
+@no_gpu
+@pytest.mark.parametrize("A,cap,T,code", [
+    (0, 0, 4, 1),                 # alignment < 1
+    (4097, 0, 4, 1),              # alignment too large
+    (4, 6, 4, 1),                 # capacity not a multiple of alignment
+    (1, -2, 4, 1),                # negative capacity
+    (4096, 0, (1 << 30) - 1, 2),  # 2^31-2 pairs + 256*4095 padding rows >= 2^31
+    (1, 1 << 24, 4, 2),           # E * capacity >= 2^31
+])
+def test_layout_ex_rejects(A, cap, T, code):
+    st = ep.lib().ep_layout_ex(FAKE, T, 2, 256, A, cap, FAKE, FAKE, FAKE, None, None, None,
+                               FAKE, 1 << 30, None)
+    assert st == code, ep.last_error()

@@ -1,0 +1,135 @@
+"""GPU parity of the backward passes against the oracle.
+
+combine backward: grad_y (w * g rounded once to bf16) bit-exact on every
+placed row, untouched elsewhere; grad_w (a length-H dot product accumulated
+in fp32 in an unspecified order) within |gpu - oracle| <= 2 H 2^-24 S +
+2^-24 |oracle|, S = sum_c |g_c y_c|, the standard bound for an fp32 sum of
+H products plus the final rounding.
+
+dispatch backward: grad_x is a unit-weight combine of mixed-sign row
+gradients: one bf16 ulp plus the fp32 bound 2 k 2^-24 sum_j |g_j|; the
+weight-gradient gather is exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_04_amd import ep
+from combine_ep_layout_04_amd.inputs import (
+    WORKLOADS, expert_outputs_scaled, float32_from_bf16_bits, make_gradient, make_inputs,
+    make_random_case,
+)
+
+from gpu_util import DEV, bf16_bits, bf16_ulp, dev, host, x_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def dot_bound(g_bits, y_bits, slot, ref_w):
+    T, k = slot.shape
+    H = g_bits.shape[1]
+    g = np.abs(float32_from_bf16_bits(g_bits))
+    y = np.abs(float32_from_bf16_bits(y_bits))
+    s = np.zeros((T, k), np.float64)
+    for j in range(k):
+        r = slot[:, j]
+        ok = r >= 0
+        s[ok, j] = np.einsum("th,th->t", g[ok], y[r[ok]], dtype=np.float64)
+    return 2.0 * H * 2.0 ** -24 * s + 2.0 ** -24 * np.abs(ref_w.astype(np.float64)) + 1e-38
+
+
+def run_combine_backward(g, y, slot, w, rows):
+    T, k = slot.shape
+    H = g.shape[1]
+    gy = torch.full((rows, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_combine_backward(x_dev(g), x_dev(y), dev(slot), None if w is None else dev(w),
+                           grad_y=gy, grad_topk_weights=gw, rows=rows)
+    torch.cuda.synchronize()
+    return bf16_bits(gy), host(gw)
+
+
+def check_combine_backward(g, y, L, w, rows):
+    slot = L.slot
+    g_gy, g_gw = run_combine_backward(g, y, slot, w, rows)
+    o_gy, o_gw = oracle.combine_backward(g, y, slot, w, rows=rows)
+    placed = np.zeros(rows, bool)
+    placed[slot[slot >= 0]] = True
+    np.testing.assert_array_equal(g_gy[placed], o_gy[placed])
+    assert np.all(g_gy[~placed] == 0xFFFF)
+    tol = dot_bound(g, y, slot, o_gw)
+    err = np.abs(g_gw.astype(np.float64) - o_gw.astype(np.float64))
+    bad = err > tol
+    assert not bad.any(), f"grad_w off at {np.argwhere(bad)[:5].tolist()}"
+    assert np.all(g_gw[slot < 0] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "headline", "skewed"])
+def test_combine_backward_workloads(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    print(f"\n[backward] combine {name}", flush=True)
+    L = oracle.layout(inp.topk_idx, w.E)
+    recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    y = expert_outputs_scaled(recv, L.offsets) if w.expert == "scaled" else recv
+    g = make_gradient(w.T, w.H, 7)
+    check_combine_backward(g, y, L, inp.topk_weights, w.T * w.k)
+
+
+@pytest.mark.parametrize("T,H,E,k,A", [
+    (1, 8, 1, 1, 1),
+    (300, 200, 16, 9, 1),      # k = 9: two slot groups; 25-vector rows (tail)
+    (257, 1032, 33, 5, 16),    # one pass + tail; aligned layout
+    (64, 2048, 64, 64, 1),     # k = EP_MAX_TOPK: eight slot groups
+])
+def test_combine_backward_shapes(T, H, E, k, A):
+    inp = make_random_case(T + k, T, H, E, k, mask_frac=0.15, dup_frac=1.0, invalid_frac=0.05)
+    print(f"\n[backward] combine T={T} H={H} E={E} k={k} A={A}", flush=True)
+    L = oracle.layout(inp.topk_idx, E, alignment=A)
+    rows = oracle.max_rows(T, k, E, A)
+    y = make_gradient(rows, H, 3)
+    g = make_gradient(T, H, 4)
+    check_combine_backward(g, y, L, inp.topk_weights, rows)
+    check_combine_backward(g, y, L, None, rows)          # unit weights
+
+
+def test_combine_backward_without_weight_grad():
+    inp = make_random_case(5, 100, 256, 8, 4, mask_frac=0.1)
+    L = oracle.layout(inp.topk_idx, 8)
+    g = make_gradient(100, 256, 9)
+    gy, gw = ep.ep_combine_backward(x_dev(g), None, dev(L.slot), dev(inp.topk_weights))
+    torch.cuda.synchronize()
+    assert gw is None
+    o_gy, _ = oracle.combine_backward(g, None, L.slot, inp.topk_weights)
+    placed = np.zeros(400, bool)
+    placed[L.slot[L.slot >= 0]] = True
+    np.testing.assert_array_equal(bf16_bits(gy)[placed], o_gy[placed])
+
+
+@pytest.mark.parametrize("name,T", [("tiny", None), ("headline", None), ("skewed", 2048)])
+def test_dispatch_backward(name, T):
+    w = WORKLOADS[name]
+    inp = make_inputs(w, T=T)
+    T = inp.topk_idx.shape[0]
+    print(f"\n[backward] dispatch {name} T={T}", flush=True)
+    L = oracle.layout(inp.topk_idx, w.E)
+    rows = T * w.k
+    grad_recv = make_gradient(rows, w.H, 21)
+    grad_recv_w = np.random.default_rng(22).standard_normal(rows).astype(np.float32)
+    gx = torch.full((T, w.H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    gx, gw = ep.ep_dispatch_backward(x_dev(grad_recv), dev(grad_recv_w), dev(L.slot), grad_x=gx)
+    torch.cuda.synchronize()
+    o_gx, o_gw = oracle.dispatch_backward(grad_recv, grad_recv_w, L.slot, T)
+    np.testing.assert_array_equal(host(gw), o_gw)
+    got = float32_from_bf16_bits(bf16_bits(gx)).astype(np.float64)
+    want = float32_from_bf16_bits(o_gx).astype(np.float64)
+    gr = np.abs(float32_from_bf16_bits(grad_recv).astype(np.float64))
+    s = np.zeros_like(want)
+    for j in range(w.k):
+        r = L.slot[:, j]
+        ok = r >= 0
+        s[ok] += gr[r[ok]]
+    tol = bf16_ulp(want) + 2.0 * w.k * 2.0 ** -24 * s
+    assert np.all(np.abs(got - want) <= tol)
