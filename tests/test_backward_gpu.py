@@ -133,3 +133,19 @@ def test_dispatch_backward(name, T):
         s[ok] += gr[r[ok]]
     tol = bf16_ulp(want) + 2.0 * w.k * 2.0 ** -24 * s
     assert np.all(np.abs(got - want) <= tol)
+
+
+def test_combine_backward_ties():
+    # weights with short significands make w * g land exactly on bf16
+    # midpoints (ties to even); full-precision weights give products that
+    # round to a midpoint in fp32 while the exact product is just off it
+    T, H, E, k = 256, 512, 8, 4
+    inp = make_random_case(31, T, H, E, k)
+    L = oracle.layout(inp.topk_idx, E)
+    rng = np.random.default_rng(32)
+    short = np.array([1 + 2.0 ** -8, 1 - 2.0 ** -9, 3 * 2.0 ** -9, 1 + 3 * 2.0 ** -8], np.float32)
+    w = np.where(rng.random((T, k)) < 0.5, short[rng.integers(0, 4, (T, k))],
+                 rng.random((T, k), dtype=np.float32)).astype(np.float32)
+    g = make_gradient(T, H, 33)
+    y = make_gradient(T * k, H, 34)
+    check_combine_backward(g, y, L, w, T * k)
