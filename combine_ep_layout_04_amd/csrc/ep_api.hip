@@ -139,16 +139,22 @@ int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num
                         src, num_invalid, nullptr, workspace, workspace_bytes, stream);
 }
 
-int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
-                const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
-                float* recv_scales, float* recv_weights, void* stream)
+int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                   const int32_t* slot, const float* topk_weights, int out_dtype,
+                   int scale_format, void* recv_x, void* recv_scales, float* recv_weights,
+                   void* stream)
 {
     g_last_error[0] = '\0';
     int st = check_tokens(num_tokens, num_topk);
     if (st) return st;
-    if (out_dtype != EP_OUT_BF16 && out_dtype != EP_OUT_FP8_E4M3)
+    if (out_dtype != EP_OUT_BF16 && out_dtype != EP_OUT_FP8_E4M3 && out_dtype != EP_OUT_FP8_E5M2)
         return fail(EP_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
-    const bool fp8 = out_dtype == EP_OUT_FP8_E4M3;
+    if (scale_format != EP_SCALE_FP32 && scale_format != EP_SCALE_FP32_POW2 &&
+        scale_format != EP_SCALE_UE8M0)
+        return fail(EP_INVALID_ARGUMENT, "unknown scale_format %d", scale_format);
+    const bool fp8 = out_dtype != EP_OUT_BF16;
+    if (!fp8 && scale_format != EP_SCALE_FP32)
+        return fail(EP_INVALID_ARGUMENT, "bf16 output takes no scale format");
     st = check_hidden(hidden, fp8 ? 128 : 8);
     if (st) return st;
     if (num_tokens == 0) return EP_SUCCESS;
@@ -159,9 +165,10 @@ int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
         return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
     if (fp8) {
         if (!recv_scales) return fail(EP_INVALID_ARGUMENT, "fp8 dispatch needs recv_scales");
-        if (reinterpret_cast<uintptr_t>(recv_scales) & 3u)
-            return fail(EP_INVALID_ARGUMENT, "recv_scales must be 4-byte aligned");
+        if (scale_format != EP_SCALE_UE8M0 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+            return fail(EP_INVALID_ARGUMENT, "fp32 recv_scales must be 4-byte aligned");
         return from_hip(ep::launch_dispatch_fp8(x, num_tokens, hidden, num_topk, slot, topk_weights,
+                                                out_dtype == EP_OUT_FP8_E5M2 ? 1 : 0, scale_format,
                                                 recv_x, recv_scales, recv_weights,
                                                 static_cast<hipStream_t>(stream)),
                         "ep_dispatch (fp8) launch");
@@ -170,6 +177,39 @@ int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
     return from_hip(ep::launch_dispatch_bf16(x, num_tokens, hidden, num_topk, slot, topk_weights,
                                              recv_x, recv_weights, static_cast<hipStream_t>(stream)),
                     "ep_dispatch (bf16) launch");
+}
+
+int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
+                float* recv_scales, float* recv_weights, void* stream)
+{
+    return ep_dispatch_ex(x, num_tokens, hidden, num_topk, slot, topk_weights, out_dtype,
+                          EP_SCALE_FP32, recv_x, recv_scales, recv_weights, stream);
+}
+
+int ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num_tokens,
+                             int hidden, int num_topk, const int32_t* slot,
+                             const float* topk_weights, void* recv_q, float* recv_scales,
+                             float* recv_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 128);
+    if (st) return st;
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x_q || !x_scales || !slot || !recv_q || !recv_scales)
+        return fail(EP_INVALID_ARGUMENT, "x_q, x_scales, slot, recv_q and recv_scales are required");
+    if (!aligned16(x_q) || !aligned16(recv_q))
+        return fail(EP_INVALID_ARGUMENT, "x_q and recv_q must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(x_scales) & 3u) || (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+    if (recv_weights && !topk_weights)
+        return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
+    return from_hip(ep::launch_dispatch_prequant(x_q, x_scales, num_tokens, hidden, num_topk, slot,
+                                                 topk_weights, recv_q, recv_scales, recv_weights,
+                                                 static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_prequantized launch");
 }
 
 int ep_combine(const void* y, const int32_t* slot, const float* topk_weights,

@@ -156,18 +156,82 @@ __device__ __forceinline__ uint32_t e4m3_small_nonneg(float q)
     return a >= 0x3C800000u ? normal : tiny;
 }
 
+// OCP E5M2 (bias 15, 2 mantissa bits, largest finite 57344 = 1.75 * 2^15,
+// codes below 2^-14 are multiples of 2^-16), written from its definition.
+// Finite q with 0 <= q < 61440: keep 2 of 23 mantissa bits with RNE; below
+// 2^-14 add 2^7, whose unit in the last place is 2^-16.
+__device__ __forceinline__ uint32_t e5m2_small_nonneg(float q)
+{
+    const uint32_t a = __float_as_uint(q);
+    const uint32_t normal = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);
+    const uint32_t tiny = __float_as_uint(q + 128.0f) - 0x43000000u;
+    return a >= 0x38800000u ? normal : tiny;
+}
+
+// Any q: saturation to 57344 (infinities included), NaN -> S.11111.11.
+__device__ __forceinline__ uint32_t e5m2_rne_sat(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a > 0x7F800000u)
+        code = 0x7Fu;
+    else if (a >= 0x47600000u)
+        code = 0x7Bu;
+    else if (a >= 0x38800000u)
+        code = ((a + 0xFFFFFu + ((a >> 21) & 1u)) >> 21) - (112u << 2);
+    else
+        code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 65536.0f);
+    return sign | code;
+}
+
+// Output formats and scale modes of the 8-bit cast.
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+constexpr int kScaleFp32 = 0;   // scale = amax / max_finite
+constexpr int kScalePow2 = 1;   // smallest power of two >= amax / max_finite, fp32
+constexpr int kScaleUe8m0 = 2;  // the same power of two as one exponent byte
+
+template <int FMT>
+__device__ __forceinline__ float max_finite() { return FMT == kE5M2 ? 57344.0f : 448.0f; }
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_nonneg(float q)
+{
+    return FMT == kE5M2 ? e5m2_small_nonneg(q) : e4m3_small_nonneg(q);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_any(float q)
+{
+    return FMT == kE5M2 ? e5m2_rne_sat(q) : e4m3_rne_sat(q);
+}
+
 constexpr int kLanesPerBlock = 8;   // 16 channels per lane, 128 per block
 
+// Smallest e with 2^e >= s (s > 0 finite): frexp gives s = m * 2^ex with
+// m in [0.5, 1); s is a power of two exactly when m == 0.5.
+__device__ __forceinline__ int ceil_log2(float s)
+{
+    int ex;
+    const float m = frexpf(s, &ex);
+    return m == 0.5f ? ex - 1 : ex;
+}
+
 // Codes (16 bytes) and block scale for the 16 channels in d0:d1; the 8
-// aligned lanes of one 128-channel block must execute this together.
-__device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, float& scale)
+// aligned lanes of one 128-channel block must execute this together.  The
+// scale comes back as fp32 (modes 0, 1) or as the UE8M0 byte in its low
+// bits (mode 2).
+template <int FMT, int SM>
+__device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, uint32_t& scale_bits)
 {
     const float f[16] = {bf16_lo(d0.x), bf16_hi(d0.x), bf16_lo(d0.y), bf16_hi(d0.y),
                          bf16_lo(d0.z), bf16_hi(d0.z), bf16_lo(d0.w), bf16_hi(d0.w),
                          bf16_lo(d1.x), bf16_hi(d1.x), bf16_lo(d1.y), bf16_hi(d1.y),
                          bf16_lo(d1.z), bf16_hi(d1.z), bf16_lo(d1.w), bf16_hi(d1.w)};
     // max |x| as an unsigned compare of the magnitude bits (same order as
-    // the values; a NaN compares above infinity and selects the slow path)
+    // the values; a NaN compares above infinity)
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
@@ -175,38 +239,62 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, fl
     for (int s = 1; s < kLanesPerBlock; s <<= 1)
         m = max(m, (uint32_t)__shfl_xor((int)m, s, kLanesPerBlock));
 
+    const float fmax = max_finite<FMT>();
     uint32_t c[16];
-    if (m >= 0x17800000u && m < 0x7F800000u) {   // 2^-80 <= amax < inf
+    if (SM == kScaleFp32 && m >= 0x17800000u && m < 0x7F800000u) {
+        // 2^-80 <= amax < inf: Markstein-corrected quotients
         const float amax = __uint_as_float(m);
-        const float sc = amax / 448.0f;
+        const float sc = amax / fmax;
         const float y = 1.0f / sc;
-        scale = sc;
+        scale_bits = __float_as_uint(sc);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float ax = fabsf(f[i]);
             const float q0 = ax * y;
             const float r = __builtin_fmaf(-q0, sc, ax);
             const float q = __builtin_fmaf(r, y, q0);
-            c[i] = e4m3_small_nonneg(q) | ((__float_as_uint(f[i]) >> 24) & 0x80u);
+            c[i] = encode_nonneg<FMT>(q) | ((__float_as_uint(f[i]) >> 24) & 0x80u);
         }
+    } else if (SM != kScaleFp32 && m > 0u && m < 0x7F800000u) {
+        // finite nonzero amax, power-of-two scale: q = x * 2^-e is exact and
+        // |q| <= max_finite
+        const float amax = __uint_as_float(m);
+        int e = ceil_log2(amax / fmax);
+        if (SM == kScaleUe8m0 && e < -127) e = -127;
+        scale_bits = SM == kScaleUe8m0 ? (uint32_t)(e + 127) : __float_as_uint(ldexpf(1.0f, e));
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            c[i] = encode_nonneg<FMT>(ldexpf(fabsf(f[i]), -e)) |
+                   ((__float_as_uint(f[i]) >> 24) & 0x80u);
     } else {
-        // tiny, zero, infinite or NaN amax: plain division; amax ignores
-        // NaN (an IEEE max), exactly as a scalar running max would
+        // zero, tiny (fp32 mode), infinite or NaN-holding blocks: amax
+        // ignores NaN (an IEEE max), plain division (or exact power-of-two
+        // scaling for a finite amax)
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
         for (int s = 1; s < kLanesPerBlock; s <<= 1)
             amax = fmaxf(amax, __shfl_xor(amax, s, kLanesPerBlock));
-        const float sc = amax / 448.0f;
-        scale = sc;
+        const bool pow2 = SM != kScaleFp32 && amax > 0.0f && amax < __builtin_inff();
+        int e = 0;
+        float sc = amax / fmax;
+        if (pow2) {
+            e = ceil_log2(sc);
+            if (SM == kScaleUe8m0 && e < -127) e = -127;
+            sc = ldexpf(1.0f, e);
+        }
+        if (SM == kScaleUe8m0)
+            scale_bits = amax == 0.0f ? 0u : (pow2 ? (uint32_t)(e + 127) : 0xFFu);
+        else
+            scale_bits = __float_as_uint(sc);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float q = f[i] / sc;
+            const float q = pow2 ? ldexpf(f[i], -e) : f[i] / sc;
             // a NaN quotient (NaN x, or infinite x over an infinite scale)
-            // is S.1111.111 with the sign of x, whatever NaN the divide made
+            // is S.1111111 with the sign of x, whatever NaN the divide made
             const uint32_t sx = (__float_as_uint(f[i]) >> 24) & 0x80u;
-            c[i] = amax == 0.0f ? 0u : (q != q ? (0x7Fu | sx) : e4m3_rne_sat(q));
+            c[i] = amax == 0.0f ? 0u : (q != q ? (0x7Fu | sx) : encode_any<FMT>(q));
         }
     }
     uint4 q;
@@ -221,16 +309,16 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, fl
 // vectors, one 16-byte output vector); a pass covers up to 64*VPT units and
 // 8*VPT <= 64 blocks.  Units past the row end read zeros and store nothing
 // (hidden is a multiple of 128, so an 8-lane block group is all in or all
-// out).
-template <int VPT>
+// out).  Scales go out as fp32 (modes 0, 1) or bytes (mode 2).
+template <int VPT, int FMT, int SM>
 __global__ __launch_bounds__(64)
 void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
                          const int32_t* __restrict__ slot, const float* __restrict__ w,
-                         uint4* __restrict__ recv_q, float* __restrict__ recv_s,
+                         uint4* __restrict__ recv_q, void* __restrict__ recv_s,
                          float* __restrict__ recv_w)
 {
     constexpr int kPass = 64 * VPT;
-    __shared__ float srow[kPass / kLanesPerBlock];
+    __shared__ uint32_t srow[kPass / kLanesPerBlock];
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t* s = slot + t * k;
@@ -257,14 +345,14 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
         uint4 q[VPT];
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
-            float sc;
-            q[u] = quantise16(d[u][0], d[u][1], sc);
-            if ((tid & (kLanesPerBlock - 1)) == 0) srow[(tid + u * 64) / kLanesPerBlock] = sc;
+            uint32_t sb;
+            q[u] = quantise16<FMT, SM>(d[u][0], d[u][1], sb);
+            if ((tid & (kLanesPerBlock - 1)) == 0) srow[(tid + u * 64) / kLanesPerBlock] = sb;
         }
         __syncthreads();
         const int b0 = p0 / kLanesPerBlock;
         const int pass_blocks = min(kPass / kLanesPerBlock, nb - b0);
-        const float my_scale = tid < pass_blocks ? srow[tid] : 0.0f;
+        const uint32_t my_scale = tid < pass_blocks ? srow[tid] : 0u;
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
             if (r < 0) continue;
@@ -274,9 +362,64 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
                 const int unit = p0 + tid + u * 64;
                 if (unit < units) store_nt(dq + unit, q[u]);
             }
-            if (tid < pass_blocks) recv_s[(int64_t)r * nb + b0 + tid] = my_scale;
+            if (tid < pass_blocks) {
+                if (SM == kScaleUe8m0)
+                    static_cast<uint8_t*>(recv_s)[(int64_t)r * nb + b0 + tid] = (uint8_t)my_scale;
+                else
+                    static_cast<uint32_t*>(recv_s)[(int64_t)r * nb + b0 + tid] = my_scale;
+            }
         }
         __syncthreads();
+    }
+}
+
+// Pre-quantized input: the 8-bit code row (hidden bytes, VPT 16-byte units
+// per lane per pass) and the fp32 scale row of token t are copied to every
+// unmasked slot.  No arithmetic: any 8-bit float format passes through.
+template <int VPT>
+__global__ __launch_bounds__(64)
+void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restrict__ xs,
+                              int units, int k, const int32_t* __restrict__ slot,
+                              const float* __restrict__ w, uint4* __restrict__ recv_q,
+                              float* __restrict__ recv_s, float* __restrict__ recv_w)
+{
+    constexpr int kPass = 64 * VPT;
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int32_t sl = token_slots(slot + t * k, k);
+    const int nb = units >> 3;
+
+    if (recv_w != nullptr && tid < k && sl >= 0) recv_w[sl] = w[t * k + tid];
+
+    const uint4* qr = xq + t * units;
+    for (int p0 = 0; p0 < units; p0 += kPass) {
+        uint4 d[VPT];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int unit = p0 + tid + u * 64;
+            d[u] = unit < units ? qr[unit] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) keep(d[u]);
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = lane_value(sl, j);
+            if (r < 0) continue;
+            uint4* dq = recv_q + (int64_t)r * units;
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) {
+                const int unit = p0 + tid + u * 64;
+                if (unit < units) store_nt(dq + unit, d[u]);
+            }
+        }
+    }
+    // the scale row: 64 floats per round
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+        const int b = b0 + tid;
+        const float v = b < nb ? xs[t * nb + b] : 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = lane_value(sl, j);
+            if (r >= 0 && b < nb) recv_s[(int64_t)r * nb + b] = v;
+        }
     }
 }
 
@@ -337,15 +480,10 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, i
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk,
-                               const int32_t* slot, const float* topk_weights, void* recv_q,
-                               float* recv_scales, float* recv_weights, hipStream_t stream)
+// the largest VPT <= 8 with 64*VPT dividing the row's units (448 = 64*7 at
+// hidden 7168), else the widest that fits
+static int units_per_lane(int units)
 {
-    if (num_tokens == 0) return hipSuccess;
-    const int nvec = hidden / 8;
-    const int units = hidden / 16;
-    // units per lane: the largest VPT <= 8 with 64*VPT dividing the row
-    // (448 = 64*7 units at hidden 7168), else the widest that fits
     const int fit = units / 64;
     int vpt = fit < 1 ? 1 : (fit > 8 ? 8 : fit);
     for (int v = 8; v >= 1; --v) {
@@ -354,12 +492,17 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
             break;
         }
     }
-    const dim3 grid((unsigned)num_tokens);
-    const uint4* xx = static_cast<const uint4*>(x);
-    uint4* qq = static_cast<uint4*>(recv_q);
-#define EP_FP8(V)                                                                          \
-    hipLaunchKernelGGL((dispatch_fp8_kernel<V>), grid, dim3(64), 0, stream, xx, nvec, num_topk, \
-                       slot, topk_weights, qq, recv_scales, recv_weights)
+    return vpt;
+}
+
+template <int FMT, int SM>
+static void launch_fp8_shape(int vpt, dim3 grid, hipStream_t stream, const uint4* xx, int nvec,
+                             int k, const int32_t* slot, const float* w, uint4* qq, void* ss,
+                             float* rw)
+{
+#define EP_FP8(V)                                                                             \
+    hipLaunchKernelGGL((dispatch_fp8_kernel<V, FMT, SM>), grid, dim3(64), 0, stream, xx, nvec, \
+                       k, slot, w, qq, ss, rw)
     switch (vpt) {
     case 1: EP_FP8(1); break;
     case 2: EP_FP8(2); break;
@@ -371,6 +514,60 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     default: EP_FP8(8); break;
     }
 #undef EP_FP8
+}
+
+hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                               const int32_t* slot, const float* topk_weights, int format,
+                               int scale_mode, void* recv_q, void* recv_scales,
+                               float* recv_weights, hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const int vpt = units_per_lane(hidden / 16);
+    const dim3 grid((unsigned)num_tokens);
+    const uint4* xx = static_cast<const uint4*>(x);
+    uint4* qq = static_cast<uint4*>(recv_q);
+#define EP_FP8_MODE(F, M)                                                                    \
+    launch_fp8_shape<F, M>(vpt, grid, stream, xx, nvec, num_topk, slot, topk_weights, qq,    \
+                           recv_scales, recv_weights)
+    if (format == kE5M2) {
+        if (scale_mode == kScalePow2) EP_FP8_MODE(kE5M2, kScalePow2);
+        else if (scale_mode == kScaleUe8m0) EP_FP8_MODE(kE5M2, kScaleUe8m0);
+        else EP_FP8_MODE(kE5M2, kScaleFp32);
+    } else {
+        if (scale_mode == kScalePow2) EP_FP8_MODE(kE4M3, kScalePow2);
+        else if (scale_mode == kScaleUe8m0) EP_FP8_MODE(kE4M3, kScaleUe8m0);
+        else EP_FP8_MODE(kE4M3, kScaleFp32);
+    }
+#undef EP_FP8_MODE
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num_tokens,
+                                    int hidden, int num_topk, const int32_t* slot,
+                                    const float* topk_weights, void* recv_q, float* recv_scales,
+                                    float* recv_weights, hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int units = hidden / 16;
+    const int vpt = units_per_lane(units);
+    const dim3 grid((unsigned)num_tokens);
+    const uint4* qq = static_cast<const uint4*>(xq);
+    uint4* rq = static_cast<uint4*>(recv_q);
+#define EP_PQ(V)                                                                                   \
+    hipLaunchKernelGGL((dispatch_prequant_kernel<V>), grid, dim3(64), 0, stream, qq, xs, units,     \
+                       num_topk, slot, topk_weights, rq, recv_scales, recv_weights)
+    switch (vpt) {
+    case 1: EP_PQ(1); break;
+    case 2: EP_PQ(2); break;
+    case 3: EP_PQ(3); break;
+    case 4: EP_PQ(4); break;
+    case 5: EP_PQ(5); break;
+    case 6: EP_PQ(6); break;
+    case 7: EP_PQ(7); break;
+    default: EP_PQ(8); break;
+    }
+#undef EP_PQ
     return hipGetLastError();
 }
 

@@ -31,6 +31,12 @@ EP_UNSUPPORTED = 2
 EP_RUNTIME_ERROR = 3
 EP_OUT_BF16 = 0
 EP_OUT_FP8_E4M3 = 1
+EP_OUT_FP8_E5M2 = 2
+EP_SCALE_FP32 = 0
+EP_SCALE_FP32_POW2 = 1
+EP_SCALE_UE8M0 = 2
+_FORMATS = {"e4m3": EP_OUT_FP8_E4M3, "e5m2": EP_OUT_FP8_E5M2}
+_SCALES = {"fp32": EP_SCALE_FP32, "pow2": EP_SCALE_FP32_POW2, "ue8m0": EP_SCALE_UE8M0}
 EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 EP_MAX_HIDDEN = 65536
@@ -38,7 +44,8 @@ EP_MAX_ALIGNMENT = 4096
 
 # every symbol include/ep.h declares
 SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspace_size",
-           "ep_layout", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_combine",
+           "ep_layout", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_dispatch_ex",
+           "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward")
 
 
@@ -76,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_max_rows.restype = i64
         L.ep_dispatch.argtypes = [P, i64, i32, i32, P, P, i32, P, P, P, P]
         L.ep_dispatch.restype = i32
+        L.ep_dispatch_ex.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P, P]
+        L.ep_dispatch_ex.restype = i32
+        L.ep_dispatch_prequantized.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, P]
+        L.ep_dispatch_prequantized.restype = i32
         L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
         L.ep_combine.restype = i32
         L.ep_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, P, P, P]
@@ -203,11 +214,15 @@ def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, alignment: int = 1, c
 # ---------------------------------------------------------------- dispatch --
 
 def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
-                *, fp8: bool = False, recv_x=None, recv_scales=None, recv_weights=None,
+                *, fp8: bool = False, fmt: str = "e4m3", scale: str = "fp32", recv_x=None,
+                recv_scales=None, recv_weights=None,
                 want_weights: bool = False, rows: Optional[int] = None,
                 trust_slots: bool = False, stream=None):
     """Permute (bf16) or cast (fp8 e4m3 + per-128 fp32 scales) the rows of
     ``x`` (bf16 [T, H]) into the expert-grouped buffer named by ``slot``.
+
+    With ``fp8`` the cast format is ``fmt`` ("e4m3" / "e5m2") and the scale
+    ``scale`` ("fp32", "pow2", "ue8m0" -- the last gives uint8 scales).
 
     Returns (recv_x, recv_scales or None, recv_weights or None); recv_x is
     bf16 [rows, H] or uint8 [rows, H].  ``rows`` is the layout's row bound
@@ -227,8 +242,9 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
     dev = x.device
     if recv_x is None:
         recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    sdt = torch.uint8 if scale == "ue8m0" else torch.float32
     if fp8 and recv_scales is None:
-        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+        recv_scales = torch.empty((R, H // 128), dtype=sdt, device=dev)
     if want_weights and recv_weights is None:
         recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
     if topk_weights is not None:
@@ -238,14 +254,52 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
     if recv_x.shape[-1] != H:
         raise ValueError("recv_x rows must have hidden elements")
     if recv_scales is not None:
-        _need(recv_scales, "recv_scales", torch.float32, cap * (H // 128))
+        _need(recv_scales, "recv_scales", sdt, cap * (H // 128))
     if recv_weights is not None:
         _need(recv_weights, "recv_weights", torch.float32, cap)
-    st = lib().ep_dispatch(_ptr(x), T, H, k, _ptr(slot), _ptr(topk_weights),
-                           EP_OUT_FP8_E4M3 if fp8 else EP_OUT_BF16, _ptr(recv_x),
-                           _ptr(recv_scales), _ptr(recv_weights), _stream(stream))
+    st = lib().ep_dispatch_ex(_ptr(x), T, H, k, _ptr(slot), _ptr(topk_weights),
+                              _FORMATS[fmt] if fp8 else EP_OUT_BF16,
+                              _SCALES[scale] if fp8 else EP_SCALE_FP32, _ptr(recv_x),
+                              _ptr(recv_scales), _ptr(recv_weights), _stream(stream))
     _check(st, "ep_dispatch")
     return recv_x, recv_scales, recv_weights
+
+
+def ep_dispatch_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor, slot: torch.Tensor,
+                             topk_weights: Optional[torch.Tensor] = None, *, recv_q=None,
+                             recv_scales=None, recv_weights=None, want_weights: bool = False,
+                             rows: Optional[int] = None, stream=None):
+    """Copy pre-quantized rows (uint8 [T, H]) and their fp32 scales
+    ([T, H/128]) to the expert-grouped buffer.  Returns (recv_q,
+    recv_scales, recv_weights or None)."""
+    _need(x_q, "x_q", torch.uint8)
+    _need(x_scales, "x_scales", torch.float32)
+    _need(slot, "slot", torch.int32)
+    if x_q.dim() != 2 or slot.dim() != 2 or slot.shape[0] != x_q.shape[0]:
+        raise ValueError("x_q must be [T, H] and slot [T, k]")
+    T, H = x_q.shape
+    k = slot.shape[1]
+    if x_scales.numel() < T * (H // 128):
+        raise ValueError("x_scales must hold T * H/128 values")
+    R = T * k if rows is None else int(rows)
+    dev = x_q.device
+    if recv_q is None:
+        recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    if recv_scales is None:
+        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
+    _need(recv_q, "recv_q", torch.uint8, R * H)
+    _need(recv_scales, "recv_scales", torch.float32, R * (H // 128))
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, R)
+    st = lib().ep_dispatch_prequantized(_ptr(x_q), _ptr(x_scales), T, H, k, _ptr(slot),
+                                        _ptr(topk_weights), _ptr(recv_q), _ptr(recv_scales),
+                                        _ptr(recv_weights), _stream(stream))
+    _check(st, "ep_dispatch_prequantized")
+    return recv_q, recv_scales, recv_weights
 
 
 # ----------------------------------------------------------------- combine --

@@ -64,9 +64,18 @@ typedef enum {
 
 typedef enum {
     EP_OUT_BF16 = 0,      /* recv_x is bf16 [rows, hidden]                  */
-    EP_OUT_FP8_E4M3 = 1   /* recv_x is OCP E4M3 bytes [rows, hidden] plus
-                             recv_scales fp32 [rows, hidden/128]            */
+    EP_OUT_FP8_E4M3 = 1,  /* recv_x is OCP E4M3 bytes [rows, hidden] plus
+                             recv_scales [rows, hidden/128]                 */
+    EP_OUT_FP8_E5M2 = 2   /* recv_x is OCP E5M2 bytes, likewise             */
 } ep_out_dtype_t;
+
+typedef enum {
+    EP_SCALE_FP32 = 0,      /* fp32 scale = amax / max_finite                 */
+    EP_SCALE_FP32_POW2 = 1, /* fp32 scale = 2^e, e the smallest integer with
+                               2^e >= amax / max_finite (rounded-up scale)   */
+    EP_SCALE_UE8M0 = 2      /* the same 2^e stored as one UE8M0 byte e + 127,
+                               e clamped to -127                             */
+} ep_scale_format_t;
 
 /* Limits checked by every call. */
 #define EP_MAX_EXPERTS 1024
@@ -200,6 +209,56 @@ int64_t ep_layout_max_rows(int64_t num_tokens, int num_topk, int num_experts, in
 int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
                 const int32_t *slot, const float *topk_weights, int out_dtype,
                 void *recv_x, float *recv_scales, float *recv_weights, void *stream);
+
+/*
+ * ep_dispatch_ex -- ep_dispatch with the 8-bit cast variants.  ep_dispatch
+ * is ep_dispatch_ex(scale_format = EP_SCALE_FP32).
+ *
+ * Passages: NCCL EP page, nccl_ep.cc: datatypes ncclFloat8e4m3 and
+ * ncclFloat8e5m2 (ncclDataTypeToCudaDataType; ncclEpDispatch FP8
+ * detection), and the low-latency dispatch kernel's round_scale and
+ * use_ue8m0 arguments (ncclEpDispatch low-latency branch).
+ *
+ *   out_dtype     EP_OUT_BF16, EP_OUT_FP8_E4M3 (largest finite 448) or
+ *                 EP_OUT_FP8_E5M2 (largest finite 57344).
+ *   scale_format  EP_SCALE_FP32: scale = amax / max_finite, code =
+ *                 RNE-saturating cast of the correctly rounded x / scale.
+ *                 EP_SCALE_FP32_POW2 / EP_SCALE_UE8M0: scale = 2^e as
+ *                 above, code = RNE-saturating cast of x * 2^-e (exact);
+ *                 recv_scales is fp32 [rows, hidden/128] or, for UE8M0,
+ *                 bytes [rows, hidden/128].  bf16 output takes
+ *                 EP_SCALE_FP32 only.
+ * amax ignores NaN.  amax == 0: codes 0 and scale 0 (fp32) or byte 0.  An
+ * infinite amax: scale inf (fp32) or byte 0xFF, finite x encode to signed
+ * zero; a NaN quotient gives 0x7F with the sign of x (both formats).
+ * Other arguments and errors as ep_dispatch.
+ */
+int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                   const int32_t *slot, const float *topk_weights, int out_dtype,
+                   int scale_format, void *recv_x, void *recv_scales, float *recv_weights,
+                   void *stream);
+
+/*
+ * ep_dispatch_prequantized -- dispatch of tokens that are already 8-bit
+ * floats with per-128-channel fp32 scales: the code row and the scale row of
+ * each token are copied, bit for bit, to every unmasked slot (any 8-bit
+ * format passes through).
+ *
+ * Passages: NCCL EP page, ncclEpDispatch high-throughput branch (FP8 is
+ * detected from the input datatype; FP8 tokens require a 2-D fp32 scales
+ * input); DeepEP page, dispatch() (x may be a (data, scale_factors) tuple).
+ *
+ * In:  x_q       bytes [num_tokens, hidden], 16-byte aligned.
+ *      x_scales  fp32 [num_tokens, hidden/128].
+ *      slot, topk_weights as ep_dispatch.
+ * Out: recv_q [rows, hidden], recv_scales fp32 [rows, hidden/128],
+ *      recv_weights [rows] or NULL.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch_prequantized(const void *x_q, const float *x_scales, int64_t num_tokens,
+                             int hidden, int num_topk, const int32_t *slot,
+                             const float *topk_weights, void *recv_q, float *recv_scales,
+                             float *recv_weights, void *stream);
 
 /*
  * ep_combine -- weighted reduction of expert outputs back to token order.

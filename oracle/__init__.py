@@ -61,6 +61,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_e4m3_decode.restype = ctypes.c_double
         L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
         L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_decode.restype = ctypes.c_double
+        L.oracle_e5m2_encode.argtypes = [ctypes.c_float]
+        L.oracle_e5m2_encode.restype = ctypes.c_uint8
+        L.oracle_dispatch_quant.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P]
+        L.oracle_dispatch_quant.restype = None
+        L.oracle_dispatch_prequant.argtypes = [P, P, i64, i32, i32, P, P, P, P, P]
+        L.oracle_dispatch_prequant.restype = None
         L.oracle_layout.argtypes = [P, i64, i32, i32, P, P, P, P, P]
         L.oracle_layout.restype = None
         L.oracle_layout_ex.argtypes = [P, i64, i32, i32, i32, i64, P, P, P, P, P, P]
@@ -103,6 +111,14 @@ def e4m3_decode(c: int) -> float:
 
 def e4m3_encode(v: float) -> int:
     return int(lib().oracle_e4m3_encode(float(v)))
+
+
+def e5m2_decode(c: int) -> float:
+    return lib().oracle_e5m2_decode(int(c) & 0xFF)
+
+
+def e5m2_encode(v: float) -> int:
+    return int(lib().oracle_e5m2_encode(float(v)))
 
 
 # ------------------------------------------------------------------ layout --
@@ -190,6 +206,53 @@ def dispatch_fp8(x_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[np
     w = None if topk_weights is None else _c(topk_weights, np.float32)
     rw = None if w is None else np.zeros(R, np.float32)
     lib().oracle_dispatch_fp8(_ptr(x), T, H, k, _ptr(s), _ptr(w), _ptr(q), _ptr(sc), _ptr(rw))
+    return q, sc, rw
+
+
+FORMATS = {"e4m3": 0, "e5m2": 1}
+SCALE_MODES = {"fp32": 0, "pow2": 1, "ue8m0": 2}
+
+
+def dispatch_quant(x_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[np.ndarray] = None,
+                   fmt: str = "e4m3", scale: str = "fp32", rows: Optional[int] = None):
+    """Return (recv_q uint8 [rows, H], recv_scales float32 or uint8
+    [rows, H/128], recv_w float32 [rows] or None)."""
+    x = _c(x_bits, np.uint16)
+    s = _c(slot, np.int32)
+    T, H = x.shape
+    if H % 128:
+        raise ValueError("fp8 dispatch needs hidden % 128 == 0")
+    k = s.shape[1]
+    R = T * k if rows is None else int(rows)
+    if s.size and s.max() >= R:
+        raise ValueError("a slot is beyond the receive buffer")
+    q = np.zeros((R, H), np.uint8)
+    sc = np.zeros((R, H // 128), np.uint8 if scale == "ue8m0" else np.float32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rw = None if w is None else np.zeros(R, np.float32)
+    lib().oracle_dispatch_quant(_ptr(x), T, H, k, _ptr(s), _ptr(w), FORMATS[fmt], SCALE_MODES[scale],
+                                _ptr(q), _ptr(sc), _ptr(rw))
+    return q, sc, rw
+
+
+def dispatch_prequant(xq: np.ndarray, xs: np.ndarray, slot: np.ndarray,
+                      topk_weights: Optional[np.ndarray] = None, rows: Optional[int] = None):
+    """Return (recv_q uint8 [rows, H], recv_scales float32 [rows, H/128],
+    recv_w float32 [rows] or None) for pre-quantized input."""
+    q_in = _c(xq, np.uint8)
+    s_in = _c(xs, np.float32)
+    s = _c(slot, np.int32)
+    T, H = q_in.shape
+    k = s.shape[1]
+    R = T * k if rows is None else int(rows)
+    if s.size and s.max() >= R:
+        raise ValueError("a slot is beyond the receive buffer")
+    q = np.zeros((R, H), np.uint8)
+    sc = np.zeros((R, H // 128), np.float32)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    rw = None if w is None else np.zeros(R, np.float32)
+    lib().oracle_dispatch_prequant(_ptr(q_in), _ptr(s_in), T, H, k, _ptr(s), _ptr(w), _ptr(q),
+                                   _ptr(sc), _ptr(rw))
     return q, sc, rw
 
 

@@ -47,6 +47,36 @@ def _e4m3_table() -> Tuple[List[Fraction], List[int]]:
 
 
 @lru_cache(maxsize=None)
+def _e5m2_table() -> Tuple[List[Fraction], List[int]]:
+    """All finite non-negative OCP E5M2 values with their codes, ascending.
+
+    Field layout S.EEEEE.MM, bias 15; exponent field 0 is subnormal
+    (exponent 1 - bias, implicit 0); exponent field 31 holds infinity and
+    NaNs, so S.11110.11 = 1.75 * 2^15 = 57344 is the largest finite value.
+    """
+    vals, codes = [], []
+    for code in range(0x00, 0x7C):
+        ef, mf = code >> 2, code & 3
+        v = Fraction(mf, 4) * Fraction(2) ** (1 - 15) if ef == 0 else \
+            (1 + Fraction(mf, 4)) * Fraction(2) ** (ef - 15)
+        vals.append(v)
+        codes.append(code)
+    return vals, codes
+
+
+def e5m2_encode(v: float) -> int:
+    """Nearest E5M2 code to v (saturating to +-57344), by table."""
+    if v != v:
+        return 0x7F
+    neg = np.signbit(np.float64(v))
+    vals, codes = _e5m2_table()
+    if np.isinf(v):
+        return codes[-1] | (0x80 if neg else 0)
+    c = _nearest_code(abs(Fraction(float(v))), vals, codes)
+    return c | (0x80 if neg else 0)
+
+
+@lru_cache(maxsize=None)
 def _bf16_table() -> Tuple[List[Fraction], List[int]]:
     """All finite non-negative bf16 values with their codes, ascending
     (8 exponent bits with bias 127, 7 stored mantissa bits)."""
@@ -196,6 +226,51 @@ def _bf16_float(code: int) -> float:
             return float("nan") if not code & 0x8000 else -float("nan")
         return -float("inf") if code & 0x8000 else float("inf")
     return float(bf16_value(code))
+
+
+def quantize_row(x_bits: np.ndarray, fmt: str = "e4m3", scale: str = "fp32"):
+    """Per 128-channel block, for every format and scale mode, from the
+    definitions with exact rationals where they decide: the power-of-two
+    exponent is the smallest integer e with 2^e >= amax / max_finite
+    (compared exactly), UE8M0 clamps e to -127; q = x * 2^-e is exact.
+    Returns (codes, scales as float32 or uint8)."""
+    H = x_bits.shape[0]
+    xs = [_bf16_float(int(b)) for b in x_bits]
+    fmax = 448 if fmt == "e4m3" else 57344
+    enc = e4m3_encode if fmt == "e4m3" else e5m2_encode
+    codes, scales = [], []
+    for b in range(H // 128):
+        blk = xs[b * 128:(b + 1) * 128]
+        amax = max((abs(v) for v in blk if v == v), default=0.0)
+        if amax == 0:
+            codes += [0] * 128
+            scales.append(0.0 if scale != "ue8m0" else 0)
+            continue
+        if scale == "fp32" or amax == float("inf"):
+            s = np.float32(np.float32(amax) / np.float32(fmax))
+            scales.append(float(s) if scale != "ue8m0" else 0xFF)
+            for v in blk:
+                with np.errstate(invalid="ignore"):
+                    q = np.float32(np.float32(v) / s)
+                codes.append(0x7F | (0x80 if np.signbit(np.float32(v)) else 0) if q != q else enc(float(q)))
+            continue
+        ratio = Fraction(amax) / fmax
+        e = 0
+        while Fraction(2) ** e < ratio:
+            e += 1
+        while Fraction(2) ** (e - 1) >= ratio:
+            e -= 1
+        if scale == "ue8m0":
+            e = max(e, -127)
+            scales.append(e + 127)
+        else:
+            scales.append(float(Fraction(2) ** e))
+        for v in blk:
+            if v != v:
+                codes.append(0x7F | (0x80 if np.signbit(np.float32(v)) else 0))
+            else:
+                codes.append(enc(float(Fraction(v) / Fraction(2) ** e)))
+    return np.array(codes, np.uint8), np.array(scales, np.uint8 if scale == "ue8m0" else np.float32)
 
 
 # ----------------------------------------------------------------- combine --

@@ -133,6 +133,44 @@ uint8_t oracle_e4m3_encode(float v)
     return (uint8_t)(sign | (uint8_t)code);
 }
 
+/* OCP E5M2 value of code c: (-1)^s 2^(e-15) (1 + m/4) for 0 < e < 31,
+ * (-1)^s 2^-14 (m/4) for e == 0; e == 31 is infinity (m == 0) or NaN. */
+double oracle_e5m2_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    double mag;
+    if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else
+        mag = (e == 0) ? ldexp((double)m / 4.0, -14) : ldexp(1.0 + (double)m / 4.0, e - 15);
+    return s ? -mag : mag;
+}
+
+/* Nearest E5M2 code to v, ties to the even code, magnitudes above the
+ * largest finite value 57344 (and infinities) saturated to it; sign kept;
+ * NaN gives S.11111.11.  Below 2^-14 the step is 2^-16. */
+uint8_t oracle_e5m2_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a > 57344.0)
+        a = 57344.0;
+    int code;
+    if (a < ldexp(1.0, -14)) {
+        code = (int)nearbyint(ldexp(a, 16));
+    } else {
+        int ex;
+        (void)frexp(a, &ex);
+        int e = ex - 1;                             /* -14 <= e <= 15 */
+        double mant = ldexp(a, -e) - 1.0;
+        int m = (int)nearbyint(mant * 4.0);
+        code = (e + 15) * 4 + m;
+    }
+    return (uint8_t)(sign | (uint8_t)code);
+}
+
 /* ------------------------------------------------------------- layout -- */
 
 static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -372,4 +410,111 @@ void oracle_dispatch_backward(const uint16_t *grad_recv, const float *grad_recv_
     if (grad_w && grad_recv_w)
         for (int64_t i = 0; i < T * (int64_t)k; ++i)
             grad_w[i] = slot[i] >= 0 ? grad_recv_w[slot[i]] : 0.0f;
+}
+
+/* ------------------------------------------------------ fp8 variants -- */
+
+/*
+ * Dispatch with an 8-bit float cast, in the variants the pages name (NCCL EP
+ * page, ncclEpDispatch: datatypes ncclFloat8e4m3 / ncclFloat8e5m2; the
+ * low-latency kernel's round_scale and use_ue8m0 arguments; DeepEP page,
+ * dispatch() FP8 data with scale factors):
+ *   format 0: OCP E4M3 (largest finite 448), 1: OCP E5M2 (57344)
+ *   scale_mode 0: scale = fl32(amax / max_finite), q = code(fl32(x / scale))
+ *   scale_mode 1: power-of-two scale 2^e, e the smallest integer with
+ *                 2^e >= amax / max_finite (ceil of log2 of fl32(amax /
+ *                 max_finite)), stored as fp32; q = code(x * 2^-e) (exact)
+ *   scale_mode 2: as 1, stored as one UE8M0 byte e + 127 with e clamped to
+ *                 -127 (the byte's smallest value)
+ * amax ignores NaN.  amax == 0: codes 0, scale 0 (fp32) or byte 0.  An
+ * infinite amax: scale inf (fp32) or byte 0xFF, finite x encode to signed
+ * zero.  A NaN quotient is S.1111111 (0x7F) with the sign of x.
+ * recv_scales is fp32 [rows, H/128] for modes 0-1 and bytes for mode 2.
+ */
+static uint8_t encode_fmt(int format, float q) { return format ? oracle_e5m2_encode(q) : oracle_e4m3_encode(q); }
+
+void oracle_dispatch_quant(const uint16_t *x, int64_t T, int H, int k, const int32_t *slot,
+                           const float *topk_weights, int format, int scale_mode,
+                           uint8_t *recv_q, void *recv_scales, float *recv_w)
+{
+    int nb = H / 128;
+    float fmax = format ? 57344.0f : 448.0f;
+    uint8_t *row_q = (uint8_t *)malloc((size_t)H);
+    float *row_s = (float *)malloc((size_t)nb * sizeof(float));
+    uint8_t *row_b = (uint8_t *)malloc((size_t)nb);
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *xr = x + t * H;
+        for (int b = 0; b < nb; ++b) {
+            float amax = 0.0f;
+            for (int c = 0; c < 128; ++c) {
+                float av = fabsf((float)oracle_bf16_to_double(xr[b * 128 + c]));
+                if (av > amax)
+                    amax = av;
+            }
+            int e = 0;
+            float scale;
+            if (scale_mode == 0 || amax == 0.0f || isinf(amax)) {
+                scale = amax / fmax;
+            } else {
+                int ex;
+                float s0 = amax / fmax;
+                double f = frexp((double)s0, &ex);      /* s0 = f * 2^ex, f in [0.5, 1) */
+                e = (f == 0.5) ? ex - 1 : ex;           /* smallest e with 2^e >= s0 */
+                if (scale_mode == 2 && e < -127)
+                    e = -127;
+                scale = ldexpf(1.0f, e);
+            }
+            row_s[b] = scale;
+            row_b[b] = amax == 0.0f ? 0 : (isinf(amax) ? 0xFF : (uint8_t)(e + 127));
+            for (int c = 0; c < 128; ++c) {
+                float v = (float)oracle_bf16_to_double(xr[b * 128 + c]);
+                if (amax == 0.0f) {
+                    row_q[b * 128 + c] = 0x00;
+                    continue;
+                }
+                float q = (scale_mode == 0 || isinf(amax)) ? v / scale : ldexpf(v, -e);
+                row_q[b * 128 + c] = isnan(q) ? (uint8_t)(0x7F | (signbit(v) ? 0x80 : 0))
+                                              : encode_fmt(format, q);
+            }
+        }
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[t * k + j];
+            if (r < 0)
+                continue;
+            memcpy(recv_q + (int64_t)r * H, row_q, (size_t)H);
+            if (scale_mode == 2)
+                memcpy((uint8_t *)recv_scales + (int64_t)r * nb, row_b, (size_t)nb);
+            else
+                memcpy((float *)recv_scales + (int64_t)r * nb, row_s, (size_t)nb * sizeof(float));
+            if (recv_w && topk_weights)
+                recv_w[r] = topk_weights[t * k + j];
+        }
+    }
+    free(row_q);
+    free(row_s);
+    free(row_b);
+}
+
+/*
+ * Dispatch of an input that is already 8-bit floats with per-128 fp32
+ * scales (NCCL EP page, ncclEpDispatch high-throughput branch: FP8 is
+ * detected from the input datatype and the scales tensor comes with it;
+ * DeepEP page, dispatch() x as a (data, scale_factors) tuple): the code row
+ * and scale row of token t are copied to every unmasked slot.
+ */
+void oracle_dispatch_prequant(const uint8_t *xq, const float *xs, int64_t T, int H, int k,
+                              const int32_t *slot, const float *topk_weights, uint8_t *recv_q,
+                              float *recv_s, float *recv_w)
+{
+    int nb = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[t * k + j];
+            if (r < 0)
+                continue;
+            memcpy(recv_q + (int64_t)r * H, xq + t * H, (size_t)H);
+            memcpy(recv_s + (int64_t)r * nb, xs + t * nb, (size_t)nb * sizeof(float));
+            if (recv_w && topk_weights)
+                recv_w[r] = topk_weights[t * k + j];
+        }
 }

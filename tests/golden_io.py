@@ -16,7 +16,11 @@ def _tok(s):
     try:
         return int(s)
     except ValueError:
+        pass
+    try:
         return float(s)
+    except ValueError:
+        return s
 
 
 def read_cases(name):
