@@ -44,6 +44,9 @@ def log(*a):
 # header and the build flags)
 KERNEL_SOURCES = {
     "dispatch_bf16": "ep_dispatch.hip", "dispatch_fp8": "ep_dispatch.hip",
+    "dispatch_fp8_e5m2_fp32": "ep_dispatch.hip", "dispatch_fp8_e4m3_pow2": "ep_dispatch.hip",
+    "dispatch_fp8_e4m3_ue8m0": "ep_dispatch.hip", "dispatch_fp8_e5m2_ue8m0": "ep_dispatch.hip",
+    "dispatch_fp8_prequantized": "ep_dispatch.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -71,6 +74,10 @@ def bytes_model(T, H, k, n):
         "dispatch_bf16": T * H * 2 + n * H * 2 + T * k * 4,
         # read x once, write codes and per-128 scales per row, read slot
         "dispatch_fp8": T * H * 2 + n * H + n * (H // 128) * 4 + T * k * 4,
+        "dispatch_fp8_ue8m0": T * H * 2 + n * H + n * (H // 128) + T * k * 4,
+        # read the code and scale rows once, write them per row, read slot
+        "dispatch_prequantized": T * H + T * (H // 128) * 4 + n * H + n * (H // 128) * 4
+                                 + T * k * 4,
         # read every dispatched row once, write out once, read slot and weights
         "combine": n * H * 2 + T * H * 2 + T * k * 4 + T * k * 4,
         # read g and every expert row once, write every row gradient once,
@@ -302,6 +309,26 @@ def main():
     lay_a128, _ = time_layout(128, 0, args.steps)
     lay_cap, dropped_cap = time_layout(1, 320, args.steps)
 
+    # ---- 8-bit cast variants and the pre-quantized copy (fp8 workload)
+    variants = {}
+    with torch.cuda.stream(stream):
+        sc_b = torch.empty((P, H // 128), dtype=torch.uint8, device=dev)
+        xq_tok = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xs_tok = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+        ident = torch.arange(T, dtype=torch.int32, device=dev).view(T, 1)
+    stream.synchronize()
+    # the tokens' own E4M3 rows and scales, for the pre-quantized input
+    check(L.ep_dispatch(xf.data_ptr(), T, H, 1, ident.data_ptr(), None, 1, xq_tok.data_ptr(),
+                        xs_tok.data_ptr(), None, s), "ep_dispatch fp8 (tokens)")
+    for name, fmt, mode, sbuf in (("e5m2_fp32", 2, 0, sc), ("e4m3_pow2", 1, 1, sc),
+                                  ("e4m3_ue8m0", 1, 2, sc_b), ("e5m2_ue8m0", 2, 2, sc_b)):
+        variants[name] = time_call(lambda: check(L.ep_dispatch_ex(
+            xf.data_ptr(), T, H, k, slotf.data_ptr(), None, fmt, mode, q.data_ptr(),
+            sbuf.data_ptr(), None, s), "ep_dispatch_ex"), args.steps)
+    variants["prequantized"] = time_call(lambda: check(L.ep_dispatch_prequantized(
+        xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
+        sc.data_ptr(), None, s), "ep_dispatch_prequantized"), args.steps)
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly 1 GiB each
         a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
@@ -320,6 +347,11 @@ def main():
                          "workload": "fp8: headline shape, 1% of rows x100"},
         "combine_backward": {"us": round(cb_us, 2), "bytes": bm["combine_backward"]},
         "dispatch_backward": {"us": round(db_us, 2), "bytes": bm["dispatch_backward"]},
+        **{f"dispatch_fp8_{name}": {"us": round(v, 2),
+                                    "bytes": bmf["dispatch_fp8_ue8m0" if "ue8m0" in name else
+                                                 ("dispatch_prequantized" if name == "prequantized"
+                                                  else "dispatch_fp8")]}
+           for name, v in variants.items()},
         "layout_aligned128": {"us": round(lay_a128, 2)},
         "layout_capacity320": {"us": round(lay_cap, 2), "dropped_pairs": dropped_cap},
     }
@@ -329,6 +361,8 @@ def main():
             v["GB_per_s"] = round(gbs, 1)
             v["frac_of_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
             v["tokens_per_s"] = round(T / (v["us"] * 1e-6), 1)
+        if key in KERNEL_SOURCES:
+            v["traffic"] = read_traffic(key)
 
     dom = "combine" if per_kernel["combine"]["us"] >= per_kernel["dispatch_bf16"]["us"] else "dispatch_bf16"
     dk = per_kernel[dom]

@@ -5,7 +5,9 @@
     python -m combine_ep_layout_04_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
         --cmd "..." --out profiles/hbm_traffic_headline.txt
 
-``stats`` reads ``*_kernel_stats.csv`` (from ``--kernel-trace --stats``);
+``stats`` reads ``*_kernel_stats.csv`` (from ``--kernel-trace --stats``,
+without ``-T`` so that template instances stay apart) and prints each
+kernel's name without its namespace and argument list;
 ``pmc`` reads ``*_counter_collection.csv`` (from ``--pmc``) and reports the
 mean counter value per dispatch for each kernel; ``traffic`` takes one
 FETCH_SIZE run and one WRITE_SIZE run of ``bench.py --copy-calibration``,
@@ -21,6 +23,7 @@ import argparse
 import csv
 import glob
 import os
+import re
 import statistics
 import sys
 from collections import defaultdict
@@ -33,6 +36,18 @@ def _find(d: str, suffix: str):
     return hits
 
 
+def short_name(name: str) -> str:
+    """``void ep::(anonymous namespace)::k<1, 2>(int, ...)`` -> ``k<1, 2>``."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.replace("ep::(anonymous namespace)::", "")
+    cut = name.find("(")
+    if cut > 0 and not name.startswith("("):
+        name = name[:cut]
+    return name if len(name) < 90 else name[:87] + "..."
+
+
 def stats(d: str):
     rows = []
     for f in _find(d, "kernel_stats.csv"):
@@ -41,7 +56,7 @@ def stats(d: str):
     out = ["| kernel | calls | average (us) | min (us) | max (us) | share |",
            "|---|---|---|---|---|---|"]
     for r in rows:
-        out.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.1f}% |")
     return out
@@ -63,38 +78,53 @@ def pmc(d: str):
     return out
 
 
-def _counter_means(d: str):
+def _counter_medians(d: str):
     vals = defaultdict(list)
     for f in _find(d, "counter_collection.csv"):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName")
                 vals[name].append(float(r.get("Counter_Value") or r.get("Counter-Value")))
-    return {k: statistics.fmean(v) for k, v in vals.items()}
+    return {k: statistics.median(v) for k, v in vals.items()}
 
 
-# library kernels by the key bench.py reports them under (the combine line
-# also averages the dispatch-backward launches, which run the same kernel
-# over the same bytes plus a [T, k] gather)
-KERNEL_KEYS = {"dispatch_bf16": "dispatch_bf16_kernel", "dispatch_fp8": "dispatch_fp8_kernel",
-               "combine": "combine_kernel", "combine_backward": "combine_backward_kernel",
-               "layout_count": "layout_count_kernel",
-               "layout_scatter": "layout_scatter_kernel"}
+# library kernels by the key bench.py reports them under, as a pattern on
+# the full kernel name; the 8-bit cast is told apart by its template
+# arguments <rows per lane, format (0 E4M3, 1 E5M2), scale (0 fp32, 1 power
+# of two, 2 UE8M0)>.  The median over a kernel's dispatches is used: the
+# E4M3 / fp32 instance also runs once over the tokens themselves (T rows,
+# one slot each) to make the pre-quantized input.  The combine line also
+# counts the dispatch-backward launches, which run the same kernel over the
+# same bytes plus a [T, k] gather.
+KERNEL_KEYS = {
+    "dispatch_bf16": r"dispatch_bf16_kernel<",
+    "dispatch_fp8": r"dispatch_fp8_kernel<\d+, 0, 0>",
+    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_kernel<\d+, 1, 0>",
+    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_kernel<\d+, 0, 1>",
+    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_kernel<\d+, 0, 2>",
+    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_kernel<\d+, 1, 2>",
+    "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
+    "combine": r"[^_]combine_kernel<",
+    "combine_backward": r"combine_backward_kernel<",
+    "layout_count": r"layout_count_kernel\(",
+    "layout_scatter": r"layout_scatter_kernel\(",
+}
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
 
 
 def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
-    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+    fetch, write = _counter_medians(fetch_dir), _counter_medians(write_dir)
 
     def pick(table, needle):
-        hits = [v for k, v in table.items() if needle in k]
+        hits = [v for k, v in table.items() if re.search(needle, k)]
         if len(hits) != 1:
             sys.exit(f"expected one kernel matching {needle!r}, found {len(hits)}")
         return hits[0]
 
     f_scale = COPY_KIB / pick(fetch, "neg_kernel")
     w_scale = COPY_KIB / pick(write, "neg_kernel")
-    lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+    lines = ["# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch,",
+             "# median over the kernel's dispatches),",
              "# each scaled by the same counter on a plain 1 GiB elementwise copy (torch.neg,",
              "# int32): scale = 1048576 KiB / counter.  Commands:",
              *[f"#   {c}" for c in cmd.split(" ;; ")],
