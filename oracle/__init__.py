@@ -83,6 +83,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine_backward.restype = None
         L.oracle_dispatch_backward.argtypes = [P, P, P, i64, i32, i32, P, P]
         L.oracle_dispatch_backward.restype = None
+        L.oracle_routing_map.argtypes = [P, i64, i32, i32, P, P]
+        L.oracle_routing_map.restype = None
+        L.oracle_rank_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.oracle_rank_layout.restype = None
+        L.oracle_dispatch_ranked.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P]
+        L.oracle_dispatch_ranked.restype = None
+        L.oracle_combine_ranked.argtypes = [P, P, i64, i32, i32, P]
+        L.oracle_combine_ranked.restype = None
         _lib = L
     return _lib
 
@@ -307,3 +315,87 @@ def dispatch_backward(grad_recv_bits: np.ndarray, grad_recv_w: Optional[np.ndarr
     gw = None if grw is None else np.zeros((T, k), np.float32)
     lib().oracle_dispatch_backward(_ptr(gr), _ptr(grw), _ptr(s), T, H, k, _ptr(gx), _ptr(gw))
     return gx, gw
+
+
+# ------------------------------------------------ per-(token, rank) path --
+
+def routing_map(topk_idx: np.ndarray, num_experts: int):
+    """Return (map uint8 [T, ceil(E/8)], num_invalid): bit e % 8 of byte
+    e // 8 of row t is set iff token t selects expert e."""
+    idx = _c(topk_idx, np.int64)
+    T, k = idx.shape
+    E = int(num_experts)
+    m = np.zeros((T, (E + 7) // 8), np.uint8)
+    bad = np.zeros(1, np.int32)
+    lib().oracle_routing_map(_ptr(idx), T, k, E, _ptr(m), _ptr(bad))
+    return m, int(bad[0])
+
+
+class RankLayout:
+    """Result of :func:`rank_layout` for one rank: sparse_to_dense [T, G],
+    local_map uint8 [G*T, E/G], recv_src [G*T], recv_topk_idx [G*T, k_out],
+    expert_counts [E/G], num_recv, num_overflow."""
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def rank_layout(global_map: np.ndarray, T: int, E: int, G: int, rank: int, k_out: int) -> RankLayout:
+    m = _c(global_map, np.uint8)
+    if m.shape != (G * T, (E + 7) // 8) or E % G or not 0 <= rank < G:
+        raise ValueError("bad rank layout shape")
+    El = E // G
+    R = G * T
+    s2d = np.zeros((T, G), np.int32)
+    lm = np.zeros((R, El), np.uint8)
+    src = np.zeros(R, np.int32)
+    rti = np.zeros((R, k_out), np.int64)
+    cnt = np.zeros(El, np.int32)
+    nr = np.zeros(1, np.int32)
+    ov = np.zeros(1, np.int32)
+    lib().oracle_rank_layout(_ptr(m), T, E, G, rank, k_out, _ptr(s2d), _ptr(lm), _ptr(src),
+                             _ptr(rti), _ptr(cnt), _ptr(nr), _ptr(ov))
+    return RankLayout(sparse_to_dense=s2d, local_map=lm, recv_src=src, recv_topk_idx=rti,
+                      expert_counts=cnt, num_recv=int(nr[0]), num_overflow=int(ov[0]))
+
+
+def _ptr_array(arrs):
+    return (ctypes.c_void_p * len(arrs))(*[None if a is None else a.ctypes.data for a in arrs])
+
+
+def dispatch_ranked(x_bits: np.ndarray, topk_idx: np.ndarray, topk_weights: Optional[np.ndarray],
+                    E: int, G: int, sparse_to_dense: np.ndarray, rows, with_weights: bool = True):
+    """Return (dest_x list of G uint16 [rows_d, H], dest_w list of G float32
+    [rows_d, k] or None).  ``rows`` is one int or G ints; unwritten rows
+    stay 0."""
+    x = _c(x_bits, np.uint16)
+    idx = _c(topk_idx, np.int64)
+    s2d = _c(sparse_to_dense, np.int32)
+    T, H = x.shape
+    k = idx.shape[1]
+    rows = [int(rows)] * G if np.isscalar(rows) else [int(r) for r in rows]
+    for d in range(G):
+        if s2d.size and s2d[:, d].max() >= rows[d]:
+            raise ValueError("a row is beyond a destination buffer")
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    dx = [np.zeros((rows[d], H), np.uint16) for d in range(G)]
+    dw = [np.zeros((rows[d], k), np.float32) for d in range(G)] if with_weights else None
+    lib().oracle_dispatch_ranked(_ptr(x), _ptr(idx), _ptr(w), T, H, k, int(E), G, _ptr(s2d),
+                                 _ptr_array(dx), None if dw is None else _ptr_array(dw))
+    return dx, dw
+
+
+def combine_ranked(src_y, sparse_to_dense: np.ndarray) -> np.ndarray:
+    """Return out uint16 [T, H]: the fp64 sum over ranks, rounded once."""
+    ys = [_c(y, np.uint16) for y in src_y]
+    s2d = _c(sparse_to_dense, np.int32)
+    T, G = s2d.shape
+    if len(ys) != G:
+        raise ValueError("one source buffer per rank")
+    H = ys[0].shape[1]
+    for d in range(G):
+        if s2d.size and s2d[:, d].max() >= ys[d].shape[0]:
+            raise ValueError("a row is beyond a source buffer")
+    out = np.zeros((T, H), np.uint16)
+    lib().oracle_combine_ranked(_ptr_array(ys), _ptr(s2d), T, H, G, _ptr(out))
+    return out

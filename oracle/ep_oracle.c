@@ -36,6 +36,13 @@
  *    j of w[t,j] * y[slot[t,j]], summed in fp64 in ascending j and rounded
  *    once to bf16 (round-to-nearest-even).  A NULL weight array means unit
  *    weights (the unweighted forward combine of the high-throughput path).
+ *
+ *  - The per-(token, rank) path (NCCL EP page, the high-throughput handle's
+ *    routing bitmap, sparse_to_dense_map, local_expert_routing_map and
+ *    num_tokens_for_experts): the routing bitmap of topk_idx, the receive
+ *    rows of every (token, destination rank) pair, the receiving rank's
+ *    per-row local expert map, and a dispatch / combine that moves each
+ *    token once per rank.  Defined in the last section of this file.
  */
 
 #include <math.h>
@@ -516,5 +523,204 @@ void oracle_dispatch_prequant(const uint8_t *xq, const float *xs, int64_t T, int
             memcpy(recv_s + (int64_t)r * nb, xs + t * nb, (size_t)nb * sizeof(float));
             if (recv_w && topk_weights)
                 recv_w[r] = topk_weights[t * k + j];
+        }
+}
+
+/* ------------------------------------------ per-(token, rank) layout -- */
+
+/*
+ * The non-expanded path (NCCL EP page, nccl_ep.cc: the high-throughput
+ * handle's routing structures global_routing_map, sparse_to_dense_map,
+ * local_expert_routing_map and num_tokens_for_experts, and the
+ * high-throughput branch of ncclEpCreateHandle: Step 1 converts topk_idx to
+ * the bitmap, Step 2 all-gathers it, Step 3 runs the metadata preprocessing
+ * with the per-expert receive counter).  A token travels to a rank once, no
+ * matter how many of that rank's experts it selected.
+ *
+ * G ranks; rank d owns experts [d*El, (d+1)*El), El = E / G.  Every rank
+ * contributes T rows to the all-gathered map, so the global token
+ * g = s*T + t is token t of rank s.  A map row has W = ceil(E/8) bytes.
+ */
+
+/* Bitmap of one rank's routing: bit (e mod 8) of byte e div 8 of row t is 1
+ * iff some slot j of token t selects expert e.  Masked slots (-1) set
+ * nothing; ids outside [-1, E) set nothing and are counted. */
+void oracle_routing_map(const int64_t *topk_idx, int64_t T, int k, int E, uint8_t *map,
+                        int32_t *num_invalid)
+{
+    int64_t W = (E + 7) / 8;
+    int32_t bad = 0;
+    memset(map, 0, (size_t)(T * W));
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            if (e == -1)
+                continue;
+            if (e < -1 || e >= E) {
+                ++bad;
+                continue;
+            }
+            map[t * W + e / 8] |= (uint8_t)(1u << (e % 8));
+        }
+    if (num_invalid)
+        *num_invalid = bad;
+}
+
+static int map_bit(const uint8_t *map, int64_t W, int64_t g, int e)
+{
+    return (map[g * W + e / 8] >> (e % 8)) & 1;
+}
+
+/* Does global token g select any expert of rank d? */
+static int routed_to_rank(const uint8_t *map, int64_t W, int64_t g, int d, int El)
+{
+    for (int e = d * El; e < (d + 1) * El; ++e)
+        if (map_bit(map, W, g, e))
+            return 1;
+    return 0;
+}
+
+/*
+ * Metadata preprocessing for rank `rank` from the all-gathered map
+ * [G*T, W].  Rank d's receive buffer holds the tokens that select one of
+ * its experts, once each, in increasing global token order.
+ *
+ *   sparse_to_dense [T, G]: row of rank `rank`'s token t in rank d's
+ *                    receive buffer, -1 if t selects none of d's experts.
+ *   num_recv:        tokens rank `rank` receives (num_tokens_for_experts).
+ *   for each received row i < num_recv (global token g):
+ *     local_map [i, e]   1 iff g selects local expert e (rank*El + e),
+ *     recv_src [i]       g,
+ *     recv_topk_idx [i]  the selected local experts in increasing order,
+ *                        the first k_out of them, then -1 (selections past
+ *                        k_out are counted in num_overflow),
+ *   rows num_recv .. G*T-1: local_map 0, recv_src -1, recv_topk_idx -1.
+ *   expert_counts [El]:  received tokens that select each local expert.
+ */
+void oracle_rank_layout(const uint8_t *map, int64_t T, int E, int G, int rank, int k_out,
+                        int32_t *sparse_to_dense, uint8_t *local_map, int32_t *recv_src,
+                        int64_t *recv_topk_idx, int32_t *expert_counts, int32_t *num_recv,
+                        int32_t *num_overflow)
+{
+    int El = E / G;
+    int64_t W = (E + 7) / 8;
+    int64_t R = (int64_t)G * T;
+    int32_t overflow = 0;
+    for (int d = 0; d < G; ++d) {
+        int32_t pos = 0;   /* rows of rank d's buffer taken so far */
+        for (int64_t g = 0; g < R; ++g) {
+            int hit = routed_to_rank(map, W, g, d, El);
+            if (g / T == rank)
+                sparse_to_dense[(g % T) * G + d] = hit ? pos : -1;
+            if (hit && d == rank) {
+                int n = 0;
+                for (int e = 0; e < El; ++e) {
+                    int b = map_bit(map, W, g, rank * El + e);
+                    local_map[(int64_t)pos * El + e] = (uint8_t)b;
+                    if (b) {
+                        if (n < k_out)
+                            recv_topk_idx[(int64_t)pos * k_out + n] = e;
+                        else
+                            ++overflow;
+                        ++n;
+                    }
+                }
+                for (; n < k_out; ++n)
+                    recv_topk_idx[(int64_t)pos * k_out + n] = -1;
+                recv_src[pos] = (int32_t)g;
+            }
+            if (hit)
+                ++pos;
+        }
+        if (d == rank) {
+            *num_recv = pos;
+            for (int64_t i = pos; i < R; ++i) {
+                for (int e = 0; e < El; ++e)
+                    local_map[i * El + e] = 0;
+                for (int n = 0; n < k_out; ++n)
+                    recv_topk_idx[i * k_out + n] = -1;
+                recv_src[i] = -1;
+            }
+        }
+    }
+    for (int e = 0; e < El; ++e) {
+        int32_t c = 0;
+        for (int64_t i = 0; i < *num_recv; ++i)
+            c += local_map[i * El + e];
+        expert_counts[e] = c;
+    }
+    if (num_overflow)
+        *num_overflow = overflow;
+}
+
+/*
+ * Dispatch of rank `rank`'s tokens, once per destination rank (NCCL EP page,
+ * ncclEpDispatch high-throughput branch: the token rows and, per received
+ * token, the weights of the receiving rank's experts; the receiver's
+ * recv_topk_weights [N_recv, k] come from the dense-to-sparse step keyed by
+ * local_expert_routing_map):
+ *   dest_x[d][sparse_to_dense[t,d]] = x[t]                  (bf16 bits)
+ *   dest_w[d][sparse_to_dense[t,d], n] = weight of the n-th selected expert
+ *       of rank d in increasing expert order, the fp32 sum in increasing j of
+ *       w[t,j] over the slots that select it (1 per slot when topk_weights
+ *       is NULL); 0 for n past the last one.  Rows are k wide.
+ * dest_w may be NULL, or hold NULL for a rank.
+ */
+void oracle_dispatch_ranked(const uint16_t *x, const int64_t *topk_idx, const float *topk_weights,
+                            int64_t T, int H, int k, int E, int G,
+                            const int32_t *sparse_to_dense, uint16_t *const *dest_x,
+                            float *const *dest_w)
+{
+    int El = E / G;
+    for (int64_t t = 0; t < T; ++t)
+        for (int d = 0; d < G; ++d) {
+            int32_t p = sparse_to_dense[t * G + d];
+            if (p < 0)
+                continue;
+            memcpy(dest_x[d] + (int64_t)p * H, x + t * H, (size_t)H * sizeof(uint16_t));
+            if (!dest_w || !dest_w[d])
+                continue;
+            float *row = dest_w[d] + (int64_t)p * k;
+            for (int n = 0; n < k; ++n)
+                row[n] = 0.0f;
+            int n = 0;
+            for (int e = d * El; e < (d + 1) * El; ++e) {
+                int hit = 0;
+                float s = 0.0f;
+                for (int j = 0; j < k; ++j)
+                    if (topk_idx[t * k + j] == e) {
+                        s = s + (topk_weights ? topk_weights[t * k + j] : 1.0f);
+                        hit = 1;
+                    }
+                if (hit) {
+                    if (n < k)
+                        row[n] = s;
+                    ++n;
+                }
+            }
+        }
+}
+
+/*
+ * Combine back to rank `rank`'s tokens (NCCL EP page, ncclEpCombine
+ * high-throughput forward combine: tokens only, unweighted; each receiving
+ * rank has already reduced its own experts' outputs of the token):
+ *   out[t] = bf16( sum over d with sparse_to_dense[t,d] >= 0 of
+ *                  src_y[d][sparse_to_dense[t,d]] ),
+ * summed in fp64 in increasing d and rounded once; +0 for a token no rank
+ * received.
+ */
+void oracle_combine_ranked(const uint16_t *const *src_y, const int32_t *sparse_to_dense, int64_t T,
+                           int H, int G, uint16_t *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int d = 0; d < G; ++d) {
+                int32_t p = sparse_to_dense[t * G + d];
+                if (p >= 0)
+                    s += oracle_bf16_to_double(src_y[d][(int64_t)p * H + c]);
+            }
+            out[t * H + c] = oracle_bf16_from_double(s);
         }
 }

@@ -1,0 +1,279 @@
+"""Pins for the oracle's per-(token, rank) path, CPU only.
+
+Routes that do not share the oracle's structure:
+
+* routing map: numpy's ``packbits(bitorder="little")`` of a boolean
+  [T, E] selection matrix built by fancy indexing (a library routine);
+* rank layout: a numpy formulation by whole-array operations (any() over
+  each rank's expert block, cumulative sums down the global token axis,
+  nonzero()) instead of the oracle's per-rank running counter;
+* dispatch: numpy fancy-index copies, and the weights from a dictionary
+  keyed by (rank, expert) filled slot by slot;
+* combine: the exact rational brute force of the expanded combine
+  (``oracle/brute.py``) on the destination buffers stacked into one, a
+  special case already pinned;
+* the hand-worked example ``tests/golden/ranked_handworked.txt``;
+* the whole non-expanded path (bitmap -> rank layout -> dispatch ->
+  receiver-side expanded layout, expert, weighted combine -> combine over
+  ranks) against the expanded path on the same routing, within the
+  rounding each one makes.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from combine_ep_layout_04_amd.inputs import (
+    bf16_bits_from_float32, float32_from_bf16_bits, make_gradient, make_random_case,
+)
+
+from golden_io import read_cases
+
+
+def np_routing_map(idx, E):
+    T, k = idx.shape
+    sel = np.zeros((T, E), bool)
+    ok = (idx >= 0) & (idx < E)
+    rows = np.repeat(np.arange(T), k).reshape(T, k)
+    sel[rows[ok], idx[ok]] = True
+    return np.packbits(sel, axis=1, bitorder="little")
+
+
+def np_rank_layout(gmap, T, E, G, rank, k_out):
+    El = E // G
+    R = G * T
+    bits = np.unpackbits(gmap, axis=1, bitorder="little")[:, :E].astype(bool)
+    routed = bits.reshape(R, G, El).any(axis=2)                 # [R, G]
+    pos = np.cumsum(routed, axis=0) - 1
+    mine = slice(rank * T, (rank + 1) * T)
+    s2d = np.where(routed[mine], pos[mine], -1).astype(np.int32)
+    src = np.nonzero(routed[:, rank])[0]
+    n = len(src)
+    local = bits[src][:, rank * El:(rank + 1) * El]
+    lm = np.zeros((R, El), np.uint8)
+    lm[:n] = local
+    rsrc = np.full(R, -1, np.int32)
+    rsrc[:n] = src
+    rti = np.full((R, k_out), -1, np.int64)
+    over = 0
+    for i in range(n):
+        es = np.nonzero(local[i])[0]
+        over += max(0, len(es) - k_out)
+        es = es[:k_out]
+        rti[i, :len(es)] = es
+    return dict(sparse_to_dense=s2d, local_map=lm, recv_src=rsrc, recv_topk_idx=rti,
+                expert_counts=local.sum(axis=0).astype(np.int32), num_recv=n, num_overflow=over)
+
+
+def np_dispatch_ranked(x, idx, w, E, G, s2d, rows):
+    T, H = x.shape
+    k = idx.shape[1]
+    El = E // G
+    dx = [np.zeros((rows, H), np.uint16) for _ in range(G)]
+    dw = [np.zeros((rows, k), np.float32) for _ in range(G)]
+    for d in range(G):
+        ts = np.nonzero(s2d[:, d] >= 0)[0]
+        dx[d][s2d[ts, d]] = x[ts]
+    for t in range(T):
+        acc = {}
+        for j in range(k):
+            e = int(idx[t, j])
+            if 0 <= e < E:
+                key = (e // El, e)
+                wt = np.float32(1.0) if w is None else w[t, j]
+                acc[key] = np.float32(acc.get(key, np.float32(0.0)) + wt)
+        for d in range(G):
+            if s2d[t, d] < 0:
+                continue
+            es = sorted(e for (dd, e) in acc if dd == d)
+            for n, e in enumerate(es[:k]):
+                dw[d][s2d[t, d], n] = acc[(d, e)]
+    return dx, dw
+
+
+def global_case(seed, T, E, G, k, mask=0.2, dup=0.0, invalid=0.0):
+    cases = [make_random_case(seed * 100 + s, T, 8, E, k, mask_frac=mask, dup_frac=dup,
+                              invalid_frac=invalid) for s in range(G)]
+    return cases
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_routing_map_vs_packbits(seed):
+    T, E, k = 37, [8, 13, 64, 256, 1][seed % 5], 5
+    inp = make_random_case(seed, T, 4, E, k, mask_frac=0.2, dup_frac=float(seed % 2),
+                           invalid_frac=0.1)
+    m, bad = oracle.routing_map(inp.topk_idx, E)
+    np.testing.assert_array_equal(m, np_routing_map(inp.topk_idx, E))
+    idx = inp.topk_idx
+    assert bad == int(((idx < -1) | (idx >= E)).sum())
+
+
+@pytest.mark.parametrize("seed,T,E,G,k,k_out", [
+    (0, 5, 8, 2, 3, 3), (1, 17, 16, 4, 4, 4), (2, 9, 12, 3, 5, 5), (3, 33, 64, 8, 8, 8),
+    (4, 1, 4, 4, 2, 2), (5, 20, 8, 1, 3, 3), (6, 24, 16, 2, 6, 2),   # k_out < k: overflow
+    (7, 40, 256, 8, 8, 8), (8, 7, 10, 5, 9, 9),
+])
+def test_rank_layout_vs_numpy(seed, T, E, G, k, k_out):
+    cases = global_case(seed, T, E, G, k, dup=float(seed % 2), invalid=0.05)
+    gmap = np.concatenate([oracle.routing_map(c.topk_idx, E)[0] for c in cases])
+    for rank in range(G):
+        got = oracle.rank_layout(gmap, T, E, G, rank, k_out)
+        want = np_rank_layout(gmap, T, E, G, rank, k_out)
+        for key, v in want.items():
+            np.testing.assert_array_equal(getattr(got, key), v, err_msg=f"{key} rank {rank}")
+
+
+def test_rank_layout_invariants():
+    T, E, G, k = 64, 32, 4, 6
+    cases = global_case(11, T, E, G, k, dup=1.0)
+    gmap = np.concatenate([oracle.routing_map(c.topk_idx, E)[0] for c in cases])
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    for d in range(G):
+        # rank d's buffer rows are filled exactly once, by the senders' pairs
+        rows = np.concatenate([L[s].sparse_to_dense[:, d] for s in range(G)])
+        rows = rows[rows >= 0]
+        assert sorted(rows.tolist()) == list(range(L[d].num_recv))
+        # and row i came from the sender recv_src[i] names
+        for s in range(G):
+            for t in range(T):
+                p = L[s].sparse_to_dense[t, d]
+                if p >= 0:
+                    assert L[d].recv_src[p] == s * T + t
+    # num_tokens_for_experts counts a token once per rank
+    for r in range(G):
+        assert L[r].num_recv <= G * T
+        assert L[r].expert_counts.sum() >= L[r].num_recv or L[r].num_recv == 0
+
+
+def test_handworked_fixture():
+    (c,) = read_cases("ranked_handworked.txt")
+    G, T, E, k = c["G"][0], c["T"][0], c["E"][0], c["k"][0]
+    idx = [np.array(c[f"idx_r{r}"], np.int64).reshape(T, k) for r in range(G)]
+    w = [np.array(c[f"w_r{r}"], np.float32).reshape(T, k) for r in range(G)]
+    maps = [oracle.routing_map(i, E)[0] for i in idx]
+    for r in range(G):
+        np.testing.assert_array_equal(maps[r][:, 0], c[f"map_r{r}"])
+    gmap = np.concatenate(maps)
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    El = E // G
+    for r in range(G):
+        np.testing.assert_array_equal(L[r].sparse_to_dense.ravel(), c[f"s2d_r{r}"])
+        assert L[r].num_recv == c[f"num_recv_r{r}"][0]
+        np.testing.assert_array_equal(L[r].local_map.ravel(), c[f"local_map_r{r}"])
+        np.testing.assert_array_equal(L[r].recv_src, c[f"recv_src_r{r}"])
+        np.testing.assert_array_equal(L[r].recv_topk_idx.ravel(), c[f"recv_topk_r{r}"])
+        np.testing.assert_array_equal(L[r].expert_counts, c[f"counts_r{r}"])
+        assert L[r].local_map.shape == (G * T, El)
+    # the weight rows each destination receives, from both senders
+    x = [make_gradient(T, 8, r) for r in range(G)]
+    got_w = [np.zeros((L[d].num_recv, k), np.float32) for d in range(G)]
+    for s in range(G):
+        _, dw = oracle.dispatch_ranked(x[s], idx[s], w[s], E, G, L[s].sparse_to_dense,
+                                       [L[d].num_recv for d in range(G)])
+        for d in range(G):
+            rows = L[s].sparse_to_dense[:, d]
+            got_w[d][rows[rows >= 0]] = dw[d][rows[rows >= 0]]
+    for d in range(G):
+        np.testing.assert_array_equal(got_w[d].ravel(), np.array(c[f"dest_w_{d}"], np.float32))
+
+
+@pytest.mark.parametrize("seed,G,E,k,weights", [(0, 2, 8, 3, True), (1, 4, 16, 5, True),
+                                                (2, 3, 9, 4, False), (3, 8, 64, 8, True)])
+def test_dispatch_ranked_vs_numpy(seed, G, E, k, weights):
+    T, H = 23, 24
+    inp = make_random_case(seed, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    others = global_case(seed + 50, T, E, G, k)
+    maps = [oracle.routing_map(c.topk_idx, E)[0] for c in others]
+    rank = seed % G
+    maps[rank] = oracle.routing_map(inp.topk_idx, E)[0]
+    L = oracle.rank_layout(np.concatenate(maps), T, E, G, rank, k)
+    rows = G * T
+    w = inp.topk_weights if weights else None
+    dx, dw = oracle.dispatch_ranked(inp.x_bits, inp.topk_idx, w, E, G, L.sparse_to_dense, rows)
+    ex, ew = np_dispatch_ranked(inp.x_bits, inp.topk_idx, w, E, G, L.sparse_to_dense, rows)
+    for d in range(G):
+        np.testing.assert_array_equal(dx[d], ex[d])
+        np.testing.assert_array_equal(dw[d], ew[d])
+
+
+@pytest.mark.parametrize("seed,G", [(0, 1), (1, 2), (2, 4), (3, 7)])
+def test_combine_ranked_vs_bruteforce(seed, G):
+    T, H = 9, 10
+    rng = np.random.default_rng(seed)
+    s2d = np.where(rng.random((T, G)) < 0.6, 0, -1).astype(np.int32)
+    rows = []
+    for d in range(G):
+        m = s2d[:, d] >= 0
+        s2d[m, d] = rng.permutation(int(m.sum()))
+        rows.append(int(m.sum()) + 1)
+    ys = []
+    for d in range(G):
+        v = (rng.standard_normal((rows[d], H)) * np.exp2(rng.integers(-5, 5, (rows[d], H))))
+        ys.append(bf16_bits_from_float32(v.astype(np.float32)))
+    got = oracle.combine_ranked(ys, s2d)
+    # stack the G buffers into one; the pair (t, d) reads row off[d] + s2d
+    off = np.cumsum([0] + rows)
+    slot = np.where(s2d >= 0, s2d + off[:-1][None, :], -1).astype(np.int32)
+    want = brute.combine(np.concatenate(ys), slot, None)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_nonexpanded_path_matches_expanded_path():
+    """Sender -> receivers -> sender with a per-expert stand-in expert,
+    against the expanded path: out[t] = sum_j w[t,j] * f_e(x[t]).  The
+    non-expanded path rounds each rank's partial sum to bf16 before the sum
+    over ranks, so the two agree within one bf16 ulp of every partial plus
+    one of the result."""
+    G, T, H, E, k = 4, 40, 32, 16, 4
+    El = E // G
+    cases = global_case(77, T, E, G, k, mask=0.1)
+    xs = [make_gradient(T, H, 10 + s) for s in range(G)]
+    gmap = np.concatenate([oracle.routing_map(c.topk_idx, E)[0] for c in cases])
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    rows = [L[d].num_recv for d in range(G)]
+    # dispatch from every sender into every receiver
+    recv_x = [np.zeros((G * T, H), np.uint16) for _ in range(G)]
+    recv_w = [np.zeros((G * T, k), np.float32) for _ in range(G)]
+    for s in range(G):
+        dx, dw = oracle.dispatch_ranked(xs[s], cases[s].topk_idx, cases[s].topk_weights, E, G,
+                                        L[s].sparse_to_dense, [G * T] * G)
+        for d in range(G):
+            m = L[s].sparse_to_dense[:, d]
+            recv_x[d][m[m >= 0]] = dx[d][m[m >= 0]]
+            recv_w[d][m[m >= 0]] = dw[d][m[m >= 0]]
+
+    def expert(e, xbits):   # f_e(x) = bf16(x * (e + 1) / 16), exact before rounding
+        f = float32_from_bf16_bits(xbits).astype(np.float64) * (e + 1) / 16.0
+        return bf16_bits_from_float32(f.astype(np.float32))
+
+    partial = []
+    for d in range(G):
+        # receiver: expanded layout of its received rows over its local experts
+        Ld = oracle.layout(L[d].recv_topk_idx, El)
+        rx, _ = oracle.dispatch_bf16(recv_x[d], Ld.slot)
+        y = np.zeros_like(rx)
+        for e in range(El):
+            a, b = Ld.offsets[e], Ld.offsets[e + 1]
+            y[a:b] = expert(d * El + e, rx[a:b])
+        partial.append(oracle.combine(y, Ld.slot, recv_w[d]))
+    out = [oracle.combine_ranked(partial, L[s].sparse_to_dense) for s in range(G)]
+    for s in range(G):
+        c = cases[s]
+        exact = np.zeros((T, H))
+        for t in range(T):
+            for j in range(k):
+                e = int(c.topk_idx[t, j])
+                if e >= 0:
+                    exact[t] += float(c.topk_weights[t, j]) * float32_from_bf16_bits(
+                        expert(e, xs[s][t:t + 1]))[0]
+        got = float32_from_bf16_bits(out[s]).astype(np.float64)
+        mag = np.zeros((T, H))
+        for t in range(T):
+            for j in range(k):
+                e = int(c.topk_idx[t, j])
+                if e >= 0:
+                    mag[t] += abs(float(c.topk_weights[t, j])) * np.abs(float32_from_bf16_bits(
+                        expert(e, xs[s][t:t + 1]))[0])
+        # G partial roundings + the final one, each at most 2^-8 relative
+        assert np.all(np.abs(got - exact) <= 2.0 ** -8 * (G + 1) * mag + 1e-30)
