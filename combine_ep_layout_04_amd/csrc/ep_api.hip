@@ -274,4 +274,160 @@ int ep_dispatch_backward(const void* grad_recv, const float* grad_recv_weights,
                     "ep_dispatch_backward launch");
 }
 
+
+// ---- per-(token, rank) path
+
+static int check_ranks(int num_experts, int num_ranks)
+{
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+        return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
+                    EP_MAX_EXPERTS);
+    if (num_ranks < 1 || num_ranks > EP_MAX_RANKS)
+        return fail(EP_INVALID_ARGUMENT, "num_ranks %d outside [1, %d]", num_ranks, EP_MAX_RANKS);
+    if (num_experts % num_ranks != 0)
+        return fail(EP_INVALID_ARGUMENT, "num_experts %d is not a multiple of num_ranks %d",
+                    num_experts, num_ranks);
+    return EP_SUCCESS;
+}
+
+int ep_routing_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                   uint8_t* routing_map, int32_t* num_invalid, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
+        return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
+                    EP_MAX_EXPERTS);
+    if (num_tokens > 0 && (!topk_idx || !routing_map))
+        return fail(EP_INVALID_ARGUMENT, "topk_idx and routing_map are required");
+    if ((reinterpret_cast<uintptr_t>(topk_idx) & 7u))
+        return fail(EP_INVALID_ARGUMENT, "topk_idx must be 8-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(num_invalid) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "num_invalid must be 4-byte aligned");
+    return from_hip(ep::launch_routing_map(topk_idx, num_tokens, num_topk, num_experts,
+                                           routing_map, num_invalid,
+                                           static_cast<hipStream_t>(stream)),
+                    "ep_routing_map launch");
+}
+
+size_t ep_rank_layout_workspace_size(int64_t tokens_per_rank, int num_experts, int num_ranks)
+{
+    if (tokens_per_rank < 0 || num_ranks < 1 || num_ranks > EP_MAX_RANKS || num_experts < 1 ||
+        num_experts > EP_MAX_EXPERTS || num_experts % num_ranks != 0)
+        return 0;
+    const size_t bytes = ep::rank_layout_workspace_bytes(tokens_per_rank, num_experts, num_ranks);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int ep_rank_layout(const uint8_t* global_routing_map, int64_t tokens_per_rank, int num_experts,
+                   int num_ranks, int rank, int k_out, int32_t* sparse_to_dense_map,
+                   uint8_t* local_expert_routing_map, int32_t* recv_src, int64_t* recv_topk_idx,
+                   int32_t* expert_counts, int32_t* num_recv, int32_t* num_overflow,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
+    if (rank < 0 || rank >= num_ranks)
+        return fail(EP_INVALID_ARGUMENT, "rank %d outside [0, %d)", rank, num_ranks);
+    if (k_out < 1 || k_out > EP_MAX_TOPK)
+        return fail(EP_INVALID_ARGUMENT, "k_out %d outside [1, %d]", k_out, EP_MAX_TOPK);
+    if (tokens_per_rank * (int64_t)num_ranks >= ((int64_t)1 << 31))
+        return fail(EP_UNSUPPORTED, "num_ranks * tokens_per_rank must be < 2^31");
+    if (!expert_counts || !num_recv)
+        return fail(EP_INVALID_ARGUMENT, "expert_counts and num_recv are required");
+    if (tokens_per_rank > 0 && (!global_routing_map || !sparse_to_dense_map ||
+                                !local_expert_routing_map || !recv_src || !recv_topk_idx))
+        return fail(EP_INVALID_ARGUMENT,
+                    "global_routing_map, sparse_to_dense_map, local_expert_routing_map, recv_src "
+                    "and recv_topk_idx are required");
+    if ((reinterpret_cast<uintptr_t>(local_expert_routing_map) & 3u) ||
+        (reinterpret_cast<uintptr_t>(sparse_to_dense_map) & 3u) ||
+        (reinterpret_cast<uintptr_t>(recv_src) & 3u) ||
+        (reinterpret_cast<uintptr_t>(expert_counts) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "int32 outputs and the local map must be 4-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(recv_topk_idx) & 7u))
+        return fail(EP_INVALID_ARGUMENT, "recv_topk_idx must be 8-byte aligned");
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(EP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    const size_t need = ep_rank_layout_workspace_size(tokens_per_rank, num_experts, num_ranks);
+    if (workspace_bytes < need)
+        return fail(EP_INVALID_ARGUMENT, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    return from_hip(ep::launch_rank_layout(global_routing_map, tokens_per_rank, num_experts,
+                                           num_ranks, rank, k_out, sparse_to_dense_map,
+                                           local_expert_routing_map, recv_src, recv_topk_idx,
+                                           expert_counts, num_recv, num_overflow, workspace,
+                                           static_cast<hipStream_t>(stream)),
+                    "ep_rank_layout launch");
+}
+
+int ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int num_ranks, const int32_t* sparse_to_dense_map, void* const* dest_x,
+                       float* const* dest_weights, int64_t dest_rows, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 8);
+    if (st) return st;
+    st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    if (dest_rows < 0) return fail(EP_INVALID_ARGUMENT, "dest_rows < 0");
+    if (!dest_x) return fail(EP_INVALID_ARGUMENT, "dest_x (a host array of pointers) is required");
+    ep::RankPtrs px = {}, pw = {};
+    for (int d = 0; d < num_ranks; ++d) {
+        if (!dest_x[d] || !aligned16(dest_x[d]))
+            return fail(EP_INVALID_ARGUMENT, "dest_x[%d] must be non-NULL and 16-byte aligned", d);
+        px.p[d] = dest_x[d];
+        if (dest_weights) {
+            if ((reinterpret_cast<uintptr_t>(dest_weights[d]) & 3u))
+                return fail(EP_INVALID_ARGUMENT, "dest_weights[%d] must be 4-byte aligned", d);
+            pw.p[d] = dest_weights[d];
+        }
+    }
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x || !sparse_to_dense_map)
+        return fail(EP_INVALID_ARGUMENT, "x and sparse_to_dense_map are required");
+    if (!aligned16(x)) return fail(EP_INVALID_ARGUMENT, "x must be 16-byte aligned");
+    if (dest_weights && (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 7u)))
+        return fail(EP_INVALID_ARGUMENT, "dest_weights needs an 8-byte aligned topk_idx");
+    return from_hip(ep::launch_dispatch_ranked(x, topk_idx, topk_weights, num_tokens, hidden,
+                                               num_topk, num_experts, num_ranks,
+                                               sparse_to_dense_map, px, pw, dest_weights != nullptr,
+                                               dest_rows, static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_ranked launch");
+}
+
+int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
+                      const int32_t* sparse_to_dense_map, int64_t num_tokens, int hidden,
+                      int num_ranks, void* out, void* stream)
+{
+    g_last_error[0] = '\0';
+    if (num_tokens < 0) return fail(EP_INVALID_ARGUMENT, "num_tokens < 0");
+    if (num_ranks < 1 || num_ranks > EP_MAX_RANKS)
+        return fail(EP_INVALID_ARGUMENT, "num_ranks %d outside [1, %d]", num_ranks, EP_MAX_RANKS);
+    if (num_tokens * (int64_t)num_ranks >= ((int64_t)1 << 31))
+        return fail(EP_UNSUPPORTED, "num_tokens * num_ranks must be < 2^31");
+    int st = check_hidden(hidden, 8);
+    if (st) return st;
+    if (src_rows < 0) return fail(EP_INVALID_ARGUMENT, "src_rows < 0");
+    if (!src_y) return fail(EP_INVALID_ARGUMENT, "src_y (a host array of pointers) is required");
+    ep::RankPtrs ps = {};
+    for (int d = 0; d < num_ranks; ++d) {
+        if (!src_y[d] || !aligned16(src_y[d]))
+            return fail(EP_INVALID_ARGUMENT, "src_y[%d] must be non-NULL and 16-byte aligned", d);
+        ps.p[d] = const_cast<void*>(src_y[d]);
+    }
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!sparse_to_dense_map || !out)
+        return fail(EP_INVALID_ARGUMENT, "sparse_to_dense_map and out are required");
+    if (!aligned16(out)) return fail(EP_INVALID_ARGUMENT, "out must be 16-byte aligned");
+    return from_hip(ep::launch_combine_ranked(ps, src_rows, sparse_to_dense_map, num_tokens, hidden,
+                                              num_ranks, out, static_cast<hipStream_t>(stream)),
+                    "ep_combine_ranked launch");
+}
+
 }  // extern "C"

@@ -48,6 +48,38 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
                           int64_t num_tokens, int hidden, int num_topk, void* out,
                           const float* row_w, float* out_w, hipStream_t stream);
 
+// ---- per-(token, rank) path (ep_ranked.hip)
+
+constexpr int kMaxRanks = 64;  // EP_MAX_RANKS
+
+// G device row pointers, passed by value as a kernel argument (a rank's
+// buffer may be NULL where the call allows it).
+struct RankPtrs {
+    void* p[kMaxRanks];
+};
+
+hipError_t launch_routing_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                              int num_experts, uint8_t* map, int32_t* num_invalid,
+                              hipStream_t stream);
+
+size_t rank_layout_workspace_bytes(int64_t tokens_per_rank, int num_experts, int num_ranks);
+
+hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int num_experts,
+                              int num_ranks, int rank, int k_out, int32_t* s2d,
+                              uint8_t* local_map, int32_t* recv_src, int64_t* recv_topk_idx,
+                              int32_t* expert_counts, int32_t* num_recv, int32_t* num_overflow,
+                              void* workspace, hipStream_t stream);
+
+hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                                  int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                  int num_ranks, const int32_t* s2d, const RankPtrs& dest_x,
+                                  const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                  hipStream_t stream);
+
+hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const int32_t* s2d,
+                                 int64_t num_tokens, int hidden, int num_ranks, void* out,
+                                 hipStream_t stream);
+
 hipError_t launch_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
                                    const float* topk_weights, int64_t num_tokens, int hidden,
                                    int num_topk, void* grad_y, float* grad_topk_weights,

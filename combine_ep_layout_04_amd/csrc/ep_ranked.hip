@@ -1,0 +1,646 @@
+// ep_ranked.hip -- the non-expanded, per-(token, rank) path on gfx950.
+//
+// Passages: NCCL EP page, nccl_ep.cc: the high-throughput handle's routing
+// structures (the all-gathered routing bitmap [tokens, ceil(E/8)], one bit
+// per expert; sparse_to_dense_map: the row of a (token, destination rank)
+// pair in that rank's buffer, -1 when not routed; local_expert_routing_map
+// [max_recv_tokens, experts_per_rank]; num_tokens_for_experts, each token
+// counted once per rank), ncclEpCreateHandle's high-throughput branch
+// (Step 1 bitmap from topk_idx, Step 2 all-gather, Step 3 preprocessing with
+// the per-expert receive counter), and the high-throughput branches of
+// ncclEpDispatch / ncclEpCombine (a token row travels once per rank; the
+// forward combine carries tokens only).
+//
+// G ranks; rank d owns experts [d*El, (d+1)*El), El = E / G.  The
+// all-gathered map has G*T rows; global token g = s*T + t is token t of
+// rank s.  Rank d's receive buffer lists the tokens that select any of its
+// experts, once each, in increasing g.
+//
+// Kernels (all deterministic: atomics only ever OR bits or add counts):
+//   routing map:  one workgroup per 64 tokens ORs every slot's bit into an
+//                 LDS copy of the rows, then writes the rows out whole.
+//   rank count:   one workgroup per chunk of global tokens counts, for every
+//                 rank, the chunk's tokens it receives (wavefront ballots),
+//                 and for the local rank the received tokens per local
+//                 expert and the selections past k_out.
+//   rank scatter: each workgroup sums the earlier chunks' counts, then walks
+//                 its chunk in batches of 256 tokens; a token's row in rank
+//                 d's buffer is that base plus its ballot prefix count in
+//                 the batch.  It writes sparse_to_dense for the local rank's
+//                 tokens and the receive-side rows; all workgroups clear the
+//                 rows past the received count; workgroup 0 writes totals.
+//   dispatch:     one workgroup per token reads the row once into registers
+//                 and stores it, non-temporally, to every rank that receives
+//                 it (a table of G row pointers passed by value), with the
+//                 token's weights for that rank's experts.
+//   combine:      one workgroup per token gathers its rows from the G
+//                 buffers through buffer resources (an unrouted rank gets a
+//                 0-byte resource: its loads return 0 without a branch) and
+//                 sums them in fp32 in increasing rank.
+
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kMaxExperts = 1024;   // EP_MAX_EXPERTS
+constexpr int kMapTokens = 64;      // tokens per routing-map workgroup
+constexpr int kMapThreads = 256;
+constexpr int kMaxRowWords = kMaxExperts / 32;
+constexpr int kRankThreads = 256;
+constexpr int kRankWaves = kRankThreads / 64;
+
+// ----------------------------------------------------------- routing map
+
+__global__ __launch_bounds__(kMapThreads)
+void routing_map_kernel(const int64_t* __restrict__ idx, int64_t T, int k, int E, int W,
+                        bool word_rows, uint8_t* __restrict__ map, int32_t* __restrict__ num_invalid)
+{
+    __shared__ uint32_t rows[kMapTokens * kMaxRowWords];
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kMapTokens;
+    const int nt = (int)min((int64_t)kMapTokens, T - t0);
+    const int W32 = (W + 3) >> 2;
+    for (int i = tid; i < nt * W32; i += kMapThreads) rows[i] = 0u;
+    __syncthreads();
+
+    int bad = 0;
+    const int pairs = nt * k;
+    const int64_t* ix = idx + t0 * k;
+    for (int i = tid; i < pairs; i += kMapThreads) {
+        const int64_t e = ix[i];
+        if (e >= 0 && e < E) {
+            // bit e of the row: word e / 32, bit e % 32 (little-endian, so
+            // byte e / 8 holds it at bit e % 8)
+            atomicOr(&rows[(i / k) * W32 + (int)(e >> 5)], 1u << (int)(e & 31));
+        } else if (e != -1) {
+            ++bad;
+        }
+    }
+    __syncthreads();
+
+    uint8_t* out = map + t0 * W;
+    if (word_rows) {
+        uint32_t* o32 = reinterpret_cast<uint32_t*>(out);
+        for (int i = tid; i < nt * W32; i += kMapThreads) o32[i] = rows[i];
+    } else {
+        for (int i = tid; i < nt * W; i += kMapThreads) {
+            const int tl = i / W;
+            const int b = i - tl * W;
+            out[i] = (uint8_t)(rows[tl * W32 + (b >> 2)] >> (8 * (b & 3)));
+        }
+    }
+    if (num_invalid != nullptr) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) bad += __shfl_xor(bad, m, 64);
+        if ((tid & 63) == 0 && bad != 0) atomicAdd(num_invalid, bad);
+    }
+}
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+// ------------------------------------------------------------ rank layout
+
+// 32 bits of a map row starting at bit p (little-endian bit order); bytes
+// past the row end read as 0.
+__device__ __forceinline__ uint32_t row_bits32(const uint8_t* row, int W, int p)
+{
+    const int b0 = p >> 3;
+    uint64_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int b = b0 + i;
+        if (b < W) v |= (uint64_t)row[b] << (8 * i);
+    }
+    return (uint32_t)(v >> (p & 7));
+}
+
+// Bit i of the result: the token selects an expert of rank i.
+template <bool WORDS>
+__device__ __forceinline__ uint64_t rank_mask(const uint8_t* row, int W, int E, int El)
+{
+    uint64_t m = 0;
+    for (int p = 0; p < E; p += 32) {
+        uint32_t w = WORDS ? reinterpret_cast<const uint32_t*>(row)[p >> 5] : row_bits32(row, W, p);
+        if (E - p < 32) w &= (1u << (E - p)) - 1u;
+        while (w != 0u) {
+            const int b = __builtin_ctz(w);
+            w &= w - 1u;
+            m |= 1ull << ((p + b) / El);
+        }
+    }
+    return m;
+}
+
+// Bits [q, q + 32) of the local rank's expert block (bit e = local expert
+// e), masked to the block.
+__device__ __forceinline__ uint32_t local_bits(const uint8_t* row, int W, int first, int El, int q)
+{
+    uint32_t w = row_bits32(row, W, first + q);
+    const int nb = El - q;
+    if (nb < 32) w &= (1u << nb) - 1u;
+    return w;
+}
+
+__device__ __forceinline__ int popc64(uint64_t v) { return __builtin_popcountll(v); }
+
+__device__ __forceinline__ uint64_t lanes_below()
+{
+    const int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Workspace: cnt[d][c] (G x C), ecnt[e][c] (El x C), ovf[c] (C), int32.
+template <bool WORDS>
+__global__ __launch_bounds__(kRankThreads)
+void rank_count_kernel(const uint8_t* __restrict__ map, int64_t R, int W, int E, int G, int El,
+                       int rank, int k_out, int64_t chunk, int C, int32_t* __restrict__ ws)
+{
+    __shared__ int32_t s_cnt[kMaxRanks];
+    __shared__ int32_t s_ecnt[kMaxExperts];
+    __shared__ int32_t s_ovf;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int c = blockIdx.x;
+    for (int i = tid; i < G; i += kRankThreads) s_cnt[i] = 0;
+    for (int i = tid; i < El; i += kRankThreads) s_ecnt[i] = 0;
+    if (tid == 0) s_ovf = 0;
+    __syncthreads();
+
+    const int64_t g0 = (int64_t)c * chunk;
+    const int64_t g1 = min(R, g0 + chunk);
+    int ovf = 0;
+    for (int64_t b = g0; b < g1; b += kRankThreads) {
+        const int64_t g = b + tid;
+        const bool live = g < g1;
+        const uint8_t* row = map + g * W;
+        const uint64_t m = live ? rank_mask<WORDS>(row, W, E, El) : 0ull;
+        for (int d = 0; d < G; ++d) {
+            const uint64_t bal = __ballot((m >> d) & 1ull);
+            if (lane == 0 && bal != 0ull) atomicAdd(&s_cnt[d], popc64(bal));
+        }
+        if ((m >> rank) & 1ull) {
+            int n = 0;
+            for (int q = 0; q < El; q += 32) {
+                uint32_t w = local_bits(row, W, rank * El, El, q);
+                n += __builtin_popcount(w);
+                while (w != 0u) {
+                    const int e = q + __builtin_ctz(w);
+                    w &= w - 1u;
+                    atomicAdd(&s_ecnt[e], 1);
+                }
+            }
+            ovf += n > k_out ? n - k_out : 0;
+        }
+    }
+    if (ovf != 0) atomicAdd(&s_ovf, ovf);
+    __syncthreads();
+    for (int i = tid; i < G; i += kRankThreads) ws[(int64_t)i * C + c] = s_cnt[i];
+    int32_t* ecnt = ws + (int64_t)G * C;
+    for (int i = tid; i < El; i += kRankThreads) ecnt[(int64_t)i * C + c] = s_ecnt[i];
+    if (tid == 0) ws[(int64_t)(G + El) * C + c] = s_ovf;
+}
+
+// Four local-map bytes (0 or 1) from four bits.
+__device__ __forceinline__ uint32_t spread4(uint32_t b)
+{
+    return (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
+}
+
+template <bool WORDS>
+__global__ __launch_bounds__(kRankThreads)
+void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, int W, int E,
+                         int G, int El, int rank, int k_out, int64_t chunk, int C,
+                         const int32_t* __restrict__ ws, int32_t* __restrict__ s2d,
+                         uint8_t* __restrict__ local_map, int32_t* __restrict__ recv_src,
+                         int64_t* __restrict__ recv_topk_idx, int32_t* __restrict__ expert_counts,
+                         int32_t* __restrict__ num_recv, int32_t* __restrict__ num_overflow)
+{
+    __shared__ int32_t s_base[kMaxRanks];
+    __shared__ int32_t s_wave[kRankWaves][kMaxRanks];
+    __shared__ int32_t s_nrecv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = blockIdx.x;
+    const int32_t* cnt = ws;
+    const int32_t* ecnt = ws + (int64_t)G * C;
+    const int32_t* ovf = ws + (int64_t)(G + El) * C;
+
+    // rows of each rank's buffer taken by earlier chunks; the received total
+    for (int d = tid; d < G; d += kRankThreads) {
+        int32_t s = 0;
+        for (int cc = 0; cc < c; ++cc) s += cnt[(int64_t)d * C + cc];
+        s_base[d] = s;
+    }
+    if (tid == 0) {
+        int32_t s = 0;
+        for (int cc = 0; cc < C; ++cc) s += cnt[(int64_t)rank * C + cc];
+        s_nrecv = s;
+    }
+    if (c == 0) {
+        for (int e = tid; e < El; e += kRankThreads) {
+            int32_t s = 0;
+            for (int cc = 0; cc < C; ++cc) s += ecnt[(int64_t)e * C + cc];
+            expert_counts[e] = s;
+        }
+        if (tid == 0 && num_overflow != nullptr) {
+            int32_t s = 0;
+            for (int cc = 0; cc < C; ++cc) s += ovf[cc];
+            *num_overflow = s;
+        }
+    }
+    __syncthreads();
+    if (c == 0 && tid == 0) *num_recv = s_nrecv;
+
+    const bool map4 = (El & 3) == 0;
+    const int64_t g0 = (int64_t)c * chunk;
+    const int64_t g1 = min(R, g0 + chunk);
+    const int64_t mine0 = (int64_t)rank * T;
+    for (int64_t b = g0; b < g1; b += kRankThreads) {
+        const int64_t g = b + tid;
+        const bool live = g < g1;
+        const uint8_t* row = map + g * W;
+        const uint64_t m = live ? rank_mask<WORDS>(row, W, E, El) : 0ull;
+        for (int d = 0; d < G; ++d) {
+            const uint64_t bal = __ballot((m >> d) & 1ull);
+            if (lane == 0) s_wave[wave][d] = popc64(bal);
+        }
+        __syncthreads();
+        const bool mine = live && g >= mine0 && g < mine0 + T;
+        for (int d = 0; d < G; ++d) {
+            const bool hit = (m >> d) & 1ull;
+            const uint64_t bal = __ballot(hit);
+            int32_t pos = s_base[d] + popc64(bal & lanes_below());
+            for (int w = 0; w < wave; ++w) pos += s_wave[w][d];
+            if (mine) s2d[(g - mine0) * G + d] = hit ? pos : -1;
+            if (hit && d == rank) {
+                // the receive-side row of token g
+                recv_src[pos] = (int32_t)g;
+                int64_t* topk = recv_topk_idx + (int64_t)pos * k_out;
+                uint8_t* lm = local_map + (int64_t)pos * El;
+                int n = 0;
+                for (int q = 0; q < El; q += 32) {
+                    uint32_t wbits = local_bits(row, W, rank * El, El, q);
+                    const int nb = min(32, El - q);
+                    if (map4) {
+                        for (int i = 0; i < nb; i += 4)
+                            *reinterpret_cast<uint32_t*>(lm + q + i) = spread4((wbits >> i) & 15u);
+                    } else {
+                        for (int i = 0; i < nb; ++i) lm[q + i] = (uint8_t)((wbits >> i) & 1u);
+                    }
+                    while (wbits != 0u) {
+                        const int e = q + __builtin_ctz(wbits);
+                        wbits &= wbits - 1u;
+                        if (n < k_out) topk[n] = e;
+                        ++n;
+                    }
+                }
+                for (; n < k_out; ++n) topk[n] = -1;
+            }
+        }
+        __syncthreads();
+        if (tid < G) {
+            int32_t s = 0;
+            for (int w = 0; w < kRankWaves; ++w) s += s_wave[w][tid];
+            s_base[tid] += s;
+        }
+        __syncthreads();
+    }
+
+    // rows past the received count: no source, no local expert
+    const int64_t nrecv = s_nrecv;
+    const int64_t stride = (int64_t)gridDim.x * kRankThreads;
+    for (int64_t i = nrecv + (int64_t)c * kRankThreads + tid; i < R; i += stride) {
+        recv_src[i] = -1;
+        int64_t* topk = recv_topk_idx + i * k_out;
+        for (int n = 0; n < k_out; ++n) topk[n] = -1;
+        uint8_t* lm = local_map + i * El;
+        if (map4) {
+            for (int e = 0; e < El; e += 4) *reinterpret_cast<uint32_t*>(lm + e) = 0u;
+        } else {
+            for (int e = 0; e < El; ++e) lm[e] = 0;
+        }
+    }
+}
+
+// --------------------------------------------------------------- dispatch
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store_nt(uint4* p, const uint4& v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+__device__ __forceinline__ void keep(uint4& v)
+{
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// The token's weights for rank d's experts, written by wavefront 0: lane j
+// (< k) holds slot j's expert e_j and weight w_j.  A lane whose expert is
+// the first slot of its expert id and belongs to rank d is a "member"; its
+// position is the number of members with a smaller expert id, its value the
+// fp32 sum in increasing j of the weights of the slots with its id.  Lanes
+// j >= members write 0 at position j, so all k positions are written.
+__device__ __forceinline__ void write_rank_weights(float* row, int k, int32_t e_j, float sum_j,
+                                                   bool first_j, int d, int El)
+{
+    const int lane = threadIdx.x & 63;
+    const bool member = lane < k && first_j && e_j >= d * El && e_j < (d + 1) * El;
+    const int members = popc64(__ballot(member));
+    int n = 0;
+    for (int jj = 0; jj < k; ++jj) {
+        const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
+        const int f2 = __builtin_amdgcn_readlane((int)first_j, jj);
+        n += (f2 != 0 && e2 >= d * El && e2 < (d + 1) * El && e2 < e_j) ? 1 : 0;
+    }
+    if (member) row[n] = sum_j;
+    if (lane < k && lane >= members) row[lane] = 0.0f;
+}
+
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT)
+void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t* __restrict__ idx,
+                            const float* __restrict__ w, int k, int E, int El, int G,
+                            const int32_t* __restrict__ s2d, int64_t dest_rows, RankPtrs dx,
+                            RankPtrs dw, bool with_weights)
+{
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // lane d: this token's row in rank d's buffer (-1: not sent; rows past
+    // the destination capacity are never written)
+    int32_t p = lane < G ? s2d[t * G + lane] : -1;
+    if (p >= dest_rows) p = -1;
+
+    if (with_weights && tid < 64) {
+        const int64_t e64 = lane < k ? idx[t * k + lane] : -1;
+        const int32_t e_j = (e64 >= 0 && e64 < E) ? (int32_t)e64 : -1;
+        const float w_j = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
+        float sum = 0.0f;
+        bool first = e_j >= 0;
+        for (int jj = 0; jj < k; ++jj) {
+            const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
+            const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_j), jj));
+            if (e2 == e_j) {
+                sum = sum + w2;
+                if (jj < lane) first = false;
+            }
+        }
+        for (int d = 0; d < G; ++d) {
+            const int32_t pd = __builtin_amdgcn_readlane(p, d);
+            float* base = static_cast<float*>(dw.p[d]);
+            if (pd < 0 || base == nullptr) continue;
+            write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
+        }
+    }
+
+    const uint4* xr = x + t * nvec;
+    constexpr int kPass = NT * VPT;
+    const int full = nvec / kPass;
+    for (int ps = 0; ps < full; ++ps) {
+        const int vb = ps * kPass + tid;
+        uint4 buf[VPT];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) buf[u] = xr[vb + u * NT];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) keep(buf[u]);
+        for (int d = 0; d < G; ++d) {
+            const int32_t r = __builtin_amdgcn_readlane(p, d);
+            if (r < 0) continue;
+            uint4* dst = static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec + vb;
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) store_nt(dst + u * NT, buf[u]);
+        }
+    }
+    for (int v = full * kPass + tid; v < nvec; v += NT) {
+        uint4 val = xr[v];
+        keep(val);
+        for (int d = 0; d < G; ++d) {
+            const int32_t r = __builtin_amdgcn_readlane(p, d);
+            if (r >= 0) store_nt(static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec + v, val);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- combine
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void add8(float (&acc)[8], const uint4& v)
+{
+    acc[0] += bf16_lo(v.x);
+    acc[1] += bf16_hi(v.x);
+    acc[2] += bf16_lo(v.y);
+    acc[3] += bf16_hi(v.y);
+    acc[4] += bf16_lo(v.z);
+    acc[5] += bf16_hi(v.z);
+    acc[6] += bf16_lo(v.w);
+    acc[7] += bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float (&acc)[8])
+{
+    uint4 o;
+    o.x = bf16_rne(acc[0]) | (bf16_rne(acc[1]) << 16);
+    o.y = bf16_rne(acc[2]) | (bf16_rne(acc[3]) << 16);
+    o.z = bf16_rne(acc[4]) | (bf16_rne(acc[5]) << 16);
+    o.w = bf16_rne(acc[6]) | (bf16_rne(acc[7]) << 16);
+    return o;
+}
+
+// Resource over one source row (0 bytes when the rank holds no row of the
+// token: its loads return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t src_rsrc(const void* base, int32_t r, int nvec)
+{
+    const uint4* row = static_cast<const uint4*>(base) + (int64_t)(r < 0 ? 0 : r) * nvec;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(row), (short)0, r < 0 ? 0 : nvec * 16,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16_nt(__amdgpu_buffer_rsrc_t rs, int v)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, v * 16, 0, 2));
+}
+
+// Ranks in groups of 8 (loads of a group back to back), U column vectors
+// per lane per iteration.  Adding a 0 from an absent rank leaves the sum
+// unchanged: it starts at +0, so it is never -0.
+template <int NT, int U>
+__global__ __launch_bounds__(NT)
+void combine_ranked_kernel(RankPtrs src, int64_t src_rows, const int32_t* __restrict__ s2d, int nvec,
+                           int G, uint4* __restrict__ out)
+{
+    constexpr int kGroup = 8;
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    int32_t p = lane < G ? s2d[t * G + lane] : -1;
+    if (p >= src_rows) p = -1;
+    uint4* o = out + t * nvec;
+    for (int v0 = tid; v0 < nvec; v0 += NT * U) {
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+        for (int d0 = 0; d0 < G; d0 += kGroup) {
+            __amdgpu_buffer_rsrc_t rs[kGroup];
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const int d = d0 + j;
+                const int32_t r = d < G ? __builtin_amdgcn_readlane(p, d) : -1;
+                rs[j] = src_rsrc(d < G ? src.p[d] : src.p[0], r, nvec);
+            }
+            uint4 val[U][kGroup];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) val[u][j] = load16_nt(rs[j], v0 + u * NT);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < kGroup; ++j) add8(acc[u], val[u][j]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (v0 + u * NT < nvec) o[v0 + u * NT] = pack8(acc[u]);
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- launchers
+
+hipError_t launch_routing_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                              int num_experts, uint8_t* map, int32_t* num_invalid,
+                              hipStream_t stream)
+{
+    if (num_invalid != nullptr) {
+        hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, stream, num_invalid);
+        if (num_tokens == 0) return hipGetLastError();
+    }
+    if (num_tokens == 0) return hipSuccess;
+    const int W = (num_experts + 7) / 8;
+    const bool words = (W & 3) == 0 && (reinterpret_cast<uintptr_t>(map) & 3u) == 0;
+    const dim3 grid((unsigned)((num_tokens + kMapTokens - 1) / kMapTokens));
+    hipLaunchKernelGGL(routing_map_kernel, grid, dim3(kMapThreads), 0, stream, topk_idx,
+                       num_tokens, num_topk, num_experts, W, words, map, num_invalid);
+    return hipGetLastError();
+}
+
+size_t rank_layout_workspace_bytes(int64_t tokens_per_rank, int num_experts, int num_ranks)
+{
+    const int64_t R = tokens_per_rank * num_ranks;
+    const int64_t C = layout_num_chunks(R < 1 ? 1 : R);
+    const int64_t El = num_experts / num_ranks;
+    return (size_t)((num_ranks + El + 1) * C) * sizeof(int32_t);
+}
+
+hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int num_experts,
+                              int num_ranks, int rank, int k_out, int32_t* s2d,
+                              uint8_t* local_map, int32_t* recv_src, int64_t* recv_topk_idx,
+                              int32_t* expert_counts, int32_t* num_recv, int32_t* num_overflow,
+                              void* workspace, hipStream_t stream)
+{
+    const int64_t T = tokens_per_rank;
+    const int G = num_ranks;
+    const int E = num_experts;
+    const int El = E / G;
+    const int W = (E + 7) / 8;
+    const int64_t R = T * G;
+    // an empty map still writes the totals (workgroup 0 of the scatter)
+    const int64_t chunk = layout_chunk_pairs(R < 1 ? 1 : R);
+    const int C = (int)layout_num_chunks(R < 1 ? 1 : R);
+    int32_t* ws = static_cast<int32_t*>(workspace);
+    const bool words = (W & 3) == 0 && (reinterpret_cast<uintptr_t>(map) & 3u) == 0;
+    if (words) {
+        hipLaunchKernelGGL(rank_count_kernel<true>, dim3(C), dim3(kRankThreads), 0, stream, map, R,
+                           W, E, G, El, rank, k_out, chunk, C, ws);
+        hipLaunchKernelGGL(rank_scatter_kernel<true>, dim3(C), dim3(kRankThreads), 0, stream, map,
+                           R, T, W, E, G, El, rank, k_out, chunk, C, ws, s2d, local_map, recv_src,
+                           recv_topk_idx, expert_counts, num_recv, num_overflow);
+    } else {
+        hipLaunchKernelGGL(rank_count_kernel<false>, dim3(C), dim3(kRankThreads), 0, stream, map,
+                           R, W, E, G, El, rank, k_out, chunk, C, ws);
+        hipLaunchKernelGGL(rank_scatter_kernel<false>, dim3(C), dim3(kRankThreads), 0, stream, map,
+                           R, T, W, E, G, El, rank, k_out, chunk, C, ws, s2d, local_map, recv_src,
+                           recv_topk_idx, expert_counts, num_recv, num_overflow);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                                  int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                  int num_ranks, const int32_t* s2d, const RankPtrs& dest_x,
+                                  const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                  hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const dim3 grid((unsigned)num_tokens);
+    const uint4* xx = static_cast<const uint4*>(x);
+    const int El = num_experts / num_ranks;
+#define EP_DR(NT, V)                                                                            \
+    hipLaunchKernelGGL((dispatch_ranked_kernel<NT, V>), grid, dim3(NT), 0, stream, xx, nvec,    \
+                       topk_idx, topk_weights, num_topk, num_experts, El, num_ranks, s2d,        \
+                       dest_rows, dest_x, dest_w, with_weights)
+    if (nvec <= 64) {
+        EP_DR(64, 1);
+        return hipGetLastError();
+    }
+    // 128 lanes with the largest VPT <= 8 whose pass divides the row
+    // (896 = 128 * 7 at hidden 7168), else the widest that fits
+    const int fit = nvec / 128;
+    int vpt = fit < 1 ? 1 : (fit > 8 ? 8 : fit);
+    for (int v = 8; v >= 1; --v) {
+        if (nvec % (128 * v) == 0) {
+            vpt = v;
+            break;
+        }
+    }
+    switch (vpt) {
+    case 1: EP_DR(128, 1); break;
+    case 2: EP_DR(128, 2); break;
+    case 3: EP_DR(128, 3); break;
+    case 4: EP_DR(128, 4); break;
+    case 5: EP_DR(128, 5); break;
+    case 6: EP_DR(128, 6); break;
+    case 7: EP_DR(128, 7); break;
+    default: EP_DR(128, 8); break;
+    }
+#undef EP_DR
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const int32_t* s2d,
+                                 int64_t num_tokens, int hidden, int num_ranks, void* out,
+                                 hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const dim3 grid((unsigned)num_tokens);
+    uint4* oo = static_cast<uint4*>(out);
+    if (nvec <= 64)
+        hipLaunchKernelGGL((combine_ranked_kernel<64, 1>), grid, dim3(64), 0, stream, src_y,
+                           src_rows, s2d, nvec, num_ranks, oo);
+    else if (nvec < 512)
+        hipLaunchKernelGGL((combine_ranked_kernel<128, 2>), grid, dim3(128), 0, stream, src_y,
+                           src_rows, s2d, nvec, num_ranks, oo);
+    else
+        hipLaunchKernelGGL((combine_ranked_kernel<256, 2>), grid, dim3(256), 0, stream, src_y,
+                           src_rows, s2d, nvec, num_ranks, oo);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -41,12 +41,15 @@ EP_MAX_EXPERTS = 1024
 EP_MAX_TOPK = 64
 EP_MAX_HIDDEN = 65536
 EP_MAX_ALIGNMENT = 4096
+EP_MAX_RANKS = 64
 
 # every symbol include/ep.h declares
 SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspace_size",
            "ep_layout", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_dispatch_ex",
            "ep_dispatch_prequantized", "ep_combine",
-           "ep_combine_backward", "ep_dispatch_backward")
+           "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
+           "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
+           "ep_combine_ranked")
 
 
 class EpError(RuntimeError):
@@ -93,6 +96,16 @@ def lib() -> ctypes.CDLL:
         L.ep_combine_backward.restype = i32
         L.ep_dispatch_backward.argtypes = [P, P, P, i64, i32, i32, P, P, P]
         L.ep_dispatch_backward.restype = i32
+        L.ep_routing_map.argtypes = [P, i64, i32, i32, P, P, P]
+        L.ep_routing_map.restype = i32
+        L.ep_rank_layout_workspace_size.argtypes = [i64, i32, i32]
+        L.ep_rank_layout_workspace_size.restype = sz
+        L.ep_rank_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+        L.ep_rank_layout.restype = i32
+        L.ep_dispatch_ranked.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, i64, P]
+        L.ep_dispatch_ranked.restype = i32
+        L.ep_combine_ranked.argtypes = [P, i64, P, i64, i32, i32, P, P]
+        L.ep_combine_ranked.restype = i32
         _lib = L
     return _lib
 
@@ -389,3 +402,169 @@ def ep_dispatch_backward(grad_recv: torch.Tensor, grad_recv_weights: Optional[to
                                     _ptr(grad_x), _ptr(grad_topk_weights), _stream(stream))
     _check(st, "ep_dispatch_backward")
     return grad_x, grad_topk_weights
+
+
+# ------------------------------------------------- per-(token, rank) path --
+
+def ep_routing_map(topk_idx: torch.Tensor, num_experts: int, *, routing_map=None,
+                   num_invalid=None, want_invalid: bool = True, stream=None):
+    """Routing bitmap of ``topk_idx`` (int64 [T, k]): uint8 [T, ceil(E/8)],
+    bit e % 8 of byte e // 8 set iff the token selects expert e.  Returns
+    (routing_map, num_invalid int32 [1] or None)."""
+    _need(topk_idx, "topk_idx", torch.int64)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be 2-D [num_tokens, num_topk]")
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    W = (E + 7) // 8
+    dev = topk_idx.device
+    if routing_map is None:
+        routing_map = torch.empty((T, W), dtype=torch.uint8, device=dev)
+    _need(routing_map, "routing_map", torch.uint8, T * W)
+    if want_invalid and num_invalid is None:
+        num_invalid = torch.empty(1, dtype=torch.int32, device=dev)
+    if num_invalid is not None:
+        _need(num_invalid, "num_invalid", torch.int32, 1)
+    st = lib().ep_routing_map(_ptr(topk_idx), T, k, E, _ptr(routing_map), _ptr(num_invalid),
+                              _stream(stream))
+    _check(st, "ep_routing_map")
+    return routing_map, num_invalid
+
+
+def rank_layout_workspace_size(tokens_per_rank: int, num_experts: int, num_ranks: int) -> int:
+    return int(lib().ep_rank_layout_workspace_size(int(tokens_per_rank), int(num_experts),
+                                                   int(num_ranks)))
+
+
+class RankLayout:
+    """Outputs of :func:`ep_rank_layout` (device tensors)."""
+
+    FIELDS = ("sparse_to_dense", "local_map", "recv_src", "recv_topk_idx", "expert_counts",
+              "num_recv", "num_overflow")
+
+    def __init__(self, **kw):
+        self.__dict__.update(kw)
+
+
+def ep_rank_layout(global_map: torch.Tensor, tokens_per_rank: int, num_experts: int,
+                   num_ranks: int, rank: int, k_out: int, *, out: Optional[RankLayout] = None,
+                   workspace=None, stream=None) -> RankLayout:
+    """Metadata preprocessing of rank ``rank`` from the all-gathered routing
+    map (uint8 [G*T, ceil(E/8)]).  Returns a RankLayout with
+    sparse_to_dense int32 [T, G], local_map uint8 [G*T, E/G], recv_src int32
+    [G*T], recv_topk_idx int64 [G*T, k_out], expert_counts int32 [E/G],
+    num_recv int32 [1], num_overflow int32 [1]."""
+    T, E, G = int(tokens_per_rank), int(num_experts), int(num_ranks)
+    if G < 1 or E % G:
+        raise ValueError("num_experts must be a multiple of num_ranks")
+    El = E // G
+    R = G * T
+    W = (E + 7) // 8
+    _need(global_map, "global_map", torch.uint8, R * W)
+    dev = global_map.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = RankLayout(sparse_to_dense=torch.empty((T, G), **i32),
+                         local_map=torch.empty((R, El), dtype=torch.uint8, device=dev),
+                         recv_src=torch.empty(R, **i32),
+                         recv_topk_idx=torch.empty((R, int(k_out)), dtype=torch.int64, device=dev),
+                         expert_counts=torch.empty(El, **i32), num_recv=torch.empty(1, **i32),
+                         num_overflow=torch.empty(1, **i32))
+    _need(out.sparse_to_dense, "sparse_to_dense", torch.int32, T * G)
+    _need(out.local_map, "local_map", torch.uint8, R * El)
+    _need(out.recv_src, "recv_src", torch.int32, R)
+    _need(out.recv_topk_idx, "recv_topk_idx", torch.int64, R * int(k_out))
+    _need(out.expert_counts, "expert_counts", torch.int32, El)
+    _need(out.num_recv, "num_recv", torch.int32, 1)
+    if out.num_overflow is not None:
+        _need(out.num_overflow, "num_overflow", torch.int32, 1)
+    need = rank_layout_workspace_size(T, E, G)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    st = lib().ep_rank_layout(_ptr(global_map), T, E, G, int(rank), int(k_out),
+                              _ptr(out.sparse_to_dense), _ptr(out.local_map), _ptr(out.recv_src),
+                              _ptr(out.recv_topk_idx), _ptr(out.expert_counts), _ptr(out.num_recv),
+                              _ptr(out.num_overflow), _ptr(workspace), workspace.numel(),
+                              _stream(stream))
+    _check(st, "ep_rank_layout")
+    return out
+
+
+def _ptr_table(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[None if t is None else t.data_ptr() for t in tensors])
+    return arr, ctypes.addressof(arr)
+
+
+def ep_dispatch_ranked(x: torch.Tensor, sparse_to_dense: torch.Tensor, dest_x, num_experts: int,
+                       *, topk_idx: Optional[torch.Tensor] = None,
+                       topk_weights: Optional[torch.Tensor] = None, dest_weights=None,
+                       stream=None):
+    """Send the rows of ``x`` (bf16 [T, H]) once to every rank that receives
+    them: ``dest_x`` is a list of G bf16 [rows_d, H] tensors, ``dest_weights``
+    None or a list of G fp32 [rows_d, k] tensors (entries may be None; needs
+    ``topk_idx``).  Rows at or past the smallest rows_d are not written."""
+    _need(x, "x", torch.bfloat16)
+    _need(sparse_to_dense, "sparse_to_dense", torch.int32)
+    if x.dim() != 2 or sparse_to_dense.dim() != 2 or sparse_to_dense.shape[0] != x.shape[0]:
+        raise ValueError("x must be [T, H] and sparse_to_dense [T, G]")
+    T, H = x.shape
+    G = sparse_to_dense.shape[1]
+    if len(dest_x) != G:
+        raise ValueError("one destination buffer per rank")
+    for d, t in enumerate(dest_x):
+        _need(t, f"dest_x[{d}]", torch.bfloat16)
+        if t.dim() != 2 or t.shape[1] != H:
+            raise ValueError(f"dest_x[{d}] must be [rows, {H}]")
+    rows = min(int(t.shape[0]) for t in dest_x)
+    k = 1
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", torch.int64)
+        if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+            raise ValueError("topk_idx must be [T, k]")
+        k = topk_idx.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    wtab = None
+    if dest_weights is not None:
+        if topk_idx is None:
+            raise ValueError("dest_weights needs topk_idx")
+        if len(dest_weights) != G:
+            raise ValueError("one weight buffer (or None) per rank")
+        for d, t in enumerate(dest_weights):
+            if t is not None:
+                _need(t, f"dest_weights[{d}]", torch.float32, rows * k)
+        wtab = _ptr_table(dest_weights)
+    xtab = _ptr_table(dest_x)
+    st = lib().ep_dispatch_ranked(_ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k,
+                                  int(num_experts), G, _ptr(sparse_to_dense), xtab[1],
+                                  None if wtab is None else wtab[1], rows, _stream(stream))
+    _check(st, "ep_dispatch_ranked")
+    return dest_x, dest_weights
+
+
+def ep_combine_ranked(src_y, sparse_to_dense: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:
+    """out[t] = bf16(sum over ranks d holding token t of src_y[d][row]) with
+    ``src_y`` a list of G bf16 [rows_d, H] tensors; rows at or past the
+    smallest rows_d read as 0."""
+    _need(sparse_to_dense, "sparse_to_dense", torch.int32)
+    if sparse_to_dense.dim() != 2:
+        raise ValueError("sparse_to_dense must be [T, G]")
+    T, G = sparse_to_dense.shape
+    if len(src_y) != G:
+        raise ValueError("one source buffer per rank")
+    H = None
+    for d, t in enumerate(src_y):
+        _need(t, f"src_y[{d}]", torch.bfloat16)
+        if t.dim() != 2 or (H is not None and t.shape[1] != H):
+            raise ValueError("every src_y must be [rows, H] with the same H")
+        H = t.shape[1]
+    rows = min(int(t.shape[0]) for t in src_y)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=sparse_to_dense.device)
+    _need(out, "out", torch.bfloat16, T * H)
+    ytab = _ptr_table(src_y)
+    st = lib().ep_combine_ranked(ytab[1], rows, _ptr(sparse_to_dense), T, H, G, _ptr(out),
+                                 _stream(stream))
+    _check(st, "ep_combine_ranked")
+    return out

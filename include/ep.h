@@ -82,6 +82,7 @@ typedef enum {
 #define EP_MAX_TOPK 64
 #define EP_MAX_HIDDEN 65536
 #define EP_MAX_ALIGNMENT 4096
+#define EP_MAX_RANKS 64
 
 /* Library version, (major << 16) | minor. */
 int ep_version(void);
@@ -330,6 +331,114 @@ int ep_combine_backward(const void *grad_out, const void *y, const int32_t *slot
 int ep_dispatch_backward(const void *grad_recv, const float *grad_recv_weights,
                          const int32_t *slot, int64_t num_tokens, int hidden, int num_topk,
                          void *grad_x, float *grad_topk_weights, void *stream);
+
+/*
+ * ---- The per-(token, rank) path: a token travels once to each rank that
+ * owns any of its experts.
+ *
+ * Passages: NCCL EP page, nccl_ep.cc: the high-throughput handle's routing
+ * structures (the all-gathered routing bitmap, one bit per expert and eight
+ * experts per byte; sparse_to_dense_map, the row of a (token, destination
+ * rank) pair in that rank's buffer, -1 when not routed;
+ * local_expert_routing_map, which local experts each received token
+ * selects; num_tokens_for_experts, received tokens counted once per rank),
+ * ncclEpCreateHandle's high-throughput branch (Step 1 bitmap, Step 2
+ * all-gather, Step 3 metadata preprocessing with the per-expert receive
+ * counter), and the high-throughput branches of ncclEpDispatch and
+ * ncclEpCombine.
+ *
+ * Notation: G ranks (1..EP_MAX_RANKS, dividing E); rank d owns experts
+ * [d*El, (d+1)*El), El = E / G.  Every rank contributes T rows to the
+ * all-gathered map [G*T, W], W = ceil(E/8) bytes a row; global token
+ * g = s*T + t is token t of rank s.  Rank d's receive buffer lists the
+ * tokens that select any of its experts, once each, in increasing g.
+ */
+
+/*
+ * ep_routing_map -- Step 1: the routing bitmap of one rank's tokens.
+ * In:  topk_idx  int64 [num_tokens, num_topk], -1 = masked.
+ * Out: routing_map  bytes [num_tokens, ceil(num_experts/8)]: bit e % 8 of
+ *                   byte e / 8 of row t is 1 iff some slot of token t
+ *                   selects expert e (duplicates select it once).
+ *      num_invalid  int32 [1] or NULL: entries outside [-1, E).
+ * Requires num_tokens * num_topk < 2^31, 1 <= num_topk <= EP_MAX_TOPK,
+ * 1 <= num_experts <= EP_MAX_EXPERTS.
+ */
+int ep_routing_map(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                   uint8_t *routing_map, int32_t *num_invalid, void *stream);
+
+/* Bytes of device workspace ep_rank_layout needs (int32 counts per chunk of
+ * 1024 or more global tokens). */
+size_t ep_rank_layout_workspace_size(int64_t tokens_per_rank, int num_experts, int num_ranks);
+
+/*
+ * ep_rank_layout -- Step 3 (metadata preprocessing) for rank `rank`.
+ * In:  global_routing_map  bytes [G*T, W]: every rank's ep_routing_map rows,
+ *                          rank s's at rows [s*T, (s+1)*T) (a rank with
+ *                          fewer tokens pads with zero rows).
+ *      k_out               width of recv_topk_idx, 1..EP_MAX_TOPK (num_topk
+ *                          is always wide enough).
+ * Out: sparse_to_dense_map  int32 [T, G]: row of this rank's token t in rank
+ *                           d's buffer, -1 if t selects none of d's experts.
+ *      num_recv             int32 [1]: tokens this rank receives.
+ *      for received row i < num_recv (global token g):
+ *        local_expert_routing_map  bytes [G*T, El]: 1 iff g selects local
+ *                                  expert e (expert rank*El + e), else 0;
+ *        recv_src                  int32 [G*T]: g;
+ *        recv_topk_idx             int64 [G*T, k_out]: the selected local
+ *                                  experts in increasing order, then -1;
+ *      rows num_recv .. G*T-1: local map 0, recv_src -1, recv_topk_idx -1,
+ *      so the three can be used at their full G*T rows (ep_layout over
+ *      recv_topk_idx with E = El groups the received rows by local expert).
+ *      expert_counts            int32 [El]: received tokens per local expert.
+ *      num_overflow             int32 [1] or NULL: selections past k_out
+ *                               (dropped from recv_topk_idx only).
+ *      workspace                ep_rank_layout_workspace_size bytes, device.
+ * Requires G*T < 2^31; local_expert_routing_map 4-byte aligned.
+ */
+int ep_rank_layout(const uint8_t *global_routing_map, int64_t tokens_per_rank, int num_experts,
+                   int num_ranks, int rank, int k_out, int32_t *sparse_to_dense_map,
+                   uint8_t *local_expert_routing_map, int32_t *recv_src, int64_t *recv_topk_idx,
+                   int32_t *expert_counts, int32_t *num_recv, int32_t *num_overflow,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ep_dispatch_ranked -- send this rank's tokens, once per destination rank.
+ * In:  x                    bf16 [num_tokens, hidden].
+ *      topk_idx, topk_weights  int64 / fp32 [num_tokens, num_topk]; read
+ *                           only for dest_weights (topk_weights NULL = 1).
+ *      sparse_to_dense_map  int32 [num_tokens, G] from ep_rank_layout.
+ *      dest_x               HOST array of G device pointers: rank d's
+ *                           receive buffer, bf16 [dest_rows, hidden] (on
+ *                           one device, or peer memory mapped into it).
+ *      dest_weights         NULL, or HOST array of G device pointers (an
+ *                           entry may be NULL): fp32 [dest_rows, num_topk].
+ * Out: dest_x[d][row] = x[t] for row = sparse_to_dense_map[t, d] >= 0;
+ *      dest_weights[d][row, n] = the fp32 sum, in increasing slot order, of
+ *      the weights of the slots selecting the n-th selected expert of rank d
+ *      (increasing expert id, the order of recv_topk_idx), 0 past the last.
+ *      Rows >= dest_rows are never written (G*T rows always suffice).
+ * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int num_ranks, const int32_t *sparse_to_dense_map, void *const *dest_x,
+                       float *const *dest_weights, int64_t dest_rows, void *stream);
+
+/*
+ * ep_combine_ranked -- gather this rank's tokens back from every rank.
+ * In:  src_y                HOST array of G device pointers: rank d's
+ *                           per-token outputs, bf16 [src_rows, hidden] (each
+ *                           already reduced over d's experts, weighted).
+ *      sparse_to_dense_map  int32 [num_tokens, G] from ep_rank_layout.
+ * Out: out  bf16 [num_tokens, hidden]: bf16_rne of the fp32 sum, in
+ *      increasing d, of src_y[d][sparse_to_dense_map[t, d]] over the ranks
+ *      that hold the token (rows >= src_rows read as 0); +0 if none.
+ * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
+ */
+int ep_combine_ranked(const void *const *src_y, int64_t src_rows,
+                      const int32_t *sparse_to_dense_map, int64_t num_tokens, int hidden,
+                      int num_ranks, void *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -171,3 +171,116 @@ def test_layout_ex_rejects(A, cap, T, code):
     st = ep.lib().ep_layout_ex(FAKE, T, 2, 256, A, cap, FAKE, FAKE, FAKE, None, None, None,
                                FAKE, 1 << 30, None)
     assert st == code, ep.last_error()
+
+
+# ---- per-(token, rank) path
+
+def test_rank_layout_workspace_size():
+    # (G + E/G + 1) int32 per chunk of global tokens, 256-byte aligned
+    def want(chunks, G, El):
+        return ((G + El + 1) * chunks * 4 + 255) // 256 * 256
+    assert ep.rank_layout_workspace_size(8192, 256, 8) == want(64, 8, 32)
+    assert ep.rank_layout_workspace_size(0, 256, 8) == want(1, 8, 32)
+    assert ep.rank_layout_workspace_size(8192, 256, 1) == want(8, 1, 256)
+    assert ep.rank_layout_workspace_size(65536, 64, 64) == want(256, 64, 1)
+    assert ep.rank_layout_workspace_size(10, 256, 3) == 0        # E % G
+    assert ep.rank_layout_workspace_size(10, 256, 65) == 0
+    assert ep.rank_layout_workspace_size(10, 0, 1) == 0
+    assert ep.rank_layout_workspace_size(-1, 8, 2) == 0
+
+
+@no_gpu
+@pytest.mark.parametrize("args,code", [
+    # (topk_idx, T, k, E, routing_map, num_invalid)
+    ((FAKE, 4, 2, 0, FAKE, None), 1),             # E < 1
+    ((FAKE, 4, 2, 1025, FAKE, None), 1),          # E too large
+    ((FAKE, 4, 0, 8, FAKE, None), 1),             # k < 1
+    ((FAKE, -1, 2, 8, FAKE, None), 1),            # T < 0
+    ((FAKE, 1 << 28, 8, 8, FAKE, None), 2),       # pairs >= 2^31
+    ((None, 4, 2, 8, FAKE, None), 1),             # no topk_idx
+    ((FAKE, 4, 2, 8, None, None), 1),             # no map
+    ((FAKE + 4, 4, 2, 8, FAKE, None), 1),         # idx misaligned
+    ((FAKE, 4, 2, 8, FAKE, FAKE + 2), 1),         # num_invalid misaligned
+])
+def test_routing_map_rejects(args, code):
+    st = ep.lib().ep_routing_map(*args, None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def _rank_layout_args(**over):
+    a = dict(map=FAKE, T=4, E=8, G=2, rank=0, k_out=2, s2d=FAKE, lm=FAKE, src=FAKE, rti=FAKE,
+             counts=FAKE, nrecv=FAKE, novf=None, ws=FAKE, ws_bytes=1 << 20)
+    a.update(over)
+    return tuple(a.values())
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(G=65, E=130), 1), (dict(E=9), 1), (dict(E=1026, G=2), 1),
+    (dict(rank=-1), 1), (dict(rank=2), 1), (dict(k_out=0), 1), (dict(k_out=65), 1),
+    (dict(T=-1), 1), (dict(T=1 << 28, G=8), 2),
+    (dict(counts=None), 1), (dict(nrecv=None), 1), (dict(map=None), 1), (dict(s2d=None), 1),
+    (dict(lm=None), 1), (dict(src=None), 1), (dict(rti=None), 1),
+    (dict(lm=FAKE + 1), 1), (dict(s2d=FAKE + 2), 1), (dict(rti=FAKE + 4), 1),
+    (dict(ws=None), 1), (dict(ws=FAKE + 16), 1), (dict(ws_bytes=16), 1),
+])
+def test_rank_layout_rejects(over, code):
+    st = ep.lib().ep_rank_layout(*_rank_layout_args(**over), None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def _table(*ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return arr
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(H=12), 1), (dict(k=0), 1), (dict(G=65, E=130), 1), (dict(E=9), 1),
+    (dict(rows=-1), 1), (dict(dx="none"), 1), (dict(dx=(FAKE, None)), 1),
+    (dict(dx=(FAKE, FAKE + 8)), 1), (dict(dw=(FAKE, FAKE + 2)), 1), (dict(x=None), 1),
+    (dict(s2d=None), 1), (dict(x=FAKE + 8), 1), (dict(dw=(FAKE, FAKE), idx=None), 1),
+    (dict(idx=FAKE + 4, dw=(FAKE, None)), 1), (dict(T=1 << 28, k=8), 2),
+])
+def test_dispatch_ranked_rejects(over, code):
+    a = dict(x=FAKE, idx=FAKE, w=None, T=4, H=256, k=2, E=8, G=2, s2d=FAKE, dx=(FAKE, FAKE),
+             dw=None, rows=16)
+    a.update(over)
+    dx = None if a["dx"] == "none" else _table(*a["dx"])
+    dw = None if a["dw"] is None else _table(*a["dw"])
+    keep = (dx, dw)
+    st = ep.lib().ep_dispatch_ranked(a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"],
+                                     a["G"], a["s2d"],
+                                     None if dx is None else ctypes.addressof(dx),
+                                     None if dw is None else ctypes.addressof(dw), a["rows"], None)
+    del keep
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(G=65), 1), (dict(H=20), 1), (dict(rows=-1), 1), (dict(T=-1), 1),
+    (dict(src="none"), 1), (dict(src=(FAKE, None)), 1), (dict(src=(FAKE, FAKE + 4)), 1),
+    (dict(s2d=None), 1), (dict(out=None), 1), (dict(out=FAKE + 8), 1),
+    (dict(T=1 << 28, G=8, src=(FAKE,) * 8), 2),
+])
+def test_combine_ranked_rejects(over, code):
+    a = dict(src=(FAKE, FAKE), rows=16, s2d=FAKE, T=4, H=256, G=2, out=FAKE)
+    a.update(over)
+    src = None if a["src"] == "none" else _table(*a["src"])
+    st = ep.lib().ep_combine_ranked(None if src is None else ctypes.addressof(src), a["rows"],
+                                    a["s2d"], a["T"], a["H"], a["G"], a["out"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_ranked_zero_tokens_are_noops():
+    dx = _table(FAKE, FAKE)
+    assert ep.lib().ep_dispatch_ranked(None, None, None, 0, 256, 2, 8, 2, None,
+                                       ctypes.addressof(dx), None, 0, None) == 0
+    assert ep.lib().ep_combine_ranked(ctypes.addressof(dx), 0, None, 0, 256, 2, None, None) == 0
+    assert ep.lib().ep_routing_map(None, 0, 2, 8, None, None, None) == 0
+    assert ep.last_error() == ""
