@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     "dispatch_fp8_e5m2_fp32": "ep_dispatch.hip", "dispatch_fp8_e4m3_pow2": "ep_dispatch.hip",
     "dispatch_fp8_e4m3_ue8m0": "ep_dispatch.hip", "dispatch_fp8_e5m2_ue8m0": "ep_dispatch.hip",
     "dispatch_fp8_prequantized": "ep_dispatch.hip",
+    "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
+    "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -88,6 +90,18 @@ def bytes_model(T, H, k, n):
         "dispatch_backward": n * H * 2 + T * H * 2 + T * k * 4 + n * 4 + T * k * 4,
         # read topk_idx, write slot and src
         "layout": T * k * 8 + T * k * 4 + n * 4,
+    }
+
+
+def ranked_bytes_model(T, H, k, G, pairs):
+    """Algorithmic bytes of the per-(token, rank) path for one rank's T
+    tokens sent to ``pairs`` (token, destination rank) rows."""
+    return {
+        # read x once, write each (token, rank) row once, read the
+        # sparse-to-dense rows, topk_idx and weights, write the weight rows
+        "dispatch_ranked": T * H * 2 + pairs * H * 2 + T * G * 4 + T * k * 12 + pairs * k * 4,
+        # read each (token, rank) row once, write out, read sparse-to-dense
+        "combine_ranked": pairs * H * 2 + T * H * 2 + T * G * 4,
     }
 
 
@@ -329,6 +343,61 @@ def main():
         xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
         sc.data_ptr(), None, s), "ep_dispatch_prequantized"), args.steps)
 
+    # ---- per-(token, rank) path: G = 8 ranks of the headline shape on this
+    # device (rank 0 holds the headline tokens, ranks 1..7 uniform routing);
+    # rank 0's share is timed: its routing bitmap, its layout over the
+    # all-gathered map, the dispatch of its tokens once per destination rank
+    # and the combine over ranks
+    from combine_ep_layout_04_amd.inputs import make_routing
+    import ctypes
+    G = 8
+    El = E // G
+    W8 = (E + 7) // 8
+    log(f"[bench] per-rank path, {G} ranks")
+    with torch.cuda.stream(stream):
+        gmap = torch.empty((G * T, W8), dtype=torch.uint8, device=dev)
+        others = [torch.from_numpy(make_routing(T, E, k, 100 + r)).to(dev) for r in range(1, G)]
+        rl = dict(s2d=torch.empty((T, G), **i32), lm=torch.empty((G * T, El), dtype=torch.uint8, device=dev),
+                  rsrc=torch.empty(G * T, **i32), rti=torch.empty((G * T, k), dtype=torch.int64, device=dev),
+                  ecnt=torch.empty(El, **i32), nrecv=torch.empty(1, **i32), novf=torch.empty(1, **i32))
+        rl_ws_bytes = ep.rank_layout_workspace_size(T, E, G)
+        rl_ws = torch.empty(rl_ws_bytes, dtype=torch.uint8, device=dev)
+    stream.synchronize()
+    for r in range(1, G):
+        check(L.ep_routing_map(others[r - 1].data_ptr(), T, k, E, gmap[r * T].data_ptr(), None, s),
+              "ep_routing_map")
+    rm_us = time_call(lambda: check(L.ep_routing_map(p["idx"], T, k, E, gmap.data_ptr(), None, s),
+                                    "ep_routing_map"), args.steps)
+    rq = {n: t.data_ptr() for n, t in rl.items()}
+    rk_us = time_call(lambda: check(L.ep_rank_layout(
+        gmap.data_ptr(), T, E, G, 0, k, rq["s2d"], rq["lm"], rq["rsrc"], rq["rti"], rq["ecnt"],
+        rq["nrecv"], rq["novf"], rl_ws.data_ptr(), rl_ws_bytes, s), "ep_rank_layout"), args.steps)
+    stream.synchronize()
+    s2d_h = rl["s2d"].cpu()
+    pairs = int((s2d_h >= 0).sum())
+    # rank 0's tokens come first in every receive buffer, so T rows hold them
+    assert int(s2d_h.max()) < T
+    with torch.cuda.stream(stream):
+        dest = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(G)]
+        dest_w = [torch.empty((T, k), dtype=torch.float32, device=dev) for _ in range(G)]
+        out_r = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream.synchronize()
+    xtab = (ctypes.c_void_p * G)(*[t.data_ptr() for t in dest])
+    wtab = (ctypes.c_void_p * G)(*[t.data_ptr() for t in dest_w])
+    dr_us = time_call(lambda: check(L.ep_dispatch_ranked(
+        p["x"], p["idx"], p["wt"], T, H, k, E, G, rq["s2d"], ctypes.addressof(xtab),
+        ctypes.addressof(wtab), T, s), "ep_dispatch_ranked"), args.steps)
+    # the combine over ranks reads back the rows just dispatched (each rank's
+    # "partial output" of a token is the token itself): out[t] = bf16(n_t x[t])
+    cr_us = time_call(lambda: check(L.ep_combine_ranked(
+        ctypes.addressof(xtab), T, rq["s2d"], T, H, G, out_r.data_ptr(), s),
+        "ep_combine_ranked"), args.steps)
+    stream.synchronize()
+    n_t = (s2d_h >= 0).sum(dim=1).to(dev).view(T, 1).float()
+    ranked_ok = bool(torch.equal(out_r, (x.float() * n_t).bfloat16()))
+    rbm = ranked_bytes_model(T, H, k, G, pairs)
+    del dest, dest_w
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly 1 GiB each
         a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
@@ -352,6 +421,12 @@ def main():
                                                  ("dispatch_prequantized" if name == "prequantized"
                                                   else "dispatch_fp8")]}
            for name, v in variants.items()},
+        "routing_map": {"us": round(rm_us, 2)},
+        "rank_layout": {"us": round(rk_us, 2), "ranks": G},
+        "dispatch_ranked": {"us": round(dr_us, 2), "bytes": rbm["dispatch_ranked"], "ranks": G,
+                            "rows_written": pairs, "expanded_rows": n},
+        "combine_ranked": {"us": round(cr_us, 2), "bytes": rbm["combine_ranked"], "ranks": G,
+                           "rows_read": pairs},
         "layout_aligned128": {"us": round(lay_a128, 2)},
         "layout_capacity320": {"us": round(lay_cap, 2), "dropped_pairs": dropped_cap},
     }
@@ -398,6 +473,7 @@ def main():
                      "traffic": read_traffic(dom)},
         "kernels": per_kernel,
         "combine_returns_x": ok,
+        "ranked_combine_returns_n_x": ranked_ok,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -19,16 +19,19 @@
 // Kernels (all deterministic: atomics only ever OR bits or add counts):
 //   routing map:  one workgroup per 64 tokens ORs every slot's bit into an
 //                 LDS copy of the rows, then writes the rows out whole.
-//   rank count:   one workgroup per chunk of global tokens counts, for every
-//                 rank, the chunk's tokens it receives (wavefront ballots),
-//                 and for the local rank the received tokens per local
-//                 expert and the selections past k_out.
-//   rank scatter: each workgroup sums the earlier chunks' counts, then walks
-//                 its chunk in batches of 256 tokens; a token's row in rank
-//                 d's buffer is that base plus its ballot prefix count in
-//                 the batch.  It writes sparse_to_dense for the local rank's
-//                 tokens and the receive-side rows; all workgroups clear the
-//                 rows past the received count; workgroup 0 writes totals.
+//   rank count:   one workgroup per chunk of 256 global tokens (more once
+//                 there would be over 256 chunks) counts, for every rank,
+//                 the chunk's tokens it receives (wavefront ballots over a
+//                 per-token rank mask; map rows of up to 8 words stay in
+//                 registers, an LDS table gives each expert's rank).
+//   rank scatter: each workgroup sums the earlier chunks' counts (all its
+//                 threads, contiguous loads), then walks its chunk in
+//                 batches of 256 tokens; a token's row in rank d's buffer
+//                 is that base plus its ballot prefix count in the batch.
+//                 It writes sparse_to_dense for the local rank's tokens and
+//                 the receive-side rows, adds its chunk's per-expert counts
+//                 (integer sums: order-free), and all workgroups clear the
+//                 rows past the received count.
 //   dispatch:     one workgroup per token reads the row once into registers
 //                 and stores it, non-temporally, to every rank that receives
 //                 it (a table of G row pointers passed by value), with the
@@ -101,45 +104,77 @@ __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 // ------------------------------------------------------------ rank layout
 
-// 32 bits of a map row starting at bit p (little-endian bit order); bytes
-// past the row end read as 0.
-__device__ __forceinline__ uint32_t row_bits32(const uint8_t* row, int W, int p)
-{
-    const int b0 = p >> 3;
-    uint64_t v = 0;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const int b = b0 + i;
-        if (b < W) v |= (uint64_t)row[b] << (8 * i);
-    }
-    return (uint32_t)(v >> (p & 7));
-}
+// One map row.  NW > 0: the row is NW 32-bit words (rows 4-byte aligned)
+// held in registers; NW == 0: any width, read from memory byte by byte.
+template <int NW>
+struct MapRow {
+    uint32_t w[NW > 0 ? NW : 1];
+    const uint8_t* row;
+    int W;
 
-// Bit i of the result: the token selects an expert of rank i.
-template <bool WORDS>
-__device__ __forceinline__ uint64_t rank_mask(const uint8_t* row, int W, int E, int El)
+    __device__ __forceinline__ void load(const uint8_t* r, int W_, bool live)
+    {
+        row = r;
+        W = W_;
+        if constexpr (NW > 0) {
+            const uint32_t* r32 = reinterpret_cast<const uint32_t*>(r);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) w[i] = live ? r32[i] : 0u;
+        }
+    }
+
+    __device__ __forceinline__ uint32_t word(int i) const
+    {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) v = (i == j) ? w[j] : v;
+        return v;
+    }
+
+    // 32 bits starting at bit p (little-endian bit order), 0 past the row.
+    __device__ __forceinline__ uint32_t bits32(int p) const
+    {
+        if constexpr (NW > 0) {
+            const int i = p >> 5;
+            const int sh = p & 31;
+            const uint32_t lo = word(i);
+            const uint32_t hi = word(i + 1);
+            return sh == 0 ? lo : ((lo >> sh) | (hi << (32 - sh)));
+        } else {
+            const int b0 = p >> 3;
+            uint64_t v = 0;
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const int b = b0 + i;
+                if (b < W) v |= (uint64_t)row[b] << (8 * i);
+            }
+            return (uint32_t)(v >> (p & 7));
+        }
+    }
+};
+
+// Bit d of the result: the token selects an expert of rank d.  rank_of is
+// the LDS table expert -> rank.
+template <int NW>
+__device__ __forceinline__ uint64_t rank_mask(const MapRow<NW>& r, int E, const uint8_t* rank_of)
 {
     uint64_t m = 0;
-    for (int p = 0; p < E; p += 32) {
-        uint32_t w = WORDS ? reinterpret_cast<const uint32_t*>(row)[p >> 5] : row_bits32(row, W, p);
-        if (E - p < 32) w &= (1u << (E - p)) - 1u;
-        while (w != 0u) {
-            const int b = __builtin_ctz(w);
-            w &= w - 1u;
-            m |= 1ull << ((p + b) / El);
+    const int nwin = NW > 0 ? NW : (E + 31) / 32;
+#pragma unroll
+    for (int i = 0; i < (NW > 0 ? NW : 1); ++i) {
+        for (int ii = (NW > 0 ? i : 0); ii < (NW > 0 ? i + 1 : nwin); ++ii) {
+            const int p = ii * 32;
+            uint32_t w = NW > 0 ? r.w[i] : r.bits32(p);
+            if (p >= E) w = 0u;
+            else if (E - p < 32) w &= (1u << (E - p)) - 1u;
+            while (w != 0u) {
+                const int e = p + __builtin_ctz(w);
+                w &= w - 1u;
+                m |= 1ull << rank_of[e];
+            }
         }
     }
     return m;
-}
-
-// Bits [q, q + 32) of the local rank's expert block (bit e = local expert
-// e), masked to the block.
-__device__ __forceinline__ uint32_t local_bits(const uint8_t* row, int W, int first, int El, int q)
-{
-    uint32_t w = row_bits32(row, W, first + q);
-    const int nb = El - q;
-    if (nb < 32) w &= (1u << nb) - 1u;
-    return w;
 }
 
 __device__ __forceinline__ int popc64(uint64_t v) { return __builtin_popcountll(v); }
@@ -150,55 +185,49 @@ __device__ __forceinline__ uint64_t lanes_below()
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Workspace: cnt[d][c] (G x C), ecnt[e][c] (El x C), ovf[c] (C), int32.
-template <bool WORDS>
+__device__ __forceinline__ void fill_rank_table(uint8_t* rank_of, int E, int El)
+{
+    for (int e = threadIdx.x; e < E; e += kRankThreads) rank_of[e] = (uint8_t)(e / El);
+}
+
+// Workspace: cnt[c][d], the tokens of chunk c that rank d receives (C x G
+// int32, chunk-major so a workgroup's prefix reads are contiguous).
+// Workgroup 0 also clears the per-expert and overflow totals the scatter
+// adds into (stream order puts every clear before every add).
+template <int NW>
 __global__ __launch_bounds__(kRankThreads)
 void rank_count_kernel(const uint8_t* __restrict__ map, int64_t R, int W, int E, int G, int El,
-                       int rank, int k_out, int64_t chunk, int C, int32_t* __restrict__ ws)
+                       int64_t chunk, int32_t* __restrict__ cnt, int32_t* __restrict__ expert_counts,
+                       int32_t* __restrict__ num_overflow)
 {
     __shared__ int32_t s_cnt[kMaxRanks];
-    __shared__ int32_t s_ecnt[kMaxExperts];
-    __shared__ int32_t s_ovf;
+    __shared__ uint8_t s_rank_of[kMaxExperts];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int c = blockIdx.x;
-    for (int i = tid; i < G; i += kRankThreads) s_cnt[i] = 0;
-    for (int i = tid; i < El; i += kRankThreads) s_ecnt[i] = 0;
-    if (tid == 0) s_ovf = 0;
+    if (tid < G) s_cnt[tid] = 0;
+    fill_rank_table(s_rank_of, E, El);
+    if (c == 0) {
+        for (int e = tid; e < El; e += kRankThreads) expert_counts[e] = 0;
+        if (tid == 0 && num_overflow != nullptr) *num_overflow = 0;
+    }
     __syncthreads();
 
     const int64_t g0 = (int64_t)c * chunk;
     const int64_t g1 = min(R, g0 + chunk);
-    int ovf = 0;
     for (int64_t b = g0; b < g1; b += kRankThreads) {
         const int64_t g = b + tid;
         const bool live = g < g1;
-        const uint8_t* row = map + g * W;
-        const uint64_t m = live ? rank_mask<WORDS>(row, W, E, El) : 0ull;
+        MapRow<NW> row;
+        row.load(map + (live ? g : g0) * W, W, live);
+        const uint64_t m = live ? rank_mask<NW>(row, E, s_rank_of) : 0ull;
         for (int d = 0; d < G; ++d) {
             const uint64_t bal = __ballot((m >> d) & 1ull);
             if (lane == 0 && bal != 0ull) atomicAdd(&s_cnt[d], popc64(bal));
         }
-        if ((m >> rank) & 1ull) {
-            int n = 0;
-            for (int q = 0; q < El; q += 32) {
-                uint32_t w = local_bits(row, W, rank * El, El, q);
-                n += __builtin_popcount(w);
-                while (w != 0u) {
-                    const int e = q + __builtin_ctz(w);
-                    w &= w - 1u;
-                    atomicAdd(&s_ecnt[e], 1);
-                }
-            }
-            ovf += n > k_out ? n - k_out : 0;
-        }
     }
-    if (ovf != 0) atomicAdd(&s_ovf, ovf);
     __syncthreads();
-    for (int i = tid; i < G; i += kRankThreads) ws[(int64_t)i * C + c] = s_cnt[i];
-    int32_t* ecnt = ws + (int64_t)G * C;
-    for (int i = tid; i < El; i += kRankThreads) ecnt[(int64_t)i * C + c] = s_ecnt[i];
-    if (tid == 0) ws[(int64_t)(G + El) * C + c] = s_ovf;
+    if (tid < G) cnt[(int64_t)c * G + tid] = s_cnt[tid];
 }
 
 // Four local-map bytes (0 or 1) from four bits.
@@ -207,61 +236,66 @@ __device__ __forceinline__ uint32_t spread4(uint32_t b)
     return (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
 }
 
-template <bool WORDS>
+template <int NW>
 __global__ __launch_bounds__(kRankThreads)
 void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, int W, int E,
                          int G, int El, int rank, int k_out, int64_t chunk, int C,
-                         const int32_t* __restrict__ ws, int32_t* __restrict__ s2d,
+                         const int32_t* __restrict__ cnt, int32_t* __restrict__ s2d,
                          uint8_t* __restrict__ local_map, int32_t* __restrict__ recv_src,
                          int64_t* __restrict__ recv_topk_idx, int32_t* __restrict__ expert_counts,
                          int32_t* __restrict__ num_recv, int32_t* __restrict__ num_overflow)
 {
     __shared__ int32_t s_base[kMaxRanks];
     __shared__ int32_t s_wave[kRankWaves][kMaxRanks];
+    __shared__ int32_t s_ecnt[kMaxExperts];
+    __shared__ uint8_t s_rank_of[kMaxExperts];
     __shared__ int32_t s_nrecv;
+    __shared__ int32_t s_ovf;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c = blockIdx.x;
-    const int32_t* cnt = ws;
-    const int32_t* ecnt = ws + (int64_t)G * C;
-    const int32_t* ovf = ws + (int64_t)(G + El) * C;
-
-    // rows of each rank's buffer taken by earlier chunks; the received total
-    for (int d = tid; d < G; d += kRankThreads) {
-        int32_t s = 0;
-        for (int cc = 0; cc < c; ++cc) s += cnt[(int64_t)d * C + cc];
-        s_base[d] = s;
-    }
+    if (tid < G) s_base[tid] = 0;
     if (tid == 0) {
-        int32_t s = 0;
-        for (int cc = 0; cc < C; ++cc) s += cnt[(int64_t)rank * C + cc];
-        s_nrecv = s;
+        s_nrecv = 0;
+        s_ovf = 0;
     }
-    if (c == 0) {
-        for (int e = tid; e < El; e += kRankThreads) {
-            int32_t s = 0;
-            for (int cc = 0; cc < C; ++cc) s += ecnt[(int64_t)e * C + cc];
-            expert_counts[e] = s;
-        }
-        if (tid == 0 && num_overflow != nullptr) {
-            int32_t s = 0;
-            for (int cc = 0; cc < C; ++cc) s += ovf[cc];
-            *num_overflow = s;
+    for (int e = tid; e < El; e += kRankThreads) s_ecnt[e] = 0;
+    fill_rank_table(s_rank_of, E, El);
+    __syncthreads();
+
+    // Rows of each rank's buffer taken by earlier chunks, and the local
+    // rank's received total: thread (d, j) sums column d of chunks j, j + S,
+    // j + 2S, ... (S = 256 / G threads per rank, contiguous loads).
+    {
+        const int S = kRankThreads / G;
+        if (tid < S * G) {
+            const int d = tid % G;
+            int32_t before = 0, all = 0;
+            for (int cc = tid / G; cc < C; cc += S) {
+                const int32_t v = cnt[(int64_t)cc * G + d];
+                before += cc < c ? v : 0;
+                all += v;
+            }
+            if (before != 0) atomicAdd(&s_base[d], before);
+            if (d == rank && all != 0) atomicAdd(&s_nrecv, all);
         }
     }
     __syncthreads();
     if (c == 0 && tid == 0) *num_recv = s_nrecv;
 
     const bool map4 = (El & 3) == 0;
+    const int first = rank * El;
     const int64_t g0 = (int64_t)c * chunk;
     const int64_t g1 = min(R, g0 + chunk);
     const int64_t mine0 = (int64_t)rank * T;
+    int ovf = 0;
     for (int64_t b = g0; b < g1; b += kRankThreads) {
         const int64_t g = b + tid;
         const bool live = g < g1;
-        const uint8_t* row = map + g * W;
-        const uint64_t m = live ? rank_mask<WORDS>(row, W, E, El) : 0ull;
+        MapRow<NW> row;
+        row.load(map + (live ? g : g0) * W, W, live);
+        const uint64_t m = live ? rank_mask<NW>(row, E, s_rank_of) : 0ull;
         for (int d = 0; d < G; ++d) {
             const uint64_t bal = __ballot((m >> d) & 1ull);
             if (lane == 0) s_wave[wave][d] = popc64(bal);
@@ -281,8 +315,9 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
                 uint8_t* lm = local_map + (int64_t)pos * El;
                 int n = 0;
                 for (int q = 0; q < El; q += 32) {
-                    uint32_t wbits = local_bits(row, W, rank * El, El, q);
+                    uint32_t wbits = row.bits32(first + q);
                     const int nb = min(32, El - q);
+                    if (nb < 32) wbits &= (1u << nb) - 1u;
                     if (map4) {
                         for (int i = 0; i < nb; i += 4)
                             *reinterpret_cast<uint32_t*>(lm + q + i) = spread4((wbits >> i) & 15u);
@@ -292,21 +327,29 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
                     while (wbits != 0u) {
                         const int e = q + __builtin_ctz(wbits);
                         wbits &= wbits - 1u;
+                        atomicAdd(&s_ecnt[e], 1);
                         if (n < k_out) topk[n] = e;
                         ++n;
                     }
                 }
+                ovf += n > k_out ? n - k_out : 0;
                 for (; n < k_out; ++n) topk[n] = -1;
             }
         }
         __syncthreads();
         if (tid < G) {
-            int32_t s = 0;
-            for (int w = 0; w < kRankWaves; ++w) s += s_wave[w][tid];
-            s_base[tid] += s;
+            int32_t sum = 0;
+            for (int w = 0; w < kRankWaves; ++w) sum += s_wave[w][tid];
+            s_base[tid] += sum;
         }
         __syncthreads();
     }
+    if (ovf != 0) atomicAdd(&s_ovf, ovf);
+    __syncthreads();
+    // this chunk's receive-side totals (the count kernel cleared them)
+    for (int e = tid; e < El; e += kRankThreads)
+        if (s_ecnt[e] != 0) atomicAdd(&expert_counts[e], s_ecnt[e]);
+    if (tid == 0 && s_ovf != 0 && num_overflow != nullptr) atomicAdd(num_overflow, s_ovf);
 
     // rows past the received count: no source, no local expert
     const int64_t nrecv = s_nrecv;
@@ -539,12 +582,35 @@ hipError_t launch_routing_map(const int64_t* topk_idx, int64_t num_tokens, int n
     return hipGetLastError();
 }
 
+// Chunks of global tokens for the rank layout: 256 tokens (one batch), or
+// more once there would be over 256 chunks.
+static int64_t rank_chunk(int64_t R)
+{
+    const int64_t need = (R + 255) / 256;
+    const int64_t c = (need + kRankThreads - 1) / kRankThreads * kRankThreads;
+    return c < kRankThreads ? kRankThreads : c;
+}
+
+static int rank_chunks(int64_t R) { return R <= 0 ? 1 : (int)((R + rank_chunk(R) - 1) / rank_chunk(R)); }
+
 size_t rank_layout_workspace_bytes(int64_t tokens_per_rank, int num_experts, int num_ranks)
 {
-    const int64_t R = tokens_per_rank * num_ranks;
-    const int64_t C = layout_num_chunks(R < 1 ? 1 : R);
-    const int64_t El = num_experts / num_ranks;
-    return (size_t)((num_ranks + El + 1) * C) * sizeof(int32_t);
+    (void)num_experts;
+    return (size_t)rank_chunks(tokens_per_rank * num_ranks) * num_ranks * sizeof(int32_t);
+}
+
+template <int NW>
+static void launch_rank_shape(hipStream_t stream, const uint8_t* map, int64_t R, int64_t T, int W,
+                              int E, int G, int El, int rank, int k_out, int64_t chunk, int C,
+                              int32_t* cnt, int32_t* s2d, uint8_t* local_map, int32_t* recv_src,
+                              int64_t* recv_topk_idx, int32_t* expert_counts, int32_t* num_recv,
+                              int32_t* num_overflow)
+{
+    hipLaunchKernelGGL(rank_count_kernel<NW>, dim3(C), dim3(kRankThreads), 0, stream, map, R, W, E,
+                       G, El, chunk, cnt, expert_counts, num_overflow);
+    hipLaunchKernelGGL(rank_scatter_kernel<NW>, dim3(C), dim3(kRankThreads), 0, stream, map, R, T,
+                       W, E, G, El, rank, k_out, chunk, C, cnt, s2d, local_map, recv_src,
+                       recv_topk_idx, expert_counts, num_recv, num_overflow);
 }
 
 hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int num_experts,
@@ -559,24 +625,29 @@ hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int n
     const int El = E / G;
     const int W = (E + 7) / 8;
     const int64_t R = T * G;
-    // an empty map still writes the totals (workgroup 0 of the scatter)
-    const int64_t chunk = layout_chunk_pairs(R < 1 ? 1 : R);
-    const int C = (int)layout_num_chunks(R < 1 ? 1 : R);
-    int32_t* ws = static_cast<int32_t*>(workspace);
+    // an empty map still clears and writes the totals (one workgroup each)
+    const int64_t chunk = rank_chunk(R);
+    const int C = rank_chunks(R);
+    int32_t* cnt = static_cast<int32_t*>(workspace);
+    // rows of up to 8 aligned words are held in registers
     const bool words = (W & 3) == 0 && (reinterpret_cast<uintptr_t>(map) & 3u) == 0;
-    if (words) {
-        hipLaunchKernelGGL(rank_count_kernel<true>, dim3(C), dim3(kRankThreads), 0, stream, map, R,
-                           W, E, G, El, rank, k_out, chunk, C, ws);
-        hipLaunchKernelGGL(rank_scatter_kernel<true>, dim3(C), dim3(kRankThreads), 0, stream, map,
-                           R, T, W, E, G, El, rank, k_out, chunk, C, ws, s2d, local_map, recv_src,
-                           recv_topk_idx, expert_counts, num_recv, num_overflow);
-    } else {
-        hipLaunchKernelGGL(rank_count_kernel<false>, dim3(C), dim3(kRankThreads), 0, stream, map,
-                           R, W, E, G, El, rank, k_out, chunk, C, ws);
-        hipLaunchKernelGGL(rank_scatter_kernel<false>, dim3(C), dim3(kRankThreads), 0, stream, map,
-                           R, T, W, E, G, El, rank, k_out, chunk, C, ws, s2d, local_map, recv_src,
-                           recv_topk_idx, expert_counts, num_recv, num_overflow);
+    const int nw = words && W / 4 <= 8 ? W / 4 : 0;
+#define EP_RL(NW)                                                                               \
+    launch_rank_shape<NW>(stream, map, R, T, W, E, G, El, rank, k_out, chunk, C, cnt, s2d,      \
+                          local_map, recv_src, recv_topk_idx, expert_counts, num_recv,          \
+                          num_overflow)
+    switch (nw) {
+    case 1: EP_RL(1); break;
+    case 2: EP_RL(2); break;
+    case 3: EP_RL(3); break;
+    case 4: EP_RL(4); break;
+    case 5: EP_RL(5); break;
+    case 6: EP_RL(6); break;
+    case 7: EP_RL(7); break;
+    case 8: EP_RL(8); break;
+    default: EP_RL(0); break;
     }
+#undef EP_RL
     return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ __all__ = [
     "expert_outputs_scaled",
     "expert_outputs_dequant",
     "make_gradient",
+    "make_routing",
 ]
 
 
@@ -223,3 +224,11 @@ def make_gradient(rows: int, H: int, seed: int = 1) -> np.ndarray:
     """A seeded upstream gradient: N(0,1) float32 [rows, H] rounded to bf16."""
     rng = np.random.default_rng(seed)
     return bf16_bits_from_float32(rng.standard_normal((rows, H), dtype=np.float32))
+
+
+def make_routing(T: int, E: int, k: int, seed: int) -> np.ndarray:
+    """Uniform routing alone: int64 [T, k], a uniformly random k-subset of
+    distinct experts per token (the ``uniform`` recipe above, drawn from
+    ``default_rng(seed)`` with no token rows), for the other ranks of a
+    simulated multi-rank map."""
+    return np.ascontiguousarray(_route_uniform(np.random.default_rng(seed), T, E, k))

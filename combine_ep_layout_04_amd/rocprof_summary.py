@@ -108,6 +108,11 @@ KERNEL_KEYS = {
     "combine_backward": r"combine_backward_kernel<",
     "layout_count": r"layout_count_kernel\(",
     "layout_scatter": r"layout_scatter_kernel\(",
+    "routing_map": r"routing_map_kernel\(",
+    "rank_count": r"rank_count_kernel<",
+    "rank_scatter": r"rank_scatter_kernel<",
+    "dispatch_ranked": r"dispatch_ranked_kernel<",
+    "combine_ranked": r"combine_ranked_kernel<",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
 
