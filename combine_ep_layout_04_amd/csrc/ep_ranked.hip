@@ -23,15 +23,17 @@
 //                 there would be over 256 chunks) counts, for every rank,
 //                 the chunk's tokens it receives (wavefront ballots over a
 //                 per-token rank mask; map rows of up to 8 words stay in
-//                 registers, an LDS table gives each expert's rank).
+//                 registers, an LDS table gives each expert's rank), and
+//                 for the local rank the received tokens per local expert
+//                 and the selections past k_out.
 //   rank scatter: each workgroup sums the earlier chunks' counts (all its
 //                 threads, contiguous loads), then walks its chunk in
 //                 batches of 256 tokens; a token's row in rank d's buffer
 //                 is that base plus its ballot prefix count in the batch.
 //                 It writes sparse_to_dense for the local rank's tokens and
-//                 the receive-side rows, adds its chunk's per-expert counts
-//                 (integer sums: order-free), and all workgroups clear the
-//                 rows past the received count.
+//                 the receive-side rows, and all workgroups clear the rows
+//                 past the received count; workgroup 0 also sums the
+//                 per-chunk receive-side counts into the totals.
 //   dispatch:     one workgroup per token reads the row once into registers
 //                 and stores it, non-temporally, to every rank that receives
 //                 it (a table of G row pointers passed by value), with the
@@ -190,44 +192,91 @@ __device__ __forceinline__ void fill_rank_table(uint8_t* rank_of, int E, int El)
     for (int e = threadIdx.x; e < E; e += kRankThreads) rank_of[e] = (uint8_t)(e / El);
 }
 
-// Workspace: cnt[c][d], the tokens of chunk c that rank d receives (C x G
-// int32, chunk-major so a workgroup's prefix reads are contiguous).
-// Workgroup 0 also clears the per-expert and overflow totals the scatter
-// adds into (stream order puts every clear before every add).
+// Workspace (int32, chunk-major so a workgroup's reads are contiguous):
+//   cnt[c][d]   tokens of chunk c that rank d receives          (C x G)
+//   ecnt[c][e]  of those the local rank receives, how many select local
+//               expert e                                          (C x El)
+//   ovf[c]      their selections past k_out                      (C)
 template <int NW>
 __global__ __launch_bounds__(kRankThreads)
 void rank_count_kernel(const uint8_t* __restrict__ map, int64_t R, int W, int E, int G, int El,
-                       int64_t chunk, int32_t* __restrict__ cnt, int32_t* __restrict__ expert_counts,
-                       int32_t* __restrict__ num_overflow)
+                       int rank, int k_out, int64_t chunk, int C, int32_t* __restrict__ ws)
 {
     __shared__ int32_t s_cnt[kMaxRanks];
+    __shared__ int32_t s_ecnt[kMaxExperts];
     __shared__ uint8_t s_rank_of[kMaxExperts];
+    __shared__ int32_t s_ovf;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int c = blockIdx.x;
-    if (tid < G) s_cnt[tid] = 0;
-    fill_rank_table(s_rank_of, E, El);
-    if (c == 0) {
-        for (int e = tid; e < El; e += kRankThreads) expert_counts[e] = 0;
-        if (tid == 0 && num_overflow != nullptr) *num_overflow = 0;
-    }
-    __syncthreads();
-
     const int64_t g0 = (int64_t)c * chunk;
     const int64_t g1 = min(R, g0 + chunk);
+    // the first batch's rows are requested before anything else
+    MapRow<NW> next;
+    if (g0 < g1) next.load(map + min(g0 + tid, g1 - 1) * W, W, g0 + tid < g1);
+    if (tid < G) s_cnt[tid] = 0;
+    if (tid == 0) s_ovf = 0;
+    for (int e = tid; e < El; e += kRankThreads) s_ecnt[e] = 0;
+    fill_rank_table(s_rank_of, E, El);
+    __syncthreads();
+
+    const int first = rank * El;
+    int ovf = 0;
     for (int64_t b = g0; b < g1; b += kRankThreads) {
         const int64_t g = b + tid;
         const bool live = g < g1;
-        MapRow<NW> row;
-        row.load(map + (live ? g : g0) * W, W, live);
+        const MapRow<NW> row = next;
+        if (b + kRankThreads < g1)
+            next.load(map + min(g + kRankThreads, g1 - 1) * W, W, g + kRankThreads < g1);
         const uint64_t m = live ? rank_mask<NW>(row, E, s_rank_of) : 0ull;
         for (int d = 0; d < G; ++d) {
             const uint64_t bal = __ballot((m >> d) & 1ull);
             if (lane == 0 && bal != 0ull) atomicAdd(&s_cnt[d], popc64(bal));
         }
+        if ((m >> rank) & 1ull) {
+            int n = 0;
+            for (int q = 0; q < El; q += 32) {
+                uint32_t wbits = row.bits32(first + q);
+                if (El - q < 32) wbits &= (1u << (El - q)) - 1u;
+                n += __builtin_popcount(wbits);
+                while (wbits != 0u) {
+                    const int e = q + __builtin_ctz(wbits);
+                    wbits &= wbits - 1u;
+                    atomicAdd(&s_ecnt[e], 1);
+                }
+            }
+            ovf += n > k_out ? n - k_out : 0;
+        }
     }
+    if (ovf != 0) atomicAdd(&s_ovf, ovf);
     __syncthreads();
+    int32_t* cnt = ws;
+    int32_t* ecnt = ws + (int64_t)C * G;
+    int32_t* ovfs = ecnt + (int64_t)C * El;
     if (tid < G) cnt[(int64_t)c * G + tid] = s_cnt[tid];
+    for (int e = tid; e < El; e += kRankThreads) ecnt[(int64_t)c * El + e] = s_ecnt[e];
+    if (tid == 0) ovfs[c] = s_ovf;
+}
+
+// sum of v[cc * stride] over cc = j, j + S, j + 2S, ... below min(C, lim):
+// loads are issued eight at a time, so a thread waits about once per eight
+// (the tables were written by another kernel, possibly on another XCD).
+__device__ __forceinline__ int32_t strided_sum(const int32_t* v, int stride, int j, int S, int C,
+                                               int lim)
+{
+    const int end = min(C, lim);
+    int32_t sum = 0;
+    for (int cc0 = j; cc0 < end; cc0 += 8 * S) {
+        int32_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int cc = cc0 + u * S;
+            x[u] = cc < end ? v[(int64_t)cc * stride] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += x[u];
+    }
+    return sum;
 }
 
 // Four local-map bytes (0 or 1) from four bits.
@@ -236,18 +285,56 @@ __device__ __forceinline__ uint32_t spread4(uint32_t b)
     return (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
 }
 
+// Sixteen local-map bytes from the low sixteen bits.
+__device__ __forceinline__ uint4 spread16(uint32_t b)
+{
+    return make_uint4(spread4(b & 15u), spread4((b >> 4) & 15u), spread4((b >> 8) & 15u),
+                      spread4((b >> 12) & 15u));
+}
+
+// Writes one recv_topk_idx row: the first k_out values put, then -1; with
+// `pairs` (k_out even, row 16-byte aligned) two entries per 16-byte store.
+struct TopkWriter {
+    int64_t* row;
+    int k_out;
+    bool pairs;
+    int n = 0;
+    int64_t held = 0;
+
+    __device__ __forceinline__ TopkWriter(int64_t* r, int k, bool p) : row(r), k_out(k), pairs(p) {}
+
+    __device__ __forceinline__ void put(int64_t v)
+    {
+        if (n < k_out) {
+            if (!pairs) {
+                row[n] = v;
+            } else if (n & 1) {
+                *reinterpret_cast<longlong2*>(row + n - 1) = make_longlong2(held, v);
+            } else {
+                held = v;
+            }
+        }
+        ++n;
+    }
+
+    __device__ __forceinline__ void finish()
+    {
+        while (n < k_out) put(-1);
+    }
+};
+
 template <int NW>
 __global__ __launch_bounds__(kRankThreads)
 void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, int W, int E,
                          int G, int El, int rank, int k_out, int64_t chunk, int C,
-                         const int32_t* __restrict__ cnt, int32_t* __restrict__ s2d,
+                         const int32_t* __restrict__ ws, int32_t* __restrict__ s2d,
                          uint8_t* __restrict__ local_map, int32_t* __restrict__ recv_src,
                          int64_t* __restrict__ recv_topk_idx, int32_t* __restrict__ expert_counts,
                          int32_t* __restrict__ num_recv, int32_t* __restrict__ num_overflow)
 {
     __shared__ int32_t s_base[kMaxRanks];
     __shared__ int32_t s_wave[kRankWaves][kMaxRanks];
-    __shared__ int32_t s_ecnt[kMaxExperts];
+    __shared__ int32_t s_tot[kMaxExperts];
     __shared__ uint8_t s_rank_of[kMaxExperts];
     __shared__ int32_t s_nrecv;
     __shared__ int32_t s_ovf;
@@ -255,14 +342,49 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c = blockIdx.x;
+    const int32_t* cnt = ws;
+    const int32_t* ecnt = ws + (int64_t)C * G;
+    const int32_t* ovfs = ecnt + (int64_t)C * El;
+    const int64_t g0 = (int64_t)c * chunk;
+    const int64_t g1 = min(R, g0 + chunk);
+    // the first batch's rows are requested before the prefix sums
+    MapRow<NW> next;
+    if (g0 < g1) next.load(map + min(g0 + tid, g1 - 1) * W, W, g0 + tid < g1);
     if (tid < G) s_base[tid] = 0;
     if (tid == 0) {
         s_nrecv = 0;
         s_ovf = 0;
     }
-    for (int e = tid; e < El; e += kRankThreads) s_ecnt[e] = 0;
+    for (int j = tid; j < kMaxExperts; j += kRankThreads) s_tot[j] = 0;
     fill_rank_table(s_rank_of, E, El);
     __syncthreads();
+
+    // The receive-side totals over all chunks, spread over the workgroups
+    // from the last one down (the first ones hold the local rank's tokens
+    // and write sparse_to_dense): workgroup C-1-i sums local experts i,
+    // i + C, i + 2C, ..., one value per load, eight loads in flight.
+    const int ci = C - 1 - c;
+    const int my_experts = ci < El ? (El - 1 - ci) / C + 1 : 0;
+    {
+        const int nv = my_experts * C;
+        for (int v0 = tid; v0 < nv; v0 += 8 * kRankThreads) {
+            int32_t x[8];
+            int j[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int v = v0 + u * kRankThreads;
+                j[u] = v < nv ? v / C : 0;
+                x[u] = v < nv ? ecnt[(int64_t)(v - j[u] * C) * El + ci + j[u] * C] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (x[u] != 0) atomicAdd(&s_tot[j[u]], x[u]);
+        }
+        if (c == 0) {
+            const int32_t o = strided_sum(ovfs, 1, tid, kRankThreads, C, C);
+            if (o != 0) atomicAdd(&s_ovf, o);
+        }
+    }
 
     // Rows of each rank's buffer taken by earlier chunks, and the local
     // rank's received total: thread (d, j) sums column d of chunks j, j + S,
@@ -271,30 +393,33 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
         const int S = kRankThreads / G;
         if (tid < S * G) {
             const int d = tid % G;
-            int32_t before = 0, all = 0;
-            for (int cc = tid / G; cc < C; cc += S) {
-                const int32_t v = cnt[(int64_t)cc * G + d];
-                before += cc < c ? v : 0;
-                all += v;
-            }
+            const int32_t before = strided_sum(cnt + d, G, tid / G, S, C, c);
             if (before != 0) atomicAdd(&s_base[d], before);
-            if (d == rank && all != 0) atomicAdd(&s_nrecv, all);
+            if (d == rank) {
+                const int32_t all = strided_sum(cnt + d, G, tid / G, S, C, C);
+                if (all != 0) atomicAdd(&s_nrecv, all);
+            }
         }
     }
     __syncthreads();
-    if (c == 0 && tid == 0) *num_recv = s_nrecv;
+    if (c == 0 && tid == 0) {
+        *num_recv = s_nrecv;
+        if (num_overflow != nullptr) *num_overflow = s_ovf;
+    }
+    for (int j = tid; j < my_experts; j += kRankThreads) expert_counts[ci + j * C] = s_tot[j];
 
     const bool map4 = (El & 3) == 0;
+    // 16-byte stores where rows stay 16-byte aligned
+    const bool map16 = (El & 15) == 0 && (reinterpret_cast<uintptr_t>(local_map) & 15u) == 0;
+    const bool topk16 = (k_out & 1) == 0 && (reinterpret_cast<uintptr_t>(recv_topk_idx) & 15u) == 0;
     const int first = rank * El;
-    const int64_t g0 = (int64_t)c * chunk;
-    const int64_t g1 = min(R, g0 + chunk);
     const int64_t mine0 = (int64_t)rank * T;
-    int ovf = 0;
     for (int64_t b = g0; b < g1; b += kRankThreads) {
         const int64_t g = b + tid;
         const bool live = g < g1;
-        MapRow<NW> row;
-        row.load(map + (live ? g : g0) * W, W, live);
+        const MapRow<NW> row = next;
+        if (b + kRankThreads < g1)
+            next.load(map + min(g + kRankThreads, g1 - 1) * W, W, g + kRankThreads < g1);
         const uint64_t m = live ? rank_mask<NW>(row, E, s_rank_of) : 0ull;
         for (int d = 0; d < G; ++d) {
             const uint64_t bal = __ballot((m >> d) & 1ull);
@@ -313,12 +438,15 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
                 recv_src[pos] = (int32_t)g;
                 int64_t* topk = recv_topk_idx + (int64_t)pos * k_out;
                 uint8_t* lm = local_map + (int64_t)pos * El;
-                int n = 0;
+                TopkWriter tw(topk, k_out, topk16);
                 for (int q = 0; q < El; q += 32) {
                     uint32_t wbits = row.bits32(first + q);
                     const int nb = min(32, El - q);
                     if (nb < 32) wbits &= (1u << nb) - 1u;
-                    if (map4) {
+                    if (map16) {
+                        for (int i = 0; i < nb; i += 16)
+                            *reinterpret_cast<uint4*>(lm + q + i) = spread16(wbits >> i);
+                    } else if (map4) {
                         for (int i = 0; i < nb; i += 4)
                             *reinterpret_cast<uint32_t*>(lm + q + i) = spread4((wbits >> i) & 15u);
                     } else {
@@ -327,13 +455,10 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
                     while (wbits != 0u) {
                         const int e = q + __builtin_ctz(wbits);
                         wbits &= wbits - 1u;
-                        atomicAdd(&s_ecnt[e], 1);
-                        if (n < k_out) topk[n] = e;
-                        ++n;
+                        tw.put(e);
                     }
                 }
-                ovf += n > k_out ? n - k_out : 0;
-                for (; n < k_out; ++n) topk[n] = -1;
+                tw.finish();
             }
         }
         __syncthreads();
@@ -344,22 +469,18 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
         }
         __syncthreads();
     }
-    if (ovf != 0) atomicAdd(&s_ovf, ovf);
-    __syncthreads();
-    // this chunk's receive-side totals (the count kernel cleared them)
-    for (int e = tid; e < El; e += kRankThreads)
-        if (s_ecnt[e] != 0) atomicAdd(&expert_counts[e], s_ecnt[e]);
-    if (tid == 0 && s_ovf != 0 && num_overflow != nullptr) atomicAdd(num_overflow, s_ovf);
 
     // rows past the received count: no source, no local expert
     const int64_t nrecv = s_nrecv;
     const int64_t stride = (int64_t)gridDim.x * kRankThreads;
     for (int64_t i = nrecv + (int64_t)c * kRankThreads + tid; i < R; i += stride) {
         recv_src[i] = -1;
-        int64_t* topk = recv_topk_idx + i * k_out;
-        for (int n = 0; n < k_out; ++n) topk[n] = -1;
+        TopkWriter tw(recv_topk_idx + i * k_out, k_out, topk16);
+        tw.finish();
         uint8_t* lm = local_map + i * El;
-        if (map4) {
+        if (map16) {
+            for (int e = 0; e < El; e += 16) *reinterpret_cast<uint4*>(lm + e) = make_uint4(0u, 0u, 0u, 0u);
+        } else if (map4) {
             for (int e = 0; e < El; e += 4) *reinterpret_cast<uint32_t*>(lm + e) = 0u;
         } else {
             for (int e = 0; e < El; ++e) lm[e] = 0;
@@ -595,8 +716,8 @@ static int rank_chunks(int64_t R) { return R <= 0 ? 1 : (int)((R + rank_chunk(R)
 
 size_t rank_layout_workspace_bytes(int64_t tokens_per_rank, int num_experts, int num_ranks)
 {
-    (void)num_experts;
-    return (size_t)rank_chunks(tokens_per_rank * num_ranks) * num_ranks * sizeof(int32_t);
+    const int64_t C = rank_chunks(tokens_per_rank * num_ranks);
+    return (size_t)(C * (num_ranks + num_experts / num_ranks + 1)) * sizeof(int32_t);
 }
 
 template <int NW>
@@ -607,7 +728,7 @@ static void launch_rank_shape(hipStream_t stream, const uint8_t* map, int64_t R,
                               int32_t* num_overflow)
 {
     hipLaunchKernelGGL(rank_count_kernel<NW>, dim3(C), dim3(kRankThreads), 0, stream, map, R, W, E,
-                       G, El, chunk, cnt, expert_counts, num_overflow);
+                       G, El, rank, k_out, chunk, C, cnt);
     hipLaunchKernelGGL(rank_scatter_kernel<NW>, dim3(C), dim3(kRankThreads), 0, stream, map, R, T,
                        W, E, G, El, rank, k_out, chunk, C, cnt, s2d, local_map, recv_src,
                        recv_topk_idx, expert_counts, num_recv, num_overflow);

@@ -176,15 +176,16 @@ def test_layout_ex_rejects(A, cap, T, code):
 # ---- per-(token, rank) path
 
 def test_rank_layout_workspace_size():
-    # one int32 per (chunk, rank), 256-byte aligned; chunks hold 256 global
-    # tokens until there would be more than 256 of them
-    def want(chunks, G):
-        return (chunks * G * 4 + 255) // 256 * 256
-    assert ep.rank_layout_workspace_size(8192, 256, 8) == want(256, 8)
-    assert ep.rank_layout_workspace_size(0, 256, 8) == want(1, 8)
-    assert ep.rank_layout_workspace_size(8192, 256, 1) == want(32, 1)
-    assert ep.rank_layout_workspace_size(65536, 64, 64) == want(256, 64)   # 16384-token chunks
-    assert ep.rank_layout_workspace_size(65537, 64, 64) == want(253, 64)   # 16640-token chunks
+    # per chunk: one int32 per rank, one per local expert and one overflow
+    # count, 256-byte aligned; chunks hold 256 global tokens until there
+    # would be more than 256 of them
+    def want(chunks, G, El):
+        return (chunks * (G + El + 1) * 4 + 255) // 256 * 256
+    assert ep.rank_layout_workspace_size(8192, 256, 8) == want(256, 8, 32)
+    assert ep.rank_layout_workspace_size(0, 256, 8) == want(1, 8, 32)
+    assert ep.rank_layout_workspace_size(8192, 256, 1) == want(32, 1, 256)
+    assert ep.rank_layout_workspace_size(65536, 64, 64) == want(256, 64, 1)   # 16384-token chunks
+    assert ep.rank_layout_workspace_size(65537, 64, 64) == want(253, 64, 1)   # 16640-token chunks
     assert ep.rank_layout_workspace_size(10, 256, 3) == 0        # E % G
     assert ep.rank_layout_workspace_size(10, 256, 65) == 0
     assert ep.rank_layout_workspace_size(10, 0, 1) == 0
