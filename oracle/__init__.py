@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_ranked.restype = None
         L.oracle_combine_ranked.argtypes = [P, P, i64, i32, i32, P]
         L.oracle_combine_ranked.restype = None
+        L.oracle_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
+                                                    P, P]
+        L.oracle_dispatch_fused_permute.restype = None
         _lib = L
     return _lib
 
@@ -399,3 +402,33 @@ def combine_ranked(src_y, sparse_to_dense: np.ndarray) -> np.ndarray:
     out = np.zeros((T, H), np.uint16)
     lib().oracle_combine_ranked(_ptr_array(ys), _ptr(s2d), T, H, G, _ptr(out))
     return out
+
+
+def dispatch_fused_permute(src_x, src_idx, src_w, E: int, rank: int, recv_src: np.ndarray,
+                           recv_topk_idx: np.ndarray, slot: np.ndarray, rows: int,
+                           with_weights: bool = True):
+    """Receiver-side dispatch with the permute fused in.  ``src_x`` /
+    ``src_idx`` / ``src_w`` are lists of the G ranks' tokens (uint16 [T, H]),
+    topk_idx (int64 [T, k]) and weights (float32 [T, k] or None).  Returns
+    (recv_x uint16 [rows, H], recv_w float32 [rows] or None); unwritten rows
+    stay 0."""
+    G = len(src_x)
+    xs = [_c(x, np.uint16) for x in src_x]
+    ids = [_c(i, np.int64) for i in src_idx]
+    ws = [None if w is None else _c(w, np.float32) for w in src_w]
+    T, H = xs[0].shape
+    k = ids[0].shape[1]
+    rs = _c(recv_src, np.int32)
+    rti = _c(recv_topk_idx, np.int64)
+    sl = _c(slot, np.int32)
+    if rs.shape != (G * T,) or rti.shape != (G * T, k) or sl.shape != (G * T, k):
+        raise ValueError("receive-side arrays must have G*T rows and k columns")
+    if sl.size and sl.max() >= rows:
+        raise ValueError("a slot is beyond the receive buffer")
+    out = np.zeros((rows, H), np.uint16)
+    rw = np.zeros(rows, np.float32) if with_weights else None
+    wtab = None if all(w is None for w in ws) else _ptr_array(ws)
+    lib().oracle_dispatch_fused_permute(_ptr_array(xs), _ptr_array(ids), wtab, T, H, k, int(E), G,
+                                        int(rank), _ptr(rs), _ptr(rti), _ptr(sl), _ptr(out),
+                                        _ptr(rw))
+    return out, rw

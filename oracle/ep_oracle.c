@@ -724,3 +724,48 @@ void oracle_combine_ranked(const uint16_t *const *src_y, const int32_t *sparse_t
             out[t * H + c] = oracle_bf16_from_double(s);
         }
 }
+
+/*
+ * Receive-side dispatch with the permute fused in (NeMo fused_a2a page,
+ * HybridEPDispatch: fuse_permute, and the dispatched rows come out grouped
+ * by local expert; NCCL EP page, sparse_to_dense_map and
+ * local_expert_routing_map).  Rank `rank` takes every token it receives
+ * once from the sending rank's rows and writes it to each of its
+ * local-expert rows, given by `slot` [G*T, k] (the expanded layout of
+ * recv_topk_idx over the E/G local experts):
+ *   for received row i with g = recv_src[i] >= 0 (s = g / T, t = g % T)
+ *   and j < k with slot[i, j] >= 0:
+ *     recv_x[slot[i, j]] = src_x[s][t]
+ *     recv_w[slot[i, j]] = the fp32 sum, in increasing j', of src_w[s][t, j']
+ *         over the j' with src_idx[s][t, j'] == rank*El + recv_topk_idx[i, j]
+ *         (1 per slot when src_w is NULL)
+ * recv_w may be NULL.
+ */
+void oracle_dispatch_fused_permute(const uint16_t *const *src_x, const int64_t *const *src_idx,
+                                   const float *const *src_w, int64_t T, int H, int k, int E, int G,
+                                   int rank, const int32_t *recv_src, const int64_t *recv_topk_idx,
+                                   const int32_t *slot, uint16_t *recv_x, float *recv_w)
+{
+    int El = E / G;
+    for (int64_t i = 0; i < (int64_t)G * T; ++i) {
+        int32_t g = recv_src[i];
+        if (g < 0)
+            continue;
+        int s = (int)(g / T);
+        int64_t t = g % T;
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[i * k + j];
+            if (r < 0)
+                continue;
+            memcpy(recv_x + (int64_t)r * H, src_x[s] + t * H, (size_t)H * sizeof(uint16_t));
+            if (!recv_w)
+                continue;
+            int64_t e = (int64_t)rank * El + recv_topk_idx[i * k + j];
+            float sum = 0.0f;
+            for (int jj = 0; jj < k; ++jj)
+                if (src_idx[s][t * k + jj] == e)
+                    sum = sum + (src_w && src_w[s] ? src_w[s][t * k + jj] : 1.0f);
+            recv_w[r] = sum;
+        }
+    }
+}

@@ -277,3 +277,58 @@ def test_nonexpanded_path_matches_expanded_path():
                         expert(e, xs[s][t:t + 1]))[0])
         # G partial roundings + the final one, each at most 2^-8 relative
         assert np.all(np.abs(got - exact) <= 2.0 ** -8 * (G + 1) * mag + 1e-30)
+
+
+def test_fused_permute_handworked():
+    (c,) = read_cases("ranked_handworked.txt")
+    G, T, E, k = c["G"][0], c["T"][0], c["E"][0], c["k"][0]
+    idx = [np.array(c[f"idx_r{r}"], np.int64).reshape(T, k) for r in range(G)]
+    w = [np.array(c[f"w_r{r}"], np.float32).reshape(T, k) for r in range(G)]
+    xs = [make_gradient(T, 16, 50 + r) for r in range(G)]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    for r in range(G):
+        L = oracle.rank_layout(gmap, T, E, G, r, k)
+        Lr = oracle.layout(L.recv_topk_idx, E // G)
+        np.testing.assert_array_equal(Lr.slot.ravel(), c[f"slot_r{r}"])
+        rx, rw = oracle.dispatch_fused_permute(xs, idx, w, E, r, L.recv_src, L.recv_topk_idx,
+                                               Lr.slot, Lr.n)
+        for row, (s, t) in enumerate(zip(c[f"perm_rank_r{r}"], c[f"perm_token_r{r}"])):
+            np.testing.assert_array_equal(rx[row], xs[s][t])
+        np.testing.assert_array_equal(rw, np.array(c[f"perm_w_r{r}"], np.float32))
+
+
+@pytest.mark.parametrize("seed,G,T,E,k,weights", [(0, 2, 30, 8, 3, True), (1, 4, 50, 32, 6, True),
+                                                  (2, 3, 20, 9, 5, False), (3, 8, 40, 64, 8, True)])
+def test_fused_permute_is_rank_dispatch_then_expert_dispatch(seed, G, T, E, k, weights):
+    # the fused permute equals: every sender's once-per-rank dispatch into
+    # this rank's receive buffer, then the expanded dispatch of that buffer
+    # by the layout of recv_topk_idx (weights: the receive rows' compact
+    # weights carried to their expert rows)
+    H = 16
+    El = E // G
+    cases = [make_random_case(seed * 10 + s, T, H, E, k, mask_frac=0.2, dup_frac=1.0,
+                              invalid_frac=0.05) for s in range(G)]
+    xs = [cs.x_bits for cs in cases]
+    idx = [cs.topk_idx for cs in cases]
+    ws = [cs.topk_weights if weights else None for cs in cases]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    for r in range(G):
+        recv = np.zeros((G * T, H), np.uint16)
+        recv_w = np.zeros((G * T, k), np.float32)
+        for s in range(G):
+            dx, dw = oracle.dispatch_ranked(xs[s], idx[s], ws[s], E, G, L[s].sparse_to_dense,
+                                            G * T)
+            p = L[s].sparse_to_dense[:, r]
+            recv[p[p >= 0]] = dx[r][p[p >= 0]]
+            recv_w[p[p >= 0]] = dw[r][p[p >= 0]]
+        Lr = oracle.layout(L[r].recv_topk_idx, El)
+        rows = max(Lr.n, 1)
+        want_x, _ = oracle.dispatch_bf16(recv, Lr.slot, rows=rows)
+        want_w = np.zeros(rows, np.float32)
+        ok = Lr.slot >= 0
+        want_w[Lr.slot[ok]] = recv_w[ok]
+        got_x, got_w = oracle.dispatch_fused_permute(xs, idx, ws, E, r, L[r].recv_src,
+                                                     L[r].recv_topk_idx, Lr.slot, rows)
+        np.testing.assert_array_equal(got_x, want_x)
+        np.testing.assert_array_equal(got_w, want_w)
