@@ -401,6 +401,57 @@ int ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk
                     "ep_dispatch_ranked launch");
 }
 
+int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,
+                              const float* const* src_topk_weights, int64_t tokens_per_rank,
+                              int hidden, int num_topk, int num_experts, int num_ranks, int rank,
+                              const int32_t* recv_src, const int64_t* recv_topk_idx,
+                              const int32_t* slot, int64_t rows, void* recv_x,
+                              float* recv_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
+    int st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    st = check_tokens(tokens_per_rank * num_ranks, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 8);
+    if (st) return st;
+    if (rank < 0 || rank >= num_ranks)
+        return fail(EP_INVALID_ARGUMENT, "rank %d outside [0, %d)", rank, num_ranks);
+    if (rows < 0) return fail(EP_INVALID_ARGUMENT, "rows < 0");
+    if (!src_x) return fail(EP_INVALID_ARGUMENT, "src_x (a host array of pointers) is required");
+    if (recv_weights && !src_topk_idx)
+        return fail(EP_INVALID_ARGUMENT, "recv_weights needs src_topk_idx");
+    ep::RankPtrs px = {}, pi = {}, pw = {};
+    for (int d = 0; d < num_ranks; ++d) {
+        if (!src_x[d] || !aligned16(src_x[d]))
+            return fail(EP_INVALID_ARGUMENT, "src_x[%d] must be non-NULL and 16-byte aligned", d);
+        px.p[d] = const_cast<void*>(src_x[d]);
+        if (recv_weights) {
+            if (!src_topk_idx[d] || (reinterpret_cast<uintptr_t>(src_topk_idx[d]) & 7u))
+                return fail(EP_INVALID_ARGUMENT,
+                            "src_topk_idx[%d] must be non-NULL and 8-byte aligned", d);
+            pi.p[d] = const_cast<int64_t*>(src_topk_idx[d]);
+            if (src_topk_weights) {
+                if ((reinterpret_cast<uintptr_t>(src_topk_weights[d]) & 3u))
+                    return fail(EP_INVALID_ARGUMENT, "src_topk_weights[%d] must be 4-byte aligned",
+                                d);
+                pw.p[d] = const_cast<float*>(src_topk_weights[d]);
+            }
+        }
+    }
+    if (tokens_per_rank == 0) return EP_SUCCESS;
+    if (!recv_src || !slot || !recv_x || (recv_weights && !recv_topk_idx))
+        return fail(EP_INVALID_ARGUMENT,
+                    "recv_src, slot, recv_x (and recv_topk_idx with recv_weights) are required");
+    if (!aligned16(recv_x)) return fail(EP_INVALID_ARGUMENT, "recv_x must be 16-byte aligned");
+    return from_hip(ep::launch_dispatch_fused_permute(px, pi, pw, tokens_per_rank, hidden, num_topk,
+                                                      num_experts, num_ranks, rank, recv_src,
+                                                      recv_topk_idx, slot, rows, recv_x,
+                                                      recv_weights, static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_fused_permute launch");
+}
+
 int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
                       const int32_t* sparse_to_dense_map, int64_t num_tokens, int hidden,
                       int num_ranks, void* out, void* stream)

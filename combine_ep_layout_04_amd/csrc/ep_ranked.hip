@@ -38,6 +38,10 @@
 //                 and stores it, non-temporally, to every rank that receives
 //                 it (a table of G row pointers passed by value), with the
 //                 token's weights for that rank's experts.
+//   fused permute: the receiving rank's dispatch with the permute folded
+//                 in: one workgroup per received token reads the sender's
+//                 row once and stores it to each of the rank's local-expert
+//                 rows, with the weights.
 //   combine:      one workgroup per token gathers its rows from the G
 //                 buffers through buffer resources (an unrouted rank gets a
 //                 0-byte resource: its loads return 0 without a branch) and
@@ -589,6 +593,78 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
     }
 }
 
+// ------------------------------------------------ receive side, fused permute
+
+// One workgroup per received row i: the token (rank s, token t) is read once
+// from rank s's rows and stored to each of this rank's local-expert rows
+// slot[i, j]; wavefront 0 writes the matching weights, the fp32 sum in
+// increasing j' of the source weights of the slots that select the pair's
+// expert.  Rows with no source (past the received count) return at once.
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT)
+void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
+                                   int nvec, int k, int E, int El, int rank,
+                                   const int32_t* __restrict__ recv_src,
+                                   const int64_t* __restrict__ recv_topk_idx,
+                                   const int32_t* __restrict__ slot, int64_t rows,
+                                   uint4* __restrict__ recv_x, float* __restrict__ recv_w)
+{
+    const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // the same value in every lane; made scalar so the pointer tables are
+    // read with scalar loads
+    const int32_t g = __builtin_amdgcn_readfirstlane(recv_src[i]);
+    if (g < 0) return;
+    const int s = (int)(g / T);
+    const int64_t t = g - (int64_t)s * T;
+    int32_t sl = lane < k ? slot[i * k + lane] : -1;
+    if (sl >= rows) sl = -1;
+
+    if (recv_w != nullptr && tid < 64) {
+        const int64_t le = lane < k ? recv_topk_idx[i * k + lane] : -1;
+        const int32_t target = (le >= 0 && le < El) ? rank * El + (int32_t)le : -2;
+        const int64_t se = lane < k ? static_cast<const int64_t*>(src_idx.p[s])[t * k + lane] : -1;
+        const int32_t se32 = (se >= 0 && se < E) ? (int32_t)se : -3;
+        const float* sw = static_cast<const float*>(src_w.p[s]);
+        const float swv = lane < k ? (sw ? sw[t * k + lane] : 1.0f) : 0.0f;
+        float sum = 0.0f;
+        for (int jj = 0; jj < k; ++jj) {
+            const int32_t e2 = __builtin_amdgcn_readlane(se32, jj);
+            const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swv), jj));
+            if (e2 == target) sum = sum + w2;
+        }
+        if (sl >= 0) recv_w[sl] = sum;
+    }
+
+    const uint4* xr = static_cast<const uint4*>(src_x.p[s]) + t * nvec;
+    constexpr int kPass = NT * VPT;
+    const int full = nvec / kPass;
+    for (int ps = 0; ps < full; ++ps) {
+        const int vb = ps * kPass + tid;
+        uint4 buf[VPT];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) buf[u] = xr[vb + u * NT];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) keep(buf[u]);
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = __builtin_amdgcn_readlane(sl, j);
+            if (r < 0) continue;
+            uint4* dst = recv_x + (int64_t)r * nvec + vb;
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) store_nt(dst + u * NT, buf[u]);
+        }
+    }
+    for (int v = full * kPass + tid; v < nvec; v += NT) {
+        uint4 val = xr[v];
+        keep(val);
+        for (int j = 0; j < k; ++j) {
+            const int32_t r = __builtin_amdgcn_readlane(sl, j);
+            if (r >= 0) store_nt(recv_x + (int64_t)r * nvec + v, val);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- combine
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
@@ -812,6 +888,50 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     default: EP_DR(128, 8); break;
     }
 #undef EP_DR
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& src_idx,
+                                         const RankPtrs& src_w, int64_t tokens_per_rank,
+                                         int hidden, int num_topk, int num_experts, int num_ranks,
+                                         int rank, const int32_t* recv_src,
+                                         const int64_t* recv_topk_idx, const int32_t* slot,
+                                         int64_t rows, void* recv_x, float* recv_w,
+                                         hipStream_t stream)
+{
+    const int64_t R = tokens_per_rank * num_ranks;
+    if (R == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const dim3 grid((unsigned)R);
+    const int El = num_experts / num_ranks;
+    uint4* rx = static_cast<uint4*>(recv_x);
+#define EP_FP(NT, V)                                                                            \
+    hipLaunchKernelGGL((dispatch_fused_permute_kernel<NT, V>), grid, dim3(NT), 0, stream, src_x, \
+                       src_idx, src_w, tokens_per_rank, nvec, num_topk, num_experts, El, rank,   \
+                       recv_src, recv_topk_idx, slot, rows, rx, recv_w)
+    if (nvec <= 64) {
+        EP_FP(64, 1);
+        return hipGetLastError();
+    }
+    const int fit = nvec / 128;
+    int vpt = fit < 1 ? 1 : (fit > 8 ? 8 : fit);
+    for (int v = 8; v >= 1; --v) {
+        if (nvec % (128 * v) == 0) {
+            vpt = v;
+            break;
+        }
+    }
+    switch (vpt) {
+    case 1: EP_FP(128, 1); break;
+    case 2: EP_FP(128, 2); break;
+    case 3: EP_FP(128, 3); break;
+    case 4: EP_FP(128, 4); break;
+    case 5: EP_FP(128, 5); break;
+    case 6: EP_FP(128, 6); break;
+    case 7: EP_FP(128, 7); break;
+    default: EP_FP(128, 8); break;
+    }
+#undef EP_FP
     return hipGetLastError();
 }
 

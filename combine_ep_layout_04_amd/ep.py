@@ -49,7 +49,7 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
-           "ep_combine_ranked")
+           "ep_dispatch_fused_permute", "ep_combine_ranked")
 
 
 class EpError(RuntimeError):
@@ -104,6 +104,9 @@ def lib() -> ctypes.CDLL:
         L.ep_rank_layout.restype = i32
         L.ep_dispatch_ranked.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, i64, P]
         L.ep_dispatch_ranked.restype = i32
+        L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
+                                                i64, P, P, P]
+        L.ep_dispatch_fused_permute.restype = i32
         L.ep_combine_ranked.argtypes = [P, i64, P, i64, i32, i32, P, P]
         L.ep_combine_ranked.restype = i32
         _lib = L
@@ -541,6 +544,60 @@ def ep_dispatch_ranked(x: torch.Tensor, sparse_to_dense: torch.Tensor, dest_x, n
                                   None if wtab is None else wtab[1], rows, _stream(stream))
     _check(st, "ep_dispatch_ranked")
     return dest_x, dest_weights
+
+
+def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torch.Tensor,
+                              slot: torch.Tensor, num_experts: int, rank: int, *, rows: int,
+                              src_topk_idx=None, src_topk_weights=None, recv_x=None,
+                              recv_weights=None, want_weights: bool = False, stream=None):
+    """The receiving rank's dispatch with the permute fused in: ``src_x`` is
+    a list of the G ranks' tokens (bf16 [T, H]); ``recv_src`` /
+    ``recv_topk_idx`` come from ep_rank_layout and ``slot`` from ep_layout of
+    recv_topk_idx over E/G experts; ``rows`` is the expert-grouped buffer's
+    row count.  Weights need ``src_topk_idx`` (list of int64 [T, k]) and
+    optionally ``src_topk_weights`` (list of fp32 [T, k] or None).  Returns
+    (recv_x bf16 [rows, H], recv_weights fp32 [rows] or None)."""
+    G = len(src_x)
+    for d, t in enumerate(src_x):
+        _need(t, f"src_x[{d}]", torch.bfloat16)
+    T, H = src_x[0].shape
+    for t in src_x:
+        if tuple(t.shape) != (T, H):
+            raise ValueError("every src_x must be [T, H]")
+    _need(recv_src, "recv_src", torch.int32, G * T)
+    _need(recv_topk_idx, "recv_topk_idx", torch.int64)
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or slot.shape[0] != G * T or recv_topk_idx.shape != slot.shape:
+        raise ValueError("slot and recv_topk_idx must be [G*T, k]")
+    k = slot.shape[1]
+    R = int(rows)
+    dev = src_x[0].device
+    if recv_x is None:
+        recv_x = torch.empty((max(R, 1), H), dtype=torch.bfloat16, device=dev)
+    _need(recv_x, "recv_x", torch.bfloat16, R * H)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
+    itab = wtab = None
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, R)
+        if src_topk_idx is None or len(src_topk_idx) != G:
+            raise ValueError("recv_weights needs src_topk_idx for every rank")
+        for d, t in enumerate(src_topk_idx):
+            _need(t, f"src_topk_idx[{d}]", torch.int64, T * k)
+        itab = _ptr_table(src_topk_idx)
+        if src_topk_weights is not None:
+            for d, t in enumerate(src_topk_weights):
+                if t is not None:
+                    _need(t, f"src_topk_weights[{d}]", torch.float32, T * k)
+            wtab = _ptr_table(src_topk_weights)
+    xtab = _ptr_table(src_x)
+    st = lib().ep_dispatch_fused_permute(xtab[1], None if itab is None else itab[1],
+                                         None if wtab is None else wtab[1], T, H, k,
+                                         int(num_experts), G, int(rank), _ptr(recv_src),
+                                         _ptr(recv_topk_idx), _ptr(slot), R, _ptr(recv_x),
+                                         _ptr(recv_weights), _stream(stream))
+    _check(st, "ep_dispatch_fused_permute")
+    return recv_x, recv_weights
 
 
 def ep_combine_ranked(src_y, sparse_to_dense: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:

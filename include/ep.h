@@ -426,6 +426,45 @@ int ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk
                        float *const *dest_weights, int64_t dest_rows, void *stream);
 
 /*
+ * ep_dispatch_fused_permute -- the receiving rank's dispatch with the
+ * permute fused in: every token it receives is read once from the sending
+ * rank's rows and written to each of its local-expert rows, so the rows come
+ * out grouped by local expert with no intermediate receive buffer.
+ *
+ * Passages: NeMo fused_a2a page, HybridEPDispatch (fuse_permute; the
+ * dispatched rows are grouped by local expert; pad_multiple); NCCL EP page,
+ * sparse_to_dense_map / local_expert_routing_map.
+ *
+ * In:  src_x              HOST array of G device pointers: rank s's tokens,
+ *                         bf16 [tokens_per_rank, hidden] (on one device, or
+ *                         peer memory mapped into it).
+ *      src_topk_idx       HOST array of G device pointers to rank s's int64
+ *                         topk_idx [tokens_per_rank, num_topk]; read only for
+ *                         recv_weights (may be NULL without them).
+ *      src_topk_weights   NULL (unit weights), or HOST array of G device
+ *                         pointers to fp32 [tokens_per_rank, num_topk]
+ *                         (an entry may be NULL: unit weights).
+ *      recv_src, recv_topk_idx  from ep_rank_layout for `rank` (k_out =
+ *                         num_topk), all G*T rows.
+ *      slot               int32 [G*T, num_topk]: ep_layout (or ep_layout_ex
+ *                         with an alignment) of recv_topk_idx over E/G
+ *                         experts.
+ * Out: recv_x [rows, hidden]: recv_x[slot[i, j]] = src_x[s][t] for received
+ *      row i (recv_src[i] = s*T + t) and slot[i, j] >= 0;
+ *      recv_weights [rows] or NULL: the fp32 sum, in increasing slot order,
+ *      of rank s's weights of the slots that select expert
+ *      rank*E/G + recv_topk_idx[i, j].
+ *      Rows past `rows` are never written; rows nothing maps to are not.
+ * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,
+                              const float *const *src_topk_weights, int64_t tokens_per_rank,
+                              int hidden, int num_topk, int num_experts, int num_ranks, int rank,
+                              const int32_t *recv_src, const int64_t *recv_topk_idx,
+                              const int32_t *slot, int64_t rows, void *recv_x,
+                              float *recv_weights, void *stream);
+
+/*
  * ep_combine_ranked -- gather this rank's tokens back from every rank.
  * In:  src_y                HOST array of G device pointers: rank d's
  *                           per-token outputs, bf16 [src_rows, hidden] (each

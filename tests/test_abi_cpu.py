@@ -287,3 +287,33 @@ def test_ranked_zero_tokens_are_noops():
     assert ep.lib().ep_combine_ranked(ctypes.addressof(dx), 0, None, 0, 256, 2, None, None) == 0
     assert ep.lib().ep_routing_map(None, 0, 2, 8, None, None, None) == 0
     assert ep.last_error() == ""
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(G=65, E=130), 1), (dict(E=9), 1), (dict(rank=2), 1),
+    (dict(rank=-1), 1), (dict(H=12), 1), (dict(k=0), 1), (dict(rows=-1), 1), (dict(T=-1), 1),
+    (dict(T=1 << 28, G=8, k=8, sx=(FAKE,) * 8), 2),
+    (dict(sx="none"), 1), (dict(sx=(FAKE, None)), 1), (dict(sx=(FAKE, FAKE + 8)), 1),
+    (dict(si="none"), 1), (dict(si=(FAKE, None)), 1), (dict(si=(FAKE, FAKE + 4)), 1),
+    (dict(sw=(FAKE, FAKE + 2)), 1), (dict(src=None), 1), (dict(slot=None), 1),
+    (dict(rti=None), 1), (dict(out=None), 1), (dict(out=FAKE + 8), 1),
+])
+def test_dispatch_fused_permute_rejects(over, code):
+    a = dict(sx=(FAKE, FAKE), si=(FAKE, FAKE), sw=None, T=4, H=256, k=2, E=8, G=2, rank=0,
+             src=FAKE, rti=FAKE, slot=FAKE, rows=16, out=FAKE, rw=FAKE)
+    a.update(over)
+    tabs = {n: (None if a[n] in (None, "none") else _table(*a[n])) for n in ("sx", "si", "sw")}
+    st = ep.lib().ep_dispatch_fused_permute(
+        *[None if tabs[n] is None else ctypes.addressof(tabs[n]) for n in ("sx", "si", "sw")],
+        a["T"], a["H"], a["k"], a["E"], a["G"], a["rank"], a["src"], a["rti"], a["slot"],
+        a["rows"], a["out"], a["rw"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_dispatch_fused_permute_zero_tokens_is_a_noop():
+    sx = _table(FAKE, FAKE)
+    assert ep.lib().ep_dispatch_fused_permute(ctypes.addressof(sx), None, None, 0, 256, 2, 8, 2,
+                                              0, None, None, None, 0, None, None, None) == 0
+    assert ep.last_error() == ""

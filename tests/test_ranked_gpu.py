@@ -347,3 +347,68 @@ def test_rank_layout_deterministic_and_on_a_side_stream():
     side.synchronize()
     for f in ep.RankLayout.FIELDS:
         assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def check_fused_permute(xs, idx, ws, E, G, r, A=1, with_weights=True, rank_layout=None):
+    T, H = xs[0].shape
+    k = idx[0].shape[1]
+    El = E // G
+    if rank_layout is None:
+        gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+        rank_layout = oracle.rank_layout(gmap, T, E, G, r, k)
+    L = rank_layout
+    Lr = oracle.layout(L.recv_topk_idx, El, alignment=A)
+    rows = max(Lr.n, 1)
+    out = torch.full((rows, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV) if with_weights else None
+    ep.ep_dispatch_fused_permute([x_dev(x) for x in xs], dev(L.recv_src), dev(L.recv_topk_idx),
+                                 dev(Lr.slot), E, r, rows=rows,
+                                 src_topk_idx=[dev(i) for i in idx] if with_weights else None,
+                                 src_topk_weights=None if ws is None else [dev(w) for w in ws],
+                                 recv_x=out, recv_weights=rw)
+    torch.cuda.synchronize()
+    ox, ow = oracle.dispatch_fused_permute(xs, idx, ws if ws is not None else [None] * G, E, r,
+                                           L.recv_src, L.recv_topk_idx, Lr.slot, rows,
+                                           with_weights)
+    written = np.zeros(rows, bool)
+    written[Lr.slot[Lr.slot >= 0]] = True
+    got = bf16_bits(out)
+    np.testing.assert_array_equal(got[written], ox[written])
+    assert np.all(got[~written] == 0xFFFD), "a padding row was written"
+    if with_weights:
+        g = host(rw)
+        np.testing.assert_array_equal(g[written].view(np.uint32), ow[written].view(np.uint32))
+        assert np.all(np.isnan(g[~written]))
+
+
+@pytest.mark.parametrize("G,T,H,E,k,A,weights", [
+    (1, 3, 8, 2, 1, 1, True),
+    (2, 40, 24, 8, 3, 1, True),       # tail-only rows
+    (4, 200, 1032, 16, 5, 4, True),   # one pass + tail, aligned segments
+    (3, 90, 2048, 9, 9, 1, False),    # k = 9, no weights
+    (8, 64, 7168, 64, 8, 16, True),
+    (64, 8, 256, 128, 64, 1, True),   # G = EP_MAX_RANKS, k = EP_MAX_TOPK
+])
+def test_fused_permute_small(G, T, H, E, k, A, weights):
+    cases = rank_cases(G + H + k, G, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    xs = [c.x_bits for c in cases]
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases] if weights else None
+    for r in sorted({0, G - 1, G // 2}):
+        print(f"\n[ranked] fused permute G={G} T={T} H={H} E={E} k={k} A={A} rank={r}", flush=True)
+        check_fused_permute(xs, idx, ws, E, G, r, A=A, with_weights=True)
+        check_fused_permute(xs, idx, ws, E, G, r, with_weights=False)
+
+
+def test_fused_permute_headline():
+    # rank 0 of 8 receives from all 8 ranks at the headline shape: about
+    # 43k tokens read once, 65k expert rows written
+    w = WORKLOADS["headline"]
+    G = 8
+    idx = headline_global_map(G)
+    inp = make_inputs(w)
+    idx[0] = inp.topk_idx
+    xs = [inp.x_bits] + [make_gradient(w.T, w.H, 300 + s) for s in range(1, G)]
+    ws = [inp.topk_weights] + [np.full((w.T, w.k), 1.0 / w.k, np.float32)] * (G - 1)
+    print("\n[ranked] fused permute headline G=8 rank 0", flush=True)
+    check_fused_permute(xs, idx, ws, w.E, G, 0)
