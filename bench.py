@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "dispatch_fp8_prequantized": "ep_dispatch.hip",
     "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
     "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
+    "dispatch_fused_permute": "ep_ranked.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -398,6 +399,44 @@ def main():
     rbm = ranked_bytes_model(T, H, k, G, pairs)
     del dest, dest_w
 
+    # receive side of rank 0 with the permute fused in: every token it
+    # receives (from 8 ranks; ranks 1..7 hold seeded N(0,1) rows and unit-sum
+    # weights) read once and written to its local-expert rows
+    with torch.cuda.stream(stream):
+        gen = torch.Generator(device=dev).manual_seed(11)
+        src_x = [x] + [torch.randn((T, H), generator=gen, device=dev).bfloat16() for _ in range(1, G)]
+        src_i = [idx] + others
+        src_w = [wt] + [torch.full((T, k), 1.0 / k, dtype=torch.float32, device=dev)
+                        for _ in range(1, G)]
+        pc = torch.empty(El, **i32)
+        po = torch.empty(El + 1, **i32)
+        pslot = torch.empty((G * T, k), **i32)
+        pws_bytes = ep.layout_workspace_size(G * T, k, El)
+        pws = torch.empty(pws_bytes, dtype=torch.uint8, device=dev)
+    stream.synchronize()
+    check(L.ep_layout(rq["rti"], G * T, k, El, pc.data_ptr(), po.data_ptr(), pslot.data_ptr(), None,
+                      None, pws.data_ptr(), pws_bytes, s), "ep_layout (received rows)")
+    stream.synchronize()
+    n_exp = int(po[El].item())
+    n_recv = int(rl["nrecv"].item())
+    with torch.cuda.stream(stream):
+        perm_x = torch.empty((n_exp, H), dtype=torch.bfloat16, device=dev)
+        perm_w = torch.empty(n_exp, dtype=torch.float32, device=dev)
+    stream.synchronize()
+    sxt = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_x])
+    sit = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_i])
+    swt = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_w])
+    fp_us = time_call(lambda: check(L.ep_dispatch_fused_permute(
+        ctypes.addressof(sxt), ctypes.addressof(sit), ctypes.addressof(swt), T, H, k, E, G, 0,
+        rq["rsrc"], rq["rti"], pslot.data_ptr(), n_exp, perm_x.data_ptr(), perm_w.data_ptr(), s),
+        "ep_dispatch_fused_permute"), args.steps)
+    # read each received token once, write each expert row once, read the
+    # receive-side rows (source, local experts, slots) and the senders'
+    # topk rows, write the row weights
+    fp_bytes = (n_recv * H * 2 + n_exp * H * 2 + G * T * (4 + k * 8 + k * 4) + n_recv * k * 12
+                + n_exp * 4)
+    del src_x, perm_x
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly 1 GiB each
         a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
@@ -427,6 +466,8 @@ def main():
                             "rows_written": pairs, "expanded_rows": n},
         "combine_ranked": {"us": round(cr_us, 2), "bytes": rbm["combine_ranked"], "ranks": G,
                            "rows_read": pairs},
+        "dispatch_fused_permute": {"us": round(fp_us, 2), "bytes": fp_bytes, "ranks": G,
+                                   "tokens_received": n_recv, "expert_rows_written": n_exp},
         "layout_aligned128": {"us": round(lay_a128, 2)},
         "layout_capacity320": {"us": round(lay_cap, 2), "dropped_pairs": dropped_cap},
     }

@@ -113,6 +113,7 @@ KERNEL_KEYS = {
     "rank_scatter": r"rank_scatter_kernel<",
     "dispatch_ranked": r"dispatch_ranked_kernel<",
     "combine_ranked": r"combine_ranked_kernel<",
+    "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
 
