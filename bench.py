@@ -335,14 +335,16 @@ def main():
     # the tokens' own E4M3 rows and scales, for the pre-quantized input
     check(L.ep_dispatch(xf.data_ptr(), T, H, 1, ident.data_ptr(), None, 1, xq_tok.data_ptr(),
                         xs_tok.data_ptr(), None, s), "ep_dispatch fp8 (tokens)")
-    for name, fmt, mode, sbuf in (("e5m2_fp32", 2, 0, sc), ("e4m3_pow2", 1, 1, sc),
-                                  ("e4m3_ue8m0", 1, 2, sc_b), ("e5m2_ue8m0", 2, 2, sc_b)):
+    # (column-major scales: [H/128, P], each block's scales contiguous over rows)
+    for name, fmt, mode, sbuf, ld in (("e5m2_fp32", 2, 0, sc, 0), ("e4m3_pow2", 1, 1, sc, 0),
+                                      ("e4m3_ue8m0", 1, 2, sc_b, 0), ("e5m2_ue8m0", 2, 2, sc_b, 0),
+                                      ("e4m3_fp32_colmajor", 1, 0, sc, P)):
         variants[name] = time_call(lambda: check(L.ep_dispatch_ex(
             xf.data_ptr(), T, H, k, slotf.data_ptr(), None, fmt, mode, q.data_ptr(),
-            sbuf.data_ptr(), None, s), "ep_dispatch_ex"), args.steps)
+            sbuf.data_ptr(), None, ld, s), "ep_dispatch_ex"), args.steps)
     variants["prequantized"] = time_call(lambda: check(L.ep_dispatch_prequantized(
         xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
-        sc.data_ptr(), None, s), "ep_dispatch_prequantized"), args.steps)
+        sc.data_ptr(), None, 0, s), "ep_dispatch_prequantized"), args.steps)
 
     # ---- per-(token, rank) path: G = 8 ranks of the headline shape on this
     # device (rank 0 holds the headline tokens, ranks 1..7 uniform routing);

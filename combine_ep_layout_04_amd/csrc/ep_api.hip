@@ -139,10 +139,21 @@ int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num
                         src, num_invalid, nullptr, workspace, workspace_bytes, stream);
 }
 
+// scale_ld: 0, or a positive multiple of the 16-byte column alignment
+static int check_scale_ld(int64_t scale_ld, int elem_bytes)
+{
+    const int64_t align = 16 / elem_bytes;
+    if (scale_ld < 0 || (scale_ld > 0 && scale_ld % align != 0))
+        return fail(EP_INVALID_ARGUMENT,
+                    "scale_ld %lld must be 0 (row-major) or a positive multiple of %lld",
+                    (long long)scale_ld, (long long)align);
+    return EP_SUCCESS;
+}
+
 int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
                    const int32_t* slot, const float* topk_weights, int out_dtype,
                    int scale_format, void* recv_x, void* recv_scales, float* recv_weights,
-                   void* stream)
+                   int64_t scale_ld, void* stream)
 {
     g_last_error[0] = '\0';
     int st = check_tokens(num_tokens, num_topk);
@@ -157,6 +168,9 @@ int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
         return fail(EP_INVALID_ARGUMENT, "bf16 output takes no scale format");
     st = check_hidden(hidden, fp8 ? 128 : 8);
     if (st) return st;
+    if (!fp8 && scale_ld != 0) return fail(EP_INVALID_ARGUMENT, "bf16 output takes no scale_ld");
+    st = check_scale_ld(scale_ld, scale_format == EP_SCALE_UE8M0 ? 1 : 4);
+    if (st) return st;
     if (num_tokens == 0) return EP_SUCCESS;
     if (!x || !slot || !recv_x) return fail(EP_INVALID_ARGUMENT, "x, slot and recv_x are required");
     if (!aligned16(x) || !aligned16(recv_x))
@@ -169,7 +183,7 @@ int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
             return fail(EP_INVALID_ARGUMENT, "fp32 recv_scales must be 4-byte aligned");
         return from_hip(ep::launch_dispatch_fp8(x, num_tokens, hidden, num_topk, slot, topk_weights,
                                                 out_dtype == EP_OUT_FP8_E5M2 ? 1 : 0, scale_format,
-                                                recv_x, recv_scales, recv_weights,
+                                                recv_x, recv_scales, recv_weights, scale_ld,
                                                 static_cast<hipStream_t>(stream)),
                         "ep_dispatch (fp8) launch");
     }
@@ -184,18 +198,20 @@ int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
                 float* recv_scales, float* recv_weights, void* stream)
 {
     return ep_dispatch_ex(x, num_tokens, hidden, num_topk, slot, topk_weights, out_dtype,
-                          EP_SCALE_FP32, recv_x, recv_scales, recv_weights, stream);
+                          EP_SCALE_FP32, recv_x, recv_scales, recv_weights, 0, stream);
 }
 
 int ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num_tokens,
                              int hidden, int num_topk, const int32_t* slot,
                              const float* topk_weights, void* recv_q, float* recv_scales,
-                             float* recv_weights, void* stream)
+                             float* recv_weights, int64_t scale_ld, void* stream)
 {
     g_last_error[0] = '\0';
     int st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 128);
+    if (st) return st;
+    st = check_scale_ld(scale_ld, 4);
     if (st) return st;
     if (num_tokens == 0) return EP_SUCCESS;
     if (!x_q || !x_scales || !slot || !recv_q || !recv_scales)
@@ -208,7 +224,7 @@ int ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num
         return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
     return from_hip(ep::launch_dispatch_prequant(x_q, x_scales, num_tokens, hidden, num_topk, slot,
                                                  topk_weights, recv_q, recv_scales, recv_weights,
-                                                 static_cast<hipStream_t>(stream)),
+                                                 scale_ld, static_cast<hipStream_t>(stream)),
                     "ep_dispatch_prequantized launch");
 }
 

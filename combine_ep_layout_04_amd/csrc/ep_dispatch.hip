@@ -309,13 +309,15 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, ui
 // vectors, one 16-byte output vector); a pass covers up to 64*VPT units and
 // 8*VPT <= 64 blocks.  Units past the row end read zeros and store nothing
 // (hidden is a multiple of 128, so an 8-lane block group is all in or all
-// out).  Scales go out as fp32 (modes 0, 1) or bytes (mode 2).
+// out).  Scales go out as fp32 (modes 0, 1) or bytes (mode 2), row-major
+// [rows, nb] (sld == 0) or column-major [nb, sld] (block b of row r at
+// b * sld + r).
 template <int VPT, int FMT, int SM>
 __global__ __launch_bounds__(64)
 void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
                          const int32_t* __restrict__ slot, const float* __restrict__ w,
                          uint4* __restrict__ recv_q, void* __restrict__ recv_s,
-                         float* __restrict__ recv_w)
+                         float* __restrict__ recv_w, int64_t sld)
 {
     constexpr int kPass = 64 * VPT;
     __shared__ uint32_t srow[kPass / kLanesPerBlock];
@@ -363,10 +365,11 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
                 if (unit < units) store_nt(dq + unit, q[u]);
             }
             if (tid < pass_blocks) {
+                const int64_t at = sld == 0 ? (int64_t)r * nb + b0 + tid : (int64_t)(b0 + tid) * sld + r;
                 if (SM == kScaleUe8m0)
-                    static_cast<uint8_t*>(recv_s)[(int64_t)r * nb + b0 + tid] = (uint8_t)my_scale;
+                    static_cast<uint8_t*>(recv_s)[at] = (uint8_t)my_scale;
                 else
-                    static_cast<uint32_t*>(recv_s)[(int64_t)r * nb + b0 + tid] = my_scale;
+                    static_cast<uint32_t*>(recv_s)[at] = my_scale;
             }
         }
         __syncthreads();
@@ -376,12 +379,13 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 // Pre-quantized input: the 8-bit code row (hidden bytes, VPT 16-byte units
 // per lane per pass) and the fp32 scale row of token t are copied to every
 // unmasked slot.  No arithmetic: any 8-bit float format passes through.
+// Output scales row-major (sld == 0) or column-major [nb, sld].
 template <int VPT>
 __global__ __launch_bounds__(64)
 void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restrict__ xs,
                               int units, int k, const int32_t* __restrict__ slot,
                               const float* __restrict__ w, uint4* __restrict__ recv_q,
-                              float* __restrict__ recv_s, float* __restrict__ recv_w)
+                              float* __restrict__ recv_s, float* __restrict__ recv_w, int64_t sld)
 {
     constexpr int kPass = 64 * VPT;
     const int64_t t = blockIdx.x;
@@ -418,7 +422,7 @@ void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restr
         const float v = b < nb ? xs[t * nb + b] : 0.0f;
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
-            if (r >= 0 && b < nb) recv_s[(int64_t)r * nb + b] = v;
+            if (r >= 0 && b < nb) recv_s[sld == 0 ? (int64_t)r * nb + b : (int64_t)b * sld + r] = v;
         }
     }
 }
@@ -498,11 +502,11 @@ static int units_per_lane(int units)
 template <int FMT, int SM>
 static void launch_fp8_shape(int vpt, dim3 grid, hipStream_t stream, const uint4* xx, int nvec,
                              int k, const int32_t* slot, const float* w, uint4* qq, void* ss,
-                             float* rw)
+                             float* rw, int64_t sld)
 {
 #define EP_FP8(V)                                                                             \
     hipLaunchKernelGGL((dispatch_fp8_kernel<V, FMT, SM>), grid, dim3(64), 0, stream, xx, nvec, \
-                       k, slot, w, qq, ss, rw)
+                       k, slot, w, qq, ss, rw, sld)
     switch (vpt) {
     case 1: EP_FP8(1); break;
     case 2: EP_FP8(2); break;
@@ -519,7 +523,7 @@ static void launch_fp8_shape(int vpt, dim3 grid, hipStream_t stream, const uint4
 hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk,
                                const int32_t* slot, const float* topk_weights, int format,
                                int scale_mode, void* recv_q, void* recv_scales,
-                               float* recv_weights, hipStream_t stream)
+                               float* recv_weights, int64_t scale_ld, hipStream_t stream)
 {
     if (num_tokens == 0) return hipSuccess;
     const int nvec = hidden / 8;
@@ -529,7 +533,7 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     uint4* qq = static_cast<uint4*>(recv_q);
 #define EP_FP8_MODE(F, M)                                                                    \
     launch_fp8_shape<F, M>(vpt, grid, stream, xx, nvec, num_topk, slot, topk_weights, qq,    \
-                           recv_scales, recv_weights)
+                           recv_scales, recv_weights, scale_ld)
     if (format == kE5M2) {
         if (scale_mode == kScalePow2) EP_FP8_MODE(kE5M2, kScalePow2);
         else if (scale_mode == kScaleUe8m0) EP_FP8_MODE(kE5M2, kScaleUe8m0);
@@ -546,7 +550,7 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
 hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num_tokens,
                                     int hidden, int num_topk, const int32_t* slot,
                                     const float* topk_weights, void* recv_q, float* recv_scales,
-                                    float* recv_weights, hipStream_t stream)
+                                    float* recv_weights, int64_t scale_ld, hipStream_t stream)
 {
     if (num_tokens == 0) return hipSuccess;
     const int units = hidden / 16;
@@ -556,7 +560,7 @@ hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num
     uint4* rq = static_cast<uint4*>(recv_q);
 #define EP_PQ(V)                                                                                   \
     hipLaunchKernelGGL((dispatch_prequant_kernel<V>), grid, dim3(64), 0, stream, qq, xs, units,     \
-                       num_topk, slot, topk_weights, rq, recv_scales, recv_weights)
+                       num_topk, slot, topk_weights, rq, recv_scales, recv_weights, scale_ld)
     switch (vpt) {
     case 1: EP_PQ(1); break;
     case 2: EP_PQ(2); break;

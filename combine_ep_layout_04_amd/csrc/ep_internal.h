@@ -31,16 +31,18 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, i
                                 float* recv_weights, hipStream_t stream);
 
 // format: 0 OCP E4M3, 1 OCP E5M2; scale_mode: 0 fp32 amax/max_finite,
-// 1 power of two (fp32), 2 power of two as a UE8M0 byte.
+// 1 power of two (fp32), 2 power of two as a UE8M0 byte.  scale_ld: 0 for
+// row-major scales [rows, hidden/128], else column-major [hidden/128,
+// scale_ld].
 hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk,
                                const int32_t* slot, const float* topk_weights, int format,
                                int scale_mode, void* recv_q, void* recv_scales,
-                               float* recv_weights, hipStream_t stream);
+                               float* recv_weights, int64_t scale_ld, hipStream_t stream);
 
 hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num_tokens,
                                     int hidden, int num_topk, const int32_t* slot,
                                     const float* topk_weights, void* recv_q, float* recv_scales,
-                                    float* recv_weights, hipStream_t stream);
+                                    float* recv_weights, int64_t scale_ld, hipStream_t stream);
 
 // row_w / out_w: optional gather out_w[t,j] = row_w[slot[t,j]] (dispatch
 // backward); both NULL for a plain combine.

@@ -86,9 +86,9 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_max_rows.restype = i64
         L.ep_dispatch.argtypes = [P, i64, i32, i32, P, P, i32, P, P, P, P]
         L.ep_dispatch.restype = i32
-        L.ep_dispatch_ex.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P, P]
+        L.ep_dispatch_ex.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P, i64, P]
         L.ep_dispatch_ex.restype = i32
-        L.ep_dispatch_prequantized.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, P]
+        L.ep_dispatch_prequantized.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, P]
         L.ep_dispatch_prequantized.restype = i32
         L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
         L.ep_combine.restype = i32
@@ -233,12 +233,14 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
                 *, fp8: bool = False, fmt: str = "e4m3", scale: str = "fp32", recv_x=None,
                 recv_scales=None, recv_weights=None,
                 want_weights: bool = False, rows: Optional[int] = None,
-                trust_slots: bool = False, stream=None):
+                trust_slots: bool = False, scale_ld: int = 0, stream=None):
     """Permute (bf16) or cast (fp8 e4m3 + per-128 fp32 scales) the rows of
     ``x`` (bf16 [T, H]) into the expert-grouped buffer named by ``slot``.
 
     With ``fp8`` the cast format is ``fmt`` ("e4m3" / "e5m2") and the scale
-    ``scale`` ("fp32", "pow2", "ue8m0" -- the last gives uint8 scales).
+    ``scale`` ("fp32", "pow2", "ue8m0" -- the last gives uint8 scales);
+    ``scale_ld`` > 0 stores the scales column-major, [H/128, scale_ld]
+    (scale_ld >= rows, a multiple of 4 fp32 / 16 UE8M0 scales).
 
     Returns (recv_x, recv_scales or None, recv_weights or None); recv_x is
     bf16 [rows, H] or uint8 [rows, H].  ``rows`` is the layout's row bound
@@ -259,8 +261,12 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
     if recv_x is None:
         recv_x = torch.empty((R, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
     sdt = torch.uint8 if scale == "ue8m0" else torch.float32
+    nb = H // 128
+    if scale_ld:
+        if scale_ld < R:
+            raise ValueError(f"scale_ld {scale_ld} is below the layout's {R} rows")
     if fp8 and recv_scales is None:
-        recv_scales = torch.empty((R, H // 128), dtype=sdt, device=dev)
+        recv_scales = torch.empty((nb, scale_ld) if scale_ld else (R, nb), dtype=sdt, device=dev)
     if want_weights and recv_weights is None:
         recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
     if topk_weights is not None:
@@ -270,13 +276,14 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
     if recv_x.shape[-1] != H:
         raise ValueError("recv_x rows must have hidden elements")
     if recv_scales is not None:
-        _need(recv_scales, "recv_scales", sdt, cap * (H // 128))
+        _need(recv_scales, "recv_scales", sdt, nb * scale_ld if scale_ld else cap * nb)
     if recv_weights is not None:
         _need(recv_weights, "recv_weights", torch.float32, cap)
     st = lib().ep_dispatch_ex(_ptr(x), T, H, k, _ptr(slot), _ptr(topk_weights),
                               _FORMATS[fmt] if fp8 else EP_OUT_BF16,
                               _SCALES[scale] if fp8 else EP_SCALE_FP32, _ptr(recv_x),
-                              _ptr(recv_scales), _ptr(recv_weights), _stream(stream))
+                              _ptr(recv_scales), _ptr(recv_weights), int(scale_ld),
+                              _stream(stream))
     _check(st, "ep_dispatch")
     return recv_x, recv_scales, recv_weights
 
@@ -284,10 +291,11 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
 def ep_dispatch_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor, slot: torch.Tensor,
                              topk_weights: Optional[torch.Tensor] = None, *, recv_q=None,
                              recv_scales=None, recv_weights=None, want_weights: bool = False,
-                             rows: Optional[int] = None, stream=None):
+                             rows: Optional[int] = None, scale_ld: int = 0, stream=None):
     """Copy pre-quantized rows (uint8 [T, H]) and their fp32 scales
-    ([T, H/128]) to the expert-grouped buffer.  Returns (recv_q,
-    recv_scales, recv_weights or None)."""
+    ([T, H/128]) to the expert-grouped buffer (scales column-major
+    [H/128, scale_ld] when scale_ld > 0).  Returns (recv_q, recv_scales,
+    recv_weights or None)."""
     _need(x_q, "x_q", torch.uint8)
     _need(x_scales, "x_scales", torch.float32)
     _need(slot, "slot", torch.int32)
@@ -301,19 +309,23 @@ def ep_dispatch_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor, slot: to
     dev = x_q.device
     if recv_q is None:
         recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    nb = H // 128
+    if scale_ld and scale_ld < R:
+        raise ValueError(f"scale_ld {scale_ld} is below the layout's {R} rows")
     if recv_scales is None:
-        recv_scales = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+        recv_scales = torch.empty((nb, scale_ld) if scale_ld else (R, nb), dtype=torch.float32,
+                                  device=dev)
     if want_weights and recv_weights is None:
         recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
     _need(recv_q, "recv_q", torch.uint8, R * H)
-    _need(recv_scales, "recv_scales", torch.float32, R * (H // 128))
+    _need(recv_scales, "recv_scales", torch.float32, nb * scale_ld if scale_ld else R * nb)
     if topk_weights is not None:
         _need(topk_weights, "topk_weights", torch.float32, T * k)
     if recv_weights is not None:
         _need(recv_weights, "recv_weights", torch.float32, R)
     st = lib().ep_dispatch_prequantized(_ptr(x_q), _ptr(x_scales), T, H, k, _ptr(slot),
                                         _ptr(topk_weights), _ptr(recv_q), _ptr(recv_scales),
-                                        _ptr(recv_weights), _stream(stream))
+                                        _ptr(recv_weights), int(scale_ld), _stream(stream))
     _check(st, "ep_dispatch_prequantized")
     return recv_q, recv_scales, recv_weights
 

@@ -229,6 +229,14 @@ int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
  *                 recv_scales is fp32 [rows, hidden/128] or, for UE8M0,
  *                 bytes [rows, hidden/128].  bf16 output takes
  *                 EP_SCALE_FP32 only.
+ *   scale_ld      0: recv_scales row-major [rows, hidden/128].  > 0:
+ *                 column-major [hidden/128, scale_ld] (block b of row r at
+ *                 b*scale_ld + r: each block's scales contiguous over rows,
+ *                 the layout a grouped GEMM reads per K block -- DeepEP
+ *                 page, dispatch() use_tma_aligned_col_major_sf); scale_ld
+ *                 must be a multiple of 16 bytes' worth of scales (4 fp32, 16
+ *                 UE8M0) and at least the layout's rows; entries of rows
+ *                 nothing maps to are not written.  fp8 output only.
  * amax ignores NaN.  amax == 0: codes 0 and scale 0 (fp32) or byte 0.  An
  * infinite amax: scale inf (fp32) or byte 0xFF, finite x encode to signed
  * zero; a NaN quotient gives 0x7F with the sign of x (both formats).
@@ -237,7 +245,7 @@ int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
 int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
                    const int32_t *slot, const float *topk_weights, int out_dtype,
                    int scale_format, void *recv_x, void *recv_scales, float *recv_weights,
-                   void *stream);
+                   int64_t scale_ld, void *stream);
 
 /*
  * ep_dispatch_prequantized -- dispatch of tokens that are already 8-bit
@@ -252,14 +260,15 @@ int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
  * In:  x_q       bytes [num_tokens, hidden], 16-byte aligned.
  *      x_scales  fp32 [num_tokens, hidden/128].
  *      slot, topk_weights as ep_dispatch.
- * Out: recv_q [rows, hidden], recv_scales fp32 [rows, hidden/128],
+ * Out: recv_q [rows, hidden], recv_scales fp32 [rows, hidden/128] (scale_ld
+ *      0) or column-major [hidden/128, scale_ld] (as ep_dispatch_ex),
  *      recv_weights [rows] or NULL.
  * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
  */
 int ep_dispatch_prequantized(const void *x_q, const float *x_scales, int64_t num_tokens,
                              int hidden, int num_topk, const int32_t *slot,
                              const float *topk_weights, void *recv_q, float *recv_scales,
-                             float *recv_weights, void *stream);
+                             float *recv_weights, int64_t scale_ld, void *stream);
 
 /*
  * ep_combine -- weighted reduction of expert outputs back to token order.

@@ -317,3 +317,24 @@ def test_dispatch_fused_permute_zero_tokens_is_a_noop():
     assert ep.lib().ep_dispatch_fused_permute(ctypes.addressof(sx), None, None, 0, 256, 2, 8, 2,
                                               0, None, None, None, 0, None, None, None) == 0
     assert ep.last_error() == ""
+
+
+@no_gpu
+@pytest.mark.parametrize("fmt,scale,ld,code", [
+    (1, 0, 6, 1),      # fp32 scales: ld not a multiple of 4
+    (1, 2, 20, 1),     # UE8M0: ld not a multiple of 16
+    (1, 0, -4, 1),     # negative
+    (0, 0, 16, 1),     # bf16 output takes no scale_ld
+])
+def test_dispatch_ex_rejects_scale_ld(fmt, scale, ld, code):
+    st = ep.lib().ep_dispatch_ex(FAKE, 4, 256, 2, FAKE, None, fmt, scale, FAKE,
+                                 FAKE if fmt else None, None, ld, None)
+    assert st == code, ep.last_error()
+    assert "scale_ld" in ep.last_error()
+
+
+@no_gpu
+def test_dispatch_prequantized_rejects_scale_ld():
+    st = ep.lib().ep_dispatch_prequantized(FAKE, FAKE, 4, 256, 2, FAKE, None, FAKE, FAKE, None,
+                                           6, None)
+    assert st == 1 and "scale_ld" in ep.last_error()

@@ -101,3 +101,62 @@ def test_prequantized_dispatch(name):
     # and it equals casting on the fly
     gq, gs = run(inp.x_bits, L.slot, "e4m3", "fp32", rows)
     np.testing.assert_array_equal(host(q)[:n], gq[:n])
+
+
+def run_colmajor(x_bits, slot, fmt, mode, rows, ld):
+    T, H = x_bits.shape
+    nb = H // 128
+    q = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    sdt = torch.uint8 if mode == "ue8m0" else torch.float32
+    s = torch.full((nb, ld), 0xAB if mode == "ue8m0" else float("nan"), dtype=sdt, device=DEV)
+    ep.ep_dispatch(x_dev(x_bits), dev(slot), None, fp8=True, fmt=fmt, scale=mode, recv_x=q,
+                   recv_scales=s, rows=rows, scale_ld=ld)
+    torch.cuda.synchronize()
+    return host(q), host(s)
+
+
+@pytest.mark.parametrize("name", ["special", "mid"])
+@pytest.mark.parametrize("fmt,mode", COMBOS)
+def test_column_major_scales(name, fmt, mode):
+    # block b of row r at b * ld + r: the row-major scales transposed; the
+    # columns' tails (rows nothing maps to, and the padding up to ld) stay
+    # untouched
+    if name == "special":
+        inp, xb = special_rows()
+        E = 8
+    else:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        xb, E = inp.x_bits, w.E
+    print(f"\n[fp8 variants] column-major scales {name} {fmt} {mode}", flush=True)
+    L = oracle.layout(inp.topk_idx, E)
+    rows = xb.shape[0] * L.slot.shape[1]
+    align = 16 if mode == "ue8m0" else 4
+    ld = (rows + align - 1) // align * align + align
+    gq, gs = run_colmajor(xb, L.slot, fmt, mode, rows, ld)
+    oq, os_, _ = oracle.dispatch_quant(xb, L.slot, fmt=fmt, scale=mode, rows=rows)
+    n = L.n
+    np.testing.assert_array_equal(gq[:n], oq[:n])
+    np.testing.assert_array_equal(gs[:, :n].view(np.uint8), os_[:n].T.copy().view(np.uint8))
+    tail = gs[:, n:]
+    assert np.all(tail == 0xAB) if mode == "ue8m0" else np.all(np.isnan(tail))
+
+
+def test_prequantized_column_major_scales():
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w)
+    T, H, k = w.T, w.H, w.k
+    xq, xs, _ = oracle.dispatch_quant(inp.x_bits, np.arange(T, dtype=np.int32)[:, None])
+    L = oracle.layout(inp.topk_idx, w.E)
+    rows = T * k
+    ld = rows + 4
+    q = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    s = torch.full((H // 128, ld), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized(dev(xq), dev(xs), dev(L.slot), None, recv_q=q, recv_scales=s,
+                                scale_ld=ld)
+    torch.cuda.synchronize()
+    oq, os_, _ = oracle.dispatch_prequant(xq, xs, L.slot)
+    n = L.n
+    np.testing.assert_array_equal(host(q)[:n], oq[:n])
+    np.testing.assert_array_equal(host(s)[:, :n].view(np.uint32), os_[:n].T.copy().view(np.uint32))
+    assert np.all(np.isnan(host(s)[:, n:]))
