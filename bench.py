@@ -5,15 +5,21 @@ One step = ep_layout -> ep_dispatch (bf16) -> ep_combine over the headline
 workload: T=8192 tokens, hidden 7168 bf16, 256 experts, top-8 distinct
 uniform routing, fp32 row-normalised weights, identity experts (combine
 reduces the dispatched rows).  Inputs are seeded synthetic data resident in
-HBM before timing starts.  ``value`` is the dispatch + combine algorithmic
-bytes of one step divided by the wall time of a step (layout included).
+HBM before timing starts.  Every timed step and launch is preceded by a
+1 GiB scratch read (outside its timing events), so inputs come from HBM,
+not from the 256 MB last-level cache.  ``value`` is the dispatch + combine
+algorithmic bytes of one step divided by the step's time (HIP events from
+the layout launch to the end of the combine, layout included).
 
-Also reported: per-kernel averages from HIP events recorded on the launch
-stream, the fp8 dispatch (same shape, with 1% x100 outlier rows) timed in
-its own loop, the roofline of the dominant kernel, and the CPU oracle timed
-on the host on the same workload.
+Also reported: per-kernel mean / median / p10 / p90 from HIP events recorded
+on the launch stream, the fp8 dispatch and its variants (same shape, 1%
+x100 outlier rows), the backward passes, the layout variants, the
+per-(token, rank) path at 8 ranks, a plain device-to-device copy for
+context, the roofline of the dominant kernel, and the CPU oracle timed on
+the host on the same workload.  ``--warm`` adds the same steps back to back
+without flushes, for context.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm]
 """
 
 from __future__ import annotations
@@ -58,12 +64,12 @@ KERNEL_SOURCES = {
 
 def source_digest(kernel_key: str) -> str:
     """Digest of what a kernel's counters depend on: its source file, the
-    internal header and the hipcc flags."""
+    internal and device headers and the hipcc flags."""
     from combine_ep_layout_04_amd.build import HIPCC_FLAGS
 
     csrc = os.path.join(ROOT, "combine_ep_layout_04_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h"):
+    for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h", "ep_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     h.update(" ".join(HIPCC_FLAGS).encode())
@@ -124,23 +130,36 @@ def read_traffic(kernel_key: str):
     return None
 
 
-def cpu_baseline(inp, E, nbytes):
-    """The oracle as it stands (single-threaded C) on the full workload."""
+def cpu_baseline(inp, inp_fp8, E, nbytes):
+    """The oracle as it stands (single-threaded C) on the full workload, and
+    each of its operations timed alone (median of 3)."""
     import oracle
 
-    times = []
+    times, ops = [], {"layout": [], "dispatch_bf16": [], "combine": [], "dispatch_fp8": []}
     for _ in range(3):
         t0 = time.perf_counter()
         L = oracle.layout(inp.topk_idx, E)
+        t1 = time.perf_counter()
         recv, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+        t2 = time.perf_counter()
         oracle.combine(recv, L.slot, inp.topk_weights)
-        times.append(time.perf_counter() - t0)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        ops["layout"].append(t1 - t0)
+        ops["dispatch_bf16"].append(t2 - t1)
+        ops["combine"].append(t3 - t2)
         del recv
+        Lf = oracle.layout(inp_fp8.topk_idx, E)
+        t4 = time.perf_counter()
+        oracle.dispatch_fp8(inp_fp8.x_bits, Lf.slot)
+        ops["dispatch_fp8"].append(time.perf_counter() - t4)
     t = statistics.median(times)
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "full headline workload (T=8192, H=7168, E=256, k=8): oracle layout + "
                       "bf16 dispatch + fp64 combine, single thread, median of 3 runs "
-                      f"({t:.2f} s each)", "seconds_per_step": round(t, 3)}
+                      f"({t:.2f} s each)", "seconds_per_step": round(t, 3),
+            "seconds_per_op": {k: round(statistics.median(v), 4) for k, v in ops.items()},
+            "host_cores_available": len(os.sched_getaffinity(0))}
 
 
 def main():
@@ -149,6 +168,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time the steps back to back without cache flushes (context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB elementwise copy (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -189,8 +210,19 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         recv = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     stream.synchronize()
     s = stream.cuda_stream
+
+    def flush():
+        """Read 1 GiB of scratch (4x the 256 MB last-level cache) so the next
+        launch finds its inputs in HBM, not in a cache.  A read leaves the
+        caches full of clean lines: the write-back of whatever was dirty is
+        paid here, not by the next kernel (a scratch *write* would leave
+        256 MB of dirty lines for the timed kernel to write back).  Issued
+        before every timed launch, outside its timing events."""
+        with torch.cuda.stream(stream):
+            scratch.sum()   # one reduction kernel over the 1 GiB, fp32 in and out
     p = {n: t.data_ptr() for n, t in dict(idx=idx, x=x, wt=wt, counts=counts, offsets=offsets,
                                           slot=slot, src=src, inval=inval, ws=ws, recv=recv,
                                           out=out).items()}
@@ -216,20 +248,39 @@ def main():
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
+        flush()
         step()
     stream.synchronize()
     n = int(offsets[E].item())
 
+    # K steps, each after a cache flush; a step's time runs from its layout
+    # launch to the end of its combine (HIP events on the launch stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        flush()
         step(evs[i])
     stream.synchronize()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    wall_ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = statistics.fmean([e[0].elapsed_time(e[3]) for e in evs])
+
+    warm = None
+    if args.warm:
+        # context only: the same steps back to back, caches as the previous
+        # step left them (x, read with cached loads, stays in the last-level
+        # cache while the non-temporal streams pass it by)
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(wev[i])
+        stream.synchronize()
+        wms = statistics.fmean([e[0].elapsed_time(e[3]) for e in wev])
+        warm = {"ms_per_step": round(wms, 4),
+                "dispatch_bf16_us": round(statistics.fmean([e[1].elapsed_time(e[2]) for e in wev]) * 1e3, 2),
+                "combine_us": round(statistics.fmean([e[2].elapsed_time(e[3]) for e in wev]) * 1e3, 2)}
 
     lay = [e[0].elapsed_time(e[1]) for e in evs]
     dis = [e[1].elapsed_time(e[2]) for e in evs]
@@ -261,9 +312,11 @@ def main():
                             sc.data_ptr(), None, s), "ep_dispatch fp8")
 
     for _ in range(args.warmup):
+        flush()
         fp8_step()
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for i in range(args.steps):
+        flush()
         fev[i][0].record(stream)
         fp8_step()
         fev[i][1].record(stream)
@@ -287,13 +340,14 @@ def main():
     def time_call(fn, reps):
         evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for i in range(-args.warmup, reps):
+            flush()
             if i >= 0:
                 evl[i][0].record(stream)
             fn()
             if i >= 0:
                 evl[i][1].record(stream)
         stream.synchronize()
-        return us([e[0].elapsed_time(e[1]) for e in evl])
+        return [e[0].elapsed_time(e[1]) for e in evl]
 
     cb_us = time_call(lambda: check(L.ep_combine_backward(
         gout.data_ptr(), p["recv"], p["slot"], p["wt"], T, H, k, grad_y.data_ptr(),
@@ -311,6 +365,7 @@ def main():
         drop = torch.empty(1, **i32)
         evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         for i in range(-args.warmup, reps):
+            flush()
             if i >= 0:
                 evl[i][0].record(stream)
             check(L.ep_layout_ex(p["idx"], T, k, E, alignment, capacity, p["counts"],
@@ -319,7 +374,7 @@ def main():
             if i >= 0:
                 evl[i][1].record(stream)
         stream.synchronize()
-        return us([e[0].elapsed_time(e[1]) for e in evl]), int(drop.item())
+        return [e[0].elapsed_time(e[1]) for e in evl], int(drop.item())
 
     lay_a128, _ = time_layout(128, 0, args.steps)
     lay_cap, dropped_cap = time_layout(1, 320, args.steps)
@@ -439,6 +494,19 @@ def main():
                 + n_exp * 4)
     del src_x, perm_x
 
+    # ---- context: a plain device-to-device copy of 1 GiB (read + write)
+    with torch.cuda.stream(stream):
+        c_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        c_dst = torch.empty_like(c_src)
+
+    def copy_on_stream():
+        with torch.cuda.stream(stream):
+            c_dst.copy_(c_src)
+
+    copy_ms = time_call(copy_on_stream, max(5, args.steps // 5))
+    copy_gbs = 2.0 * (1 << 30) / (statistics.median(copy_ms) * 1e-3) / 1e9
+    del c_src, c_dst
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly 1 GiB each
         a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
@@ -449,35 +517,43 @@ def main():
 
     bm = bytes_model(T, H, k, n)
     bmf = bytes_model(T, H, k, nf)
+
+    def entry(ms, **extra):
+        """mean (us, the roofline's figure), median and p10 / p90 of the
+        per-launch HIP-event times."""
+        q = statistics.quantiles(ms, n=10) if len(ms) > 1 else [ms[0]] * 9
+        return {"us": round(us(ms), 2), "median_us": round(statistics.median(ms) * 1e3, 2),
+                "p10_us": round(q[0] * 1e3, 2), "p90_us": round(q[-1] * 1e3, 2), **extra}
+
     per_kernel = {
-        "layout": {"us": round(us(lay), 2)},
-        "dispatch_bf16": {"us": round(us(dis), 2), "bytes": bm["dispatch_bf16"]},
-        "combine": {"us": round(us(com), 2), "bytes": bm["combine"]},
-        "dispatch_fp8": {"us": round(us(f8), 2), "bytes": bmf["dispatch_fp8"],
-                         "workload": "fp8: headline shape, 1% of rows x100"},
-        "combine_backward": {"us": round(cb_us, 2), "bytes": bm["combine_backward"]},
-        "dispatch_backward": {"us": round(db_us, 2), "bytes": bm["dispatch_backward"]},
-        **{f"dispatch_fp8_{name}": {"us": round(v, 2),
-                                    "bytes": bmf["dispatch_fp8_ue8m0" if "ue8m0" in name else
-                                                 ("dispatch_prequantized" if name == "prequantized"
-                                                  else "dispatch_fp8")]}
+        "layout": entry(lay),
+        "dispatch_bf16": entry(dis, bytes=bm["dispatch_bf16"]),
+        "combine": entry(com, bytes=bm["combine"]),
+        "dispatch_fp8": entry(f8, bytes=bmf["dispatch_fp8"],
+                              workload="fp8: headline shape, 1% of rows x100"),
+        "combine_backward": entry(cb_us, bytes=bm["combine_backward"]),
+        "dispatch_backward": entry(db_us, bytes=bm["dispatch_backward"]),
+        **{f"dispatch_fp8_{name}": entry(v, bytes=bmf["dispatch_fp8_ue8m0" if "ue8m0" in name else
+                                                      ("dispatch_prequantized" if name == "prequantized"
+                                                       else "dispatch_fp8")])
            for name, v in variants.items()},
-        "routing_map": {"us": round(rm_us, 2)},
-        "rank_layout": {"us": round(rk_us, 2), "ranks": G},
-        "dispatch_ranked": {"us": round(dr_us, 2), "bytes": rbm["dispatch_ranked"], "ranks": G,
-                            "rows_written": pairs, "expanded_rows": n},
-        "combine_ranked": {"us": round(cr_us, 2), "bytes": rbm["combine_ranked"], "ranks": G,
-                           "rows_read": pairs},
-        "dispatch_fused_permute": {"us": round(fp_us, 2), "bytes": fp_bytes, "ranks": G,
-                                   "tokens_received": n_recv, "expert_rows_written": n_exp},
-        "layout_aligned128": {"us": round(lay_a128, 2)},
-        "layout_capacity320": {"us": round(lay_cap, 2), "dropped_pairs": dropped_cap},
+        "routing_map": entry(rm_us),
+        "rank_layout": entry(rk_us, ranks=G),
+        "dispatch_ranked": entry(dr_us, bytes=rbm["dispatch_ranked"], ranks=G,
+                                 rows_written=pairs, expanded_rows=n),
+        "combine_ranked": entry(cr_us, bytes=rbm["combine_ranked"], ranks=G, rows_read=pairs),
+        "dispatch_fused_permute": entry(fp_us, bytes=fp_bytes, ranks=G, tokens_received=n_recv,
+                                        expert_rows_written=n_exp),
+        "layout_aligned128": entry(lay_a128),
+        "layout_capacity320": entry(lay_cap, dropped_pairs=dropped_cap),
     }
     for key, v in per_kernel.items():
         if "bytes" in v:
             gbs = v["bytes"] / (v["us"] * 1e-6) / 1e9
             v["GB_per_s"] = round(gbs, 1)
+            v["GB_per_s_at_median"] = round(v["bytes"] / (v["median_us"] * 1e-6) / 1e9, 1)
             v["frac_of_hbm_peak"] = round(gbs / HBM_PEAK_GBS, 4)
+            v["frac_of_d2d_copy"] = round(gbs / copy_gbs, 4)
             v["tokens_per_s"] = round(T / (v["us"] * 1e-6), 1)
         if key in KERNEL_SOURCES:
             v["traffic"] = read_traffic(key)
@@ -490,7 +566,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(inp, E, step_bytes)
+        cpu = cpu_baseline(inp, inpf, E, step_bytes)
 
     rec = {
         "metric": METRIC,
@@ -500,6 +576,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "wall_ms_per_step_incl_cache_flush": round(wall_ms_step, 4),
+        "caches": "a 1 GiB scratch read before every timed launch and step (outside its events)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -510,6 +588,9 @@ def main():
                                "+ weighted combine", "T": T, "H": H, "E": E, "k": k,
                    "dispatched_rows": n},
         "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "tokens_per_s_dispatch_plus_combine": round(
+            T / ((per_kernel["dispatch_bf16"]["us"] + per_kernel["combine"]["us"]) * 1e-6), 1),
+        "d2d_copy_GB_per_s": round(copy_gbs, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["GB_per_s"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dk["frac_of_hbm_peak"],
@@ -518,6 +599,7 @@ def main():
         "combine_returns_x": ok,
         "ranked_combine_returns_n_x": ranked_ok,
         "cpu_baseline": cpu,
+        "back_to_back": warm,
     }
     print(json.dumps(rec), flush=True)
 

@@ -25,12 +25,11 @@
 // decides; this is exact whenever w * g is not an fp32 subnormal.  The
 // branch-free form of that rule measured ~1.6x faster than a branchy one.
 
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -73,11 +72,6 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float acc)
     acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(b.w), acc);
     acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(b.w), acc);
     return acc;
-}
-
-__device__ __forceinline__ void store_nt(uint4* p, const uint4& v)
-{
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
 
 // y rows are read once: non-temporal buffer loads (gfx950 "nt" policy bit);
@@ -138,7 +132,7 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
                 if (r < 0) continue;
                 const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jg + q));
                 const uint4* yr = y + (int64_t)r * nvec;
-                uint4* dst = grad_y + (int64_t)r * nvec;
+                const __amdgpu_buffer_rsrc_t dst = buffer_rsrc(grad_y + (int64_t)r * nvec, nvec * 16);
                 if (want_dot) {
                     uint4 yv[VPT];
 #pragma unroll
@@ -149,7 +143,7 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
 #pragma unroll
                 for (int u = 0; u < VPT; ++u) {
                     const int v = p0 + tid + u * NT;
-                    if (v < nvec) store_nt(dst + v, scale_row8(wj, gv[u]));
+                    if (v < nvec) store_row16(dst, v * 16, scale_row8(wj, gv[u]));
                 }
             }
         }

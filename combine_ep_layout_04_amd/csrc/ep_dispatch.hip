@@ -34,6 +34,7 @@
 //     coalesced store per destination row: scattered 4-byte scale stores
 //     interleaved with the code stores measured ~30% slower.
 
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -81,15 +82,8 @@ __device__ __forceinline__ int32_t lane_value(int32_t v, int j)
 }
 
 // Destination rows are written once and not read again by this kernel:
-// non-temporal stores (the "nt" cache policy) measured ~12% faster than
-// cached stores on MI355X.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void store_nt(uint4* p, const uint4& v)
-{
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
-}
-
+// they go out as streaming buffer stores (store_row16: sc1 | nt), which
+// measured ~12% faster than cached stores on MI355X back to back.
 
 // Keeps a loaded vector in registers: without it the compiler may sink the
 // load into the destination loop and read the source row k times.
@@ -126,9 +120,9 @@ void dispatch_bf16_kernel(const uint4* __restrict__ x, int nvec, int k,
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
             if (r < 0) continue;
-            uint4* dst = recv + (int64_t)r * nvec + vb;
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16);
 #pragma unroll
-            for (int u = 0; u < VPT; ++u) store_nt(dst + u * NT, buf[u]);
+            for (int u = 0; u < VPT; ++u) store_row16(rs, (vb + u * NT) * 16, buf[u]);
         }
     }
     // ragged tail: one vector per lane
@@ -137,7 +131,7 @@ void dispatch_bf16_kernel(const uint4* __restrict__ x, int nvec, int k,
         keep(d);
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
-            if (r >= 0) store_nt(recv + (int64_t)r * nvec + v, d);
+            if (r >= 0) store_row16(buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16), v * 16, d);
         }
     }
 }
@@ -358,11 +352,11 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
             if (r < 0) continue;
-            uint4* dq = recv_q + (int64_t)r * units;
+            const __amdgpu_buffer_rsrc_t dq = buffer_rsrc(recv_q + (int64_t)r * units, units * 16);
 #pragma unroll
             for (int u = 0; u < VPT; ++u) {
                 const int unit = p0 + tid + u * 64;
-                if (unit < units) store_nt(dq + unit, q[u]);
+                if (unit < units) store_row16(dq, unit * 16, q[u]);
             }
             if (tid < pass_blocks) {
                 const int64_t at = sld == 0 ? (int64_t)r * nb + b0 + tid : (int64_t)(b0 + tid) * sld + r;
@@ -408,11 +402,11 @@ void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restr
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
             if (r < 0) continue;
-            uint4* dq = recv_q + (int64_t)r * units;
+            const __amdgpu_buffer_rsrc_t dq = buffer_rsrc(recv_q + (int64_t)r * units, units * 16);
 #pragma unroll
             for (int u = 0; u < VPT; ++u) {
                 const int unit = p0 + tid + u * 64;
-                if (unit < units) store_nt(dq + unit, d[u]);
+                if (unit < units) store_row16(dq, unit * 16, d[u]);
             }
         }
     }

@@ -51,6 +51,10 @@ namespace {
 
 constexpr int kMaxExperts = 1024;                 // EP_MAX_EXPERTS
 constexpr int kWords = kLayoutThreads / 32;       // bit words per expert per batch
+// LDS row stride of the bit matrix: one word of padding makes it odd, so
+// the rows of different experts start in different banks (a stride of 8
+// words put 64 lanes with random experts on 8 of the 32 banks)
+constexpr int kRowStride = kWords + 1;
 
 static_assert(kLayoutMinChunk % kLayoutThreads == 0, "chunk must be whole batches");
 
@@ -142,7 +146,7 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
     __shared__ int32_t total[kMaxExperts];
     __shared__ int32_t seg[kMaxExperts];
     __shared__ int32_t ndrop;
-    __shared__ uint32_t bits[kMaxExperts * kWords];
+    __shared__ uint32_t bits[kMaxExperts * kRowStride];
     __shared__ int32_t waves[kLayoutThreads / 64];
     __shared__ int32_t nbad;
     const int tid = threadIdx.x;
@@ -155,7 +159,7 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
         total[e] = all;
         base[e] = before;
     }
-    for (int w = tid; w < E * kWords; w += kLayoutThreads) bits[w] = 0;
+    for (int w = tid; w < E * kRowStride; w += kLayoutThreads) bits[w] = 0;
     if (tid == 0) nbad = 0;
     __syncthreads();
 
@@ -214,12 +218,12 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
         const int64_t e64 = live ? idx[i] : -1;
         const bool ok = e64 >= 0 && e64 < E;
         const int e = ok ? (int)e64 : 0;
-        if (ok) atomicOr(&bits[e * kWords + word], bit);
+        if (ok) atomicOr(&bits[e * kRowStride + word], bit);
         __syncthreads();
 
         int rank = 0, tot = 0;
         if (ok) {
-            const uint32_t* row = &bits[e * kWords];
+            const uint32_t* row = &bits[e * kRowStride];
 #pragma unroll
             for (int q = 0; q < kWords; ++q) {
                 const uint32_t m = row[q];
@@ -241,7 +245,7 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
 
         if (ok) {
             if (rank == tot - 1) base[e] += tot;   // the batch's last pair of e
-            bits[e * kWords + word] = 0;
+            bits[e * kRowStride + word] = 0;
         }
         __syncthreads();
     }

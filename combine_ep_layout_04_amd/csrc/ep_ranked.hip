@@ -47,6 +47,7 @@
 //                 0-byte resource: its loads return 0 without a branch) and
 //                 sums them in fp32 in increasing rank.
 
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -494,13 +495,6 @@ void rank_scatter_kernel(const uint8_t* __restrict__ map, int64_t R, int64_t T, 
 
 // --------------------------------------------------------------- dispatch
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void store_nt(uint4* p, const uint4& v)
-{
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
-}
-
 __device__ __forceinline__ void keep(uint4& v)
 {
     asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
@@ -578,9 +572,10 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
         for (int d = 0; d < G; ++d) {
             const int32_t r = __builtin_amdgcn_readlane(p, d);
             if (r < 0) continue;
-            uint4* dst = static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec + vb;
+            const __amdgpu_buffer_rsrc_t dst =
+                buffer_rsrc(static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec, nvec * 16);
 #pragma unroll
-            for (int u = 0; u < VPT; ++u) store_nt(dst + u * NT, buf[u]);
+            for (int u = 0; u < VPT; ++u) store_row16(dst, (vb + u * NT) * 16, buf[u]);
         }
     }
     for (int v = full * kPass + tid; v < nvec; v += NT) {
@@ -588,7 +583,9 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
         keep(val);
         for (int d = 0; d < G; ++d) {
             const int32_t r = __builtin_amdgcn_readlane(p, d);
-            if (r >= 0) store_nt(static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec + v, val);
+            if (r >= 0)
+                store_row16(buffer_rsrc(static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec, nvec * 16),
+                            v * 16, val);
         }
     }
 }
@@ -650,9 +647,9 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
         for (int j = 0; j < k; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(sl, j);
             if (r < 0) continue;
-            uint4* dst = recv_x + (int64_t)r * nvec + vb;
+            const __amdgpu_buffer_rsrc_t dst = buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16);
 #pragma unroll
-            for (int u = 0; u < VPT; ++u) store_nt(dst + u * NT, buf[u]);
+            for (int u = 0; u < VPT; ++u) store_row16(dst, (vb + u * NT) * 16, buf[u]);
         }
     }
     for (int v = full * kPass + tid; v < nvec; v += NT) {
@@ -660,7 +657,7 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
         keep(val);
         for (int j = 0; j < k; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(sl, j);
-            if (r >= 0) store_nt(recv_x + (int64_t)r * nvec + v, val);
+            if (r >= 0) store_row16(buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16), v * 16, val);
         }
     }
 }
