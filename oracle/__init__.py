@@ -94,6 +94,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
                                                     P, P]
         L.oracle_dispatch_fused_permute.restype = None
+        L.oracle_dispatch_ranked_prequant.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
+                                                      P]
+        L.oracle_dispatch_ranked_prequant.restype = None
         _lib = L
     return _lib
 
@@ -432,3 +435,30 @@ def dispatch_fused_permute(src_x, src_idx, src_w, E: int, rank: int, recv_src: n
                                         int(rank), _ptr(rs), _ptr(rti), _ptr(sl), _ptr(out),
                                         _ptr(rw))
     return out, rw
+
+
+def dispatch_ranked_prequant(xq: np.ndarray, xs: np.ndarray, topk_idx: np.ndarray,
+                             topk_weights: Optional[np.ndarray], E: int, G: int,
+                             sparse_to_dense: np.ndarray, rows, with_weights: bool = True):
+    """Once-per-rank dispatch of pre-quantized tokens: returns (dest_q list of
+    G uint8 [rows_d, H], dest_s list of G float32 [rows_d, H/128], dest_w
+    list of G float32 [rows_d, k] or None)."""
+    q = _c(xq, np.uint8)
+    sc = _c(xs, np.float32)
+    idx = _c(topk_idx, np.int64)
+    s2d = _c(sparse_to_dense, np.int32)
+    T, H = q.shape
+    k = idx.shape[1]
+    nb = H // 128
+    rows = [int(rows)] * G if np.isscalar(rows) else [int(r) for r in rows]
+    for d in range(G):
+        if s2d.size and s2d[:, d].max() >= rows[d]:
+            raise ValueError("a row is beyond a destination buffer")
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    dq = [np.zeros((rows[d], H), np.uint8) for d in range(G)]
+    ds = [np.zeros((rows[d], nb), np.float32) for d in range(G)]
+    dw = [np.zeros((rows[d], k), np.float32) for d in range(G)] if with_weights else None
+    lib().oracle_dispatch_ranked_prequant(_ptr(q), _ptr(sc), _ptr(idx), _ptr(w), T, H, k, int(E),
+                                          G, _ptr(s2d), _ptr_array(dq), _ptr_array(ds),
+                                          None if dw is None else _ptr_array(dw))
+    return dq, ds, dw

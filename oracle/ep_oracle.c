@@ -653,6 +653,32 @@ void oracle_rank_layout(const uint8_t *map, int64_t T, int E, int G, int rank, i
         *num_overflow = overflow;
 }
 
+/* Token t's weight row for rank d (k wide): the n-th selected expert of
+ * rank d in increasing expert order gets the fp32 sum, in increasing j, of
+ * the weights of the slots that select it (1 per slot without weights);
+ * 0 past the last one. */
+static void rank_weight_row(const int64_t *topk_idx, const float *topk_weights, int64_t t, int k,
+                            int d, int El, float *row)
+{
+    for (int n = 0; n < k; ++n)
+        row[n] = 0.0f;
+    int n = 0;
+    for (int e = d * El; e < (d + 1) * El; ++e) {
+        int hit = 0;
+        float s = 0.0f;
+        for (int j = 0; j < k; ++j)
+            if (topk_idx[t * k + j] == e) {
+                s = s + (topk_weights ? topk_weights[t * k + j] : 1.0f);
+                hit = 1;
+            }
+        if (hit) {
+            if (n < k)
+                row[n] = s;
+            ++n;
+        }
+    }
+}
+
 /*
  * Dispatch of rank `rank`'s tokens, once per destination rank (NCCL EP page,
  * ncclEpDispatch high-throughput branch: the token rows and, per received
@@ -678,26 +704,8 @@ void oracle_dispatch_ranked(const uint16_t *x, const int64_t *topk_idx, const fl
             if (p < 0)
                 continue;
             memcpy(dest_x[d] + (int64_t)p * H, x + t * H, (size_t)H * sizeof(uint16_t));
-            if (!dest_w || !dest_w[d])
-                continue;
-            float *row = dest_w[d] + (int64_t)p * k;
-            for (int n = 0; n < k; ++n)
-                row[n] = 0.0f;
-            int n = 0;
-            for (int e = d * El; e < (d + 1) * El; ++e) {
-                int hit = 0;
-                float s = 0.0f;
-                for (int j = 0; j < k; ++j)
-                    if (topk_idx[t * k + j] == e) {
-                        s = s + (topk_weights ? topk_weights[t * k + j] : 1.0f);
-                        hit = 1;
-                    }
-                if (hit) {
-                    if (n < k)
-                        row[n] = s;
-                    ++n;
-                }
-            }
+            if (dest_w && dest_w[d])
+                rank_weight_row(topk_idx, topk_weights, t, k, d, El, dest_w[d] + (int64_t)p * k);
         }
 }
 
@@ -768,4 +776,36 @@ void oracle_dispatch_fused_permute(const uint16_t *const *src_x, const int64_t *
             recv_w[r] = sum;
         }
     }
+}
+
+/*
+ * Once-per-rank dispatch of tokens already cast to 8 bits (NCCL EP page,
+ * ncclEpDispatch high-throughput branch: FP8 tokens come with a 2-D fp32
+ * scales tensor and travel as they are).  As oracle_dispatch_ranked, with
+ * the token's code row (H bytes) and scale row (H/128 fp32) copied to each
+ * destination rank that receives it:
+ *   dest_q[d][p] = xq[t], dest_s[d][p] = xs[t]     (p = sparse_to_dense[t,d])
+ * and the same weight rows as oracle_dispatch_ranked (dest_w may be NULL).
+ */
+void oracle_dispatch_ranked_prequant(const uint8_t *xq, const float *xs, const int64_t *topk_idx,
+                                     const float *topk_weights, int64_t T, int H, int k, int E,
+                                     int G, const int32_t *sparse_to_dense, uint8_t *const *dest_q,
+                                     float *const *dest_s, float *const *dest_w)
+{
+    int nb = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int d = 0; d < G; ++d) {
+            int32_t p = sparse_to_dense[t * G + d];
+            if (p < 0)
+                continue;
+            memcpy(dest_q[d] + (int64_t)p * H, xq + t * H, (size_t)H);
+            memcpy(dest_s[d] + (int64_t)p * nb, xs + t * nb, (size_t)nb * sizeof(float));
+        }
+    int El = E / G;
+    for (int64_t t = 0; t < T; ++t)
+        for (int d = 0; d < G; ++d) {
+            int32_t p = sparse_to_dense[t * G + d];
+            if (p >= 0 && dest_w && dest_w[d])
+                rank_weight_row(topk_idx, topk_weights, t, k, d, El, dest_w[d] + (int64_t)p * k);
+        }
 }

@@ -332,3 +332,33 @@ def test_fused_permute_is_rank_dispatch_then_expert_dispatch(seed, G, T, E, k, w
                                                      L[r].recv_topk_idx, Lr.slot, rows)
         np.testing.assert_array_equal(got_x, want_x)
         np.testing.assert_array_equal(got_w, want_w)
+
+
+@pytest.mark.parametrize("seed,G,E,k", [(0, 2, 8, 3), (1, 4, 16, 5), (2, 8, 64, 8)])
+def test_dispatch_ranked_prequant(seed, G, E, k):
+    # codes and scales: numpy fancy-index copies; weights: the bf16
+    # once-per-rank dispatch's weight rows on the same routing
+    T, H = 21, 256
+    inp = make_random_case(seed, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    rng = np.random.default_rng(seed)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    maps = [oracle.routing_map(make_random_case(seed + 9 + s, T, 8, E, k).topk_idx, E)[0]
+            for s in range(G)]
+    maps[0] = oracle.routing_map(inp.topk_idx, E)[0]
+    L = oracle.rank_layout(np.concatenate(maps), T, E, G, 0, k)
+    rows = G * T
+    dq, ds, dw = oracle.dispatch_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, E, G,
+                                                 L.sparse_to_dense, rows)
+    _, dw_ref = oracle.dispatch_ranked(inp.x_bits, inp.topk_idx, inp.topk_weights, E, G,
+                                       L.sparse_to_dense, rows)
+    for d in range(G):
+        p = L.sparse_to_dense[:, d]
+        ts = np.nonzero(p >= 0)[0]
+        want_q = np.zeros((rows, H), np.uint8)
+        want_q[p[ts]] = xq[ts]
+        want_s = np.zeros((rows, H // 128), np.float32)
+        want_s[p[ts]] = xs[ts]
+        np.testing.assert_array_equal(dq[d], want_q)
+        np.testing.assert_array_equal(ds[d], want_s)
+        np.testing.assert_array_equal(dw[d], dw_ref[d])
