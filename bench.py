@@ -55,7 +55,7 @@ KERNEL_SOURCES = {
     "dispatch_fp8_prequantized": "ep_dispatch.hip",
     "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
     "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
-    "dispatch_fused_permute": "ep_ranked.hip",
+    "dispatch_fused_permute": "ep_ranked.hip", "dispatch_ranked_prequantized": "ep_ranked.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -454,7 +454,23 @@ def main():
     n_t = (s2d_h >= 0).sum(dim=1).to(dev).view(T, 1).float()
     ranked_ok = bool(torch.equal(out_r, (x.float() * n_t).bfloat16()))
     rbm = ranked_bytes_model(T, H, k, G, pairs)
-    del dest, dest_w
+    del dest
+
+    # the same sends for 8-bit tokens (the fp8 workload's tokens, cast once
+    # per token above): code and scale rows once per destination rank
+    with torch.cuda.stream(stream):
+        dest_q = [torch.empty((T, H), dtype=torch.uint8, device=dev) for _ in range(G)]
+        dest_s = [torch.empty((T, H // 128), dtype=torch.float32, device=dev) for _ in range(G)]
+    stream.synchronize()
+    qtab = (ctypes.c_void_p * G)(*[t.data_ptr() for t in dest_q])
+    stab = (ctypes.c_void_p * G)(*[t.data_ptr() for t in dest_s])
+    drq_us = time_call(lambda: check(L.ep_dispatch_ranked_prequantized(
+        xq_tok.data_ptr(), xs_tok.data_ptr(), p["idx"], p["wt"], T, H, k, E, G, rq["s2d"],
+        ctypes.addressof(qtab), ctypes.addressof(stab), ctypes.addressof(wtab), T, s),
+        "ep_dispatch_ranked_prequantized"), args.steps)
+    drq_bytes = (T * H + T * (H // 128) * 4 + pairs * (H + (H // 128) * 4) + T * G * 4 + T * k * 12
+                 + pairs * k * 4)
+    del dest_q, dest_s, dest_w
 
     # receive side of rank 0 with the permute fused in: every token it
     # receives (from 8 ranks; ranks 1..7 hold seeded N(0,1) rows and unit-sum
@@ -542,6 +558,7 @@ def main():
         "dispatch_ranked": entry(dr_us, bytes=rbm["dispatch_ranked"], ranks=G,
                                  rows_written=pairs, expanded_rows=n),
         "combine_ranked": entry(cr_us, bytes=rbm["combine_ranked"], ranks=G, rows_read=pairs),
+        "dispatch_ranked_prequantized": entry(drq_us, bytes=drq_bytes, ranks=G, rows_written=pairs),
         "dispatch_fused_permute": entry(fp_us, bytes=fp_bytes, ranks=G, tokens_received=n_recv,
                                         expert_rows_written=n_exp),
         "layout_aligned128": entry(lay_a128),

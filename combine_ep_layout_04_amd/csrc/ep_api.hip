@@ -410,11 +410,60 @@ int ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk
     if (!aligned16(x)) return fail(EP_INVALID_ARGUMENT, "x must be 16-byte aligned");
     if (dest_weights && (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 7u)))
         return fail(EP_INVALID_ARGUMENT, "dest_weights needs an 8-byte aligned topk_idx");
-    return from_hip(ep::launch_dispatch_ranked(x, topk_idx, topk_weights, num_tokens, hidden,
+    const ep::RankPtrs none = {};
+    return from_hip(ep::launch_dispatch_ranked(x, topk_idx, topk_weights, num_tokens, hidden * 2,
                                                num_topk, num_experts, num_ranks,
                                                sparse_to_dense_map, px, pw, dest_weights != nullptr,
-                                               dest_rows, static_cast<hipStream_t>(stream)),
+                                               nullptr, none, 0, dest_rows,
+                                               static_cast<hipStream_t>(stream)),
                     "ep_dispatch_ranked launch");
+}
+
+int ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scales,
+                                    const int64_t* topk_idx, const float* topk_weights,
+                                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                    int num_ranks, const int32_t* sparse_to_dense_map,
+                                    void* const* dest_q, float* const* dest_scales,
+                                    float* const* dest_weights, int64_t dest_rows, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 128);
+    if (st) return st;
+    st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    if (dest_rows < 0) return fail(EP_INVALID_ARGUMENT, "dest_rows < 0");
+    if (!dest_q || !dest_scales)
+        return fail(EP_INVALID_ARGUMENT, "dest_q and dest_scales (host arrays of pointers) are required");
+    ep::RankPtrs pq = {}, ps = {}, pw = {};
+    for (int d = 0; d < num_ranks; ++d) {
+        if (!dest_q[d] || !aligned16(dest_q[d]))
+            return fail(EP_INVALID_ARGUMENT, "dest_q[%d] must be non-NULL and 16-byte aligned", d);
+        if (!dest_scales[d] || (reinterpret_cast<uintptr_t>(dest_scales[d]) & 3u))
+            return fail(EP_INVALID_ARGUMENT, "dest_scales[%d] must be non-NULL and 4-byte aligned", d);
+        pq.p[d] = dest_q[d];
+        ps.p[d] = dest_scales[d];
+        if (dest_weights) {
+            if ((reinterpret_cast<uintptr_t>(dest_weights[d]) & 3u))
+                return fail(EP_INVALID_ARGUMENT, "dest_weights[%d] must be 4-byte aligned", d);
+            pw.p[d] = dest_weights[d];
+        }
+    }
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x_q || !x_scales || !sparse_to_dense_map)
+        return fail(EP_INVALID_ARGUMENT, "x_q, x_scales and sparse_to_dense_map are required");
+    if (!aligned16(x_q)) return fail(EP_INVALID_ARGUMENT, "x_q must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(x_scales) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "x_scales must be 4-byte aligned");
+    if (dest_weights && (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 7u)))
+        return fail(EP_INVALID_ARGUMENT, "dest_weights needs an 8-byte aligned topk_idx");
+    return from_hip(ep::launch_dispatch_ranked(x_q, topk_idx, topk_weights, num_tokens, hidden,
+                                               num_topk, num_experts, num_ranks,
+                                               sparse_to_dense_map, pq, pw, dest_weights != nullptr,
+                                               x_scales, ps, hidden / 128, dest_rows,
+                                               static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_ranked_prequantized launch");
 }
 
 int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,

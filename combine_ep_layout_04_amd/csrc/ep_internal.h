@@ -72,10 +72,13 @@ hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int n
                               int32_t* expert_counts, int32_t* num_recv, int32_t* num_overflow,
                               void* workspace, hipStream_t stream);
 
+// Rows of row_bytes (a multiple of 16): bf16 tokens or 8-bit codes; with
+// x_scales, num_scales fp32 per token are copied to dest_scales too.
 hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
-                                  int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                  int64_t num_tokens, int row_bytes, int num_topk, int num_experts,
                                   int num_ranks, const int32_t* s2d, const RankPtrs& dest_x,
-                                  const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                  const RankPtrs& dest_w, bool with_weights, const float* x_scales,
+                                  const RankPtrs& dest_scales, int num_scales, int64_t dest_rows,
                                   hipStream_t stream);
 
 hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& src_idx,

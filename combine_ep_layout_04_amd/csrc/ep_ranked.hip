@@ -522,12 +522,15 @@ __device__ __forceinline__ void write_rank_weights(float* row, int k, int32_t e_
     if (lane < k && lane >= members) row[lane] = 0.0f;
 }
 
+// Rows are nvec 16-byte vectors (bf16 tokens, or 8-bit codes); with xs, the
+// token's nb fp32 scales are copied to ds[d] as well.
 template <int NT, int VPT>
 __global__ __launch_bounds__(NT)
 void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t* __restrict__ idx,
                             const float* __restrict__ w, int k, int E, int El, int G,
                             const int32_t* __restrict__ s2d, int64_t dest_rows, RankPtrs dx,
-                            RankPtrs dw, bool with_weights)
+                            RankPtrs dw, bool with_weights, const float* __restrict__ xs,
+                            RankPtrs ds, int nb)
 {
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
@@ -556,6 +559,17 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
             float* base = static_cast<float*>(dw.p[d]);
             if (pd < 0 || base == nullptr) continue;
             write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
+        }
+    }
+
+    if (xs != nullptr) {
+        for (int b0 = 0; b0 < nb; b0 += NT) {
+            const int b = b0 + tid;
+            const float v = b < nb ? xs[t * nb + b] : 0.0f;
+            for (int d = 0; d < G; ++d) {
+                const int32_t r = __builtin_amdgcn_readlane(p, d);
+                if (r >= 0 && b < nb) static_cast<float*>(ds.p[d])[(int64_t)r * nb + b] = v;
+            }
         }
     }
 
@@ -846,22 +860,38 @@ hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int n
 }
 
 hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
-                                  int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                  int64_t num_tokens, int row_bytes, int num_topk, int num_experts,
                                   int num_ranks, const int32_t* s2d, const RankPtrs& dest_x,
-                                  const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                  const RankPtrs& dest_w, bool with_weights, const float* x_scales,
+                                  const RankPtrs& dest_scales, int num_scales, int64_t dest_rows,
                                   hipStream_t stream)
 {
     if (num_tokens == 0) return hipSuccess;
-    const int nvec = hidden / 8;
+    const int nvec = row_bytes / 16;
     const dim3 grid((unsigned)num_tokens);
     const uint4* xx = static_cast<const uint4*>(x);
     const int El = num_experts / num_ranks;
 #define EP_DR(NT, V)                                                                            \
     hipLaunchKernelGGL((dispatch_ranked_kernel<NT, V>), grid, dim3(NT), 0, stream, xx, nvec,    \
                        topk_idx, topk_weights, num_topk, num_experts, El, num_ranks, s2d,        \
-                       dest_rows, dest_x, dest_w, with_weights)
+                       dest_rows, dest_x, dest_w, with_weights, x_scales, dest_scales,           \
+                       num_scales)
     if (nvec <= 64) {
         EP_DR(64, 1);
+        return hipGetLastError();
+    }
+    // 64 lanes when the row is whole 64-lane passes of at most 8 vectors
+    // and not whole 128-lane passes (448 = 64 * 7: 8-bit codes at 7168)
+    if (nvec % 128 != 0 && nvec % 64 == 0 && nvec <= 64 * 8) {
+        switch (nvec / 64) {
+        case 2: EP_DR(64, 2); break;
+        case 3: EP_DR(64, 3); break;
+        case 4: EP_DR(64, 4); break;
+        case 5: EP_DR(64, 5); break;
+        case 6: EP_DR(64, 6); break;
+        case 7: EP_DR(64, 7); break;
+        default: EP_DR(64, 8); break;
+        }
         return hipGetLastError();
     }
     // 128 lanes with the largest VPT <= 8 whose pass divides the row

@@ -49,7 +49,7 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
-           "ep_dispatch_fused_permute", "ep_combine_ranked")
+           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked")
 
 
 class EpError(RuntimeError):
@@ -104,6 +104,9 @@ def lib() -> ctypes.CDLL:
         L.ep_rank_layout.restype = i32
         L.ep_dispatch_ranked.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, P, P, i64, P]
         L.ep_dispatch_ranked.restype = i32
+        L.ep_dispatch_ranked_prequantized.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
+                                                      P, i64, P]
+        L.ep_dispatch_ranked_prequantized.restype = i32
         L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
                                                 i64, P, P, P]
         L.ep_dispatch_fused_permute.restype = i32
@@ -556,6 +559,60 @@ def ep_dispatch_ranked(x: torch.Tensor, sparse_to_dense: torch.Tensor, dest_x, n
                                   None if wtab is None else wtab[1], rows, _stream(stream))
     _check(st, "ep_dispatch_ranked")
     return dest_x, dest_weights
+
+
+def ep_dispatch_ranked_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor,
+                                    sparse_to_dense: torch.Tensor, dest_q, dest_scales,
+                                    num_experts: int, *, topk_idx: Optional[torch.Tensor] = None,
+                                    topk_weights: Optional[torch.Tensor] = None, dest_weights=None,
+                                    stream=None):
+    """Once-per-rank dispatch of 8-bit tokens: ``x_q`` uint8 [T, H] and
+    ``x_scales`` fp32 [T, H/128] go to the G ranks' ``dest_q`` (uint8
+    [rows_d, H]) and ``dest_scales`` (fp32 [rows_d, H/128]); weights as
+    ep_dispatch_ranked.  Rows at or past the smallest rows_d are not
+    written."""
+    _need(x_q, "x_q", torch.uint8)
+    _need(x_scales, "x_scales", torch.float32)
+    _need(sparse_to_dense, "sparse_to_dense", torch.int32)
+    if x_q.dim() != 2 or sparse_to_dense.dim() != 2 or sparse_to_dense.shape[0] != x_q.shape[0]:
+        raise ValueError("x_q must be [T, H] and sparse_to_dense [T, G]")
+    T, H = x_q.shape
+    nb = H // 128
+    _need(x_scales, "x_scales", torch.float32, T * nb)
+    G = sparse_to_dense.shape[1]
+    if len(dest_q) != G or len(dest_scales) != G:
+        raise ValueError("one code and one scale buffer per rank")
+    for d in range(G):
+        _need(dest_q[d], f"dest_q[{d}]", torch.uint8)
+        if dest_q[d].dim() != 2 or dest_q[d].shape[1] != H:
+            raise ValueError(f"dest_q[{d}] must be [rows, {H}]")
+        _need(dest_scales[d], f"dest_scales[{d}]", torch.float32)
+    rows = min(int(t.shape[0]) for t in dest_q)
+    for d in range(G):
+        _need(dest_scales[d], f"dest_scales[{d}]", torch.float32, rows * nb)
+    k = 1
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", torch.int64)
+        k = topk_idx.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    wtab = None
+    if dest_weights is not None:
+        if topk_idx is None or len(dest_weights) != G:
+            raise ValueError("dest_weights needs topk_idx and one buffer (or None) per rank")
+        for d, t in enumerate(dest_weights):
+            if t is not None:
+                _need(t, f"dest_weights[{d}]", torch.float32, rows * k)
+        wtab = _ptr_table(dest_weights)
+    qtab = _ptr_table(dest_q)
+    stab = _ptr_table(dest_scales)
+    st = lib().ep_dispatch_ranked_prequantized(_ptr(x_q), _ptr(x_scales), _ptr(topk_idx),
+                                               _ptr(topk_weights), T, H, k, int(num_experts), G,
+                                               _ptr(sparse_to_dense), qtab[1], stab[1],
+                                               None if wtab is None else wtab[1], rows,
+                                               _stream(stream))
+    _check(st, "ep_dispatch_ranked_prequantized")
+    return dest_q, dest_scales, dest_weights
 
 
 def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torch.Tensor,

@@ -111,7 +111,9 @@ KERNEL_KEYS = {
     "routing_map": r"routing_map_kernel\(",
     "rank_count": r"rank_count_kernel<",
     "rank_scatter": r"rank_scatter_kernel<",
-    "dispatch_ranked": r"dispatch_ranked_kernel<",
+    # bf16 rows (896 vectors: 128 lanes) and 8-bit code rows (448: 64 lanes)
+    "dispatch_ranked": r"dispatch_ranked_kernel<128,",
+    "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64,",
     "combine_ranked": r"combine_ranked_kernel<",
     "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }

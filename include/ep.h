@@ -435,6 +435,30 @@ int ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk
                        float *const *dest_weights, int64_t dest_rows, void *stream);
 
 /*
+ * ep_dispatch_ranked_prequantized -- ep_dispatch_ranked for tokens already
+ * cast to 8 bits: each token's code row (hidden bytes) and scale row
+ * (hidden/128 fp32) go to every destination rank that receives it, bit for
+ * bit (any 8-bit format passes through).
+ *
+ * Passages: NCCL EP page, ncclEpDispatch high-throughput branch (FP8 tokens
+ * need a 2-D fp32 scales tensor and travel as they are); DeepEP page,
+ * dispatch() (x may be a (data, scale factors) pair).
+ *
+ * In:  x_q bytes [num_tokens, hidden] (16-byte aligned), x_scales fp32
+ *      [num_tokens, hidden/128]; other inputs as ep_dispatch_ranked.
+ * Out: dest_q      HOST array of G device pointers: bytes [dest_rows, hidden].
+ *      dest_scales HOST array of G device pointers: fp32 [dest_rows, hidden/128].
+ *      dest_weights as ep_dispatch_ranked.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
+                                    const int64_t *topk_idx, const float *topk_weights,
+                                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                    int num_ranks, const int32_t *sparse_to_dense_map,
+                                    void *const *dest_q, float *const *dest_scales,
+                                    float *const *dest_weights, int64_t dest_rows, void *stream);
+
+/*
  * ep_dispatch_fused_permute -- the receiving rank's dispatch with the
  * permute fused in: every token it receives is read once from the sending
  * rank's rows and written to each of its local-expert rows, so the rows come

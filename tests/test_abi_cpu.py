@@ -338,3 +338,24 @@ def test_dispatch_prequantized_rejects_scale_ld():
     st = ep.lib().ep_dispatch_prequantized(FAKE, FAKE, 4, 256, 2, FAKE, None, FAKE, FAKE, None,
                                            6, None)
     assert st == 1 and "scale_ld" in ep.last_error()
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(H=200), 1), (dict(k=0), 1), (dict(G=65, E=130), 1), (dict(E=9), 1), (dict(rows=-1), 1),
+    (dict(dq="none"), 1), (dict(ds="none"), 1), (dict(dq=(FAKE, FAKE + 8)), 1),
+    (dict(ds=(FAKE, FAKE + 2)), 1), (dict(ds=(FAKE, None)), 1), (dict(dw=(FAKE, FAKE + 2)), 1),
+    (dict(x=None), 1), (dict(xs=None), 1), (dict(s2d=None), 1), (dict(x=FAKE + 8), 1),
+    (dict(xs=FAKE + 2), 1), (dict(dw=(FAKE, FAKE), idx=None), 1), (dict(T=1 << 28, k=8), 2),
+])
+def test_dispatch_ranked_prequantized_rejects(over, code):
+    a = dict(x=FAKE, xs=FAKE, idx=FAKE, w=None, T=4, H=256, k=2, E=8, G=2, s2d=FAKE,
+             dq=(FAKE, FAKE), ds=(FAKE, FAKE), dw=None, rows=16)
+    a.update(over)
+    tabs = {n: (None if a[n] in (None, "none") else _table(*a[n])) for n in ("dq", "ds", "dw")}
+    st = ep.lib().ep_dispatch_ranked_prequantized(
+        a["x"], a["xs"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["G"], a["s2d"],
+        *[None if tabs[n] is None else ctypes.addressof(tabs[n]) for n in ("dq", "ds", "dw")],
+        a["rows"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()

@@ -412,3 +412,56 @@ def test_fused_permute_headline():
     ws = [inp.topk_weights] + [np.full((w.T, w.k), 1.0 / w.k, np.float32)] * (G - 1)
     print("\n[ranked] fused permute headline G=8 rank 0", flush=True)
     check_fused_permute(xs, idx, ws, w.E, G, 0)
+
+
+def check_ranked_prequant(xq, xs, idx, w, E, G, s2d, rows):
+    T, H = xq.shape
+    k = idx.shape[1]
+    nb = H // 128
+    dq = [torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+    ds = [torch.full((rows, nb), float("nan"), dtype=torch.float32, device=DEV) for _ in range(G)]
+    dw = [torch.full((rows, k), float("nan"), dtype=torch.float32, device=DEV) for _ in range(G)]
+    ep.ep_dispatch_ranked_prequantized(dev(xq), dev(xs), dev(s2d), dq, ds, E, topk_idx=dev(idx),
+                                       topk_weights=None if w is None else dev(w), dest_weights=dw)
+    torch.cuda.synchronize()
+    oq, os_, ow = oracle.dispatch_ranked_prequant(xq, xs, idx, w, E, G,
+                                                  np.where(s2d < rows, s2d, -1), rows)
+    for d in range(G):
+        written = np.zeros(rows, bool)
+        p = s2d[:, d]
+        written[p[(p >= 0) & (p < rows)]] = True
+        gq, gs, gw = host(dq[d]), host(ds[d]), host(dw[d])
+        np.testing.assert_array_equal(gq[written], oq[d][written])
+        np.testing.assert_array_equal(gs[written].view(np.uint32), os_[d][written].view(np.uint32))
+        np.testing.assert_array_equal(gw[written].view(np.uint32), ow[d][written].view(np.uint32))
+        assert np.all(gq[~written] == 0xEE) and np.all(np.isnan(gs[~written]))
+
+
+@pytest.mark.parametrize("G,T,H,E,k", [(1, 3, 128, 2, 1), (2, 37, 256, 8, 3), (4, 200, 1152, 16, 5),
+                                       (8, 130, 7168, 64, 8), (64, 10, 2048, 64, 64)])
+def test_dispatch_ranked_prequantized(G, T, H, E, k):
+    inp = make_random_case(G * 3 + H, T, 8, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    rng = np.random.default_rng(G + T)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    xs = rng.standard_normal((T, H // 128)).astype(np.float32)
+    others = rank_cases(G + 5, G, T, 8, E, k, mask_frac=0.2)
+    maps = [oracle.routing_map(c.topk_idx, E)[0] for c in others]
+    rank = G // 2
+    maps[rank] = oracle.routing_map(inp.topk_idx, E)[0]
+    L = oracle.rank_layout(np.concatenate(maps), T, E, G, rank, k)
+    print(f"\n[ranked] pre-quantized dispatch G={G} T={T} H={H} E={E} k={k}", flush=True)
+    check_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, E, G, L.sparse_to_dense, G * T)
+    check_ranked_prequant(xq, xs, inp.topk_idx, None, E, G, L.sparse_to_dense, max(1, T // 2))
+
+
+def test_dispatch_ranked_prequantized_headline():
+    w = WORKLOADS["fp8"]
+    G = 8
+    inp = make_inputs(w)
+    idx = headline_global_map(G)
+    idx[0] = inp.topk_idx
+    xq, xs, _ = oracle.dispatch_quant(inp.x_bits, np.arange(w.T, dtype=np.int32)[:, None])
+    gmap = np.concatenate([oracle.routing_map(i, w.E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, w.T, w.E, G, 0, w.k)
+    print("\n[ranked] pre-quantized dispatch, fp8 workload, G=8", flush=True)
+    check_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, w.E, G, L.sparse_to_dense, w.T)
