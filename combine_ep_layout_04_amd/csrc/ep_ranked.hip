@@ -614,7 +614,7 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
 template <int NT, int VPT>
 __global__ __launch_bounds__(NT)
 void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
-                                   int nvec, int k, int E, int El, int rank,
+                                   int nvec, int k, int E, int El, int G, int rank,
                                    const int32_t* __restrict__ recv_src,
                                    const int64_t* __restrict__ recv_topk_idx,
                                    const int32_t* __restrict__ slot, int64_t rows,
@@ -626,7 +626,7 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
     // the same value in every lane; made scalar so the pointer tables are
     // read with scalar loads
     const int32_t g = __builtin_amdgcn_readfirstlane(recv_src[i]);
-    if (g < 0) return;
+    if (g < 0 || g >= (int64_t)G * T) return;   // no source (or not a global token)
     const int s = (int)(g / T);
     const int64_t t = g - (int64_t)s * T;
     int32_t sl = lane < k ? slot[i * k + lane] : -1;
@@ -934,7 +934,8 @@ hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& 
     uint4* rx = static_cast<uint4*>(recv_x);
 #define EP_FP(NT, V)                                                                            \
     hipLaunchKernelGGL((dispatch_fused_permute_kernel<NT, V>), grid, dim3(NT), 0, stream, src_x, \
-                       src_idx, src_w, tokens_per_rank, nvec, num_topk, num_experts, El, rank,   \
+                       src_idx, src_w, tokens_per_rank, nvec, num_topk, num_experts, El,        \
+                       num_ranks, rank,                                                          \
                        recv_src, recv_topk_idx, slot, rows, rx, recv_w)
     if (nvec <= 64) {
         EP_FP(64, 1);

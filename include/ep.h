@@ -488,6 +488,7 @@ int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
  *      of rank s's weights of the slots that select expert
  *      rank*E/G + recv_topk_idx[i, j].
  *      Rows past `rows` are never written; rows nothing maps to are not.
+ *      A received row whose recv_src is not in [0, G*T) is skipped.
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
 int ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,

@@ -465,3 +465,39 @@ def test_dispatch_ranked_prequantized_headline():
     L = oracle.rank_layout(gmap, w.T, w.E, G, 0, w.k)
     print("\n[ranked] pre-quantized dispatch, fp8 workload, G=8", flush=True)
     check_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, w.E, G, L.sparse_to_dense, w.T)
+
+
+def test_fused_permute_skips_rows_without_a_valid_source():
+    # recv_src entries outside [0, G*T) name no token: their rows are skipped
+    # (the result equals the oracle's with those entries set to -1)
+    G, T, H, E, k = 4, 50, 256, 16, 4
+    El = E // G
+    cases = rank_cases(77, G, T, H, E, k, mask_frac=0.1)
+    xs = [c.x_bits for c in cases]
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, T, E, G, 1, k)
+    Lr = oracle.layout(L.recv_topk_idx, El)
+    rows = max(Lr.n, 1)
+    bad_src = L.recv_src.copy()
+    bad_src[0] = G * T
+    bad_src[1] = 2 ** 31 - 1
+    out = torch.full((rows, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_fused_permute([x_dev(x) for x in xs], dev(bad_src), dev(L.recv_topk_idx),
+                                 dev(Lr.slot), E, 1, rows=rows, src_topk_idx=[dev(i) for i in idx],
+                                 src_topk_weights=[dev(w) for w in ws], recv_x=out,
+                                 recv_weights=rw)
+    torch.cuda.synchronize()
+    want_src = L.recv_src.copy()
+    want_src[:2] = -1
+    ox, ow = oracle.dispatch_fused_permute(xs, idx, ws, E, 1, want_src, L.recv_topk_idx, Lr.slot,
+                                           rows)
+    written = np.zeros(rows, bool)
+    sl = Lr.slot[2:]
+    written[sl[sl >= 0]] = True
+    got = bf16_bits(out)
+    np.testing.assert_array_equal(got[written], ox[written])
+    assert np.all(got[~written] == 0xFFFD)
+    np.testing.assert_array_equal(host(rw)[written].view(np.uint32), ow[written].view(np.uint32))
