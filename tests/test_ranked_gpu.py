@@ -501,3 +501,32 @@ def test_fused_permute_skips_rows_without_a_valid_source():
     np.testing.assert_array_equal(got[written], ox[written])
     assert np.all(got[~written] == 0xFFFD)
     np.testing.assert_array_equal(host(rw)[written].view(np.uint32), ow[written].view(np.uint32))
+
+
+def test_ranked_calls_with_no_tokens():
+    # T = 0: the layout still writes its totals (zero), the routing map clears
+    # num_invalid, and the data movers do nothing
+    G, E, k = 4, 32, 2
+    idx = torch.empty((0, k), dtype=torch.int64, device=DEV)
+    bad = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    m, _ = ep.ep_routing_map(idx, E, num_invalid=bad)
+    gmap = torch.empty((0, (E + 7) // 8), dtype=torch.uint8, device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    out = ep.RankLayout(sparse_to_dense=torch.empty((0, G), **i32),
+                        local_map=torch.empty((0, E // G), dtype=torch.uint8, device=DEV),
+                        recv_src=torch.empty(0, **i32),
+                        recv_topk_idx=torch.empty((0, k), dtype=torch.int64, device=DEV),
+                        expert_counts=torch.full((E // G,), -1, **i32),
+                        num_recv=torch.full((1,), -1, **i32), num_overflow=torch.full((1,), -1, **i32))
+    ep.ep_rank_layout(gmap, 0, E, G, 2, k, out=out)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    s2d = torch.empty((0, G), **i32)
+    dest = [torch.full((4, 256), 1.0, dtype=torch.bfloat16, device=DEV) for _ in range(G)]
+    ep.ep_dispatch_ranked(x, s2d, dest, E, topk_idx=idx)
+    o = ep.ep_combine_ranked(dest, s2d)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert int(out.num_recv.item()) == 0 and int(out.num_overflow.item()) == 0
+    assert torch.all(out.expert_counts == 0)
+    assert o.shape == (0, 256)
+    assert all(torch.all(d == 1.0) for d in dest)
