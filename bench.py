@@ -510,6 +510,48 @@ def main():
                 + n_exp * 4)
     del src_x, perm_x
 
+    # ---- the other seeded configs (tiny, mid, skewed): layout, dispatch and
+    # combine each timed alone, caches emptied before every launch
+    configs = {}
+    for cname in ("tiny", "mid", "skewed"):
+        wc = WORKLOADS[cname]
+        ic = make_inputs(wc)
+        Tc, Hc, Ec, kc = wc.T, wc.H, wc.E, wc.k
+        with torch.cuda.stream(stream):
+            c_idx = torch.from_numpy(ic.topk_idx).to(dev)
+            c_x = torch.from_numpy(ic.x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+            c_w = torch.from_numpy(ic.topk_weights).to(dev)
+            c_cnt = torch.empty(Ec, **i32)
+            c_off = torch.empty(Ec + 1, **i32)
+            c_slot = torch.empty((Tc, kc), **i32)
+            c_ws_bytes = ep.layout_workspace_size(Tc, kc, Ec)
+            c_ws = torch.empty(max(c_ws_bytes, 256), dtype=torch.uint8, device=dev)
+            c_recv = torch.empty((Tc * kc, Hc), dtype=torch.bfloat16, device=dev)
+            c_out = torch.empty((Tc, Hc), dtype=torch.bfloat16, device=dev)
+        stream.synchronize()
+        c_lay = time_call(lambda: check(L.ep_layout(
+            c_idx.data_ptr(), Tc, kc, Ec, c_cnt.data_ptr(), c_off.data_ptr(), c_slot.data_ptr(),
+            None, None, c_ws.data_ptr(), c_ws_bytes, s), "ep_layout"), args.steps)
+        c_dis = time_call(lambda: check(L.ep_dispatch(
+            c_x.data_ptr(), Tc, Hc, kc, c_slot.data_ptr(), None, 0, c_recv.data_ptr(), None, None,
+            s), "ep_dispatch"), args.steps)
+        c_com = time_call(lambda: check(L.ep_combine(
+            c_recv.data_ptr(), c_slot.data_ptr(), c_w.data_ptr(), Tc, Hc, kc, c_out.data_ptr(), s),
+            "ep_combine"), args.steps)
+        stream.synchronize()
+        nc = int(c_off[Ec].item())
+        bmc = bytes_model(Tc, Hc, kc, nc)
+        d_us, c_us = us(c_dis), us(c_com)
+        configs[cname] = {
+            "T": Tc, "H": Hc, "E": Ec, "k": kc, "dispatched_rows": nc,
+            "layout_us": round(us(c_lay), 2),
+            "dispatch_us": round(d_us, 2), "dispatch_GB_per_s": round(bmc["dispatch_bf16"] / d_us / 1e3, 1),
+            "combine_us": round(c_us, 2), "combine_GB_per_s": round(bmc["combine"] / c_us / 1e3, 1),
+            "dispatch_frac_of_hbm_peak": round(bmc["dispatch_bf16"] / d_us / 1e3 / HBM_PEAK_GBS, 4),
+            "combine_frac_of_hbm_peak": round(bmc["combine"] / c_us / 1e3 / HBM_PEAK_GBS, 4),
+        }
+        del c_recv, c_out, c_x
+
     # ---- context: a plain device-to-device copy of 1 GiB (read + write)
     with torch.cuda.stream(stream):
         c_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -617,6 +659,7 @@ def main():
         "ranked_combine_returns_n_x": ranked_ok,
         "cpu_baseline": cpu,
         "back_to_back": warm,
+        "configs": configs,
     }
     print(json.dumps(rec), flush=True)
 
