@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny / mid / skewed timings (profiling runs: the skewed config "
+                         "shares the headline kernels)")
     ap.add_argument("--warm", action="store_true",
                     help="also time the steps back to back without cache flushes (context)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -513,7 +516,7 @@ def main():
     # ---- the other seeded configs (tiny, mid, skewed): layout, dispatch and
     # combine each timed alone, caches emptied before every launch
     configs = {}
-    for cname in ("tiny", "mid", "skewed"):
+    for cname in (() if args.no_configs else ("tiny", "mid", "skewed")):
         wc = WORKLOADS[cname]
         ic = make_inputs(wc)
         Tc, Hc, Ec, kc = wc.T, wc.H, wc.E, wc.k
