@@ -149,3 +149,26 @@ def test_combine_backward_ties():
     g = make_gradient(T, H, 33)
     y = make_gradient(T * k, H, 34)
     check_combine_backward(g, y, L, w, T * k)
+
+
+def test_backward_at_max_hidden():
+    # hidden = EP_MAX_HIDDEN: eight 128-lane passes of 8 vectors per lane
+    T, H, E, k = 8, 65536, 4, 2
+    inp = make_random_case(41, T, H, E, k, mask_frac=0.1)
+    print("\n[backward] hidden 65536", flush=True)
+    L = oracle.layout(inp.topk_idx, E)
+    y = make_gradient(T * k, H, 42)
+    g = make_gradient(T, H, 43)
+    check_combine_backward(g, y, L, inp.topk_weights, T * k)
+    grad_recv = make_gradient(T * k, H, 44)
+    gx, _ = ep.ep_dispatch_backward(x_dev(grad_recv), None, dev(L.slot))
+    torch.cuda.synchronize()
+    o_gx, _ = oracle.dispatch_backward(grad_recv, None, L.slot, T)
+    got = float32_from_bf16_bits(bf16_bits(gx)).astype(np.float64)
+    want = float32_from_bf16_bits(o_gx).astype(np.float64)
+    s = np.zeros_like(want)
+    gr = np.abs(float32_from_bf16_bits(grad_recv).astype(np.float64))
+    for j in range(k):
+        r = L.slot[:, j]
+        s[r >= 0] += gr[r[r >= 0]]
+    assert np.all(np.abs(got - want) <= bf16_ulp(want) + 2.0 * k * 2.0 ** -24 * s)

@@ -160,3 +160,12 @@ def test_prequantized_column_major_scales():
     np.testing.assert_array_equal(host(q)[:n], oq[:n])
     np.testing.assert_array_equal(host(s)[:, :n].view(np.uint32), os_[:n].T.copy().view(np.uint32))
     assert np.all(np.isnan(host(s)[:, n:]))
+
+
+@pytest.mark.parametrize("fmt,mode", [("e4m3", "fp32"), ("e5m2", "ue8m0")])
+def test_variants_at_max_hidden(fmt, mode):
+    # hidden = EP_MAX_HIDDEN: 512 scale blocks, eight passes of 64 blocks
+    inp = make_random_case(51, 6, 65536, 4, 2, mask_frac=0.1)
+    print(f"\n[fp8 variants] hidden 65536 {fmt} {mode}", flush=True)
+    L = oracle.layout(inp.topk_idx, 4)
+    check(inp.x_bits, L, fmt, mode)

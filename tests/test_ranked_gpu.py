@@ -530,3 +530,24 @@ def test_ranked_calls_with_no_tokens():
     assert torch.all(out.expert_counts == 0)
     assert o.shape == (0, 256)
     assert all(torch.all(d == 1.0) for d in dest)
+
+
+def test_ranked_path_at_max_hidden():
+    # hidden = EP_MAX_HIDDEN through the once-per-rank dispatch (bf16 and
+    # 8-bit), the fused permute and the combine over ranks
+    G, T, H, E, k = 2, 6, 65536, 4, 2
+    cases = rank_cases(61, G, T, H, E, k, mask_frac=0.1)
+    xs = [c.x_bits for c in cases]
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, T, E, G, 0, k)
+    print("\n[ranked] hidden 65536", flush=True)
+    check_dispatch(xs[0], idx[0], ws[0], E, G, L.sparse_to_dense, G * T)
+    rng = np.random.default_rng(62)
+    xq = rng.integers(0, 256, (T, H), dtype=np.uint8)
+    xsc = rng.standard_normal((T, H // 128)).astype(np.float32)
+    check_ranked_prequant(xq, xsc, idx[0], ws[0], E, G, L.sparse_to_dense, G * T)
+    check_fused_permute(xs, idx, ws, E, G, 1)
+    ys = [make_gradient(G * T, H, 70 + d) for d in range(G)]
+    check_combine(ys, L.sparse_to_dense)
