@@ -1,0 +1,211 @@
+"""Seeded random sweep of the whole library against the oracle on the GPU.
+
+Each case draws a shape (tokens, hidden, experts, top-k), routing with
+masked, duplicate and out-of-range entries, a segment alignment or a fixed
+capacity, an 8-bit format and scale, and a rank count dividing the experts,
+then checks every entry point the shape allows, to the same gates as the
+dedicated tests:
+
+* layout, dispatch copies, 8-bit codes and scales, the rank layout and the
+  per-rank copies: bit-exact, with sentinel-filled outputs;
+* combine, combine backward, dispatch backward and the combine over ranks:
+  one bf16 ulp plus the fp32 accumulation bound (and the dot-product bound
+  for the weight gradients).
+
+Shapes stay small (the oracle runs each case in well under a second) but
+cover ragged rows (hidden not a multiple of the vector pass), one-token and
+one-expert cases, and k above the expert count.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_layout_04_amd import ep
+from combine_ep_layout_04_amd.inputs import float32_from_bf16_bits, make_gradient, make_random_case
+
+from gpu_util import DEV, bf16_bits, bf16_ulp, dev, host, x_dev
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = range(200)
+
+
+def draw(seed):
+    rng = np.random.default_rng(1000 + seed)
+    T = int(rng.choice([1, 2, 7, 64, 129, 300, 1000, 2500]))
+    E = int(rng.choice([1, 2, 3, 8, 16, 24, 64, 96, 256]))
+    k = int(rng.integers(1, 13))
+    fp8 = bool(rng.random() < 0.5)
+    H = int(rng.choice([128, 256, 1152, 2048])) if fp8 else int(rng.choice([8, 24, 136, 1032, 2048]))
+    mode = rng.choice(["plain", "aligned", "capacity"], p=[0.5, 0.3, 0.2])
+    A = int(rng.choice([2, 16, 128])) if mode == "aligned" else 1
+    cap = int(rng.choice([1, 4, 32])) * A if mode == "capacity" else 0
+    G = int(rng.choice([g for g in (1, 2, 3, 4, 8) if E % g == 0]))
+    # keep every array small: at most 2^23 elements per token-shaped buffer
+    # and 2^24 per receive buffer
+    while T > 1 and T * max(k, G) * H > (1 << 23):
+        T //= 2
+    while A > 1 and (T * k + min(E, T * k) * (A - 1)) * H > (1 << 24):
+        A //= 2
+    return dict(T=T, E=E, k=k, H=H, fp8=fp8, A=A, cap=cap, G=G,
+                mask=float(rng.random() * 0.3), dup=float(rng.random() < 0.5),
+                invalid=float(rng.random() * 0.05), fmt=str(rng.choice(["e4m3", "e5m2"])),
+                scale=str(rng.choice(["fp32", "pow2", "ue8m0"])))
+
+
+def mixed_tol(rows_bits, slot, w, ref_bits):
+    """one bf16 ulp of the oracle value + 2 k 2^-24 sum_j |w_j y_j|"""
+    T, k = slot.shape
+    yf = float32_from_bf16_bits(rows_bits).astype(np.float64)
+    s = np.zeros((T, rows_bits.shape[1]))
+    for j in range(k):
+        r = slot[:, j]
+        ok = r >= 0
+        wj = np.ones(T) if w is None else np.abs(w[:, j].astype(np.float64))
+        s[ok] += wj[ok, None] * np.abs(yf[r[ok]])
+    ref = float32_from_bf16_bits(ref_bits).astype(np.float64)
+    return bf16_ulp(ref) + 2.0 * k * 2.0 ** -24 * s
+
+
+def close(got_bits, ref_bits, tol, what):
+    got = float32_from_bf16_bits(got_bits).astype(np.float64)
+    ref = float32_from_bf16_bits(ref_bits).astype(np.float64)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off, first {np.argwhere(bad)[0]}"
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_case(seed):
+    c = draw(seed)
+    T, E, k, H, A, cap, G = c["T"], c["E"], c["k"], c["H"], c["A"], c["cap"], c["G"]
+    print(f"\n[sweep] seed {seed}: {c}", flush=True)
+    inp = make_random_case(5000 + seed, T, H, E, k, mask_frac=c["mask"], dup_frac=c["dup"],
+                           invalid_frac=c["invalid"])
+    rows = oracle.max_rows(T, k, E, A, cap)
+    L = oracle.layout(inp.topk_idx, E, alignment=A, capacity=cap)
+
+    # layout (sentinel-filled outputs)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    counts = torch.full((E,), -5, **i32)
+    offsets = torch.full((E + 1,), -5, **i32)
+    slot = torch.full((T, k), -9, **i32)
+    src = torch.full((max(rows, 1),), -7, **i32)
+    inval = torch.full((1,), -1, **i32)
+    drop = torch.full((1,), -1, **i32)
+    ep.ep_layout(dev(inp.topk_idx), E, alignment=A, capacity=cap, counts=counts, offsets=offsets,
+                 slot=slot, src=src, num_invalid=inval, num_dropped=drop)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(counts), L.counts)
+    np.testing.assert_array_equal(host(offsets), L.offsets)
+    np.testing.assert_array_equal(host(slot), L.slot)
+    n = L.n
+    placed = L.slot[L.slot >= 0]
+    np.testing.assert_array_equal(host(src)[placed], L.src[placed])
+    assert int(inval.item()) == L.num_invalid
+    if cap:
+        assert int(drop.item()) == L.num_dropped
+
+    # dispatch: bf16 copy with weights, or an 8-bit cast
+    R = max(rows, 1)
+    if c["fp8"]:
+        q = torch.full((R, H), 0xEE, dtype=torch.uint8, device=DEV)
+        sdt = torch.uint8 if c["scale"] == "ue8m0" else torch.float32
+        s = torch.full((R, H // 128), 0xAB if c["scale"] == "ue8m0" else float("nan"), dtype=sdt,
+                       device=DEV)
+        ep.ep_dispatch(x_dev(inp.x_bits), slot, None, fp8=True, fmt=c["fmt"], scale=c["scale"],
+                       recv_x=q, recv_scales=s, rows=R)
+        torch.cuda.synchronize()
+        oq, os_, _ = oracle.dispatch_quant(inp.x_bits, L.slot, fmt=c["fmt"], scale=c["scale"],
+                                           rows=R)
+        np.testing.assert_array_equal(host(q)[placed], oq[placed])
+        np.testing.assert_array_equal(host(s)[placed].view(np.uint8), os_[placed].view(np.uint8))
+    recv = torch.full((R, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch(x_dev(inp.x_bits), slot, dev(inp.topk_weights), recv_x=recv, recv_weights=rw,
+                   rows=R)
+    torch.cuda.synchronize()
+    o_recv, o_rw = oracle.dispatch_bf16(inp.x_bits, L.slot, inp.topk_weights, rows=R)
+    np.testing.assert_array_equal(bf16_bits(recv)[placed], o_recv[placed])
+    np.testing.assert_array_equal(host(rw)[placed], o_rw[placed])
+    unplaced = np.ones(R, bool)
+    unplaced[placed] = False
+    assert np.all(bf16_bits(recv)[unplaced] == 0xFFFD)
+
+    # combine over random mixed-sign expert outputs, then both backward passes
+    y = make_gradient(R, H, 6000 + seed)
+    out = ep.ep_combine(x_dev(y), slot, dev(inp.topk_weights), rows=R)
+    torch.cuda.synchronize()
+    o_out = oracle.combine(y, L.slot, inp.topk_weights)
+    close(bf16_bits(out), o_out, mixed_tol(y, L.slot, inp.topk_weights, o_out), "combine")
+
+    g = make_gradient(T, H, 7000 + seed)
+    gy = torch.full((R, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_combine_backward(x_dev(g), x_dev(y), slot, dev(inp.topk_weights), grad_y=gy,
+                           grad_topk_weights=gw, rows=R)
+    torch.cuda.synchronize()
+    o_gy, o_gw = oracle.combine_backward(g, y, L.slot, inp.topk_weights, rows=R)
+    np.testing.assert_array_equal(bf16_bits(gy)[placed], o_gy[placed])
+    gf = np.abs(float32_from_bf16_bits(g).astype(np.float64))
+    yf = np.abs(float32_from_bf16_bits(y).astype(np.float64))
+    dots = np.zeros((T, k))
+    for j in range(k):
+        r = L.slot[:, j]
+        ok = r >= 0
+        dots[ok, j] = (gf[ok] * yf[r[ok]]).sum(axis=1)
+    tol_w = 2.0 * H * 2.0 ** -24 * dots + 2.0 ** -24 * np.abs(o_gw) + 1e-38
+    assert np.all(np.abs(host(gw).astype(np.float64) - o_gw) <= tol_w)
+
+    gx, _ = ep.ep_dispatch_backward(x_dev(y), None, slot, rows=R)
+    torch.cuda.synchronize()
+    o_gx, _ = oracle.dispatch_backward(y, None, L.slot, T)
+    close(bf16_bits(gx), o_gx, mixed_tol(y, L.slot, None, o_gx), "dispatch backward")
+
+    # the per-rank path: this token set as rank 0 of G, the other ranks
+    # drawn alike
+    others = [make_random_case(8000 + seed * 10 + r, T, 8, E, k, mask_frac=c["mask"],
+                               dup_frac=c["dup"]).topk_idx for r in range(1, G)]
+    idx_all = [inp.topk_idx] + others
+    maps = [ep.ep_routing_map(dev(i), E)[0] for i in idx_all]
+    gmap_d = torch.cat(maps)
+    torch.cuda.synchronize()
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx_all])
+    np.testing.assert_array_equal(host(gmap_d), gmap)
+    RL = oracle.rank_layout(gmap, T, E, G, 0, k)
+    lay = ep.ep_rank_layout(gmap_d, T, E, G, 0, k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(lay.sparse_to_dense), RL.sparse_to_dense)
+    np.testing.assert_array_equal(host(lay.local_map), RL.local_map)
+    np.testing.assert_array_equal(host(lay.recv_topk_idx), RL.recv_topk_idx)
+    np.testing.assert_array_equal(host(lay.recv_src), RL.recv_src)
+    np.testing.assert_array_equal(host(lay.expert_counts), RL.expert_counts)
+    assert int(lay.num_recv.item()) == RL.num_recv
+
+    rows_r = G * T
+    dx = [torch.full((rows_r, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+          for _ in range(G)]
+    dwt = [torch.full((rows_r, k), float("nan"), dtype=torch.float32, device=DEV)
+           for _ in range(G)]
+    ep.ep_dispatch_ranked(x_dev(inp.x_bits), lay.sparse_to_dense, dx, E, topk_idx=dev(inp.topk_idx),
+                          topk_weights=dev(inp.topk_weights), dest_weights=dwt)
+    torch.cuda.synchronize()
+    ox, ow = oracle.dispatch_ranked(inp.x_bits, inp.topk_idx, inp.topk_weights, E, G,
+                                    RL.sparse_to_dense, rows_r)
+    for d in range(G):
+        pr = RL.sparse_to_dense[:, d]
+        pr = pr[pr >= 0]
+        np.testing.assert_array_equal(bf16_bits(dx[d])[pr], ox[d][pr])
+        np.testing.assert_array_equal(host(dwt[d])[pr].view(np.uint32), ow[d][pr].view(np.uint32))
+    ys = [make_gradient(rows_r, H, 9000 + seed * 10 + d) for d in range(G)]
+    o = ep.ep_combine_ranked([x_dev(v) for v in ys], lay.sparse_to_dense)
+    torch.cuda.synchronize()
+    ref = oracle.combine_ranked(ys, RL.sparse_to_dense)
+    s2d = RL.sparse_to_dense
+    acc = np.zeros((T, H))
+    for d in range(G):
+        ok = s2d[:, d] >= 0
+        acc[ok] += np.abs(float32_from_bf16_bits(ys[d][s2d[ok, d]]).astype(np.float64))
+    tol = bf16_ulp(float32_from_bf16_bits(ref).astype(np.float64)) + G * 2.0 ** -24 * acc
+    close(bf16_bits(o), ref, tol, "combine over ranks")
