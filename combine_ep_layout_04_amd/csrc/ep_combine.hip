@@ -11,17 +11,25 @@
 // accumulated in fp32, one fused multiply-add per term, in increasing j,
 // starting from +0; the bf16 rounding is done once at the end.
 //
-// Design (HBM-bound): one workgroup per token; each lane owns 16-byte
-// column vectors of the row.  For U column vectors at a time the k source
-// rows are loaded back to back (U*k independent 16-byte loads in flight per
-// lane before the first is consumed), then reduced in j order.  Each loaded
-// byte is used once by the lane that loaded it, so the gather goes straight
-// to registers; an LDS round trip would add traffic without reuse.  The
-// loads carry the non-temporal hint: the expert outputs are read exactly
-// once, and streaming them past the caches measured ~12% faster than
-// cached loads on MI355X.  k is a template parameter for k <= 8 so the
-// loads are fully unrolled.
+// Design (HBM-bound): one workgroup per (token, 2 KiB tile of the row),
+// one 16-byte column vector per lane.  The lane loads its vector from the
+// k source rows back to back (k independent loads in flight before the
+// first is consumed), reduces them in j order and stores the result once,
+// as a streaming store.  Each loaded byte is used once by the lane that
+// loaded it, so the gather goes straight to registers; an LDS round trip
+// would add traffic without reuse.  The loads carry the non-temporal hint:
+// the expert outputs are read exactly once, and streaming them past the
+// caches measured ~12% faster than cached loads on MI355X.  k is a template
+// parameter for k <= 8 so the loads are fully unrolled.
+//
+// The output goes out with streaming stores too.  Plain stores leave the
+// output's write-back to whatever runs next: at T=8192, hidden 7168, k=8
+// the combine then reads 188 us in its own events but 202 us once a
+// following read pass is charged for the write-back; the tiled kernel with
+// streaming stores takes 185 us either way.  Rows of at most 64 vectors,
+// and grids past 2^31 workgroups, keep one workgroup per token.
 
+#include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
@@ -101,7 +109,7 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
     const int kk = K > 0 ? K : k;
     const int32_t sl = lane < kk ? slot[t * kk + lane] : -1;
     const float wl = lane < kk ? (w ? w[t * kk + lane] : 1.0f) : 0.0f;
-    uint4* o = out + t * nvec;
+    const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(out + t * nvec, nvec * 16);
     if (out_w != nullptr && tid < kk) out_w[t * kk + tid] = sl >= 0 ? row_w[sl] : 0.0f;
 
     if constexpr (K > 0) {
@@ -129,7 +137,7 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
                 float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < K; ++j) fma8(acc, g[j], d[u][j]);
-                if (v0 + u * NT < nvec) o[v0 + u * NT] = pack8(acc);
+                if (v0 + u * NT < nvec) store_row16(ors, (v0 + u * NT) * 16, pack8(acc));
             }
         }
     } else {
@@ -141,9 +149,49 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
                 const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
                 fma8(acc, g, y[(int64_t)r * nvec + v]);
             }
-            o[v] = pack8(acc);
+            store_row16(ors, v * 16, pack8(acc));
         }
     }
+}
+
+// Tiled form: workgroup b is tile b % tpr of token b / tpr.  K > 0: exactly
+// K = k slots, unrolled; K == 0: any k, 8 slots' loads in flight at a time
+// (slots past k count as masked: zero data, zero weight).
+template <int K>
+__global__ __launch_bounds__(kTileLanes)
+void combine_tile_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slot,
+                         const float* __restrict__ w, int nvec, int k, int tpr,
+                         uint4* __restrict__ out, const float* __restrict__ row_w,
+                         float* __restrict__ out_w)
+{
+    const int64_t tile = blockIdx.x;
+    const int64_t t = tile / tpr;
+    const int p = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int kk = K > 0 ? K : k;
+    const int32_t sl = lane < kk ? slot[t * kk + lane] : -1;
+    const float wl = lane < kk ? (w ? w[t * kk + lane] : 1.0f) : 0.0f;
+    if (out_w != nullptr && p == 0 && tid < kk) out_w[t * kk + tid] = sl >= 0 ? row_w[sl] : 0.0f;
+
+    const int v = p * kTileLanes + tid;     // past the row end: reads 0, stores nothing
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int kBatch = K > 0 ? K : 8;
+    for (int j0 = 0; j0 < kk; j0 += kBatch) {
+        uint4 d[kBatch];
+        float g[kBatch];
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+            const int j = j0 + q;
+            const int32_t r = j < kk ? __builtin_amdgcn_readlane(sl, j) : -1;
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j & 63));
+            g[q] = r >= 0 ? wj : 0.0f;
+            d[q] = load16(row_rsrc(y, r, nvec), v);
+        }
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) fma8(acc, g[q], d[q]);
+    }
+    if (v < nvec) store_row16(buffer_rsrc(out + t * nvec, nvec * 16), v * 16, pack8(acc));
 }
 
 template <int NT, int U>
@@ -178,6 +226,27 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
     const dim3 grid((unsigned)num_tokens);
     const uint4* yy = static_cast<const uint4*>(y);
     uint4* oo = static_cast<uint4*>(out);
+    const int tpr = tiles_per_row(nvec);
+    const int64_t tiles = num_tokens * tpr;
+    if (nvec > 64 && tiles <= INT32_MAX) {
+        const dim3 tg((unsigned)tiles);
+#define EP_COMBINE_TILE(KV)                                                                     \
+    hipLaunchKernelGGL((combine_tile_kernel<KV>), tg, dim3(kTileLanes), 0, stream, yy, slot,      \
+                       topk_weights, nvec, num_topk, tpr, oo, row_w, out_w)
+        switch (num_topk) {
+        case 1: EP_COMBINE_TILE(1); break;
+        case 2: EP_COMBINE_TILE(2); break;
+        case 3: EP_COMBINE_TILE(3); break;
+        case 4: EP_COMBINE_TILE(4); break;
+        case 5: EP_COMBINE_TILE(5); break;
+        case 6: EP_COMBINE_TILE(6); break;
+        case 7: EP_COMBINE_TILE(7); break;
+        case 8: EP_COMBINE_TILE(8); break;
+        default: EP_COMBINE_TILE(0); break;
+        }
+#undef EP_COMBINE_TILE
+        return hipGetLastError();
+    }
     // 256 lanes x 2 vectors for long rows (hidden >= 4096: 896 vectors at
     // 7168 take two iterations); smaller workgroups for short rows
     if (nvec <= 64)

@@ -8,12 +8,19 @@
 // and recv_topk_weights.
 //
 // Design (HBM-bound; no arithmetic worth a matrix core):
-//   - one workgroup per token: x[t] is read from HBM exactly once into
-//     registers (16-byte loads, `VPT` per lane) and written to each of the
-//     token's k destination rows with 16-byte stores, so every wavefront
-//     store instruction covers 1 KiB of one contiguous row;
-//   - the k slots of a token are wavefront-uniform (scalar loads), so the
-//     loop over destinations is a scalar loop with no divergence;
+//   - bf16: one workgroup per (2 KiB row tile, group of up to 4 of the
+//     token's slots), one 16-byte vector per lane: it loads its tile of x[t]
+//     and stores it to the group's destination rows, at most 4 stores per
+//     lane.  The ceil(k/4) workgroups of a tile run back to back on one XCD,
+//     so x[t] comes from HBM once and the other loads hit that XCD's L2.
+//     Against one workgroup per token (the row held in registers and
+//     written to all k rows) this measured 200 us instead of 218 us at
+//     T=8192, hidden 7168, k=8 with cold caches: workgroups that each write
+//     a few 2 KiB pieces stream faster than ones that write 56 in turn.
+//     Rows of at most 64 vectors, and grids past 2^31 workgroups, keep one
+//     workgroup per token;
+//   - the slots a workgroup serves are wavefront-uniform (read into lanes,
+//     then readlane), so the loop over destinations has no divergence;
 //   - fp8: one 64-lane wavefront per token, each lane owning 16 channels
 //     (two 16-byte loads in, one 16-byte store out), so 8 aligned lanes hold
 //     one 128-channel block and amax is an 8-lane shuffle reduction.  The
@@ -134,6 +141,40 @@ void dispatch_bf16_kernel(const uint4* __restrict__ x, int nvec, int k,
             if (r >= 0) store_row16(buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16), v * 16, d);
         }
     }
+}
+
+// Tiled form: workgroup b maps (XCD-aware) to tile `tile` = (token t, tile
+// p of its row) and slot group g (slots 4g .. 4g+3).
+constexpr int kSlotsPerGroup = 4;
+
+__global__ __launch_bounds__(kTileLanes)
+void dispatch_bf16_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int tpr,
+                               int64_t num_tiles, int groups, const int32_t* __restrict__ slot,
+                               const float* __restrict__ w, uint4* __restrict__ recv,
+                               float* __restrict__ recv_w)
+{
+    int64_t tile;
+    int g;
+    if (!xcd_tile(blockIdx.x, groups, num_tiles, tile, g)) return;
+    const int64_t t = tile / tpr;
+    const int p = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int j0 = g * kSlotsPerGroup;
+    // lanes 0..3 of each wavefront hold the group's slots
+    const int32_t sl = lane < kSlotsPerGroup && j0 + lane < k ? slot[t * k + j0 + lane] : -1;
+    if (recv_w != nullptr && p == 0 && tid < kSlotsPerGroup && sl >= 0)
+        recv_w[sl] = w[t * k + j0 + tid];
+
+    int32_t r[kSlotsPerGroup];
+#pragma unroll
+    for (int q = 0; q < kSlotsPerGroup; ++q) r[q] = lane_value(sl, q);
+    const int v = p * kTileLanes + tid;     // past the row end (last tile) stores nothing
+    uint4 d = load_row16<0>(buffer_rsrc(x + t * nvec, nvec * 16), v * 16);
+    keep(d);
+#pragma unroll
+    for (int q = 0; q < kSlotsPerGroup; ++q)
+        if (r[q] >= 0 && v < nvec) store_row16(buffer_rsrc(recv + (int64_t)r[q] * nvec, nvec * 16), v * 16, d);
 }
 
 // ---------------------------------------------------------------- fp8 ---
@@ -471,6 +512,16 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, i
 {
     if (num_tokens == 0) return hipSuccess;
     const int nvec = hidden / 8;
+    const int tpr = tiles_per_row(nvec);
+    const int groups = (num_topk + kSlotsPerGroup - 1) / kSlotsPerGroup;
+    const int64_t num_tiles = num_tokens * tpr;
+    const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
+    if (nvec > 64 && blocks <= INT32_MAX) {
+        hipLaunchKernelGGL(dispatch_bf16_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
+                           stream, static_cast<const uint4*>(x), nvec, num_topk, tpr, num_tiles,
+                           groups, slot, topk_weights, static_cast<uint4*>(recv_x), recv_weights);
+        return hipGetLastError();
+    }
     const Shape sh = pick_shape(nvec);
     const dim3 grid((unsigned)num_tokens);
     EP_DISPATCH_CASES(dispatch_bf16_kernel, static_cast<const uint4*>(x), nvec, num_topk, slot,
