@@ -141,15 +141,20 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
             }
         }
     } else {
-        for (int v = tid; v < nvec; v += NT) {
+        // the trip count is the same for every lane, so readlane always runs
+        // with the whole wavefront active (it reads other lanes' registers,
+        // whose values are only kept for lanes that are active); past the
+        // row end the loads read 0 and nothing is stored
+        for (int v0 = 0; v0 < nvec; v0 += NT) {
+            const int v = v0 + tid;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int j = 0; j < kk; ++j) {
                 const int32_t r = __builtin_amdgcn_readlane(sl, j);
                 if (r < 0) continue;
                 const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
-                fma8(acc, g, y[(int64_t)r * nvec + v]);
+                fma8(acc, g, load16(row_rsrc(y, r, nvec), v));
             }
-            store_row16(ors, v * 16, pack8(acc));
+            if (v < nvec) store_row16(ors, v * 16, pack8(acc));
         }
     }
 }

@@ -132,13 +132,19 @@ void dispatch_bf16_kernel(const uint4* __restrict__ x, int nvec, int k,
             for (int u = 0; u < VPT; ++u) store_row16(rs, (vb + u * NT) * 16, buf[u]);
         }
     }
-    // ragged tail: one vector per lane
-    for (int v = full * kPass + tid; v < nvec; v += NT) {
-        uint4 d = xr[v];
+    // ragged tail: one vector per lane.  The trip count is the same for
+    // every lane, so lane_value always runs with the whole wavefront active
+    // (it reads another lane's register, whose value is only kept for lanes
+    // that are active); past the row end the load reads 0 and nothing is
+    // stored.
+    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(xr, nvec * 16);
+    for (int v0 = full * kPass; v0 < nvec; v0 += NT) {
+        const int v = v0 + tid;
+        uint4 d = load_row16<0>(xs, v * 16);
         keep(d);
         for (int j = 0; j < k; ++j) {
             const int32_t r = lane_value(sl, j);
-            if (r >= 0) store_row16(buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16), v * 16, d);
+            if (r >= 0 && v < nvec) store_row16(buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16), v * 16, d);
         }
     }
 }

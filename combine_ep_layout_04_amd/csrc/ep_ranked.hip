@@ -592,16 +592,81 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
             for (int u = 0; u < VPT; ++u) store_row16(dst, (vb + u * NT) * 16, buf[u]);
         }
     }
-    for (int v = full * kPass + tid; v < nvec; v += NT) {
-        uint4 val = xr[v];
+    // ragged tail, the same trip count for every lane (readlane needs the
+    // whole wavefront active); past the row end reads 0, stores nothing
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(xr, nvec * 16);
+    for (int v0 = full * kPass; v0 < nvec; v0 += NT) {
+        const int v = v0 + tid;
+        uint4 val = load_row16<0>(xrs, v * 16);
         keep(val);
         for (int d = 0; d < G; ++d) {
             const int32_t r = __builtin_amdgcn_readlane(p, d);
-            if (r >= 0)
+            if (r >= 0 && v < nvec)
                 store_row16(buffer_rsrc(static_cast<uint4*>(dx.p[d]) + (int64_t)r * nvec, nvec * 16),
                             v * 16, val);
         }
     }
+}
+
+// Tiled form (token rows of more than 64 vectors, no scale rows): workgroup
+// b maps (XCD-aware) to tile = (token t, tile pt of its row) and a group of
+// kRanksPerGroup destination ranks; the tile's loads after the first hit
+// the XCD's L2.  Tile 0's workgroups also write the group's weight rows.
+// The expanded dispatch's tiling; its measurements apply.
+constexpr int kRanksPerGroup = 4;
+
+__global__ __launch_bounds__(kTileLanes)
+void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
+                                 const int64_t* __restrict__ idx, const float* __restrict__ w,
+                                 int k, int E, int El, int G, const int32_t* __restrict__ s2d,
+                                 int64_t dest_rows, RankPtrs dx, RankPtrs dw, bool with_weights,
+                                 int tpr, int64_t num_tiles, int groups)
+{
+    int64_t tile;
+    int g;
+    if (!xcd_tile(blockIdx.x, groups, num_tiles, tile, g)) return;
+    const int64_t t = tile / tpr;
+    const int pt = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int d0 = g * kRanksPerGroup;
+    int32_t p = lane < G ? s2d[t * G + lane] : -1;
+    if (p >= dest_rows) p = -1;
+
+    if (with_weights && pt == 0 && tid < 64) {
+        const int64_t e64 = lane < k ? idx[t * k + lane] : -1;
+        const int32_t e_j = (e64 >= 0 && e64 < E) ? (int32_t)e64 : -1;
+        const float w_j = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
+        float sum = 0.0f;
+        bool first = e_j >= 0;
+        for (int jj = 0; jj < k; ++jj) {
+            const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
+            const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_j), jj));
+            if (e2 == e_j) {
+                sum = sum + w2;
+                if (jj < lane) first = false;
+            }
+        }
+        for (int d = d0; d < G && d < d0 + kRanksPerGroup; ++d) {
+            const int32_t pd = __builtin_amdgcn_readlane(p, d);
+            float* base = static_cast<float*>(dw.p[d]);
+            if (pd < 0 || base == nullptr) continue;
+            write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
+        }
+    }
+
+    int32_t r[kRanksPerGroup];
+#pragma unroll
+    for (int q = 0; q < kRanksPerGroup; ++q)
+        r[q] = d0 + q < G ? __builtin_amdgcn_readlane(p, d0 + q) : -1;
+    const int v = pt * kTileLanes + tid;    // past the row end: reads 0, stores nothing
+    uint4 val = load_row16<0>(buffer_rsrc(x + t * nvec, nvec * 16), v * 16);
+    keep(val);
+#pragma unroll
+    for (int q = 0; q < kRanksPerGroup; ++q)
+        if (r[q] >= 0 && v < nvec)
+            store_row16(buffer_rsrc(static_cast<uint4*>(dx.p[d0 + q]) + (int64_t)r[q] * nvec, nvec * 16),
+                        v * 16, val);
 }
 
 // ------------------------------------------------ receive side, fused permute
@@ -611,6 +676,12 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
 // slot[i, j]; wavefront 0 writes the matching weights, the fp32 sum in
 // increasing j' of the source weights of the slots that select the pair's
 // expert.  Rows with no source (past the received count) return at once.
+// This kernel keeps one workgroup per row: split into 2 KiB row tiles (as
+// the send-side copies are) it took 545 us, or 331 us with one slot group
+// per tile, against 307 us, at 8 ranks x 8192 tokens, hidden 7168.  A
+// received row usually has one or two local slots and a third of the rows
+// have no source, so most tile workgroups only wait on the recv_src -> slot
+// loads and exit.
 template <int NT, int VPT>
 __global__ __launch_bounds__(NT)
 void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
@@ -666,12 +737,17 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
             for (int u = 0; u < VPT; ++u) store_row16(dst, (vb + u * NT) * 16, buf[u]);
         }
     }
-    for (int v = full * kPass + tid; v < nvec; v += NT) {
-        uint4 val = xr[v];
+    // ragged tail, the same trip count for every lane (readlane needs the
+    // whole wavefront active); past the row end reads 0, stores nothing
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(xr, nvec * 16);
+    for (int v0 = full * kPass; v0 < nvec; v0 += NT) {
+        const int v = v0 + tid;
+        uint4 val = load_row16<0>(xrs, v * 16);
         keep(val);
         for (int j = 0; j < k; ++j) {
             const int32_t r = __builtin_amdgcn_readlane(sl, j);
-            if (r >= 0) store_row16(buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16), v * 16, val);
+            if (r >= 0 && v < nvec)
+                store_row16(buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16), v * 16, val);
         }
     }
 }
@@ -738,8 +814,11 @@ void combine_ranked_kernel(RankPtrs src, int64_t src_rows, const int32_t* __rest
     const int lane = tid & 63;
     int32_t p = lane < G ? s2d[t * G + lane] : -1;
     if (p >= src_rows) p = -1;
-    uint4* o = out + t * nvec;
-    for (int v0 = tid; v0 < nvec; v0 += NT * U) {
+    const __amdgpu_buffer_rsrc_t ors = buffer_rsrc(out + t * nvec, nvec * 16);
+    // the same trip count for every lane (readlane needs the whole wavefront
+    // active); vectors past the row end read 0 and are not stored
+    for (int vb = 0; vb < nvec; vb += NT * U) {
+        const int v0 = vb + tid;
         float acc[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -765,8 +844,39 @@ void combine_ranked_kernel(RankPtrs src, int64_t src_rows, const int32_t* __rest
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (v0 + u * NT < nvec) o[v0 + u * NT] = pack8(acc[u]);
+            if (v0 + u * NT < nvec) store_row16(ors, (v0 + u * NT) * 16, pack8(acc[u]));
     }
+}
+
+// Tiled form (rows of more than 64 vectors): workgroup b is tile b % tpr of
+// token b / tpr, one 16-byte column vector per lane, stored once with a
+// streaming store (the expanded combine's tiling; its measurements apply).
+__global__ __launch_bounds__(kTileLanes)
+void combine_ranked_tile_kernel(RankPtrs src, int64_t src_rows, const int32_t* __restrict__ s2d,
+                                int nvec, int G, int tpr, uint4* __restrict__ out)
+{
+    constexpr int kGroup = 8;
+    const int64_t tile = blockIdx.x;
+    const int64_t t = tile / tpr;
+    const int pt = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    int32_t p = lane < G ? s2d[t * G + lane] : -1;
+    if (p >= src_rows) p = -1;
+    const int v = pt * kTileLanes + tid;    // past the row end: reads 0, stores nothing
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int d0 = 0; d0 < G; d0 += kGroup) {
+        uint4 val[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+            const int d = d0 + j;
+            const int32_t r = d < G ? __builtin_amdgcn_readlane(p, d) : -1;
+            val[j] = load16_nt(src_rsrc(d < G ? src.p[d] : src.p[0], r, nvec), v);
+        }
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) add8(acc, val[j]);
+    }
+    if (v < nvec) store_row16(buffer_rsrc(out + t * nvec, nvec * 16), v * 16, pack8(acc));
 }
 
 }  // namespace
@@ -871,6 +981,17 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     const dim3 grid((unsigned)num_tokens);
     const uint4* xx = static_cast<const uint4*>(x);
     const int El = num_experts / num_ranks;
+    const int tpr = tiles_per_row(nvec);
+    const int groups = (num_ranks + kRanksPerGroup - 1) / kRanksPerGroup;
+    const int64_t num_tiles = num_tokens * tpr;
+    const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
+    if (x_scales == nullptr && nvec > 64 && blocks <= INT32_MAX) {
+        hipLaunchKernelGGL(dispatch_ranked_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
+                           stream, xx, nvec, topk_idx, topk_weights, num_topk, num_experts, El,
+                           num_ranks, s2d, dest_rows, dest_x, dest_w, with_weights, tpr, num_tiles,
+                           groups);
+        return hipGetLastError();
+    }
 #define EP_DR(NT, V)                                                                            \
     hipLaunchKernelGGL((dispatch_ranked_kernel<NT, V>), grid, dim3(NT), 0, stream, xx, nvec,    \
                        topk_idx, topk_weights, num_topk, num_experts, El, num_ranks, s2d,        \
@@ -971,6 +1092,13 @@ hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const 
     const int nvec = hidden / 8;
     const dim3 grid((unsigned)num_tokens);
     uint4* oo = static_cast<uint4*>(out);
+    const int tpr = tiles_per_row(nvec);
+    const int64_t tiles = num_tokens * tpr;
+    if (nvec > 64 && tiles <= INT32_MAX) {
+        hipLaunchKernelGGL(combine_ranked_tile_kernel, dim3((unsigned)tiles), dim3(kTileLanes), 0,
+                           stream, src_y, src_rows, s2d, nvec, num_ranks, tpr, oo);
+        return hipGetLastError();
+    }
     if (nvec <= 64)
         hipLaunchKernelGGL((combine_ranked_kernel<64, 1>), grid, dim3(64), 0, stream, src_y,
                            src_rows, s2d, nvec, num_ranks, oo);

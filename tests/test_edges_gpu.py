@@ -131,6 +131,11 @@ def check_case(idx, x_bits, w, E, seed=0, use_weights=True, stream=None):
     (16, 2, 8, 65536),     # hidden = EP_MAX_HIDDEN
     (40000, 8, 1024, 8),   # 320000 pairs: 1280-pair chunks, 250 of them
     (65537, 8, 256, 8),    # 524296 pairs: 2304-pair chunks, a ragged last one
+    # rows shorter than k lanes: the slots of lanes past the row end are
+    # still read (by readlane) while only the row's lanes have work
+    (129, 8, 16, 24),      # 3-vector rows, 8 slots
+    (77, 12, 16, 24),      # 3-vector rows, k = 12: the generic combine loop
+    (40, 40, 64, 520),     # 65-vector rows: a one-vector tail past 64 lanes, k = 40
 ])
 def test_shapes(T, k, E, H):
     inp = make_random_case(T * 31 + k, T, H, E, k, mask_frac=0.1, dup_frac=0.0 if k <= E else 1.0)

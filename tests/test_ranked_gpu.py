@@ -242,7 +242,10 @@ def check_combine(ys, s2d, clip_rows=None):
 
 
 @pytest.mark.parametrize("G,T,H", [(1, 5, 8), (2, 100, 24), (3, 257, 1032), (8, 300, 7168),
-                                   (9, 64, 256), (64, 20, 512)])
+                                   (9, 64, 256), (64, 20, 512),
+                                   # more ranks than the row has vectors: every rank's
+                                   # row is read (readlane) while few lanes have work
+                                   (8, 129, 24), (64, 20, 40)])
 def test_combine_ranked_small(G, T, H):
     rng = np.random.default_rng(G * 31 + T)
     s2d = np.full((T, G), -1, np.int32)
