@@ -608,7 +608,7 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
     }
 }
 
-// Tiled form (token rows of more than 64 vectors, no scale rows): workgroup
+// Tiled form (token rows of at least 512 vectors, no scale rows): workgroup
 // b maps (XCD-aware) to tile = (token t, tile pt of its row) and a group of
 // kRanksPerGroup destination ranks; the tile's loads after the first hit
 // the XCD's L2.  Tile 0's workgroups also write the group's weight rows.
@@ -985,7 +985,7 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     const int groups = (num_ranks + kRanksPerGroup - 1) / kRanksPerGroup;
     const int64_t num_tiles = num_tokens * tpr;
     const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
-    if (x_scales == nullptr && nvec > 64 && blocks <= INT32_MAX) {
+    if (x_scales == nullptr && nvec >= kMinTiledDispatchVectors && blocks <= INT32_MAX) {
         hipLaunchKernelGGL(dispatch_ranked_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
                            stream, xx, nvec, topk_idx, topk_weights, num_topk, num_experts, El,
                            num_ranks, s2d, dest_rows, dest_x, dest_w, with_weights, tpr, num_tiles,

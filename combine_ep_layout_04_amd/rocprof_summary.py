@@ -2,6 +2,7 @@
 
     python -m combine_ep_layout_04_amd.rocprof_summary stats DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary pmc DIR --cmd "..." > profiles/X.md
+    python -m combine_ep_layout_04_amd.rocprof_summary counters DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
         --cmd "..." --out profiles/hbm_traffic_headline.txt
 
@@ -9,7 +10,8 @@
 without ``-T`` so that template instances stay apart) and prints each
 kernel's name without its namespace and argument list;
 ``pmc`` reads ``*_counter_collection.csv`` (from ``--pmc``) and reports the
-mean counter value per dispatch for each kernel; ``traffic`` takes one
+mean counter value per dispatch for each kernel; ``counters`` makes one row
+per kernel with the median per dispatch of each counter; ``traffic`` takes one
 FETCH_SIZE run and one WRITE_SIZE run of ``bench.py --copy-calibration``,
 scales each counter by what it reads for the plain 1 GiB elementwise copy
 (torch.neg on int32: 1 GiB read, 1 GiB written) and writes HBM bytes per
@@ -78,6 +80,33 @@ def pmc(d: str):
     return out
 
 
+def _library_kernel(short: str) -> bool:
+    """The library's own kernels (not torch's or the HIP runtime's)."""
+    return not short.startswith(("at::", "__amd_rocclr", "(anonymous namespace)::elementwise"))
+
+
+def counters(d: str):
+    """One row per library kernel, one column per counter: the median per
+    dispatch."""
+    vals = defaultdict(list)
+    names = set()
+    for f in _find(d, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = short_name(r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName"))
+                counter = r.get("Counter_Name") or r.get("Counter-Name")
+                vals[(name, counter)].append(float(r.get("Counter_Value") or r.get("Counter-Value")))
+                names.add(counter)
+    cols = sorted(names)
+    kernels = sorted({k for k, _ in vals if _library_kernel(k)})
+    out = ["| kernel | dispatches | " + " | ".join(cols) + " |", "|---" * (len(cols) + 2) + "|"]
+    for k in kernels:
+        n = max(len(vals.get((k, c), [])) for c in cols)
+        cells = [f"{statistics.median(vals[(k, c)]):.0f}" if (k, c) in vals else "" for c in cols]
+        out.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
+    return out
+
+
 def _counter_medians(d: str):
     vals = defaultdict(list)
     for f in _find(d, "counter_collection.csv"):
@@ -89,7 +118,8 @@ def _counter_medians(d: str):
 
 
 # library kernels by the key bench.py reports them under, as a pattern on
-# the full kernel name; the 8-bit cast is told apart by its template
+# the full kernel name (the headline workload's instance: rows of 896
+# vectors take the tiled bf16 dispatch, combine and per-rank kernels); the 8-bit cast is told apart by its template
 # arguments <rows per lane, format (0 E4M3, 1 E5M2), scale (0 fp32, 1 power
 # of two, 2 UE8M0)>.  The median over a kernel's dispatches is used: the
 # E4M3 / fp32 instance also runs once over the tokens themselves (T rows,
@@ -97,24 +127,25 @@ def _counter_medians(d: str):
 # counts the dispatch-backward launches, which run the same kernel over the
 # same bytes plus a [T, k] gather.
 KERNEL_KEYS = {
-    "dispatch_bf16": r"dispatch_bf16_kernel<",
+    "dispatch_bf16": r"dispatch_bf16_tile_kernel",
     "dispatch_fp8": r"dispatch_fp8_kernel<\d+, 0, 0>",
     "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_kernel<\d+, 1, 0>",
     "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_kernel<\d+, 0, 1>",
     "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_kernel<\d+, 0, 2>",
     "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_kernel<\d+, 1, 2>",
     "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
-    "combine": r"[^_]combine_kernel<",
+    "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": r"combine_backward_kernel<",
     "layout_count": r"layout_count_kernel\(",
     "layout_scatter": r"layout_scatter_kernel\(",
     "routing_map": r"routing_map_kernel\(",
     "rank_count": r"rank_count_kernel<",
     "rank_scatter": r"rank_scatter_kernel<",
-    # bf16 rows (896 vectors: 128 lanes) and 8-bit code rows (448: 64 lanes)
-    "dispatch_ranked": r"dispatch_ranked_kernel<128,",
+    # bf16 rows go through the tiled kernel, 8-bit code rows with their
+    # scales (448 vectors: 64 lanes) through the per-token one
+    "dispatch_ranked": r"dispatch_ranked_tile_kernel",
     "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64,",
-    "combine_ranked": r"combine_ranked_kernel<",
+    "combine_ranked": r"combine_ranked_tile_kernel",
     "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
@@ -148,11 +179,12 @@ def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc", "traffic"])
+    ap.add_argument("kind", choices=["stats", "pmc", "counters", "traffic"])
     ap.add_argument("dir")
     ap.add_argument("dir2", nargs="?")
     ap.add_argument("--cmd", required=True, help="the command(s) that produced the data")
     ap.add_argument("--title", default="")
+    ap.add_argument("--note", default="", help="a paragraph printed under the command")
     ap.add_argument("--out")
     a = ap.parse_args()
     if a.kind == "traffic":
@@ -166,7 +198,9 @@ def main():
         print(text, end="")
         return
     lines = [f"# {a.title or a.kind}", "", "Command:", "", "```", a.cmd, "```", ""]
-    lines += stats(a.dir) if a.kind == "stats" else pmc(a.dir)
+    if a.note:
+        lines += [a.note, ""]
+    lines += {"stats": stats, "pmc": pmc, "counters": counters}[a.kind](a.dir)
     print("\n".join(lines))
 
 

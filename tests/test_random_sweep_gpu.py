@@ -13,7 +13,8 @@ dedicated tests:
   for the weight gradients).
 
 Shapes stay small (the oracle runs each case in well under a second) but
-cover ragged rows (hidden not a multiple of the vector pass), one-token and
+cover ragged rows (hidden not a multiple of the vector pass, and rows long
+enough to be split into tiles with a one-vector last tile), one-token and
 one-expert cases, and k above the expert count.
 """
 
@@ -38,7 +39,8 @@ def draw(seed):
     E = int(rng.choice([1, 2, 3, 8, 16, 24, 64, 96, 256]))
     k = int(rng.integers(1, 13))
     fp8 = bool(rng.random() < 0.5)
-    H = int(rng.choice([128, 256, 1152, 2048])) if fp8 else int(rng.choice([8, 24, 136, 1032, 2048]))
+    # 4104: 513-vector rows, tiled with a one-vector last tile
+    H = int(rng.choice([128, 256, 1152, 2048])) if fp8 else int(rng.choice([8, 24, 136, 1032, 2048, 4104]))
     mode = rng.choice(["plain", "aligned", "capacity"], p=[0.5, 0.3, 0.2])
     A = int(rng.choice([2, 16, 128])) if mode == "aligned" else 1
     cap = int(rng.choice([1, 4, 32])) * A if mode == "capacity" else 0
