@@ -34,18 +34,25 @@
 //                 the receive-side rows, and all workgroups clear the rows
 //                 past the received count; workgroup 0 also sums the
 //                 per-chunk receive-side counts into the totals.
-//   dispatch:     one workgroup per token reads the row once into registers
-//                 and stores it, non-temporally, to every rank that receives
-//                 it (a table of G row pointers passed by value), with the
-//                 token's weights for that rank's experts.
+//   dispatch:     one workgroup per (2 KiB tile of a token's row, group of
+//                 4 destination ranks), the tile's workgroups back to back
+//                 on one XCD; it loads its tile once and stores it, with
+//                 streaming stores, to each rank of the group that receives
+//                 the token (a table of G row pointers passed by value);
+//                 tile 0 also writes the token's weights for those ranks'
+//                 experts.  Rows under 512 vectors, and 8-bit rows with
+//                 their scales, take one workgroup per token that holds the
+//                 row in registers.
 //   fused permute: the receiving rank's dispatch with the permute folded
 //                 in: one workgroup per received token reads the sender's
 //                 row once and stores it to each of the rank's local-expert
 //                 rows, with the weights.
-//   combine:      one workgroup per token gathers its rows from the G
-//                 buffers through buffer resources (an unrouted rank gets a
-//                 0-byte resource: its loads return 0 without a branch) and
-//                 sums them in fp32 in increasing rank.
+//   combine:      one workgroup per (token, 2 KiB tile) gathers its
+//                 vectors from the G buffers through buffer resources (an
+//                 unrouted rank gets a 0-byte resource: its loads return 0
+//                 without a branch), sums them in fp32 in increasing rank
+//                 and stores once, with a streaming store (rows of at most
+//                 64 vectors: one workgroup per token).
 
 #include "ep_device.h"
 #include "ep_internal.h"
