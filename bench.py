@@ -29,6 +29,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -62,16 +63,24 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed, so
+    that editing a comment does not count as changing the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel_key: str) -> str:
-    """Digest of what a kernel's counters depend on: its source file, the
-    internal and device headers and the hipcc flags."""
+    """Digest of what a kernel's counters depend on: the code of its source
+    file and of the internal and device headers, and the hipcc flags."""
     from combine_ep_layout_04_amd.build import HIPCC_FLAGS
 
     csrc = os.path.join(ROOT, "combine_ep_layout_04_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h", "ep_device.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     h.update(" ".join(HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 

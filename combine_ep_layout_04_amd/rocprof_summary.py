@@ -167,7 +167,8 @@ def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
              "# each scaled by the same counter on a plain 1 GiB elementwise copy (torch.neg,",
              "# int32): scale = 1048576 KiB / counter.  Commands:",
              *[f"#   {c}" for c in cmd.split(" ;; ")],
-             "# source_digest: the kernel's source file, internal header and hipcc flags",
+             "# source_digest: the code (comments and spacing left out) of the kernel's source",
+             "# file and of the internal and device headers, and the hipcc flags",
              f"copy_scale fetch={f_scale:.4f} write={w_scale:.4f}"]
     for key, needle in KERNEL_KEYS.items():
         fk, wk = pick(fetch, needle), pick(write, needle)
