@@ -10,11 +10,15 @@
 namespace ep {
 
 // Layout: pairs are processed in chunks of flat indices, one workgroup of
-// kLayoutThreads per chunk in both launches.  A chunk holds at least
-// kLayoutMinChunk pairs and the chunk count never exceeds kLayoutMaxChunks,
-// so the per-workgroup histogram pass stays bounded for any input size.
+// kLayoutThreads per chunk in both launches.  Inputs of up to
+// kLayoutSmallChunks * kLayoutMinChunk pairs are cut into about
+// kLayoutSmallChunks chunks of at least one 256-pair batch (more workgroups,
+// shorter chains); larger ones into chunks of at least kLayoutMinChunk
+// pairs, never more than kLayoutMaxChunks of them, so the per-workgroup
+// histogram pass stays bounded for any input size.
 constexpr int kLayoutThreads = 256;
 constexpr int64_t kLayoutMinChunk = 1024;
+constexpr int64_t kLayoutSmallChunks = 64;
 constexpr int64_t kLayoutMaxChunks = 256;
 
 int64_t layout_chunk_pairs(int64_t pairs);

@@ -41,14 +41,17 @@ def test_version_and_status_strings():
 
 def test_workspace_size():
     # one int32 per (chunk, expert) plus one per chunk, chunks padded to a
-    # multiple of 4, 256-byte aligned; chunks hold 1024 pairs until there
-    # would be more than 256 of them
+    # multiple of 4, 256-byte aligned; up to 65536 pairs about 64 chunks of
+    # at least 256 pairs, beyond that chunks of 1024 pairs until there would
+    # be more than 256 of them
     def want(chunks, E):
         cp = (chunks + 3) // 4 * 4
         return ((cp * E + cp) * 4 + 255) // 256 * 256
     assert ep.layout_workspace_size(8192, 8, 256) == want(64, 256) == 64 * 257 * 4
     assert ep.layout_workspace_size(0, 8, 256) == want(1, 256)
-    assert ep.layout_workspace_size(1000, 3, 7) == want(3, 7)
+    assert ep.layout_workspace_size(1000, 3, 7) == want(12, 7)          # 256-pair chunks
+    assert ep.layout_workspace_size(4096, 4, 64) == want(64, 64)        # 256-pair chunks
+    assert ep.layout_workspace_size(4096, 8, 64) == want(64, 64)        # 512-pair chunks
     assert ep.layout_workspace_size(65536, 8, 256) == want(256, 256)     # 2048-pair chunks
     assert ep.layout_workspace_size(65537, 8, 256) == want(228, 256)     # 2304-pair chunks
     assert ep.layout_workspace_size(10, 0, 8) == 0
