@@ -176,6 +176,7 @@ def check_dispatch(x_bits, idx, w, E, G, s2d, rows, with_weights=True):
     (3, 64, 2048, 9, 9, False),       # k = 9 > E/G, no weights
     (8, 130, 7168, 64, 8, True),
     (64, 10, 256, 64, 64, True),      # k = EP_MAX_TOPK, G = EP_MAX_RANKS
+    (64, 20, 4104, 64, 8, True),      # tiled rows (513 vectors), 16 groups of 4 ranks
 ])
 def test_dispatch_ranked_small(G, T, H, E, k, weights):
     inp = make_random_case(G * 7 + H, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
@@ -245,7 +246,9 @@ def check_combine(ys, s2d, clip_rows=None):
                                    (9, 64, 256), (64, 20, 512),
                                    # more ranks than the row has vectors: every rank's
                                    # row is read (readlane) while few lanes have work
-                                   (8, 129, 24), (64, 20, 40)])
+                                   (8, 129, 24), (64, 20, 40),
+                                   # tiled rows with every rank group of 8 loads
+                                   (64, 20, 4104)])
 def test_combine_ranked_small(G, T, H):
     rng = np.random.default_rng(G * 31 + T)
     s2d = np.full((T, G), -1, np.int32)
