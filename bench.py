@@ -187,8 +187,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of dispatch/combine; runs on more than one GPU "
-              "are not part of this build (see the sharding design).", file=sys.stderr)
+        print("bench.py measures one GPU's share of dispatch and combine; it does not run on "
+              "more than one GPU.", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
