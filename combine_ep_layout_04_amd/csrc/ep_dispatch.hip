@@ -485,7 +485,8 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
 }
 
 // Pre-quantized input (one wavefront per token; the cast's tiling, tried
-// here too, measured 117 us against 114 us): the 8-bit code row (hidden bytes, VPT 16-byte units
+// here too in both workgroup orders, measured 117 us against 114 us): the
+// 8-bit code row (hidden bytes, VPT 16-byte units
 // per lane per pass) and the fp32 scale row of token t are copied to every
 // unmasked slot.  No arithmetic: any 8-bit float format passes through.
 // Output scales row-major (sld == 0) or column-major [nb, sld].
