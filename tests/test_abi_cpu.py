@@ -5,6 +5,8 @@ launching anything (these calls fail validation, so no HIP call is made)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -22,6 +24,25 @@ def declared_functions():
 
 def test_header_declares_the_binding_symbols():
     assert declared_functions() == sorted(ep.SYMBOLS)
+
+
+@pytest.mark.parametrize("compiler,flags", [
+    ("gcc", ["-x", "c", "-std=c99", "-pedantic-errors"]),
+    ("g++", ["-x", "c++", "-std=c++17", "-pedantic-errors"]),
+])
+def test_header_is_plain_c(tmp_path, compiler, flags):
+    # the header compiles as strict C99 and as C++ on its own (no HIP or
+    # torch headers), and every declared function can be named from C
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    names = declared_functions()
+    src = tmp_path / "use_ep.c"
+    src.write_text('#include "ep.h"\n'
+                   "typedef void (*fn)(void);\n"
+                   "fn table[] = {\n" + "".join(f"    (fn){n},\n" for n in names) + "};\n")
+    r = subprocess.run([compiler, *flags, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
 
 
 def test_library_exports_every_declared_symbol():
