@@ -35,6 +35,11 @@ HIPCC_FLAGS = [
 ]
 
 
+DEMO_SRC = os.path.join(PKG, "examples", "c_abi_demo.c")
+DEMO = os.path.join(PKG, "examples", "c_abi_demo")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -63,5 +68,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_demo(verbose: bool = False) -> str:
+    """Compile the plain-C example (examples/c_abi_demo.c) with gcc against
+    include/ep.h and libep.so: the C ABI used with no Python in the way."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or "cc"
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{INCLUDE}", f"-I{ROCM}/include", "-o", DEMO, DEMO_SRC, f"-L{PKG}", "-lep",
+           f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{ROCM}/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the C example failed:\n" + res.stdout + res.stderr)
+    return DEMO
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_demo(verbose="-v" in sys.argv))

@@ -1,0 +1,29 @@
+"""The C ABI from plain C: examples/c_abi_demo (built by build() with gcc
+against include/ep.h and libep.so, no Python or PyTorch in the process)
+runs layout, bf16 dispatch and combine on hipMalloc'd buffers and checks
+the invariants its header comment lists; it exits 0 when they all hold."""
+
+import os
+import subprocess
+
+import pytest
+
+from combine_ep_layout_04_amd.build import DEMO
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T,H,E,k", [
+    (1024, 7168, 256, 8),   # tiled dispatch and combine
+    (513, 4104, 64, 6),     # ragged last tiles, two slot groups
+    (100, 24, 8, 3),        # short rows: one workgroup per token
+    (1, 8, 1, 1),
+])
+def test_c_demo(T, H, E, k):
+    assert os.path.exists(DEMO), "build() makes the C example"
+    print(f"\n[c-abi] c_abi_demo {T} {H} {E} {k}", flush=True)
+    r = subprocess.run([DEMO, str(T), str(H), str(E), str(k)], capture_output=True, text=True,
+                       timeout=120)
+    print(r.stdout.strip(), r.stderr.strip(), flush=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "layout ok, rows ok, combine ok" in r.stdout
