@@ -48,10 +48,22 @@ constexpr int kTileLanes = 128;
 
 __host__ __device__ inline int tiles_per_row(int nvec) { return (nvec + kTileLanes - 1) / kTileLanes; }
 
-// The dispatches (one row to several destinations) are tiled from rows of
-// this many vectors on; shorter rows stay one workgroup per token, which
-// measured faster for them (hidden 2048, k 4: 19.2 us against 21.6 us).
+// When a dispatch (one row to several destinations) is tiled.  Measured
+// against one workgroup per token on MI355X (T 2048-8192, k 4 and 8,
+// hidden 1536-4096, caches emptied before each launch):
+//   - rows of 512 vectors and more: tiles as fast or faster everywhere;
+//   - rows of 256 or 384 vectors (whole tiles): tiles 3-7% faster once the
+//     dispatch writes at least 2^23 vectors (134 MB), up to 19% slower below;
+//   - rows that end in a partial tile (192 vectors): tiles 7-11% slower.
 constexpr int kMinTiledDispatchVectors = 512;
+constexpr int64_t kMinTiledDispatchWork = int64_t(1) << 23;   // vectors written
+
+__host__ __device__ inline bool tile_dispatch(int nvec, int64_t rows_written)
+{
+    return nvec >= kMinTiledDispatchVectors ||
+           (nvec >= 2 * kTileLanes && nvec % kTileLanes == 0 &&
+            rows_written * nvec >= kMinTiledDispatchWork);
+}
 
 // Workgroups are dispatched to the 8 XCDs round robin (workgroup b runs on
 // XCD b % 8), and each XCD has its own L2.  When `per_tile` workgroups

@@ -17,8 +17,9 @@
 //     written to all k rows) this measured 200 us instead of 218 us at
 //     T=8192, hidden 7168, k=8 with cold caches: workgroups that each write
 //     a few 2 KiB pieces stream faster than ones that write 56 in turn.
-//     Rows of fewer than 512 vectors, and grids past 2^31 workgroups, keep
-//     one workgroup per token;
+//     Short rows (under 512 vectors, unless they are whole tiles and the
+//     dispatch writes at least 2^23 vectors), and grids past 2^31
+//     workgroups, keep one workgroup per token;
 //   - the slots a workgroup serves are wavefront-uniform (read into lanes,
 //     then readlane), so the loop over destinations has no divergence;
 //   - fp8: each lane owns 16 channels (a "unit": two 16-byte loads in, one
@@ -591,7 +592,7 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, i
     const int groups = (num_topk + kSlotsPerGroup - 1) / kSlotsPerGroup;
     const int64_t num_tiles = num_tokens * tpr;
     const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
-    if (nvec >= kMinTiledDispatchVectors && blocks <= INT32_MAX) {
+    if (tile_dispatch(nvec, num_tokens * num_topk) && blocks <= INT32_MAX) {
         hipLaunchKernelGGL(dispatch_bf16_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
                            stream, static_cast<const uint4*>(x), nvec, num_topk, tpr, num_tiles,
                            groups, slot, topk_weights, static_cast<uint4*>(recv_x), recv_weights);

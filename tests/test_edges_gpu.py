@@ -136,6 +136,10 @@ def check_case(idx, x_bits, w, E, seed=0, use_weights=True, stream=None):
     (129, 8, 16, 24),      # 3-vector rows, 8 slots
     (77, 12, 16, 24),      # 3-vector rows, k = 12: the generic combine loop
     (40, 40, 64, 520),     # 65-vector rows: a one-vector tail past 64 lanes, k = 40
+    # whole-tile rows under 512 vectors in dispatches that write >= 2^23
+    # vectors: the tiled dispatch
+    (8192, 4, 64, 2048),   # 256-vector rows, one slot group
+    (6144, 8, 256, 3072),  # 384-vector rows, two slot groups
 ])
 def test_shapes(T, k, E, H):
     inp = make_random_case(T * 31 + k, T, H, E, k, mask_frac=0.1, dup_frac=0.0 if k <= E else 1.0)
