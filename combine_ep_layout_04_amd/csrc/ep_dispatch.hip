@@ -425,19 +425,25 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 }
 
 // Tiled cast (rows of more than 64 units, row-major scales): workgroup b
-// is (token t, tile p of kTileLanes units = 16 scale blocks, slot group g of
-// up to kCastSlots slots), and all of a token's workgroups run back to back
-// on one XCD, so the pieces of a token's scale rows that different tiles
-// write meet in that XCD's L2.  Each lane casts one unit; lanes 0..7 of each
+// is (token t, tile p of NL units = NL/8 scale blocks, slot group g of up to
+// kCastSlots slots), and all of a token's workgroups run back to back on one
+// XCD, so the pieces of a token's scale rows that different tiles write
+// meet in that XCD's L2.  Each lane casts one unit; lanes 0..7 of each
 // wavefront then hold that wavefront's 8 block scales and store them per
 // destination.  At T=8192, hidden 7168, k=8 this took 122 us against 126 us
 // for one wavefront per token; with tiles spread over the XCDs it took
 // 127 us.  Column-major scales (each a separate 4-byte store) measured
 // slower tiled, 163 us against 140 us, and keep one wavefront per token.
+//
+// Tiles are 128 lanes (NL = kTileLanes), or 64 where 128-lane tiles would
+// launch a third more lanes than the row has units (rows of 129-192 units,
+// hidden 2176-3072): hidden 3072 took 52.7 us in 64-lane tiles against
+// 59.1 us in 128-lane ones.  Elsewhere widths of 64 to 512 lanes measured
+// within 3% of 128 (hidden 4096-16384, T=8192, k=8).
 constexpr int kCastSlots = 8;
 
-template <int FMT, int SM>
-__global__ __launch_bounds__(kTileLanes)
+template <int FMT, int SM, int NL>
+__global__ __launch_bounds__(NL)
 void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int tpr, int64_t T,
                               int groups, const int32_t* __restrict__ slot,
                               const float* __restrict__ w, uint4* __restrict__ recv_q,
@@ -461,14 +467,14 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
 
     // units past the row end (last tile) read zeros and store nothing; whole
     // blocks lie on one side of the row end (units is a multiple of 8)
-    const int unit = p * kTileLanes + tid;
+    const int unit = p * NL + tid;
     const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x + t * nvec, nvec * 16);
     const uint4 d0 = load_row16<0>(xs, unit * 32);
     const uint4 d1 = load_row16<0>(xs, unit * 32 + 16);
     uint32_t sb;
     const uint4 code = quantise16<FMT, SM>(d0, d1, sb);
     const uint32_t my_scale = (uint32_t)__shfl((int)sb, (lane & 7) * kLanesPerBlock, 64);
-    const int bk = p * (kTileLanes / kLanesPerBlock) + (tid >> 6) * 8 + lane;   // lanes 0..7
+    const int bk = p * (NL / kLanesPerBlock) + (tid >> 6) * 8 + lane;   // lanes 0..7
     const bool scale_lane = lane < 8 && bk < nb;
 #pragma unroll
     for (int q = 0; q < kCastSlots; ++q) {
@@ -653,15 +659,22 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     const uint4* xx = static_cast<const uint4*>(x);
     uint4* qq = static_cast<uint4*>(recv_q);
     const int units = hidden / 16;
-    const int tpr = (units + kTileLanes - 1) / kTileLanes;
+    // 64-lane tiles when 128-lane ones would launch at least 4/3 as many lanes
+    const bool narrow = 4 * ((units + 63) / 64 * 64) <= 3 * ((units + 127) / 128 * 128);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (units + lanes - 1) / lanes;
     const int groups = (num_topk + kCastSlots - 1) / kCastSlots;
     const int64_t blocks = (num_tokens + 7) / 8 * 8 * tpr * groups;
     const bool tiled = units > 64 && blocks <= INT32_MAX && scale_ld == 0;
+#define EP_FP8_TILES(F, M, NL)                                                                  \
+    hipLaunchKernelGGL((dispatch_fp8_tile_kernel<F, M, NL>), dim3((unsigned)blocks), dim3(NL), 0, \
+                       stream, xx, nvec, num_topk, tpr, num_tokens, groups, slot, topk_weights, qq, \
+                       recv_scales, recv_weights)
 #define EP_FP8_MODE(F, M)                                                                    \
-    if (tiled)                                                                               \
-        hipLaunchKernelGGL((dispatch_fp8_tile_kernel<F, M>), dim3((unsigned)blocks),         \
-                           dim3(kTileLanes), 0, stream, xx, nvec, num_topk, tpr, num_tokens, \
-                           groups, slot, topk_weights, qq, recv_scales, recv_weights);       \
+    if (tiled && narrow)                                                                     \
+        EP_FP8_TILES(F, M, kTileLanes / 2);                                                  \
+    else if (tiled)                                                                          \
+        EP_FP8_TILES(F, M, kTileLanes);                                                      \
     else                                                                                     \
         launch_fp8_shape<F, M>(vpt, grid, stream, xx, nvec, num_topk, slot, topk_weights, qq, \
                                recv_scales, recv_weights, scale_ld)
@@ -675,6 +688,7 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
         else EP_FP8_MODE(kE4M3, kScaleFp32);
     }
 #undef EP_FP8_MODE
+#undef EP_FP8_TILES
     return hipGetLastError();
 }
 

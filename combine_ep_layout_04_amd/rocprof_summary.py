@@ -129,11 +129,11 @@ def _counter_medians(d: str):
 # same bytes plus a [T, k] gather.
 KERNEL_KEYS = {
     "dispatch_bf16": r"dispatch_bf16_tile_kernel",
-    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0>",
-    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0>",
-    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1>",
-    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2>",
-    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2>",
+    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 128>",
+    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 128>",
+    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 128>",
+    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 128>",
+    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 128>",
     "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
     "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": r"combine_backward_kernel<",

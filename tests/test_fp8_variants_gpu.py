@@ -165,6 +165,24 @@ def test_prequantized_column_major_scales():
     assert np.all(np.isnan(host(s)[:, n:]))
 
 
+@pytest.mark.parametrize("fmt,mode", COMBOS)
+def test_variants_narrow_tiles(fmt, mode):
+    # hidden 2560 (160 units): the tiled cast in 64-lane tiles, three per
+    # row (the last half empty), 10 slots in two groups, special blocks in
+    # every tile
+    inp = make_random_case(57, 101, 2560, 16, 10, mask_frac=0.1)
+    x = float32_from_bf16_bits(inp.x_bits).copy()
+    x[0, :128] = 0.0
+    x[1, 1024:1152] *= 1e-37
+    x[2, 2100] = np.inf
+    x[3, 2500] = np.nan
+    x[4, 1100] = -57344.0
+    x[5, 2048:2176] = 2.0 ** -90
+    print(f"\n[fp8 variants] 64-lane tiles {fmt} {mode}", flush=True)
+    L = oracle.layout(inp.topk_idx, 16)
+    check(bf16_bits_from_float32(x), L, fmt, mode)
+
+
 @pytest.mark.parametrize("fmt,mode", [("e4m3", "fp32"), ("e5m2", "ue8m0")])
 def test_variants_at_max_hidden(fmt, mode):
     # hidden = EP_MAX_HIDDEN: 512 scale blocks, eight passes of 64 blocks
