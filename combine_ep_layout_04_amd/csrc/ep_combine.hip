@@ -26,8 +26,12 @@
 // output's write-back to whatever runs next: at T=8192, hidden 7168, k=8
 // the combine then reads 188 us in its own events but 202 us once a
 // following read pass is charged for the write-back; the tiled kernel with
-// streaming stores takes 185 us either way.  Rows of at most 64 vectors,
-// and grids past 2^31 workgroups, keep one workgroup per token.
+// streaming stores takes 185 us either way.  Tiles are 128 lanes, or 64
+// for rows of 129-192 vectors (hidden 1032-1536), where 128-lane tiles
+// leave a quarter or more of their lanes idle: hidden 1152, 1280 and 1536
+// took 33.3, 36.2 and 42.1 us in 64-lane tiles against 37.7, 40.4 and
+// 45.3 us (T=8192, k=8).  Rows of at most 64 vectors, and grids past 2^31
+// workgroups, keep one workgroup per token.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -159,11 +163,11 @@ void combine_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slo
     }
 }
 
-// Tiled form: workgroup b is tile b % tpr of token b / tpr.  K > 0: exactly
-// K = k slots, unrolled; K == 0: any k, 8 slots' loads in flight at a time
-// (slots past k count as masked: zero data, zero weight).
-template <int K>
-__global__ __launch_bounds__(kTileLanes)
+// Tiled form: workgroup b is tile b % tpr (NL vectors) of token b / tpr.
+// K > 0: exactly K = k slots, unrolled; K == 0: any k, 8 slots' loads in
+// flight at a time (slots past k count as masked: zero data, zero weight).
+template <int K, int NL>
+__global__ __launch_bounds__(NL)
 void combine_tile_kernel(const uint4* __restrict__ y, const int32_t* __restrict__ slot,
                          const float* __restrict__ w, int nvec, int k, int tpr,
                          uint4* __restrict__ out, const float* __restrict__ row_w,
@@ -179,7 +183,7 @@ void combine_tile_kernel(const uint4* __restrict__ y, const int32_t* __restrict_
     const float wl = lane < kk ? (w ? w[t * kk + lane] : 1.0f) : 0.0f;
     if (out_w != nullptr && p == 0 && tid < kk) out_w[t * kk + tid] = sl >= 0 ? row_w[sl] : 0.0f;
 
-    const int v = p * kTileLanes + tid;     // past the row end: reads 0, stores nothing
+    const int v = p * NL + tid;             // past the row end: reads 0, stores nothing
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     constexpr int kBatch = K > 0 ? K : 8;
     for (int j0 = 0; j0 < kk; j0 += kBatch) {
@@ -231,13 +235,20 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
     const dim3 grid((unsigned)num_tokens);
     const uint4* yy = static_cast<const uint4*>(y);
     uint4* oo = static_cast<uint4*>(out);
-    const int tpr = tiles_per_row(nvec);
+    const bool narrow = narrow_tiles(nvec);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (nvec + lanes - 1) / lanes;
     const int64_t tiles = num_tokens * tpr;
     if (nvec > 64 && tiles <= INT32_MAX) {
         const dim3 tg((unsigned)tiles);
-#define EP_COMBINE_TILE(KV)                                                                     \
-    hipLaunchKernelGGL((combine_tile_kernel<KV>), tg, dim3(kTileLanes), 0, stream, yy, slot,      \
+#define EP_COMBINE_TILE_NL(KV, NL)                                                            \
+    hipLaunchKernelGGL((combine_tile_kernel<KV, NL>), tg, dim3(NL), 0, stream, yy, slot,        \
                        topk_weights, nvec, num_topk, tpr, oo, row_w, out_w)
+#define EP_COMBINE_TILE(KV)                                                                     \
+    if (narrow)                                                                                 \
+        EP_COMBINE_TILE_NL(KV, kTileLanes / 2);                                                 \
+    else                                                                                        \
+        EP_COMBINE_TILE_NL(KV, kTileLanes)
         switch (num_topk) {
         case 1: EP_COMBINE_TILE(1); break;
         case 2: EP_COMBINE_TILE(2); break;
@@ -250,6 +261,7 @@ hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_
         default: EP_COMBINE_TILE(0); break;
         }
 #undef EP_COMBINE_TILE
+#undef EP_COMBINE_TILE_NL
         return hipGetLastError();
     }
     // 256 lanes x 2 vectors for long rows (hidden >= 4096: 896 vectors at

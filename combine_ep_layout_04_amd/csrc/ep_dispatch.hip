@@ -435,11 +435,10 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 // 127 us.  Column-major scales (each a separate 4-byte store) measured
 // slower tiled, 163 us against 140 us, and keep one wavefront per token.
 //
-// Tiles are 128 lanes (NL = kTileLanes), or 64 where 128-lane tiles would
-// launch a third more lanes than the row has units (rows of 129-192 units,
-// hidden 2176-3072): hidden 3072 took 52.7 us in 64-lane tiles against
-// 59.1 us in 128-lane ones.  Elsewhere widths of 64 to 512 lanes measured
-// within 3% of 128 (hidden 4096-16384, T=8192, k=8).
+// Tiles are 128 lanes (NL = kTileLanes), or 64 for rows of 129-192 units
+// (narrow_tiles; hidden 2176-3072): hidden 3072 took 52.7 us in 64-lane
+// tiles against 59.1 us in 128-lane ones.  Elsewhere widths of 64 to 512
+// lanes measured within 3% of 128 (hidden 4096-16384, T=8192, k=8).
 constexpr int kCastSlots = 8;
 
 template <int FMT, int SM, int NL>
@@ -659,8 +658,7 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     const uint4* xx = static_cast<const uint4*>(x);
     uint4* qq = static_cast<uint4*>(recv_q);
     const int units = hidden / 16;
-    // 64-lane tiles when 128-lane ones would launch at least 4/3 as many lanes
-    const bool narrow = 4 * ((units + 63) / 64 * 64) <= 3 * ((units + 127) / 128 * 128);
+    const bool narrow = narrow_tiles(units);
     const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
     const int tpr = (units + lanes - 1) / lanes;
     const int groups = (num_topk + kCastSlots - 1) / kCastSlots;

@@ -135,6 +135,31 @@ def test_dispatch_backward(name, T):
     assert np.all(np.abs(got - want) <= tol)
 
 
+@pytest.mark.parametrize("T,H,E,k", [(333, 1536, 24, 6), (129, 1288, 16, 11)])
+def test_dispatch_backward_narrow_tiles(T, H, E, k):
+    # rows of 129-192 vectors: the combine kernel in 64-lane tiles, with the
+    # weight gather from tile 0 (k = 11: the generic slot loop)
+    inp = make_random_case(T + H, T, H, E, k, mask_frac=0.1)
+    print(f"\n[backward] dispatch, 64-lane tiles T={T} H={H} k={k}", flush=True)
+    L = oracle.layout(inp.topk_idx, E)
+    rows = T * k
+    grad_recv = make_gradient(rows, H, 23)
+    grad_recv_w = np.random.default_rng(24).standard_normal(rows).astype(np.float32)
+    gx, gw = ep.ep_dispatch_backward(x_dev(grad_recv), dev(grad_recv_w), dev(L.slot))
+    torch.cuda.synchronize()
+    o_gx, o_gw = oracle.dispatch_backward(grad_recv, grad_recv_w, L.slot, T)
+    np.testing.assert_array_equal(host(gw), o_gw)
+    got = float32_from_bf16_bits(bf16_bits(gx)).astype(np.float64)
+    want = float32_from_bf16_bits(o_gx).astype(np.float64)
+    gr = np.abs(float32_from_bf16_bits(grad_recv).astype(np.float64))
+    s = np.zeros_like(want)
+    for j in range(k):
+        r = L.slot[:, j]
+        ok = r >= 0
+        s[ok] += gr[r[ok]]
+    assert np.all(np.abs(got - want) <= bf16_ulp(want) + 2.0 * k * 2.0 ** -24 * s)
+
+
 def test_combine_backward_ties():
     # weights with short significands make w * g land exactly on bf16
     # midpoints (ties to even); full-precision weights give products that
