@@ -50,10 +50,11 @@ __host__ __device__ inline int tiles_per_row(int nvec) { return (nvec + kTileLan
 
 // Rows of 129-192 units fill 128-lane tiles only three quarters or less (a
 // 192-unit row takes 256 lanes); in 64-lane tiles they take at most 192.
-// There, 64-lane tiles measured faster on MI355X (T=8192, k=8, caches
-// emptied before each launch, interleaved rounds): the combine at hidden
-// 1152-1536 by 7-12%, the 8-bit cast at hidden 3072 by 11%.  At the other
-// sizes measured the width made under 3% of difference.
+// There, 64-lane tiles measured faster on MI355X (T=8192, caches emptied
+// before each launch, interleaved rounds): the combine (k=8) at hidden
+// 1152-1536 by 7-12%, the combine over 8 ranks by 3-12%, the 8-bit cast at
+// hidden 3072 by 11%.  At the other sizes measured the width made under 3%
+// of difference.
 __host__ __device__ inline bool narrow_tiles(int units)
 {
     return units > kTileLanes && 4 * ((units + 63) / 64 * 64) <= 3 * tiles_per_row(units) * kTileLanes;

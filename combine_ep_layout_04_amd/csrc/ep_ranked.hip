@@ -856,9 +856,13 @@ void combine_ranked_kernel(RankPtrs src, int64_t src_rows, const int32_t* __rest
 }
 
 // Tiled form (rows of more than 64 vectors): workgroup b is tile b % tpr of
-// token b / tpr, one 16-byte column vector per lane, stored once with a
-// streaming store (the expanded combine's tiling; its measurements apply).
-__global__ __launch_bounds__(kTileLanes)
+// token b / tpr, NL vectors, one 16-byte column vector per lane, stored once
+// with a streaming store (the expanded combine's tiling; its measurements
+// apply).  NL is 128, or 64 for rows of 129-192 vectors (narrow_tiles): at
+// 8 ranks x 8192 tokens those took 24.2, 26.6 and 30.7 us at hidden 1152,
+// 1280 and 1536 against 27.4, 28.2 and 31.6 us in 128-lane tiles.
+template <int NL>
+__global__ __launch_bounds__(NL)
 void combine_ranked_tile_kernel(RankPtrs src, int64_t src_rows, const int32_t* __restrict__ s2d,
                                 int nvec, int G, int tpr, uint4* __restrict__ out)
 {
@@ -870,7 +874,7 @@ void combine_ranked_tile_kernel(RankPtrs src, int64_t src_rows, const int32_t* _
     const int lane = tid & 63;
     int32_t p = lane < G ? s2d[t * G + lane] : -1;
     if (p >= src_rows) p = -1;
-    const int v = pt * kTileLanes + tid;    // past the row end: reads 0, stores nothing
+    const int v = pt * NL + tid;            // past the row end: reads 0, stores nothing
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int d0 = 0; d0 < G; d0 += kGroup) {
         uint4 val[kGroup];
@@ -1099,11 +1103,19 @@ hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const 
     const int nvec = hidden / 8;
     const dim3 grid((unsigned)num_tokens);
     uint4* oo = static_cast<uint4*>(out);
-    const int tpr = tiles_per_row(nvec);
+    const bool narrow = narrow_tiles(nvec);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (nvec + lanes - 1) / lanes;
     const int64_t tiles = num_tokens * tpr;
     if (nvec > 64 && tiles <= INT32_MAX) {
-        hipLaunchKernelGGL(combine_ranked_tile_kernel, dim3((unsigned)tiles), dim3(kTileLanes), 0,
-                           stream, src_y, src_rows, s2d, nvec, num_ranks, tpr, oo);
+        if (narrow)
+            hipLaunchKernelGGL(combine_ranked_tile_kernel<kTileLanes / 2>, dim3((unsigned)tiles),
+                               dim3(kTileLanes / 2), 0, stream, src_y, src_rows, s2d, nvec,
+                               num_ranks, tpr, oo);
+        else
+            hipLaunchKernelGGL(combine_ranked_tile_kernel<kTileLanes>, dim3((unsigned)tiles),
+                               dim3(kTileLanes), 0, stream, src_y, src_rows, s2d, nvec, num_ranks,
+                               tpr, oo);
         return hipGetLastError();
     }
     if (nvec <= 64)

@@ -146,7 +146,7 @@ KERNEL_KEYS = {
     # scales (448 vectors: 64 lanes) through the per-token one
     "dispatch_ranked": r"dispatch_ranked_tile_kernel",
     "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64,",
-    "combine_ranked": r"combine_ranked_tile_kernel",
+    "combine_ranked": r"combine_ranked_tile_kernel<128>",
     "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
