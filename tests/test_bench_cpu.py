@@ -52,3 +52,18 @@ def test_stale_counters_are_not_reported(tmp_path, monkeypatch):
     f.write_text(f"kernel={key} fetch_kib=1.0 write_kib=1.0 hbm_bytes_per_launch=123 "
                  f"source_digest={good}\n")
     assert bench.read_traffic(key) == 123
+
+
+def test_more_than_one_gpu_is_refused():
+    # one GPU's share is what bench.py measures: --gpus N > 1, or a launch
+    # with WORLD_SIZE > 1, exits with status 2 and says why, before touching
+    # torch or a device
+    import subprocess
+    import sys
+    for extra, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})):
+        res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *extra],
+                             capture_output=True, text=True, timeout=60,
+                             env={**os.environ, **env}, cwd=ROOT)
+        assert res.returncode == 2
+        assert "more than one GPU" in res.stderr
+        assert res.stdout == ""
