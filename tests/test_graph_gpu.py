@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from combine_ep_layout_04_amd import ep
-from combine_ep_layout_04_amd.inputs import make_random_case, make_routing
+from combine_ep_layout_04_amd.inputs import make_gradient, make_random_case, make_routing
 
 from gpu_util import DEV, dev, host, x_dev
 
@@ -182,3 +182,130 @@ def test_ranked_path_graph():
                 f"replay {rep}: rows of rank {d} differ"
             assert torch.equal(dw[d][rows[d]].view(torch.int32), ref_dw[d].view(torch.int32)), \
                 f"replay {rep}: weights of rank {d} differ"
+
+
+def test_variants_and_backward_graph():
+    # every other entry point in one captured step: aligned and fixed-stride
+    # layouts, the 8-bit cast variants (row- and column-major scales), the
+    # pre-quantized copy, both backward passes, the routing map, the rank
+    # layout, the pre-quantized once-per-rank copy and the fused permute.
+    # All outputs start as the 0x55 sentinel, so rows a call does not write
+    # keep it in the eager run and in every replay alike.
+    T, H, E, k, G = 1024, 2560, 64, 8, 4
+    A, cap = 16, 96
+    print(f"\n[graph] variants and backward T={T} H={H} E={E} k={k} G={G}", flush=True)
+    inp = make_random_case(75, T, H, E, k, mask_frac=0.05, invalid_frac=0.01)
+    idx, x, w = dev(inp.topk_idx), x_dev(inp.x_bits), dev(inp.topk_weights)
+    P = T * k
+    nb = H // 128
+    R_al = ep.layout_max_rows(T, k, E, A, 0)
+    R_cap = ep.layout_max_rows(T, k, E, 1, cap)
+    xq_h, xs_h, _ = oracle.dispatch_quant(inp.x_bits, np.arange(T, dtype=np.int32)[:, None],
+                                          fmt="e4m3", scale="fp32")
+    xq, xs = dev(xq_h), dev(xs_h)
+    rng = np.random.default_rng(76)
+    g_out = x_dev(make_gradient(T, H, 77))
+    g_recv = x_dev(make_gradient(P, H, 78))
+    g_recv_w = dev(rng.standard_normal(P).astype(np.float32))
+    idx_all = [idx] + [dev(make_routing(T, E, k, 950 + r)) for r in range(1, G)]
+    x_all = [x] + [x_dev(make_random_case(960 + r, T, H, E, k).x_bits) for r in range(1, G)]
+    w_all = [w] + [torch.full((T, k), 1.0 / k, dtype=torch.float32, device=DEV) for _ in range(1, G)]
+    El, W8, RG = E // G, (E + 7) // 8, G * T
+    i32 = dict(dtype=torch.int32, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    bf = dict(dtype=torch.bfloat16, device=DEV)
+    o = {
+        # compact layout (feeds the copies and the backward passes)
+        "counts": torch.empty(E, **i32), "offsets": torch.empty(E + 1, **i32),
+        "slot": torch.empty((T, k), **i32), "src": torch.empty(P, **i32),
+        # aligned and fixed-stride layouts
+        "a_counts": torch.empty(E, **i32), "a_offsets": torch.empty(E + 1, **i32),
+        "a_slot": torch.empty((T, k), **i32), "a_src": torch.empty(R_al, **i32),
+        "c_counts": torch.empty(E, **i32), "c_offsets": torch.empty(E + 1, **i32),
+        "c_slot": torch.empty((T, k), **i32), "c_src": torch.empty(R_cap, **i32),
+        "c_dropped": torch.empty(1, **i32), "num_invalid": torch.empty(1, **i32),
+        # 8-bit casts: E5M2 / UE8M0 on the aligned layout, E4M3 column-major
+        "q_al": torch.empty((R_al, H), **u8), "s_al": torch.empty((R_al, nb), **u8),
+        "q_cm": torch.empty((P, H), **u8), "s_cm": torch.empty((nb, P + 4), **f32),
+        "q_pre": torch.empty((P, H), **u8), "s_pre": torch.empty((P, nb), **f32),
+        "rw_pre": torch.empty(P, **f32),
+        # backward
+        "recv": torch.empty((P, H), **bf), "gy": torch.empty((P, H), **bf),
+        "gw": torch.empty((T, k), **f32), "gx": torch.empty((T, H), **bf),
+        "gxw": torch.empty((T, k), **f32),
+        # per-rank: map, layout, pre-quantized sends, fused permute
+        "gmap": torch.empty((RG, W8), **u8),
+        "s2d": torch.empty((T, G), **i32), "lmap": torch.empty((RG, El), **u8),
+        "rsrc": torch.empty(RG, **i32), "rti": torch.empty((RG, k), dtype=torch.int64, device=DEV),
+        "ecnt": torch.empty(El, **i32), "nrecv": torch.empty(1, **i32), "novf": torch.empty(1, **i32),
+        "p_counts": torch.empty(El, **i32), "p_offsets": torch.empty(El + 1, **i32),
+        "p_slot": torch.empty((RG, k), **i32),
+        "perm_x": torch.empty((RG * k, H), **bf), "perm_w": torch.empty(RG * k, **f32),
+    }
+    dq = [torch.empty((RG, H), **u8) for _ in range(G)]
+    ds = [torch.empty((RG, nb), **f32) for _ in range(G)]
+    dw = [torch.empty((RG, k), **f32) for _ in range(G)]
+    for d in range(G):
+        o[f"dq{d}"], o[f"ds{d}"], o[f"dw{d}"] = dq[d], ds[d], dw[d]
+    ws = torch.empty(max(ep.layout_workspace_size(T, k, E), 256), **u8)
+    pws = torch.empty(max(ep.layout_workspace_size(RG, k, El), 256), **u8)
+    rws = torch.empty(max(ep.rank_layout_workspace_size(T, E, G), 256), **u8)
+    lay = ep.RankLayout(sparse_to_dense=o["s2d"], local_map=o["lmap"], recv_src=o["rsrc"],
+                        recv_topk_idx=o["rti"], expert_counts=o["ecnt"], num_recv=o["nrecv"],
+                        num_overflow=o["novf"])
+
+    def step():
+        ep.ep_layout(idx, E, counts=o["counts"], offsets=o["offsets"], slot=o["slot"], src=o["src"],
+                     num_invalid=o["num_invalid"], workspace=ws)
+        ep.ep_layout(idx, E, alignment=A, counts=o["a_counts"], offsets=o["a_offsets"],
+                     slot=o["a_slot"], src=o["a_src"], want_invalid=False, workspace=ws)
+        ep.ep_layout(idx, E, capacity=cap, counts=o["c_counts"], offsets=o["c_offsets"],
+                     slot=o["c_slot"], src=o["c_src"], num_dropped=o["c_dropped"],
+                     want_invalid=False, workspace=ws)
+        ep.ep_dispatch(x, o["a_slot"], None, fp8=True, fmt="e5m2", scale="ue8m0", recv_x=o["q_al"],
+                       recv_scales=o["s_al"], rows=R_al)
+        ep.ep_dispatch(x, o["slot"], None, fp8=True, recv_x=o["q_cm"], recv_scales=o["s_cm"],
+                       scale_ld=P + 4)
+        ep.ep_dispatch_prequantized(xq, xs, o["slot"], w, recv_q=o["q_pre"], recv_scales=o["s_pre"],
+                                    recv_weights=o["rw_pre"])
+        ep.ep_dispatch(x, o["slot"], None, recv_x=o["recv"])
+        ep.ep_combine_backward(g_out, o["recv"], o["slot"], w, grad_y=o["gy"], grad_topk_weights=o["gw"])
+        ep.ep_dispatch_backward(g_recv, g_recv_w, o["slot"], grad_x=o["gx"], grad_topk_weights=o["gxw"])
+        for r in range(G):
+            ep.ep_routing_map(idx_all[r], E, routing_map=o["gmap"][r * T:(r + 1) * T], want_invalid=False)
+        ep.ep_rank_layout(o["gmap"], T, E, G, 0, k, out=lay, workspace=rws)
+        ep.ep_dispatch_ranked_prequantized(xq, xs, o["s2d"], dq, ds, E, topk_idx=idx, topk_weights=w,
+                                           dest_weights=dw)
+        ep.ep_layout(o["rti"], El, counts=o["p_counts"], offsets=o["p_offsets"], slot=o["p_slot"],
+                     want_src=False, want_invalid=False, workspace=pws)
+        ep.ep_dispatch_fused_permute(x_all, o["rsrc"], o["rti"], o["p_slot"], E, 0, rows=RG * k,
+                                     src_topk_idx=idx_all, src_topk_weights=w_all,
+                                     recv_x=o["perm_x"], recv_weights=o["perm_w"])
+
+    for t in o.values():
+        _bits(t).fill_(0x55)
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    # the eager step is right (spot checks against the oracle; the dedicated
+    # tests check each call in full)
+    La = oracle.layout(inp.topk_idx, E, alignment=A)
+    Lc = oracle.layout(inp.topk_idx, E, capacity=cap)
+    np.testing.assert_array_equal(host(o["a_slot"]), La.slot)
+    np.testing.assert_array_equal(host(o["c_slot"]), Lc.slot)
+    assert int(o["c_dropped"].item()) > 0
+    oq, os_, _ = oracle.dispatch_quant(inp.x_bits, La.slot, fmt="e5m2", scale="ue8m0", rows=R_al)
+    placed = La.slot[La.slot >= 0]
+    np.testing.assert_array_equal(host(o["q_al"])[placed], oq[placed])
+    np.testing.assert_array_equal(host(o["s_al"])[placed], os_[placed])
+    ref = {name: t.clone() for name, t in o.items()}
+
+    g = _capture(step)
+    scratch = torch.empty((T, H), **bf)
+
+    def between(rep):
+        ep.ep_combine(ref["recv"], ref["slot"], None, out=scratch)
+        torch.mul(scratch, 3.0, out=scratch)
+
+    _replay_and_check(g, o, ref, between)
