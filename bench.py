@@ -299,6 +299,44 @@ def main():
     com = [e[2].elapsed_time(e[3]) for e in evs]
     us = lambda v: statistics.fmean(v) * 1e3  # noqa: E731
 
+    # ---- the dispatch and the combine charged with the write-back they
+    # leave behind: each launch followed by a 256 MiB read pass, minus that
+    # pass alone (caches emptied before each).  Stores that stayed dirty in
+    # the last-level cache when the kernel ended would be written back
+    # during the pass and make it slower; the row outputs are streaming
+    # stores, so the charged time should not exceed the kernel's own (the
+    # pass may overlap the kernel's last waves).  The pass reads a buffer of
+    # its own, which the 1 GiB flush evicts: a pass over the flush's last
+    # 256 MiB would find them in the last-level cache alone but not after a
+    # kernel whose reads evict them, and charge that difference instead.
+    with torch.cuda.stream(stream):
+        tail = torch.zeros(1 << 26, dtype=torch.float32, device=dev)
+    stream.synchronize()
+
+    def tail_pass():
+        with torch.cuda.stream(stream):
+            tail.sum()
+
+    def charged(fn, reps):
+        evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(-1, reps):
+            flush()
+            if i >= 0:
+                evl[i][0].record(stream)
+            fn()
+            tail_pass()
+            if i >= 0:
+                evl[i][1].record(stream)
+        stream.synchronize()
+        return statistics.median([e[0].elapsed_time(e[1]) for e in evl])
+
+    log("[bench] write-back charged timings")
+    pass_alone = charged(lambda: None, args.steps)
+    dis_charged = charged(lambda: check(L.ep_dispatch(p["x"], T, H, k, p["slot"], None, 0, p["recv"],
+                                                      None, None, s), "ep_dispatch"), args.steps)
+    com_charged = charged(lambda: check(L.ep_combine(p["recv"], p["slot"], p["wt"], T, H, k, p["out"],
+                                                     s), "ep_combine"), args.steps)
+
     # correctness spot check of what was timed: identity experts give x back
     # (compared as values: a -0.0 in x comes back as +0.0)
     ok = bool(torch.equal(out.float(), x.float()))
@@ -597,8 +635,10 @@ def main():
 
     per_kernel = {
         "layout": entry(lay),
-        "dispatch_bf16": entry(dis, bytes=bm["dispatch_bf16"]),
-        "combine": entry(com, bytes=bm["combine"]),
+        "dispatch_bf16": entry(dis, bytes=bm["dispatch_bf16"],
+                               write_back_charged_median_us=round((dis_charged - pass_alone) * 1e3, 2)),
+        "combine": entry(com, bytes=bm["combine"],
+                         write_back_charged_median_us=round((com_charged - pass_alone) * 1e3, 2)),
         "dispatch_fp8": entry(f8, bytes=bmf["dispatch_fp8"],
                               workload="fp8: headline shape, 1% of rows x100"),
         "combine_backward": entry(cb_us, bytes=bm["combine_backward"]),
