@@ -13,12 +13,28 @@
 //                                                   product
 //   grad_w[t,j]       = sum_c g[t,c] * y[slot[t,j], c]   fp32 accumulation
 //
-// Design (HBM-bound): one 128-lane workgroup per token reads g[t] once into
-// registers (VPT 16-byte vectors per lane).  For each slot it streams the
-// expert row y[slot] (when grad_w is wanted), accumulates the per-lane dot
-// product with fp32 FMAs and writes the scaled gradient row with
-// non-temporal 16-byte stores; the per-slot partial dots are reduced across
-// the workgroup at the end (8 slots at a time).  The bf16 rounding of
+// Design (HBM-bound).  Rows that the bf16 dispatch tiles (tile_dispatch) go
+// through two launches:
+//   1. grad_y, tiled exactly like the bf16 dispatch: a 128-lane workgroup
+//      per (token, 2 KiB tile, group of 4 slots), XCD-aware, loads its
+//      vector of g[t] and stores bf16(w * g) to each slot's row;
+//   2. grad_w (when wanted): one workgroup per token reads g[t] and streams
+//      each y[slot] with fp32 dot products, storing nothing else.
+// Each is one pattern HBM runs well: a write stream with few reads, and a
+// read stream.  One fused pass moves fewer bytes (g is read once) but mixes
+// reads and writes half and half; at T=8192, hidden 7168, k=8 it took
+// 406.5 us against 359.1 us for the two launches (grad_y alone 221.0
+// against 204.4 us), and at hidden 2048-4096 the split was 3-8% faster.
+// Shorter rows keep the fused pass (hidden 1536: 97.2 fused against
+// 106.5 us split).  Both forms give the same bits: the dot products are
+// accumulated in the same order.
+//
+// The fused pass and the grad_w pass: one 128-lane workgroup per token
+// reads g[t] once into registers (VPT 16-byte vectors per lane).  For each
+// slot it streams the expert row y[slot] (when grad_w is wanted),
+// accumulates the per-lane dot product with fp32 FMAs and (fused) writes the
+// scaled gradient row with streaming 16-byte stores; the per-slot partial
+// dots are reduced across the workgroup at the end (8 slots at a time).  The bf16 rounding of
 // w * g uses the exact product error e = fma(w, g, -p) of p = fl32(w * g):
 // p is on the same side of every bf16 rounding boundary as the exact product
 // unless p is itself a boundary (a bf16 midpoint), where the sign of e
@@ -91,8 +107,8 @@ __device__ __forceinline__ void keep(uint4& v)
 constexpr int kGroup = 8;   // slots whose partial dots are carried together
 
 // A pass covers NT*VPT vectors of the row; lanes past the row end hold
-// zeros and store nothing.
-template <int NT, int VPT>
+// zeros and store nothing.  STORE: also write grad_y (the fused pass).
+template <int NT, int VPT, bool STORE>
 __global__ __launch_bounds__(NT)
 void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restrict__ y,
                              const int32_t* __restrict__ slot, const float* __restrict__ w,
@@ -140,10 +156,12 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
 #pragma unroll
                     for (int u = 0; u < VPT; ++u) acc[q] = dot8(gv[u], yv[u], acc[q]);
                 }
+                if (STORE) {
 #pragma unroll
-                for (int u = 0; u < VPT; ++u) {
-                    const int v = p0 + tid + u * NT;
-                    if (v < nvec) store_row16(dst, v * 16, scale_row8(wj, gv[u]));
+                    for (int u = 0; u < VPT; ++u) {
+                        const int v = p0 + tid + u * NT;
+                        if (v < nvec) store_row16(dst, v * 16, scale_row8(wj, gv[u]));
+                    }
                 }
             }
         }
@@ -171,6 +189,47 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
     }
 }
 
+// grad_y alone, tiled like the bf16 dispatch: workgroup b maps (XCD-aware)
+// to tile `tile` = (token t, tile p of its row) and slot group gi (slots
+// 4gi .. 4gi+3); one 16-byte vector per lane, past the row end nothing.
+constexpr int kGradYSlots = 4;
+
+__global__ __launch_bounds__(kTileLanes)
+void combine_backward_grad_y_tile_kernel(const uint4* __restrict__ g, int nvec, int k, int tpr,
+                                         int64_t num_tiles, int groups,
+                                         const int32_t* __restrict__ slot,
+                                         const float* __restrict__ w, uint4* __restrict__ grad_y)
+{
+    int64_t tile;
+    int gi;
+    if (!xcd_tile(blockIdx.x, groups, num_tiles, tile, gi)) return;
+    const int64_t t = tile / tpr;
+    const int p = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int j0 = gi * kGradYSlots;
+    // lanes 0..3 of each wavefront hold the group's slots and weights; read
+    // back with readlane before any lane diverges
+    const bool mine = lane < kGradYSlots && j0 + lane < k;
+    const int32_t sl = mine ? slot[t * k + j0 + lane] : -1;
+    const float wl = mine ? (w ? w[t * k + j0 + lane] : 1.0f) : 0.0f;
+    int32_t r[kGradYSlots];
+    float wq[kGradYSlots];
+#pragma unroll
+    for (int q = 0; q < kGradYSlots; ++q) {
+        r[q] = __builtin_amdgcn_readlane(sl, q);
+        wq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), q));
+    }
+    const int v = p * kTileLanes + tid;
+    uint4 d = load_row16<0>(buffer_rsrc(g + t * nvec, nvec * 16), v * 16);
+    keep(d);
+#pragma unroll
+    for (int q = 0; q < kGradYSlots; ++q)
+        if (r[q] >= 0 && v < nvec)
+            store_row16(buffer_rsrc(grad_y + (int64_t)r[q] * nvec, nvec * 16), v * 16,
+                        scale_row8(wq[q], d));
+}
+
 }  // namespace
 
 hipError_t launch_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
@@ -184,11 +243,23 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, const in
     const uint4* gg = static_cast<const uint4*>(grad_out);
     const uint4* yy = static_cast<const uint4*>(y);
     uint4* gy = static_cast<uint4*>(grad_y);
+    // rows the bf16 dispatch tiles: grad_y in tiles, then grad_w alone
+    const int tpr = tiles_per_row(nvec);
+    const int groups = (num_topk + kGradYSlots - 1) / kGradYSlots;
+    const int64_t num_tiles = num_tokens * tpr;
+    const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
+    const bool split = tile_dispatch(nvec, num_tokens * num_topk) && blocks <= INT32_MAX;
+    if (split) {
+        hipLaunchKernelGGL(combine_backward_grad_y_tile_kernel, dim3((unsigned)blocks),
+                           dim3(kTileLanes), 0, stream, gg, nvec, num_topk, tpr, num_tiles, groups,
+                           slot, topk_weights, gy);
+        if (grad_topk_weights == nullptr) return hipGetLastError();
+    }
     // 64 lanes for short rows; else 128 lanes with the largest VPT <= 8
     // whose pass divides the row (896 = 128*7 at hidden 7168)
     if (nvec <= 64) {
-        hipLaunchKernelGGL((combine_backward_kernel<64, 1>), grid, dim3(64), 0, stream, gg, yy,
-                           slot, topk_weights, nvec, num_topk, gy, grad_topk_weights);
+        hipLaunchKernelGGL((combine_backward_kernel<64, 1, true>), grid, dim3(64), 0, stream, gg,
+                           yy, slot, topk_weights, nvec, num_topk, gy, grad_topk_weights);
         return hipGetLastError();
     }
     const int fit = nvec / 128;
@@ -200,8 +271,12 @@ hipError_t launch_combine_backward(const void* grad_out, const void* y, const in
         }
     }
 #define EP_CB(V)                                                                             \
-    hipLaunchKernelGGL((combine_backward_kernel<128, V>), grid, dim3(128), 0, stream, gg, yy, \
-                       slot, topk_weights, nvec, num_topk, gy, grad_topk_weights)
+    if (split)                                                                               \
+        hipLaunchKernelGGL((combine_backward_kernel<128, V, false>), grid, dim3(128), 0, stream, \
+                           gg, yy, slot, topk_weights, nvec, num_topk, gy, grad_topk_weights); \
+    else                                                                                     \
+        hipLaunchKernelGGL((combine_backward_kernel<128, V, true>), grid, dim3(128), 0, stream, \
+                           gg, yy, slot, topk_weights, nvec, num_topk, gy, grad_topk_weights)
     switch (vpt) {
     case 1: EP_CB(1); break;
     case 2: EP_CB(2); break;

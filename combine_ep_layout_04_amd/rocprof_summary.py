@@ -126,7 +126,9 @@ def _counter_medians(d: str):
 # E4M3 / fp32 instance also runs once over the tokens themselves (T rows,
 # one slot each) to make the pre-quantized input.  The combine line also
 # counts the dispatch-backward launches, which run the same kernel over the
-# same bytes plus a [T, k] gather.
+# same bytes plus a [T, k] gather.  A tuple names the launches of one
+# operation (the combine backward's grad_y tiles and its grad_w pass), whose
+# bytes are summed.
 KERNEL_KEYS = {
     "dispatch_bf16": r"dispatch_bf16_tile_kernel",
     "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 128>",
@@ -136,7 +138,8 @@ KERNEL_KEYS = {
     "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 128>",
     "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
     "combine": r"[^_]combine_tile_kernel<",
-    "combine_backward": r"combine_backward_kernel<",
+    "combine_backward": (r"combine_backward_grad_y_tile_kernel",
+                         r"combine_backward_kernel<128, 7, false>"),
     "layout_count": r"layout_count_kernel\(",
     "layout_scatter": r"layout_scatter_kernel\(",
     "routing_map": r"routing_map_kernel\(",
@@ -172,7 +175,9 @@ def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
              "# file and of the internal and device headers, and the hipcc flags",
              f"copy_scale fetch={f_scale:.4f} write={w_scale:.4f}"]
     for key, needle in KERNEL_KEYS.items():
-        fk, wk = pick(fetch, needle), pick(write, needle)
+        needles = needle if isinstance(needle, tuple) else (needle,)
+        fk = sum(pick(fetch, n) for n in needles)
+        wk = sum(pick(write, n) for n in needles)
         b = (fk * f_scale + wk * w_scale) * 1024.0
         lines.append(f"kernel={key} fetch_kib={fk:.1f} write_kib={wk:.1f} "
                      f"hbm_bytes_per_launch={b:.0f} source_digest={digest(key)}")

@@ -83,6 +83,10 @@ def test_combine_backward_workloads(name):
     (300, 200, 16, 9, 1),      # k = 9: two slot groups; 25-vector rows (tail)
     (257, 1032, 33, 5, 16),    # one pass + tail; aligned layout
     (64, 2048, 64, 64, 1),     # k = EP_MAX_TOPK: eight slot groups
+    # rows the bf16 dispatch tiles: grad_y in tiles of 4 slots, then grad_w
+    (300, 4096, 40, 11, 1),    # three slot groups, the last partial; ragged T
+    (129, 4104, 24, 6, 4),     # 513 vectors: a one-vector last tile; aligned layout
+    (40, 7168, 64, 64, 1),     # k = EP_MAX_TOPK: sixteen slot groups of tiles
 ])
 def test_combine_backward_shapes(T, H, E, k, A):
     inp = make_random_case(T + k, T, H, E, k, mask_frac=0.15, dup_frac=1.0, invalid_frac=0.05)
@@ -95,10 +99,11 @@ def test_combine_backward_shapes(T, H, E, k, A):
     check_combine_backward(g, y, L, None, rows)          # unit weights
 
 
-def test_combine_backward_without_weight_grad():
-    inp = make_random_case(5, 100, 256, 8, 4, mask_frac=0.1)
+@pytest.mark.parametrize("H", [256, 4104])   # one fused pass; grad_y tiles alone
+def test_combine_backward_without_weight_grad(H):
+    inp = make_random_case(5, 100, H, 8, 4, mask_frac=0.1)
     L = oracle.layout(inp.topk_idx, 8)
-    g = make_gradient(100, 256, 9)
+    g = make_gradient(100, H, 9)
     gy, gw = ep.ep_combine_backward(x_dev(g), None, dev(L.slot), dev(inp.topk_weights))
     torch.cuda.synchronize()
     assert gw is None

@@ -77,8 +77,12 @@ def test_forward_step_graph():
         "q": torch.empty((P, H), dtype=torch.uint8, device=DEV),
         "scales": torch.empty((P, H // 128), dtype=torch.float32, device=DEV),
         "out": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+        # the combine's backward at this row length: grad_y tiles, then grad_w
+        "gy": torch.empty((P, H), dtype=torch.bfloat16, device=DEV),
+        "gw": torch.empty((T, k), dtype=torch.float32, device=DEV),
     }
     ws = torch.empty(max(ep.layout_workspace_size(T, k, E), 256), dtype=torch.uint8, device=DEV)
+    g_out = x_dev(make_gradient(T, H, 72))
 
     def step():
         ep.ep_layout(idx, E, counts=o["counts"], offsets=o["offsets"], slot=o["slot"], src=o["src"],
@@ -86,6 +90,7 @@ def test_forward_step_graph():
         ep.ep_dispatch(x, o["slot"], w, recv_x=o["recv"], recv_weights=o["recv_w"])
         ep.ep_dispatch(x, o["slot"], None, fp8=True, recv_x=o["q"], recv_scales=o["scales"])
         ep.ep_combine(o["recv"], o["slot"], w, out=o["out"])
+        ep.ep_combine_backward(g_out, o["recv"], o["slot"], w, grad_y=o["gy"], grad_topk_weights=o["gw"])
 
     step()
     torch.cuda.synchronize()
@@ -104,7 +109,7 @@ def test_forward_step_graph():
         # eager work of the same library and of torch between replays
         ep.ep_combine(ref["recv"], ref["slot"], None, out=scratch)
         torch.mul(scratch, 2.0, out=scratch)
-        for name in ("recv", "q", "scales", "recv_w", "src"):
+        for name in ("recv", "q", "scales", "recv_w", "src", "gy"):
             if unplaced.numel():
                 _bits(o[name])[unplaced] = _bits(ref[name])[unplaced]
 
