@@ -15,9 +15,11 @@ Also reported: per-kernel mean / median / p10 / p90 from HIP events recorded
 on the launch stream, the fp8 dispatch and its variants (same shape, 1%
 x100 outlier rows), the backward passes, the layout variants, the
 per-(token, rank) path at 8 ranks, a plain device-to-device copy for
-context, the roofline of the dominant kernel, and the CPU oracle timed on
-the host on the same workload.  ``--warm`` adds the same steps back to back
-without flushes, for context.
+context, the roofline of the dominant kernel, the headline dispatch and
+combine with the write-back they leave charged to them (a read pass after
+each launch, minus the pass alone), and the CPU oracle timed on the host on
+the same workload.  ``--warm`` adds the same steps back to back without
+flushes, for context.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm]
 """
