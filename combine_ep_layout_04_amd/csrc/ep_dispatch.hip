@@ -26,11 +26,11 @@
 //     16-byte store out), so 8 aligned lanes hold one 128-channel block and
 //     amax is an 8-lane shuffle reduction.  With row-major scales and rows
 //     of more than 64 units, one 128-lane workgroup per (token, tile of 128
-//     units, group of up to 8 slots), all of a token's workgroups back to
-//     back on one XCD (its scale rows are written in pieces by several
-//     tiles, and those pieces then meet in one L2); otherwise one 64-lane
-//     wavefront per token.  The
-//     scale is a correctly rounded fp32 division.  Each quotient x / scale
+//     units, group of up to 8 slots) -- 64-lane tiles for rows of 129-192
+//     units -- with all of a token's workgroups back to back on one XCD
+//     (its scale rows are written in pieces by several tiles, and those
+//     pieces then meet in one L2); otherwise one 64-lane wavefront per
+//     token.  The scale is a correctly rounded fp32 division.  Each quotient x / scale
 //     must be the correctly rounded fp32 quotient too; instead of a full
 //     division per element it uses Markstein's correction (P. Markstein,
 //     "Computation of elementary functions on the IBM RISC System/6000

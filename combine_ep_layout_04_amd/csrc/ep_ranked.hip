@@ -47,12 +47,13 @@
 //                 in: one workgroup per received token reads the sender's
 //                 row once and stores it to each of the rank's local-expert
 //                 rows, with the weights.
-//   combine:      one workgroup per (token, 2 KiB tile) gathers its
-//                 vectors from the G buffers through buffer resources (an
-//                 unrouted rank gets a 0-byte resource: its loads return 0
-//                 without a branch), sums them in fp32 in increasing rank
-//                 and stores once, with a streaming store (rows of at most
-//                 64 vectors: one workgroup per token).
+//   combine:      one workgroup per (token, 2 KiB tile; 1 KiB for rows of
+//                 129-192 vectors) gathers its vectors from the G buffers
+//                 through buffer resources (an unrouted rank gets a 0-byte
+//                 resource: its loads return 0 without a branch), sums them
+//                 in fp32 in increasing rank and stores once, with a
+//                 streaming store (rows of at most 64 vectors: one
+//                 workgroup per token).
 
 #include "ep_device.h"
 #include "ep_internal.h"
