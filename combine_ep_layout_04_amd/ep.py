@@ -694,3 +694,38 @@ def ep_combine_ranked(src_y, sparse_to_dense: torch.Tensor, *, out=None, stream=
                                  _stream(stream))
     _check(st, "ep_combine_ranked")
     return out
+
+
+# ------------------------------------------------------ C-ABI names, 1:1 --
+# Every function include/ep.h declares is reachable here under its own name.
+# The helpers above keep short names and ep_layout / ep_dispatch take the
+# _ex arguments as keywords; these are the same calls under the header's
+# names.
+
+ep_version = version
+ep_status_string = status_string
+ep_last_error = last_error
+ep_layout_workspace_size = layout_workspace_size
+ep_layout_max_rows = layout_max_rows
+ep_rank_layout_workspace_size = rank_layout_workspace_size
+
+
+def ep_layout_ex(topk_idx: torch.Tensor, num_experts: int, alignment: int, capacity: int, **kw):
+    """ep_layout with segment starts aligned to ``alignment`` rows, or a fixed
+    ``capacity`` rows per expert (overflow dropped, counted in num_dropped)."""
+    return ep_layout(topk_idx, num_experts, alignment=alignment, capacity=capacity, **kw)
+
+
+def ep_dispatch_ex(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torch.Tensor] = None,
+                   *, out_dtype: str = "e4m3", scale: str = "fp32", scale_ld: int = 0, **kw):
+    """ep_dispatch with the output type named: ``out_dtype`` "bf16" (a copy),
+    "e4m3" or "e5m2" (a cast with ``scale`` "fp32", "pow2" or "ue8m0" block
+    scales, row-major or, with ``scale_ld`` > 0, column-major)."""
+    if out_dtype == "bf16":
+        if scale_ld:
+            raise ValueError("bf16 output takes no scale_ld")
+        return ep_dispatch(x, slot, topk_weights, **kw)
+    if out_dtype not in _FORMATS:
+        raise ValueError(f"unknown out_dtype {out_dtype!r}")
+    return ep_dispatch(x, slot, topk_weights, fp8=True, fmt=out_dtype, scale=scale,
+                       scale_ld=scale_ld, **kw)

@@ -45,6 +45,15 @@ def test_header_is_plain_c(tmp_path, compiler, flags):
     assert r.returncode == 0, r.stderr
 
 
+def test_binding_has_every_declared_name():
+    # the Python binding offers each entry point under the header's name
+    for name in declared_functions():
+        assert callable(getattr(ep, name, None)), name
+    assert ep.ep_layout_workspace_size(4096, 8, 64) == ep.layout_workspace_size(4096, 8, 64)
+    assert ep.ep_layout_max_rows(100, 4, 8, 16, 0) == ep.layout_max_rows(100, 4, 8, 16, 0)
+    assert ep.ep_status_string(1) == "EP_INVALID_ARGUMENT"
+
+
 def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(ep.LIB_PATH)
     for name in declared_functions():

@@ -190,3 +190,25 @@ def test_variants_at_max_hidden(fmt, mode):
     print(f"\n[fp8 variants] hidden 65536 {fmt} {mode}", flush=True)
     L = oracle.layout(inp.topk_idx, 4)
     check(inp.x_bits, L, fmt, mode)
+
+
+def test_header_named_calls_match():
+    # ep_layout_ex / ep_dispatch_ex under the header's names give the same
+    # bytes as the keyword forms of ep_layout / ep_dispatch
+    inp = make_random_case(58, 300, 1024, 16, 6, mask_frac=0.1)
+    idx, x = dev(inp.topk_idx), x_dev(inp.x_bits)
+    a = ep.ep_layout_ex(idx, 16, 16, 0)
+    b = ep.ep_layout(idx, 16, alignment=16)
+    for u, v in zip(a, b):
+        if u is not None:
+            assert torch.equal(u, v)
+    rows = ep.ep_layout_max_rows(300, 6, 16, 16, 0)
+    q1, s1, _ = ep.ep_dispatch_ex(x, a[2], out_dtype="e5m2", scale="ue8m0", rows=rows)
+    q2, s2, _ = ep.ep_dispatch(x, a[2], None, fp8=True, fmt="e5m2", scale="ue8m0", rows=rows)
+    r1, _, _ = ep.ep_dispatch_ex(x, a[2], out_dtype="bf16", rows=rows)
+    r2, _, _ = ep.ep_dispatch(x, a[2], rows=rows)
+    torch.cuda.synchronize()
+    placed = torch.from_numpy(oracle.layout(inp.topk_idx, 16, alignment=16).slot).to(DEV)
+    placed = placed[placed >= 0].long()
+    assert torch.equal(q1[placed], q2[placed]) and torch.equal(s1[placed], s2[placed])
+    assert torch.equal(r1[placed].view(torch.int16), r2[placed].view(torch.int16))
