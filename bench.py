@@ -141,13 +141,16 @@ def read_traffic(kernel_key: str):
     return None
 
 
+CPU_RUNS = 7   # about 13 s of oracle work at the headline workload
+
+
 def cpu_baseline(inp, inp_fp8, E, nbytes):
     """The oracle as it stands (single-threaded C) on the full workload, and
-    each of its operations timed alone (median of 3)."""
+    each of its operations timed alone (median of CPU_RUNS)."""
     import oracle
 
     times, ops = [], {"layout": [], "dispatch_bf16": [], "combine": [], "dispatch_fp8": []}
-    for _ in range(3):
+    for _ in range(CPU_RUNS):
         t0 = time.perf_counter()
         L = oracle.layout(inp.topk_idx, E)
         t1 = time.perf_counter()
@@ -167,8 +170,9 @@ def cpu_baseline(inp, inp_fp8, E, nbytes):
     t = statistics.median(times)
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "full headline workload (T=8192, H=7168, E=256, k=8): oracle layout + "
-                      "bf16 dispatch + fp64 combine, single thread, median of 3 runs "
-                      f"({t:.2f} s each)", "seconds_per_step": round(t, 3),
+                      f"bf16 dispatch + fp64 combine, single thread, median of {CPU_RUNS} runs "
+                      f"({t:.2f} s each; the fp8 dispatch timed alone in each run too)",
+            "seconds_per_step": round(t, 3),
             "seconds_per_op": {k: round(statistics.median(v), 4) for k, v in ops.items()},
             "host_cores_available": len(os.sched_getaffinity(0))}
 
