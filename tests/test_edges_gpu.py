@@ -223,6 +223,37 @@ def test_zero_tokens():
     assert recv.shape == (0, 256) and out.shape == (0, 256)
 
 
+def test_zero_tokens_every_entry_point():
+    # T = 0 through the layout variants, the 8-bit casts, the pre-quantized
+    # copy and both backward passes: no rows, and the layouts' count and
+    # offset arrays as the oracle gives them for an empty batch
+    idx0 = np.empty((0, 4), dtype=np.int64)
+    for A, cap in ((1, 0), (16, 0), (1, 8)):
+        nd = torch.full((1,), -5, dtype=torch.int32, device=DEV)
+        counts, offsets, slot, src, inval = ep.ep_layout(dev(idx0), 16, alignment=A, capacity=cap,
+                                                         num_dropped=nd if cap else None)
+        torch.cuda.synchronize()
+        L = oracle.layout(idx0, 16, alignment=A, capacity=cap)
+        np.testing.assert_array_equal(host(counts), L.counts)
+        np.testing.assert_array_equal(host(offsets), L.offsets)
+        assert int(host(inval)[0]) == 0
+        if cap:
+            assert int(host(nd)[0]) == 0
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    slot = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    for fmt, mode in (("e4m3", "fp32"), ("e5m2", "ue8m0")):
+        q, s, _ = ep.ep_dispatch(x, slot, None, fp8=True, fmt=fmt, scale=mode)
+        assert q.shape == (0, 256) and s.shape[0] == 0
+    q, s, _ = ep.ep_dispatch_prequantized(torch.empty((0, 256), dtype=torch.uint8, device=DEV),
+                                          torch.empty((0, 2), dtype=torch.float32, device=DEV), slot)
+    gy, gw = ep.ep_combine_backward(x, torch.empty((0, 256), dtype=torch.bfloat16, device=DEV), slot, None)
+    gx, gxw = ep.ep_dispatch_backward(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV),
+                                      torch.empty(0, dtype=torch.float32, device=DEV), slot)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 256) and gy.shape == (0, 256) and gw.shape == (0, 4)
+    assert gx.shape == (0, 256) and gxw.shape == (0, 4)
+
+
 def test_deterministic_and_side_stream():
     inp = make_random_case(12, 3000, 1024, 64, 8, mask_frac=0.05)
     s = torch.cuda.Stream()
