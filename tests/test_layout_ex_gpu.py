@@ -29,6 +29,10 @@ CASES = [
     ("skewed", None, 128, 0),
     ("skewed", 2048, 32, 96),
     ("fp8", 1024, 16, 64),
+    # EP_MAX_ALIGNMENT: every segment start on a multiple of 4096 rows, and
+    # a 4096-row capacity (one aligned block per expert)
+    ("tiny", None, 4096, 0),
+    ("tiny", None, 4096, 4096),
 ]
 
 
