@@ -169,7 +169,12 @@ def make_random_case(seed: int, T: int, H: int, E: int, k: int,
     idx[m] = -1
     bad = rng.random((T, k)) < invalid_frac
     if bad.any():
-        choices = np.array([E, E + 3, -2, -7, 1 << 40, -(1 << 40)], dtype=np.int64)
+        # out of range, including values whose low 32 bits read as a valid
+        # expert (1 << 40, 2^32 + 5, INT64_MIN) or as the mask (-1:
+        # 2^32 - 1, INT64_MAX) if an index were narrowed before the check
+        i64 = np.iinfo(np.int64)
+        choices = np.array([E, E + 3, -2, -7, 1 << 40, -(1 << 40), (1 << 32) - 1, (1 << 32) + 5,
+                            i64.max, i64.min], dtype=np.int64)
         idx[bad] = choices[rng.integers(0, len(choices), size=int(bad.sum()))]
     wts = _weights(rng, np.where((idx >= 0) & (idx < E), idx, -1))
     wl = Workload("random", T=T, H=H, E=E, k=k, seed=seed)
