@@ -26,7 +26,7 @@
 //     16-byte store out), so 8 aligned lanes hold one 128-channel block and
 //     amax is an 8-lane shuffle reduction.  With row-major scales and rows
 //     of more than 64 units, one 128-lane workgroup per (token, tile of 128
-//     units, group of up to 8 slots) -- 64-lane tiles for rows of 129-192
+//     units, group of up to 4 slots) -- 64-lane tiles for rows of 129-192
 //     units -- with all of a token's workgroups back to back on one XCD
 //     (its scale rows are written in pieces by several tiles, and those
 //     pieces then meet in one L2); otherwise one 64-lane wavefront per
@@ -439,7 +439,15 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 // (narrow_tiles; hidden 2176-3072): hidden 3072 took 52.7 us in 64-lane
 // tiles against 59.1 us in 128-lane ones.  Elsewhere widths of 64 to 512
 // lanes measured within 3% of 128 (hidden 4096-16384, T=8192, k=8).
-constexpr int kCastSlots = 8;
+//
+// Slot groups of 4: each tile is cast once per group, and each workgroup
+// stores 4 code pieces instead of 8.  Against groups of 8 (ten interleaved
+// rounds, T=8192, k=8, fp32 scales) that was 0.8% faster at hidden 4096,
+// 1.7% at 7168 (121.6 against 123.7 us), 2.6% at 8192 and 5.1% at 16384;
+// with power-of-two and UE8M0 scales the two were within 0.2% at 7168.
+// Groups of 2 were 33% slower, and putting a tile's groups together on one
+// XCD, or plain order, instead of a token's tiles, 3-5% slower.
+constexpr int kCastSlots = 4;
 
 template <int FMT, int SM, int NL>
 __global__ __launch_bounds__(NL)
