@@ -27,10 +27,10 @@
 // the combine then reads 188 us in its own events but 202 us once a
 // following read pass is charged for the write-back; the tiled kernel with
 // streaming stores takes 185 us either way.  Tiles are 128 lanes, or 64
-// for rows of 129-192 vectors (hidden 1032-1536), where 128-lane tiles
-// leave a quarter or more of their lanes idle: hidden 1152, 1280 and 1536
-// took 33.3, 36.2 and 42.1 us in 64-lane tiles against 37.7, 40.4 and
-// 45.3 us (T=8192, k=8).  Rows of at most 64 vectors, and grids past 2^31
+// where the last 128-lane tile would be at most half full (narrow_tiles:
+// hidden 1032-1536, 2560, 3584, ...): hidden 1152, 1280, 1536 and 3584
+// took 33.3, 36.2, 42.1 and 93.3 us in 64-lane tiles against 37.7, 40.4,
+// 45.3 and 96.7 us (T=8192, k=8).  Rows of at most 64 vectors, and grids past 2^31
 // workgroups, keep one workgroup per token.
 
 #include "ep_device.h"

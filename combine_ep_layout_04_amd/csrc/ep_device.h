@@ -48,16 +48,19 @@ constexpr int kTileLanes = 128;
 
 __host__ __device__ inline int tiles_per_row(int nvec) { return (nvec + kTileLanes - 1) / kTileLanes; }
 
-// Rows of 129-192 units fill 128-lane tiles only three quarters or less (a
-// 192-unit row takes 256 lanes); in 64-lane tiles they take at most 192.
-// There, 64-lane tiles measured faster on MI355X (T=8192, caches emptied
-// before each launch, interleaved rounds): the combine (k=8) at hidden
-// 1152-1536 by 7-12%, the combine over 8 ranks by 3-12%, the 8-bit cast at
-// hidden 3072 by 11%.  At the other sizes measured the width made under 3%
-// of difference.
+// Rows whose last 128-lane tile would be at most half full (units mod 128 in
+// 1..64, for rows of more than 128 units) take 64-lane tiles: 64 fewer
+// lanes per row launched.  Measured on MI355X (T=8192, caches emptied
+// before each launch, interleaved A/B rounds on one machine), 64-lane tiles
+// were faster on every such row tried: the combine (k=8) by 7-12% at hidden
+// 1152-1536 and 3.5% at 3584, the combine over 8 ranks by 3-12% at
+// 1152-1536 and 3.4% at 3584, the 8-bit cast by 11% at 3072 and 1-2% at
+// 7168; within 1% at hidden 2560, 5120 and 5632.  On rows of whole 128-lane
+// tiles 64-lane ones were up to 2% slower.
 __host__ __device__ inline bool narrow_tiles(int units)
 {
-    return units > kTileLanes && 4 * ((units + 63) / 64 * 64) <= 3 * tiles_per_row(units) * kTileLanes;
+    const int tail = units % kTileLanes;
+    return units > kTileLanes && tail != 0 && tail <= kTileLanes / 2;
 }
 
 // When a dispatch (one row to several destinations) is tiled.  Measured

@@ -26,8 +26,9 @@
 //     16-byte store out), so 8 aligned lanes hold one 128-channel block and
 //     amax is an 8-lane shuffle reduction.  With row-major scales and rows
 //     of more than 64 units, one 128-lane workgroup per (token, tile of 128
-//     units, group of up to 4 slots) -- 64-lane tiles for rows of 129-192
-//     units -- with all of a token's workgroups back to back on one XCD
+//     units, group of up to 4 slots; 8 on rows of at most 256 units), or
+//     64-lane tiles where the last 128-lane tile would be at most half
+//     full, with all of a token's workgroups back to back on one XCD
 //     (its scale rows are written in pieces by several tiles, and those
 //     pieces then meet in one L2); otherwise one 64-lane wavefront per
 //     token.  The scale is a correctly rounded fp32 division.  Each quotient x / scale
@@ -426,7 +427,7 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 
 // Tiled cast (rows of more than 64 units, row-major scales): workgroup b
 // is (token t, tile p of NL units = NL/8 scale blocks, slot group g of up to
-// kCastSlots slots), and all of a token's workgroups run back to back on one
+// CS slots), and all of a token's workgroups run back to back on one
 // XCD, so the pieces of a token's scale rows that different tiles write
 // meet in that XCD's L2.  Each lane casts one unit; lanes 0..7 of each
 // wavefront then hold that wavefront's 8 block scales and store them per
@@ -435,21 +436,27 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 // 127 us.  Column-major scales (each a separate 4-byte store) measured
 // slower tiled, 163 us against 140 us, and keep one wavefront per token.
 //
-// Tiles are 128 lanes (NL = kTileLanes), or 64 for rows of 129-192 units
-// (narrow_tiles; hidden 2176-3072): hidden 3072 took 52.7 us in 64-lane
-// tiles against 59.1 us in 128-lane ones.  Elsewhere widths of 64 to 512
-// lanes measured within 3% of 128 (hidden 4096-16384, T=8192, k=8).
+// Tiles are 128 lanes (NL = kTileLanes), or 64 where the last 128-lane tile
+// would be at most half full (narrow_tiles: hidden 2176-3072, 5120, 7168,
+// ...): hidden 3072 took 52.7 us in 64-lane tiles against 59.1 us in
+// 128-lane ones, hidden 7168 1-2% less.  On rows of whole 128-lane tiles
+// widths of 64 to 512 lanes measured within 3% of 128 (hidden 4096-16384,
+// T=8192, k=8).
 //
-// Slot groups of 4: each tile is cast once per group, and each workgroup
-// stores 4 code pieces instead of 8.  Against groups of 8 (ten interleaved
-// rounds, T=8192, k=8, fp32 scales) that was 0.8% faster at hidden 4096,
-// 1.7% at 7168 (121.6 against 123.7 us), 2.6% at 8192 and 5.1% at 16384;
-// with power-of-two and UE8M0 scales the two were within 0.2% at 7168.
-// Groups of 2 were 33% slower, and putting a tile's groups together on one
-// XCD, or plain order, instead of a token's tiles, 3-5% slower.
-constexpr int kCastSlots = 4;
+// Slot groups (CS slots per workgroup): 4 on rows of more than 256 units,
+// 8 on shorter ones.  With groups of 4 each tile is cast once per group,
+// and each workgroup stores 4 code pieces instead of 8.  Against groups of
+// 8 (interleaved A/B rounds, T=8192, k=8, fp32 scales) groups of 4 ran
+// 1.7-2.3% faster at hidden 7168, 2.6% at 8192 and 5.1% at 16384, within
+// 1% at 4096, and 1-8% slower at hidden 1536-3072; with power-of-two and
+// UE8M0 scales the two were within 0.2% at 7168.  Groups of 2 were 33%
+// slower, and putting a tile's groups together on one XCD, or plain order,
+// instead of a token's tiles, 3-5% slower.
+constexpr int kCastSlotsLong = 4;
+constexpr int kCastSlotsShort = 8;
+constexpr int kCastLongUnits = 2 * kTileLanes;   // rows of more than this many units
 
-template <int FMT, int SM, int NL>
+template <int FMT, int SM, int NL, int CS>
 __global__ __launch_bounds__(NL)
 void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int tpr, int64_t T,
                               int groups, const int32_t* __restrict__ slot,
@@ -465,12 +472,12 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
     const int lane = tid & 63;
     const int units = nvec >> 1;
     const int nb = nvec >> 4;
-    const int j0 = g * kCastSlots;
-    const int32_t sl = lane < kCastSlots && j0 + lane < k ? slot[t * k + j0 + lane] : -1;
-    if (recv_w != nullptr && p == 0 && tid < kCastSlots && sl >= 0) recv_w[sl] = w[t * k + j0 + tid];
-    int32_t r[kCastSlots];
+    const int j0 = g * CS;
+    const int32_t sl = lane < CS && j0 + lane < k ? slot[t * k + j0 + lane] : -1;
+    if (recv_w != nullptr && p == 0 && tid < CS && sl >= 0) recv_w[sl] = w[t * k + j0 + tid];
+    int32_t r[CS];
 #pragma unroll
-    for (int q = 0; q < kCastSlots; ++q) r[q] = lane_value(sl, q);
+    for (int q = 0; q < CS; ++q) r[q] = lane_value(sl, q);
 
     // units past the row end (last tile) read zeros and store nothing; whole
     // blocks lie on one side of the row end (units is a multiple of 8)
@@ -484,7 +491,7 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
     const int bk = p * (NL / kLanesPerBlock) + (tid >> 6) * 8 + lane;   // lanes 0..7
     const bool scale_lane = lane < 8 && bk < nb;
 #pragma unroll
-    for (int q = 0; q < kCastSlots; ++q) {
+    for (int q = 0; q < CS; ++q) {
         if (r[q] < 0) continue;
         if (unit < units)
             store_row16(buffer_rsrc(recv_q + (int64_t)r[q] * units, units * 16), unit * 16, code);
@@ -669,18 +676,26 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     const bool narrow = narrow_tiles(units);
     const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
     const int tpr = (units + lanes - 1) / lanes;
-    const int groups = (num_topk + kCastSlots - 1) / kCastSlots;
+    const int cs = units > kCastLongUnits ? kCastSlotsLong : kCastSlotsShort;
+    const int groups = (num_topk + cs - 1) / cs;
     const int64_t blocks = (num_tokens + 7) / 8 * 8 * tpr * groups;
     const bool tiled = units > 64 && blocks <= INT32_MAX && scale_ld == 0;
-#define EP_FP8_TILES(F, M, NL)                                                                  \
-    hipLaunchKernelGGL((dispatch_fp8_tile_kernel<F, M, NL>), dim3((unsigned)blocks), dim3(NL), 0, \
-                       stream, xx, nvec, num_topk, tpr, num_tokens, groups, slot, topk_weights, qq, \
-                       recv_scales, recv_weights)
+#define EP_FP8_LAUNCH(F, M, NL, CS)                                                          \
+    hipLaunchKernelGGL((dispatch_fp8_tile_kernel<F, M, NL, CS>), dim3((unsigned)blocks), dim3(NL), \
+                       0, stream, xx, nvec, num_topk, tpr, num_tokens, groups, slot, topk_weights, \
+                       qq, recv_scales, recv_weights)
+#define EP_FP8_TILES(F, M, NL)                                                                \
+    {                                                                                         \
+        if (cs == kCastSlotsLong)                                                             \
+            EP_FP8_LAUNCH(F, M, NL, kCastSlotsLong);                                          \
+        else                                                                                  \
+            EP_FP8_LAUNCH(F, M, NL, kCastSlotsShort);                                         \
+    }
 #define EP_FP8_MODE(F, M)                                                                    \
     if (tiled && narrow)                                                                     \
-        EP_FP8_TILES(F, M, kTileLanes / 2);                                                  \
+        EP_FP8_TILES(F, M, kTileLanes / 2)                                                   \
     else if (tiled)                                                                          \
-        EP_FP8_TILES(F, M, kTileLanes);                                                      \
+        EP_FP8_TILES(F, M, kTileLanes)                                                       \
     else                                                                                     \
         launch_fp8_shape<F, M>(vpt, grid, stream, xx, nvec, num_topk, slot, topk_weights, qq, \
                                recv_scales, recv_weights, scale_ld)
@@ -695,6 +710,7 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
     }
 #undef EP_FP8_MODE
 #undef EP_FP8_TILES
+#undef EP_FP8_LAUNCH
     return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@
 //                 in: one workgroup per received token reads the sender's
 //                 row once and stores it to each of the rank's local-expert
 //                 rows, with the weights.
-//   combine:      one workgroup per (token, 2 KiB tile; 1 KiB for rows of
-//                 129-192 vectors) gathers its vectors from the G buffers
+//   combine:      one workgroup per (token, 2 KiB tile; 1 KiB where the
+//                 last 2 KiB tile would be at most half full) gathers its vectors from the G buffers
 //                 through buffer resources (an unrouted rank gets a 0-byte
 //                 resource: its loads return 0 without a branch), sums them
 //                 in fp32 in increasing rank and stores once, with a
@@ -859,9 +859,10 @@ void combine_ranked_kernel(RankPtrs src, int64_t src_rows, const int32_t* __rest
 // Tiled form (rows of more than 64 vectors): workgroup b is tile b % tpr of
 // token b / tpr, NL vectors, one 16-byte column vector per lane, stored once
 // with a streaming store (the expanded combine's tiling; its measurements
-// apply).  NL is 128, or 64 for rows of 129-192 vectors (narrow_tiles): at
-// 8 ranks x 8192 tokens those took 24.2, 26.6 and 30.7 us at hidden 1152,
-// 1280 and 1536 against 27.4, 28.2 and 31.6 us in 128-lane tiles.
+// apply).  NL is 128, or 64 where the last 128-lane tile would be at most
+// half full (narrow_tiles): at 8 ranks x 8192 tokens those took 24.2, 26.6,
+// 30.7 and 64.4 us at hidden 1152, 1280, 1536 and 3584 against 27.4, 28.2,
+// 31.6 and 66.6 us in 128-lane tiles.
 template <int NL>
 __global__ __launch_bounds__(NL)
 void combine_ranked_tile_kernel(RankPtrs src, int64_t src_rows, const int32_t* __restrict__ s2d,

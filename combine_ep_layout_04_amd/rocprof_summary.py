@@ -120,9 +120,10 @@ def _counter_medians(d: str):
 # library kernels by the key bench.py reports them under, as a pattern on
 # the full kernel name (the headline workload's instance: rows of 896
 # vectors take the tiled bf16 dispatch, combine and per-rank kernels, and
-# the row-major 8-bit casts the tiled cast); the 8-bit cast is told apart by
+# the row-major 8-bit casts the tiled cast in 64-lane tiles: 448 units end in
+# a half tile at 128 lanes); the 8-bit cast is told apart by
 # its template arguments <format (0 E4M3, 1 E5M2), scale (0 fp32, 1 power of
-# two, 2 UE8M0)>.  The median over a kernel's dispatches is used: the
+# two, 2 UE8M0), tile lanes, slots per workgroup>.  The median over a kernel's dispatches is used: the
 # E4M3 / fp32 instance also runs once over the tokens themselves (T rows,
 # one slot each) to make the pre-quantized input.  The combine line also
 # counts the dispatch-backward launches, which run the same kernel over the
@@ -131,11 +132,11 @@ def _counter_medians(d: str):
 # bytes are summed.
 KERNEL_KEYS = {
     "dispatch_bf16": r"dispatch_bf16_tile_kernel",
-    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 128>",
-    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 128>",
-    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 128>",
-    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 128>",
-    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 128>",
+    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 64, 4>",
+    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 64, 4>",
+    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 64, 4>",
+    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 64, 4>",
+    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 64, 4>",
     "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
     "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": (r"combine_backward_grad_y_tile_kernel",

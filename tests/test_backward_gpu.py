@@ -142,7 +142,7 @@ def test_dispatch_backward(name, T):
 
 @pytest.mark.parametrize("T,H,E,k", [(333, 1536, 24, 6), (129, 1288, 16, 11)])
 def test_dispatch_backward_narrow_tiles(T, H, E, k):
-    # rows of 129-192 vectors: the combine kernel in 64-lane tiles, with the
+    # 192 and 161 vectors: the combine kernel in 64-lane tiles, with the
     # weight gather from tile 0 (k = 11: the generic slot loop)
     inp = make_random_case(T + H, T, H, E, k, mask_frac=0.1)
     print(f"\n[backward] dispatch, 64-lane tiles T={T} H={H} k={k}", flush=True)

@@ -140,12 +140,13 @@ def check_case(idx, x_bits, w, E, seed=0, use_weights=True, stream=None):
     # vectors: the tiled dispatch
     (8192, 4, 64, 2048),   # 256-vector rows, one slot group
     (6144, 8, 256, 3072),  # 384-vector rows, two slot groups
-    # the combine in 64-lane tiles (rows of 129-192 vectors)
-    (300, 9, 40, 1536),    # 192 vectors: three full tiles, k = 9 (generic loop)
-    (257, 8, 64, 1152),    # 144 vectors: tiles of 64, 64 and 16
-    # the 8-bit cast in 64-lane tiles (rows of 129-192 16-channel units)
-    (333, 12, 32, 2176),   # 136 units: tiles of 64, 64 and 8, two slot groups
-    (200, 3, 16, 2944),    # 184 units: tiles of 64, 64 and 56
+    # 64-lane tiles, where the last 128-lane tile would be at most half full
+    (300, 9, 40, 1536),    # combine, 192 vectors: three full tiles, k = 9 (generic loop)
+    (257, 8, 64, 1152),    # combine, 144 vectors: tiles of 64, 64 and 16
+    (257, 6, 40, 3584),    # combine, 448 vectors: seven full tiles
+    (333, 12, 32, 2176),   # cast, 136 units: tiles of 64, 64 and 8, three slot groups
+    (200, 3, 16, 2944),    # cast, 184 units: tiles of 64, 64 and 56
+    (130, 8, 32, 5120),    # cast, 320 units: five full tiles, two slot groups
 ])
 def test_shapes(T, k, E, H):
     inp = make_random_case(T * 31 + k, T, H, E, k, mask_frac=0.1, dup_frac=0.0 if k <= E else 1.0)

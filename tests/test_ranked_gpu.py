@@ -249,8 +249,9 @@ def check_combine(ys, s2d, clip_rows=None):
                                    (8, 129, 24), (64, 20, 40),
                                    # tiled rows with every rank group of 8 loads
                                    (64, 20, 4104),
-                                   # 64-lane tiles (rows of 129-192 vectors)
-                                   (8, 300, 1536), (12, 77, 1288)])
+                                   # 64-lane tiles (the last 128-lane tile at
+                                   # most half full)
+                                   (8, 300, 1536), (12, 77, 1288), (8, 200, 3584)])
 def test_combine_ranked_small(G, T, H):
     rng = np.random.default_rng(G * 31 + T)
     s2d = np.full((T, G), -1, np.int32)
