@@ -35,7 +35,7 @@
 //                 past the received count; workgroup 0 also sums the
 //                 per-chunk receive-side counts into the totals.
 //   dispatch:     one workgroup per (2 KiB tile of a token's row, group of
-//                 4 destination ranks), the tile's workgroups back to back
+//                 8 destination ranks), the tile's workgroups back to back
 //                 on one XCD; it loads its tile once and stores it, with
 //                 streaming stores, to each rank of the group that receives
 //                 the token (a table of G row pointers passed by value);
@@ -620,8 +620,13 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
 // b maps (XCD-aware) to tile = (token t, tile pt of its row) and a group of
 // kRanksPerGroup destination ranks; the tile's loads after the first hit
 // the XCD's L2.  Tile 0's workgroups also write the group's weight rows.
-// The expanded dispatch's tiling; its measurements apply.
-constexpr int kRanksPerGroup = 4;
+// The expanded dispatch's tiling, with groups of 8 ranks: a token reaches
+// only some of a group's ranks (5.3 of 8 on average with 8 ranks, k=8), so
+// a group of 8 stores about as many rows as the expanded dispatch's group
+// of 4 slots.  At T=8192, hidden 7168 (interleaved A/B rounds) groups of 8
+// took 130.6 against 144.1 us for 4 at 8 ranks and 172.3 against 208.1 us
+// at 16 ranks, the same at 4; groups of 2 and 3 were 12-43% slower.
+constexpr int kRanksPerGroup = 8;
 
 __global__ __launch_bounds__(kTileLanes)
 void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,

@@ -176,7 +176,8 @@ def check_dispatch(x_bits, idx, w, E, G, s2d, rows, with_weights=True):
     (3, 64, 2048, 9, 9, False),       # k = 9 > E/G, no weights
     (8, 130, 7168, 64, 8, True),
     (64, 10, 256, 64, 64, True),      # k = EP_MAX_TOPK, G = EP_MAX_RANKS
-    (64, 20, 4104, 64, 8, True),      # tiled rows (513 vectors), 16 groups of 4 ranks
+    (64, 20, 4104, 64, 8, True),      # tiled rows (513 vectors), 8 groups of 8 ranks
+    (12, 40, 4096, 48, 8, True),      # tiled rows, a full and a partial group of ranks
 ])
 def test_dispatch_ranked_small(G, T, H, E, k, weights):
     inp = make_random_case(G * 7 + H, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
