@@ -137,7 +137,7 @@ KERNEL_KEYS = {
     "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 64, 4>",
     "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 64, 4>",
     "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 64, 4>",
-    "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<",
+    "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<7, 4>",
     "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": (r"combine_backward_grad_y_tile_kernel",
                          r"combine_backward_kernel<128, 7, false>"),

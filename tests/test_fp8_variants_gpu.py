@@ -214,3 +214,28 @@ def test_header_named_calls_match():
     assert torch.equal(a[3][placed], b[3][placed])
     assert torch.equal(q1[placed], q2[placed]) and torch.equal(s1[placed], s2[placed])
     assert torch.equal(r1[placed].view(torch.int16), r2[placed].view(torch.int16))
+
+
+@pytest.mark.parametrize("T,H,E,k", [(257, 4224, 24, 11), (100, 7168, 16, 6), (64, 5120, 8, 3)])
+def test_prequantized_slot_groups(T, H, E, k):
+    # rows of more than 256 units with row-major scales: one wavefront per
+    # (token, group of 4 slots), the last group partial; masked and invalid
+    # slots, weights
+    inp = make_random_case(T + k, T, H, E, k, mask_frac=0.15, dup_frac=1.0, invalid_frac=0.05)
+    print(f"\n[prequantized] slot groups T={T} H={H} k={k}", flush=True)
+    xq, xs, _ = oracle.dispatch_quant(inp.x_bits, np.arange(T, dtype=np.int32)[:, None],
+                                      fmt="e4m3", scale="fp32")
+    L = oracle.layout(inp.topk_idx, E)
+    rows = T * k
+    q = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    s = torch.full((rows, H // 128), float("nan"), dtype=torch.float32, device=DEV)
+    rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized(dev(xq), dev(xs), dev(L.slot), dev(inp.topk_weights), recv_q=q,
+                                recv_scales=s, recv_weights=rw)
+    torch.cuda.synchronize()
+    oq, os_, orw = oracle.dispatch_prequant(xq, xs, L.slot, inp.topk_weights)
+    n = L.n
+    np.testing.assert_array_equal(host(q)[:n], oq[:n])
+    np.testing.assert_array_equal(host(s)[:n].view(np.uint32), os_[:n].view(np.uint32))
+    np.testing.assert_array_equal(host(rw)[:n], orw[:n])
+    assert np.all(host(q)[n:] == 0xEE) and np.all(np.isnan(host(s)[n:]))
