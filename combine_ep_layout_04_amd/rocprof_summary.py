@@ -149,7 +149,7 @@ KERNEL_KEYS = {
     # bf16 rows go through the tiled kernel, 8-bit code rows with their
     # scales (448 vectors: 64 lanes) through the per-token one
     "dispatch_ranked": r"dispatch_ranked_tile_kernel",
-    "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64,",
+    "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64, 7, 4>",
     "combine_ranked": r"combine_ranked_tile_kernel<128>",
     "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }
