@@ -534,10 +534,13 @@ __device__ __forceinline__ void write_rank_weights(float* row, int k, int32_t e_
 // token's nb fp32 scales are copied to ds[d] as well.  RG == 0: one
 // workgroup per token, all G ranks.  RG > 0: one workgroup per (token,
 // group of RG ranks), a token's workgroups back to back on one XCD
-// (xcd_tile), so its row comes from HBM once.  For 8-bit rows of more than
-// 256 vectors, groups of 4 ranks took 75.1 against 83.1 us at 8 ranks and
-// 88.6 against 100.2 us at 16 (T=8192 per rank, hidden 7168, interleaved
-// A/B); groups of 2 were as fast at 8 ranks but 10% slower at 16.
+// (xcd_tile), so its row comes from HBM once.  Used for rows of more than
+// 384 vectors when there are more than 4 ranks: for 8-bit rows at hidden
+// 7168 (448 vectors) groups of 4 ranks took 75.1 against 83.1 us at 8 ranks
+// and 88.6 against 100.2 us at 16 (T=8192 per rank, interleaved A/B;
+// groups of 2 were as fast at 8 ranks but 10% slower at 16); for bf16 rows
+// of 448 vectors (hidden 3584) 76.4 against 82.9 us and 85.4 against
+// 98.1 us.  At 384 vectors and below groups were 2% faster to 41% slower.
 template <int NT, int VPT, int RG>
 __global__ __launch_bounds__(NT)
 void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t* __restrict__ idx,
@@ -997,8 +1000,8 @@ hipError_t launch_rank_layout(const uint8_t* map, int64_t tokens_per_rank, int n
     return hipGetLastError();
 }
 
-constexpr int kPrequantRankGroup = 4;           // ranks per workgroup, grouped 8-bit rows
-constexpr int kPrequantRankGroupVectors = 256;  // grouped for rows of more than this
+constexpr int kRankGroup = 4;            // ranks per workgroup when grouped
+constexpr int kRankGroupVectors = 384;   // grouped for rows of more than this many vectors
 
 hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
                                   int64_t num_tokens, int row_bytes, int num_topk, int num_experts,
@@ -1023,16 +1026,16 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
                            groups);
         return hipGetLastError();
     }
-    // 8-bit rows of more than 256 vectors: one workgroup per (token, group
-    // of kPrequantRankGroup ranks)
-    const int rgroups = (num_ranks + kPrequantRankGroup - 1) / kPrequantRankGroup;
+    // rows of more than kRankGroupVectors vectors: one workgroup per
+    // (token, group of kRankGroup ranks)
+    const int rgroups = (num_ranks + kRankGroup - 1) / kRankGroup;
     const int64_t gblocks = (num_tokens + 7) / 8 * 8 * rgroups;
-    const bool rank_grouped = x_scales != nullptr && nvec > kPrequantRankGroupVectors &&
-                              num_ranks > kPrequantRankGroup && gblocks <= INT32_MAX;
+    const bool rank_grouped = nvec > kRankGroupVectors && num_ranks > kRankGroup &&
+                              gblocks <= INT32_MAX;
     const dim3 ggrid((unsigned)gblocks);
 #define EP_DR(NT, V)                                                                            \
     if (rank_grouped)                                                                           \
-        hipLaunchKernelGGL((dispatch_ranked_kernel<NT, V, kPrequantRankGroup>), ggrid, dim3(NT),  \
+        hipLaunchKernelGGL((dispatch_ranked_kernel<NT, V, kRankGroup>), ggrid, dim3(NT),          \
                            0, stream, xx, nvec, topk_idx, topk_weights, num_topk, num_experts, El, \
                            num_ranks, s2d, dest_rows, dest_x, dest_w, with_weights, x_scales,      \
                            dest_scales, num_scales, num_tokens);                                  \

@@ -178,6 +178,7 @@ def check_dispatch(x_bits, idx, w, E, G, s2d, rows, with_weights=True):
     (64, 10, 256, 64, 64, True),      # k = EP_MAX_TOPK, G = EP_MAX_RANKS
     (64, 20, 4104, 64, 8, True),      # tiled rows (513 vectors), 8 groups of 8 ranks
     (12, 40, 4096, 48, 8, True),      # tiled rows, a full and a partial group of ranks
+    (10, 40, 3584, 40, 8, True),      # 448 vectors, per token: groups of 4 ranks, the last of 2
 ])
 def test_dispatch_ranked_small(G, T, H, E, k, weights):
     inp = make_random_case(G * 7 + H, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
@@ -449,9 +450,9 @@ def check_ranked_prequant(xq, xs, idx, w, E, G, s2d, rows):
 
 @pytest.mark.parametrize("G,T,H,E,k", [(1, 3, 128, 2, 1), (2, 37, 256, 8, 3), (4, 200, 1152, 16, 5),
                                        (8, 130, 7168, 64, 8), (64, 10, 2048, 64, 64),
-                                       # rows of more than 256 vectors: groups of 4 ranks
-                                       (10, 40, 5120, 40, 8),    # the last group of 2 ranks
-                                       (64, 20, 4224, 64, 8)])   # 16 groups
+                                       # rows of more than 384 vectors: groups of 4 ranks
+                                       (10, 40, 7168, 40, 8),    # the last group of 2 ranks
+                                       (64, 20, 6400, 64, 8)])   # 16 groups
 def test_dispatch_ranked_prequantized(G, T, H, E, k):
     inp = make_random_case(G * 3 + H, T, 8, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
     rng = np.random.default_rng(G + T)
