@@ -161,7 +161,8 @@ void dispatch_bf16_kernel(const uint4* __restrict__ x, int nvec, int k,
 // p of its row) and slot group g (slots 4g .. 4g+3).
 constexpr int kSlotsPerGroup = 4;
 
-__global__ __launch_bounds__(kTileLanes)
+template <int NL>
+__global__ __launch_bounds__(NL)
 void dispatch_bf16_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int tpr,
                                int64_t num_tiles, int groups, const int32_t* __restrict__ slot,
                                const float* __restrict__ w, uint4* __restrict__ recv,
@@ -183,7 +184,7 @@ void dispatch_bf16_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int
     int32_t r[kSlotsPerGroup];
 #pragma unroll
     for (int q = 0; q < kSlotsPerGroup; ++q) r[q] = lane_value(sl, q);
-    const int v = p * kTileLanes + tid;     // past the row end (last tile) stores nothing
+    const int v = p * NL + tid;             // past the row end (last tile) stores nothing
     uint4 d = load_row16<0>(buffer_rsrc(x + t * nvec, nvec * 16), v * 16);
     keep(d);
 #pragma unroll
@@ -622,14 +623,29 @@ hipError_t launch_dispatch_bf16(const void* x, int64_t num_tokens, int hidden, i
 {
     if (num_tokens == 0) return hipSuccess;
     const int nvec = hidden / 8;
-    const int tpr = tiles_per_row(nvec);
+    // rows of 257-511 vectors whose last 128-lane tile would be at most half
+    // full go in 64-lane tiles: at T=8192, k=8 (interleaved A/B) hidden
+    // 2560, 3200 and 3584 took 74.1, 93.0 and 103.5 us against 80.3, 98.6
+    // and 111.9 us for one workgroup per token, and 2-5% less at T=4096 or
+    // k=4; at 129-192 vectors (hidden 1152-1536) they were 3% faster to 7%
+    // slower, and those rows stay per token
+    const bool narrow = nvec > 2 * kTileLanes && nvec < kMinTiledDispatchVectors && narrow_tiles(nvec);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (nvec + lanes - 1) / lanes;
     const int groups = (num_topk + kSlotsPerGroup - 1) / kSlotsPerGroup;
     const int64_t num_tiles = num_tokens * tpr;
     const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
-    if (tile_dispatch(nvec, num_tokens * num_topk) && blocks <= INT32_MAX) {
-        hipLaunchKernelGGL(dispatch_bf16_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
-                           stream, static_cast<const uint4*>(x), nvec, num_topk, tpr, num_tiles,
-                           groups, slot, topk_weights, static_cast<uint4*>(recv_x), recv_weights);
+    if ((narrow || tile_dispatch(nvec, num_tokens * num_topk)) && blocks <= INT32_MAX) {
+        if (narrow)
+            hipLaunchKernelGGL(dispatch_bf16_tile_kernel<kTileLanes / 2>, dim3((unsigned)blocks),
+                               dim3(kTileLanes / 2), 0, stream, static_cast<const uint4*>(x), nvec,
+                               num_topk, tpr, num_tiles, groups, slot, topk_weights,
+                               static_cast<uint4*>(recv_x), recv_weights);
+        else
+            hipLaunchKernelGGL(dispatch_bf16_tile_kernel<kTileLanes>, dim3((unsigned)blocks),
+                               dim3(kTileLanes), 0, stream, static_cast<const uint4*>(x), nvec,
+                               num_topk, tpr, num_tiles, groups, slot, topk_weights,
+                               static_cast<uint4*>(recv_x), recv_weights);
         return hipGetLastError();
     }
     const Shape sh = pick_shape(nvec);

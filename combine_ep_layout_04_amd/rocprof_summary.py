@@ -131,7 +131,7 @@ def _counter_medians(d: str):
 # operation (the combine backward's grad_y tiles and its grad_w pass), whose
 # bytes are summed.
 KERNEL_KEYS = {
-    "dispatch_bf16": r"dispatch_bf16_tile_kernel",
+    "dispatch_bf16": r"dispatch_bf16_tile_kernel<128>",
     "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 64, 4>",
     "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 64, 4>",
     "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 64, 4>",

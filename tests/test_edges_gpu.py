@@ -143,7 +143,8 @@ def check_case(idx, x_bits, w, E, seed=0, use_weights=True, stream=None):
     # 64-lane tiles, where the last 128-lane tile would be at most half full
     (300, 9, 40, 1536),    # combine, 192 vectors: three full tiles, k = 9 (generic loop)
     (257, 8, 64, 1152),    # combine, 144 vectors: tiles of 64, 64 and 16
-    (257, 6, 40, 3584),    # combine, 448 vectors: seven full tiles
+    (257, 6, 40, 3584),    # dispatch and combine, 448 vectors: seven full tiles
+    (129, 8, 16, 3200),    # dispatch and combine, 400 vectors: the last tile of 16 lanes
     (333, 12, 32, 2176),   # cast, 136 units: tiles of 64, 64 and 8, three slot groups
     (200, 3, 16, 2944),    # cast, 184 units: tiles of 64, 64 and 56
     (130, 8, 32, 5120),    # cast, 320 units: five full tiles, two slot groups

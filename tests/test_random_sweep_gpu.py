@@ -40,10 +40,11 @@ def draw(seed):
     k = int(rng.integers(1, 13))
     fp8 = bool(rng.random() < 0.5)
     # 4104: 513-vector rows, tiled with a one-vector last tile; 1032 and
-    # 1288 (129 and 161 vectors): the combine in 64-lane tiles; 2560 (160
-    # units): the 8-bit cast in 64-lane tiles
+    # 1288 (129 and 161 vectors): the combine in 64-lane tiles; 3200 (400
+    # vectors): the dispatch and the combine in 64-lane tiles, the last one
+    # of 16 lanes; 2560 (160 units): the 8-bit cast in 64-lane tiles
     H = (int(rng.choice([128, 256, 1152, 2048, 2560])) if fp8
-         else int(rng.choice([8, 24, 136, 1032, 1288, 2048, 4104])))
+         else int(rng.choice([8, 24, 136, 1032, 1288, 2048, 3200, 4104])))
     mode = rng.choice(["plain", "aligned", "capacity"], p=[0.5, 0.3, 0.2])
     A = int(rng.choice([2, 16, 128])) if mode == "aligned" else 1
     cap = int(rng.choice([1, 4, 32])) * A if mode == "capacity" else 0
