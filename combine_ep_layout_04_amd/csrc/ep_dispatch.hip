@@ -18,8 +18,9 @@
 //     T=8192, hidden 7168, k=8 with cold caches: workgroups that each write
 //     a few 2 KiB pieces stream faster than ones that write 56 in turn.
 //     Short rows (under 512 vectors, unless they are whole tiles and the
-//     dispatch writes at least 2^23 vectors), and grids past 2^31
-//     workgroups, keep one workgroup per token;
+//     dispatch writes at least 2^23 vectors, or rows of 257-511 vectors
+//     whose last tile would be at most half full, which take 64-lane
+//     tiles), and grids past 2^31 workgroups, keep one workgroup per token;
 //   - the slots a workgroup serves are wavefront-uniform (read into lanes,
 //     then readlane), so the loop over destinations has no divergence;
 //   - fp8: each lane owns 16 channels (a "unit": two 16-byte loads in, one
