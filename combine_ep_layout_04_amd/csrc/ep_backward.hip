@@ -38,8 +38,11 @@
 // w * g uses the exact product error e = fma(w, g, -p) of p = fl32(w * g):
 // p is on the same side of every bf16 rounding boundary as the exact product
 // unless p is itself a boundary (a bf16 midpoint), where the sign of e
-// decides; this is exact whenever w * g is not an fp32 subnormal.  The
-// branch-free form of that rule measured ~1.6x faster than a branchy one.
+// decides; this is exact whenever |w * g| >= 2^-117.  The branch-free form
+// of that rule measured ~1.6x faster than a branchy one.  A vector that may
+// hold a smaller nonzero or a NaN product (found from the vector's smallest
+// nonzero and largest |g|, once per vector, and the slot's weight) is
+// rounded exactly in fp64 instead.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -55,7 +58,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // the low 16 bits of p are exactly 0x8000 (a bf16 midpoint), and there the
 // exact product lies above the midpoint's magnitude iff e has p's sign, is
 // on it iff e == 0 (then ties go to even: c = lsb).  So c is chosen without
-// testing for the midpoint at all.  Products are finite or quiet NaN here.
+// testing for the midpoint at all.
+//
+// e is exact when w = Mw 2^a, g = Mg 2^b (Mw < 2^24, Mg < 2^8 integers)
+// have a + b >= -149: e is a multiple of 2^(a+b) below half an ulp of p.
+// The exact product is below 2^(a+b+32), so |w g| >= 2^-117 guarantees it.
+// Smaller nonzero products (where e may round to 0 and lose the side of a
+// midpoint: w = 1.25 * 2^-32 + 2^-55, g = 2^-100 is one) and NaN products
+// are left to bf16_of_product_exact; vector_needs_exact finds them.
 __device__ __forceinline__ uint32_t bf16_of_product(float w, float g)
 {
     const float p = w * g;
@@ -67,13 +77,80 @@ __device__ __forceinline__ uint32_t bf16_of_product(float w, float g)
     return (u + 0x7FFFu + c) >> 16;
 }
 
-__device__ __forceinline__ uint4 scale_row8(float w, const uint4& g)
+// The same rounding without the fast path's limits: the product is formed
+// in fp64, where it is exact (at most 24 + 8 significant bits, exponent
+// from -282 up), then rounded to nearest even on the bf16 grid: multiples
+// of 2^-133 below 2^-126, otherwise 8 significant bits by an integer RNE on
+// the fp64 bit pattern, where a result past the largest finite bf16 (an
+// infinite product included) is infinity.  A NaN product gives the
+// canonical quiet NaN 0x7FC0 (the sign and payload of a NaN a multiply
+// makes are not portable).
+__device__ __forceinline__ uint32_t bf16_of_product_exact(float w, float g)
+{
+    const double d = (double)w * (double)g;
+    if (d != d) return 0x7FC0u;
+    const uint64_t u = (uint64_t)__double_as_longlong(d);
+    const uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+    const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
+    if (a < 0x3810000000000000ull)   // |d| < 2^-126
+        return sign | (uint32_t)__builtin_rint(__longlong_as_double((long long)a) * 0x1p133);
+    const uint64_t r = ((a + ((1ull << 44) - 1) + ((a >> 45) & 1ull)) >> 45) - ((uint64_t)(1023 - 127) << 7);
+    return sign | (uint32_t)(r < 0x7F80ull ? r : 0x7F80ull);
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// What one vector of 8 bf16 gradients contributes to that test, computed
+// once and shared by every slot the vector is scaled for: `gmin`, the
+// smallest nonzero |g| as fp32 (+inf past the bf16 range when all are 0),
+// and whether any |g| is infinite or NaN.  Packed 16-bit operations on the
+// bf16 magnitudes: m - 1 wraps 0 to 0xFFFF, so the minimum skips zeros.
+struct GradStat {
+    float gmin;
+    bool special;
+};
+
+__device__ __forceinline__ GradStat grad_stat(const uint4& g)
+{
+    const u16x2 one = {1, 1};
+    const u16x2 m0 = __builtin_bit_cast(u16x2, g.x & 0x7FFF7FFFu);
+    const u16x2 m1 = __builtin_bit_cast(u16x2, g.y & 0x7FFF7FFFu);
+    const u16x2 m2 = __builtin_bit_cast(u16x2, g.z & 0x7FFF7FFFu);
+    const u16x2 m3 = __builtin_bit_cast(u16x2, g.w & 0x7FFF7FFFu);
+    const u16x2 lo = __builtin_elementwise_min(__builtin_elementwise_min(m0 - one, m1 - one),
+                                               __builtin_elementwise_min(m2 - one, m3 - one));
+    const u16x2 hi = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                               __builtin_elementwise_max(m2, m3));
+    const uint32_t mn = (uint32_t)min(lo.x, lo.y) + 1u;   // 0x10000 if all are 0
+    GradStat st;
+    st.gmin = __uint_as_float(min(mn, 0x7F80u) << 16);     // all 0: +inf
+    st.special = max(hi.x, hi.y) >= 0x7F80u;
+    return st;
+}
+
+// True when some product w * g of the vector may fall outside the fast
+// path: a NaN or infinite w, an infinite or NaN g, or a nonzero product
+// below 2^-116 (fl32(|w| gmin) is at most 2^-117 whenever the smallest
+// exact nonzero product is, since rounding is monotone).
+__device__ __forceinline__ bool vector_needs_exact(float w, const GradStat& st)
+{
+    return !(fabsf(w) <= 0x1.fffffep127f) || st.special || fabsf(w) * st.gmin < 0x1p-116f;
+}
+
+__device__ __forceinline__ uint4 scale_row8(float w, const uint4& g, const GradStat& st)
 {
     uint4 o;
-    o.x = bf16_of_product(w, bf16_lo(g.x)) | (bf16_of_product(w, bf16_hi(g.x)) << 16);
-    o.y = bf16_of_product(w, bf16_lo(g.y)) | (bf16_of_product(w, bf16_hi(g.y)) << 16);
-    o.z = bf16_of_product(w, bf16_lo(g.z)) | (bf16_of_product(w, bf16_hi(g.z)) << 16);
-    o.w = bf16_of_product(w, bf16_lo(g.w)) | (bf16_of_product(w, bf16_hi(g.w)) << 16);
+    if (!vector_needs_exact(w, st)) {
+        o.x = bf16_of_product(w, bf16_lo(g.x)) | (bf16_of_product(w, bf16_hi(g.x)) << 16);
+        o.y = bf16_of_product(w, bf16_lo(g.y)) | (bf16_of_product(w, bf16_hi(g.y)) << 16);
+        o.z = bf16_of_product(w, bf16_lo(g.z)) | (bf16_of_product(w, bf16_hi(g.z)) << 16);
+        o.w = bf16_of_product(w, bf16_lo(g.w)) | (bf16_of_product(w, bf16_hi(g.w)) << 16);
+    } else {
+        o.x = bf16_of_product_exact(w, bf16_lo(g.x)) | (bf16_of_product_exact(w, bf16_hi(g.x)) << 16);
+        o.y = bf16_of_product_exact(w, bf16_lo(g.y)) | (bf16_of_product_exact(w, bf16_hi(g.y)) << 16);
+        o.z = bf16_of_product_exact(w, bf16_lo(g.z)) | (bf16_of_product_exact(w, bf16_hi(g.z)) << 16);
+        o.w = bf16_of_product_exact(w, bf16_lo(g.w)) | (bf16_of_product_exact(w, bf16_hi(g.w)) << 16);
+    }
     return o;
 }
 
@@ -141,6 +218,9 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
             }
 #pragma unroll
             for (int u = 0; u < VPT; ++u) keep(gv[u]);
+            GradStat gs[VPT];
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) gs[u] = STORE ? grad_stat(gv[u]) : GradStat{0.0f, false};
 #pragma unroll
             for (int q = 0; q < kGroup; ++q) {
                 if (q >= jn) break;
@@ -160,7 +240,7 @@ void combine_backward_kernel(const uint4* __restrict__ g, const uint4* __restric
 #pragma unroll
                     for (int u = 0; u < VPT; ++u) {
                         const int v = p0 + tid + u * NT;
-                        if (v < nvec) store_row16(dst, v * 16, scale_row8(wj, gv[u]));
+                        if (v < nvec) store_row16(dst, v * 16, scale_row8(wj, gv[u], gs[u]));
                     }
                 }
             }
@@ -223,11 +303,12 @@ void combine_backward_grad_y_tile_kernel(const uint4* __restrict__ g, int nvec, 
     const int v = p * kTileLanes + tid;
     uint4 d = load_row16<0>(buffer_rsrc(g + t * nvec, nvec * 16), v * 16);
     keep(d);
+    const GradStat gs = grad_stat(d);
 #pragma unroll
     for (int q = 0; q < kGradYSlots; ++q)
         if (r[q] >= 0 && v < nvec)
             store_row16(buffer_rsrc(grad_y + (int64_t)r[q] * nvec, nvec * 16), v * 16,
-                        scale_row8(wq[q], d));
+                        scale_row8(wq[q], d, gs));
 }
 
 }  // namespace

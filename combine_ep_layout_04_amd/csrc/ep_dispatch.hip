@@ -38,9 +38,10 @@
 //     "Computation of elementary functions on the IBM RISC System/6000
 //     processor", IBM J. Res. Dev. 34(1), 1990): with y = RN(1/scale)
 //     computed once, q0 = |x| * y, r = fma(-q0, scale, |x|) (exact),
-//     q = fma(r, y, q0).  That q was checked to give the same E4M3 code as
-//     the correctly rounded quotient for every bf16 amax >= 2^-80 and every
-//     bf16 |x| <= amax; blocks with a smaller, infinite or NaN amax take the
+//     q = fma(r, y, q0).  That q was checked to give the same code as the
+//     correctly rounded quotient, in E4M3 (scale amax / 448) and in E5M2
+//     (scale amax / 57344), for every bf16 amax >= 2^-80 and every bf16
+//     |x| <= amax; blocks with a smaller, infinite or NaN amax take the
 //     plain division.  The sign is applied after encoding |q|, so -0 stays
 //     -0.  The E4M3 code comes from an integer round-to-nearest-even on the
 //     fp32 bit pattern (written from the OCP E4M3 definition: bias 7,
@@ -270,6 +271,22 @@ __device__ __forceinline__ int ceil_log2(float s)
     return m == 0.5f ? ex - 1 : ex;
 }
 
+// Exponent of a power-of-two scale: the smallest e with 2^e >= amax / fmax,
+// the exact quotient, for finite amax > 0.  amax is a bf16 value (8
+// significant bits) and fmax is 7 * 2^n, so the quotient is a power of two
+// only when the division is exact, and otherwise lies at least 2^-8
+// (relative) away from one: a correctly rounded fp32 quotient decides e, as
+// long as it is normal.  For amax below 2^-64 the fp32 quotient would be
+// subnormal (amax 2^-133 over 57344 rounds down onto 2^-149, one binade
+// short, and the codes would then overflow), so such an amax is scaled by
+// 2^64 first; amax >= 2^-133 keeps the scaled quotient normal.
+__device__ __forceinline__ int pow2_exponent(float amax, float fmax)
+{
+    const bool tiny = amax < 0x1p-64f;
+    const int e = ceil_log2((tiny ? amax * 0x1p64f : amax) / fmax);
+    return tiny ? e - 64 : e;
+}
+
 // Codes (16 bytes) and block scale for the 16 channels in d0:d1; the 8
 // aligned lanes of one 128-channel block must execute this together.  The
 // scale comes back as fp32 (modes 0, 1) or as the UE8M0 byte in its low
@@ -309,8 +326,7 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, ui
     } else if (SM != kScaleFp32 && m > 0u && m < 0x7F800000u) {
         // finite nonzero amax, power-of-two scale: q = x * 2^-e is exact and
         // |q| <= max_finite
-        const float amax = __uint_as_float(m);
-        int e = ceil_log2(amax / fmax);
+        int e = pow2_exponent(__uint_as_float(m), fmax);
         if (SM == kScaleUe8m0 && e < -127) e = -127;
         scale_bits = SM == kScaleUe8m0 ? (uint32_t)(e + 127) : __float_as_uint(ldexpf(1.0f, e));
 #pragma unroll
@@ -331,7 +347,7 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, ui
         int e = 0;
         float sc = amax / fmax;
         if (pow2) {
-            e = ceil_log2(sc);
+            e = pow2_exponent(amax, fmax);
             if (SM == kScaleUe8m0 && e < -127) e = -127;
             sc = ldexpf(1.0f, e);
         }

@@ -375,7 +375,10 @@ void oracle_combine(const uint16_t *y, const int32_t *slot, const float *topk_we
  *                                                     one rounding)
  *   grad_w[t,j] = fl32( sum_c g[t,c] * y[slot[t,j], c] )   (fp64 sum)
  * Masked pairs write no row and get grad_w 0.  w == NULL means unit
- * weights; grad_w may be NULL (then y is not read).
+ * weights; grad_w may be NULL (then y is not read).  A NaN product (a NaN
+ * weight or gradient, or 0 * inf) gives the canonical quiet NaN 0x7FC0, the
+ * bf16 NaN torch's float-to-bf16 cast returns for any NaN: the sign of a
+ * NaN that a multiply makes is not the same on every machine.
  */
 void oracle_combine_backward(const uint16_t *g, const uint16_t *y, const int32_t *slot,
                              const float *topk_weights, int64_t T, int H, int k,
@@ -393,7 +396,8 @@ void oracle_combine_backward(const uint16_t *g, const uint16_t *y, const int32_t
             double dot = 0.0;
             for (int c = 0; c < H; ++c) {
                 double gv = oracle_bf16_to_double(g[t * H + c]);
-                grad_y[(int64_t)r * H + c] = oracle_bf16_from_double(w * gv);
+                double prod = w * gv;               /* exact: 24 + 8 significant bits */
+                grad_y[(int64_t)r * H + c] = isnan(prod) ? 0x7FC0u : oracle_bf16_from_double(prod);
                 if (grad_w)
                     dot += gv * oracle_bf16_to_double(y[(int64_t)r * H + c]);
             }
@@ -429,8 +433,9 @@ void oracle_dispatch_backward(const uint16_t *grad_recv, const float *grad_recv_
  *   format 0: OCP E4M3 (largest finite 448), 1: OCP E5M2 (57344)
  *   scale_mode 0: scale = fl32(amax / max_finite), q = code(fl32(x / scale))
  *   scale_mode 1: power-of-two scale 2^e, e the smallest integer with
- *                 2^e >= amax / max_finite (ceil of log2 of fl32(amax /
- *                 max_finite)), stored as fp32; q = code(x * 2^-e) (exact)
+ *                 2^e >= amax / max_finite (the exact quotient), stored as
+ *                 fp32; q = code(x * 2^-e) (exact, and never above
+ *                 max_finite)
  *   scale_mode 2: as 1, stored as one UE8M0 byte e + 127 with e clamped to
  *                 -127 (the byte's smallest value)
  * amax ignores NaN.  amax == 0: codes 0, scale 0 (fp32) or byte 0.  An
@@ -463,9 +468,17 @@ void oracle_dispatch_quant(const uint16_t *x, int64_t T, int H, int k, const int
             if (scale_mode == 0 || amax == 0.0f || isinf(amax)) {
                 scale = amax / fmax;
             } else {
+                /* e from the quotient amax / max_finite in double: amax is a
+                 * bf16 value (8 significant bits) and max_finite is 7 * 2^n,
+                 * so the quotient is a power of two only when the division is
+                 * exact, and otherwise lies at least 2^-11 (relative) away
+                 * from one; its double rounding (2^-53) never crosses a power
+                 * of two.  The fp32 quotient would not do: below 2^-126 it
+                 * keeps too few bits, and for amax 2^-133 over 57344 it
+                 * rounds down onto 2^-149, one binade short. */
                 int ex;
-                float s0 = amax / fmax;
-                double f = frexp((double)s0, &ex);      /* s0 = f * 2^ex, f in [0.5, 1) */
+                double s0 = (double)amax / (double)fmax;
+                double f = frexp(s0, &ex);              /* s0 = f * 2^ex, f in [0.5, 1) */
                 e = (f == 0.5) ? ex - 1 : ex;           /* smallest e with 2^e >= s0 */
                 if (scale_mode == 2 && e < -127)
                     e = -127;

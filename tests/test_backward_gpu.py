@@ -18,6 +18,7 @@ import torch
 import oracle
 from combine_ep_layout_04_amd import ep
 from combine_ep_layout_04_amd.inputs import (
+    bf16_bits_from_float32,
     WORKLOADS, expert_outputs_scaled, float32_from_bf16_bits, make_gradient, make_inputs,
     make_random_case,
 )
@@ -202,3 +203,38 @@ def test_backward_at_max_hidden():
         r = L.slot[:, j]
         s[r >= 0] += gr[r[r >= 0]]
     assert np.all(np.abs(got - want) <= bf16_ulp(want) + 2.0 * k * 2.0 ** -24 * s)
+
+
+@pytest.mark.parametrize("H", [64, 4096])
+def test_combine_backward_tiny_and_nan_products(H):
+    # products below 2^-116 (around the bf16 subnormal range, where an fp32
+    # product-error test can miss the side of a midpoint), exact midpoints,
+    # NaN weights (one with high half 0x7FFF) and 0 * inf: grad_y bit-exact
+    # against the oracle.  H 64 runs the fused pass, 4096 the tiled grad_y.
+    rng = np.random.default_rng(H)
+    T, k = 64, 4
+    g = bf16_bits_from_float32((rng.choice([-1.0, 1.0], (T, H)) * (1 + rng.integers(0, 128, (T, H)) / 128.0)
+                                * np.exp2(rng.integers(-110, -90, (T, H)))).astype(np.float32))
+    w = (rng.choice([-1.0, 1.0], (T, k)) * rng.uniform(1, 2, (T, k))
+         * np.exp2(rng.integers(-40, -20, (T, k)))).astype(np.float32)
+    w[0, 0] = np.float32(1.25 * 2.0 ** -32 + 2.0 ** -55)
+    g[0, :] = bf16_bits_from_float32(np.full(H, 2.0 ** -100, np.float32))
+    w[1, 0] = np.float32(1.5 * 2.0 ** -33)
+    g[1, :] = g[0, :]
+    w.view(np.uint32)[2, 1] = 0x7FFFFFFF
+    w.view(np.uint32)[2, 2] = 0xFFFFFFFF
+    g[3, 5] = 0x7F80
+    g[3, 6] = 0xFF80
+    w[3, 0] = 0.0
+    g[4, :] = 0                                    # exact zeros among tiny products
+    g[5, ::2] = bf16_bits_from_float32(np.ones(H // 2, np.float32))   # normal products too
+    slot = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    slot[6, 1] = -1
+    g_gy, _ = run_combine_backward(g, g[:1].repeat(T * k, 0), slot, w, T * k)
+    o_gy, _ = oracle.combine_backward(g, None, slot, w, rows=T * k)
+    placed = np.zeros(T * k, bool)
+    placed[slot[slot >= 0]] = True
+    np.testing.assert_array_equal(g_gy[placed], o_gy[placed])
+    assert g_gy[slot[0, 0], 0] == 0x0003 and g_gy[slot[1, 0], 0] == 0x0002
+    assert np.all(g_gy[slot[2, 1]] == 0x7FC0) and np.all(g_gy[slot[2, 2]] == 0x7FC0)
+    assert g_gy[slot[3, 0], 5] == 0x7FC0

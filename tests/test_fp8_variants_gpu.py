@@ -32,6 +32,9 @@ def special_rows():
     x[7, 900] = -57344.0
     x[8, :128] = 2.0 ** -90      # below the fast-quotient threshold
     x[9, 3] = -0.0
+    x[10, 128:256] = 0.0         # amax 2^-133, the smallest bf16: its fp32
+    x[10, 128] = 2.0 ** -133     # quotient by 57344 is subnormal
+    x[10, 129] = -(2.0 ** -133)
     return inp, bf16_bits_from_float32(x)
 
 
@@ -61,6 +64,31 @@ def test_variants_special_blocks(fmt, mode):
     inp, xb = special_rows()
     L = oracle.layout(inp.topk_idx, 8)
     check(xb, L, fmt, mode)
+
+
+@pytest.mark.parametrize("hidden", [128, 2048])
+@pytest.mark.parametrize("fmt,mode", COMBOS)
+def test_variants_every_bf16_amax(fmt, mode, hidden):
+    # every finite positive bf16 magnitude as the amax of one 128-channel
+    # block, the other channels random bf16 values of at most that
+    # magnitude (either sign): hidden 128 runs the per-token kernel, 2048
+    # the tiled one
+    rng = np.random.default_rng(77)
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    nb = hidden // 128
+    T = -(-bits.size // nb)
+    amax = np.ones(T * nb, np.uint16)
+    amax[:bits.size] = bits
+    blk = (rng.random((T * nb, 128)) * (amax[:, None].astype(np.float64) + 1)).astype(np.uint16)
+    blk |= (rng.integers(0, 2, blk.shape, dtype=np.uint16) << 15)
+    blk[:, 0] = amax
+    blk[:, 1] = amax | 0x8000
+    xb = blk.reshape(T, hidden)
+    slot = np.arange(T, dtype=np.int32)[:, None]
+    gq, gs = run(xb, slot, fmt, mode, T)
+    oq, os_, _ = oracle.dispatch_quant(xb, slot, fmt=fmt, scale=mode, rows=T)
+    np.testing.assert_array_equal(gq, oq)
+    np.testing.assert_array_equal(gs.view(np.uint8), os_.view(np.uint8))
 
 
 # every workload and format / scale combination, except the fp8 workload's

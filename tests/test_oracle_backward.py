@@ -75,6 +75,53 @@ def test_combine_backward_ties_round_to_even():
     assert gy[0, 3] == 0x3F82
 
 
+def tiny_product_case(seed=0):
+    """Weights and gradients whose products land below 2^-116, around the
+    bf16 subnormal range (2^-133 steps below 2^-126), with exact bf16
+    midpoints among them, plus a NaN weight and a NaN-making 0 * inf."""
+    rng = np.random.default_rng(seed)
+    T, H, k = 6, 64, 2
+    gexp = rng.integers(-110, -90, (T, H))
+    g = bf16_bits_from_float32((rng.choice([-1.0, 1.0], (T, H)) * (1 + rng.integers(0, 128, (T, H)) / 128.0)
+                                * np.exp2(gexp)).astype(np.float32))
+    w = (rng.uniform(1, 2, (T, k)) * np.exp2(rng.integers(-40, -20, (T, k)))).astype(np.float32)
+    # the counterexample to an fp32 product-error test: w * g = 1.25 * 2^-132
+    # + 2^-155, a hair above a bf16 midpoint that fp32 cannot see
+    w[0, 0] = np.float32(1.25 * 2.0 ** -32 + 2.0 ** -55)
+    g[0, 0] = bf16_bits_from_float32(np.array([2.0 ** -100], np.float32))[0]
+    # an exact midpoint below 2^-126: 1.5 * 2^-133 -> ties to even (2^-132)
+    w[1, 0] = np.float32(1.5 * 2.0 ** -33)
+    g[1, 0] = bf16_bits_from_float32(np.array([2.0 ** -100], np.float32))[0]
+    w.view(np.uint32)[2, 1] = 0x7FFFFFFF           # a NaN whose high half is 0x7FFF
+    g[3, 5] = 0x7F80                               # +inf gradient
+    w[3, 0] = 0.0                                  # 0 * inf = NaN
+    slot = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    return g, w, slot
+
+
+def test_combine_backward_tiny_and_nan_products():
+    g, w, slot = tiny_product_case()
+    gy, _ = oracle.combine_backward(g, None, slot, w)
+    T, k = slot.shape
+    gf = float32_from_bf16_bits(g)
+    for t in range(T):
+        for j in range(k):
+            r = slot[t, j]
+            for c in range(g.shape[1]):
+                wv, gv = float(w[t, j]), float(gf[t, c])
+                if np.isnan(wv) or (wv == 0 and np.isinf(gv)):
+                    assert gy[r, c] == 0x7FC0, (t, j, c)
+                elif np.isinf(gv):
+                    assert gy[r, c] == (0x7F80 if wv * gv > 0 else 0xFF80)
+                else:
+                    want = brute.bf16_round(Fraction(wv) * Fraction(gv))
+                    if wv * gv < 0 or (wv * gv == 0 and np.signbit(wv) != np.signbit(gv)):
+                        want |= 0x8000
+                    assert gy[r, c] == want, (t, j, c)
+    assert gy[0, 0] == 0x0003        # above the midpoint 2.5 * 2^-133
+    assert gy[2, 0] == 0x0002        # the midpoint 1.5 * 2^-133 goes to even
+
+
 def test_combine_backward_adjoint_identity():
     T, H, E, k = 64, 32, 8, 4
     inp = make_random_case(7, T, H, E, k, mask_frac=0.1)

@@ -94,6 +94,44 @@ def test_dispatch_quant_vs_bruteforce(fmt, mode):
                 np.testing.assert_array_equal(sc[r].view(np.uint8), bs.view(np.uint8))
 
 
+def _exact_pow2_exponent(amax: float, fmax: float) -> int:
+    """Smallest e with 2^e >= amax / fmax, by exact rational comparisons."""
+    from fractions import Fraction
+    r = Fraction(amax) / Fraction(fmax)
+    e = r.numerator.bit_length() - r.denominator.bit_length()
+    while Fraction(2) ** e < r:
+        e += 1
+    while Fraction(2) ** (e - 1) >= r:
+        e -= 1
+    return e
+
+
+@pytest.mark.parametrize("fmt,fmax", [("e4m3", 448.0), ("e5m2", 57344.0)])
+def test_pow2_exponent_every_bf16_amax(fmt, fmax):
+    # every finite positive bf16 magnitude as the amax of one block (the
+    # block is [amax, -amax, 0, ...]): the power-of-two scale is the exact
+    # smallest 2^e >= amax / fmax, so amax * 2^-e lies in (fmax / 2, fmax]
+    # and its code (rounding is monotone, fmax / 2 and fmax are codes)
+    # decodes to a value in [fmax / 2, fmax]: it never saturates; with UE8M0
+    # the exponent is the same clamped at -127
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    xb = np.zeros((bits.size, 128), np.uint16)
+    xb[:, 0] = bits
+    xb[:, 1] = bits | 0x8000
+    slot = np.arange(bits.size, dtype=np.int32)[:, None]
+    q, sc, _ = oracle.dispatch_quant(xb, slot, fmt=fmt, scale="pow2")
+    qb, sb, _ = oracle.dispatch_quant(xb, slot, fmt=fmt, scale="ue8m0")
+    amax = float32_from_bf16_bits(bits).astype(np.float64)
+    want = np.array([_exact_pow2_exponent(a, fmax) for a in amax])
+    got = np.frexp(sc[:, 0].astype(np.float64))[1] - 1
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(sb[:, 0].astype(np.int64), np.maximum(want, -127) + 127)
+    dec = oracle.e5m2_decode if fmt == "e5m2" else oracle.e4m3_decode
+    v = np.array([dec(int(c)) for c in q[:, 0]])
+    assert np.all((v >= fmax / 2) & (v <= fmax))
+    np.testing.assert_array_equal(q[:, 1], q[:, 0] | 0x80)
+
+
 def test_dispatch_quant_e4m3_fp32_is_dispatch_fp8():
     inp = make_inputs(WORKLOADS["fp8"], T=96)
     L = oracle.layout(inp.topk_idx, 256)
