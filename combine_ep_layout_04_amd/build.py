@@ -35,6 +35,8 @@ HIPCC_FLAGS = [
 ]
 
 
+PROBE_SRC = os.path.join(PKG, "probes", "write_pattern.hip")
+PROBE_LIB = os.path.join(PKG, "probes", "libep_probe.so")
 DEMO_SRC = os.path.join(PKG, "examples", "c_abi_demo.c")
 DEMO = os.path.join(PKG, "examples", "c_abi_demo")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -68,6 +70,20 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement kernels (probes/write_pattern.hip) into
+    probes/libep_probe.so, with the library's flags."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{CSRC}", "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on the probes:\n" + res.stdout + res.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build_demo(verbose: bool = False) -> str:
     """Compile the plain-C example (examples/c_abi_demo.c) with gcc against
     include/ep.h and libep.so: the C ABI used with no Python in the way."""
@@ -86,3 +102,4 @@ def build_demo(verbose: bool = False) -> str:
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build_demo(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

@@ -43,7 +43,7 @@ def short_name(name: str) -> str:
     name = name.strip()
     if name.startswith("void "):
         name = name[5:]
-    name = name.replace("ep::(anonymous namespace)::", "")
+    name = name.replace("ep::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     cut = name.find("(")
     if cut > 0 and not name.startswith("("):
         name = name[:cut]
