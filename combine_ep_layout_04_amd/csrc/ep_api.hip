@@ -10,6 +10,10 @@
 #include "ep.h"
 #include "ep_internal.h"
 
+static_assert(EP_LAYOUT_NOALLOC_SCRATCH_BYTES == ep::kLayoutScratchBytes,
+              "the header states the layout scratch size");
+static_assert(EP_MAX_EXPERTS == ep::kLayoutScratchExperts, "the scratch covers every expert count");
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -137,6 +141,28 @@ int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num
 {
     return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets, slot,
                         src, num_invalid, nullptr, workspace, workspace_bytes, stream);
+}
+
+int ep_layout_noalloc(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                      int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                      int32_t* num_invalid, void* stream)
+{
+    g_last_error[0] = '\0';
+    const size_t need = ep_layout_workspace_size(num_tokens, num_topk, num_experts);
+    if (need == 0)   // an invalid shape: ep_layout_ex names the argument, before any HIP call
+        return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets,
+                            slot, src, num_invalid, nullptr, nullptr, 0, stream);
+    const size_t have = ep::layout_scratch_bytes();
+    if (need > have)
+        return fail(EP_UNSUPPORTED,
+                    "ep_layout_noalloc: this shape needs %zu bytes of scratch, more than the %zu "
+                    "bytes the library holds per device",
+                    need, have);
+    void* scratch = nullptr;
+    const int st = from_hip(ep::layout_scratch(&scratch), "ep_layout_noalloc scratch address");
+    if (st) return st;
+    return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets, slot,
+                        src, num_invalid, nullptr, scratch, have, stream);
 }
 
 // scale_ld: 0, or a positive multiple of the 16-byte column alignment

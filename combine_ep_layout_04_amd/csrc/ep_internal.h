@@ -25,6 +25,16 @@ int64_t layout_chunk_pairs(int64_t pairs);
 int64_t layout_num_chunks(int64_t pairs);
 size_t layout_workspace_bytes(int64_t pairs, int num_experts);
 
+// The layout's fixed per-device scratch (the no-allocation entry point):
+// its size (every accepted shape: kLayoutMaxChunks chunks of
+// EP_MAX_EXPERTS counts plus a count per chunk), and its device address on
+// the current device.
+constexpr int kLayoutScratchExperts = 1024;   // EP_MAX_EXPERTS
+constexpr size_t kLayoutScratchBytes =
+    ((size_t)kLayoutMaxChunks * kLayoutScratchExperts + kLayoutMaxChunks) * sizeof(int32_t);
+size_t layout_scratch_bytes();
+hipError_t layout_scratch(void** ptr);
+
 hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
                          int num_experts, int alignment, int capacity, int32_t* counts,
                          int32_t* offsets, int32_t* slot, int32_t* src, int32_t* num_invalid,

@@ -46,6 +46,7 @@
 // redundant per-workgroup reads are 64 KiB from L2 each.
 
 #include <algorithm>
+#include <mutex>
 
 #include "ep_internal.h"
 
@@ -254,7 +255,17 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
     }
 }
 
+static_assert(kMaxExperts == kLayoutScratchExperts, "scratch sized for EP_MAX_EXPERTS");
+
 }  // namespace
+
+// Scratch of the no-allocation entry point: room for the largest histogram
+// any accepted layout needs (at most kLayoutMaxChunks chunks, a multiple of
+// 4, times EP_MAX_EXPERTS experts, plus one invalid-entry count per chunk).
+// Each device holds its own copy from the library's load until the process
+// ends.  Host code never passes this name to a kernel: on the host it only
+// names the symbol, whose device address hipGetSymbolAddress returns.
+static __device__ __align__(256) int32_t scratch[kLayoutScratchBytes / sizeof(int32_t)];
 
 static int64_t whole_batches(int64_t n)
 {
@@ -313,6 +324,30 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_to
                        topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C, alignment,
                        capacity, hist, bad, counts, offsets, slot, src, num_invalid, num_dropped);
     return hipGetLastError();
+}
+
+size_t layout_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of this device's scratch, looked up once per device (with
+// that device current) and kept.
+hipError_t layout_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace ep

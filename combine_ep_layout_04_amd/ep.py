@@ -45,7 +45,7 @@ EP_MAX_RANKS = 64
 
 # every symbol include/ep.h declares
 SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspace_size",
-           "ep_layout", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_dispatch_ex",
+           "ep_layout", "ep_layout_noalloc", "ep_layout_ex", "ep_layout_max_rows", "ep_dispatch", "ep_dispatch_ex",
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.ep_layout_workspace_size.restype = sz
         L.ep_layout.argtypes = [P, i64, i32, i32, P, P, P, P, P, P, sz, P]
         L.ep_layout.restype = i32
+        L.ep_layout_noalloc.argtypes = [P, i64, i32, i32, P, P, P, P, P, P]
+        L.ep_layout_noalloc.restype = i32
         L.ep_layout_ex.argtypes = [P, i64, i32, i32, i32, i64, P, P, P, P, P, P, P, sz, P]
         L.ep_layout_ex.restype = i32
         L.ep_layout_max_rows.argtypes = [i64, i32, i32, i32, i64]
@@ -227,6 +229,30 @@ def ep_layout(topk_idx: torch.Tensor, num_experts: int, *, alignment: int = 1, c
                                 _ptr(num_invalid), _ptr(num_dropped), _ptr(workspace),
                                 workspace.numel(), _stream(stream))
     _check(st, "ep_layout")
+    return counts, offsets, slot, src, num_invalid
+
+
+def ep_layout_noalloc(topk_idx: torch.Tensor, num_experts: int, counts: torch.Tensor,
+                      offsets: torch.Tensor, slot: torch.Tensor, src: Optional[torch.Tensor] = None,
+                      num_invalid: Optional[torch.Tensor] = None, stream=None):
+    """ep_layout with the library's fixed per-device scratch: no workspace,
+    and nothing allocated here or in the library (every output is the
+    caller's).  Outputs as ep_layout; returns them."""
+    _need(topk_idx, "topk_idx", torch.int64)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be 2-D [num_tokens, num_topk]")
+    T, k = topk_idx.shape
+    E = int(num_experts)
+    _need(counts, "counts", torch.int32, E)
+    _need(offsets, "offsets", torch.int32, E + 1)
+    _need(slot, "slot", torch.int32, T * k)
+    if src is not None:
+        _need(src, "src", torch.int32, T * k)
+    if num_invalid is not None:
+        _need(num_invalid, "num_invalid", torch.int32, 1)
+    st = lib().ep_layout_noalloc(_ptr(topk_idx), T, k, E, _ptr(counts), _ptr(offsets), _ptr(slot),
+                                 _ptr(src), _ptr(num_invalid), _stream(stream))
+    _check(st, "ep_layout_noalloc")
     return counts, offsets, slot, src, num_invalid
 
 

@@ -135,6 +135,30 @@ int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num
               int32_t *num_invalid, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ep_layout_noalloc -- ep_layout for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc): the scratch is a fixed array the library holds on each
+ * device (EP_LAYOUT_NOALLOC_SCRATCH_BYTES, its size, is enough for every
+ * shape ep_layout accepts: 256 chunks of EP_MAX_EXPERTS counts), so the
+ * call takes no workspace and allocates nothing.  The first call on a
+ * device looks up that device's array (hipGetSymbolAddress, with the
+ * device current); make it once before graph capture if the capture must
+ * hold launches only.
+ *
+ * Arguments, outputs and errors as ep_layout, minus the workspace; a shape
+ * whose scratch need exceeds the array returns EP_UNSUPPORTED (none that
+ * ep_layout accepts does).  Nothing in the scratch needs clearing: the
+ * first launch writes every entry the second reads.  All calls on one
+ * device share its array: calls that may overlap on one device (on
+ * different streams without ordering between them) race and must not be
+ * made; calls ordered on one stream are safe.
+ */
+#define EP_LAYOUT_NOALLOC_SCRATCH_BYTES ((size_t)(256 * 1024 + 256) * 4)
+int ep_layout_noalloc(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                      int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
+                      int32_t *num_invalid, void *stream);
+
+/*
  * ep_layout_ex -- ep_layout with the segment placements the pages' expanded
  * layouts offer.  ep_layout is ep_layout_ex(alignment 1, capacity 0).
  *

@@ -125,6 +125,33 @@ def test_layout_rejects(args, code):
 
 @no_gpu
 @pytest.mark.parametrize("args,code", [
+    # (topk_idx, T, k, E, counts, offsets, slot, src, invalid): invalid shapes
+    # are rejected before the library looks up its scratch
+    ((FAKE, 4, 2, 0, FAKE, FAKE, FAKE, None, None), 1),          # E < 1
+    ((FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, None, None), 1),       # E too large
+    ((FAKE, 4, 0, 8, FAKE, FAKE, FAKE, None, None), 1),          # k < 1
+    ((FAKE, -1, 2, 8, FAKE, FAKE, FAKE, None, None), 1),         # T < 0
+    ((FAKE, 1 << 28, 8, 8, FAKE, FAKE, FAKE, None, None), 2),    # pairs >= 2^31
+])
+def test_layout_noalloc_rejects(args, code):
+    st = ep.lib().ep_layout_noalloc(*args, None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_layout_noalloc_scratch_covers_every_accepted_shape():
+    # the fixed scratch equals the largest workspace ep_layout can ask for:
+    # 256 chunks (the most the layout cuts) of EP_MAX_EXPERTS counts
+    L = ep.lib()
+    biggest = max(L.ep_layout_workspace_size(T, k, ep.EP_MAX_EXPERTS)
+                  for T, k in ((1 << 20, 8), ((1 << 31) // 64 - 1, 64), (1 << 26, 16)))
+    assert biggest == (256 * 1024 + 256) * 4
+    header = open(HEADER).read()
+    assert "#define EP_LAYOUT_NOALLOC_SCRATCH_BYTES ((size_t)(256 * 1024 + 256) * 4)" in header
+
+
+@no_gpu
+@pytest.mark.parametrize("args,code", [
     # (x, T, H, k, slot, w, out_dtype, recv_x, recv_scales, recv_w)
     ((FAKE, 4, 7, 2, FAKE, None, 0, FAKE, None, None), 1),          # H % 8
     ((FAKE, 4, 0, 2, FAKE, None, 0, FAKE, None, None), 1),          # H < 1

@@ -1,0 +1,115 @@
+"""ep_layout_noalloc (the layout with the library's fixed per-device
+scratch) against ep_layout with a caller workspace, through the C ABI, bit
+for bit: counts, offsets, slot, src and num_invalid, on consecutive calls
+whose second input is smaller than the first (the scratch keeps the first
+call's contents), and on the largest shape the scratch is sized for."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from combine_ep_layout_04_amd import ep
+from combine_ep_layout_04_amd.inputs import WORKLOADS, make_inputs
+
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def routing(T, k, E, seed, invalid=0.0, masked=0.0):
+    rng = np.random.default_rng(seed)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int64) if k <= E else \
+        rng.integers(0, E, (T, k)).astype(np.int64)
+    flat = idx.reshape(-1)
+    if masked:
+        flat[rng.random(flat.size) < masked] = -1
+    if invalid:
+        pick = rng.random(flat.size) < invalid
+        flat[pick] = rng.choice([E, E + 5, -2, -100], int(pick.sum()))
+    return idx
+
+
+def run_both(idx_np, E, stream):
+    T, k = idx_np.shape
+    L = ep.lib()
+    idx = torch.from_numpy(idx_np).to(DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    out = {}
+    for name in ("ref", "noalloc"):
+        counts = torch.full((E,), -7, **i32)
+        offsets = torch.full((E + 1,), -7, **i32)
+        slot = torch.full((max(T * k, 1),), -7, **i32)
+        src = torch.full((max(T * k, 1),), -7, **i32)
+        inval = torch.full((1,), -7, **i32)
+        if name == "ref":
+            wsb = L.ep_layout_workspace_size(T, k, E)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+            st = L.ep_layout(idx.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                             slot.data_ptr(), src.data_ptr(), inval.data_ptr(), ws.data_ptr(),
+                             ws.numel(), ctypes.c_void_p(stream.cuda_stream))
+        else:
+            st = L.ep_layout_noalloc(idx.data_ptr(), T, k, E, counts.data_ptr(), offsets.data_ptr(),
+                                     slot.data_ptr(), src.data_ptr(), inval.data_ptr(),
+                                     ctypes.c_void_p(stream.cuda_stream))
+        assert st == 0, f"{name}: {ep.status_string(st)}: {ep.last_error()}"
+        out[name] = (counts, offsets, slot, src, inval)
+    stream.synchronize()
+    return {n: [t.cpu().numpy() for t in v] for n, v in out.items()}
+
+
+def check(idx_np, E, stream):
+    r = run_both(idx_np, E, stream)
+    names = ("counts", "offsets", "slot", "src", "num_invalid")
+    for name, a, b in zip(names, r["ref"], r["noalloc"]):
+        np.testing.assert_array_equal(b, a, err_msg=name)
+    n = int(r["ref"][1][E])
+    assert n == int((r["ref"][2] >= 0).sum())
+
+
+SHAPES = [
+    # (T, k, E): the headline, then smaller ones
+    (8192, 8, 256),
+    (4096, 4, 64),
+    (128, 2, 8),
+]
+
+
+def test_noalloc_two_calls_second_smaller():
+    stream = torch.cuda.Stream(device=DEV)
+    print("\n[no-alloc] headline then tiny", flush=True)
+    w = WORKLOADS["headline"]
+    check(make_inputs(w).topk_idx, w.E, stream)
+    w = WORKLOADS["tiny"]
+    check(make_inputs(w).topk_idx, w.E, stream)
+
+
+@pytest.mark.parametrize("order", ["large_first", "small_first"])
+def test_noalloc_sequences(order):
+    stream = torch.cuda.Stream(device=DEV)
+    shapes = SHAPES if order == "large_first" else SHAPES[::-1]
+    for i, (T, k, E) in enumerate(shapes):
+        print(f"\n[no-alloc] {order} T={T} k={k} E={E}", flush=True)
+        check(routing(T, k, E, seed=10 + i, invalid=0.01, masked=0.05), E, stream)
+
+
+def test_noalloc_largest_scratch_then_smaller():
+    # 256 chunks of 1024 experts: the whole scratch; then a smaller call
+    stream = torch.cuda.Stream(device=DEV)
+    print("\n[no-alloc] T=65536 k=8 E=1024, then T=1000 k=3 E=1024", flush=True)
+    check(routing(65536, 8, 1024, seed=3, invalid=0.001, masked=0.02), 1024, stream)
+    check(routing(1000, 3, 1024, seed=4, masked=0.1), 1024, stream)
+
+
+def test_noalloc_empty_input():
+    stream = torch.cuda.Stream(device=DEV)
+    check(np.zeros((0, 4), np.int64), 16, stream)
+
+
+def test_noalloc_rejects_bad_arguments():
+    L = ep.lib()
+    st = L.ep_layout_noalloc(None, 16, 2, 0, None, None, None, None, None, None)
+    assert st == ep.EP_INVALID_ARGUMENT
+    st = L.ep_layout_noalloc(None, 16, 2, 2048, None, None, None, None, None, None)
+    assert st != 0
