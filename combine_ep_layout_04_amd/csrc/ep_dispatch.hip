@@ -25,7 +25,7 @@
 //     then readlane), so the loop over destinations has no divergence;
 //   - fp8: each lane owns 16 channels (a "unit": two 16-byte loads in, one
 //     16-byte store out), so 8 aligned lanes hold one 128-channel block and
-//     amax is an 8-lane shuffle reduction.  With row-major scales and rows
+//     amax is an 8-lane reduction by DPP lane moves (no LDS traffic).  With row-major scales and rows
 //     of more than 64 units, one 128-lane workgroup per (token, tile of 128
 //     units, group of up to 4 slots; 8 on rows of at most 256 units), or
 //     64-lane tiles where the last 128-lane tile would be at most half
@@ -262,6 +262,38 @@ __device__ __forceinline__ uint32_t encode_any(float q)
 
 constexpr int kLanesPerBlock = 8;   // 16 channels per lane, 128 per block
 
+// DPP lane moves within a row of 16 lanes (gfx9 DPP control codes):
+// quad_perm [1,0,3,2] swaps neighbours, quad_perm [2,3,0,1] swaps pairs of a
+// quad, row_half_mirror reverses each group of 8 lanes.  Moved through the
+// data-parallel ALU instead of LDS (ds_bpermute).
+constexpr int kDppSwap1 = 0xB1;
+constexpr int kDppSwap2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum of v over each aligned group of 8 lanes, returned to all 8.  Max
+// is order-free, so swap-1, swap-2 and a mirror of the 8 lanes (which pairs
+// each quad with the other) reach every lane of the group.  All 8 lanes of
+// a group must be active together (they always take the same branch here).
+__device__ __forceinline__ uint32_t group8_max_u32(uint32_t v)
+{
+    v = max(v, dpp_move<kDppSwap1>(v));
+    v = max(v, dpp_move<kDppSwap2>(v));
+    return max(v, dpp_move<kDppHalfMirror>(v));
+}
+
+__device__ __forceinline__ float group8_max_f32(float v)
+{
+    v = fmaxf(v, __uint_as_float(dpp_move<kDppSwap1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_move<kDppSwap2>(__float_as_uint(v))));
+    return fmaxf(v, __uint_as_float(dpp_move<kDppHalfMirror>(__float_as_uint(v))));
+}
+
 // Smallest e with 2^e >= s (s > 0 finite): frexp gives s = m * 2^ex with
 // m in [0.5, 1); s is a power of two exactly when m == 0.5.
 __device__ __forceinline__ int ceil_log2(float s)
@@ -303,9 +335,7 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, ui
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = max(m, __float_as_uint(f[i]) & 0x7FFFFFFFu);
-#pragma unroll
-    for (int s = 1; s < kLanesPerBlock; s <<= 1)
-        m = max(m, (uint32_t)__shfl_xor((int)m, s, kLanesPerBlock));
+    m = group8_max_u32(m);
 
     const float fmax = max_finite<FMT>();
     uint32_t c[16];
@@ -340,9 +370,7 @@ __device__ __forceinline__ uint4 quantise16(const uint4& d0, const uint4& d1, ui
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-        for (int s = 1; s < kLanesPerBlock; s <<= 1)
-            amax = fmaxf(amax, __shfl_xor(amax, s, kLanesPerBlock));
+        amax = group8_max_f32(amax);
         const bool pow2 = SM != kScaleFp32 && amax > 0.0f && amax < __builtin_inff();
         int e = 0;
         float sc = amax / fmax;
@@ -447,9 +475,8 @@ void dispatch_fp8_kernel(const uint4* __restrict__ x, int nvec, int k,
 // is (token t, tile p of NL units = NL/8 scale blocks, slot group g of up to
 // CS slots), and all of a token's workgroups run back to back on one
 // XCD, so the pieces of a token's scale rows that different tiles write
-// meet in that XCD's L2.  Each lane casts one unit; lanes 0..7 of each
-// wavefront then hold that wavefront's 8 block scales and store them per
-// destination.  At T=8192, hidden 7168, k=8 this took 122 us against 126 us
+// meet in that XCD's L2.  Each lane casts one unit; the first lane of each
+// 8-lane block stores the block's scale per destination.  At T=8192, hidden 7168, k=8 this took 122 us against 126 us
 // for one wavefront per token; with tiles spread over the XCDs it took
 // 127 us.  Column-major scales (each a separate 4-byte store) measured
 // slower tiled, 163 us against 140 us, and keep one wavefront per token.
@@ -505,9 +532,12 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
     const uint4 d1 = load_row16<0>(xs, unit * 32 + 16);
     uint32_t sb;
     const uint4 code = quantise16<FMT, SM>(d0, d1, sb);
-    const uint32_t my_scale = (uint32_t)__shfl((int)sb, (lane & 7) * kLanesPerBlock, 64);
-    const int bk = p * (NL / kLanesPerBlock) + (tid >> 6) * 8 + lane;   // lanes 0..7
-    const bool scale_lane = lane < 8 && bk < nb;
+    // every lane of a block holds the block's scale; the block's first lane
+    // stores it, so lanes 0, 8, ..., 56 of a wavefront write its 8
+    // consecutive scales (no exchange between lanes)
+    const uint32_t my_scale = sb;
+    const int bk = unit / kLanesPerBlock;
+    const bool scale_lane = (lane & (kLanesPerBlock - 1)) == 0 && bk < nb;
 #pragma unroll
     for (int q = 0; q < CS; ++q) {
         if (r[q] < 0) continue;

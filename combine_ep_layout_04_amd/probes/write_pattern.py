@@ -8,7 +8,9 @@ on the headline workload (T=8192, hidden 7168, E=256, k=8), caches emptied
 Kernels: the library's ep_dispatch; stores_only (its grid, XCD order and
 slot map, no loads of x); write streams of the same bytes in destination
 order (2 KiB and 4 KiB one-shot workgroups, 14 KiB per workgroup in turn);
-a read of x; the dispatch in destination order (gather: x read k times)."""
+a read of x; the dispatch in destination order (gather: x read k times);
+and for the 8-bit cast, the library's E4M3 dispatch next to the same slot
+map stored at its code-row size and a stream of its code bytes."""
 
 import argparse
 import ctypes
@@ -62,6 +64,8 @@ def main():
         wsb = ep.layout_workspace_size(T, k, E)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         recv = torch.empty((P, H), dtype=torch.bfloat16, device=dev)
+        q8 = torch.empty((P, H), dtype=torch.uint8, device=dev)
+        s8 = torch.empty((P, H // 128), dtype=torch.float32, device=dev)
         sink = torch.zeros(4, **i32d)
         scratch = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
     st.synchronize()
@@ -82,9 +86,20 @@ def main():
         "read x": lambda: pr.probe_read_x(x.data_ptr(), T * H * 2, sink.data_ptr(), s),
         "gather (destination order)": lambda: pr.probe_gather(x.data_ptr(), H, n, src.data_ptr(),
                                                               recv.data_ptr(), s),
+        # the 8-bit cast writes rows of H code bytes (and H/128 scales): the
+        # same slot map stored at that row size, with no loads
+        "fp8 dispatch (library, E4M3, fp32 scales)": lambda: L.ep_dispatch(
+            x.data_ptr(), T, H, k, slot.data_ptr(), None, 1, q8.data_ptr(), s8.data_ptr(), None, s),
+        "stores_only at the fp8 code row size": lambda: pr.probe_stores_only(T, H // 2, k, slot.data_ptr(),
+                                                                             q8.data_ptr(), s),
+        "write stream of the fp8 code bytes, 2 KiB workgroups": lambda: pr.probe_write_stream(
+            q8.data_ptr(), n * H, 2, s),
     }
     algo = {"dispatch (library)": T * H * 2 + wbytes + P * 4, "read x": T * H * 2,
-            "gather (destination order)": T * H * 2 + wbytes + P * 4}
+            "gather (destination order)": T * H * 2 + wbytes + P * 4,
+            "fp8 dispatch (library, E4M3, fp32 scales)": T * H * 2 + n * H + n * (H // 128) * 4 + P * 4,
+            "stores_only at the fp8 code row size": n * H,
+            "write stream of the fp8 code bytes, 2 KiB workgroups": n * H}
 
     def flush():
         with torch.cuda.stream(st):
