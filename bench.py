@@ -168,13 +168,37 @@ def cpu_baseline(inp, inp_fp8, E, nbytes):
         oracle.dispatch_fp8(inp_fp8.x_bits, Lf.slot)
         ops["dispatch_fp8"].append(time.perf_counter() - t4)
     t = statistics.median(times)
+    # the same loops built with -fopenmp, token loops on all host cores
+    # (layout stays the single-thread stable pass)
+    ptimes, pops = [], {"dispatch_bf16": [], "combine": []}
+    for _ in range(CPU_RUNS):
+        t0 = time.perf_counter()
+        L = oracle.layout(inp.topk_idx, E)
+        t1 = time.perf_counter()
+        recv = oracle.dispatch_bf16_parallel(inp.x_bits, L.slot)
+        t2 = time.perf_counter()
+        oracle.combine_parallel(recv, L.slot, inp.topk_weights)
+        t3 = time.perf_counter()
+        ptimes.append(t3 - t0)
+        pops["dispatch_bf16"].append(t2 - t1)
+        pops["combine"].append(t3 - t2)
+        del recv
+    tp = statistics.median(ptimes)
+    threads = oracle.parallel_threads()
     return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "full headline workload (T=8192, H=7168, E=256, k=8): oracle layout + "
                       f"bf16 dispatch + fp64 combine, single thread, median of {CPU_RUNS} runs "
                       f"({t:.2f} s each; the fp8 dispatch timed alone in each run too)",
             "seconds_per_step": round(t, 3),
             "seconds_per_op": {k: round(statistics.median(v), 4) for k, v in ops.items()},
-            "host_cores_available": len(os.sched_getaffinity(0))}
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "openmp": {"value": round(nbytes / tp / 1e9, 3), "unit": "GB/s", "cores": threads,
+                       "kind": "oracle loops built with -fopenmp",
+                       "sample": "the same workload and step: single-thread layout, then the "
+                                 f"bf16 dispatch and fp64 combine token loops on {threads} "
+                                 f"threads, median of {CPU_RUNS} runs ({tp:.3f} s each)",
+                       "seconds_per_step": round(tp, 4),
+                       "seconds_per_op": {k: round(statistics.median(v), 4) for k, v in pops.items()}}}
 
 
 def main():
@@ -608,6 +632,11 @@ def main():
         }
         del c_recv, c_out, c_x
 
+    # the floor of this timing method: two events recorded back to back on the
+    # stream after the same flush, nothing between them (short launches'
+    # times include it)
+    event_floor_us = us(time_call(lambda: None, args.steps))
+
     # ---- context: a plain device-to-device copy of 1 GiB (read + write)
     with torch.cuda.stream(stream):
         c_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -718,6 +747,7 @@ def main():
         "cpu_baseline": cpu,
         "back_to_back": warm,
         "configs": configs,
+        "event_timing_floor_us": round(event_floor_us, 2),
     }
     print(json.dumps(rec), flush=True)
 

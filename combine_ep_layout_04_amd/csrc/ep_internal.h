@@ -21,6 +21,10 @@ constexpr int64_t kLayoutMinChunk = 1024;
 constexpr int64_t kLayoutSmallChunks = 64;
 constexpr int64_t kLayoutMaxChunks = 256;
 
+// Inputs of at most kLayoutSmallMaxPairs pairs (and at most 256 experts)
+// take a single launch instead of the two chunked ones.
+constexpr int64_t kLayoutSmallMaxPairs = 16384;
+
 int64_t layout_chunk_pairs(int64_t pairs);
 int64_t layout_num_chunks(int64_t pairs);
 size_t layout_workspace_bytes(int64_t pairs, int num_experts);

@@ -33,13 +33,72 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
+_LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
+
+
 def build(force: bool = True) -> str:
-    """Compile ``ep_oracle.c`` into ``liboracle.so`` with gcc."""
+    """Compile ``ep_oracle.c`` into ``liboracle.so`` with gcc (single
+    thread: the oracle), and the same source with -fopenmp into
+    ``liboracle_omp.so`` (the multi-core CPU baseline)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
+    if force or not os.path.exists(_LIB_OMP):
+        tmp = _LIB_OMP + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-fopenmp", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_OMP)
     return _LIB
+
+
+_lib_omp: Optional[ctypes.CDLL] = None
+
+
+def omp_lib() -> ctypes.CDLL:
+    """The -fopenmp build: oracle_dispatch_bf16 and oracle_combine run their
+    token loops on all host cores (the benchmark's multi-core baseline)."""
+    global _lib_omp
+    if _lib_omp is None:
+        if not os.path.exists(_LIB_OMP):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_OMP)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int
+        L.oracle_dispatch_bf16.argtypes = [P, i64, i32, i32, P, P, P, P]
+        L.oracle_dispatch_bf16.restype = None
+        L.oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+        L.oracle_combine.restype = None
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = i32
+        _lib_omp = L
+    return _lib_omp
+
+
+def dispatch_bf16_parallel(x_bits: np.ndarray, slot: np.ndarray, rows: Optional[int] = None) -> np.ndarray:
+    """oracle_dispatch_bf16 on all host cores (no weights); [rows, H] uint16."""
+    x = _c(x_bits, np.uint16)
+    s = _c(slot, np.int32)
+    T, H = x.shape
+    k = s.shape[1]
+    out = np.zeros((T * k if rows is None else int(rows), H), np.uint16)
+    omp_lib().oracle_dispatch_bf16(_ptr(x), T, H, k, _ptr(s), None, _ptr(out), None)
+    return out
+
+
+def combine_parallel(y_bits: np.ndarray, slot: np.ndarray, topk_weights: Optional[np.ndarray]) -> np.ndarray:
+    """oracle_combine on all host cores; [T, H] uint16."""
+    y = _c(y_bits, np.uint16)
+    s = _c(slot, np.int32)
+    T, k = s.shape
+    H = y.shape[1]
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    out = np.empty((T, H), np.uint16)
+    omp_lib().oracle_combine(_ptr(y), _ptr(s), _ptr(w), T, H, k, _ptr(out))
+    return out
+
+
+def parallel_threads() -> int:
+    return int(omp_lib().oracle_threads())
 
 
 _lib: Optional[ctypes.CDLL] = None

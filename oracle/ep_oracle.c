@@ -7,7 +7,10 @@
  * code, header, table or constant with the HIP library.
  *
  * Built with gcc, -O2 -ffp-contract=off, no fast-math, so every float
- * operation below is one IEEE-754 operation in the stated precision.
+ * operation below is one IEEE-754 operation in the stated precision.  The
+ * same source built with -fopenmp (liboracle_omp.so) runs the bf16 dispatch
+ * and combine token loops on all host cores: the benchmark's multi-core CPU
+ * baseline, with the same results (tokens write disjoint rows).
  *
  * What is computed, and the passages it follows:
  *
@@ -46,6 +49,9 @@
  */
 
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -280,6 +286,10 @@ void oracle_dispatch_bf16(const uint16_t *x, int64_t T, int H, int k,
                           const int32_t *slot, const float *topk_weights,
                           uint16_t *recv_x, float *recv_w)
 {
+    /* tokens write disjoint rows: the loop may run in parallel (only in the
+     * -fopenmp build that serves as the multi-core CPU baseline; the
+     * oracle itself is built without it and runs this loop in order) */
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t)
         for (int j = 0; j < k; ++j) {
             int32_t r = slot[t * k + j];
@@ -349,6 +359,8 @@ void oracle_dispatch_fp8(const uint16_t *x, int64_t T, int H, int k,
 void oracle_combine(const uint16_t *y, const int32_t *slot, const float *topk_weights,
                     int64_t T, int H, int k, uint16_t *out)
 {
+    /* each token's row is its own: parallel only in the -fopenmp build */
+#pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < T; ++t)
         for (int c = 0; c < H; ++c) {
             double acc = 0.0;
@@ -361,6 +373,23 @@ void oracle_combine(const uint16_t *y, const int32_t *slot, const float *topk_we
             }
             out[t * H + c] = oracle_bf16_from_double(acc);
         }
+}
+
+/* Threads the multi-core baseline build runs its parallel loops on (1 in the
+ * oracle's own build, which has no OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    int n = 0;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    return 1;
+#endif
 }
 
 /* ----------------------------------------------------------- backward -- */

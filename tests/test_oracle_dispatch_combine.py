@@ -232,3 +232,17 @@ def test_combine_unit_weights_all_masked_and_zero_tokens():
     out = oracle.combine(recv, L.slot, None)
     np.testing.assert_array_equal(out, brute.combine(recv, L.slot, None))
     assert not out[2].any()
+
+
+def test_openmp_build_matches_the_oracle():
+    # the multi-core CPU baseline runs the same dispatch and combine loops
+    # over tokens in parallel: its results must be the oracle's, bit for bit
+    from combine_ep_layout_04_amd.inputs import make_random_case
+    inp = make_random_case(91, 300, 256, 16, 4, mask_frac=0.2, dup_frac=0.5)
+    L = oracle.layout(inp.topk_idx, 16)
+    r1, _ = oracle.dispatch_bf16(inp.x_bits, L.slot)
+    r2 = oracle.dispatch_bf16_parallel(inp.x_bits, L.slot)
+    np.testing.assert_array_equal(r1, r2)
+    np.testing.assert_array_equal(oracle.combine(r1, L.slot, inp.topk_weights),
+                                  oracle.combine_parallel(r1, L.slot, inp.topk_weights))
+    assert oracle.parallel_threads() >= 1
