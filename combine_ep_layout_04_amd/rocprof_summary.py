@@ -3,6 +3,7 @@
     python -m combine_ep_layout_04_amd.rocprof_summary stats DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary pmc DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary counters DIR --cmd "..." > profiles/X.md
+    python -m combine_ep_layout_04_amd.rocprof_summary trace DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
         --cmd "..." --out profiles/hbm_traffic_headline.txt
 
@@ -80,9 +81,34 @@ def pmc(d: str):
     return out
 
 
+def trace(d: str):
+    """One row per (library kernel, grid size) from ``*_kernel_trace.csv``:
+    the median duration of its dispatches.  The grid size tells apart the
+    same kernel run on different workloads (e.g. the tiny, mid and headline
+    configs)."""
+    vals = defaultdict(list)
+    for f in _find(d, "kernel_trace.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = short_name(r["Kernel_Name"])
+                if not _library_kernel(name) or not name:
+                    continue
+                grid = int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+                wg = int(r["Workgroup_Size_X"])
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                vals[(name, grid // max(wg, 1), wg)].append(dur)
+    out = ["| kernel | workgroups | lanes per workgroup | dispatches | median (us) | min (us) |",
+           "|---|---|---|---|---|---|"]
+    for (name, wgs, wg), v in sorted(vals.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        out.append(f"| {name} | {wgs} | {wg} | {len(v)} | {statistics.median(v):.2f} | {min(v):.2f} |")
+    return out
+
+
 def _library_kernel(short: str) -> bool:
     """The library's own kernels (not torch's or the HIP runtime's)."""
-    return not short.startswith(("at::", "__amd_rocclr", "(anonymous namespace)::elementwise"))
+    return (not short.startswith(("at::", "__amd_rocclr", "(anonymous namespace)::elementwise",
+                                  "elementwise_kernel"))
+            and "at::native" not in short)
 
 
 def counters(d: str):
@@ -187,7 +213,7 @@ def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc", "counters", "traffic"])
+    ap.add_argument("kind", choices=["stats", "pmc", "counters", "traffic", "trace"])
     ap.add_argument("dir")
     ap.add_argument("dir2", nargs="?")
     ap.add_argument("--cmd", required=True, help="the command(s) that produced the data")
@@ -208,7 +234,7 @@ def main():
     lines = [f"# {a.title or a.kind}", "", "Command:", "", "```", a.cmd, "```", ""]
     if a.note:
         lines += [a.note, ""]
-    lines += {"stats": stats, "pmc": pmc, "counters": counters}[a.kind](a.dir)
+    lines += {"stats": stats, "pmc": pmc, "counters": counters, "trace": trace}[a.kind](a.dir)
     print("\n".join(lines))
 
 
