@@ -156,6 +156,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_ranked_prequant.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
                                                       P]
         L.oracle_dispatch_ranked_prequant.restype = None
+        L.oracle_dispatch_ranked_backward.argtypes = [P, P, P, i64, P, P, i64, i32, i32, i32, i32,
+                                                      P, P]
+        L.oracle_dispatch_ranked_backward.restype = None
         _lib = L
     return _lib
 
@@ -464,6 +467,45 @@ def combine_ranked(src_y, sparse_to_dense: np.ndarray) -> np.ndarray:
     out = np.zeros((T, H), np.uint16)
     lib().oracle_combine_ranked(_ptr_array(ys), _ptr(s2d), T, H, G, _ptr(out))
     return out
+
+
+def dispatch_ranked_backward(grad_recv_x, grad_recv_w, recv_topk_idx, topk_idx: np.ndarray,
+                             sparse_to_dense: np.ndarray, E: int):
+    """Backward of the once-per-rank dispatch for one sending rank.
+    ``grad_recv_x`` / ``grad_recv_w`` / ``recv_topk_idx``: lists of the G
+    receivers' row gradients (uint16 [rows, H], or None for no grad_x),
+    weight gradients (float32 [rows, k], or None for no grad_w) and listed
+    local experts (int64 [rows, k], from rank_layout with k_out = k).
+    Returns (grad_x uint16 [T, H] or None, grad_w float32 [T, k] or None)."""
+    idx = _c(topk_idx, np.int64)
+    s2d = _c(sparse_to_dense, np.int32)
+    T, k = idx.shape
+    G = s2d.shape[1]
+    if E % G:
+        raise ValueError("E must be a multiple of G")
+    rti = [_c(r, np.int64) for r in recv_topk_idx]
+    rows = rti[0].shape[0]
+    if len(rti) != G or any(r.shape != (rows, k) for r in rti):
+        raise ValueError("one [rows, k] recv_topk_idx per rank")
+    gx = gw = None
+    gxs = gws = None
+    H = 0
+    if grad_recv_x is not None:
+        gxs = [_c(g, np.uint16) for g in grad_recv_x]
+        H = gxs[0].shape[1]
+        for d in range(G):
+            if gxs[d].shape[0] != rows or (s2d.size and s2d[:, d].max() >= rows):
+                raise ValueError("row gradients must have the receive rows")
+        gx = np.zeros((T, H), np.uint16)
+    if grad_recv_w is not None:
+        gws = [_c(g, np.float32) for g in grad_recv_w]
+        if any(g.shape != (rows, k) for g in gws):
+            raise ValueError("weight gradients must be [rows, k]")
+        gw = np.zeros((T, k), np.float32)
+    lib().oracle_dispatch_ranked_backward(
+        None if gxs is None else _ptr_array(gxs), None if gws is None else _ptr_array(gws),
+        _ptr_array(rti), rows, _ptr(idx), _ptr(s2d), T, H, k, int(E), G, _ptr(gx), _ptr(gw))
+    return gx, gw
 
 
 def dispatch_fused_permute(src_x, src_idx, src_w, E: int, rank: int, recv_src: np.ndarray,

@@ -776,6 +776,64 @@ void oracle_combine_ranked(const uint16_t *const *src_y, const int32_t *sparse_t
 }
 
 /*
+ * Backward of the once-per-rank dispatch, for the sending rank's T tokens
+ * (NCCL EP page, ncclEpCombine high-throughput branch: the backward combine
+ * carries the tokens and the top-k weight gradients; each receiver turns its
+ * [rows, k] weight gradients dense, keyed by local_expert_routing_map, and
+ * the sender brings them back to [T, k] through its own rows of the routing
+ * map; DeepEP page, "MoE Dispatch and Combine for Training/Inference with
+ * ElasticBuffer": the backward of dispatch is a combine that also returns
+ * the reduced weight gradients):
+ *   grad_x[t] = the combine over ranks of the receivers' row gradients
+ *               (oracle_combine_ranked: fp64 sum over d, one rounding)
+ *   step 1, each receiver d: dense_d[row, e'] = grad_recv_w[d][row, n] for
+ *           the n-th listed local expert e' = recv_topk_idx[d][row, n] >= 0
+ *   step 2, the sender: grad_w[t, j] = dense_d[s2d[t, d], e - d*El] for
+ *           e = topk_idx[t, j] in [0, E) and d = e / El: every slot that
+ *           selected e gets the gradient of the weight sum it fed; 0 for a
+ *           masked or invalid slot, or a row outside [0, rows).
+ * Rows hold `rows` entries per receiver.  grad_x or grad_w may be NULL.
+ */
+void oracle_dispatch_ranked_backward(const uint16_t *const *grad_recv_x,
+                                     const float *const *grad_recv_w,
+                                     const int64_t *const *recv_topk_idx, int64_t rows,
+                                     const int64_t *topk_idx, const int32_t *sparse_to_dense,
+                                     int64_t T, int H, int k, int E, int G, uint16_t *grad_x,
+                                     float *grad_w)
+{
+    if (grad_x)
+        oracle_combine_ranked(grad_recv_x, sparse_to_dense, T, H, G, grad_x);
+    if (!grad_w)
+        return;
+    int El = E / G;
+    float **dense = (float **)malloc((size_t)G * sizeof(float *));
+    for (int d = 0; d < G; ++d) {
+        dense[d] = (float *)calloc((size_t)(rows * El > 0 ? rows * El : 1), sizeof(float));
+        for (int64_t row = 0; row < rows; ++row)
+            for (int n = 0; n < k; ++n) {
+                int64_t e = recv_topk_idx[d][row * k + n];
+                if (e >= 0 && e < El)
+                    dense[d][row * El + e] = grad_recv_w[d][row * k + n];
+            }
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            float g = 0.0f;
+            if (e >= 0 && e < E) {
+                int d = (int)(e / El);
+                int32_t row = sparse_to_dense[t * G + d];
+                if (row >= 0 && row < rows)
+                    g = dense[d][(int64_t)row * El + (e - (int64_t)d * El)];
+            }
+            grad_w[t * k + j] = g;
+        }
+    for (int d = 0; d < G; ++d)
+        free(dense[d]);
+    free(dense);
+}
+
+/*
  * Receive-side dispatch with the permute fused in (NeMo fused_a2a page,
  * HybridEPDispatch: fuse_permute, and the dispatched rows come out grouped
  * by local expert; NCCL EP page, sparse_to_dense_map and

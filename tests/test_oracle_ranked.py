@@ -362,3 +362,94 @@ def test_dispatch_ranked_prequant(seed, G, E, k):
         np.testing.assert_array_equal(dq[d], want_q)
         np.testing.assert_array_equal(ds[d], want_s)
         np.testing.assert_array_equal(dw[d], dw_ref[d])
+
+
+# ---- backward of the once-per-rank dispatch (weight gradients back to [T, k])
+
+def ranked_world(seed, G, T, E, k, dup=0.0, mask=0.2, invalid=0.0):
+    cases = global_case(seed, T, E, G, k, mask=mask, dup=dup, invalid=invalid)
+    gmap = np.concatenate([oracle.routing_map(c.topk_idx, E)[0] for c in cases])
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    return cases, L
+
+
+def test_ranked_backward_handworked():
+    (c,) = read_cases("ranked_handworked.txt")
+    G, T, E, k = c["G"][0], c["T"][0], c["E"][0], c["k"][0]
+    idx = [np.array(c[f"idx_r{r}"], np.int64).reshape(T, k) for r in range(G)]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = [oracle.rank_layout(gmap, T, E, G, r, k) for r in range(G)]
+    gws = [np.array(c[f"gw_recv_{d}"], np.float32).reshape(G * T, k) for d in range(G)]
+    for r in range(G):
+        _, gw = oracle.dispatch_ranked_backward(None, gws, [L[d].recv_topk_idx for d in range(G)],
+                                                idx[r], L[r].sparse_to_dense, E)
+        np.testing.assert_array_equal(gw.ravel(), np.array(c[f"grad_w_r{r}"], np.float32))
+
+
+@pytest.mark.parametrize("seed,G,E,k,dup,invalid", [
+    (0, 2, 8, 3, 0.0, 0.0), (1, 4, 16, 4, 1.0, 0.05), (2, 8, 64, 8, 0.5, 0.0),
+    (3, 3, 9, 5, 1.0, 0.1), (4, 1, 4, 2, 0.0, 0.0), (5, 8, 256, 8, 0.0, 0.02),
+])
+def test_ranked_backward_is_the_adjoint_of_the_weight_rows(seed, G, E, k, dup, invalid):
+    # <dispatch_w(w), G> = <w, backward(G)>: the forward weight rows (already
+    # pinned) against the weight gradients, every value a small integer so
+    # every fp32 sum is exact and the two sides are equal in fp64
+    T = 19
+    cases, L = ranked_world(seed, G, T, E, k, dup=dup, invalid=invalid)
+    rng = np.random.default_rng(seed)
+    rows = G * T
+    gws = [rng.integers(-8, 9, (rows, k)).astype(np.float32) for _ in range(G)]
+    rti = [L[d].recv_topk_idx for d in range(G)]
+    for r in range(G):
+        idx = cases[r].topk_idx
+        w = rng.integers(0, 9, (T, k)).astype(np.float32)
+        _, dw = oracle.dispatch_ranked(cases[r].x_bits, idx, w, E, G, L[r].sparse_to_dense, rows)
+        _, gw = oracle.dispatch_ranked_backward(None, gws, rti, idx, L[r].sparse_to_dense, E)
+        lhs = sum(float((dw[d].astype(np.float64) * gws[d]).sum()) for d in range(G))
+        rhs = float((w.astype(np.float64) * gw).sum())
+        assert lhs == rhs, (r, lhs, rhs)
+        masked = (idx < 0) | (idx >= E)
+        assert np.all(gw[masked] == 0)
+
+
+@pytest.mark.parametrize("seed,G,T,E,k", [(21, 4, 30, 16, 4), (22, 8, 17, 64, 8), (23, 2, 11, 6, 3)])
+def test_ranked_backward_matches_expanded_weight_gather(seed, G, T, E, k):
+    # distinct experts per token: the per-rank path and the expanded path
+    # carry the same per-(token, expert) weights, so with receiver gradients
+    # g(token, expert) from one table, the sender's gradients must equal the
+    # expanded dispatch backward's gather of the same table (already pinned)
+    cases, L = ranked_world(seed, G, T, E, k, dup=0.0)
+    El = E // G
+    rng = np.random.default_rng(seed)
+    table = rng.standard_normal((G * T, E)).astype(np.float32)
+    gws = []
+    for d in range(G):
+        gw = np.full((G * T, k), 123.0, np.float32)   # entries nothing lists are ignored
+        for i in range(L[d].num_recv):
+            for n in range(k):
+                e = int(L[d].recv_topk_idx[i, n])
+                if e >= 0:
+                    gw[i, n] = table[L[d].recv_src[i], d * El + e]
+        gws.append(gw)
+    rti = [L[d].recv_topk_idx for d in range(G)]
+    for r in range(G):
+        idx = cases[r].topk_idx
+        _, got = oracle.dispatch_ranked_backward(None, gws, rti, idx, L[r].sparse_to_dense, E)
+        Lx = oracle.layout(idx, E)
+        row_w = np.zeros(T * k, np.float32)
+        t, j = np.nonzero(Lx.slot >= 0)
+        row_w[Lx.slot[t, j]] = table[r * T + t, idx[t, j]]
+        _, want = oracle.dispatch_backward(np.zeros((T * k, 8), np.uint16), row_w, Lx.slot, T)
+        np.testing.assert_array_equal(got, want)
+
+
+def test_ranked_backward_grad_x_is_the_combine_over_ranks():
+    G, T, E, k = 4, 13, 16, 4
+    cases, L = ranked_world(31, G, T, E, k, dup=1.0)
+    gxs = [make_gradient(G * T, 8, 40 + d) for d in range(G)]
+    rti = [L[d].recv_topk_idx for d in range(G)]
+    for r in range(G):
+        gx, gw = oracle.dispatch_ranked_backward(gxs, None, rti, cases[r].topk_idx,
+                                                 L[r].sparse_to_dense, E)
+        assert gw is None
+        np.testing.assert_array_equal(gx, oracle.combine_ranked(gxs, L[r].sparse_to_dense))
