@@ -120,6 +120,9 @@ def ranked_bytes_model(T, H, k, G, pairs):
         "dispatch_ranked": T * H * 2 + pairs * H * 2 + T * G * 4 + T * k * 12 + pairs * k * 4,
         # read each (token, rank) row once, write out, read sparse-to-dense
         "combine_ranked": pairs * H * 2 + T * H * 2 + T * G * 4,
+        # the same, plus topk_idx read, one weight gradient read and one
+        # written per slot
+        "dispatch_ranked_backward": pairs * H * 2 + T * H * 2 + T * G * 4 + T * k * 16,
     }
 
 
@@ -533,6 +536,16 @@ def main():
     stream.synchronize()
     n_t = (s2d_h >= 0).sum(dim=1).to(dev).view(T, 1).float()
     ranked_ok = bool(torch.equal(out_r, (x.float() * n_t).bfloat16()))
+    # the backward of the once-per-rank dispatch, with the rows and weight
+    # rows just dispatched standing in for their gradients: the token
+    # gradients are the combine over ranks, the weight gradients come back
+    # to [T, k]
+    with torch.cuda.stream(stream):
+        gtw_r = torch.empty((T, k), dtype=torch.float32, device=dev)
+    stream.synchronize()
+    rb_us = time_call(lambda: check(L.ep_dispatch_ranked_backward(
+        ctypes.addressof(xtab), ctypes.addressof(wtab), T, p["idx"], rq["s2d"], T, H, k, E, G,
+        out_r.data_ptr(), gtw_r.data_ptr(), s), "ep_dispatch_ranked_backward"), args.steps)
     rbm = ranked_bytes_model(T, H, k, G, pairs)
     del dest
 
@@ -687,6 +700,8 @@ def main():
         "dispatch_ranked": entry(dr_us, bytes=rbm["dispatch_ranked"], ranks=G,
                                  rows_written=pairs, expanded_rows=n),
         "combine_ranked": entry(cr_us, bytes=rbm["combine_ranked"], ranks=G, rows_read=pairs),
+        "dispatch_ranked_backward": entry(rb_us, bytes=rbm["dispatch_ranked_backward"], ranks=G,
+                                          rows_read=pairs),
         "dispatch_ranked_prequantized": entry(drq_us, bytes=drq_bytes, ranks=G, rows_written=pairs),
         "dispatch_fused_permute": entry(fp_us, bytes=fp_bytes, ranks=G, tokens_received=n_recv,
                                         expert_rows_written=n_exp),

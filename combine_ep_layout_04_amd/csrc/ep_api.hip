@@ -572,4 +572,66 @@ int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
                     "ep_combine_ranked launch");
 }
 
+int ep_dispatch_ranked_backward(const void* const* grad_recv_x,
+                                const float* const* grad_recv_weights, int64_t src_rows,
+                                const int64_t* topk_idx, const int32_t* sparse_to_dense_map,
+                                int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                int num_ranks, void* grad_x, float* grad_topk_weights,
+                                void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    if (num_tokens * (int64_t)num_ranks >= ((int64_t)1 << 31))
+        return fail(EP_UNSUPPORTED, "num_tokens * num_ranks must be < 2^31");
+    if (src_rows < 0) return fail(EP_INVALID_ARGUMENT, "src_rows < 0");
+    if (!grad_recv_x && !grad_recv_weights)
+        return fail(EP_INVALID_ARGUMENT, "nothing to do: grad_recv_x and grad_recv_weights are NULL");
+    if ((grad_recv_x != nullptr) != (grad_x != nullptr))
+        return fail(EP_INVALID_ARGUMENT, "grad_recv_x and grad_x go together");
+    if ((grad_recv_weights != nullptr) != (grad_topk_weights != nullptr))
+        return fail(EP_INVALID_ARGUMENT, "grad_recv_weights and grad_topk_weights go together");
+    ep::RankPtrs px = {}, pw = {};
+    if (grad_recv_x) {
+        st = check_hidden(hidden, 8);
+        if (st) return st;
+        for (int d = 0; d < num_ranks; ++d) {
+            if (!grad_recv_x[d] || !aligned16(grad_recv_x[d]))
+                return fail(EP_INVALID_ARGUMENT, "grad_recv_x[%d] must be non-NULL and 16-byte aligned",
+                            d);
+            px.p[d] = const_cast<void*>(grad_recv_x[d]);
+        }
+        if (num_tokens > 0 && !aligned16(grad_x))
+            return fail(EP_INVALID_ARGUMENT, "grad_x must be 16-byte aligned");
+    }
+    if (grad_recv_weights) {
+        for (int d = 0; d < num_ranks; ++d) {
+            if ((reinterpret_cast<uintptr_t>(grad_recv_weights[d]) & 3u))
+                return fail(EP_INVALID_ARGUMENT, "grad_recv_weights[%d] must be 4-byte aligned", d);
+            pw.p[d] = const_cast<float*>(grad_recv_weights[d]);
+        }
+        if (num_tokens > 0 && (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 7u)))
+            return fail(EP_INVALID_ARGUMENT, "grad_recv_weights needs an 8-byte aligned topk_idx");
+        if (num_tokens > 0 && (reinterpret_cast<uintptr_t>(grad_topk_weights) & 3u))
+            return fail(EP_INVALID_ARGUMENT, "grad_topk_weights must be 4-byte aligned");
+    }
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!sparse_to_dense_map) return fail(EP_INVALID_ARGUMENT, "sparse_to_dense_map is required");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (grad_recv_x) {
+        st = from_hip(ep::launch_combine_ranked(px, src_rows, sparse_to_dense_map, num_tokens,
+                                                hidden, num_ranks, grad_x, s),
+                      "ep_dispatch_ranked_backward launch (tokens)");
+        if (st) return st;
+    }
+    if (grad_recv_weights)
+        return from_hip(ep::launch_ranked_weight_grad(pw, src_rows, topk_idx, sparse_to_dense_map,
+                                                      num_tokens, num_topk, num_experts, num_ranks,
+                                                      grad_topk_weights, s),
+                        "ep_dispatch_ranked_backward launch (weights)");
+    return EP_SUCCESS;
+}
+
 }  // extern "C"

@@ -111,6 +111,13 @@ hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const 
                                  int64_t num_tokens, int hidden, int num_ranks, void* out,
                                  hipStream_t stream);
 
+// grad_topk_weights[t, j] from the receivers' [src_rows, num_topk] weight
+// gradients (backward of the once-per-rank dispatch).
+hipError_t launch_ranked_weight_grad(const RankPtrs& grad_w, int64_t src_rows,
+                                     const int64_t* topk_idx, const int32_t* s2d,
+                                     int64_t num_tokens, int num_topk, int num_experts,
+                                     int num_ranks, float* grad_topk_weights, hipStream_t stream);
+
 hipError_t launch_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
                                    const float* topk_weights, int64_t num_tokens, int hidden,
                                    int num_topk, void* grad_y, float* grad_topk_weights,

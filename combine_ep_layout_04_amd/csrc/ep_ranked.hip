@@ -1166,4 +1166,59 @@ hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const 
     return hipGetLastError();
 }
 
+// ---- backward of the once-per-rank dispatch: the weight gradients
+//
+// NCCL EP page, ncclEpCombine high-throughput branch (the backward combine
+// returns the top-k weight gradients: each receiver's [rows, k] gradients,
+// aligned with its recv_topk_idx, made dense over its local experts, then
+// brought back to [T, k] through the sender's routing rows).  Both steps are
+// fused on the sender's side: one lane per (token, slot) with expert e of
+// rank d = e / El reads receiver d's row sparse_to_dense[t, d] at position
+// n = the number of distinct experts of rank d the token selects below e,
+// which is where that receiver lists e.  Masked or invalid slots, and rows
+// outside [0, src_rows), get 0.
+__global__ __launch_bounds__(256)
+void ranked_weight_grad_kernel(RankPtrs grad_w, int64_t src_rows, const int64_t* __restrict__ idx,
+                               const int32_t* __restrict__ s2d, int64_t pairs, int k, int E,
+                               int G, float* __restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= pairs) return;
+    const int64_t t = i / k;
+    const int64_t e = idx[i];
+    float g = 0.0f;
+    if (e >= 0 && e < E) {
+        const int El = E / G;
+        const int d = (int)(e / El);
+        const int32_t row = s2d[t * G + d];
+        const float* src = static_cast<const float*>(grad_w.p[d]);
+        if (row >= 0 && row < src_rows && src != nullptr) {
+            const int64_t* ti = idx + t * k;
+            int n = 0;
+            for (int j = 0; j < k; ++j) {
+                const int64_t ej = ti[j];
+                if (ej < (int64_t)d * El || ej >= e) continue;
+                bool first = true;   // count each selected expert once
+                for (int q = 0; q < j; ++q) first = first && ti[q] != ej;
+                n += first;
+            }
+            g = src[(int64_t)row * k + n];
+        }
+    }
+    out[i] = g;
+}
+
+hipError_t launch_ranked_weight_grad(const RankPtrs& grad_w, int64_t src_rows,
+                                     const int64_t* topk_idx, const int32_t* s2d,
+                                     int64_t num_tokens, int num_topk, int num_experts,
+                                     int num_ranks, float* grad_topk_weights, hipStream_t stream)
+{
+    const int64_t pairs = num_tokens * num_topk;
+    if (pairs == 0) return hipSuccess;
+    hipLaunchKernelGGL(ranked_weight_grad_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0,
+                       stream, grad_w, src_rows, topk_idx, s2d, pairs, num_topk, num_experts,
+                       num_ranks, grad_topk_weights);
+    return hipGetLastError();
+}
+
 }  // namespace ep

@@ -49,7 +49,8 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
-           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked")
+           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked",
+           "ep_dispatch_ranked_backward")
 
 
 class EpError(RuntimeError):
@@ -114,6 +115,9 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_fused_permute.restype = i32
         L.ep_combine_ranked.argtypes = [P, i64, P, i64, i32, i32, P, P]
         L.ep_combine_ranked.restype = i32
+        L.ep_dispatch_ranked_backward.argtypes = [P, P, i64, P, P, i64, i32, i32, i32, i32, P, P,
+                                                  P]
+        L.ep_dispatch_ranked_backward.restype = i32
         _lib = L
     return _lib
 
@@ -720,6 +724,69 @@ def ep_combine_ranked(src_y, sparse_to_dense: torch.Tensor, *, out=None, stream=
                                  _stream(stream))
     _check(st, "ep_combine_ranked")
     return out
+
+
+def ep_dispatch_ranked_backward(sparse_to_dense: torch.Tensor, num_experts: int, *,
+                                grad_recv_x=None, grad_recv_weights=None,
+                                topk_idx: Optional[torch.Tensor] = None, grad_x=None,
+                                grad_topk_weights=None, stream=None):
+    """Backward of ep_dispatch_ranked for this rank's tokens.
+    ``grad_recv_x``: None or a list of G bf16 [rows, H] row gradients (gives
+    grad_x [T, H], the combine over ranks); ``grad_recv_weights``: None or a
+    list of G fp32 [rows, k] weight gradients (entries may be None; gives
+    grad_topk_weights [T, k], needs ``topk_idx``).  Rows at or past the
+    smallest buffer's rows read as 0.  Returns (grad_x, grad_topk_weights)."""
+    _need(sparse_to_dense, "sparse_to_dense", torch.int32)
+    if sparse_to_dense.dim() != 2:
+        raise ValueError("sparse_to_dense must be [T, G]")
+    T, G = sparse_to_dense.shape
+    dev = sparse_to_dense.device
+    rows = None
+    H = 0
+    k = 1
+    xtab = wtab = None
+    if grad_recv_x is not None:
+        if len(grad_recv_x) != G:
+            raise ValueError("one row-gradient buffer per rank")
+        for d, t in enumerate(grad_recv_x):
+            _need(t, f"grad_recv_x[{d}]", torch.bfloat16)
+            if t.dim() != 2 or (H and t.shape[1] != H):
+                raise ValueError("every grad_recv_x must be [rows, H] with the same H")
+            H = t.shape[1]
+        rows = min(int(t.shape[0]) for t in grad_recv_x)
+        if grad_x is None:
+            grad_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _need(grad_x, "grad_x", torch.bfloat16, T * H)
+        xtab = _ptr_table(grad_recv_x)
+    if grad_recv_weights is not None:
+        if topk_idx is None:
+            raise ValueError("grad_recv_weights needs topk_idx")
+        _need(topk_idx, "topk_idx", torch.int64, T)
+        k = topk_idx.shape[1]
+        if len(grad_recv_weights) != G:
+            raise ValueError("one weight-gradient buffer per rank")
+        wrows = []
+        for d, t in enumerate(grad_recv_weights):
+            if t is None:
+                continue
+            _need(t, f"grad_recv_weights[{d}]", torch.float32)
+            if t.dim() != 2 or t.shape[1] != k:
+                raise ValueError("every grad_recv_weights must be [rows, k]")
+            wrows.append(int(t.shape[0]))
+        if wrows:
+            rows = min(wrows + ([rows] if rows is not None else []))
+        if grad_topk_weights is None:
+            grad_topk_weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+        _need(grad_topk_weights, "grad_topk_weights", torch.float32, T * k)
+        wtab = _ptr_table(grad_recv_weights)
+    st = lib().ep_dispatch_ranked_backward(
+        None if xtab is None else xtab[1], None if wtab is None else wtab[1], rows or 0,
+        _ptr(topk_idx), _ptr(sparse_to_dense), T, H or 8, k, int(num_experts), G,
+        _ptr(grad_x) if xtab is not None else None,
+        _ptr(grad_topk_weights) if wtab is not None else None, _stream(stream))
+    _check(st, "ep_dispatch_ranked_backward")
+    return (grad_x if xtab is not None else None,
+            grad_topk_weights if wtab is not None else None)
 
 
 # ------------------------------------------------------ C-ABI names, 1:1 --

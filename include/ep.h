@@ -537,6 +537,48 @@ int ep_combine_ranked(const void *const *src_y, int64_t src_rows,
                       const int32_t *sparse_to_dense_map, int64_t num_tokens, int hidden,
                       int num_ranks, void *out, void *stream);
 
+/*
+ * ep_dispatch_ranked_backward -- backward of ep_dispatch_ranked for this
+ * rank's tokens: the row gradients come back as the combine over ranks and
+ * the receivers' weight gradients come back to [num_tokens, num_topk].
+ *
+ * Passages: NCCL EP page, ncclEpCombine high-throughput branch (the backward
+ * combine carries the tokens and the top-k weight gradients: each receiver's
+ * weight gradients are made dense keyed by local_expert_routing_map, then
+ * the sender brings them back to [T, k] through its rows of the routing
+ * map); DeepEP page, "MoE Dispatch and Combine for Training/Inference with
+ * ElasticBuffer" (the backward of dispatch is a combine that also reduces
+ * the weight gradients).
+ *
+ * In:  grad_recv_x        NULL, or HOST array of G device pointers: rank d's
+ *                         row gradients, bf16 [src_rows, hidden].
+ *      grad_recv_weights  NULL, or HOST array of G device pointers (an entry
+ *                         may be NULL: its gradients read as 0): fp32
+ *                         [src_rows, num_topk], entry n of a row the gradient
+ *                         of that row's weight for its n-th listed local
+ *                         expert (recv_topk_idx order, as ep_dispatch_ranked
+ *                         wrote dest_weights).
+ *      topk_idx           int64 [num_tokens, num_topk] (this rank's).
+ *      sparse_to_dense_map int32 [num_tokens, G] from ep_rank_layout.
+ * Out: grad_x             bf16 [num_tokens, hidden] (with grad_recv_x): as
+ *                         ep_combine_ranked of the row gradients.
+ *      grad_topk_weights  fp32 [num_tokens, num_topk] (with
+ *                         grad_recv_weights): for slot j with expert e of
+ *                         rank d = e / (E/G), the entry of receiver d's row
+ *                         sparse_to_dense_map[t, d] for e; every slot that
+ *                         selected e (duplicates included) gets it.  0 for a
+ *                         masked or invalid slot or a row outside
+ *                         [0, src_rows).
+ * At least one of the two pairs is given; hidden (with grad_recv_x) must be
+ * a positive multiple of 8, at most EP_MAX_HIDDEN.
+ */
+int ep_dispatch_ranked_backward(const void *const *grad_recv_x,
+                                const float *const *grad_recv_weights, int64_t src_rows,
+                                const int64_t *topk_idx, const int32_t *sparse_to_dense_map,
+                                int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                int num_ranks, void *grad_x, float *grad_topk_weights,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -340,12 +340,37 @@ def test_combine_ranked_rejects(over, code):
     assert ep.last_error()
 
 
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(G=65), 1), (dict(E=7), 1), (dict(rows=-1), 1), (dict(T=-1), 1),
+    (dict(k=0), 1), (dict(gx="none", gw="none"), 1), (dict(out_x=None), 1), (dict(out_w=None), 1),
+    (dict(gx=(FAKE, FAKE + 4)), 1), (dict(gx=(FAKE, None)), 1), (dict(H=20), 1),
+    (dict(gw=(FAKE, FAKE + 2)), 1), (dict(idx=None), 1), (dict(idx=FAKE + 4), 1),
+    (dict(out_x=FAKE + 8), 1), (dict(out_w=FAKE + 2), 1), (dict(s2d=None), 1),
+    (dict(T=1 << 28, G=8, gx=(FAKE,) * 8, gw=(FAKE,) * 8), 2),
+])
+def test_dispatch_ranked_backward_rejects(over, code):
+    a = dict(gx=(FAKE, FAKE), gw=(FAKE, FAKE), rows=16, idx=FAKE, s2d=FAKE, T=4, H=256, k=2, E=8,
+             G=2, out_x=FAKE, out_w=FAKE)
+    a.update(over)
+    gx = None if a["gx"] == "none" else _table(*a["gx"])
+    gw = None if a["gw"] == "none" else _table(*a["gw"])
+    st = ep.lib().ep_dispatch_ranked_backward(
+        None if gx is None else ctypes.addressof(gx), None if gw is None else ctypes.addressof(gw),
+        a["rows"], a["idx"], a["s2d"], a["T"], a["H"], a["k"], a["E"], a["G"], a["out_x"],
+        a["out_w"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
 def test_ranked_zero_tokens_are_noops():
     dx = _table(FAKE, FAKE)
     assert ep.lib().ep_dispatch_ranked(None, None, None, 0, 256, 2, 8, 2, None,
                                        ctypes.addressof(dx), None, 0, None) == 0
     assert ep.lib().ep_combine_ranked(ctypes.addressof(dx), 0, None, 0, 256, 2, None, None) == 0
     assert ep.lib().ep_routing_map(None, 0, 2, 8, None, None, None) == 0
+    assert ep.lib().ep_dispatch_ranked_backward(ctypes.addressof(dx), ctypes.addressof(dx), 0, None,
+                                                None, 0, 256, 2, 8, 2, FAKE, FAKE, None) == 0
     assert ep.last_error() == ""
 
 

@@ -142,6 +142,8 @@ def test_ranked_path_graph():
     dx = [torch.full((R, H), 0, dtype=torch.int16, device=DEV).view(torch.bfloat16) for _ in range(G)]
     dw = [torch.full((R, k), 0.0, dtype=torch.float32, device=DEV) for _ in range(G)]
     out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    gtw = torch.empty((T, k), dtype=torch.float32, device=DEV)
 
     def step():
         for r in range(G):
@@ -150,6 +152,10 @@ def test_ranked_path_graph():
         ep.ep_dispatch_ranked(x, lay.sparse_to_dense, dx, E, topk_idx=idx_d[me], topk_weights=w,
                               dest_weights=dw)
         ep.ep_combine_ranked(dx, lay.sparse_to_dense, out=out)
+        # the backward, with the dispatched rows and weights standing in for
+        # their gradients
+        ep.ep_dispatch_ranked_backward(lay.sparse_to_dense, E, grad_recv_x=dx, grad_recv_weights=dw,
+                                       topk_idx=idx_d[me], grad_x=gx, grad_topk_weights=gtw)
 
     step()
     torch.cuda.synchronize()
@@ -157,7 +163,7 @@ def test_ranked_path_graph():
     RL = oracle.rank_layout(gm, T, E, G, me, k)
     np.testing.assert_array_equal(host(lay.sparse_to_dense), RL.sparse_to_dense)
 
-    o = {"gmap": gmap, "num_invalid": inval, "out": out}
+    o = {"gmap": gmap, "num_invalid": inval, "out": out, "grad_x": gx, "grad_topk_weights": gtw}
     o.update({f"layout.{f}": getattr(lay, f) for f in ep.RankLayout.FIELDS})
     # destination rows this rank does not write keep their content: compare
     # only the written ones, through gathered copies after each replay

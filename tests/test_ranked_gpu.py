@@ -565,3 +565,80 @@ def test_ranked_path_at_max_hidden():
     check_fused_permute(xs, idx, ws, E, G, 1)
     ys = [make_gradient(G * T, H, 70 + d) for d in range(G)]
     check_combine(ys, L.sparse_to_dense)
+
+
+# ---- backward of the once-per-rank dispatch
+
+def check_ranked_backward(idx_all, E, G, T, H, r, seed, want_x=True, clip_rows=None, none_rank=None):
+    """Sender r's backward: grad_topk_weights bit-exact against the oracle's
+    two-step definition (receivers' listed experts from the oracle's rank
+    layouts), grad_x within the combine-over-ranks tolerance.  Every
+    receiver buffer holds R rows: the rows sender r's tokens occupy (or
+    ``clip_rows`` fewer, which then read as 0)."""
+    k = idx_all[0].shape[1]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx_all])
+    L = [oracle.rank_layout(gmap, T, E, G, d, k) for d in range(G)]
+    s2d = L[r].sparse_to_dense
+    R = max(int(s2d.max()) + 1, 1) if s2d.size else 1
+    if clip_rows is not None:
+        R = min(R, clip_rows)
+    rng = np.random.default_rng(seed)
+    gws = [(rng.standard_normal((R, k)) * np.exp2(rng.integers(-8, 8, (R, k)))).astype(np.float32)
+           for _ in range(G)]
+    gxs = [make_gradient(R, H, seed + d) for d in range(G)] if want_x else None
+    gws_dev = [dev(g) for g in gws]
+    if none_rank is not None:
+        gws_dev[none_rank] = None
+    gw_out = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    gx_out = torch.full((T, H), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16) if want_x else None
+    ep.ep_dispatch_ranked_backward(
+        dev(s2d), E, grad_recv_x=None if gxs is None else [x_dev(g) for g in gxs],
+        grad_recv_weights=gws_dev, topk_idx=dev(idx_all[r]), grad_x=gx_out, grad_topk_weights=gw_out)
+    torch.cuda.synchronize()
+    # the oracle on all G*T receive rows: rows past R (and a missing rank's
+    # gradients) are 0, as the kernel reads them
+    s_eff = np.where(s2d < R, s2d, -1)
+    gws_ref = [np.zeros((G * T, k), np.float32) for _ in range(G)]
+    for d in range(G):
+        if d != none_rank:
+            gws_ref[d][:R] = gws[d]
+    rti = [L[d].recv_topk_idx for d in range(G)]
+    _, ref_w = oracle.dispatch_ranked_backward(None, gws_ref, rti, idx_all[r], s_eff, E)
+    np.testing.assert_array_equal(host(gw_out), ref_w)
+    if want_x:
+        ref_x = oracle.combine_ranked(gxs, s_eff)
+        got = float32_from_bf16_bits(bf16_bits(gx_out)).astype(np.float64)
+        want = float32_from_bf16_bits(ref_x).astype(np.float64)
+        bad = np.abs(got - want) > combine_tol(gxs, s_eff, ref_x)
+        assert not bad.any(), f"grad_x: {int(bad.sum())} elements off"
+
+
+@pytest.mark.parametrize("G,T,H,E,k,dup", [
+    (1, 9, 8, 4, 2, 0.0), (2, 50, 24, 8, 3, 1.0), (4, 300, 256, 32, 4, 0.5),
+    (8, 200, 1536, 64, 8, 0.0), (3, 77, 40, 9, 5, 1.0), (8, 64, 32, 1024, 64, 0.5),
+    (64, 16, 16, 64, 2, 0.0), (64, 20, 24, 256, 8, 1.0),
+])
+def test_dispatch_ranked_backward_small(G, T, H, E, k, dup):
+    cases = rank_cases(G * 7 + T, G, T, 8, E, k, mask_frac=0.15, dup_frac=dup, invalid_frac=0.03)
+    idx = [c.topk_idx for c in cases]
+    for r in sorted({0, G - 1}):
+        print(f"\n[ranked] dispatch backward G={G} T={T} H={H} E={E} k={k} rank {r}", flush=True)
+        check_ranked_backward(idx, E, G, T, H, r, seed=G + T + r)
+
+
+def test_dispatch_ranked_backward_clips_rows_and_missing_rank():
+    G, T, E, k = 4, 120, 16, 4
+    cases = rank_cases(5, G, T, 8, E, k, mask_frac=0.1, dup_frac=0.5)
+    idx = [c.topk_idx for c in cases]
+    print("\n[ranked] dispatch backward, clipped rows and a NULL rank", flush=True)
+    check_ranked_backward(idx, E, G, T, 64, 1, seed=9, clip_rows=T // 3, none_rank=2)
+    check_ranked_backward(idx, E, G, T, 64, 2, seed=10, want_x=False)
+
+
+def test_dispatch_ranked_backward_headline():
+    w = WORKLOADS["headline"]
+    G = 8
+    idx = headline_global_map(G)
+    idx[0] = make_inputs(w).topk_idx
+    print("\n[ranked] dispatch backward headline G=8 (T=8192, H=7168)", flush=True)
+    check_ranked_backward(idx, w.E, G, w.T, w.H, 0, seed=300)
