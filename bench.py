@@ -480,6 +480,19 @@ def main():
         variants[name] = time_call(lambda: check(L.ep_dispatch_ex(
             xf.data_ptr(), T, H, k, slotf.data_ptr(), None, fmt, mode, q.data_ptr(),
             sbuf.data_ptr(), None, ld, s), "ep_dispatch_ex"), args.steps)
+    # the same column-major scales in two passes (codes and per-token scales
+    # through a workspace, then the columns one receive row per lane)
+    with torch.cuda.stream(stream):
+        srcf = torch.empty(P, dtype=torch.int32, device=dev)
+        cm_ws_bytes = L.ep_dispatch_colmajor_workspace_size(T, H, 0)
+        cm_ws = torch.empty(cm_ws_bytes, dtype=torch.uint8, device=dev)
+    stream.synchronize()
+    check(L.ep_layout(idxf.data_ptr(), T, k, E, p["counts"], p["offsets"], slotf.data_ptr(),
+                      srcf.data_ptr(), None, p["ws"], ws_bytes, s), "ep_layout")
+    variants["e4m3_fp32_colmajor_two_pass"] = time_call(lambda: check(L.ep_dispatch_colmajor_scales(
+        xf.data_ptr(), T, H, k, slotf.data_ptr(), srcf.data_ptr(), None, 1, 0, q.data_ptr(),
+        sc.data_ptr(), None, P, P, cm_ws.data_ptr(), cm_ws_bytes, s), "ep_dispatch_colmajor_scales"),
+        args.steps)
     variants["prequantized"] = time_call(lambda: check(L.ep_dispatch_prequantized(
         xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
         sc.data_ptr(), None, 0, s), "ep_dispatch_prequantized"), args.steps)

@@ -219,6 +219,63 @@ int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
                     "ep_dispatch (bf16) launch");
 }
 
+size_t ep_dispatch_colmajor_workspace_size(int64_t num_tokens, int hidden, int scale_format)
+{
+    if (num_tokens < 0 || hidden < 128 || hidden > EP_MAX_HIDDEN || hidden % 128 != 0 ||
+        (scale_format != EP_SCALE_FP32 && scale_format != EP_SCALE_FP32_POW2 &&
+         scale_format != EP_SCALE_UE8M0))
+        return 0;
+    return ep::colmajor_workspace_bytes(num_tokens, hidden, scale_format);
+}
+
+int ep_dispatch_colmajor_scales(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                                const int32_t* slot, const int32_t* src, const float* topk_weights,
+                                int out_dtype, int scale_format, void* recv_x, void* recv_scales,
+                                float* recv_weights, int64_t scale_ld, int64_t num_rows,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    g_last_error[0] = '\0';
+    int st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    if (out_dtype != EP_OUT_FP8_E4M3 && out_dtype != EP_OUT_FP8_E5M2)
+        return fail(EP_INVALID_ARGUMENT, "out_dtype %d: column-major scales come with an 8-bit cast",
+                    out_dtype);
+    if (scale_format != EP_SCALE_FP32 && scale_format != EP_SCALE_FP32_POW2 &&
+        scale_format != EP_SCALE_UE8M0)
+        return fail(EP_INVALID_ARGUMENT, "unknown scale_format %d", scale_format);
+    st = check_hidden(hidden, 128);
+    if (st) return st;
+    if (scale_ld <= 0) return fail(EP_INVALID_ARGUMENT, "scale_ld must be positive (column-major)");
+    st = check_scale_ld(scale_ld, scale_format == EP_SCALE_UE8M0 ? 1 : 4);
+    if (st) return st;
+    if (num_rows < 0 || num_rows > INT32_MAX)
+        return fail(EP_INVALID_ARGUMENT, "num_rows %lld outside [0, 2^31-1] (slot entries are int32)",
+                    (long long)num_rows);
+    if (scale_ld < num_rows)
+        return fail(EP_INVALID_ARGUMENT, "scale_ld %lld is below num_rows %lld", (long long)scale_ld,
+                    (long long)num_rows);
+    const size_t need = ep_dispatch_colmajor_workspace_size(num_tokens, hidden, scale_format);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return fail(EP_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(EP_INVALID_ARGUMENT, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x || !slot || !src || !recv_x || !recv_scales)
+        return fail(EP_INVALID_ARGUMENT, "x, slot, src, recv_x and recv_scales are required");
+    if (!aligned16(x) || !aligned16(recv_x))
+        return fail(EP_INVALID_ARGUMENT, "x and recv_x must be 16-byte aligned");
+    if (scale_format != EP_SCALE_UE8M0 && (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "fp32 recv_scales must be 4-byte aligned");
+    if (recv_weights && !topk_weights)
+        return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
+    return from_hip(ep::launch_dispatch_fp8_colmajor(
+                        x, num_tokens, hidden, num_topk, slot, src, topk_weights,
+                        out_dtype == EP_OUT_FP8_E5M2 ? 1 : 0, scale_format, recv_x, recv_scales,
+                        recv_weights, scale_ld, num_rows, workspace,
+                        static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_colmajor_scales launch");
+}
+
 int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
                 const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
                 float* recv_scales, float* recv_weights, void* stream)

@@ -51,6 +51,8 @@
 //     4-byte scale stores interleaved with the code stores measured ~30%
 //     slower.
 
+#include <algorithm>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -501,7 +503,10 @@ constexpr int kCastSlotsLong = 4;
 constexpr int kCastSlotsShort = 8;
 constexpr int kCastLongUnits = 2 * kTileLanes;   // rows of more than this many units
 
-template <int FMT, int SM, int NL, int CS>
+// WS: instead of a scale row per destination, the token's scale row goes
+// once (from slot group 0) to a per-token workspace [T, nb], for the
+// column-major pass below.
+template <int FMT, int SM, int NL, int CS, bool WS = false>
 __global__ __launch_bounds__(NL)
 void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int tpr, int64_t T,
                               int groups, const int32_t* __restrict__ slot,
@@ -538,17 +543,134 @@ void dispatch_fp8_tile_kernel(const uint4* __restrict__ x, int nvec, int k, int 
     const uint32_t my_scale = sb;
     const int bk = unit / kLanesPerBlock;
     const bool scale_lane = (lane & (kLanesPerBlock - 1)) == 0 && bk < nb;
+    if (WS && g == 0 && scale_lane) {
+        const int64_t at = t * nb + bk;
+        if (SM == kScaleUe8m0)
+            static_cast<uint8_t*>(recv_s)[at] = (uint8_t)my_scale;
+        else
+            static_cast<uint32_t*>(recv_s)[at] = my_scale;
+    }
 #pragma unroll
     for (int q = 0; q < CS; ++q) {
         if (r[q] < 0) continue;
         if (unit < units)
             store_row16(buffer_rsrc(recv_q + (int64_t)r[q] * units, units * 16), unit * 16, code);
-        if (scale_lane) {
+        if (!WS && scale_lane) {
             const int64_t at = (int64_t)r[q] * nb + bk;
             if (SM == kScaleUe8m0)
                 static_cast<uint8_t*>(recv_s)[at] = (uint8_t)my_scale;
             else
                 static_cast<uint32_t*>(recv_s)[at] = my_scale;
+        }
+    }
+}
+
+// Column-major scales from the per-token workspace (DeepEP page, dispatch()
+// use_tma_aligned_col_major_sf: each block's scales contiguous over rows).
+// One lane per receive row r, so a wavefront writes 64 consecutive entries
+// of a block's column at a time; written one row at a time, a row's scales
+// would be nb separate 4-byte stores into nb lines.  t = src[r] is taken
+// only if one of t's slots is r, so rows nothing maps to (padding, dropped
+// pairs, rows past N) are skipped whatever src holds there.
+//
+// The pieces of a row (4 scales each when nb % 4 == 0: 16 bytes of fp32 or
+// 4 UE8M0 bytes) are split over gridDim.y workgroups, part blockIdx.y taking
+// pieces part, part + gridDim.y, ..., kColBatch of them loaded (clamped
+// indices, no branch between the loads) before their stores.  The kernel is
+// bound by its chain of dependent loads (src, then t's slot row, then the
+// scale row) rather than by its stores (14.7 MB at T=8192, hidden 7168,
+// k=8), so the slot row is read 16 bytes at a time when aligned (V4).
+// Measured there (device time): 11.6 us with 8 pieces per batch over 4
+// parts and 4-byte slot loads, 8.1 with 4 per batch and 16-byte slot loads,
+// 7.7 with 4 per batch over 2 parts; 1 part, or 8 per batch, 7.9-8.6.
+// Loading the first pieces together with the slot row, ahead of the check,
+// measured slower (10.3 us).
+constexpr int kColmajorParts = 2;   // workgroups per 256 rows
+constexpr int kColBatch = 4;        // pieces loaded before their stores
+
+template <int SM> struct ColPiece;          // 4 scales of one row
+template <> struct ColPiece<kScaleFp32> {
+    using V = uint4;
+    __device__ static void put(void* out, int64_t at, int64_t ld, V v) {
+        uint32_t* o = static_cast<uint32_t*>(out) + at;
+        o[0] = v.x; o[ld] = v.y; o[2 * ld] = v.z; o[3 * ld] = v.w;
+    }
+};
+template <> struct ColPiece<kScaleUe8m0> {
+    using V = uint32_t;
+    __device__ static void put(void* out, int64_t at, int64_t ld, V v) {
+        uint8_t* o = static_cast<uint8_t*>(out) + at;
+        o[0] = (uint8_t)v; o[ld] = (uint8_t)(v >> 8); o[2 * ld] = (uint8_t)(v >> 16);
+        o[3 * ld] = (uint8_t)(v >> 24);
+    }
+};
+
+// whether r is one of the k slots of the row at s (aligned to 16 bytes and
+// k % 4 == 0 when V4); every load is issued before the first comparison
+template <bool V4>
+__device__ __forceinline__ bool row_is_slot(const int32_t* __restrict__ s, int k, int64_t r)
+{
+    bool mine = false;
+    if (V4) {
+        const int4* s4 = reinterpret_cast<const int4*>(s);
+        const int n4 = k / 4;
+        for (int j0 = 0; j0 < n4; j0 += 2) {
+            int4 v[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) v[q] = s4[min(j0 + q, n4 - 1)];   // clamped: no branch
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                mine |= j0 + q < n4 && (v[q].x == r || v[q].y == r || v[q].z == r || v[q].w == r);
+        }
+    } else {
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = s[min(j0 + q, k - 1)];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) mine |= j0 + q < k && v[q] == r;
+        }
+    }
+    return mine;
+}
+
+template <int SM, bool V4>
+__global__ __launch_bounds__(256)
+void scales_colmajor_kernel(const void* __restrict__ ws, const int32_t* __restrict__ src,
+                            const int32_t* __restrict__ slot, int64_t T, int k, int nb,
+                            int64_t rows, void* __restrict__ scales, int64_t ld)
+{
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int part = blockIdx.y, parts = gridDim.y;
+    if (r >= rows) return;
+    const int32_t t = src[r];
+    if (t < 0 || t >= T) return;
+    if ((nb & 3) != 0) {       // one scale at a time
+        if (!row_is_slot<V4>(slot + (int64_t)t * k, k, r)) return;
+        for (int b = part; b < nb; b += parts) {
+            if (SM == kScaleUe8m0)
+                static_cast<uint8_t*>(scales)[(int64_t)b * ld + r] =
+                    static_cast<const uint8_t*>(ws)[(int64_t)t * nb + b];
+            else
+                static_cast<uint32_t*>(scales)[(int64_t)b * ld + r] =
+                    static_cast<const uint32_t*>(ws)[(int64_t)t * nb + b];
+        }
+        return;
+    }
+    using P = ColPiece<SM>;
+    using V = typename P::V;
+    const V* in = reinterpret_cast<const V*>(static_cast<const uint8_t*>(ws) +
+                                             (int64_t)t * nb * (SM == kScaleUe8m0 ? 1 : 4));
+    const int np = nb / 4;
+    if (!row_is_slot<V4>(slot + (int64_t)t * k, k, r)) return;
+    for (int c0 = part; c0 < np; c0 += kColBatch * parts) {
+        V v[kColBatch];
+#pragma unroll
+        for (int u = 0; u < kColBatch; ++u) v[u] = in[min(c0 + u * parts, np - 1)];   // clamped
+#pragma unroll
+        for (int u = 0; u < kColBatch; ++u) {
+            const int c = c0 + u * parts;
+            if (c < np) P::put(scales, (int64_t)4 * c * ld + r, ld, v[u]);
         }
     }
 }
@@ -788,6 +910,76 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
 #undef EP_FP8_MODE
 #undef EP_FP8_TILES
 #undef EP_FP8_LAUNCH
+    return hipGetLastError();
+}
+
+
+size_t colmajor_workspace_bytes(int64_t num_tokens, int hidden, int scale_mode)
+{
+    const size_t bytes = (size_t)num_tokens * (hidden / 128) * (scale_mode == kScaleUe8m0 ? 1 : 4);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_dispatch_fp8_colmajor(const void* x, int64_t num_tokens, int hidden,
+                                        int num_topk, const int32_t* slot, const int32_t* src,
+                                        const float* topk_weights, int format, int scale_mode,
+                                        void* recv_q, void* recv_scales, float* recv_weights,
+                                        int64_t scale_ld, int64_t rows, void* workspace,
+                                        hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const int units = hidden / 16;
+    const int nb = hidden / 128;
+    const bool narrow = narrow_tiles(units);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (units + lanes - 1) / lanes;
+    const int cs = units > kCastLongUnits ? kCastSlotsLong : kCastSlotsShort;
+    const int groups = (num_topk + cs - 1) / cs;
+    const int64_t blocks = (num_tokens + 7) / 8 * 8 * tpr * groups;
+    if (units <= 64 || blocks > INT32_MAX)   // short rows: the one-wavefront-per-token cast
+        return launch_dispatch_fp8(x, num_tokens, hidden, num_topk, slot, topk_weights, format,
+                                   scale_mode, recv_q, recv_scales, recv_weights, scale_ld, stream);
+    const uint4* xx = static_cast<const uint4*>(x);
+    uint4* qq = static_cast<uint4*>(recv_q);
+#define EP_CM_LAUNCH(F, M, NL, CS)                                                              \
+    hipLaunchKernelGGL((dispatch_fp8_tile_kernel<F, M, NL, CS, true>), dim3((unsigned)blocks),     \
+                       dim3(NL), 0, stream, xx, nvec, num_topk, tpr, num_tokens, groups, slot,    \
+                       topk_weights, qq, workspace, recv_weights)
+#define EP_CM_TILES(F, M)                                                                       \
+    {                                                                                           \
+        if (narrow && cs == kCastSlotsLong) EP_CM_LAUNCH(F, M, kTileLanes / 2, kCastSlotsLong);   \
+        else if (narrow) EP_CM_LAUNCH(F, M, kTileLanes / 2, kCastSlotsShort);                    \
+        else if (cs == kCastSlotsLong) EP_CM_LAUNCH(F, M, kTileLanes, kCastSlotsLong);           \
+        else EP_CM_LAUNCH(F, M, kTileLanes, kCastSlotsShort);                                    \
+    }
+    if (format == kE5M2) {
+        if (scale_mode == kScalePow2) EP_CM_TILES(kE5M2, kScalePow2)
+        else if (scale_mode == kScaleUe8m0) EP_CM_TILES(kE5M2, kScaleUe8m0)
+        else EP_CM_TILES(kE5M2, kScaleFp32)
+    } else {
+        if (scale_mode == kScalePow2) EP_CM_TILES(kE4M3, kScalePow2)
+        else if (scale_mode == kScaleUe8m0) EP_CM_TILES(kE4M3, kScaleUe8m0)
+        else EP_CM_TILES(kE4M3, kScaleFp32)
+    }
+#undef EP_CM_TILES
+#undef EP_CM_LAUNCH
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || rows == 0) return err;
+    const int pieces = (nb & 3) == 0 ? nb / 4 : nb;
+    const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)std::min(kColmajorParts, pieces));
+    const bool v4 = num_topk % 4 == 0 && (reinterpret_cast<uintptr_t>(slot) & 15) == 0;
+#define EP_CM_COLS(SM, V4)                                                                      \
+    hipLaunchKernelGGL((scales_colmajor_kernel<SM, V4>), grid, dim3(256), 0, stream, workspace,     \
+                       src, slot, num_tokens, num_topk, nb, rows, recv_scales, scale_ld)
+    if (scale_mode == kScaleUe8m0) {
+        if (v4) EP_CM_COLS(kScaleUe8m0, true);
+        else EP_CM_COLS(kScaleUe8m0, false);
+    } else {
+        if (v4) EP_CM_COLS(kScaleFp32, true);
+        else EP_CM_COLS(kScaleFp32, false);
+    }
+#undef EP_CM_COLS
     return hipGetLastError();
 }
 

@@ -57,6 +57,18 @@ hipError_t launch_dispatch_fp8(const void* x, int64_t num_tokens, int hidden, in
                                int scale_mode, void* recv_q, void* recv_scales,
                                float* recv_weights, int64_t scale_ld, hipStream_t stream);
 
+// The 8-bit cast with column-major scales in two passes: codes per slot
+// and each token's scale row once into `workspace` (colmajor_workspace_bytes),
+// then the scales written to [hidden/128, scale_ld] one receive row per lane
+// (src: the source token of each of the `rows` receive rows).
+size_t colmajor_workspace_bytes(int64_t num_tokens, int hidden, int scale_mode);
+hipError_t launch_dispatch_fp8_colmajor(const void* x, int64_t num_tokens, int hidden,
+                                        int num_topk, const int32_t* slot, const int32_t* src,
+                                        const float* topk_weights, int format, int scale_mode,
+                                        void* recv_q, void* recv_scales, float* recv_weights,
+                                        int64_t scale_ld, int64_t rows, void* workspace,
+                                        hipStream_t stream);
+
 hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num_tokens,
                                     int hidden, int num_topk, const int32_t* slot,
                                     const float* topk_weights, void* recv_q, float* recv_scales,

@@ -50,7 +50,8 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
            "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked",
-           "ep_dispatch_ranked_backward")
+           "ep_dispatch_ranked_backward", "ep_dispatch_colmajor_workspace_size",
+           "ep_dispatch_colmajor_scales")
 
 
 class EpError(RuntimeError):
@@ -91,6 +92,11 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch.restype = i32
         L.ep_dispatch_ex.argtypes = [P, i64, i32, i32, P, P, i32, i32, P, P, P, i64, P]
         L.ep_dispatch_ex.restype = i32
+        L.ep_dispatch_colmajor_workspace_size.argtypes = [i64, i32, i32]
+        L.ep_dispatch_colmajor_workspace_size.restype = sz
+        L.ep_dispatch_colmajor_scales.argtypes = [P, i64, i32, i32, P, P, P, i32, i32, P, P, P, i64,
+                                                  i64, P, sz, P]
+        L.ep_dispatch_colmajor_scales.restype = i32
         L.ep_dispatch_prequantized.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, P]
         L.ep_dispatch_prequantized.restype = i32
         L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
@@ -318,6 +324,60 @@ def ep_dispatch(x: torch.Tensor, slot: torch.Tensor, topk_weights: Optional[torc
                               _ptr(recv_scales), _ptr(recv_weights), int(scale_ld),
                               _stream(stream))
     _check(st, "ep_dispatch")
+    return recv_x, recv_scales, recv_weights
+
+
+def ep_dispatch_colmajor_workspace_size(num_tokens: int, hidden: int, scale: str = "fp32") -> int:
+    return int(lib().ep_dispatch_colmajor_workspace_size(int(num_tokens), int(hidden), _SCALES[scale]))
+
+
+def ep_dispatch_colmajor_scales(x: torch.Tensor, slot: torch.Tensor, src: torch.Tensor,
+                                topk_weights: Optional[torch.Tensor] = None, *, fmt: str = "e4m3",
+                                scale: str = "fp32", scale_ld: int, rows: Optional[int] = None,
+                                recv_x=None, recv_scales=None, recv_weights=None,
+                                want_weights: bool = False, workspace=None, stream=None):
+    """The 8-bit cast with column-major scales [H/128, scale_ld] written in
+    two passes through a workspace (allocated here with torch when not
+    given).  ``src`` is the layout's int32 source token of each of the
+    ``rows`` receive rows (T*k by default).  Returns (recv_x uint8 [rows, H],
+    recv_scales, recv_weights or None)."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [num_tokens, hidden]")
+    T, H = x.shape
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or slot.shape[0] != T:
+        raise ValueError("slot must be 2-D [num_tokens, num_topk]")
+    k = slot.shape[1]
+    R = T * k if rows is None else int(rows)
+    if scale_ld < R:
+        raise ValueError(f"scale_ld {scale_ld} is below the {R} rows")
+    _need(src, "src", torch.int32, R)
+    dev = x.device
+    sdt = torch.uint8 if scale == "ue8m0" else torch.float32
+    nb = H // 128
+    if recv_x is None:
+        recv_x = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    if recv_scales is None:
+        recv_scales = torch.empty((nb, scale_ld), dtype=sdt, device=dev)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
+    need = ep_dispatch_colmajor_workspace_size(T, H, scale)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(recv_x, "recv_x", torch.uint8, R * H)
+    _need(recv_scales, "recv_scales", sdt, nb * scale_ld)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, R)
+    _need(workspace, "workspace", torch.uint8)
+    st = lib().ep_dispatch_colmajor_scales(_ptr(x), T, H, k, _ptr(slot), _ptr(src),
+                                           _ptr(topk_weights), _FORMATS[fmt], _SCALES[scale],
+                                           _ptr(recv_x), _ptr(recv_scales), _ptr(recv_weights),
+                                           int(scale_ld), R, _ptr(workspace), workspace.numel(),
+                                           _stream(stream))
+    _check(st, "ep_dispatch_colmajor_scales")
     return recv_x, recv_scales, recv_weights
 
 

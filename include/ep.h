@@ -272,6 +272,42 @@ int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
                    int64_t scale_ld, void *stream);
 
 /*
+ * ep_dispatch_colmajor_scales -- the 8-bit cast of ep_dispatch_ex with
+ * column-major scales, written in two passes through a caller workspace so
+ * that each block's column is written in runs of consecutive rows: first the
+ * codes of every slot and each token's scale row once (into the workspace),
+ * then one lane per receive row copies its token's scales into the columns.
+ * (ep_dispatch_ex with scale_ld > 0 writes the same bytes in one pass, one
+ * row's scales at a time.)
+ *
+ * Passages: DeepEP page, dispatch() use_tma_aligned_col_major_sf (scale
+ * factors stored column-major for the grouped GEMM); NCCL EP page,
+ * ncclEpDispatch (per-128-channel scales of the cast).
+ *
+ * In:  x, slot, topk_weights, out_dtype (EP_OUT_FP8_E4M3 / _E5M2) and
+ *      scale_format as ep_dispatch_ex.
+ *      src        int32 [num_rows]: the source token of each receive row
+ *                 (ep_layout's src); entries of rows nothing maps to may hold
+ *                 anything: a row is filled only when one of its token's
+ *                 slots is that row.
+ *      num_rows   rows of the receive buffers (e.g. T*k, or
+ *                 ep_layout_max_rows for ep_layout_ex layouts).
+ *      workspace  >= ep_dispatch_colmajor_workspace_size(...) bytes,
+ *                 256-byte aligned, contents clobbered.
+ * Out: recv_x codes as ep_dispatch_ex; recv_scales [hidden/128, scale_ld]
+ *      (fp32, or bytes for UE8M0): block b of row r at b*scale_ld + r, for
+ *      the rows a slot maps to; other entries untouched.  scale_ld >= num_rows,
+ *      a multiple of 16 bytes' worth of scales.
+ * Rows of at most 1024 channels take ep_dispatch_ex's one-pass path.
+ */
+size_t ep_dispatch_colmajor_workspace_size(int64_t num_tokens, int hidden, int scale_format);
+int ep_dispatch_colmajor_scales(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                                const int32_t *slot, const int32_t *src, const float *topk_weights,
+                                int out_dtype, int scale_format, void *recv_x, void *recv_scales,
+                                float *recv_weights, int64_t scale_ld, int64_t num_rows,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * ep_dispatch_prequantized -- dispatch of tokens that are already 8-bit
  * floats with per-128-channel fp32 scales: the code row and the scale row of
  * each token are copied, bit for bit, to every unmasked slot (any 8-bit

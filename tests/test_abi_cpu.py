@@ -444,3 +444,39 @@ def test_dispatch_ranked_prequantized_rejects(over, code):
         a["rows"], None)
     assert st == code, ep.last_error()
     assert ep.last_error()
+
+
+@no_gpu
+def test_colmajor_workspace_size():
+    lib = ep.lib()
+    assert lib.ep_dispatch_colmajor_workspace_size(8192, 7168, 0) == 8192 * 56 * 4
+    assert lib.ep_dispatch_colmajor_workspace_size(3, 256, 2) == 256   # 6 bytes, rounded up
+    assert lib.ep_dispatch_colmajor_workspace_size(10, 200, 0) == 0    # not a multiple of 128
+    assert lib.ep_dispatch_colmajor_workspace_size(10, 256, 7) == 0    # unknown scale format
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(fmt=0), 1), (dict(fmt=3), 1), (dict(scale=5), 1), (dict(H=200), 1), (dict(k=0), 1),
+    (dict(T=-1), 1), (dict(ld=0), 1), (dict(ld=6), 1), (dict(scale=2, ld=20), 1),
+    (dict(rows=-1), 1), (dict(rows=20), 1), (dict(rows=1 << 31, ld=1 << 32), 1),
+    (dict(ws=None), 1), (dict(ws=FAKE + 16), 1), (dict(wsb=255), 1), (dict(x=None), 1),
+    (dict(slot=None), 1), (dict(src=None), 1), (dict(q=None), 1), (dict(s=None), 1),
+    (dict(x=FAKE + 8), 1), (dict(q=FAKE + 8), 1), (dict(s=FAKE + 2), 1), (dict(rw=FAKE), 1),
+])
+def test_dispatch_colmajor_scales_rejects(over, code):
+    a = dict(x=FAKE, T=4, H=256, k=2, slot=FAKE, src=FAKE, w=None, fmt=1, scale=0, q=FAKE, s=FAKE,
+             rw=None, ld=16, rows=8, ws=FAKE, wsb=256)
+    a.update(over)
+    st = ep.lib().ep_dispatch_colmajor_scales(
+        a["x"], a["T"], a["H"], a["k"], a["slot"], a["src"], a["w"], a["fmt"], a["scale"], a["q"],
+        a["s"], a["rw"], a["ld"], a["rows"], a["ws"], a["wsb"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+@no_gpu
+def test_dispatch_colmajor_scales_zero_tokens_is_a_noop():
+    st = ep.lib().ep_dispatch_colmajor_scales(None, 0, 256, 2, None, None, None, 1, 0, None, None,
+                                              None, 16, 0, FAKE, 256, None)
+    assert st == 0 and ep.last_error() == ""

@@ -267,3 +267,95 @@ def test_prequantized_slot_groups(T, H, E, k):
     np.testing.assert_array_equal(host(s)[:n].view(np.uint32), os_[:n].view(np.uint32))
     np.testing.assert_array_equal(host(rw)[:n], orw[:n])
     assert np.all(host(q)[n:] == 0xEE) and np.all(np.isnan(host(s)[n:]))
+
+
+# ---- column-major scales in two passes (ep_dispatch_colmajor_scales)
+
+def check_colmajor_staged(x_bits, slot, src, rows, fmt, mode, seed, slot_off=False):
+    """Codes and column-major scales of the two-pass cast against the
+    oracle's row-major scales transposed, for every row a slot maps to;
+    every other entry untouched.  ``src`` holds garbage (including valid
+    token ids) at every row nothing maps to.  ``slot_off``: the slot table
+    starts 4 bytes past a 16-byte boundary (the column pass then reads it
+    one entry at a time)."""
+    T, H = x_bits.shape
+    nb = H // 128
+    align = 16 if mode == "ue8m0" else 4
+    ld = (rows + align - 1) // align * align + align
+    mapped = np.zeros(rows, bool)
+    mapped[slot[slot >= 0]] = True
+    rng = np.random.default_rng(seed)
+    src_g = np.where(mapped, src[:rows], rng.integers(-5, T + 5, rows)).astype(np.int32)
+    q = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    sdt = torch.uint8 if mode == "ue8m0" else torch.float32
+    s = torch.full((nb, ld), 0xAB if mode == "ue8m0" else float("nan"), dtype=sdt, device=DEV)
+    d_slot = dev(slot)
+    if slot_off:
+        buf = torch.empty(slot.size + 1, dtype=torch.int32, device=DEV)
+        d_slot = buf[1:].view(slot.shape)
+        d_slot.copy_(dev(slot))
+        assert d_slot.data_ptr() % 16 == 4
+    ep.ep_dispatch_colmajor_scales(x_dev(x_bits), d_slot, dev(src_g), None, fmt=fmt, scale=mode,
+                                   scale_ld=ld, rows=rows, recv_x=q, recv_scales=s)
+    torch.cuda.synchronize()
+    oq, os_, _ = oracle.dispatch_quant(x_bits, slot, fmt=fmt, scale=mode, rows=rows)
+    gq, gs = host(q), host(s)
+    np.testing.assert_array_equal(gq[mapped], oq[mapped])
+    assert np.all(gq[~mapped] == 0xEE)
+    np.testing.assert_array_equal(np.ascontiguousarray(gs[:, :rows][:, mapped]).view(np.uint8),
+                                  np.ascontiguousarray(os_[mapped].T).view(np.uint8))
+    rest = np.concatenate([gs[:, :rows][:, ~mapped].ravel(), gs[:, rows:].ravel()])
+    assert np.all(rest == 0xAB) if mode == "ue8m0" else np.all(np.isnan(rest))
+
+
+@pytest.mark.parametrize("name", ["mid", "narrow", "fp8_slice"])
+@pytest.mark.parametrize("fmt,mode", COMBOS)
+def test_column_major_scales_two_pass(name, fmt, mode):
+    if name == "mid":
+        w = WORKLOADS["mid"]
+        inp = make_inputs(w)
+        xb, idx, E = inp.x_bits, inp.topk_idx, w.E
+    elif name == "narrow":    # hidden 2560: 64-lane tiles, two slot groups of 8
+        inp = make_random_case(83, 300, 2560, 16, 10, mask_frac=0.1, dup_frac=0.3)
+        xb, idx, E = inp.x_bits, inp.topk_idx, 16
+    else:                     # the fp8 workload's rows (outliers), 1024 tokens
+        inp = make_inputs(WORKLOADS["fp8"], T=1024)
+        xb, idx, E = inp.x_bits, inp.topk_idx, 256
+    print(f"\n[fp8 variants] column-major two-pass {name} {fmt} {mode}", flush=True)
+    L = oracle.layout(idx, E)
+    rows = idx.size
+    check_colmajor_staged(xb, L.slot, L.src, rows, fmt, mode, seed=len(name))
+
+
+@pytest.mark.parametrize("alignment,capacity", [(16, 0), (4, 12)])
+def test_column_major_scales_two_pass_padded_layouts(alignment, capacity):
+    # padding rows and dropped pairs: src holds garbage there, and nothing
+    # is written to those rows
+    inp = make_random_case(91, 200, 2048, 8, 4, mask_frac=0.1)
+    print(f"\n[fp8 variants] column-major two-pass, alignment {alignment} capacity {capacity}",
+          flush=True)
+    L = oracle.layout(inp.topk_idx, 8, alignment=alignment, capacity=capacity)
+    rows = ep.layout_max_rows(200, 4, 8, alignment, capacity)
+    src = np.zeros(rows, np.int32)
+    src[:L.src.size] = L.src[:rows]
+    check_colmajor_staged(inp.x_bits, L.slot, src, rows, "e4m3", "fp32", seed=alignment + capacity)
+
+
+@pytest.mark.parametrize("H,k,slot_off", [(1152, 8, False), (1664, 6, False), (2048, 8, True),
+                                          (1152, 8, True)])
+def test_column_major_scales_two_pass_odd_shapes(H, k, slot_off):
+    # block counts not a multiple of 4 (9, 13: one scale at a time), top-k
+    # not a multiple of 4, and a slot table off 16-byte alignment
+    inp = make_random_case(97 + H + k, 260, H, 12, k, mask_frac=0.1, dup_frac=0.2)
+    print(f"\n[fp8 variants] column-major two-pass H={H} k={k} slot_off={slot_off}", flush=True)
+    L = oracle.layout(inp.topk_idx, 12)
+    for fmt, mode in (("e4m3", "fp32"), ("e5m2", "ue8m0")):
+        check_colmajor_staged(inp.x_bits, L.slot, L.src, inp.topk_idx.size, fmt, mode, seed=H + k,
+                              slot_off=slot_off)
+
+
+def test_column_major_scales_two_pass_short_rows():
+    # hidden 1024 (64 units): ep_dispatch_ex's one-pass path, same contract
+    inp = make_random_case(95, 100, 1024, 8, 2, mask_frac=0.1)
+    L = oracle.layout(inp.topk_idx, 8)
+    check_colmajor_staged(inp.x_bits, L.slot, L.src, 200, "e5m2", "ue8m0", seed=3)
