@@ -607,12 +607,14 @@ def main():
     swt = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_w])
     fp_us = time_call(lambda: check(L.ep_dispatch_fused_permute(
         ctypes.addressof(sxt), ctypes.addressof(sit), ctypes.addressof(swt), T, H, k, E, G, 0,
-        rq["rsrc"], rq["rti"], pslot.data_ptr(), n_exp, perm_x.data_ptr(), perm_w.data_ptr(), s),
+        rq["rsrc"], rq["rti"], rq["nrecv"], pslot.data_ptr(), n_exp, perm_x.data_ptr(),
+        perm_w.data_ptr(), s),
         "ep_dispatch_fused_permute"), args.steps)
     # read each received token once, write each expert row once, read the
-    # receive-side rows (source, local experts, slots) and the senders'
-    # topk rows, write the row weights
-    fp_bytes = (n_recv * H * 2 + n_exp * H * 2 + G * T * (4 + k * 8 + k * 4) + n_recv * k * 12
+    # received rows' metadata (source, local experts, slots) and the senders'
+    # topk rows, write the row weights (rows past the received count, read
+    # on the device, are not visited)
+    fp_bytes = (n_recv * H * 2 + n_exp * H * 2 + n_recv * (4 + k * 8 + k * 4) + n_recv * k * 12
                 + n_exp * 4)
     del src_x, perm_x
 

@@ -553,8 +553,8 @@ int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* sr
                               const float* const* src_topk_weights, int64_t tokens_per_rank,
                               int hidden, int num_topk, int num_experts, int num_ranks, int rank,
                               const int32_t* recv_src, const int64_t* recv_topk_idx,
-                              const int32_t* slot, int64_t rows, void* recv_x,
-                              float* recv_weights, void* stream)
+                              const int32_t* num_recv, const int32_t* slot, int64_t rows,
+                              void* recv_x, float* recv_weights, void* stream)
 {
     g_last_error[0] = '\0';
     if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
@@ -593,9 +593,11 @@ int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* sr
         return fail(EP_INVALID_ARGUMENT,
                     "recv_src, slot, recv_x (and recv_topk_idx with recv_weights) are required");
     if (!aligned16(recv_x)) return fail(EP_INVALID_ARGUMENT, "recv_x must be 16-byte aligned");
+    if (num_recv && (reinterpret_cast<uintptr_t>(num_recv) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "num_recv must be 4-byte aligned");
     return from_hip(ep::launch_dispatch_fused_permute(px, pi, pw, tokens_per_rank, hidden, num_topk,
                                                       num_experts, num_ranks, rank, recv_src,
-                                                      recv_topk_idx, slot, rows, recv_x,
+                                                      recv_topk_idx, num_recv, slot, rows, recv_x,
                                                       recv_weights, static_cast<hipStream_t>(stream)),
                     "ep_dispatch_fused_permute launch");
 }

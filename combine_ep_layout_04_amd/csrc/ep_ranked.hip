@@ -55,6 +55,8 @@
 //                 streaming store (rows of at most 64 vectors: one
 //                 workgroup per token).
 
+#include <algorithm>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -697,27 +699,22 @@ void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
 
 // ------------------------------------------------ receive side, fused permute
 
-// One workgroup per received row i: the token (rank s, token t) is read once
-// from rank s's rows and stored to each of this rank's local-expert rows
-// slot[i, j]; wavefront 0 writes the matching weights, the fp32 sum in
-// increasing j' of the source weights of the slots that select the pair's
-// expert.  Rows with no source (past the received count) return at once.
-// This kernel keeps one workgroup per row: split into 2 KiB row tiles (as
-// the send-side copies are) it took 545 us, or 331 us with one slot group
-// per tile, against 307 us, at 8 ranks x 8192 tokens, hidden 7168.  A
-// received row usually has one or two local slots and a third of the rows
-// have no source, so most tile workgroups only wait on the recv_src -> slot
-// loads and exit.
+// Received row i: the token (rank s, token t) is read once from rank s's
+// rows and stored to each of this rank's local-expert rows slot[i, j];
+// wavefront 0 writes the matching weights, the fp32 sum in increasing j' of
+// the source weights of the slots that select the pair's expert.  Rows with
+// no source return at once.  Tiling a row into 2 KiB pieces (as the send-side
+// copies are) took 545 us, or 331 us with one slot group per tile, against
+// 307 us for whole rows, at 8 ranks x 8192 tokens, hidden 7168: a received
+// row usually has one or two local slots, so most tile workgroups only wait
+// on the recv_src -> slot loads and exit.
 template <int NT, int VPT>
-__global__ __launch_bounds__(NT)
-void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
-                                   int nvec, int k, int E, int El, int G, int rank,
-                                   const int32_t* __restrict__ recv_src,
-                                   const int64_t* __restrict__ recv_topk_idx,
-                                   const int32_t* __restrict__ slot, int64_t rows,
-                                   uint4* __restrict__ recv_x, float* __restrict__ recv_w)
+__device__ __forceinline__ void fused_permute_row(
+    const RankPtrs& src_x, const RankPtrs& src_idx, const RankPtrs& src_w, int64_t T, int nvec,
+    int k, int E, int El, int G, int rank, const int32_t* __restrict__ recv_src,
+    const int64_t* __restrict__ recv_topk_idx, const int32_t* __restrict__ slot, int64_t rows,
+    uint4* __restrict__ recv_x, float* __restrict__ recv_w, int64_t i)
 {
-    const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the same value in every lane; made scalar so the pointer tables are
@@ -776,6 +773,38 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
                 store_row16(buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16), v * 16, val);
         }
     }
+}
+
+// Only the first n rows are visited, n the received count read on the
+// device (all G*T rows when num_recv is NULL): no host round trip, and the
+// rows past it cost one scalar load each.  One workgroup per row (the grid
+// is capped at kFusedPermuteGrid, workgroup b taking rows b, b + gridDim.x,
+// ... past it).  At 8 ranks x 8192 tokens, hidden 7168, rank 0: 306 us,
+// the same as before the bound (the rows past the count exited at once
+// anyway); persistent grids of 2048-16384 workgroups took 315-322 us;
+// non-temporal or sc1 loads of the source rows, and issuing the row loads
+// before the weights, 302-309 us.  The kernel moves a 40/60 mix of reads
+// and writes at the rate of a device-to-device copy.
+constexpr int64_t kFusedPermuteGrid = 1 << 30;
+template <int NT, int VPT>
+__global__ __launch_bounds__(NT)
+void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
+                                   int nvec, int k, int E, int El, int G, int rank,
+                                   const int32_t* __restrict__ recv_src,
+                                   const int64_t* __restrict__ recv_topk_idx,
+                                   const int32_t* __restrict__ num_recv,
+                                   const int32_t* __restrict__ slot, int64_t rows,
+                                   uint4* __restrict__ recv_x, float* __restrict__ recv_w)
+{
+    const int64_t R = (int64_t)G * T;
+    int64_t n = R;
+    if (num_recv != nullptr) {
+        const int64_t c = __builtin_amdgcn_readfirstlane(*num_recv);
+        n = c < 0 ? 0 : (c < R ? c : R);
+    }
+    for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
+        fused_permute_row<NT, VPT>(src_x, src_idx, src_w, T, nvec, k, E, El, G, rank, recv_src,
+                                   recv_topk_idx, slot, rows, recv_x, recv_w, i);
 }
 
 // ---------------------------------------------------------------- combine
@@ -1090,21 +1119,21 @@ hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& 
                                          const RankPtrs& src_w, int64_t tokens_per_rank,
                                          int hidden, int num_topk, int num_experts, int num_ranks,
                                          int rank, const int32_t* recv_src,
-                                         const int64_t* recv_topk_idx, const int32_t* slot,
-                                         int64_t rows, void* recv_x, float* recv_w,
-                                         hipStream_t stream)
+                                         const int64_t* recv_topk_idx, const int32_t* num_recv,
+                                         const int32_t* slot, int64_t rows, void* recv_x,
+                                         float* recv_w, hipStream_t stream)
 {
     const int64_t R = tokens_per_rank * num_ranks;
     if (R == 0) return hipSuccess;
     const int nvec = hidden / 8;
-    const dim3 grid((unsigned)R);
+    const dim3 grid((unsigned)std::min(R, kFusedPermuteGrid));
     const int El = num_experts / num_ranks;
     uint4* rx = static_cast<uint4*>(recv_x);
 #define EP_FP(NT, V)                                                                            \
     hipLaunchKernelGGL((dispatch_fused_permute_kernel<NT, V>), grid, dim3(NT), 0, stream, src_x, \
                        src_idx, src_w, tokens_per_rank, nvec, num_topk, num_experts, El,        \
                        num_ranks, rank,                                                          \
-                       recv_src, recv_topk_idx, slot, rows, rx, recv_w)
+                       recv_src, recv_topk_idx, num_recv, slot, rows, rx, recv_w)
     if (nvec <= 64) {
         EP_FP(64, 1);
         return hipGetLastError();

@@ -116,7 +116,7 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_ranked_prequantized.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
                                                       P, i64, P]
         L.ep_dispatch_ranked_prequantized.restype = i32
-        L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
+        L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P,
                                                 i64, P, P, P]
         L.ep_dispatch_fused_permute.restype = i32
         L.ep_combine_ranked.argtypes = [P, i64, P, i64, i32, i32, P, P]
@@ -707,15 +707,18 @@ def ep_dispatch_ranked_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor,
 
 def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torch.Tensor,
                               slot: torch.Tensor, num_experts: int, rank: int, *, rows: int,
-                              src_topk_idx=None, src_topk_weights=None, recv_x=None,
-                              recv_weights=None, want_weights: bool = False, stream=None):
+                              src_topk_idx=None, src_topk_weights=None, num_recv=None,
+                              recv_x=None, recv_weights=None, want_weights: bool = False,
+                              stream=None):
     """The receiving rank's dispatch with the permute fused in: ``src_x`` is
     a list of the G ranks' tokens (bf16 [T, H]); ``recv_src`` /
     ``recv_topk_idx`` come from ep_rank_layout and ``slot`` from ep_layout of
     recv_topk_idx over E/G experts; ``rows`` is the expert-grouped buffer's
     row count.  Weights need ``src_topk_idx`` (list of int64 [T, k]) and
-    optionally ``src_topk_weights`` (list of fp32 [T, k] or None).  Returns
-    (recv_x bf16 [rows, H], recv_weights fp32 [rows] or None)."""
+    optionally ``src_topk_weights`` (list of fp32 [T, k] or None).
+    ``num_recv`` (int32 [1] on the device, from ep_rank_layout) bounds the
+    rows visited; None visits all G*T.  Returns (recv_x bf16 [rows, H],
+    recv_weights fp32 [rows] or None)."""
     G = len(src_x)
     for d, t in enumerate(src_x):
         _need(t, f"src_x[{d}]", torch.bfloat16)
@@ -749,11 +752,14 @@ def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torc
                 if t is not None:
                     _need(t, f"src_topk_weights[{d}]", torch.float32, T * k)
             wtab = _ptr_table(src_topk_weights)
+    if num_recv is not None:
+        _need(num_recv, "num_recv", torch.int32, 1)
     xtab = _ptr_table(src_x)
     st = lib().ep_dispatch_fused_permute(xtab[1], None if itab is None else itab[1],
                                          None if wtab is None else wtab[1], T, H, k,
                                          int(num_experts), G, int(rank), _ptr(recv_src),
-                                         _ptr(recv_topk_idx), _ptr(slot), R, _ptr(recv_x),
+                                         _ptr(recv_topk_idx), _ptr(num_recv), _ptr(slot), R,
+                                         _ptr(recv_x),
                                          _ptr(recv_weights), _stream(stream))
     _check(st, "ep_dispatch_fused_permute")
     return recv_x, recv_weights

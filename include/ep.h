@@ -539,6 +539,12 @@ int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
  *                         (an entry may be NULL: unit weights).
  *      recv_src, recv_topk_idx  from ep_rank_layout for `rank` (k_out =
  *                         num_topk), all G*T rows.
+ *      num_recv           NULL, or device int32 [1] (ep_rank_layout's
+ *                         num_recv): only received rows i < num_recv
+ *                         (clamped to [0, G*T]) are visited, and the count is
+ *                         read on the device (no host round trip); rows past
+ *                         it are not read;
+ *                         NULL visits all G*T rows.
  *      slot               int32 [G*T, num_topk]: ep_layout (or ep_layout_ex
  *                         with an alignment) of recv_topk_idx over E/G
  *                         experts.
@@ -548,15 +554,16 @@ int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
  *      of rank s's weights of the slots that select expert
  *      rank*E/G + recv_topk_idx[i, j].
  *      Rows past `rows` are never written; rows nothing maps to are not.
- *      A received row whose recv_src is not in [0, G*T) is skipped.
+ *      A received row whose recv_src is not in [0, G*T), or past num_recv,
+ *      is skipped.
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
 int ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,
                               const float *const *src_topk_weights, int64_t tokens_per_rank,
                               int hidden, int num_topk, int num_experts, int num_ranks, int rank,
                               const int32_t *recv_src, const int64_t *recv_topk_idx,
-                              const int32_t *slot, int64_t rows, void *recv_x,
-                              float *recv_weights, void *stream);
+                              const int32_t *num_recv, const int32_t *slot, int64_t rows,
+                              void *recv_x, float *recv_weights, void *stream);
 
 /*
  * ep_combine_ranked -- gather this rank's tokens back from every rank.

@@ -382,16 +382,16 @@ def test_ranked_zero_tokens_are_noops():
     (dict(sx="none"), 1), (dict(sx=(FAKE, None)), 1), (dict(sx=(FAKE, FAKE + 8)), 1),
     (dict(si="none"), 1), (dict(si=(FAKE, None)), 1), (dict(si=(FAKE, FAKE + 4)), 1),
     (dict(sw=(FAKE, FAKE + 2)), 1), (dict(src=None), 1), (dict(slot=None), 1),
-    (dict(rti=None), 1), (dict(out=None), 1), (dict(out=FAKE + 8), 1),
+    (dict(rti=None), 1), (dict(out=None), 1), (dict(out=FAKE + 8), 1), (dict(nr=FAKE + 2), 1),
 ])
 def test_dispatch_fused_permute_rejects(over, code):
     a = dict(sx=(FAKE, FAKE), si=(FAKE, FAKE), sw=None, T=4, H=256, k=2, E=8, G=2, rank=0,
-             src=FAKE, rti=FAKE, slot=FAKE, rows=16, out=FAKE, rw=FAKE)
+             src=FAKE, rti=FAKE, nr=None, slot=FAKE, rows=16, out=FAKE, rw=FAKE)
     a.update(over)
     tabs = {n: (None if a[n] in (None, "none") else _table(*a[n])) for n in ("sx", "si", "sw")}
     st = ep.lib().ep_dispatch_fused_permute(
         *[None if tabs[n] is None else ctypes.addressof(tabs[n]) for n in ("sx", "si", "sw")],
-        a["T"], a["H"], a["k"], a["E"], a["G"], a["rank"], a["src"], a["rti"], a["slot"],
+        a["T"], a["H"], a["k"], a["E"], a["G"], a["rank"], a["src"], a["rti"], a["nr"], a["slot"],
         a["rows"], a["out"], a["rw"], None)
     assert st == code, ep.last_error()
     assert ep.last_error()
@@ -400,7 +400,7 @@ def test_dispatch_fused_permute_rejects(over, code):
 def test_dispatch_fused_permute_zero_tokens_is_a_noop():
     sx = _table(FAKE, FAKE)
     assert ep.lib().ep_dispatch_fused_permute(ctypes.addressof(sx), None, None, 0, 256, 2, 8, 2,
-                                              0, None, None, None, 0, None, None, None) == 0
+                                              0, None, None, None, None, 0, None, None, None) == 0
     assert ep.last_error() == ""
 
 

@@ -239,6 +239,8 @@ def test_variants_and_backward_graph():
         # 8-bit casts: E5M2 / UE8M0 on the aligned layout, E4M3 column-major
         "q_al": torch.empty((R_al, H), **u8), "s_al": torch.empty((R_al, nb), **u8),
         "q_cm": torch.empty((P, H), **u8), "s_cm": torch.empty((nb, P + 4), **f32),
+        "q_cm2": torch.empty((P, H), **u8), "s_cm2": torch.empty((nb, P + 4), **f32),
+        "rw_cm2": torch.empty(P, **f32),
         "q_pre": torch.empty((P, H), **u8), "s_pre": torch.empty((P, nb), **f32),
         "rw_pre": torch.empty(P, **f32),
         # backward
@@ -260,6 +262,7 @@ def test_variants_and_backward_graph():
     for d in range(G):
         o[f"dq{d}"], o[f"ds{d}"], o[f"dw{d}"] = dq[d], ds[d], dw[d]
     ws = torch.empty(max(ep.layout_workspace_size(T, k, E), 256), **u8)
+    cmws = torch.empty(max(ep.ep_dispatch_colmajor_workspace_size(T, H, "fp32"), 256), **u8)
     pws = torch.empty(max(ep.layout_workspace_size(RG, k, El), 256), **u8)
     rws = torch.empty(max(ep.rank_layout_workspace_size(T, E, G), 256), **u8)
     lay = ep.RankLayout(sparse_to_dense=o["s2d"], local_map=o["lmap"], recv_src=o["rsrc"],
@@ -278,6 +281,9 @@ def test_variants_and_backward_graph():
                        recv_scales=o["s_al"], rows=R_al)
         ep.ep_dispatch(x, o["slot"], None, fp8=True, recv_x=o["q_cm"], recv_scales=o["s_cm"],
                        scale_ld=P + 4)
+        ep.ep_dispatch_colmajor_scales(x, o["slot"], o["src"], w, scale_ld=P + 4, recv_x=o["q_cm2"],
+                                       recv_scales=o["s_cm2"], recv_weights=o["rw_cm2"],
+                                       workspace=cmws)
         ep.ep_dispatch_prequantized(xq, xs, o["slot"], w, recv_q=o["q_pre"], recv_scales=o["s_pre"],
                                     recv_weights=o["rw_pre"])
         ep.ep_dispatch(x, o["slot"], None, recv_x=o["recv"])
@@ -292,7 +298,8 @@ def test_variants_and_backward_graph():
                      want_src=False, want_invalid=False, workspace=pws)
         ep.ep_dispatch_fused_permute(x_all, o["rsrc"], o["rti"], o["p_slot"], E, 0, rows=RG * k,
                                      src_topk_idx=idx_all, src_topk_weights=w_all,
-                                     recv_x=o["perm_x"], recv_weights=o["perm_w"])
+                                     num_recv=o["nrecv"], recv_x=o["perm_x"],
+                                     recv_weights=o["perm_w"])
 
     for t in o.values():
         _bits(t).fill_(0x55)
@@ -310,6 +317,9 @@ def test_variants_and_backward_graph():
     placed = La.slot[La.slot >= 0]
     np.testing.assert_array_equal(host(o["q_al"])[placed], oq[placed])
     np.testing.assert_array_equal(host(o["s_al"])[placed], os_[placed])
+    # the two-pass column-major cast writes what the one-pass form does
+    assert torch.equal(_bits(o["q_cm2"]), _bits(o["q_cm"]))
+    assert torch.equal(_bits(o["s_cm2"]), _bits(o["s_cm"]))
     ref = {name: t.clone() for name, t in o.items()}
 
     g = _capture(step)

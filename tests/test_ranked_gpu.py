@@ -360,7 +360,12 @@ def test_rank_layout_deterministic_and_on_a_side_stream():
         assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
-def check_fused_permute(xs, idx, ws, E, G, r, A=1, with_weights=True, rank_layout=None):
+def check_fused_permute(xs, idx, ws, E, G, r, A=1, with_weights=True, rank_layout=None,
+                        bound="layout"):
+    """``bound``: the num_recv passed on the device ("layout": the rank
+    layout's count; None: no count, every row visited; an int: that count,
+    which may be negative or past G*T).  Rows at or past the clamped count
+    are expected untouched, as if their recv_src were -1."""
     T, H = xs[0].shape
     k = idx[0].shape[1]
     El = E // G
@@ -372,17 +377,23 @@ def check_fused_permute(xs, idx, ws, E, G, r, A=1, with_weights=True, rank_layou
     rows = max(Lr.n, 1)
     out = torch.full((rows, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV) if with_weights else None
+    n = L.num_recv if bound == "layout" else bound
+    nr = None if n is None else dev(np.array([n], np.int32))
     ep.ep_dispatch_fused_permute([x_dev(x) for x in xs], dev(L.recv_src), dev(L.recv_topk_idx),
                                  dev(Lr.slot), E, r, rows=rows,
                                  src_topk_idx=[dev(i) for i in idx] if with_weights else None,
                                  src_topk_weights=None if ws is None else [dev(w) for w in ws],
-                                 recv_x=out, recv_weights=rw)
+                                 num_recv=nr, recv_x=out, recv_weights=rw)
     torch.cuda.synchronize()
+    visited = G * T if n is None else min(max(n, 0), G * T)
+    want_src = L.recv_src.copy()
+    want_src[visited:] = -1
     ox, ow = oracle.dispatch_fused_permute(xs, idx, ws if ws is not None else [None] * G, E, r,
-                                           L.recv_src, L.recv_topk_idx, Lr.slot, rows,
+                                           want_src, L.recv_topk_idx, Lr.slot, rows,
                                            with_weights)
     written = np.zeros(rows, bool)
-    written[Lr.slot[Lr.slot >= 0]] = True
+    sl = Lr.slot[:visited]
+    written[sl[(sl >= 0) & (want_src[:visited, None] >= 0)]] = True
     got = bf16_bits(out)
     np.testing.assert_array_equal(got[written], ox[written])
     assert np.all(got[~written] == 0xFFFD), "a padding row was written"
@@ -408,7 +419,24 @@ def test_fused_permute_small(G, T, H, E, k, A, weights):
     for r in sorted({0, G - 1, G // 2}):
         print(f"\n[ranked] fused permute G={G} T={T} H={H} E={E} k={k} A={A} rank={r}", flush=True)
         check_fused_permute(xs, idx, ws, E, G, r, A=A, with_weights=True)
-        check_fused_permute(xs, idx, ws, E, G, r, with_weights=False)
+        check_fused_permute(xs, idx, ws, E, G, r, with_weights=False, bound=None)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.5, -1.0, 3.0])
+def test_fused_permute_bounded_by_num_recv(frac):
+    # a count below the received rows stops the walk there (the rows past it
+    # are left as they were); a negative count visits nothing, one past G*T
+    # every row
+    G, T, H, E, k = 8, 300, 1032, 32, 6
+    cases = rank_cases(123, G, T, H, E, k, mask_frac=0.1, dup_frac=0.3)
+    xs = [c.x_bits for c in cases]
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, T, E, G, 3, k)
+    n = int(frac * L.num_recv) if frac >= 0 and frac <= 1 else (-7 if frac < 0 else G * T + 5)
+    print(f"\n[ranked] fused permute bounded by num_recv={n} of {L.num_recv}", flush=True)
+    check_fused_permute(xs, idx, ws, E, G, 3, rank_layout=L, bound=n)
 
 
 def test_fused_permute_headline():
