@@ -18,7 +18,7 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
-int fail(int status, const char* fmt, ...)
+ep_status_t fail(ep_status_t status, const char* fmt, ...)
 {
     va_list ap;
     va_start(ap, fmt);
@@ -27,7 +27,7 @@ int fail(int status, const char* fmt, ...)
     return status;
 }
 
-int from_hip(hipError_t err, const char* what)
+ep_status_t from_hip(hipError_t err, const char* what)
 {
     if (err == hipSuccess) return EP_SUCCESS;
     return fail(EP_RUNTIME_ERROR, "%s: %s", what, hipGetErrorString(err));
@@ -35,7 +35,7 @@ int from_hip(hipError_t err, const char* what)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_tokens(int64_t num_tokens, int num_topk)
+ep_status_t check_tokens(int64_t num_tokens, int num_topk)
 {
     if (num_tokens < 0) return fail(EP_INVALID_ARGUMENT, "num_tokens < 0");
     if (num_topk < 1 || num_topk > EP_MAX_TOPK)
@@ -45,7 +45,7 @@ int check_tokens(int64_t num_tokens, int num_topk)
     return EP_SUCCESS;
 }
 
-int check_hidden(int hidden, int multiple)
+ep_status_t check_hidden(int hidden, int multiple)
 {
     if (hidden < 1 || hidden > EP_MAX_HIDDEN || hidden % multiple != 0)
         return fail(EP_INVALID_ARGUMENT, "hidden %d must be a positive multiple of %d, at most %d",
@@ -95,13 +95,13 @@ int64_t ep_layout_max_rows(int64_t num_tokens, int num_topk, int num_experts, in
     return pairs + touched * (alignment - 1);
 }
 
-int ep_layout_ex(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                 int alignment, int64_t expert_capacity, int32_t* counts, int32_t* offsets,
-                 int32_t* slot, int32_t* src, int32_t* num_invalid, int32_t* num_dropped,
-                 void* workspace, size_t workspace_bytes, void* stream)
+ep_status_t ep_layout_ex(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                         int alignment, int64_t expert_capacity, int32_t* counts, int32_t* offsets,
+                         int32_t* slot, int32_t* src, int32_t* num_invalid, int32_t* num_dropped,
+                         void* workspace, size_t workspace_bytes, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
         return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
@@ -135,17 +135,17 @@ int ep_layout_ex(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int 
                     "ep_layout launch");
 }
 
-int ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-              int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
-              int32_t* num_invalid, void* workspace, size_t workspace_bytes, void* stream)
+ep_status_t ep_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                      int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
+                      int32_t* num_invalid, void* workspace, size_t workspace_bytes, void* stream)
 {
     return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets, slot,
                         src, num_invalid, nullptr, workspace, workspace_bytes, stream);
 }
 
-int ep_layout_noalloc(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                      int32_t* counts, int32_t* offsets, int32_t* slot, int32_t* src,
-                      int32_t* num_invalid, void* stream)
+ep_status_t ep_layout_noalloc(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                              int num_experts, int32_t* counts, int32_t* offsets, int32_t* slot,
+                              int32_t* src, int32_t* num_invalid, void* stream)
 {
     g_last_error[0] = '\0';
     const size_t need = ep_layout_workspace_size(num_tokens, num_topk, num_experts);
@@ -159,14 +159,14 @@ int ep_layout_noalloc(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
                     "bytes the library holds per device",
                     need, have);
     void* scratch = nullptr;
-    const int st = from_hip(ep::layout_scratch(&scratch), "ep_layout_noalloc scratch address");
+    const ep_status_t st = from_hip(ep::layout_scratch(&scratch), "ep_layout_noalloc scratch address");
     if (st) return st;
     return ep_layout_ex(topk_idx, num_tokens, num_topk, num_experts, 1, 0, counts, offsets, slot,
                         src, num_invalid, nullptr, scratch, have, stream);
 }
 
 // scale_ld: 0, or a positive multiple of the 16-byte column alignment
-static int check_scale_ld(int64_t scale_ld, int elem_bytes)
+static ep_status_t check_scale_ld(int64_t scale_ld, int elem_bytes)
 {
     const int64_t align = 16 / elem_bytes;
     if (scale_ld < 0 || (scale_ld > 0 && scale_ld % align != 0))
@@ -176,13 +176,13 @@ static int check_scale_ld(int64_t scale_ld, int elem_bytes)
     return EP_SUCCESS;
 }
 
-int ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
-                   const int32_t* slot, const float* topk_weights, int out_dtype,
-                   int scale_format, void* recv_x, void* recv_scales, float* recv_weights,
-                   int64_t scale_ld, void* stream)
+ep_status_t ep_dispatch_ex(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                           const int32_t* slot, const float* topk_weights, int out_dtype,
+                           int scale_format, void* recv_x, void* recv_scales, float* recv_weights,
+                           int64_t scale_ld, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     if (out_dtype != EP_OUT_BF16 && out_dtype != EP_OUT_FP8_E4M3 && out_dtype != EP_OUT_FP8_E5M2)
         return fail(EP_INVALID_ARGUMENT, "unknown out_dtype %d", out_dtype);
@@ -228,14 +228,15 @@ size_t ep_dispatch_colmajor_workspace_size(int64_t num_tokens, int hidden, int s
     return ep::colmajor_workspace_bytes(num_tokens, hidden, scale_format);
 }
 
-int ep_dispatch_colmajor_scales(const void* x, int64_t num_tokens, int hidden, int num_topk,
-                                const int32_t* slot, const int32_t* src, const float* topk_weights,
-                                int out_dtype, int scale_format, void* recv_x, void* recv_scales,
-                                float* recv_weights, int64_t scale_ld, int64_t num_rows,
-                                void* workspace, size_t workspace_bytes, void* stream)
+ep_status_t ep_dispatch_colmajor_scales(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                                        const int32_t* slot, const int32_t* src,
+                                        const float* topk_weights, int out_dtype, int scale_format,
+                                        void* recv_x, void* recv_scales, float* recv_weights,
+                                        int64_t scale_ld, int64_t num_rows, void* workspace,
+                                        size_t workspace_bytes, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     if (out_dtype != EP_OUT_FP8_E4M3 && out_dtype != EP_OUT_FP8_E5M2)
         return fail(EP_INVALID_ARGUMENT, "out_dtype %d: column-major scales come with an 8-bit cast",
@@ -276,21 +277,21 @@ int ep_dispatch_colmajor_scales(const void* x, int64_t num_tokens, int hidden, i
                     "ep_dispatch_colmajor_scales launch");
 }
 
-int ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
-                const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
-                float* recv_scales, float* recv_weights, void* stream)
+ep_status_t ep_dispatch(const void* x, int64_t num_tokens, int hidden, int num_topk,
+                        const int32_t* slot, const float* topk_weights, int out_dtype, void* recv_x,
+                        float* recv_scales, float* recv_weights, void* stream)
 {
     return ep_dispatch_ex(x, num_tokens, hidden, num_topk, slot, topk_weights, out_dtype,
                           EP_SCALE_FP32, recv_x, recv_scales, recv_weights, 0, stream);
 }
 
-int ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num_tokens,
-                             int hidden, int num_topk, const int32_t* slot,
-                             const float* topk_weights, void* recv_q, float* recv_scales,
-                             float* recv_weights, int64_t scale_ld, void* stream)
+ep_status_t ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num_tokens,
+                                     int hidden, int num_topk, const int32_t* slot,
+                                     const float* topk_weights, void* recv_q, float* recv_scales,
+                                     float* recv_weights, int64_t scale_ld, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 128);
     if (st) return st;
@@ -311,11 +312,11 @@ int ep_dispatch_prequantized(const void* x_q, const float* x_scales, int64_t num
                     "ep_dispatch_prequantized launch");
 }
 
-int ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
-               int64_t num_tokens, int hidden, int num_topk, void* out, void* stream)
+ep_status_t ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, void* out, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 8);
     if (st) return st;
@@ -328,12 +329,12 @@ int ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
                     "ep_combine launch");
 }
 
-int ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
-                        const float* topk_weights, int64_t num_tokens, int hidden, int num_topk,
-                        void* grad_y, float* grad_topk_weights, void* stream)
+ep_status_t ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot,
+                                const float* topk_weights, int64_t num_tokens, int hidden,
+                                int num_topk, void* grad_y, float* grad_topk_weights, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 8);
     if (st) return st;
@@ -350,12 +351,12 @@ int ep_combine_backward(const void* grad_out, const void* y, const int32_t* slot
                     "ep_combine_backward launch");
 }
 
-int ep_dispatch_backward(const void* grad_recv, const float* grad_recv_weights,
-                         const int32_t* slot, int64_t num_tokens, int hidden, int num_topk,
-                         void* grad_x, float* grad_topk_weights, void* stream)
+ep_status_t ep_dispatch_backward(const void* grad_recv, const float* grad_recv_weights,
+                                 const int32_t* slot, int64_t num_tokens, int hidden, int num_topk,
+                                 void* grad_x, float* grad_topk_weights, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 8);
     if (st) return st;
@@ -376,7 +377,7 @@ int ep_dispatch_backward(const void* grad_recv, const float* grad_recv_weights,
 
 // ---- per-(token, rank) path
 
-static int check_ranks(int num_experts, int num_ranks)
+static ep_status_t check_ranks(int num_experts, int num_ranks)
 {
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
         return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
@@ -389,11 +390,12 @@ static int check_ranks(int num_experts, int num_ranks)
     return EP_SUCCESS;
 }
 
-int ep_routing_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                   uint8_t* routing_map, int32_t* num_invalid, void* stream)
+ep_status_t ep_routing_map(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, uint8_t* routing_map, int32_t* num_invalid,
+                           void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     if (num_experts < 1 || num_experts > EP_MAX_EXPERTS)
         return fail(EP_INVALID_ARGUMENT, "num_experts %d outside [1, %d]", num_experts,
@@ -419,14 +421,15 @@ size_t ep_rank_layout_workspace_size(int64_t tokens_per_rank, int num_experts, i
     return (bytes + 255) & ~(size_t)255;
 }
 
-int ep_rank_layout(const uint8_t* global_routing_map, int64_t tokens_per_rank, int num_experts,
-                   int num_ranks, int rank, int k_out, int32_t* sparse_to_dense_map,
-                   uint8_t* local_expert_routing_map, int32_t* recv_src, int64_t* recv_topk_idx,
-                   int32_t* expert_counts, int32_t* num_recv, int32_t* num_overflow,
-                   void* workspace, size_t workspace_bytes, void* stream)
+ep_status_t ep_rank_layout(const uint8_t* global_routing_map, int64_t tokens_per_rank,
+                           int num_experts, int num_ranks, int rank, int k_out,
+                           int32_t* sparse_to_dense_map, uint8_t* local_expert_routing_map,
+                           int32_t* recv_src, int64_t* recv_topk_idx, int32_t* expert_counts,
+                           int32_t* num_recv, int32_t* num_overflow, void* workspace,
+                           size_t workspace_bytes, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_ranks(num_experts, num_ranks);
+    ep_status_t st = check_ranks(num_experts, num_ranks);
     if (st) return st;
     if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
     if (rank < 0 || rank >= num_ranks)
@@ -462,13 +465,14 @@ int ep_rank_layout(const uint8_t* global_routing_map, int64_t tokens_per_rank, i
                     "ep_rank_layout launch");
 }
 
-int ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
-                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int num_ranks, const int32_t* sparse_to_dense_map, void* const* dest_x,
-                       float* const* dest_weights, int64_t dest_rows, void* stream)
+ep_status_t ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                               int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                               int num_ranks, const int32_t* sparse_to_dense_map,
+                               void* const* dest_x, float* const* dest_weights, int64_t dest_rows,
+                               void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 8);
     if (st) return st;
@@ -502,15 +506,16 @@ int ep_dispatch_ranked(const void* x, const int64_t* topk_idx, const float* topk
                     "ep_dispatch_ranked launch");
 }
 
-int ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scales,
-                                    const int64_t* topk_idx, const float* topk_weights,
-                                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                    int num_ranks, const int32_t* sparse_to_dense_map,
-                                    void* const* dest_q, float* const* dest_scales,
-                                    float* const* dest_weights, int64_t dest_rows, void* stream)
+ep_status_t ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scales,
+                                            const int64_t* topk_idx, const float* topk_weights,
+                                            int64_t num_tokens, int hidden, int num_topk,
+                                            int num_experts, int num_ranks,
+                                            const int32_t* sparse_to_dense_map, void* const* dest_q,
+                                            float* const* dest_scales, float* const* dest_weights,
+                                            int64_t dest_rows, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_hidden(hidden, 128);
     if (st) return st;
@@ -549,16 +554,17 @@ int ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scales,
                     "ep_dispatch_ranked_prequantized launch");
 }
 
-int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,
-                              const float* const* src_topk_weights, int64_t tokens_per_rank,
-                              int hidden, int num_topk, int num_experts, int num_ranks, int rank,
-                              const int32_t* recv_src, const int64_t* recv_topk_idx,
-                              const int32_t* num_recv, const int32_t* slot, int64_t rows,
-                              void* recv_x, float* recv_weights, void* stream)
+ep_status_t ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,
+                                      const float* const* src_topk_weights, int64_t tokens_per_rank,
+                                      int hidden, int num_topk, int num_experts, int num_ranks,
+                                      int rank, const int32_t* recv_src,
+                                      const int64_t* recv_topk_idx, const int32_t* num_recv,
+                                      const int32_t* slot, int64_t rows, void* recv_x,
+                                      float* recv_weights, void* stream)
 {
     g_last_error[0] = '\0';
     if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
-    int st = check_ranks(num_experts, num_ranks);
+    ep_status_t st = check_ranks(num_experts, num_ranks);
     if (st) return st;
     st = check_tokens(tokens_per_rank * num_ranks, num_topk);
     if (st) return st;
@@ -602,9 +608,9 @@ int ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* sr
                     "ep_dispatch_fused_permute launch");
 }
 
-int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
-                      const int32_t* sparse_to_dense_map, int64_t num_tokens, int hidden,
-                      int num_ranks, void* out, void* stream)
+ep_status_t ep_combine_ranked(const void* const* src_y, int64_t src_rows,
+                              const int32_t* sparse_to_dense_map, int64_t num_tokens, int hidden,
+                              int num_ranks, void* out, void* stream)
 {
     g_last_error[0] = '\0';
     if (num_tokens < 0) return fail(EP_INVALID_ARGUMENT, "num_tokens < 0");
@@ -612,7 +618,7 @@ int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
         return fail(EP_INVALID_ARGUMENT, "num_ranks %d outside [1, %d]", num_ranks, EP_MAX_RANKS);
     if (num_tokens * (int64_t)num_ranks >= ((int64_t)1 << 31))
         return fail(EP_UNSUPPORTED, "num_tokens * num_ranks must be < 2^31");
-    int st = check_hidden(hidden, 8);
+    ep_status_t st = check_hidden(hidden, 8);
     if (st) return st;
     if (src_rows < 0) return fail(EP_INVALID_ARGUMENT, "src_rows < 0");
     if (!src_y) return fail(EP_INVALID_ARGUMENT, "src_y (a host array of pointers) is required");
@@ -631,15 +637,15 @@ int ep_combine_ranked(const void* const* src_y, int64_t src_rows,
                     "ep_combine_ranked launch");
 }
 
-int ep_dispatch_ranked_backward(const void* const* grad_recv_x,
-                                const float* const* grad_recv_weights, int64_t src_rows,
-                                const int64_t* topk_idx, const int32_t* sparse_to_dense_map,
-                                int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                int num_ranks, void* grad_x, float* grad_topk_weights,
-                                void* stream)
+ep_status_t ep_dispatch_ranked_backward(const void* const* grad_recv_x,
+                                        const float* const* grad_recv_weights, int64_t src_rows,
+                                        const int64_t* topk_idx, const int32_t* sparse_to_dense_map,
+                                        int64_t num_tokens, int hidden, int num_topk,
+                                        int num_experts, int num_ranks, void* grad_x,
+                                        float* grad_topk_weights, void* stream)
 {
     g_last_error[0] = '\0';
-    int st = check_tokens(num_tokens, num_topk);
+    ep_status_t st = check_tokens(num_tokens, num_topk);
     if (st) return st;
     st = check_ranks(num_experts, num_ranks);
     if (st) return st;

@@ -130,9 +130,9 @@ size_t ep_layout_workspace_size(int64_t num_tokens, int num_topk, int num_expert
  * Requires num_tokens * num_topk < 2^31, 1 <= num_topk <= EP_MAX_TOPK,
  * 1 <= num_experts <= EP_MAX_EXPERTS.
  */
-int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-              int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
-              int32_t *num_invalid, void *workspace, size_t workspace_bytes, void *stream);
+ep_status_t ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                      int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
+                      int32_t *num_invalid, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * ep_layout_noalloc -- ep_layout for callers that cannot allocate device
@@ -154,9 +154,9 @@ int ep_layout(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num
  * made; calls ordered on one stream are safe.
  */
 #define EP_LAYOUT_NOALLOC_SCRATCH_BYTES ((size_t)(256 * 1024 + 256) * 4)
-int ep_layout_noalloc(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                      int32_t *counts, int32_t *offsets, int32_t *slot, int32_t *src,
-                      int32_t *num_invalid, void *stream);
+ep_status_t ep_layout_noalloc(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
+                              int num_experts, int32_t *counts, int32_t *offsets, int32_t *slot,
+                              int32_t *src, int32_t *num_invalid, void *stream);
 
 /*
  * ep_layout_ex -- ep_layout with the segment placements the pages' expanded
@@ -186,10 +186,10 @@ int ep_layout_noalloc(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
  * Other arguments, errors and requirements as ep_layout; additionally the
  * layout's row count bound must be below 2^31 (else EP_UNSUPPORTED).
  */
-int ep_layout_ex(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                 int alignment, int64_t expert_capacity, int32_t *counts, int32_t *offsets,
-                 int32_t *slot, int32_t *src, int32_t *num_invalid, int32_t *num_dropped,
-                 void *workspace, size_t workspace_bytes, void *stream);
+ep_status_t ep_layout_ex(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                         int alignment, int64_t expert_capacity, int32_t *counts, int32_t *offsets,
+                         int32_t *slot, int32_t *src, int32_t *num_invalid, int32_t *num_dropped,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Rows a receive buffer needs for any routing of this shape and placement:
@@ -231,9 +231,9 @@ int64_t ep_layout_max_rows(int64_t num_tokens, int num_topk, int num_experts, in
  * always enough.  hidden must be a positive multiple of 8 (of 128 for FP8),
  * at most EP_MAX_HIDDEN.
  */
-int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
-                const int32_t *slot, const float *topk_weights, int out_dtype,
-                void *recv_x, float *recv_scales, float *recv_weights, void *stream);
+ep_status_t ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                        const int32_t *slot, const float *topk_weights, int out_dtype, void *recv_x,
+                        float *recv_scales, float *recv_weights, void *stream);
 
 /*
  * ep_dispatch_ex -- ep_dispatch with the 8-bit cast variants.  ep_dispatch
@@ -266,10 +266,10 @@ int ep_dispatch(const void *x, int64_t num_tokens, int hidden, int num_topk,
  * zero; a NaN quotient gives 0x7F with the sign of x (both formats).
  * Other arguments and errors as ep_dispatch.
  */
-int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
-                   const int32_t *slot, const float *topk_weights, int out_dtype,
-                   int scale_format, void *recv_x, void *recv_scales, float *recv_weights,
-                   int64_t scale_ld, void *stream);
+ep_status_t ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                           const int32_t *slot, const float *topk_weights, int out_dtype,
+                           int scale_format, void *recv_x, void *recv_scales, float *recv_weights,
+                           int64_t scale_ld, void *stream);
 
 /*
  * ep_dispatch_colmajor_scales -- the 8-bit cast of ep_dispatch_ex with
@@ -301,11 +301,12 @@ int ep_dispatch_ex(const void *x, int64_t num_tokens, int hidden, int num_topk,
  * Rows of at most 1024 channels take ep_dispatch_ex's one-pass path.
  */
 size_t ep_dispatch_colmajor_workspace_size(int64_t num_tokens, int hidden, int scale_format);
-int ep_dispatch_colmajor_scales(const void *x, int64_t num_tokens, int hidden, int num_topk,
-                                const int32_t *slot, const int32_t *src, const float *topk_weights,
-                                int out_dtype, int scale_format, void *recv_x, void *recv_scales,
-                                float *recv_weights, int64_t scale_ld, int64_t num_rows,
-                                void *workspace, size_t workspace_bytes, void *stream);
+ep_status_t ep_dispatch_colmajor_scales(const void *x, int64_t num_tokens, int hidden, int num_topk,
+                                        const int32_t *slot, const int32_t *src,
+                                        const float *topk_weights, int out_dtype, int scale_format,
+                                        void *recv_x, void *recv_scales, float *recv_weights,
+                                        int64_t scale_ld, int64_t num_rows, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /*
  * ep_dispatch_prequantized -- dispatch of tokens that are already 8-bit
@@ -325,10 +326,10 @@ int ep_dispatch_colmajor_scales(const void *x, int64_t num_tokens, int hidden, i
  *      recv_weights [rows] or NULL.
  * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
  */
-int ep_dispatch_prequantized(const void *x_q, const float *x_scales, int64_t num_tokens,
-                             int hidden, int num_topk, const int32_t *slot,
-                             const float *topk_weights, void *recv_q, float *recv_scales,
-                             float *recv_weights, int64_t scale_ld, void *stream);
+ep_status_t ep_dispatch_prequantized(const void *x_q, const float *x_scales, int64_t num_tokens,
+                                     int hidden, int num_topk, const int32_t *slot,
+                                     const float *topk_weights, void *recv_q, float *recv_scales,
+                                     float *recv_weights, int64_t scale_ld, void *stream);
 
 /*
  * ep_combine -- weighted reduction of expert outputs back to token order.
@@ -349,8 +350,8 @@ int ep_dispatch_prequantized(const void *x_q, const float *x_scales, int64_t num
  *                    a token whose slots are all masked gets +0.
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
-int ep_combine(const void *y, const int32_t *slot, const float *topk_weights,
-               int64_t num_tokens, int hidden, int num_topk, void *out, void *stream);
+ep_status_t ep_combine(const void *y, const int32_t *slot, const float *topk_weights,
+                       int64_t num_tokens, int hidden, int num_topk, void *out, void *stream);
 
 /*
  * ep_combine_backward -- gradients of ep_combine.
@@ -375,9 +376,9 @@ int ep_combine(const void *y, const int32_t *slot, const float *topk_weights,
  *                        sum_c g[t,c] * y[slot[t,j],c] accumulated in fp32
  *                        (in an unspecified order), 0 for a masked pair.
  */
-int ep_combine_backward(const void *grad_out, const void *y, const int32_t *slot,
-                        const float *topk_weights, int64_t num_tokens, int hidden, int num_topk,
-                        void *grad_y, float *grad_topk_weights, void *stream);
+ep_status_t ep_combine_backward(const void *grad_out, const void *y, const int32_t *slot,
+                                const float *topk_weights, int64_t num_tokens, int hidden,
+                                int num_topk, void *grad_y, float *grad_topk_weights, void *stream);
 
 /*
  * ep_dispatch_backward -- gradients of ep_dispatch.
@@ -397,9 +398,9 @@ int ep_combine_backward(const void *grad_out, const void *y, const int32_t *slot
  *                         grad_recv_weights is NULL): grad_recv_weights[slot],
  *                         0 for a masked pair.
  */
-int ep_dispatch_backward(const void *grad_recv, const float *grad_recv_weights,
-                         const int32_t *slot, int64_t num_tokens, int hidden, int num_topk,
-                         void *grad_x, float *grad_topk_weights, void *stream);
+ep_status_t ep_dispatch_backward(const void *grad_recv, const float *grad_recv_weights,
+                                 const int32_t *slot, int64_t num_tokens, int hidden, int num_topk,
+                                 void *grad_x, float *grad_topk_weights, void *stream);
 
 /*
  * ---- The per-(token, rank) path: a token travels once to each rank that
@@ -433,8 +434,9 @@ int ep_dispatch_backward(const void *grad_recv, const float *grad_recv_weights,
  * Requires num_tokens * num_topk < 2^31, 1 <= num_topk <= EP_MAX_TOPK,
  * 1 <= num_experts <= EP_MAX_EXPERTS.
  */
-int ep_routing_map(const int64_t *topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                   uint8_t *routing_map, int32_t *num_invalid, void *stream);
+ep_status_t ep_routing_map(const int64_t *topk_idx, int64_t num_tokens, int num_topk,
+                           int num_experts, uint8_t *routing_map, int32_t *num_invalid,
+                           void *stream);
 
 /* Bytes of device workspace ep_rank_layout needs (int32 counts per chunk of
  * 1024 or more global tokens). */
@@ -465,11 +467,12 @@ size_t ep_rank_layout_workspace_size(int64_t tokens_per_rank, int num_experts, i
  *      workspace                ep_rank_layout_workspace_size bytes, device.
  * Requires G*T < 2^31; local_expert_routing_map 4-byte aligned.
  */
-int ep_rank_layout(const uint8_t *global_routing_map, int64_t tokens_per_rank, int num_experts,
-                   int num_ranks, int rank, int k_out, int32_t *sparse_to_dense_map,
-                   uint8_t *local_expert_routing_map, int32_t *recv_src, int64_t *recv_topk_idx,
-                   int32_t *expert_counts, int32_t *num_recv, int32_t *num_overflow,
-                   void *workspace, size_t workspace_bytes, void *stream);
+ep_status_t ep_rank_layout(const uint8_t *global_routing_map, int64_t tokens_per_rank,
+                           int num_experts, int num_ranks, int rank, int k_out,
+                           int32_t *sparse_to_dense_map, uint8_t *local_expert_routing_map,
+                           int32_t *recv_src, int64_t *recv_topk_idx, int32_t *expert_counts,
+                           int32_t *num_recv, int32_t *num_overflow, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * ep_dispatch_ranked -- send this rank's tokens, once per destination rank.
@@ -489,10 +492,11 @@ int ep_rank_layout(const uint8_t *global_routing_map, int64_t tokens_per_rank, i
  *      Rows >= dest_rows are never written (G*T rows always suffice).
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
-int ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk_weights,
-                       int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int num_ranks, const int32_t *sparse_to_dense_map, void *const *dest_x,
-                       float *const *dest_weights, int64_t dest_rows, void *stream);
+ep_status_t ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                               int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                               int num_ranks, const int32_t *sparse_to_dense_map,
+                               void *const *dest_x, float *const *dest_weights, int64_t dest_rows,
+                               void *stream);
 
 /*
  * ep_dispatch_ranked_prequantized -- ep_dispatch_ranked for tokens already
@@ -511,12 +515,13 @@ int ep_dispatch_ranked(const void *x, const int64_t *topk_idx, const float *topk
  *      dest_weights as ep_dispatch_ranked.
  * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
  */
-int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
-                                    const int64_t *topk_idx, const float *topk_weights,
-                                    int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                    int num_ranks, const int32_t *sparse_to_dense_map,
-                                    void *const *dest_q, float *const *dest_scales,
-                                    float *const *dest_weights, int64_t dest_rows, void *stream);
+ep_status_t ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
+                                            const int64_t *topk_idx, const float *topk_weights,
+                                            int64_t num_tokens, int hidden, int num_topk,
+                                            int num_experts, int num_ranks,
+                                            const int32_t *sparse_to_dense_map, void *const *dest_q,
+                                            float *const *dest_scales, float *const *dest_weights,
+                                            int64_t dest_rows, void *stream);
 
 /*
  * ep_dispatch_fused_permute -- the receiving rank's dispatch with the
@@ -558,12 +563,13 @@ int ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scales,
  *      is skipped.
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
-int ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,
-                              const float *const *src_topk_weights, int64_t tokens_per_rank,
-                              int hidden, int num_topk, int num_experts, int num_ranks, int rank,
-                              const int32_t *recv_src, const int64_t *recv_topk_idx,
-                              const int32_t *num_recv, const int32_t *slot, int64_t rows,
-                              void *recv_x, float *recv_weights, void *stream);
+ep_status_t ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,
+                                      const float *const *src_topk_weights, int64_t tokens_per_rank,
+                                      int hidden, int num_topk, int num_experts, int num_ranks,
+                                      int rank, const int32_t *recv_src,
+                                      const int64_t *recv_topk_idx, const int32_t *num_recv,
+                                      const int32_t *slot, int64_t rows, void *recv_x,
+                                      float *recv_weights, void *stream);
 
 /*
  * ep_combine_ranked -- gather this rank's tokens back from every rank.
@@ -576,9 +582,9 @@ int ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *sr
  *      that hold the token (rows >= src_rows read as 0); +0 if none.
  * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
-int ep_combine_ranked(const void *const *src_y, int64_t src_rows,
-                      const int32_t *sparse_to_dense_map, int64_t num_tokens, int hidden,
-                      int num_ranks, void *out, void *stream);
+ep_status_t ep_combine_ranked(const void *const *src_y, int64_t src_rows,
+                              const int32_t *sparse_to_dense_map, int64_t num_tokens, int hidden,
+                              int num_ranks, void *out, void *stream);
 
 /*
  * ep_dispatch_ranked_backward -- backward of ep_dispatch_ranked for this
@@ -615,12 +621,12 @@ int ep_combine_ranked(const void *const *src_y, int64_t src_rows,
  * At least one of the two pairs is given; hidden (with grad_recv_x) must be
  * a positive multiple of 8, at most EP_MAX_HIDDEN.
  */
-int ep_dispatch_ranked_backward(const void *const *grad_recv_x,
-                                const float *const *grad_recv_weights, int64_t src_rows,
-                                const int64_t *topk_idx, const int32_t *sparse_to_dense_map,
-                                int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                int num_ranks, void *grad_x, float *grad_topk_weights,
-                                void *stream);
+ep_status_t ep_dispatch_ranked_backward(const void *const *grad_recv_x,
+                                        const float *const *grad_recv_weights, int64_t src_rows,
+                                        const int64_t *topk_idx, const int32_t *sparse_to_dense_map,
+                                        int64_t num_tokens, int hidden, int num_topk,
+                                        int num_experts, int num_ranks, void *grad_x,
+                                        float *grad_topk_weights, void *stream);
 
 #ifdef __cplusplus
 }
