@@ -12,7 +12,11 @@
 //   read_x_kernel            x read once, 2 KiB per workgroup;
 //   gather_kernel            the dispatch in destination order: each
 //                            workgroup writes one 2 KiB tile of a receive row
-//                            and loads it from x[src[row]] (x read k times).
+//                            and loads it from x[src[row]] (x read k times);
+//   order_row_kernel         whole receive rows, one workgroup each, visited
+//                            in a given order (token order, destination
+//                            order, or windows of tokens expert by expert),
+//                            each loaded from x[src[row]].
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -81,6 +85,27 @@ void gather_kernel(const uint4* __restrict__ x, int nvec, int tpr, int n_rows,
     if (v < nvec) store_row16(buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16), v * 16, d);
 }
 
+// workgroup b copies receive row order[b] from x[src[order[b]]], the whole
+// row (up to 8 vectors per lane) loaded before it is stored
+__global__ __launch_bounds__(kTileLanes)
+void order_row_kernel(const uint4* __restrict__ x, int64_t T, int nvec, int n_rows,
+                      const int32_t* __restrict__ order, const int32_t* __restrict__ src,
+                      uint4* __restrict__ recv)
+{
+    const int r = __builtin_amdgcn_readfirstlane(order[blockIdx.x]);
+    if (r < 0 || r >= n_rows) return;
+    const int t = __builtin_amdgcn_readfirstlane(src[r]);
+    if (t < 0 || t >= T) return;
+    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x + (int64_t)t * nvec, nvec * 16);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(recv + (int64_t)r * nvec, nvec * 16);
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = load_row16<0>(xs, (u * kTileLanes + (int)threadIdx.x) * 16);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        if (u * kTileLanes + (int)threadIdx.x < nvec)
+            store_row16(rs, (u * kTileLanes + (int)threadIdx.x) * 16, v[u]);
+}
 }  // namespace
 
 // recv: [T*k, hidden/8] 16-byte vectors; slot: [T, k] rows of recv (or -1)
@@ -128,5 +153,17 @@ extern "C" int probe_gather(const void* x, int hidden, int n_rows, const int32_t
     if ((int64_t)n_rows * tpr > INT32_MAX) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(n_rows * tpr)), dim3(kTileLanes), 0, s,
                        (const uint4*)x, nvec, tpr, n_rows, src, (uint4*)recv);
+    return (int)hipGetLastError();
+}
+
+// order: a permutation of [0, n_rows); src: [n_rows] tokens in [0, T);
+// rows of at most 8 * 128 vectors (hidden <= 8192)
+extern "C" int probe_order_rows(const void* x, int64_t T, int hidden, int n_rows, const int32_t* order,
+                                const int32_t* src, void* recv, hipStream_t s)
+{
+    const int nvec = hidden / 8;
+    if (nvec > 8 * kTileLanes || n_rows <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(order_row_kernel, dim3((unsigned)n_rows), dim3(kTileLanes), 0, s,
+                       (const uint4*)x, T, nvec, n_rows, order, src, (uint4*)recv);
     return (int)hipGetLastError();
 }

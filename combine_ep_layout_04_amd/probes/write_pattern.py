@@ -9,7 +9,10 @@ Kernels: the library's ep_dispatch; stores_only (its grid, XCD order and
 slot map, no loads of x); write streams of the same bytes in destination
 order (2 KiB and 4 KiB one-shot workgroups, 14 KiB per workgroup in turn);
 a read of x; the dispatch in destination order (gather: x read k times);
-and for the 8-bit cast, the library's E4M3 dispatch next to the same slot
+the stores-only grid under other slot maps (each token's rows adjacent, k
+sequential streams, a random permutation); whole rows copied in token
+order, destination order, or windows of 256 tokens expert by expert; and
+for the 8-bit cast, the library's E4M3 dispatch next to the same slot
 map stored at its code-row size and a stream of its code bytes."""
 
 import argparse
@@ -47,6 +50,7 @@ def main():
     pr.probe_write_stream.argtypes = [vp, i64, i32, vp]
     pr.probe_read_x.argtypes = [vp, i64, vp, vp]
     pr.probe_gather.argtypes = [vp, i32, i32, vp, vp, vp]
+    pr.probe_order_rows.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
 
     w = WORKLOADS["headline"]
     inp = make_inputs(w)
@@ -74,7 +78,28 @@ def main():
         raise SystemExit("ep_layout failed")
     st.synchronize()
     n = int(offsets[E].item())
+    if n != P:
+        raise SystemExit("the probes assume no masked slots")
     wbytes = n * H * 2
+    # other slot maps for the stores-only grid, and visiting orders of the
+    # receive rows (permutations of [0, P)) for the whole-row copy
+    slot_h = slot.cpu().numpy()
+    tok = np.repeat(np.arange(T), k)
+    rows = slot_h.reshape(-1)
+    perm = np.random.default_rng(0).permutation(P)
+    orders = {
+        "token order": rows,
+        "destination order": np.arange(P),
+        "windows of 256 tokens, expert by expert": rows[np.lexsort((tok, inp.topk_idx.reshape(-1),
+                                                                    tok // 256))],
+    }
+    with torch.cuda.stream(st):
+        maps = {"each token's rows adjacent (t*k+j)": torch.arange(P, **i32d).view(T, k),
+                "k sequential streams (j*T+t)": torch.arange(P, **i32d).view(k, T).t().contiguous(),
+                "a random permutation": torch.from_numpy(perm.astype(np.int32)).to(dev).view(T, k)}
+        d_orders = {nm: torch.from_numpy(np.ascontiguousarray(o, dtype=np.int32)).to(dev)
+                    for nm, o in orders.items()}
+    st.synchronize()
     ops = {
         "dispatch (library)": lambda: L.ep_dispatch(x.data_ptr(), T, H, k, slot.data_ptr(), None, 0,
                                                     recv.data_ptr(), None, None, s),
@@ -86,6 +111,12 @@ def main():
         "read x": lambda: pr.probe_read_x(x.data_ptr(), T * H * 2, sink.data_ptr(), s),
         "gather (destination order)": lambda: pr.probe_gather(x.data_ptr(), H, n, src.data_ptr(),
                                                               recv.data_ptr(), s),
+        **{f"stores_only, slot map: {nm}": (lambda m=m: pr.probe_stores_only(T, H, k, m.data_ptr(),
+                                                                              recv.data_ptr(), s))
+           for nm, m in maps.items()},
+        **{f"whole rows in {nm}": (lambda o=o: pr.probe_order_rows(x.data_ptr(), T, H, n, o.data_ptr(),
+                                                                  src.data_ptr(), recv.data_ptr(), s))
+           for nm, o in d_orders.items()},
         # the 8-bit cast writes rows of H code bytes (and H/128 scales): the
         # same slot map stored at that row size, with no loads
         "fp8 dispatch (library, E4M3, fp32 scales)": lambda: L.ep_dispatch(
@@ -97,6 +128,7 @@ def main():
     }
     algo = {"dispatch (library)": T * H * 2 + wbytes + P * 4, "read x": T * H * 2,
             "gather (destination order)": T * H * 2 + wbytes + P * 4,
+            **{f"whole rows in {nm}": T * H * 2 + wbytes + P * 4 for nm in orders},
             "fp8 dispatch (library, E4M3, fp32 scales)": T * H * 2 + n * H + n * (H // 128) * 4 + P * 4,
             "stores_only at the fp8 code row size": n * H,
             "write stream of the fp8 code bytes, 2 KiB workgroups": n * H}
