@@ -6,8 +6,10 @@ capacity, an 8-bit format and scale, and a rank count dividing the experts,
 then checks every entry point the shape allows, to the same gates as the
 dedicated tests:
 
-* layout, dispatch copies, 8-bit codes and scales, the rank layout and the
-  per-rank copies: bit-exact, with sentinel-filled outputs;
+* layout, dispatch copies, 8-bit codes and scales (row-major, and
+  column-major through the two-pass cast), the rank layout, the per-rank
+  copies and the fused permute bounded by the device-side received count:
+  bit-exact, with sentinel-filled outputs;
 * combine, combine backward, dispatch backward and the combine over ranks:
   one bf16 ulp plus the fp32 accumulation bound (and the dot-product bound
   for the weight gradients).
@@ -127,6 +129,25 @@ def test_random_case(seed):
                                            rows=R)
         np.testing.assert_array_equal(host(q)[placed], oq[placed])
         np.testing.assert_array_equal(host(s)[placed].view(np.uint8), os_[placed].view(np.uint8))
+        # column-major scales in two passes, with the layout's src (its
+        # unused entries still hold the sentinel)
+        al = 16 if c["scale"] == "ue8m0" else 4
+        ld = (R + al - 1) // al * al + al
+        q2 = torch.full((R, H), 0xEE, dtype=torch.uint8, device=DEV)
+        s2 = torch.full((H // 128, ld), 0xAB if c["scale"] == "ue8m0" else float("nan"), dtype=sdt,
+                        device=DEV)
+        ep.ep_dispatch_colmajor_scales(x_dev(inp.x_bits), slot, src[:R], None, fmt=c["fmt"],
+                                       scale=c["scale"], scale_ld=ld, rows=R, recv_x=q2,
+                                       recv_scales=s2)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(q2)[placed], oq[placed])
+        hs2 = host(s2)
+        np.testing.assert_array_equal(np.ascontiguousarray(hs2[:, placed].T).view(np.uint8),
+                                      np.ascontiguousarray(os_[placed]).view(np.uint8))
+        keep = np.ones(ld, bool)
+        keep[placed] = False
+        rest = hs2[:, keep]
+        assert np.all(rest == 0xAB) if c["scale"] == "ue8m0" else np.all(np.isnan(rest))
     recv = torch.full((R, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
     rw = torch.full((R,), float("nan"), dtype=torch.float32, device=DEV)
     ep.ep_dispatch(x_dev(inp.x_bits), slot, dev(inp.topk_weights), recv_x=recv, recv_weights=rw,
@@ -215,3 +236,26 @@ def test_random_case(seed):
         acc[ok] += np.abs(float32_from_bf16_bits(ys[d][s2d[ok, d]]).astype(np.float64))
     tol = bf16_ulp(float32_from_bf16_bits(ref).astype(np.float64)) + G * 2.0 ** -24 * acc
     close(bf16_bits(o), ref, tol, "combine over ranks")
+
+    # the receive side of rank 0 with the permute fused in, bounded by the
+    # received count the rank layout left on the device
+    El = E // G
+    xs = [inp.x_bits] + [make_gradient(T, H, 9500 + seed * 10 + r) for r in range(1, G)]
+    ws_all = [inp.topk_weights] + [None] * (G - 1)
+    Lr = oracle.layout(RL.recv_topk_idx, El)
+    prow = max(Lr.n, 1)
+    px = torch.full((prow, H), -3, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pw = torch.full((prow,), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_fused_permute([x_dev(v) for v in xs], lay.recv_src, lay.recv_topk_idx,
+                                 dev(Lr.slot), E, 0, rows=prow,
+                                 src_topk_idx=[dev(i) for i in idx_all],
+                                 src_topk_weights=[None if v is None else dev(v) for v in ws_all],
+                                 num_recv=lay.num_recv, recv_x=px, recv_weights=pw)
+    torch.cuda.synchronize()
+    ox, ow = oracle.dispatch_fused_permute(xs, idx_all, ws_all, E, 0, RL.recv_src, RL.recv_topk_idx,
+                                           Lr.slot, prow)
+    wr = np.zeros(prow, bool)
+    wr[Lr.slot[Lr.slot >= 0]] = True
+    np.testing.assert_array_equal(bf16_bits(px)[wr], ox[wr])
+    assert np.all(bf16_bits(px)[~wr] == 0xFFFD)
+    np.testing.assert_array_equal(host(pw)[wr].view(np.uint32), ow[wr].view(np.uint32))
