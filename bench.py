@@ -55,7 +55,9 @@ KERNEL_SOURCES = {
     "dispatch_bf16": "ep_dispatch.hip", "dispatch_fp8": "ep_dispatch.hip",
     "dispatch_fp8_e5m2_fp32": "ep_dispatch.hip", "dispatch_fp8_e4m3_pow2": "ep_dispatch.hip",
     "dispatch_fp8_e4m3_ue8m0": "ep_dispatch.hip", "dispatch_fp8_e5m2_ue8m0": "ep_dispatch.hip",
-    "dispatch_fp8_prequantized": "ep_dispatch.hip",
+    "dispatch_fp8_prequantized": "ep_dispatch.hip", "dispatch_fp8_e4m3_fp32_colmajor": "ep_dispatch.hip",
+    "dispatch_fp8_e4m3_fp32_colmajor_two_pass": "ep_dispatch.hip",
+    "dispatch_ranked_backward": "ep_ranked.hip",
     "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
     "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
     "dispatch_fused_permute": "ep_ranked.hip", "dispatch_ranked_prequantized": "ep_ranked.hip",

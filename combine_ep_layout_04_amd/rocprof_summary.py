@@ -40,11 +40,14 @@ def _find(d: str, suffix: str):
 
 
 def short_name(name: str) -> str:
-    """``void ep::(anonymous namespace)::k<1, 2>(int, ...)`` -> ``k<1, 2>``."""
+    """``void ep::(anonymous namespace)::k<1, 2>(int, ...)`` or ``void ep::k(...)`` -> ``k<1, 2>``
+    or ``k``."""
     name = name.strip()
     if name.startswith("void "):
         name = name[5:]
     name = name.replace("ep::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    if name.startswith("ep::"):
+        name = name[4:]
     cut = name.find("(")
     if cut > 0 and not name.startswith("("):
         name = name[:cut]
@@ -158,11 +161,16 @@ def _counter_medians(d: str):
 # bytes are summed.
 KERNEL_KEYS = {
     "dispatch_bf16": r"dispatch_bf16_tile_kernel<128>",
-    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 64, 4>",
-    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 64, 4>",
-    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 64, 4>",
-    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 64, 4>",
-    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 64, 4>",
+    "dispatch_fp8": r"dispatch_fp8_tile_kernel<0, 0, 64, 4, false>",
+    "dispatch_fp8_e5m2_fp32": r"dispatch_fp8_tile_kernel<1, 0, 64, 4, false>",
+    "dispatch_fp8_e4m3_pow2": r"dispatch_fp8_tile_kernel<0, 1, 64, 4, false>",
+    "dispatch_fp8_e4m3_ue8m0": r"dispatch_fp8_tile_kernel<0, 2, 64, 4, false>",
+    "dispatch_fp8_e5m2_ue8m0": r"dispatch_fp8_tile_kernel<1, 2, 64, 4, false>",
+    # column-major scales: one pass per token, or the tiled cast into the
+    # workspace followed by the column pass
+    "dispatch_fp8_e4m3_fp32_colmajor": r"dispatch_fp8_kernel<7, 0, 0>",
+    "dispatch_fp8_e4m3_fp32_colmajor_two_pass": (r"dispatch_fp8_tile_kernel<0, 0, 64, 4, true>",
+                                                 r"scales_colmajor_kernel<0, true>"),
     "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<7, 4>",
     "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": (r"combine_backward_grad_y_tile_kernel",
@@ -177,6 +185,9 @@ KERNEL_KEYS = {
     "dispatch_ranked": r"dispatch_ranked_tile_kernel",
     "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64, 7, 4>",
     "combine_ranked": r"combine_ranked_tile_kernel<128>",
+    # the combine over ranks of the row gradients (the same kernel and bytes
+    # as combine_ranked) and the weight-gradient gather
+    "dispatch_ranked_backward": (r"combine_ranked_tile_kernel<128>", r"ranked_weight_grad_kernel"),
     "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
