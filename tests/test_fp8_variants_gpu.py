@@ -354,6 +354,28 @@ def test_column_major_scales_two_pass_odd_shapes(H, k, slot_off):
                               slot_off=slot_off)
 
 
+@pytest.mark.parametrize("T,H,k,E", [
+    (7, 65536, 8, 16),      # hidden = EP_MAX_HIDDEN: 512 blocks per row
+    (40, 2048, 64, 64),     # k = EP_MAX_TOPK: 16 slot rows of 4 per token
+    (300, 1152, 4, 1024),   # E = EP_MAX_EXPERTS, 9 blocks per row
+])
+def test_column_major_scales_two_pass_limits(T, H, k, E):
+    inp = make_random_case(T + H + k, T, H, E, k, mask_frac=0.1, dup_frac=1.0 if k > E else 0.0)
+    print(f"\n[fp8 variants] column-major two-pass limits T={T} H={H} k={k} E={E}", flush=True)
+    L = oracle.layout(inp.topk_idx, E)
+    for fmt, mode in (("e4m3", "fp32"), ("e5m2", "ue8m0")):
+        check_colmajor_staged(inp.x_bits, L.slot, L.src, T * k, fmt, mode, seed=T)
+
+
+def test_column_major_scales_two_pass_zero_tokens():
+    x = torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV)
+    slot = torch.empty((0, 4), dtype=torch.int32, device=DEV)
+    src = torch.empty(0, dtype=torch.int32, device=DEV)
+    q, s, w = ep.ep_dispatch_colmajor_scales(x, slot, src, None, scale_ld=16)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 2048) and s.shape == (16, 16) and w is None
+
+
 def test_column_major_scales_two_pass_short_rows():
     # hidden 1024 (64 units): ep_dispatch_ex's one-pass path, same contract
     inp = make_random_case(95, 100, 1024, 8, 2, mask_frac=0.1)
