@@ -8,13 +8,15 @@
  * (h(t) + j * (E / k)) mod E, a fixed pattern of slots is masked (-1), the
  * weights of a token's unmasked slots are equal and sum to 1, and x holds
  * bf16 values from a fixed integer hash.  The program runs ep_layout,
- * ep_dispatch (bf16) and ep_combine on the null stream and checks what
- * holds at any size:
+ * ep_dispatch (bf16) and ep_combine on the null stream, and
+ * ep_layout_noalloc (no workspace) beside ep_layout, and checks what holds
+ * at any size:
  *   - counts sum to the unmasked pairs, offsets are their exclusive prefix
  *     sum, slots of one expert are consecutive in pair order;
  *   - every dispatched row equals its source token, bit for bit;
  *   - combine of the dispatched rows (identity experts) with weights
- *     summing to 1 returns x (by value: a -0 element comes back +0).
+ *     summing to 1 returns x (by value: a -0 element comes back +0);
+ *   - ep_layout_noalloc writes the same counts, offsets, slots and sources.
  * It prints one line and exits 0 when all hold, 1 otherwise.
  */
 #include <stdint.h>
@@ -37,7 +39,7 @@
 
 #define EP_OK(call)                                                                   \
     do {                                                                              \
-        int s_ = (call);                                                              \
+        ep_status_t s_ = (call);                                                              \
         if (s_ != EP_SUCCESS) {                                                       \
             fprintf(stderr, "%s: %s (%s)\n", #call, ep_status_string(s_), ep_last_error()); \
             exit(1);                                                                  \
@@ -116,6 +118,10 @@ int main(int argc, char **argv)
     uint16_t *d_recv = dev_alloc((size_t)P * H * 2);
     float *d_recv_w = dev_alloc(P * sizeof(float));
     uint16_t *d_out = dev_alloc((size_t)T * H * 2);
+    int32_t *d_counts2 = dev_alloc(E * sizeof(int32_t));
+    int32_t *d_offsets2 = dev_alloc((E + 1) * sizeof(int32_t));
+    int32_t *d_slot2 = dev_alloc(P * sizeof(int32_t));
+    int32_t *d_src2 = dev_alloc(P * sizeof(int32_t));
     HIP_OK(hipMemcpy(d_idx, idx, P * sizeof *idx, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_w, w, P * sizeof *w, hipMemcpyHostToDevice));
     HIP_OK(hipMemcpy(d_x, x, (size_t)T * H * 2, hipMemcpyHostToDevice));
@@ -124,6 +130,7 @@ int main(int argc, char **argv)
                     NULL));
     EP_OK(ep_dispatch(d_x, T, H, k, d_slot, d_w, EP_OUT_BF16, d_recv, NULL, d_recv_w, NULL));
     EP_OK(ep_combine(d_recv, d_slot, d_w, T, H, k, d_out, NULL));
+    EP_OK(ep_layout_noalloc(d_idx, T, k, E, d_counts2, d_offsets2, d_slot2, d_src2, NULL, NULL));
     HIP_OK(hipDeviceSynchronize());
 
     int32_t *counts = malloc(E * sizeof *counts);
@@ -138,6 +145,16 @@ int main(int argc, char **argv)
     HIP_OK(hipMemcpy(recv, d_recv, (size_t)P * H * 2, hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(out, d_out, (size_t)T * H * 2, hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(&inval, d_inval, sizeof inval, hipMemcpyDeviceToHost));
+    int32_t *counts2 = malloc(E * sizeof *counts2);
+    int32_t *offsets2 = malloc((E + 1) * sizeof *offsets2);
+    int32_t *slot2 = malloc(P * sizeof *slot2);
+    int32_t *src = malloc(P * sizeof *src);
+    int32_t *src2 = malloc(P * sizeof *src2);
+    HIP_OK(hipMemcpy(counts2, d_counts2, E * sizeof *counts2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(offsets2, d_offsets2, (E + 1) * sizeof *offsets2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(slot2, d_slot2, P * sizeof *slot2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(src, d_src, P * sizeof *src, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(src2, d_src2, P * sizeof *src2, hipMemcpyDeviceToHost));
 
     /* layout: counts, exclusive offsets, no invalid entries */
     int layout_ok = inval == 0;
@@ -174,11 +191,17 @@ int main(int argc, char **argv)
             bad += bf16_value(out[t * H + c]) != want;
         }
     }
-    const int ok = layout_ok && rows_ok && bad == 0;
+    /* the no-allocation layout: the same outputs (src over the routed rows) */
+    const int noalloc_ok = memcmp(counts, counts2, E * sizeof *counts) == 0 &&
+                           memcmp(offsets, offsets2, (E + 1) * sizeof *offsets) == 0 &&
+                           memcmp(slot, slot2, P * sizeof *slot) == 0 &&
+                           memcmp(src, src2, (size_t)live * sizeof *src) == 0;
+    const int ok = layout_ok && rows_ok && bad == 0 && noalloc_ok;
 
     printf("c_abi_demo T=%lld H=%d E=%d k=%d: %lld of %lld pairs routed; layout %s, rows %s, "
-           "combine %s (%lld elements off)\n",
+           "combine %s (%lld elements off), noalloc %s\n",
            (long long)T, H, E, k, (long long)live, (long long)P, layout_ok ? "ok" : "WRONG",
-           rows_ok ? "ok" : "WRONG", bad == 0 ? "ok" : "WRONG", (long long)bad);
+           rows_ok ? "ok" : "WRONG", bad == 0 ? "ok" : "WRONG", (long long)bad,
+           noalloc_ok ? "ok" : "WRONG");
     return ok ? 0 : 1;
 }
