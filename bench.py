@@ -652,6 +652,19 @@ def main():
         nc = int(c_off[Ec].item())
         bmc = bytes_model(Tc, Hc, kc, nc)
         d_us, c_us = us(c_dis), us(c_com)
+        # context at this size: torch's device-to-device copy of half the
+        # dispatch's bytes into the other half (the same bytes moved), timed
+        # the same way
+        with torch.cuda.stream(stream):
+            cp_src = torch.empty(bmc["dispatch_bf16"] // 2, dtype=torch.uint8, device=dev)
+            cp_dst = torch.empty_like(cp_src)
+
+        def copy_same_bytes():
+            with torch.cuda.stream(stream):
+                cp_dst.copy_(cp_src)
+
+        cp_us = us(time_call(copy_same_bytes, args.steps))
+        del cp_src, cp_dst
         configs[cname] = {
             "T": Tc, "H": Hc, "E": Ec, "k": kc, "dispatched_rows": nc,
             "layout_us": round(us(c_lay), 2),
@@ -659,6 +672,9 @@ def main():
             "combine_us": round(c_us, 2), "combine_GB_per_s": round(bmc["combine"] / c_us / 1e3, 1),
             "dispatch_frac_of_hbm_peak": round(bmc["dispatch_bf16"] / d_us / 1e3 / HBM_PEAK_GBS, 4),
             "combine_frac_of_hbm_peak": round(bmc["combine"] / c_us / 1e3 / HBM_PEAK_GBS, 4),
+            "d2d_copy_us_same_bytes": round(cp_us, 2),
+            "dispatch_frac_of_d2d_copy": round(cp_us / d_us, 4),
+            "combine_frac_of_d2d_copy": round(cp_us * bmc["combine"] / bmc["dispatch_bf16"] / c_us, 4),
         }
         del c_recv, c_out, c_x
 
