@@ -16,7 +16,10 @@
 //   order_row_kernel         whole receive rows, one workgroup each, visited
 //                            in a given order (token order, destination
 //                            order, or windows of tokens expert by expert),
-//                            each loaded from x[src[row]].
+//                            each loaded from x[src[row]]; or, XCD-aware,
+//                            one list of rows per XCD (workgroup b runs on
+//                            XCD b mod 8), so that a window's rows, and its
+//                            tokens' re-reads, stay in one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -86,13 +89,16 @@ void gather_kernel(const uint4* __restrict__ x, int nvec, int tpr, int n_rows,
 }
 
 // workgroup b copies receive row order[b] from x[src[order[b]]], the whole
-// row (up to 8 vectors per lane) loaded before it is stored
+// row (up to 8 vectors per lane) loaded before it is stored.  With per_xcd
+// > 0, order is [8, per_xcd] and workgroup b takes entry b / 8 of list b % 8
+// (entries of -1 pad the shorter lists).
 __global__ __launch_bounds__(kTileLanes)
 void order_row_kernel(const uint4* __restrict__ x, int64_t T, int nvec, int n_rows,
-                      const int32_t* __restrict__ order, const int32_t* __restrict__ src,
+                      const int32_t* __restrict__ order, int per_xcd, const int32_t* __restrict__ src,
                       uint4* __restrict__ recv)
 {
-    const int r = __builtin_amdgcn_readfirstlane(order[blockIdx.x]);
+    const int at = per_xcd > 0 ? (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+    const int r = __builtin_amdgcn_readfirstlane(order[at]);
     if (r < 0 || r >= n_rows) return;
     const int t = __builtin_amdgcn_readfirstlane(src[r]);
     if (t < 0 || t >= T) return;
@@ -156,14 +162,17 @@ extern "C" int probe_gather(const void* x, int hidden, int n_rows, const int32_t
     return (int)hipGetLastError();
 }
 
-// order: a permutation of [0, n_rows); src: [n_rows] tokens in [0, T);
-// rows of at most 8 * 128 vectors (hidden <= 8192)
+// order: a permutation of [0, n_rows) (per_xcd == 0), or 8 lists of
+// per_xcd entries, each a row or -1, together holding every row once;
+// src: [n_rows] tokens in [0, T); rows of at most 8 * 128 vectors
+// (hidden <= 8192)
 extern "C" int probe_order_rows(const void* x, int64_t T, int hidden, int n_rows, const int32_t* order,
-                                const int32_t* src, void* recv, hipStream_t s)
+                                int per_xcd, const int32_t* src, void* recv, hipStream_t s)
 {
     const int nvec = hidden / 8;
-    if (nvec > 8 * kTileLanes || n_rows <= 0) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(order_row_kernel, dim3((unsigned)n_rows), dim3(kTileLanes), 0, s,
-                       (const uint4*)x, T, nvec, n_rows, order, src, (uint4*)recv);
+    if (nvec > 8 * kTileLanes || n_rows <= 0 || per_xcd < 0) return (int)hipErrorInvalidValue;
+    const unsigned grid = per_xcd > 0 ? 8u * (unsigned)per_xcd : (unsigned)n_rows;
+    hipLaunchKernelGGL(order_row_kernel, dim3(grid), dim3(kTileLanes), 0, s,
+                       (const uint4*)x, T, nvec, n_rows, order, per_xcd, src, (uint4*)recv);
     return (int)hipGetLastError();
 }

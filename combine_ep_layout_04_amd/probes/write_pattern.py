@@ -11,7 +11,8 @@ order (2 KiB and 4 KiB one-shot workgroups, 14 KiB per workgroup in turn);
 a read of x; the dispatch in destination order (gather: x read k times);
 the stores-only grid under other slot maps (each token's rows adjacent, k
 sequential streams, a random permutation); whole rows copied in token
-order, destination order, or windows of 256 tokens expert by expert; and
+order, destination order, or windows of 256 tokens expert by expert, and
+in windows of 64 tokens expert by expert with each window on one XCD; and
 for the 8-bit cast, the library's E4M3 dispatch next to the same slot
 map stored at its code-row size and a stream of its code bytes."""
 
@@ -50,7 +51,7 @@ def main():
     pr.probe_write_stream.argtypes = [vp, i64, i32, vp]
     pr.probe_read_x.argtypes = [vp, i64, vp, vp]
     pr.probe_gather.argtypes = [vp, i32, i32, vp, vp, vp]
-    pr.probe_order_rows.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp]
+    pr.probe_order_rows.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp]
 
     w = WORKLOADS["headline"]
     inp = make_inputs(w)
@@ -93,7 +94,20 @@ def main():
         "windows of 256 tokens, expert by expert": rows[np.lexsort((tok, inp.topk_idx.reshape(-1),
                                                                     tok // 256))],
     }
+    # windows of 64 tokens, each on one XCD (window w on XCD w mod 8), its
+    # rows expert by expert: 8 lists padded with -1
+    ex = inp.topk_idx.reshape(-1)
+    lists = [[] for _ in range(8)]
+    for w0 in range(0, T, 64):
+        sel = np.nonzero((tok >= w0) & (tok < w0 + 64))[0]
+        lists[(w0 // 64) % 8].append(rows[sel[np.lexsort((tok[sel], ex[sel]))]])
+    lists = [np.concatenate(li) for li in lists]
+    per_xcd = max(len(li) for li in lists)
+    xcd_lists = np.full((8, per_xcd), -1, np.int32)
+    for i, li in enumerate(lists):
+        xcd_lists[i, :len(li)] = li
     with torch.cuda.stream(st):
+        d_xcd_lists = torch.from_numpy(xcd_lists).to(dev)
         maps = {"each token's rows adjacent (t*k+j)": torch.arange(P, **i32d).view(T, k),
                 "k sequential streams (j*T+t)": torch.arange(P, **i32d).view(k, T).t().contiguous(),
                 "a random permutation": torch.from_numpy(perm.astype(np.int32)).to(dev).view(T, k)}
@@ -114,9 +128,11 @@ def main():
         **{f"stores_only, slot map: {nm}": (lambda m=m: pr.probe_stores_only(T, H, k, m.data_ptr(),
                                                                               recv.data_ptr(), s))
            for nm, m in maps.items()},
-        **{f"whole rows in {nm}": (lambda o=o: pr.probe_order_rows(x.data_ptr(), T, H, n, o.data_ptr(),
+        **{f"whole rows in {nm}": (lambda o=o: pr.probe_order_rows(x.data_ptr(), T, H, n, o.data_ptr(), 0,
                                                                   src.data_ptr(), recv.data_ptr(), s))
            for nm, o in d_orders.items()},
+        "whole rows in windows of 64 tokens on one XCD each, expert by expert": lambda: pr.probe_order_rows(
+            x.data_ptr(), T, H, n, d_xcd_lists.data_ptr(), per_xcd, src.data_ptr(), recv.data_ptr(), s),
         # the 8-bit cast writes rows of H code bytes (and H/128 scales): the
         # same slot map stored at that row size, with no loads
         "fp8 dispatch (library, E4M3, fp32 scales)": lambda: L.ep_dispatch(
@@ -129,6 +145,7 @@ def main():
     algo = {"dispatch (library)": T * H * 2 + wbytes + P * 4, "read x": T * H * 2,
             "gather (destination order)": T * H * 2 + wbytes + P * 4,
             **{f"whole rows in {nm}": T * H * 2 + wbytes + P * 4 for nm in orders},
+            "whole rows in windows of 64 tokens on one XCD each, expert by expert": T * H * 2 + wbytes + P * 4,
             "fp8 dispatch (library, E4M3, fp32 scales)": T * H * 2 + n * H + n * (H // 128) * 4 + P * 4,
             "stores_only at the fp8 code row size": n * H,
             "write stream of the fp8 code bytes, 2 KiB workgroups": n * H}
