@@ -277,7 +277,8 @@ def check_colmajor_staged(x_bits, slot, src, rows, fmt, mode, seed, slot_off=Fal
     every other entry untouched.  ``src`` holds garbage (including valid
     token ids) at every row nothing maps to.  ``slot_off``: the slot table
     starts 4 bytes past a 16-byte boundary (the column pass then reads it
-    one entry at a time)."""
+    one entry at a time).  Seeded weights go along: each mapped row's
+    weight bit for bit, the other rows untouched."""
     T, H = x_bits.shape
     nb = H // 128
     align = 16 if mode == "ue8m0" else 4
@@ -295,10 +296,16 @@ def check_colmajor_staged(x_bits, slot, src, rows, fmt, mode, seed, slot_off=Fal
         d_slot = buf[1:].view(slot.shape)
         d_slot.copy_(dev(slot))
         assert d_slot.data_ptr() % 16 == 4
-    ep.ep_dispatch_colmajor_scales(x_dev(x_bits), d_slot, dev(src_g), None, fmt=fmt, scale=mode,
-                                   scale_ld=ld, rows=rows, recv_x=q, recv_scales=s)
+    wts = rng.random(slot.shape, dtype=np.float32)
+    rw = torch.full((max(rows, 1),), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_colmajor_scales(x_dev(x_bits), d_slot, dev(src_g), dev(wts), fmt=fmt, scale=mode,
+                                   scale_ld=ld, rows=rows, recv_x=q, recv_scales=s,
+                                   recv_weights=rw[:rows])
     torch.cuda.synchronize()
-    oq, os_, _ = oracle.dispatch_quant(x_bits, slot, fmt=fmt, scale=mode, rows=rows)
+    oq, os_, ow = oracle.dispatch_quant(x_bits, slot, wts, fmt=fmt, scale=mode, rows=rows)
+    grw = host(rw)[:rows]
+    np.testing.assert_array_equal(grw[mapped].view(np.uint32), ow[mapped].view(np.uint32))
+    assert np.all(np.isnan(grw[~mapped]))
     gq, gs = host(q), host(s)
     np.testing.assert_array_equal(gq[mapped], oq[mapped])
     assert np.all(gq[~mapped] == 0xEE)
