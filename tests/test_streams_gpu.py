@@ -2,7 +2,8 @@
 arrays and the caller's workspace are the only memory it touches), so
 independent pipelines on different streams can overlap.
 
-Two forward steps (layout -> bf16 and 8-bit dispatch -> combine) with
+Two forward steps (layout -> bf16 and 8-bit dispatch, the 8-bit cast with
+column-major scales through each pipeline's own workspace -> combine) with
 different inputs and shapes are launched interleaved on two streams,
 several rounds, with no synchronisation between the streams; every output
 must equal the one from running the same pipeline alone on the default
@@ -37,7 +38,12 @@ class Pipeline:
             "q": torch.empty((P, H), dtype=torch.uint8, device=DEV),
             "s": torch.empty((P, H // 128), dtype=torch.float32, device=DEV),
             "out": torch.empty((T, H), dtype=torch.bfloat16, device=DEV),
+            "q2": torch.empty((P, H), dtype=torch.uint8, device=DEV),
+            "s2": torch.empty((H // 128, P + 16), dtype=torch.float32, device=DEV),
         }
+        self.ld = P + 16
+        self.cm_ws = torch.empty(max(ep.ep_dispatch_colmajor_workspace_size(T, H), 256),
+                                 dtype=torch.uint8, device=DEV)
         self.ws = torch.empty(max(ep.layout_workspace_size(T, k, E), 256), dtype=torch.uint8,
                               device=DEV)
 
@@ -56,6 +62,10 @@ class Pipeline:
                                    stream=stream),
             lambda: ep.ep_dispatch(self.x, o["slot"], None, fp8=True, recv_x=o["q"],
                                    recv_scales=o["s"], stream=stream),
+            lambda: ep.ep_dispatch_colmajor_scales(self.x, o["slot"], o["src"], None,
+                                                   scale_ld=self.ld, recv_x=o["q2"],
+                                                   recv_scales=o["s2"], workspace=self.cm_ws,
+                                                   stream=stream),
             lambda: ep.ep_combine(o["recv"], o["slot"], self.w, out=o["out"], stream=stream),
         ]
 
