@@ -15,7 +15,8 @@ receive buffers past 4 GiB (row byte offsets that need 64 bits).
   element by element against the oracle.
 * fp8 dispatch into 4.43 GB of codes: sampled tokens (again including the
   rows past 4 GiB) bit-exact against the oracle's cast; every copy of a
-  token's codes and scales equal.
+  token's codes and scales equal; the two-pass column-major cast into a
+  second 4.43 GB buffer gives the same codes and the scales transposed.
 * Once-per-rank dispatch from rank 7 of 8 (65536 tokens per rank, hidden
   7168), whose rows sit past 4 GiB in every receive buffer, then the
   combine over ranks: every written row equals its token, sampled tokens
@@ -187,6 +188,19 @@ def test_fp8_dispatch_past_4gib():
         rows_j = torch.from_numpy(L.slot[ts, j].astype(np.int64)).to(DEV)
         np.testing.assert_array_equal(host(q[rows_j]), o_q)
         np.testing.assert_array_equal(host(s[rows_j]).view(np.uint32), o_s.view(np.uint32))
+
+    # the two-pass column-major cast into a second buffer: the same codes at
+    # every routed row, and its scale columns the row-major scales transposed
+    n_rows = L.n
+    ld = (P + 3) // 4 * 4
+    q2 = torch.full((P, H), 0xEE, dtype=torch.uint8, device=DEV)
+    s2 = torch.full((nb, ld), float("nan"), dtype=torch.float32, device=DEV)
+    src_d = torch.from_numpy(L.src.astype(np.int32)).to(DEV)
+    ep.ep_dispatch_colmajor_scales(x_d, slot, src_d, None, scale_ld=ld, recv_x=q2, recv_scales=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(q2[:n_rows], q[:n_rows])
+    assert torch.equal(s2[:, :n_rows].t().contiguous().view(torch.int32), s[:n_rows].view(torch.int32))
+    del q2, s2
 
 
 def test_ranked_dispatch_combine_past_4gib():
