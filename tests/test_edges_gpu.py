@@ -15,7 +15,7 @@ import torch
 import oracle
 from combine_ep_layout_04_amd import ep
 from combine_ep_layout_04_amd.inputs import (
-    bf16_bits_from_float32, float32_from_bf16_bits, make_random_case,
+    bf16_bits_from_float32, float32_from_bf16_bits, make_gradient, make_random_case,
 )
 
 from gpu_util import DEV, bf16_bits, bf16_ulp, dev, host, x_dev
@@ -267,3 +267,67 @@ def test_deterministic_and_side_stream():
             assert a[key] == b[key], key
             continue
         np.testing.assert_array_equal(np.asarray(a[key]).view(np.uint8), np.asarray(b[key]).view(np.uint8))
+
+
+def test_combine_non_finite_inputs():
+    # expert rows holding +-inf and NaN: a sum with a NaN term, or with
+    # infinities of both signs, is NaN on both sides (the NaN's sign and
+    # payload are not compared); a sum with infinities of one sign is that
+    # infinity; every other element is within the usual gate
+    T, H, E, k = 96, 256, 8, 4
+    inp = make_random_case(33, T, H, E, k, mask_frac=0.1)
+    L = oracle.layout(inp.topk_idx, E)
+    P = T * k
+    rng = np.random.default_rng(34)
+    y = make_gradient(P, H, 35)
+    for bits, count in ((0x7F80, 60), (0xFF80, 60), (0x7FC1, 30), (0xFFC0, 30)):
+        rows = rng.integers(0, max(L.n, 1), count)
+        cols = rng.integers(0, H, count)
+        y[rows, cols] = bits
+    out = ep.ep_combine(x_dev(y), dev(L.slot), dev(inp.topk_weights), rows=P)
+    torch.cuda.synchronize()
+    got = float32_from_bf16_bits(bf16_bits(out)).astype(np.float64)
+    ref_bits = oracle.combine(y, L.slot, inp.topk_weights)
+    want = float32_from_bf16_bits(ref_bits).astype(np.float64)
+    assert np.isnan(want).any() and np.isinf(want).any()
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    inf = np.isinf(want)
+    np.testing.assert_array_equal(got[inf], want[inf])
+    fin = np.isfinite(want)
+    tol = combine_tolerance(y, L.slot, inp.topk_weights, ref_bits)
+    assert np.all(np.abs(got[fin] - want[fin]) <= tol[fin])
+
+
+def test_combine_unit_weights_fp32_partial_overflow():
+    # unit weights (the unweighted combine) over rows near the bf16 maximum:
+    # the kernel accumulates in fp32 in slot order, so a partial sum past the
+    # fp32 maximum becomes an infinity even where the exact sum is finite
+    # (+m + m - m).  Checked against that fp32 accumulation written out in
+    # numpy; the exact-sum oracle is compared where no partial sum overflows.
+    T, H, k = 64, 128, 3
+    m = 0x7F70  # bf16 3.19e38: two of them overflow fp32
+    P = T * k
+    slot = np.arange(P, dtype=np.int32).reshape(T, k)
+    rng = np.random.default_rng(36)
+    y = make_gradient(P, H, 37)
+    pick = rng.random((T, H)) < 0.3
+    for j, sign in ((0, 0), (1, 0), (2, 0x8000)):
+        yj = y[j::k]
+        yj[pick] = m | sign
+    out = ep.ep_combine(x_dev(y), dev(slot), None, rows=P)
+    torch.cuda.synchronize()
+    got = bf16_bits(out)
+    acc = np.zeros((T, H), np.float32)
+    with np.errstate(over="ignore"):
+        for j in range(k):
+            acc = acc + float32_from_bf16_bits(y[j::k])    # fp32 adds, slot order
+    u = acc.view(np.uint32).astype(np.uint64)
+    want = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # RNE (no NaN here)
+    assert np.isinf(acc[pick]).all() and not np.isnan(acc).any()
+    np.testing.assert_array_equal(got, want)
+    ref = oracle.combine(y, slot, None)
+    assert np.all(ref[pick] == m)                       # the exact sum is finite there
+    tol = combine_tolerance(y, slot, None, ref)
+    g64 = float32_from_bf16_bits(got).astype(np.float64)
+    r64 = float32_from_bf16_bits(ref).astype(np.float64)
+    assert np.all(np.abs(g64 - r64)[~pick] <= tol[~pick])
