@@ -27,11 +27,18 @@
 //               histogram -- every expert's total (for offsets) and its rows
 //               in earlier chunks -- reading each expert's chunk counts as
 //               16-byte vectors; workgroup 0 also writes counts, offsets and
-//               num_invalid.  Then it walks its chunk in batches of 256
-//               pairs: every pair sets its bit in an LDS bit-matrix row of
-//               its expert (256 bits = 8 words per expert); its rank among
-//               earlier pairs of the same expert is a popcount of the bits
-//               below its own, so no position depends on atomic timing.
+//               num_invalid.  Then it ranks its chunk's pairs.  Up to 256
+//               experts (layout_scatter_wide_kernel): 1024 lanes, 1024 pairs
+//               at a time, a pair's rank within its wavefront found by
+//               ballots over its expert id's bits, and per-(wavefront,
+//               expert) base rows from an exclusive sum over the
+//               wavefronts (at T=8192, k=8, E=256: 6.6 against 8.7 us, the
+//               layout 14.0 against 16.1 us by HIP events).  More experts
+//               (layout_scatter_kernel): 256 lanes, batches of 256 pairs,
+//               every pair setting its bit in an LDS bit-matrix row of its
+//               expert (256 bits = 8 words per expert), its rank the
+//               popcount of the bits below its own.  Either way no position
+//               depends on atomic timing.
 //
 // Segment placement (DeepEP page, "Prefix Sum Interpretation for Expert
 // Token Counts": in expand mode an expert's rows start at
@@ -257,6 +264,144 @@ void layout_scatter_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64
     }
 }
 
+// Wide scatter, for at most kWideMaxExperts experts: the same result as
+// layout_scatter_kernel from workgroups of 16 wavefronts, which take their
+// chunk 1024 pairs at a time (one per lane) and rank them without a bit
+// matrix: within a wavefront, the lanes holding the same expert are found
+// by ballots over the id's bits (the popcount of the lower ones is a pair's
+// rank there), each wavefront's per-expert count is written by that
+// expert's lowest lane, and an exclusive sum over the wavefronts, per
+// expert, gives every (wavefront, expert) base row.  Four lanes share each
+// expert's histogram row in the prologue.
+constexpr int kWideThreads = 1024;
+constexpr int kWideWaves = kWideThreads / 64;
+constexpr int kWideMaxExperts = 256;
+
+__global__ __launch_bounds__(kWideThreads)
+void layout_scatter_wide_kernel(const int64_t* __restrict__ idx, int64_t pairs, int64_t chunk, int k,
+                                int E, int cpad, int num_chunks, int alignment, int capacity,
+                                const int32_t* __restrict__ hist, const int32_t* __restrict__ bad,
+                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                int32_t* __restrict__ slot, int32_t* __restrict__ src,
+                                int32_t* __restrict__ num_invalid, int32_t* __restrict__ num_dropped)
+{
+    __shared__ int32_t base[kWideMaxExperts];
+    __shared__ int32_t total[kWideMaxExperts];
+    __shared__ int32_t seg[kWideMaxExperts];
+    __shared__ int32_t wcnt[kWideWaves][kWideMaxExperts];
+    __shared__ int32_t waves[kWideWaves];
+    __shared__ int32_t nbad, ndrop;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int64_t c = blockIdx.x;
+
+    // 1. every expert's total and its rows in earlier chunks: lanes 4e..4e+3
+    // each sum a quarter of expert e's histogram row (16-byte vectors)
+    {
+        const int e = tid >> 2, part = tid & 3;
+        int32_t a = 0, b = 0;
+        if (e < E) {
+            const int nv = cpad / 4;
+            const int4* v = reinterpret_cast<const int4*>(hist + (int64_t)e * cpad);
+            for (int q = part; q < nv; q += 4) {
+                const int4 h = v[q];
+                const int c0 = 4 * q;
+                a += h.x + h.y + h.z + h.w;
+                b += (c0 < c ? h.x : 0) + (c0 + 1 < c ? h.y : 0) + (c0 + 2 < c ? h.z : 0) +
+                     (c0 + 3 < c ? h.w : 0);
+            }
+        }
+        a += __shfl_xor(a, 1, 64);
+        b += __shfl_xor(b, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        b += __shfl_xor(b, 2, 64);
+        if (e < E && part == 0) {
+            total[e] = a;
+            base[e] = b;
+        }
+    }
+    if (tid == 0) {
+        nbad = 0;
+        ndrop = 0;
+    }
+    __syncthreads();
+
+    // 2. segment starts (thread e owns expert e)
+    const int32_t tot = tid < E ? total[tid] : 0;
+    const int32_t padded = tid < E ? (tot + alignment - 1) / alignment * alignment : 0;
+    int32_t n = 0;
+    const int32_t run = block_exclusive_scan(padded, waves, &n);
+    if (tid < E) {
+        const int32_t start = capacity > 0 ? tid * capacity : run;
+        seg[tid] = start;
+        base[tid] += start;
+        if (c == 0) {
+            counts[tid] = capacity > 0 ? min(tot, capacity) : tot;
+            offsets[tid] = start;
+            if (capacity > 0 && tot > capacity) atomicAdd(&ndrop, tot - capacity);
+        }
+    }
+    if (c == 0) {
+        if (tid == 0) offsets[E] = capacity > 0 ? E * capacity : n;
+        if (num_invalid) {
+            int32_t bb = 0;
+            for (int cc = tid; cc < num_chunks; cc += kWideThreads) bb += bad[cc];
+            if (bb) atomicAdd(&nbad, bb);
+        }
+    }
+    __syncthreads();
+    if (c == 0 && tid == 0) {
+        if (num_invalid) *num_invalid = nbad;
+        if (num_dropped) *num_dropped = ndrop;
+    }
+
+    // 3. the chunk, 1024 pairs at a time
+    const int64_t begin = c * chunk;
+    const int64_t end = min(begin + chunk, pairs);
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    for (int64_t b0 = begin; b0 < end; b0 += kWideThreads) {
+        const int64_t i = b0 + tid;
+        const bool live = i < end;
+        const int64_t e64 = live ? idx[i] : -1;
+        const bool ok = e64 >= 0 && e64 < E;
+        const int ex = ok ? (int)e64 : 0;
+        uint64_t m = __ballot(ok);
+        for (int bt = 0; bt < nbits; ++bt) {
+            const bool bit = ok && ((ex >> bt) & 1);
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const uint64_t below = m & ((1ull << lane) - 1ull);
+        for (int q = tid; q < kWideWaves * kWideMaxExperts; q += kWideThreads) (&wcnt[0][0])[q] = 0;
+        __syncthreads();
+        if (ok && below == 0) wcnt[w][ex] = __popcll(m);     // the expert's lowest lane
+        __syncthreads();
+        if (tid < E) {
+            int32_t r = base[tid];
+            for (int v = 0; v < kWideWaves; ++v) {
+                const int32_t cnt = wcnt[v][tid];
+                wcnt[v][tid] = r;
+                r += cnt;
+            }
+            base[tid] = r;
+        }
+        __syncthreads();
+        if (ok) {
+            const int32_t r = wcnt[w][ex] + __popcll(below);
+            if (capacity > 0 && r - seg[ex] >= capacity) {
+                slot[i] = -1;                       // past the expert's capacity
+            } else {
+                slot[i] = r;
+                if (src) src[r] = (int32_t)(i / k);
+            }
+        } else if (live) {
+            slot[i] = -1;
+        }
+        __syncthreads();
+    }
+}
+
 static_assert(kMaxExperts == kLayoutScratchExperts, "scratch sized for EP_MAX_EXPERTS");
 
 // ---- one launch for small inputs ----------------------------------------
@@ -474,9 +619,16 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_to
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
 
-    hipLaunchKernelGGL(layout_scatter_kernel, dim3((unsigned)C), dim3(kLayoutThreads), 0, stream,
-                       topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C, alignment,
-                       capacity, hist, bad, counts, offsets, slot, src, num_invalid, num_dropped);
+    if (num_experts <= kWideMaxExperts)
+        hipLaunchKernelGGL(layout_scatter_wide_kernel, dim3((unsigned)C), dim3(kWideThreads), 0,
+                           stream, topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C,
+                           alignment, capacity, hist, bad, counts, offsets, slot, src, num_invalid,
+                           num_dropped);
+    else
+        hipLaunchKernelGGL(layout_scatter_kernel, dim3((unsigned)C), dim3(kLayoutThreads), 0, stream,
+                           topk_idx, pairs, chunk, num_topk, num_experts, (int)Cp, (int)C,
+                           alignment, capacity, hist, bad, counts, offsets, slot, src, num_invalid,
+                           num_dropped);
     return hipGetLastError();
 }
 

@@ -176,7 +176,7 @@ KERNEL_KEYS = {
     "combine_backward": (r"combine_backward_grad_y_tile_kernel",
                          r"combine_backward_kernel<128, 7, false>"),
     "layout_count": r"layout_count_kernel\(",
-    "layout_scatter": r"layout_scatter_kernel\(",
+    "layout_scatter": r"layout_scatter(_wide)?_kernel\(",
     "routing_map": r"routing_map_kernel\(",
     "rank_count": r"rank_count_kernel<",
     "rank_scatter": r"rank_scatter_kernel<",
