@@ -2,7 +2,8 @@
 scratch) against ep_layout with a caller workspace, through the C ABI, bit
 for bit: counts, offsets, slot, src and num_invalid, on consecutive calls
 whose second input is smaller than the first (the scratch keeps the first
-call's contents), and on the largest shape the scratch is sized for."""
+call's contents), on the largest shape the scratch is sized for, and
+captured in a HIP graph and replayed (the callers it is for)."""
 
 import ctypes
 
@@ -113,3 +114,54 @@ def test_noalloc_rejects_bad_arguments():
     assert st == ep.EP_INVALID_ARGUMENT
     st = L.ep_layout_noalloc(None, 16, 2, 2048, None, None, None, None, None, None)
     assert st != 0
+
+
+def test_noalloc_in_a_captured_graph():
+    # the callers this entry point is for: a graph captured once and
+    # replayed.  Two layouts in one graph (sharing the scratch one after the
+    # other), replayed three times with an eager no-allocation call between
+    # replays; every replay equals ep_layout with a workspace, bit for bit
+    i32 = dict(dtype=torch.int32, device=DEV)
+    cases = [(make_inputs(WORKLOADS["headline"]).topk_idx, 256),
+             (routing(4096, 4, 64, seed=21, invalid=0.01, masked=0.05), 64)]
+    print("\n[no-alloc] captured graph: headline and T=4096 k=4 E=64 layouts", flush=True)
+    refs, outs, idxs = [], [], []
+    for idx_np, E in cases:
+        T, k = idx_np.shape
+        idx = torch.from_numpy(idx_np).to(DEV)
+        idxs.append(idx)
+        refs.append([t.clone() for t in ep.ep_layout(idx, E)])
+        outs.append((torch.empty(E, **i32), torch.empty(E + 1, **i32), torch.empty((T, k), **i32),
+                     torch.empty(T * k, **i32), torch.empty(1, **i32)))
+    torch.cuda.synchronize()
+
+    def step():
+        for (idx_np, E), idx, o in zip(cases, idxs, outs):
+            ep.ep_layout_noalloc(idx, E, *o)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                      # warm-up (and the device's scratch address)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    other = torch.from_numpy(routing(300, 6, 32, seed=22)).to(DEV)
+    scratch_outs = (torch.empty(32, **i32), torch.empty(33, **i32), torch.empty((300, 6), **i32))
+    for rep in range(3):
+        for o in outs:
+            for t in o:
+                t.fill_(-55)
+        ep.ep_layout_noalloc(other, 32, *scratch_outs)   # eager use of the same scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (idx_np, E), ref, o in zip(cases, refs, outs):
+            n = int(ref[1][E].item())
+            for name, a, b in zip(("counts", "offsets", "slot"), ref[:3], o[:3]):
+                assert torch.equal(a.view(-1), b.view(-1)), f"replay {rep}: {name}"
+            assert torch.equal(ref[3][:n], o[3][:n]), f"replay {rep}: src"
+            assert torch.equal(ref[4], o[4]), f"replay {rep}: num_invalid"
