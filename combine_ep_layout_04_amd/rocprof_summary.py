@@ -6,10 +6,17 @@
     python -m combine_ep_layout_04_amd.rocprof_summary trace DIR --cmd "..." > profiles/X.md
     python -m combine_ep_layout_04_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \
         --cmd "..." --out profiles/hbm_traffic_headline.txt
+    python -m combine_ep_layout_04_amd.rocprof_summary sequence DIR --kernel NAME \
+        --labels a,b,c --per 3 --cmd "..."
 
 ``stats`` reads ``*_kernel_stats.csv`` (from ``--kernel-trace --stats``,
 without ``-T`` so that template instances stay apart) and prints each
 kernel's name without its namespace and argument list;
+``sequence`` splits one kernel's dispatches, in dispatch order, into
+consecutive groups of ``--per`` launches named by ``--labels`` (a driver
+that runs the same kernel under several inputs) and reports each group's
+median of every counter, with write latency and writes in flight derived
+when the EA write counters are present;
 ``pmc`` reads ``*_counter_collection.csv`` (from ``--pmc``) and reports the
 mean counter value per dispatch for each kernel; ``counters`` makes one row
 per kernel with the median per dispatch of each counter; ``traffic`` takes one
@@ -222,15 +229,47 @@ def traffic(fetch_dir: str, write_dir: str, digest, cmd: str):
     return lines
 
 
+def sequence(d: str, kernel: str, labels, per: int):
+    """Median counters per group of ``per`` consecutive dispatches of
+    ``kernel`` (dispatch order), one row per label."""
+    by = defaultdict(dict)
+    for f in _find(d, "counter_collection.csv"):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel not in short_name(r["Kernel_Name"]):
+                    continue
+                c = by[int(r["Dispatch_Id"])]
+                c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    runs = [by[k] for k in sorted(by)]
+    if len(runs) != per * len(labels):
+        sys.exit(f"{len(runs)} dispatches of {kernel}, expected {per} x {len(labels)}")
+    cols = sorted({c for r in runs for c in r})
+    derived = {"TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum", "GRBM_GUI_ACTIVE"} <= set(cols)
+    head = ["input"] + cols + (["write latency (cycles)", "writes in flight"] if derived else [])
+    out = ["| " + " | ".join(head) + " |", "|---" * len(head) + "|"]
+    for i, lab in enumerate(labels):
+        grp = runs[per * i: per * (i + 1)]
+        med = {c: statistics.median(g.get(c, 0.0) for g in grp) for c in cols}
+        cells = [f"{med[c]:.0f}" for c in cols]
+        if derived:
+            cells += [f"{med['TCC_EA0_WRREQ_LEVEL_sum'] / max(med['TCC_EA0_WRREQ_sum'], 1):.0f}",
+                      f"{med['TCC_EA0_WRREQ_LEVEL_sum'] / max(med['GRBM_GUI_ACTIVE'], 1):.0f}"]
+        out.append(f"| {lab} | " + " | ".join(cells) + " |")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "pmc", "counters", "traffic", "trace"])
+    ap.add_argument("kind", choices=["stats", "pmc", "counters", "traffic", "trace", "sequence"])
     ap.add_argument("dir")
     ap.add_argument("dir2", nargs="?")
     ap.add_argument("--cmd", required=True, help="the command(s) that produced the data")
     ap.add_argument("--title", default="")
     ap.add_argument("--note", default="", help="a paragraph printed under the command")
     ap.add_argument("--out")
+    ap.add_argument("--kernel", help="sequence: the kernel whose dispatches are grouped")
+    ap.add_argument("--labels", help="sequence: comma-separated group names, in dispatch order")
+    ap.add_argument("--per", type=int, default=3, help="sequence: dispatches per group")
     a = ap.parse_args()
     if a.kind == "traffic":
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -245,7 +284,10 @@ def main():
     lines = [f"# {a.title or a.kind}", "", "Command:", "", "```", a.cmd, "```", ""]
     if a.note:
         lines += [a.note, ""]
-    lines += {"stats": stats, "pmc": pmc, "counters": counters, "trace": trace}[a.kind](a.dir)
+    if a.kind == "sequence":
+        lines += sequence(a.dir, a.kernel, a.labels.split(","), a.per)
+    else:
+        lines += {"stats": stats, "pmc": pmc, "counters": counters, "trace": trace}[a.kind](a.dir)
     print("\n".join(lines))
 
 
