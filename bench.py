@@ -57,6 +57,8 @@ KERNEL_SOURCES = {
     "dispatch_fp8_e4m3_ue8m0": "ep_dispatch.hip", "dispatch_fp8_e5m2_ue8m0": "ep_dispatch.hip",
     "dispatch_fp8_prequantized": "ep_dispatch.hip", "dispatch_fp8_e4m3_fp32_colmajor": "ep_dispatch.hip",
     "dispatch_fp8_e4m3_fp32_colmajor_two_pass": "ep_dispatch.hip",
+    "dispatch_fp8_prequantized_colmajor": "ep_dispatch.hip",
+    "dispatch_fp8_prequantized_colmajor_two_pass": "ep_dispatch.hip",
     "dispatch_ranked_backward": "ep_ranked.hip",
     "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
     "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
@@ -126,6 +128,13 @@ def ranked_bytes_model(T, H, k, G, pairs):
         # written per slot
         "dispatch_ranked_backward": pairs * H * 2 + T * H * 2 + T * G * 4 + T * k * 16,
     }
+
+
+def variant_bytes_key(name: str) -> str:
+    """The bytes-model entry of an 8-bit variant line."""
+    if name.startswith("prequantized"):
+        return "dispatch_prequantized"
+    return "dispatch_fp8_ue8m0" if "ue8m0" in name else "dispatch_fp8"
 
 
 def read_traffic(kernel_key: str):
@@ -498,6 +507,16 @@ def main():
     variants["prequantized"] = time_call(lambda: check(L.ep_dispatch_prequantized(
         xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
         sc.data_ptr(), None, 0, s), "ep_dispatch_prequantized"), args.steps)
+    # pre-quantized rows with column-major scales: one pass, and two (the
+    # code rows, then the columns straight from the token scales)
+    variants["prequantized_colmajor"] = time_call(lambda: check(L.ep_dispatch_prequantized(
+        xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), None, q.data_ptr(),
+        sc.data_ptr(), None, P, s), "ep_dispatch_prequantized"), args.steps)
+    variants["prequantized_colmajor_two_pass"] = time_call(lambda: check(
+        L.ep_dispatch_prequantized_colmajor(
+            xq_tok.data_ptr(), xs_tok.data_ptr(), T, H, k, slotf.data_ptr(), srcf.data_ptr(), None,
+            q.data_ptr(), sc.data_ptr(), None, P, P, s), "ep_dispatch_prequantized_colmajor"),
+        args.steps)
 
     # ---- per-(token, rank) path: G = 8 ranks of the headline shape on this
     # device (rank 0 holds the headline tokens, ranks 1..7 uniform routing);
@@ -724,9 +743,7 @@ def main():
                               workload="fp8: headline shape, 1% of rows x100"),
         "combine_backward": entry(cb_us, bytes=bm["combine_backward"]),
         "dispatch_backward": entry(db_us, bytes=bm["dispatch_backward"]),
-        **{f"dispatch_fp8_{name}": entry(v, bytes=bmf["dispatch_fp8_ue8m0" if "ue8m0" in name else
-                                                      ("dispatch_prequantized" if name == "prequantized"
-                                                       else "dispatch_fp8")])
+        **{f"dispatch_fp8_{name}": entry(v, bytes=bmf[variant_bytes_key(name)])
            for name, v in variants.items()},
         "routing_map": entry(rm_us),
         "rank_layout": entry(rk_us, ranks=G),

@@ -312,6 +312,44 @@ ep_status_t ep_dispatch_prequantized(const void* x_q, const float* x_scales, int
                     "ep_dispatch_prequantized launch");
 }
 
+ep_status_t ep_dispatch_prequantized_colmajor(const void* x_q, const float* x_scales,
+                                              int64_t num_tokens, int hidden, int num_topk,
+                                              const int32_t* slot, const int32_t* src,
+                                              const float* topk_weights, void* recv_q,
+                                              float* recv_scales, float* recv_weights,
+                                              int64_t scale_ld, int64_t num_rows, void* stream)
+{
+    g_last_error[0] = '\0';
+    ep_status_t st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    st = check_hidden(hidden, 128);
+    if (st) return st;
+    if (scale_ld <= 0) return fail(EP_INVALID_ARGUMENT, "scale_ld must be positive (column-major)");
+    st = check_scale_ld(scale_ld, 4);
+    if (st) return st;
+    if (num_rows < 0 || num_rows > INT32_MAX)
+        return fail(EP_INVALID_ARGUMENT, "num_rows %lld outside [0, 2^31-1] (slot entries are int32)",
+                    (long long)num_rows);
+    if (scale_ld < num_rows)
+        return fail(EP_INVALID_ARGUMENT, "scale_ld %lld is below num_rows %lld", (long long)scale_ld,
+                    (long long)num_rows);
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x_q || !x_scales || !slot || !src || !recv_q || !recv_scales)
+        return fail(EP_INVALID_ARGUMENT,
+                    "x_q, x_scales, slot, src, recv_q and recv_scales are required");
+    if (!aligned16(x_q) || !aligned16(recv_q))
+        return fail(EP_INVALID_ARGUMENT, "x_q and recv_q must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(x_scales) & 3u) || (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+    if (recv_weights && !topk_weights)
+        return fail(EP_INVALID_ARGUMENT, "recv_weights needs topk_weights");
+    return from_hip(ep::launch_dispatch_prequant_colmajor(
+                        x_q, x_scales, num_tokens, hidden, num_topk, slot, src, topk_weights, recv_q,
+                        recv_scales, recv_weights, scale_ld, num_rows,
+                        static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_prequantized_colmajor launch");
+}
+
 ep_status_t ep_combine(const void* y, const int32_t* slot, const float* topk_weights,
                        int64_t num_tokens, int hidden, int num_topk, void* out, void* stream)
 {

@@ -636,7 +636,7 @@ __device__ __forceinline__ bool row_is_slot(const int32_t* __restrict__ s, int k
 
 template <int SM, bool V4>
 __global__ __launch_bounds__(256)
-void scales_colmajor_kernel(const void* __restrict__ ws, const int32_t* __restrict__ src,
+void scales_colmajor_kernel(const void* __restrict__ ws, bool vec, const int32_t* __restrict__ src,
                             const int32_t* __restrict__ slot, int64_t T, int k, int nb,
                             int64_t rows, void* __restrict__ scales, int64_t ld)
 {
@@ -645,7 +645,7 @@ void scales_colmajor_kernel(const void* __restrict__ ws, const int32_t* __restri
     if (r >= rows) return;
     const int32_t t = src[r];
     if (t < 0 || t >= T) return;
-    if ((nb & 3) != 0) {       // one scale at a time
+    if (!vec) {                // one scale at a time
         if (!row_is_slot<V4>(slot + (int64_t)t * k, k, r)) return;
         for (int b = part; b < nb; b += parts) {
             if (SM == kScaleUe8m0)
@@ -731,6 +731,7 @@ void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restr
             }
         }
     }
+    if (recv_s == nullptr) return;    // scales written by a later pass
     // the scale row: 64 floats per round
     for (int b0 = 0; b0 < nb; b0 += 64) {
         const int b = b0 + tid;
@@ -920,6 +921,32 @@ size_t colmajor_workspace_bytes(int64_t num_tokens, int hidden, int scale_mode)
     return (bytes + 255) & ~(size_t)255;
 }
 
+// The column pass: rows [0, rows) of [nb, scale_ld] scales from per-token
+// scale rows ws [T, nb] (fp32, or bytes for UE8M0); vec: nb % 4 == 0 and
+// ws 16-byte aligned, so each row is read in pieces of 4 scales.
+static hipError_t launch_scales_colmajor(const void* ws, bool vec, const int32_t* src,
+                                         const int32_t* slot, int64_t num_tokens, int num_topk,
+                                         int nb, int scale_mode, int64_t rows, void* recv_scales,
+                                         int64_t scale_ld, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    const int pieces = vec ? nb / 4 : nb;
+    const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)std::min(kColmajorParts, pieces));
+    const bool v4 = num_topk % 4 == 0 && (reinterpret_cast<uintptr_t>(slot) & 15) == 0;
+#define EP_CM_COLS(SM, V4)                                                                      \
+    hipLaunchKernelGGL((scales_colmajor_kernel<SM, V4>), grid, dim3(256), 0, stream, ws, vec, src, \
+                       slot, num_tokens, num_topk, nb, rows, recv_scales, scale_ld)
+    if (scale_mode == kScaleUe8m0) {
+        if (v4) EP_CM_COLS(kScaleUe8m0, true);
+        else EP_CM_COLS(kScaleUe8m0, false);
+    } else {
+        if (v4) EP_CM_COLS(kScaleFp32, true);
+        else EP_CM_COLS(kScaleFp32, false);
+    }
+#undef EP_CM_COLS
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch_fp8_colmajor(const void* x, int64_t num_tokens, int hidden,
                                         int num_topk, const int32_t* slot, const int32_t* src,
                                         const float* topk_weights, int format, int scale_mode,
@@ -966,21 +993,8 @@ hipError_t launch_dispatch_fp8_colmajor(const void* x, int64_t num_tokens, int h
 #undef EP_CM_LAUNCH
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || rows == 0) return err;
-    const int pieces = (nb & 3) == 0 ? nb / 4 : nb;
-    const dim3 grid((unsigned)((rows + 255) / 256), (unsigned)std::min(kColmajorParts, pieces));
-    const bool v4 = num_topk % 4 == 0 && (reinterpret_cast<uintptr_t>(slot) & 15) == 0;
-#define EP_CM_COLS(SM, V4)                                                                      \
-    hipLaunchKernelGGL((scales_colmajor_kernel<SM, V4>), grid, dim3(256), 0, stream, workspace,     \
-                       src, slot, num_tokens, num_topk, nb, rows, recv_scales, scale_ld)
-    if (scale_mode == kScaleUe8m0) {
-        if (v4) EP_CM_COLS(kScaleUe8m0, true);
-        else EP_CM_COLS(kScaleUe8m0, false);
-    } else {
-        if (v4) EP_CM_COLS(kScaleFp32, true);
-        else EP_CM_COLS(kScaleFp32, false);
-    }
-#undef EP_CM_COLS
-    return hipGetLastError();
+    return launch_scales_colmajor(workspace, (nb & 3) == 0, src, slot, num_tokens, num_topk, nb,
+                                  scale_mode, rows, recv_scales, scale_ld, stream);
 }
 
 constexpr int kPrequantSlots = 4;          // slots per wavefront when grouped
@@ -1022,6 +1036,26 @@ hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num
     }
 #undef EP_PQ
     return hipGetLastError();
+}
+
+// Pre-quantized rows with column-major scales in two passes: the code rows
+// as in the row-major copy (a token's wavefronts on one XCD), then the
+// column pass reading each receive row's scales straight from x_scales,
+// which already holds every token's scale row once.
+hipError_t launch_dispatch_prequant_colmajor(const void* xq, const float* xs, int64_t num_tokens,
+                                             int hidden, int num_topk, const int32_t* slot,
+                                             const int32_t* src, const float* topk_weights,
+                                             void* recv_q, float* recv_scales, float* recv_weights,
+                                             int64_t scale_ld, int64_t rows, hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    hipError_t err = launch_dispatch_prequant(xq, xs, num_tokens, hidden, num_topk, slot,
+                                              topk_weights, recv_q, nullptr, recv_weights, 0, stream);
+    if (err != hipSuccess) return err;
+    const int nb = hidden / 128;
+    const bool vec = (nb & 3) == 0 && (reinterpret_cast<uintptr_t>(xs) & 15) == 0;
+    return launch_scales_colmajor(xs, vec, src, slot, num_tokens, num_topk, nb, kScaleFp32, rows,
+                                  recv_scales, scale_ld, stream);
 }
 
 }  // namespace ep

@@ -74,6 +74,15 @@ hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num
                                     const float* topk_weights, void* recv_q, float* recv_scales,
                                     float* recv_weights, int64_t scale_ld, hipStream_t stream);
 
+// Pre-quantized rows with column-major scales in two passes: the code rows
+// per slot, then the scales of each of the `rows` receive rows from its
+// token's row of xs (src: the source token of each receive row).
+hipError_t launch_dispatch_prequant_colmajor(const void* xq, const float* xs, int64_t num_tokens,
+                                             int hidden, int num_topk, const int32_t* slot,
+                                             const int32_t* src, const float* topk_weights,
+                                             void* recv_q, float* recv_scales, float* recv_weights,
+                                             int64_t scale_ld, int64_t rows, hipStream_t stream);
+
 // row_w / out_w: optional gather out_w[t,j] = row_w[slot[t,j]] (dispatch
 // backward); both NULL for a plain combine.
 hipError_t launch_combine(const void* y, const int32_t* slot, const float* topk_weights,

@@ -51,7 +51,7 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
            "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked",
            "ep_dispatch_ranked_backward", "ep_dispatch_colmajor_workspace_size",
-           "ep_dispatch_colmajor_scales")
+           "ep_dispatch_colmajor_scales", "ep_dispatch_prequantized_colmajor")
 
 
 class EpError(RuntimeError):
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_colmajor_scales.restype = i32
         L.ep_dispatch_prequantized.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, i64, P]
         L.ep_dispatch_prequantized.restype = i32
+        L.ep_dispatch_prequantized_colmajor.argtypes = [P, P, i64, i32, i32, P, P, P, P, P, P, i64,
+                                                        i64, P]
+        L.ep_dispatch_prequantized_colmajor.restype = i32
         L.ep_combine.argtypes = [P, P, P, i64, i32, i32, P, P]
         L.ep_combine.restype = i32
         L.ep_combine_backward.argtypes = [P, P, P, P, i64, i32, i32, P, P, P]
@@ -420,6 +423,52 @@ def ep_dispatch_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor, slot: to
                                         _ptr(topk_weights), _ptr(recv_q), _ptr(recv_scales),
                                         _ptr(recv_weights), int(scale_ld), _stream(stream))
     _check(st, "ep_dispatch_prequantized")
+    return recv_q, recv_scales, recv_weights
+
+
+def ep_dispatch_prequantized_colmajor(x_q: torch.Tensor, x_scales: torch.Tensor,
+                                      slot: torch.Tensor, src: torch.Tensor,
+                                      topk_weights: Optional[torch.Tensor] = None, *,
+                                      scale_ld: int, rows: Optional[int] = None, recv_q=None,
+                                      recv_scales=None, recv_weights=None,
+                                      want_weights: bool = False, stream=None):
+    """The pre-quantized copy with column-major scales [H/128, scale_ld]
+    written in two passes (the code rows, then the scale columns from
+    x_scales).  ``src`` is the layout's int32 source token of each of the
+    ``rows`` receive rows (T*k by default).  Returns (recv_q, recv_scales,
+    recv_weights or None)."""
+    _need(x_q, "x_q", torch.uint8)
+    _need(x_scales, "x_scales", torch.float32)
+    _need(slot, "slot", torch.int32)
+    if x_q.dim() != 2 or slot.dim() != 2 or slot.shape[0] != x_q.shape[0]:
+        raise ValueError("x_q must be [T, H] and slot [T, k]")
+    T, H = x_q.shape
+    k = slot.shape[1]
+    nb = H // 128
+    if x_scales.numel() < T * nb:
+        raise ValueError("x_scales must hold T * H/128 values")
+    R = T * k if rows is None else int(rows)
+    if scale_ld < R:
+        raise ValueError(f"scale_ld {scale_ld} is below the {R} rows")
+    _need(src, "src", torch.int32, R)
+    dev = x_q.device
+    if recv_q is None:
+        recv_q = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    if recv_scales is None:
+        recv_scales = torch.empty((nb, scale_ld), dtype=torch.float32, device=dev)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(R, dtype=torch.float32, device=dev)
+    _need(recv_q, "recv_q", torch.uint8, R * H)
+    _need(recv_scales, "recv_scales", torch.float32, nb * scale_ld)
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, R)
+    st = lib().ep_dispatch_prequantized_colmajor(_ptr(x_q), _ptr(x_scales), T, H, k, _ptr(slot),
+                                                 _ptr(src), _ptr(topk_weights), _ptr(recv_q),
+                                                 _ptr(recv_scales), _ptr(recv_weights),
+                                                 int(scale_ld), R, _stream(stream))
+    _check(st, "ep_dispatch_prequantized_colmajor")
     return recv_q, recv_scales, recv_weights
 
 

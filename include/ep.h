@@ -332,6 +332,39 @@ ep_status_t ep_dispatch_prequantized(const void *x_q, const float *x_scales, int
                                      float *recv_weights, int64_t scale_ld, void *stream);
 
 /*
+ * ep_dispatch_prequantized_colmajor -- ep_dispatch_prequantized with
+ * column-major scales written in two passes: the code rows per slot, then
+ * one lane per receive row copies its token's scales from x_scales (which
+ * already holds each token's scale row once) into the columns, so each
+ * column is written in runs of consecutive rows.  No workspace.
+ * (ep_dispatch_prequantized with scale_ld > 0 writes the same bytes in one
+ * pass, one row's scales at a time.)
+ *
+ * Passages: DeepEP page, dispatch() (x may be a (data, scale factors) pair;
+ * use_tma_aligned_col_major_sf: scale factors stored column-major); NCCL EP
+ * page, ncclEpDispatch high-throughput branch (FP8 input with a 2-D fp32
+ * scales tensor).
+ *
+ * In:  x_q, x_scales, slot, topk_weights as ep_dispatch_prequantized.
+ *      src        int32 [num_rows]: the source token of each receive row
+ *                 (ep_layout's src); entries of rows nothing maps to may hold
+ *                 anything: a row is filled only when one of its token's
+ *                 slots is that row.
+ *      num_rows   rows of the receive buffers.
+ * Out: recv_q [rows, hidden] as ep_dispatch_prequantized; recv_scales fp32
+ *      [hidden/128, scale_ld]: block b of row r at b*scale_ld + r, for the
+ *      rows a slot maps to, other entries untouched; scale_ld >= num_rows,
+ *      a multiple of 4; recv_weights [rows] or NULL.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
+ */
+ep_status_t ep_dispatch_prequantized_colmajor(const void *x_q, const float *x_scales,
+                                              int64_t num_tokens, int hidden, int num_topk,
+                                              const int32_t *slot, const int32_t *src,
+                                              const float *topk_weights, void *recv_q,
+                                              float *recv_scales, float *recv_weights,
+                                              int64_t scale_ld, int64_t num_rows, void *stream);
+
+/*
  * ep_combine -- weighted reduction of expert outputs back to token order.
  *
  * Passages: NCCL EP page, nccl_ep.cc, ncclEpCombine (low-latency branch:

@@ -480,3 +480,29 @@ def test_dispatch_colmajor_scales_zero_tokens_is_a_noop():
     st = ep.lib().ep_dispatch_colmajor_scales(None, 0, 256, 2, None, None, None, 1, 0, None, None,
                                               None, 16, 0, FAKE, 256, None)
     assert st == 0 and ep.last_error() == ""
+
+
+@no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(H=200), 1), (dict(k=0), 1), (dict(T=-1), 1), (dict(ld=0), 1), (dict(ld=6), 1),
+    (dict(rows=-1), 1), (dict(rows=20), 1), (dict(rows=1 << 31, ld=1 << 32), 1),
+    (dict(xq=None), 1), (dict(xs=None), 1), (dict(slot=None), 1), (dict(src=None), 1),
+    (dict(q=None), 1), (dict(s=None), 1), (dict(xq=FAKE + 8), 1), (dict(q=FAKE + 8), 1),
+    (dict(xs=FAKE + 2), 1), (dict(s=FAKE + 2), 1), (dict(rw=FAKE), 1),
+])
+def test_dispatch_prequantized_colmajor_rejects(over, code):
+    a = dict(xq=FAKE, xs=FAKE, T=4, H=256, k=2, slot=FAKE, src=FAKE, w=None, q=FAKE, s=FAKE,
+             rw=None, ld=16, rows=8)
+    a.update(over)
+    st = ep.lib().ep_dispatch_prequantized_colmajor(
+        a["xq"], a["xs"], a["T"], a["H"], a["k"], a["slot"], a["src"], a["w"], a["q"], a["s"],
+        a["rw"], a["ld"], a["rows"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+@no_gpu
+def test_dispatch_prequantized_colmajor_zero_tokens_is_a_noop():
+    st = ep.lib().ep_dispatch_prequantized_colmajor(None, None, 0, 256, 2, None, None, None, None,
+                                                    None, None, 16, 0, None)
+    assert st == 0 and ep.last_error() == ""

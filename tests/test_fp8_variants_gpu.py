@@ -193,6 +193,64 @@ def test_prequantized_column_major_scales():
     assert np.all(np.isnan(host(s)[:, n:]))
 
 
+@pytest.mark.parametrize("case", ["fp8_slice", "mid", "blocks_9", "padded", "xs_off"])
+def test_prequantized_column_major_two_pass(case):
+    # ep_dispatch_prequantized_colmajor: the oracle's row-major copy, its
+    # scales transposed, for every row a slot maps to; everything else
+    # untouched; src garbage (valid token ids among it) where nothing maps.
+    # blocks_9: 9 blocks per row, one scale at a time; padded: aligned
+    # segments with a capacity (dropped pairs); xs_off: x_scales 4 bytes off
+    # a 16-byte boundary (one scale at a time again)
+    E, A, cap = 256, 1, 0
+    if case == "fp8_slice":
+        inp = make_inputs(WORKLOADS["fp8"], T=1024)
+    elif case == "mid":
+        w = WORKLOADS["mid"]
+        inp, E = make_inputs(w), w.E
+    elif case == "padded":
+        inp, E, A, cap = make_random_case(61, 300, 2048, 16, 6, mask_frac=0.1), 16, 4, 96
+    else:
+        inp, E = make_random_case(62, 400, 1152 if case == "blocks_9" else 2048, 32, 8,
+                                  mask_frac=0.1, dup_frac=0.2), 32
+    T, H = inp.x_bits.shape
+    k = inp.topk_idx.shape[1]
+    nb = H // 128
+    print(f"\n[prequantized] column-major two-pass {case} T={T} H={H} k={k}", flush=True)
+    xq, xs, _ = oracle.dispatch_quant(inp.x_bits, np.arange(T, dtype=np.int32)[:, None])
+    L = oracle.layout(inp.topk_idx, E, alignment=A, capacity=cap)
+    rows = ep.layout_max_rows(T, k, E, A, cap)
+    ld = (rows + 3) // 4 * 4 + 4
+    mapped = np.zeros(rows, bool)
+    mapped[L.slot[L.slot >= 0]] = True
+    rng = np.random.default_rng(63)
+    src_l = np.zeros(rows, np.int32)
+    src_l[:min(rows, L.src.size)] = L.src[:rows]
+    src = np.where(mapped, src_l, rng.integers(-5, T + 5, rows)).astype(np.int32)
+    d_xs = dev(xs)
+    if case == "xs_off":
+        buf = torch.empty(xs.size + 1, dtype=torch.float32, device=DEV)
+        d_xs = buf[1:].view(xs.shape)
+        d_xs.copy_(dev(xs))
+        assert d_xs.data_ptr() % 16 == 4
+    q = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    sc = torch.full((nb, ld), float("nan"), dtype=torch.float32, device=DEV)
+    rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_prequantized_colmajor(dev(xq), d_xs, dev(L.slot), dev(src),
+                                         dev(inp.topk_weights), scale_ld=ld, rows=rows, recv_q=q,
+                                         recv_scales=sc, recv_weights=rw)
+    torch.cuda.synchronize()
+    oq, os_, orw = oracle.dispatch_prequant(xq, xs, L.slot, inp.topk_weights, rows=rows)
+    gq, gs, grw = host(q), host(sc), host(rw)
+    np.testing.assert_array_equal(gq[mapped], oq[mapped])
+    assert np.all(gq[~mapped] == 0xEE)
+    np.testing.assert_array_equal(np.ascontiguousarray(gs[:, :rows][:, mapped]).view(np.uint32),
+                                  np.ascontiguousarray(os_[mapped].T).view(np.uint32))
+    rest = np.concatenate([gs[:, :rows][:, ~mapped].ravel(), gs[:, rows:].ravel()])
+    assert np.all(np.isnan(rest))
+    np.testing.assert_array_equal(grw[mapped].view(np.uint32), orw[mapped].view(np.uint32))
+    assert np.all(np.isnan(grw[~mapped]))
+
+
 @pytest.mark.parametrize("fmt,mode", COMBOS)
 def test_variants_narrow_tiles(fmt, mode):
     # hidden 2560 (160 units): the tiled cast in 64-lane tiles, three per

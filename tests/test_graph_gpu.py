@@ -241,6 +241,7 @@ def test_variants_and_backward_graph():
         "q_cm": torch.empty((P, H), **u8), "s_cm": torch.empty((nb, P + 4), **f32),
         "q_cm2": torch.empty((P, H), **u8), "s_cm2": torch.empty((nb, P + 4), **f32),
         "rw_cm2": torch.empty(P, **f32),
+        "q_pcm": torch.empty((P, H), **u8), "s_pcm": torch.empty((nb, P + 4), **f32),
         "q_pre": torch.empty((P, H), **u8), "s_pre": torch.empty((P, nb), **f32),
         "rw_pre": torch.empty(P, **f32),
         # backward
@@ -286,6 +287,8 @@ def test_variants_and_backward_graph():
                                        workspace=cmws)
         ep.ep_dispatch_prequantized(xq, xs, o["slot"], w, recv_q=o["q_pre"], recv_scales=o["s_pre"],
                                     recv_weights=o["rw_pre"])
+        ep.ep_dispatch_prequantized_colmajor(xq, xs, o["slot"], o["src"], scale_ld=P + 4,
+                                             recv_q=o["q_pcm"], recv_scales=o["s_pcm"])
         ep.ep_dispatch(x, o["slot"], None, recv_x=o["recv"])
         ep.ep_combine_backward(g_out, o["recv"], o["slot"], w, grad_y=o["gy"], grad_topk_weights=o["gw"])
         ep.ep_dispatch_backward(g_recv, g_recv_w, o["slot"], grad_x=o["gx"], grad_topk_weights=o["gxw"])
@@ -317,9 +320,12 @@ def test_variants_and_backward_graph():
     placed = La.slot[La.slot >= 0]
     np.testing.assert_array_equal(host(o["q_al"])[placed], oq[placed])
     np.testing.assert_array_equal(host(o["s_al"])[placed], os_[placed])
-    # the two-pass column-major cast writes what the one-pass form does
+    # the two-pass column-major cast writes what the one-pass form does, and
+    # the pre-quantized copy of the cast tokens gives the same codes and scales
     assert torch.equal(_bits(o["q_cm2"]), _bits(o["q_cm"]))
     assert torch.equal(_bits(o["s_cm2"]), _bits(o["s_cm"]))
+    assert torch.equal(_bits(o["q_pcm"]), _bits(o["q_cm"]))
+    assert torch.equal(_bits(o["s_pcm"]), _bits(o["s_cm"]))
     ref = {name: t.clone() for name, t in o.items()}
 
     g = _capture(step)
