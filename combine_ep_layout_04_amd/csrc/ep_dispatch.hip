@@ -688,7 +688,9 @@ void scales_colmajor_kernel(const void* __restrict__ ws, bool vec, const int32_t
 // copy took 106.9 against 111.1 us at T=8192, hidden 7168, k=8 (interleaved
 // A/B) and 62.6 against 63.5 us at 4096; at hidden 2048, and with
 // column-major scales, groups were as fast or up to 11% slower.
-template <int VPT, int SG>
+// SCALES false: the code rows only (the two-pass column-major copy writes
+// the scales in its second pass).
+template <int VPT, int SG, bool SCALES>
 __global__ __launch_bounds__(64)
 void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restrict__ xs,
                               int units, int k, const int32_t* __restrict__ slot,
@@ -731,7 +733,7 @@ void dispatch_prequant_kernel(const uint4* __restrict__ xq, const float* __restr
             }
         }
     }
-    if (recv_s == nullptr) return;    // scales written by a later pass
+    if (!SCALES) return;              // scales written by a later pass
     // the scale row: 64 floats per round
     for (int b0 = 0; b0 < nb; b0 += 64) {
         const int b = b0 + tid;
@@ -1015,15 +1017,17 @@ hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num
     const int64_t gblocks = (num_tokens + 7) / 8 * 8 * ((num_topk + kPrequantSlots - 1) / kPrequantSlots);
     const bool grouped = scale_ld == 0 && units > kPrequantGroupUnits && gblocks <= INT32_MAX;
     const dim3 ggrid((unsigned)gblocks);
-#define EP_PQ(V)                                                                                   \
+#define EP_PQ_SC(V, SC)                                                                          \
     if (grouped)                                                                               \
-        hipLaunchKernelGGL((dispatch_prequant_kernel<V, kPrequantSlots>), ggrid, dim3(64), 0,     \
+        hipLaunchKernelGGL((dispatch_prequant_kernel<V, kPrequantSlots, SC>), ggrid, dim3(64), 0, \
                            stream, qq, xs, units, num_topk, slot, topk_weights, rq, recv_scales,   \
                            recv_weights, scale_ld, num_tokens);                                   \
     else                                                                                       \
-        hipLaunchKernelGGL((dispatch_prequant_kernel<V, 0>), grid, dim3(64), 0, stream, qq, xs,    \
-                           units, num_topk, slot, topk_weights, rq, recv_scales, recv_weights,     \
+        hipLaunchKernelGGL((dispatch_prequant_kernel<V, 0, SC>), grid, dim3(64), 0, stream, qq,    \
+                           xs, units, num_topk, slot, topk_weights, rq, recv_scales, recv_weights, \
                            scale_ld, num_tokens)
+#define EP_PQ(V)                                                                                   \
+    if (recv_scales != nullptr) { EP_PQ_SC(V, true); } else { EP_PQ_SC(V, false); }
     switch (vpt) {
     case 1: EP_PQ(1); break;
     case 2: EP_PQ(2); break;
@@ -1035,6 +1039,7 @@ hipError_t launch_dispatch_prequant(const void* xq, const float* xs, int64_t num
     default: EP_PQ(8); break;
     }
 #undef EP_PQ
+#undef EP_PQ_SC
     return hipGetLastError();
 }
 

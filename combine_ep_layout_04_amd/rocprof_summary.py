@@ -178,12 +178,14 @@ KERNEL_KEYS = {
     "dispatch_fp8_e4m3_fp32_colmajor": r"dispatch_fp8_kernel<7, 0, 0>",
     "dispatch_fp8_e4m3_fp32_colmajor_two_pass": (r"dispatch_fp8_tile_kernel<0, 0, 64, 4, true>",
                                                  r"scales_colmajor_kernel<0, true>"),
-    "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<7, 4>",
+    "dispatch_fp8_prequantized": r"dispatch_prequant_kernel<7, 4, true>",
     # the pre-quantized copy with column-major scales: one wavefront per
     # token with the column stride (one pass), or the code rows through the
-    # grouped copy (the row-major copy's kernel, so its traffic is the
-    # row-major line's) and then the column pass
-    "dispatch_fp8_prequantized_colmajor": r"dispatch_prequant_kernel<7, 0>",
+    # grouped copy with its scale stores off and then the column pass (the
+    # same kernel as the cast's column pass, whose dispatches it shares)
+    "dispatch_fp8_prequantized_colmajor": r"dispatch_prequant_kernel<7, 0, true>",
+    "dispatch_fp8_prequantized_colmajor_two_pass": (r"dispatch_prequant_kernel<7, 4, false>",
+                                                    r"scales_colmajor_kernel<0, true>"),
     "combine": r"[^_]combine_tile_kernel<",
     "combine_backward": (r"combine_backward_grad_y_tile_kernel",
                          r"combine_backward_kernel<128, 7, false>"),
