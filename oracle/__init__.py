@@ -153,6 +153,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P,
                                                     P, P]
         L.oracle_dispatch_fused_permute.restype = None
+        L.oracle_dispatch_fused_permute_prequant.argtypes = [P, P, P, P, i64, i32, i32, i32, i32,
+                                                             i32, P, P, P, P, P, P]
+        L.oracle_dispatch_fused_permute_prequant.restype = None
         L.oracle_dispatch_ranked_prequant.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
                                                       P]
         L.oracle_dispatch_ranked_prequant.restype = None
@@ -536,6 +539,42 @@ def dispatch_fused_permute(src_x, src_idx, src_w, E: int, rank: int, recv_src: n
                                         int(rank), _ptr(rs), _ptr(rti), _ptr(sl), _ptr(out),
                                         _ptr(rw))
     return out, rw
+
+
+def dispatch_fused_permute_prequant(src_q, src_s, src_idx, src_w, E: int, rank: int,
+                                    recv_src: np.ndarray, recv_topk_idx: np.ndarray,
+                                    slot: np.ndarray, rows: int, with_weights: bool = True):
+    """oracle_dispatch_fused_permute for tokens already cast to 8 bits:
+    ``src_q`` / ``src_s`` are lists of the G ranks' code rows (uint8 [T, H])
+    and scale rows (float32 [T, H/128]).  Returns (recv_q uint8 [rows, H],
+    recv_s float32 [rows, H/128], recv_w float32 [rows] or None); unwritten
+    rows stay 0."""
+    G = len(src_q)
+    qs = [_c(q, np.uint8) for q in src_q]
+    ss = [_c(x, np.float32) for x in src_s]
+    ids = [_c(i, np.int64) for i in src_idx]
+    ws = [None if w is None else _c(w, np.float32) for w in src_w]
+    T, H = qs[0].shape
+    nb = H // 128
+    k = ids[0].shape[1]
+    rs = _c(recv_src, np.int32)
+    rti = _c(recv_topk_idx, np.int64)
+    sl = _c(slot, np.int32)
+    if rs.shape != (G * T,) or rti.shape != (G * T, k) or sl.shape != (G * T, k):
+        raise ValueError("receive-side arrays must have G*T rows and k columns")
+    if sl.size and sl.max() >= rows:
+        raise ValueError("a slot is beyond the receive buffer")
+    if any(x.shape != (T, nb) for x in ss):
+        raise ValueError("every src_s must be [T, H/128]")
+    out_q = np.zeros((rows, H), np.uint8)
+    out_s = np.zeros((rows, nb), np.float32)
+    rw = np.zeros(rows, np.float32) if with_weights else None
+    wtab = None if all(w is None for w in ws) else _ptr_array(ws)
+    lib().oracle_dispatch_fused_permute_prequant(_ptr_array(qs), _ptr_array(ss), _ptr_array(ids),
+                                                 wtab, T, H, k, int(E), G, int(rank), _ptr(rs),
+                                                 _ptr(rti), _ptr(sl), _ptr(out_q), _ptr(out_s),
+                                                 _ptr(rw))
+    return out_q, out_s, rw
 
 
 def dispatch_ranked_prequant(xq: np.ndarray, xs: np.ndarray, topk_idx: np.ndarray,

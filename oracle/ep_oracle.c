@@ -879,6 +879,52 @@ void oracle_dispatch_fused_permute(const uint16_t *const *src_x, const int64_t *
 }
 
 /*
+ * The same receive-side dispatch for tokens already cast to 8 bits (NeMo
+ * fused_a2a page: fp8_dispatch, FP8 communication in the dispatch phase,
+ * with fuse_permute; NCCL EP page, ncclEpDispatch high-throughput branch:
+ * FP8 tokens come with a 2-D fp32 scales tensor).  Each received token's
+ * code row (H bytes) and scale row (H/128 fp32) are copied from the sending
+ * rank to each of this rank's local-expert rows:
+ *   recv_q[slot[i, j]] = src_q[s][t],  recv_s[slot[i, j]] = src_s[s][t]
+ * and recv_w as oracle_dispatch_fused_permute (NULL: not written).
+ */
+void oracle_dispatch_fused_permute_prequant(const uint8_t *const *src_q,
+                                            const float *const *src_s,
+                                            const int64_t *const *src_idx,
+                                            const float *const *src_w, int64_t T, int H, int k,
+                                            int E, int G, int rank, const int32_t *recv_src,
+                                            const int64_t *recv_topk_idx, const int32_t *slot,
+                                            uint8_t *recv_q, float *recv_s, float *recv_w)
+{
+    int El = E / G;
+    int nb = H / 128;
+    for (int64_t i = 0; i < (int64_t)G * T; ++i) {
+        int32_t g = recv_src[i];
+        if (g < 0)
+            continue;
+        int s = (int)(g / T);
+        int64_t t = g % T;
+        for (int j = 0; j < k; ++j) {
+            int32_t r = slot[i * k + j];
+            if (r < 0)
+                continue;
+            for (int c = 0; c < H; ++c)
+                recv_q[(int64_t)r * H + c] = src_q[s][t * H + c];
+            for (int b = 0; b < nb; ++b)
+                recv_s[(int64_t)r * nb + b] = src_s[s][t * nb + b];
+            if (!recv_w)
+                continue;
+            int64_t e = (int64_t)rank * El + recv_topk_idx[i * k + j];
+            float sum = 0.0f;
+            for (int jj = 0; jj < k; ++jj)
+                if (src_idx[s][t * k + jj] == e)
+                    sum = sum + (src_w && src_w[s] ? src_w[s][t * k + jj] : 1.0f);
+            recv_w[r] = sum;
+        }
+    }
+}
+
+/*
  * Once-per-rank dispatch of tokens already cast to 8 bits (NCCL EP page,
  * ncclEpDispatch high-throughput branch: FP8 tokens come with a 2-D fp32
  * scales tensor and travel as they are).  As oracle_dispatch_ranked, with

@@ -61,6 +61,12 @@ void oracle_dispatch_fused_permute(const uint16_t *const *src_x, const int64_t *
                                    const float *const *src_w, int64_t T, int H, int k, int E, int G,
                                    int rank, const int32_t *recv_src, const int64_t *recv_topk_idx,
                                    const int32_t *slot, uint16_t *recv_x, float *recv_w);
+void oracle_dispatch_fused_permute_prequant(const uint8_t *const *src_q, const float *const *src_s,
+                                            const int64_t *const *src_idx,
+                                            const float *const *src_w, int64_t T, int H, int k,
+                                            int E, int G, int rank, const int32_t *recv_src,
+                                            const int64_t *recv_topk_idx, const int32_t *slot,
+                                            uint8_t *recv_q, float *recv_s, float *recv_w);
 void oracle_dispatch_ranked_prequant(const uint8_t *xq, const float *xs, const int64_t *topk_idx,
                                      const float *topk_weights, int64_t T, int H, int k, int E,
                                      int G, const int32_t *sparse_to_dense, uint8_t *const *dest_q,
@@ -295,6 +301,18 @@ int main(void)
         oracle_dispatch_fused_permute((const uint16_t *const *)xs_r, src_idx,
                                       (const float *const *)ws_r, T, H, k, E, G, rank, rsrc, rtopk,
                                       pslot, px, pw);
+        /* and its 8-bit form: every rank sends the same code and scale rows */
+        const uint8_t **sq = xalloc((size_t)G * sizeof(void *));
+        const float **ssc = xalloc((size_t)G * sizeof(void *));
+        for (int s = 0; s < G; ++s) {
+            sq[s] = xq;
+            ssc[s] = xsc;
+        }
+        uint8_t *pq = xalloc((size_t)R * k * H);
+        float *ps = xalloc((size_t)R * k * 4);
+        oracle_dispatch_fused_permute_prequant(sq, ssc, src_idx, (const float *const *)ws_r, T, H, k,
+                                               E, G, rank, rsrc, rtopk, pslot, pq, ps, pw);
+        free(sq); free(ssc); free(pq); free(ps);
 
         for (int s = 0; s < G; ++s) {
             free(xs_r[s]);

@@ -334,6 +334,51 @@ def test_fused_permute_is_rank_dispatch_then_expert_dispatch(seed, G, T, E, k, w
         np.testing.assert_array_equal(got_w, want_w)
 
 
+@pytest.mark.parametrize("seed,G,T,E,k,weights", [(0, 2, 30, 8, 3, True), (1, 4, 50, 32, 6, True),
+                                                  (2, 3, 20, 9, 5, False), (3, 8, 40, 64, 8, True)])
+def test_fused_permute_prequant_pins(seed, G, T, E, k, weights):
+    # the 8-bit receive-side copy against two other oracle functions on the
+    # same routing: (a) the bf16 fused permute applied to the code rows and
+    # to the scale rows, each reinterpreted as 16-bit words (a byte copy is a
+    # byte copy), its weights included; (b) the expanded pre-quantized copy
+    # of the received tokens (row i = sender s's token t, recv_src[i] =
+    # s*T + t) by the layout of recv_topk_idx
+    H, El = 256, E // G
+    nb = H // 128
+    rng = np.random.default_rng(seed)
+    cases = [make_random_case(seed * 10 + s, T, 8, E, k, mask_frac=0.2, dup_frac=1.0,
+                              invalid_frac=0.05) for s in range(G)]
+    idx = [cs.topk_idx for cs in cases]
+    ws = [cs.topk_weights if weights else None for cs in cases]
+    qs = [rng.integers(0, 256, (T, H)).astype(np.uint8) for _ in range(G)]
+    ss = [rng.standard_normal((T, nb)).astype(np.float32) for _ in range(G)]
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    for r in range(G):
+        L = oracle.rank_layout(gmap, T, E, G, r, k)
+        Lr = oracle.layout(L.recv_topk_idx, El)
+        rows = max(Lr.n, 1)
+        gq, gs, gw = oracle.dispatch_fused_permute_prequant(qs, ss, idx, ws, E, r, L.recv_src,
+                                                            L.recv_topk_idx, Lr.slot, rows)
+        # (a)
+        aq, aw = oracle.dispatch_fused_permute([q.view(np.uint16) for q in qs], idx, ws, E, r,
+                                               L.recv_src, L.recv_topk_idx, Lr.slot, rows)
+        a_s, _ = oracle.dispatch_fused_permute([x.view(np.uint16) for x in ss], idx, ws, E, r,
+                                               L.recv_src, L.recv_topk_idx, Lr.slot, rows)
+        np.testing.assert_array_equal(gq, aq.view(np.uint8))
+        np.testing.assert_array_equal(gs.view(np.uint32), a_s.view(np.uint32))
+        np.testing.assert_array_equal(gw.view(np.uint32), aw.view(np.uint32))
+        # (b)
+        src = L.recv_src
+        live = src >= 0
+        g = np.where(live, src, 0)
+        xq_recv = np.stack([qs[int(v) // T][int(v) % T] for v in g])
+        xs_recv = np.stack([ss[int(v) // T][int(v) % T] for v in g])
+        slot_live = np.where(live[:, None], Lr.slot, -1).astype(np.int32)
+        bq, bs, _ = oracle.dispatch_prequant(xq_recv, xs_recv, slot_live, rows=rows)
+        np.testing.assert_array_equal(gq, bq)
+        np.testing.assert_array_equal(gs.view(np.uint32), bs.view(np.uint32))
+
+
 @pytest.mark.parametrize("seed,G,E,k", [(0, 2, 8, 3), (1, 4, 16, 5), (2, 8, 64, 8)])
 def test_dispatch_ranked_prequant(seed, G, E, k):
     # codes and scales: numpy fancy-index copies; weights: the bf16
