@@ -62,7 +62,9 @@ KERNEL_SOURCES = {
     "dispatch_ranked_backward": "ep_ranked.hip",
     "routing_map": "ep_ranked.hip", "rank_count": "ep_ranked.hip", "rank_scatter": "ep_ranked.hip",
     "dispatch_ranked": "ep_ranked.hip", "combine_ranked": "ep_ranked.hip",
-    "dispatch_fused_permute": "ep_ranked.hip", "dispatch_ranked_prequantized": "ep_ranked.hip",
+    "dispatch_fused_permute": "ep_ranked.hip",
+    "dispatch_fused_permute_prequantized": "ep_ranked.hip",
+    "dispatch_ranked_prequantized": "ep_ranked.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -639,6 +641,29 @@ def main():
                 + n_exp * 4)
     del src_x, perm_x
 
+    # the same receive for 8-bit tokens: rank 0's code and scale rows are the
+    # fp8 workload's cast above, ranks 1..7 hold seeded bytes and unit scales
+    nb = H // 128
+    with torch.cuda.stream(stream):
+        src_q = [xq_tok] + [torch.randint(0, 256, (T, H), generator=gen, device=dev,
+                                          dtype=torch.uint8) for _ in range(1, G)]
+        src_s = [xs_tok] + [torch.ones((T, nb), dtype=torch.float32, device=dev)
+                            for _ in range(1, G)]
+        perm_q = torch.empty((n_exp, H), dtype=torch.uint8, device=dev)
+        perm_s = torch.empty((n_exp, nb), dtype=torch.float32, device=dev)
+    stream.synchronize()
+    sqt = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_q])
+    sst = (ctypes.c_void_p * G)(*[t.data_ptr() for t in src_s])
+    fpq_us = time_call(lambda: check(L.ep_dispatch_fused_permute_prequantized(
+        ctypes.addressof(sqt), ctypes.addressof(sst), ctypes.addressof(sit), ctypes.addressof(swt),
+        T, H, k, E, G, 0, rq["rsrc"], rq["rti"], rq["nrecv"], pslot.data_ptr(), n_exp,
+        perm_q.data_ptr(), perm_s.data_ptr(), perm_w.data_ptr(), s),
+        "ep_dispatch_fused_permute_prequantized"), args.steps)
+    # as the bf16 receive with code rows of H bytes plus scale rows of H/128 fp32
+    fpq_bytes = ((n_recv + n_exp) * (H + nb * 4) + n_recv * (4 + k * 8 + k * 4) + n_recv * k * 12
+                 + n_exp * 4)
+    del src_q, src_s, perm_q, perm_s
+
     # ---- the other seeded configs (tiny, mid, skewed): layout, dispatch and
     # combine each timed alone, caches emptied before every launch
     configs = {}
@@ -755,6 +780,9 @@ def main():
         "dispatch_ranked_prequantized": entry(drq_us, bytes=drq_bytes, ranks=G, rows_written=pairs),
         "dispatch_fused_permute": entry(fp_us, bytes=fp_bytes, ranks=G, tokens_received=n_recv,
                                         expert_rows_written=n_exp),
+        "dispatch_fused_permute_prequantized": entry(fpq_us, bytes=fpq_bytes, ranks=G,
+                                                     tokens_received=n_recv,
+                                                     expert_rows_written=n_exp),
         "layout_aligned128": entry(lay_a128),
         "layout_capacity320": entry(lay_cap, dropped_pairs=dropped_cap),
     }

@@ -592,33 +592,41 @@ ep_status_t ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scal
                     "ep_dispatch_ranked_prequantized launch");
 }
 
-ep_status_t ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,
-                                      const float* const* src_topk_weights, int64_t tokens_per_rank,
-                                      int hidden, int num_topk, int num_experts, int num_ranks,
-                                      int rank, const int32_t* recv_src,
-                                      const int64_t* recv_topk_idx, const int32_t* num_recv,
-                                      const int32_t* slot, int64_t rows, void* recv_x,
-                                      float* recv_weights, void* stream)
+// Checks shared by the two fused-permute entry points; fills the pointer
+// tables (src_s only when scales is true).
+static ep_status_t fused_permute_args(const void* const* src_x, const float* const* src_s,
+                                      bool scales, const int64_t* const* src_topk_idx,
+                                      const float* const* src_topk_weights,
+                                      int64_t tokens_per_rank, int hidden, int hidden_multiple,
+                                      int num_topk, int num_experts, int num_ranks, int rank,
+                                      int64_t rows, float* recv_weights, ep::RankPtrs& px,
+                                      ep::RankPtrs& ps, ep::RankPtrs& pi, ep::RankPtrs& pw)
 {
-    g_last_error[0] = '\0';
     if (tokens_per_rank < 0) return fail(EP_INVALID_ARGUMENT, "tokens_per_rank < 0");
     ep_status_t st = check_ranks(num_experts, num_ranks);
     if (st) return st;
     st = check_tokens(tokens_per_rank * num_ranks, num_topk);
     if (st) return st;
-    st = check_hidden(hidden, 8);
+    st = check_hidden(hidden, hidden_multiple);
     if (st) return st;
     if (rank < 0 || rank >= num_ranks)
         return fail(EP_INVALID_ARGUMENT, "rank %d outside [0, %d)", rank, num_ranks);
     if (rows < 0) return fail(EP_INVALID_ARGUMENT, "rows < 0");
     if (!src_x) return fail(EP_INVALID_ARGUMENT, "src_x (a host array of pointers) is required");
+    if (scales && !src_s)
+        return fail(EP_INVALID_ARGUMENT, "src_scales (a host array of pointers) is required");
     if (recv_weights && !src_topk_idx)
         return fail(EP_INVALID_ARGUMENT, "recv_weights needs src_topk_idx");
-    ep::RankPtrs px = {}, pi = {}, pw = {};
     for (int d = 0; d < num_ranks; ++d) {
         if (!src_x[d] || !aligned16(src_x[d]))
             return fail(EP_INVALID_ARGUMENT, "src_x[%d] must be non-NULL and 16-byte aligned", d);
         px.p[d] = const_cast<void*>(src_x[d]);
+        if (scales) {
+            if (!src_s[d] || (reinterpret_cast<uintptr_t>(src_s[d]) & 3u))
+                return fail(EP_INVALID_ARGUMENT,
+                            "src_scales[%d] must be non-NULL and 4-byte aligned", d);
+            ps.p[d] = const_cast<float*>(src_s[d]);
+        }
         if (recv_weights) {
             if (!src_topk_idx[d] || (reinterpret_cast<uintptr_t>(src_topk_idx[d]) & 7u))
                 return fail(EP_INVALID_ARGUMENT,
@@ -632,18 +640,69 @@ ep_status_t ep_dispatch_fused_permute(const void* const* src_x, const int64_t* c
             }
         }
     }
-    if (tokens_per_rank == 0) return EP_SUCCESS;
+    return EP_SUCCESS;
+}
+
+static ep_status_t fused_permute_outputs(const int32_t* recv_src, const int32_t* slot,
+                                         const void* recv_x, const int64_t* recv_topk_idx,
+                                         const float* recv_weights, const int32_t* num_recv)
+{
     if (!recv_src || !slot || !recv_x || (recv_weights && !recv_topk_idx))
         return fail(EP_INVALID_ARGUMENT,
                     "recv_src, slot, recv_x (and recv_topk_idx with recv_weights) are required");
     if (!aligned16(recv_x)) return fail(EP_INVALID_ARGUMENT, "recv_x must be 16-byte aligned");
     if (num_recv && (reinterpret_cast<uintptr_t>(num_recv) & 3u))
         return fail(EP_INVALID_ARGUMENT, "num_recv must be 4-byte aligned");
+    return EP_SUCCESS;
+}
+
+ep_status_t ep_dispatch_fused_permute(const void* const* src_x, const int64_t* const* src_topk_idx,
+                                      const float* const* src_topk_weights, int64_t tokens_per_rank,
+                                      int hidden, int num_topk, int num_experts, int num_ranks,
+                                      int rank, const int32_t* recv_src,
+                                      const int64_t* recv_topk_idx, const int32_t* num_recv,
+                                      const int32_t* slot, int64_t rows, void* recv_x,
+                                      float* recv_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    ep::RankPtrs px = {}, ps = {}, pi = {}, pw = {};
+    ep_status_t st = fused_permute_args(src_x, nullptr, false, src_topk_idx, src_topk_weights,
+                                        tokens_per_rank, hidden, 8, num_topk, num_experts,
+                                        num_ranks, rank, rows, recv_weights, px, ps, pi, pw);
+    if (st) return st;
+    if (tokens_per_rank == 0) return EP_SUCCESS;
+    st = fused_permute_outputs(recv_src, slot, recv_x, recv_topk_idx, recv_weights, num_recv);
+    if (st) return st;
     return from_hip(ep::launch_dispatch_fused_permute(px, pi, pw, tokens_per_rank, hidden, num_topk,
                                                       num_experts, num_ranks, rank, recv_src,
                                                       recv_topk_idx, num_recv, slot, rows, recv_x,
                                                       recv_weights, static_cast<hipStream_t>(stream)),
                     "ep_dispatch_fused_permute launch");
+}
+
+ep_status_t ep_dispatch_fused_permute_prequantized(
+    const void* const* src_q, const float* const* src_scales, const int64_t* const* src_topk_idx,
+    const float* const* src_topk_weights, int64_t tokens_per_rank, int hidden, int num_topk,
+    int num_experts, int num_ranks, int rank, const int32_t* recv_src,
+    const int64_t* recv_topk_idx, const int32_t* num_recv, const int32_t* slot, int64_t rows,
+    void* recv_q, float* recv_scales, float* recv_weights, void* stream)
+{
+    g_last_error[0] = '\0';
+    ep::RankPtrs px = {}, ps = {}, pi = {}, pw = {};
+    ep_status_t st = fused_permute_args(src_q, src_scales, true, src_topk_idx, src_topk_weights,
+                                        tokens_per_rank, hidden, 128, num_topk, num_experts,
+                                        num_ranks, rank, rows, recv_weights, px, ps, pi, pw);
+    if (st) return st;
+    if (tokens_per_rank == 0) return EP_SUCCESS;
+    st = fused_permute_outputs(recv_src, slot, recv_q, recv_topk_idx, recv_weights, num_recv);
+    if (st) return st;
+    if (!recv_scales || (reinterpret_cast<uintptr_t>(recv_scales) & 3u))
+        return fail(EP_INVALID_ARGUMENT, "recv_scales must be non-NULL and 4-byte aligned");
+    return from_hip(ep::launch_dispatch_fused_permute_prequant(
+                        px, ps, pi, pw, tokens_per_rank, hidden, num_topk, num_experts, num_ranks,
+                        rank, recv_src, recv_topk_idx, num_recv, slot, rows, recv_q, recv_scales,
+                        recv_weights, static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_fused_permute_prequantized launch");
 }
 
 ep_status_t ep_combine_ranked(const void* const* src_y, int64_t src_rows,

@@ -128,6 +128,18 @@ hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& 
                                          const int32_t* slot, int64_t rows, void* recv_x,
                                          float* recv_w, hipStream_t stream);
 
+// The same for 8-bit code rows (hidden bytes) with their fp32 scale rows
+// (hidden / 128 per token, row-major on both sides).
+hipError_t launch_dispatch_fused_permute_prequant(const RankPtrs& src_q, const RankPtrs& src_s,
+                                                  const RankPtrs& src_idx, const RankPtrs& src_w,
+                                                  int64_t tokens_per_rank, int hidden,
+                                                  int num_topk, int num_experts, int num_ranks,
+                                                  int rank, const int32_t* recv_src,
+                                                  const int64_t* recv_topk_idx,
+                                                  const int32_t* num_recv, const int32_t* slot,
+                                                  int64_t rows, void* recv_q, float* recv_s,
+                                                  float* recv_w, hipStream_t stream);
+
 hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const int32_t* s2d,
                                  int64_t num_tokens, int hidden, int num_ranks, void* out,
                                  hipStream_t stream);

@@ -708,12 +708,16 @@ void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
 // 307 us for whole rows, at 8 ranks x 8192 tokens, hidden 7168: a received
 // row usually has one or two local slots, so most tile workgroups only wait
 // on the recv_src -> slot loads and exit.
-template <int NT, int VPT>
+// SC: the rows are 8-bit codes (nvec 16-byte vectors) and each carries a
+// scale row of nb fp32 (src_s[s] [T, nb] -> recv_s [rows, nb]) copied the
+// same way.
+template <int NT, int VPT, bool SC>
 __device__ __forceinline__ void fused_permute_row(
-    const RankPtrs& src_x, const RankPtrs& src_idx, const RankPtrs& src_w, int64_t T, int nvec,
-    int k, int E, int El, int G, int rank, const int32_t* __restrict__ recv_src,
-    const int64_t* __restrict__ recv_topk_idx, const int32_t* __restrict__ slot, int64_t rows,
-    uint4* __restrict__ recv_x, float* __restrict__ recv_w, int64_t i)
+    const RankPtrs& src_x, const RankPtrs& src_s, const RankPtrs& src_idx, const RankPtrs& src_w,
+    int64_t T, int nvec, int nb, int k, int E, int El, int G, int rank,
+    const int32_t* __restrict__ recv_src, const int64_t* __restrict__ recv_topk_idx,
+    const int32_t* __restrict__ slot, int64_t rows, uint4* __restrict__ recv_x,
+    float* __restrict__ recv_s, float* __restrict__ recv_w, int64_t i)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -773,6 +777,19 @@ __device__ __forceinline__ void fused_permute_row(
                 store_row16(buffer_rsrc(recv_x + (int64_t)r * nvec, nvec * 16), v * 16, val);
         }
     }
+    if (SC) {
+        // the scale row, one fp32 per lane, the same trip count for every
+        // lane
+        const float* sr = static_cast<const float*>(src_s.p[s]) + t * nb;
+        for (int b0 = 0; b0 < nb; b0 += NT) {
+            const int b = b0 + tid;
+            const float v = b < nb ? sr[b] : 0.0f;
+            for (int j = 0; j < k; ++j) {
+                const int32_t r = __builtin_amdgcn_readlane(sl, j);
+                if (r >= 0 && b < nb) recv_s[(int64_t)r * nb + b] = v;
+            }
+        }
+    }
 }
 
 // Only the first n rows are visited, n the received count read on the
@@ -786,15 +803,16 @@ __device__ __forceinline__ void fused_permute_row(
 // before the weights, 302-309 us.  The kernel moves a 40/60 mix of reads
 // and writes at the rate of a device-to-device copy.
 constexpr int64_t kFusedPermuteGrid = 1 << 30;
-template <int NT, int VPT>
+template <int NT, int VPT, bool SC>
 __global__ __launch_bounds__(NT)
-void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs src_w, int64_t T,
-                                   int nvec, int k, int E, int El, int G, int rank,
-                                   const int32_t* __restrict__ recv_src,
+void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_s, RankPtrs src_idx, RankPtrs src_w,
+                                   int64_t T, int nvec, int nb, int k, int E, int El, int G,
+                                   int rank, const int32_t* __restrict__ recv_src,
                                    const int64_t* __restrict__ recv_topk_idx,
                                    const int32_t* __restrict__ num_recv,
                                    const int32_t* __restrict__ slot, int64_t rows,
-                                   uint4* __restrict__ recv_x, float* __restrict__ recv_w)
+                                   uint4* __restrict__ recv_x, float* __restrict__ recv_s,
+                                   float* __restrict__ recv_w)
 {
     const int64_t R = (int64_t)G * T;
     int64_t n = R;
@@ -803,8 +821,9 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_idx, RankPtrs sr
         n = c < 0 ? 0 : (c < R ? c : R);
     }
     for (int64_t i = blockIdx.x; i < n; i += gridDim.x)
-        fused_permute_row<NT, VPT>(src_x, src_idx, src_w, T, nvec, k, E, El, G, rank, recv_src,
-                                   recv_topk_idx, slot, rows, recv_x, recv_w, i);
+        fused_permute_row<NT, VPT, SC>(src_x, src_s, src_idx, src_w, T, nvec, nb, k, E, El, G,
+                                       rank, recv_src, recv_topk_idx, slot, rows, recv_x, recv_s,
+                                       recv_w, i);
 }
 
 // ---------------------------------------------------------------- combine
@@ -1115,36 +1134,54 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& src_idx,
-                                         const RankPtrs& src_w, int64_t tokens_per_rank,
-                                         int hidden, int num_topk, int num_experts, int num_ranks,
-                                         int rank, const int32_t* recv_src,
-                                         const int64_t* recv_topk_idx, const int32_t* num_recv,
-                                         const int32_t* slot, int64_t rows, void* recv_x,
-                                         float* recv_w, hipStream_t stream)
+static hipError_t launch_fused_permute_rows(const RankPtrs& src_x, const RankPtrs& src_s,
+                                            const RankPtrs& src_idx, const RankPtrs& src_w,
+                                            int64_t tokens_per_rank, int nvec, int nb,
+                                            int num_topk, int num_experts, int num_ranks,
+                                            int rank, const int32_t* recv_src,
+                                            const int64_t* recv_topk_idx, const int32_t* num_recv,
+                                            const int32_t* slot, int64_t rows, void* recv_x,
+                                            float* recv_s, float* recv_w, hipStream_t stream)
 {
     const int64_t R = tokens_per_rank * num_ranks;
     if (R == 0) return hipSuccess;
-    const int nvec = hidden / 8;
     const dim3 grid((unsigned)std::min(R, kFusedPermuteGrid));
     const int El = num_experts / num_ranks;
     uint4* rx = static_cast<uint4*>(recv_x);
+    const bool sc = recv_s != nullptr;
+#define EP_FP_SC(NT, V, SC)                                                                      \
+    hipLaunchKernelGGL((dispatch_fused_permute_kernel<NT, V, SC>), grid, dim3(NT), 0, stream,      \
+                       src_x, src_s, src_idx, src_w, tokens_per_rank, nvec, nb, num_topk,          \
+                       num_experts, El, num_ranks, rank, recv_src, recv_topk_idx, num_recv, slot,  \
+                       rows, rx, recv_s, recv_w)
 #define EP_FP(NT, V)                                                                            \
-    hipLaunchKernelGGL((dispatch_fused_permute_kernel<NT, V>), grid, dim3(NT), 0, stream, src_x, \
-                       src_idx, src_w, tokens_per_rank, nvec, num_topk, num_experts, El,        \
-                       num_ranks, rank,                                                          \
-                       recv_src, recv_topk_idx, num_recv, slot, rows, rx, recv_w)
+    if (sc) { EP_FP_SC(NT, V, true); } else { EP_FP_SC(NT, V, false); }
     if (nvec <= 64) {
         EP_FP(64, 1);
         return hipGetLastError();
     }
+    // whole passes of 128 lanes if some vpt <= 8 gives them, else whole
+    // passes of 64 lanes (an 8-bit row of 7168 bytes: 448 vectors, 64 x 7),
+    // else 128 lanes and a ragged tail
     const int fit = nvec / 128;
     int vpt = fit < 1 ? 1 : (fit > 8 ? 8 : fit);
-    for (int v = 8; v >= 1; --v) {
-        if (nvec % (128 * v) == 0) {
-            vpt = v;
-            break;
+    int nt = 0;
+    for (int v = 8; v >= 1 && !nt; --v)
+        if (nvec % (128 * v) == 0) nt = 128, vpt = v;
+    for (int v = 8; v >= 1 && !nt; --v)
+        if (nvec % (64 * v) == 0) nt = 64, vpt = v;
+    if (nt == 64) {
+        switch (vpt) {
+        case 1: EP_FP(64, 1); break;
+        case 2: EP_FP(64, 2); break;
+        case 3: EP_FP(64, 3); break;
+        case 4: EP_FP(64, 4); break;
+        case 5: EP_FP(64, 5); break;
+        case 6: EP_FP(64, 6); break;
+        case 7: EP_FP(64, 7); break;
+        default: EP_FP(64, 8); break;
         }
+        return hipGetLastError();
     }
     switch (vpt) {
     case 1: EP_FP(128, 1); break;
@@ -1157,8 +1194,41 @@ hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& 
     default: EP_FP(128, 8); break;
     }
 #undef EP_FP
+#undef EP_FP_SC
     return hipGetLastError();
 }
+
+hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& src_idx,
+                                         const RankPtrs& src_w, int64_t tokens_per_rank,
+                                         int hidden, int num_topk, int num_experts, int num_ranks,
+                                         int rank, const int32_t* recv_src,
+                                         const int64_t* recv_topk_idx, const int32_t* num_recv,
+                                         const int32_t* slot, int64_t rows, void* recv_x,
+                                         float* recv_w, hipStream_t stream)
+{
+    const RankPtrs none = {};
+    return launch_fused_permute_rows(src_x, none, src_idx, src_w, tokens_per_rank, hidden / 8, 0,
+                                     num_topk, num_experts, num_ranks, rank, recv_src,
+                                     recv_topk_idx, num_recv, slot, rows, recv_x, nullptr, recv_w,
+                                     stream);
+}
+
+hipError_t launch_dispatch_fused_permute_prequant(const RankPtrs& src_q, const RankPtrs& src_s,
+                                                  const RankPtrs& src_idx, const RankPtrs& src_w,
+                                                  int64_t tokens_per_rank, int hidden,
+                                                  int num_topk, int num_experts, int num_ranks,
+                                                  int rank, const int32_t* recv_src,
+                                                  const int64_t* recv_topk_idx,
+                                                  const int32_t* num_recv, const int32_t* slot,
+                                                  int64_t rows, void* recv_q, float* recv_s,
+                                                  float* recv_w, hipStream_t stream)
+{
+    return launch_fused_permute_rows(src_q, src_s, src_idx, src_w, tokens_per_rank, hidden / 16,
+                                     hidden / 128, num_topk, num_experts, num_ranks, rank, recv_src,
+                                     recv_topk_idx, num_recv, slot, rows, recv_q, recv_s, recv_w,
+                                     stream);
+}
+
 
 hipError_t launch_combine_ranked(const RankPtrs& src_y, int64_t src_rows, const int32_t* s2d,
                                  int64_t num_tokens, int hidden, int num_ranks, void* out,

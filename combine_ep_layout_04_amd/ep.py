@@ -49,7 +49,8 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
-           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute", "ep_combine_ranked",
+           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute",
+           "ep_dispatch_fused_permute_prequantized", "ep_combine_ranked",
            "ep_dispatch_ranked_backward", "ep_dispatch_colmajor_workspace_size",
            "ep_dispatch_colmajor_scales", "ep_dispatch_prequantized_colmajor")
 
@@ -122,6 +123,9 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P,
                                                 i64, P, P, P]
         L.ep_dispatch_fused_permute.restype = i32
+        L.ep_dispatch_fused_permute_prequantized.argtypes = [P, P, P, P, i64, i32, i32, i32, i32,
+                                                             i32, P, P, P, P, i64, P, P, P, P]
+        L.ep_dispatch_fused_permute_prequantized.restype = i32
         L.ep_combine_ranked.argtypes = [P, i64, P, i64, i32, i32, P, P]
         L.ep_combine_ranked.restype = i32
         L.ep_dispatch_ranked_backward.argtypes = [P, P, i64, P, P, i64, i32, i32, i32, i32, P, P,
@@ -754,6 +758,34 @@ def ep_dispatch_ranked_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor,
     return dest_q, dest_scales, dest_weights
 
 
+def _fused_permute_tables(G, T, k, R, src_topk_idx, src_topk_weights, recv_weights):
+    itab = wtab = None
+    if recv_weights is not None:
+        _need(recv_weights, "recv_weights", torch.float32, R)
+        if src_topk_idx is None or len(src_topk_idx) != G:
+            raise ValueError("recv_weights needs src_topk_idx for every rank")
+        for d, t in enumerate(src_topk_idx):
+            _need(t, f"src_topk_idx[{d}]", torch.int64, T * k)
+        itab = _ptr_table(src_topk_idx)
+        if src_topk_weights is not None:
+            for d, t in enumerate(src_topk_weights):
+                if t is not None:
+                    _need(t, f"src_topk_weights[{d}]", torch.float32, T * k)
+            wtab = _ptr_table(src_topk_weights)
+    return itab, wtab
+
+
+def _fused_permute_routing(G, T, recv_src, recv_topk_idx, slot, num_recv):
+    _need(recv_src, "recv_src", torch.int32, G * T)
+    _need(recv_topk_idx, "recv_topk_idx", torch.int64)
+    _need(slot, "slot", torch.int32)
+    if slot.dim() != 2 or slot.shape[0] != G * T or recv_topk_idx.shape != slot.shape:
+        raise ValueError("slot and recv_topk_idx must be [G*T, k]")
+    if num_recv is not None:
+        _need(num_recv, "num_recv", torch.int32, 1)
+    return slot.shape[1]
+
+
 def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torch.Tensor,
                               slot: torch.Tensor, num_experts: int, rank: int, *, rows: int,
                               src_topk_idx=None, src_topk_weights=None, num_recv=None,
@@ -775,12 +807,7 @@ def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torc
     for t in src_x:
         if tuple(t.shape) != (T, H):
             raise ValueError("every src_x must be [T, H]")
-    _need(recv_src, "recv_src", torch.int32, G * T)
-    _need(recv_topk_idx, "recv_topk_idx", torch.int64)
-    _need(slot, "slot", torch.int32)
-    if slot.dim() != 2 or slot.shape[0] != G * T or recv_topk_idx.shape != slot.shape:
-        raise ValueError("slot and recv_topk_idx must be [G*T, k]")
-    k = slot.shape[1]
+    k = _fused_permute_routing(G, T, recv_src, recv_topk_idx, slot, num_recv)
     R = int(rows)
     dev = src_x[0].device
     if recv_x is None:
@@ -788,21 +815,7 @@ def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torc
     _need(recv_x, "recv_x", torch.bfloat16, R * H)
     if want_weights and recv_weights is None:
         recv_weights = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
-    itab = wtab = None
-    if recv_weights is not None:
-        _need(recv_weights, "recv_weights", torch.float32, R)
-        if src_topk_idx is None or len(src_topk_idx) != G:
-            raise ValueError("recv_weights needs src_topk_idx for every rank")
-        for d, t in enumerate(src_topk_idx):
-            _need(t, f"src_topk_idx[{d}]", torch.int64, T * k)
-        itab = _ptr_table(src_topk_idx)
-        if src_topk_weights is not None:
-            for d, t in enumerate(src_topk_weights):
-                if t is not None:
-                    _need(t, f"src_topk_weights[{d}]", torch.float32, T * k)
-            wtab = _ptr_table(src_topk_weights)
-    if num_recv is not None:
-        _need(num_recv, "num_recv", torch.int32, 1)
+    itab, wtab = _fused_permute_tables(G, T, k, R, src_topk_idx, src_topk_weights, recv_weights)
     xtab = _ptr_table(src_x)
     st = lib().ep_dispatch_fused_permute(xtab[1], None if itab is None else itab[1],
                                          None if wtab is None else wtab[1], T, H, k,
@@ -812,6 +825,52 @@ def ep_dispatch_fused_permute(src_x, recv_src: torch.Tensor, recv_topk_idx: torc
                                          _ptr(recv_weights), _stream(stream))
     _check(st, "ep_dispatch_fused_permute")
     return recv_x, recv_weights
+
+
+def ep_dispatch_fused_permute_prequantized(src_q, src_scales, recv_src: torch.Tensor,
+                                           recv_topk_idx: torch.Tensor, slot: torch.Tensor,
+                                           num_experts: int, rank: int, *, rows: int,
+                                           src_topk_idx=None, src_topk_weights=None,
+                                           num_recv=None, recv_q=None, recv_scales=None,
+                                           recv_weights=None, want_weights: bool = False,
+                                           stream=None):
+    """ep_dispatch_fused_permute for tokens the senders already cast to
+    8 bits: ``src_q`` is a list of the G ranks' code rows (uint8 [T, H], H a
+    multiple of 128) and ``src_scales`` their scale rows (fp32 [T, H/128]).
+    Returns (recv_q uint8 [rows, H], recv_scales fp32 [rows, H/128],
+    recv_weights fp32 [rows] or None)."""
+    G = len(src_q)
+    if len(src_scales) != G:
+        raise ValueError("one scale tensor per rank")
+    for d, t in enumerate(src_q):
+        _need(t, f"src_q[{d}]", torch.uint8)
+    T, H = src_q[0].shape
+    nb = H // 128
+    for d in range(G):
+        if tuple(src_q[d].shape) != (T, H):
+            raise ValueError("every src_q must be [T, H]")
+        _need(src_scales[d], f"src_scales[{d}]", torch.float32, T * nb)
+    k = _fused_permute_routing(G, T, recv_src, recv_topk_idx, slot, num_recv)
+    R = int(rows)
+    dev = src_q[0].device
+    if recv_q is None:
+        recv_q = torch.empty((max(R, 1), H), dtype=torch.uint8, device=dev)
+    if recv_scales is None:
+        recv_scales = torch.empty((max(R, 1), max(nb, 1)), dtype=torch.float32, device=dev)
+    _need(recv_q, "recv_q", torch.uint8, R * H)
+    _need(recv_scales, "recv_scales", torch.float32, R * nb)
+    if want_weights and recv_weights is None:
+        recv_weights = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
+    itab, wtab = _fused_permute_tables(G, T, k, R, src_topk_idx, src_topk_weights, recv_weights)
+    qtab = _ptr_table(src_q)
+    stab = _ptr_table(src_scales)
+    st = lib().ep_dispatch_fused_permute_prequantized(
+        qtab[1], stab[1], None if itab is None else itab[1], None if wtab is None else wtab[1], T,
+        H, k, int(num_experts), G, int(rank), _ptr(recv_src), _ptr(recv_topk_idx),
+        _ptr(num_recv), _ptr(slot), R, _ptr(recv_q), _ptr(recv_scales), _ptr(recv_weights),
+        _stream(stream))
+    _check(st, "ep_dispatch_fused_permute_prequantized")
+    return recv_q, recv_scales, recv_weights
 
 
 def ep_combine_ranked(src_y, sparse_to_dense: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:

@@ -202,7 +202,8 @@ KERNEL_KEYS = {
     # the combine over ranks of the row gradients (the same kernel and bytes
     # as combine_ranked) and the weight-gradient gather
     "dispatch_ranked_backward": (r"combine_ranked_tile_kernel<128>", r"ranked_weight_grad_kernel"),
-    "dispatch_fused_permute": r"dispatch_fused_permute_kernel<",
+    "dispatch_fused_permute": r"dispatch_fused_permute_kernel<\d+, \d+, false>",
+    "dispatch_fused_permute_prequantized": r"dispatch_fused_permute_kernel<\d+, \d+, true>",
 }
 COPY_KIB = float(1 << 20)  # the calibration kernel reads and writes 1 GiB
 

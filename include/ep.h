@@ -605,6 +605,35 @@ ep_status_t ep_dispatch_fused_permute(const void *const *src_x, const int64_t *c
                                       float *recv_weights, void *stream);
 
 /*
+ * ep_dispatch_fused_permute_prequantized -- ep_dispatch_fused_permute for
+ * tokens the senders already cast to 8 bits: each received token's code row
+ * (hidden bytes) and its scale row (hidden/128 fp32) are read once and
+ * written, bit for bit, to each of the token's local-expert rows.
+ *
+ * Passages: NeMo fused_a2a page, HybridEPDispatch (fp8_dispatch together
+ * with fuse_permute); NCCL EP page, ncclEpDispatch high-throughput branch
+ * (FP8 tokens travel with a 2-D fp32 scales tensor).
+ *
+ * In:  src_q       HOST array of G device pointers: rank s's code rows,
+ *                  bytes [tokens_per_rank, hidden] (16-byte aligned).
+ *      src_scales  HOST array of G device pointers: rank s's scale rows,
+ *                  fp32 [tokens_per_rank, hidden/128] (4-byte aligned).
+ *      the rest as ep_dispatch_fused_permute.
+ * Out: recv_q [rows, hidden] bytes (16-byte aligned) and recv_scales
+ *      [rows, hidden/128] fp32 (4-byte aligned): row slot[i, j] >= 0 of both
+ *      gets received row i's code and scale rows;
+ *      recv_weights as ep_dispatch_fused_permute.
+ *      Rows past `rows` are never written; rows nothing maps to are not.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
+ */
+ep_status_t ep_dispatch_fused_permute_prequantized(
+    const void *const *src_q, const float *const *src_scales, const int64_t *const *src_topk_idx,
+    const float *const *src_topk_weights, int64_t tokens_per_rank, int hidden, int num_topk,
+    int num_experts, int num_ranks, int rank, const int32_t *recv_src,
+    const int64_t *recv_topk_idx, const int32_t *num_recv, const int32_t *slot, int64_t rows,
+    void *recv_q, float *recv_scales, float *recv_weights, void *stream);
+
+/*
  * ep_combine_ranked -- gather this rank's tokens back from every rank.
  * In:  src_y                HOST array of G device pointers: rank d's
  *                           per-token outputs, bf16 [src_rows, hidden] (each

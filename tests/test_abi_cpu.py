@@ -405,6 +405,39 @@ def test_dispatch_fused_permute_zero_tokens_is_a_noop():
 
 
 @no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(G=0), 1), (dict(E=9), 1), (dict(rank=2), 1), (dict(H=136), 1), (dict(H=8), 1),
+    (dict(k=0), 1), (dict(rows=-1), 1), (dict(T=-1), 1),
+    (dict(sq="none"), 1), (dict(sq=(FAKE, FAKE + 8)), 1), (dict(ss="none"), 1),
+    (dict(ss=(FAKE, None)), 1), (dict(ss=(FAKE, FAKE + 2)), 1), (dict(si="none"), 1),
+    (dict(sw=(FAKE, FAKE + 2)), 1), (dict(src=None), 1), (dict(slot=None), 1),
+    (dict(out_q=None), 1), (dict(out_q=FAKE + 8), 1), (dict(out_s=None), 1),
+    (dict(out_s=FAKE + 2), 1), (dict(nr=FAKE + 2), 1),
+])
+def test_dispatch_fused_permute_prequantized_rejects(over, code):
+    a = dict(sq=(FAKE, FAKE), ss=(FAKE, FAKE), si=(FAKE, FAKE), sw=None, T=4, H=256, k=2, E=8,
+             G=2, rank=0, src=FAKE, rti=FAKE, nr=None, slot=FAKE, rows=16, out_q=FAKE,
+             out_s=FAKE, rw=FAKE)
+    a.update(over)
+    names = ("sq", "ss", "si", "sw")
+    tabs = {n: (None if a[n] in (None, "none") else _table(*a[n])) for n in names}
+    st = ep.lib().ep_dispatch_fused_permute_prequantized(
+        *[None if tabs[n] is None else ctypes.addressof(tabs[n]) for n in names],
+        a["T"], a["H"], a["k"], a["E"], a["G"], a["rank"], a["src"], a["rti"], a["nr"], a["slot"],
+        a["rows"], a["out_q"], a["out_s"], a["rw"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_dispatch_fused_permute_prequantized_zero_tokens_is_a_noop():
+    sq = _table(FAKE, FAKE)
+    assert ep.lib().ep_dispatch_fused_permute_prequantized(
+        ctypes.addressof(sq), ctypes.addressof(sq), None, None, 0, 256, 2, 8, 2, 0, None, None,
+        None, None, 0, None, None, None, None) == 0
+    assert ep.last_error() == ""
+
+
+@no_gpu
 @pytest.mark.parametrize("fmt,scale,ld,code", [
     (1, 0, 6, 1),      # fp32 scales: ld not a multiple of 4
     (1, 2, 20, 1),     # UE8M0: ld not a multiple of 16

@@ -221,6 +221,8 @@ def test_variants_and_backward_graph():
     idx_all = [idx] + [dev(make_routing(T, E, k, 950 + r)) for r in range(1, G)]
     x_all = [x] + [x_dev(make_random_case(960 + r, T, H, E, k).x_bits) for r in range(1, G)]
     w_all = [w] + [torch.full((T, k), 1.0 / k, dtype=torch.float32, device=DEV) for _ in range(1, G)]
+    q_all = [xq] + [x_all[r].view(torch.uint8)[:, :H].contiguous() for r in range(1, G)]
+    s_all = [xs] + [xs * (r + 1) for r in range(1, G)]
     El, W8, RG = E // G, (E + 7) // 8, G * T
     i32 = dict(dtype=torch.int32, device=DEV)
     f32 = dict(dtype=torch.float32, device=DEV)
@@ -256,6 +258,8 @@ def test_variants_and_backward_graph():
         "p_counts": torch.empty(El, **i32), "p_offsets": torch.empty(El + 1, **i32),
         "p_slot": torch.empty((RG, k), **i32),
         "perm_x": torch.empty((RG * k, H), **bf), "perm_w": torch.empty(RG * k, **f32),
+        "perm_q": torch.empty((RG * k, H), **u8), "perm_s": torch.empty((RG * k, nb), **f32),
+        "perm_qw": torch.empty(RG * k, **f32),
     }
     dq = [torch.empty((RG, H), **u8) for _ in range(G)]
     ds = [torch.empty((RG, nb), **f32) for _ in range(G)]
@@ -303,6 +307,11 @@ def test_variants_and_backward_graph():
                                      src_topk_idx=idx_all, src_topk_weights=w_all,
                                      num_recv=o["nrecv"], recv_x=o["perm_x"],
                                      recv_weights=o["perm_w"])
+        ep.ep_dispatch_fused_permute_prequantized(q_all, s_all, o["rsrc"], o["rti"], o["p_slot"], E,
+                                                  0, rows=RG * k, src_topk_idx=idx_all,
+                                                  src_topk_weights=w_all, num_recv=o["nrecv"],
+                                                  recv_q=o["perm_q"], recv_scales=o["perm_s"],
+                                                  recv_weights=o["perm_qw"])
 
     for t in o.values():
         _bits(t).fill_(0x55)

@@ -8,7 +8,8 @@ dedicated tests:
 
 * layout, dispatch copies, 8-bit codes and scales (row-major, and
   column-major through the two-pass cast), the rank layout, the per-rank
-  copies and the fused permute bounded by the device-side received count:
+  copies and the fused permute (bf16 rows, and 8-bit code rows with their
+  scale rows) bounded by the device-side received count:
   bit-exact, with sentinel-filled outputs;
 * combine, combine backward, dispatch backward and the combine over ranks:
   one bf16 ulp plus the fp32 accumulation bound (and the dot-product bound
@@ -259,3 +260,26 @@ def test_random_case(seed):
     np.testing.assert_array_equal(bf16_bits(px)[wr], ox[wr])
     assert np.all(bf16_bits(px)[~wr] == 0xFFFD)
     np.testing.assert_array_equal(host(pw)[wr].view(np.uint32), ow[wr].view(np.uint32))
+
+    if H % 128 == 0:
+        # the same receive for 8-bit code rows and their scale rows
+        nb = H // 128
+        srng = np.random.default_rng(9700 + seed)
+        qs = [srng.integers(0, 256, (T, H), dtype=np.uint8) for _ in range(G)]
+        ss = [srng.standard_normal((T, nb)).astype(np.float32) for _ in range(G)]
+        pq = torch.full((prow, H), 0xEE, dtype=torch.uint8, device=DEV)
+        psc = torch.full((prow, nb), float("nan"), dtype=torch.float32, device=DEV)
+        pqw = torch.full((prow,), float("nan"), dtype=torch.float32, device=DEV)
+        ep.ep_dispatch_fused_permute_prequantized(
+            [dev(v) for v in qs], [dev(v) for v in ss], lay.recv_src, lay.recv_topk_idx,
+            dev(Lr.slot), E, 0, rows=prow, src_topk_idx=[dev(i) for i in idx_all],
+            src_topk_weights=[None if v is None else dev(v) for v in ws_all],
+            num_recv=lay.num_recv, recv_q=pq, recv_scales=psc, recv_weights=pqw)
+        torch.cuda.synchronize()
+        oq, osc, oqw = oracle.dispatch_fused_permute_prequant(
+            qs, ss, idx_all, ws_all, E, 0, RL.recv_src, RL.recv_topk_idx, Lr.slot, prow)
+        np.testing.assert_array_equal(host(pq)[wr], oq[wr])
+        assert np.all(host(pq)[~wr] == 0xEE)
+        np.testing.assert_array_equal(host(psc)[wr].view(np.uint32), osc[wr].view(np.uint32))
+        assert np.all(np.isnan(host(psc)[~wr]))
+        np.testing.assert_array_equal(host(pqw)[wr].view(np.uint32), oqw[wr].view(np.uint32))

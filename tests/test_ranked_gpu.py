@@ -509,6 +509,115 @@ def test_dispatch_ranked_prequantized_headline():
     check_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, w.E, G, L.sparse_to_dense, w.T)
 
 
+def code_rows(seed, G, T, H):
+    """G ranks' code rows and scale rows; the scales hold a few special
+    values (infinities, a NaN payload, -0, a subnormal) that a bit copy keeps."""
+    rng = np.random.default_rng(seed)
+    qs = [rng.integers(0, 256, (T, H), dtype=np.uint8) for _ in range(G)]
+    ss = []
+    for _ in range(G):
+        s = rng.standard_normal((T, H // 128)).astype(np.float32)
+        flat = s.reshape(-1)
+        special = np.array([0x7F800000, 0xFF800000, 0x7FC01234, 0x80000000, 0x00000005],
+                           np.uint32).view(np.float32)
+        at = rng.choice(flat.size, size=min(flat.size, 5), replace=False)
+        flat[at] = special[:at.size]
+        ss.append(s)
+    return qs, ss
+
+
+def check_fused_permute_prequant(qs, ss, idx, ws, E, G, r, A=1, with_weights=True,
+                                 bound="layout"):
+    T, H = qs[0].shape
+    nb = H // 128
+    El = E // G
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, T, E, G, r, idx[0].shape[1])
+    Lr = oracle.layout(L.recv_topk_idx, El, alignment=A)
+    rows = max(Lr.n, 1)
+    oq = torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV)
+    osc = torch.full((rows, nb), 0x7FBADBAD, dtype=torch.int32, device=DEV).view(torch.float32)
+    rw = torch.full((rows,), float("nan"), dtype=torch.float32, device=DEV) if with_weights else None
+    n = L.num_recv if bound == "layout" else bound
+    nr = None if n is None else dev(np.array([n], np.int32))
+    ep.ep_dispatch_fused_permute_prequantized(
+        [dev(q) for q in qs], [dev(x) for x in ss], dev(L.recv_src), dev(L.recv_topk_idx),
+        dev(Lr.slot), E, r, rows=rows, src_topk_idx=[dev(i) for i in idx] if with_weights else None,
+        src_topk_weights=None if ws is None else [dev(w) for w in ws], num_recv=nr, recv_q=oq,
+        recv_scales=osc, recv_weights=rw)
+    torch.cuda.synchronize()
+    visited = G * T if n is None else min(max(n, 0), G * T)
+    want_src = L.recv_src.copy()
+    want_src[visited:] = -1
+    wq, wsc, ww = oracle.dispatch_fused_permute_prequant(
+        qs, ss, idx, ws if ws is not None else [None] * G, E, r, want_src, L.recv_topk_idx,
+        Lr.slot, rows, with_weights)
+    written = np.zeros(rows, bool)
+    sl = Lr.slot[:visited]
+    written[sl[(sl >= 0) & (want_src[:visited, None] >= 0)]] = True
+    gq, gs = host(oq), host(osc).view(np.uint32)
+    np.testing.assert_array_equal(gq[written], wq[written])
+    np.testing.assert_array_equal(gs[written], wsc[written].view(np.uint32))
+    assert np.all(gq[~written] == 0xEE), "a padding code row was written"
+    assert np.all(gs[~written] == 0x7FBADBAD), "a padding scale row was written"
+    if with_weights:
+        g = host(rw)
+        np.testing.assert_array_equal(g[written].view(np.uint32), ww[written].view(np.uint32))
+        assert np.all(np.isnan(g[~written]))
+    return int(written.sum())
+
+
+@pytest.mark.parametrize("G,T,H,E,k,A,weights", [
+    (1, 3, 128, 2, 1, 1, True),
+    (2, 40, 256, 8, 3, 1, True),       # 16 vectors: one short wavefront pass
+    (4, 200, 2176, 16, 5, 4, True),    # 136 vectors: one pass + tail, 17 scales
+    (3, 90, 2048, 9, 9, 1, False),     # k = 9, no weights
+    (8, 64, 7168, 64, 8, 16, True),    # 448 vectors, 56 scales
+    (64, 8, 256, 128, 64, 1, True),    # G = EP_MAX_RANKS, k = EP_MAX_TOPK
+])
+def test_fused_permute_prequantized_small(G, T, H, E, k, A, weights):
+    cases = rank_cases(G + H + k + 7, G, T, 8, E, k, mask_frac=0.2, dup_frac=1.0,
+                       invalid_frac=0.05)
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases] if weights else None
+    qs, ss = code_rows(G * 31 + T, G, T, H)
+    for r in sorted({0, G - 1, G // 2}):
+        print(f"\n[ranked] fused permute 8-bit G={G} T={T} H={H} E={E} k={k} A={A} rank={r}",
+              flush=True)
+        check_fused_permute_prequant(qs, ss, idx, ws, E, G, r, A=A)
+        check_fused_permute_prequant(qs, ss, idx, ws, E, G, r, with_weights=False, bound=None)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.5, -1.0, 3.0])
+def test_fused_permute_prequantized_bounded_by_num_recv(frac):
+    G, T, H, E, k = 8, 300, 1152, 32, 6
+    cases = rank_cases(321, G, T, 8, E, k, mask_frac=0.1, dup_frac=0.3)
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases]
+    qs, ss = code_rows(17, G, T, H)
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    nrecv = oracle.rank_layout(gmap, T, E, G, 5, k).num_recv
+    n = int(frac * nrecv) if 0 <= frac <= 1 else (-7 if frac < 0 else G * T + 5)
+    print(f"\n[ranked] fused permute 8-bit bounded by num_recv={n} of {nrecv}", flush=True)
+    check_fused_permute_prequant(qs, ss, idx, ws, E, G, 5, bound=n)
+
+
+def test_fused_permute_prequantized_headline():
+    # rank 0 of 8 at the 8-bit workload's shape (T=8192, H=7168, E=256, k=8):
+    # the senders' code rows and scale rows as the oracle's cast makes them
+    w = WORKLOADS["fp8"]
+    G = 8
+    idx = headline_global_map(G)
+    inp = make_inputs(w)
+    idx[0] = inp.topk_idx
+    xq, xs, _ = oracle.dispatch_quant(inp.x_bits, np.arange(w.T, dtype=np.int32)[:, None])
+    qs, ss = code_rows(99, G, w.T, w.H)
+    qs[0], ss[0] = xq, xs
+    ws = [inp.topk_weights] + [np.full((w.T, w.k), 1.0 / w.k, np.float32)] * (G - 1)
+    print("\n[ranked] fused permute 8-bit, fp8 workload, G=8 rank 0", flush=True)
+    assert check_fused_permute_prequant(qs, ss, idx, ws, w.E, G, 0) > w.T
+
+
 def test_fused_permute_skips_rows_without_a_valid_source():
     # recv_src entries outside [0, G*T) name no token: their rows are skipped
     # (the result equals the oracle's with those entries set to -1)
