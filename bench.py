@@ -49,8 +49,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# the source file of each kernel bench.py reports (plus the shared internal
-# header and the build flags)
+# the source file of each kernel bench.py reports (plus the shared internal,
+# device and cast headers and the build flags)
 KERNEL_SOURCES = {
     "dispatch_bf16": "ep_dispatch.hip", "dispatch_fp8": "ep_dispatch.hip",
     "dispatch_fp8_e5m2_fp32": "ep_dispatch.hip", "dispatch_fp8_e4m3_pow2": "ep_dispatch.hip",
@@ -65,6 +65,7 @@ KERNEL_SOURCES = {
     "dispatch_fused_permute": "ep_ranked.hip",
     "dispatch_fused_permute_prequantized": "ep_ranked.hip",
     "dispatch_ranked_prequantized": "ep_ranked.hip",
+    "dispatch_ranked_fp8": "ep_ranked.hip",
     "combine": "ep_combine.hip", "combine_backward": "ep_backward.hip",
     "layout_count": "ep_layout.hip",
     "layout_scatter": "ep_layout.hip",
@@ -81,12 +82,12 @@ def _code_only(text: str) -> str:
 
 def source_digest(kernel_key: str) -> str:
     """Digest of what a kernel's counters depend on: the code of its source
-    file and of the internal and device headers, and the hipcc flags."""
+    file and of the internal, device and cast headers, and the hipcc flags."""
     from combine_ep_layout_04_amd.build import HIPCC_FLAGS
 
     csrc = os.path.join(ROOT, "combine_ep_layout_04_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h", "ep_device.h"):
+    for f in (KERNEL_SOURCES[kernel_key], "ep_internal.h", "ep_device.h", "ep_cast.h"):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     h.update(" ".join(HIPCC_FLAGS).encode())
@@ -599,6 +600,14 @@ def main():
         "ep_dispatch_ranked_prequantized"), args.steps)
     drq_bytes = (T * H + T * (H // 128) * 4 + pairs * (H + (H // 128) * 4) + T * G * 4 + T * k * 12
                  + pairs * k * 4)
+    # the same sends with the cast on the way (the fp8 workload's bf16
+    # tokens, E4M3 with fp32 scales): no per-token code and scale buffers
+    drf_us = time_call(lambda: check(L.ep_dispatch_ranked_fp8(
+        xf.data_ptr(), p["idx"], p["wt"], T, H, k, E, G, rq["s2d"], 1, 0, ctypes.addressof(qtab),
+        ctypes.addressof(stab), ctypes.addressof(wtab), T, s), "ep_dispatch_ranked_fp8"),
+        args.steps)
+    drf_bytes = (T * H * 2 + pairs * (H + (H // 128) * 4) + T * G * 4 + T * k * 12
+                 + pairs * k * 4)
     del dest_q, dest_s, dest_w
 
     # receive side of rank 0 with the permute fused in: every token it
@@ -778,6 +787,8 @@ def main():
         "dispatch_ranked_backward": entry(rb_us, bytes=rbm["dispatch_ranked_backward"], ranks=G,
                                           rows_read=pairs),
         "dispatch_ranked_prequantized": entry(drq_us, bytes=drq_bytes, ranks=G, rows_written=pairs),
+        "dispatch_ranked_fp8": entry(drf_us, bytes=drf_bytes, ranks=G, rows_written=pairs,
+                                     workload="fp8 tokens, headline routing"),
         "dispatch_fused_permute": entry(fp_us, bytes=fp_bytes, ranks=G, tokens_received=n_recv,
                                         expert_rows_written=n_exp),
         "dispatch_fused_permute_prequantized": entry(fpq_us, bytes=fpq_bytes, ranks=G,

@@ -592,6 +592,63 @@ ep_status_t ep_dispatch_ranked_prequantized(const void* x_q, const float* x_scal
                     "ep_dispatch_ranked_prequantized launch");
 }
 
+ep_status_t ep_dispatch_ranked_fp8(const void* x, const int64_t* topk_idx, const float* topk_weights,
+                                   int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                   int num_ranks, const int32_t* sparse_to_dense_map,
+                                   int out_dtype, int scale_format, void* const* dest_q,
+                                   void* const* dest_scales, float* const* dest_weights,
+                                   int64_t dest_rows, void* stream)
+{
+    g_last_error[0] = '\0';
+    ep_status_t st = check_tokens(num_tokens, num_topk);
+    if (st) return st;
+    if (out_dtype != EP_OUT_FP8_E4M3 && out_dtype != EP_OUT_FP8_E5M2)
+        return fail(EP_INVALID_ARGUMENT, "out_dtype %d is not an 8-bit format", out_dtype);
+    if (scale_format != EP_SCALE_FP32 && scale_format != EP_SCALE_FP32_POW2 &&
+        scale_format != EP_SCALE_UE8M0)
+        return fail(EP_INVALID_ARGUMENT, "unknown scale_format %d", scale_format);
+    st = check_hidden(hidden, 128);
+    if (st) return st;
+    st = check_ranks(num_experts, num_ranks);
+    if (st) return st;
+    if (dest_rows < 0) return fail(EP_INVALID_ARGUMENT, "dest_rows < 0");
+    if (ep::ranked_fp8_blocks(num_tokens, hidden, num_ranks) > INT32_MAX)
+        return fail(EP_UNSUPPORTED, "num_tokens too large for hidden %d and %d ranks", hidden,
+                    num_ranks);
+    if (!dest_q || !dest_scales)
+        return fail(EP_INVALID_ARGUMENT, "dest_q and dest_scales (host arrays of pointers) are required");
+    const bool bytes = scale_format == EP_SCALE_UE8M0;
+    ep::RankPtrs pq = {}, ps = {}, pw = {};
+    for (int d = 0; d < num_ranks; ++d) {
+        if (!dest_q[d] || !aligned16(dest_q[d]))
+            return fail(EP_INVALID_ARGUMENT, "dest_q[%d] must be non-NULL and 16-byte aligned", d);
+        if (!dest_scales[d] || (!bytes && (reinterpret_cast<uintptr_t>(dest_scales[d]) & 3u)))
+            return fail(EP_INVALID_ARGUMENT, "dest_scales[%d] must be non-NULL%s", d,
+                        bytes ? "" : " and 4-byte aligned");
+        pq.p[d] = dest_q[d];
+        ps.p[d] = dest_scales[d];
+        if (dest_weights) {
+            if ((reinterpret_cast<uintptr_t>(dest_weights[d]) & 3u))
+                return fail(EP_INVALID_ARGUMENT, "dest_weights[%d] must be 4-byte aligned", d);
+            pw.p[d] = dest_weights[d];
+        }
+    }
+    if (num_tokens == 0) return EP_SUCCESS;
+    if (!x || !sparse_to_dense_map)
+        return fail(EP_INVALID_ARGUMENT, "x and sparse_to_dense_map are required");
+    if (!aligned16(x)) return fail(EP_INVALID_ARGUMENT, "x must be 16-byte aligned");
+    if (dest_weights && (!topk_idx || (reinterpret_cast<uintptr_t>(topk_idx) & 7u)))
+        return fail(EP_INVALID_ARGUMENT, "dest_weights needs an 8-byte aligned topk_idx");
+    return from_hip(ep::launch_dispatch_ranked_fp8(x, topk_idx, topk_weights, num_tokens, hidden,
+                                                   num_topk, num_experts, num_ranks,
+                                                   sparse_to_dense_map,
+                                                   out_dtype == EP_OUT_FP8_E5M2 ? 1 : 0,
+                                                   scale_format, pq, ps, pw,
+                                                   dest_weights != nullptr, dest_rows,
+                                                   static_cast<hipStream_t>(stream)),
+                    "ep_dispatch_ranked_fp8 launch");
+}
+
 // Checks shared by the two fused-permute entry points; fills the pointer
 // tables (src_s only when scales is true).
 static ep_status_t fused_permute_args(const void* const* src_x, const float* const* src_s,

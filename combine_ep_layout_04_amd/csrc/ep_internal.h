@@ -120,6 +120,19 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
                                   const RankPtrs& dest_scales, int num_scales, int64_t dest_rows,
                                   hipStream_t stream);
 
+// The 8-bit cast of ep_dispatch_ex sent once per destination rank: codes
+// [dest_rows, hidden] and scale rows [dest_rows, hidden/128] (fp32, or UE8M0
+// bytes) per rank.  ranked_fp8_blocks: the workgroups it launches (the call
+// fails past INT32_MAX).
+int64_t ranked_fp8_blocks(int64_t num_tokens, int hidden, int num_ranks);
+hipError_t launch_dispatch_ranked_fp8(const void* x, const int64_t* topk_idx,
+                                      const float* topk_weights, int64_t num_tokens, int hidden,
+                                      int num_topk, int num_experts, int num_ranks,
+                                      const int32_t* s2d, int format, int scale_mode,
+                                      const RankPtrs& dest_q, const RankPtrs& dest_scales,
+                                      const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                      hipStream_t stream);
+
 hipError_t launch_dispatch_fused_permute(const RankPtrs& src_x, const RankPtrs& src_idx,
                                          const RankPtrs& src_w, int64_t tokens_per_rank,
                                          int hidden, int num_topk, int num_experts, int num_ranks,

@@ -42,7 +42,8 @@
 //                 tile 0 also writes the token's weights for those ranks'
 //                 experts.  Rows under 512 vectors, and 8-bit rows with
 //                 their scales, take one workgroup per token that holds the
-//                 row in registers.
+//                 row in registers.  The 8-bit cast sent once per rank is
+//                 tiled the same way, each lane casting 16 channels.
 //   fused permute: the receiving rank's dispatch with the permute folded
 //                 in: one workgroup per received token reads the sender's
 //                 row once and stores it to each of the rank's local-expert
@@ -57,6 +58,7 @@
 
 #include <algorithm>
 
+#include "ep_cast.h"
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -532,6 +534,37 @@ __device__ __forceinline__ void write_rank_weights(float* row, int k, int32_t e_
     if (lane < k && lane >= members) row[lane] = 0.0f;
 }
 
+// Wavefront 0 of a workgroup serving token t: lane j (< k) takes slot j's
+// expert and the fp32 sum, in increasing j, of the weights of the slots with
+// the same expert, and each rank d in [d0, d1) that receives the token (row
+// readlane(p, d) >= 0) gets its weight row.
+__device__ __forceinline__ void ranked_token_weights(const int64_t* __restrict__ idx,
+                                                     const float* __restrict__ w, int64_t t, int k,
+                                                     int E, int El, int32_t p, int d0, int d1,
+                                                     const RankPtrs& dw)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t e64 = lane < k ? idx[t * k + lane] : -1;
+    const int32_t e_j = (e64 >= 0 && e64 < E) ? (int32_t)e64 : -1;
+    const float w_j = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
+    float sum = 0.0f;
+    bool first = e_j >= 0;
+    for (int jj = 0; jj < k; ++jj) {
+        const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
+        const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_j), jj));
+        if (e2 == e_j) {
+            sum = sum + w2;
+            if (jj < lane) first = false;
+        }
+    }
+    for (int d = d0; d < d1; ++d) {
+        const int32_t pd = __builtin_amdgcn_readlane(p, d);
+        float* base = static_cast<float*>(dw.p[d]);
+        if (pd < 0 || base == nullptr) continue;
+        write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
+    }
+}
+
 // Rows are nvec 16-byte vectors (bf16 tokens, or 8-bit codes); with xs, the
 // token's nb fp32 scales are copied to ds[d] as well.  RG == 0: one
 // workgroup per token, all G ranks.  RG > 0: one workgroup per (token,
@@ -563,27 +596,7 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
     int32_t p = lane < G ? s2d[t * G + lane] : -1;
     if (p >= dest_rows) p = -1;
 
-    if (with_weights && tid < 64) {
-        const int64_t e64 = lane < k ? idx[t * k + lane] : -1;
-        const int32_t e_j = (e64 >= 0 && e64 < E) ? (int32_t)e64 : -1;
-        const float w_j = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
-        float sum = 0.0f;
-        bool first = e_j >= 0;
-        for (int jj = 0; jj < k; ++jj) {
-            const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
-            const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_j), jj));
-            if (e2 == e_j) {
-                sum = sum + w2;
-                if (jj < lane) first = false;
-            }
-        }
-        for (int d = d0; d < d1; ++d) {
-            const int32_t pd = __builtin_amdgcn_readlane(p, d);
-            float* base = static_cast<float*>(dw.p[d]);
-            if (pd < 0 || base == nullptr) continue;
-            write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
-        }
-    }
+    if (with_weights && tid < 64) ranked_token_weights(idx, w, t, k, E, El, p, d0, d1, dw);
 
     if (xs != nullptr) {
         for (int b0 = 0; b0 < nb; b0 += NT) {
@@ -661,27 +674,8 @@ void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
     int32_t p = lane < G ? s2d[t * G + lane] : -1;
     if (p >= dest_rows) p = -1;
 
-    if (with_weights && pt == 0 && tid < 64) {
-        const int64_t e64 = lane < k ? idx[t * k + lane] : -1;
-        const int32_t e_j = (e64 >= 0 && e64 < E) ? (int32_t)e64 : -1;
-        const float w_j = lane < k ? (w ? w[t * k + lane] : 1.0f) : 0.0f;
-        float sum = 0.0f;
-        bool first = e_j >= 0;
-        for (int jj = 0; jj < k; ++jj) {
-            const int32_t e2 = __builtin_amdgcn_readlane(e_j, jj);
-            const float w2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_j), jj));
-            if (e2 == e_j) {
-                sum = sum + w2;
-                if (jj < lane) first = false;
-            }
-        }
-        for (int d = d0; d < G && d < d0 + kRanksPerGroup; ++d) {
-            const int32_t pd = __builtin_amdgcn_readlane(p, d);
-            float* base = static_cast<float*>(dw.p[d]);
-            if (pd < 0 || base == nullptr) continue;
-            write_rank_weights(base + (int64_t)pd * k, k, e_j, sum, first, d, El);
-        }
-    }
+    if (with_weights && pt == 0 && tid < 64)
+        ranked_token_weights(idx, w, t, k, E, El, p, d0, min(G, d0 + kRanksPerGroup), dw);
 
     int32_t r[kRanksPerGroup];
 #pragma unroll
@@ -695,6 +689,67 @@ void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
         if (r[q] >= 0 && v < nvec)
             store_row16(buffer_rsrc(static_cast<uint4*>(dx.p[d0 + q]) + (int64_t)r[q] * nvec, nvec * 16),
                         v * 16, val);
+}
+
+// The 8-bit cast sent once per destination rank: the tiled form above with
+// each lane casting one unit of 16 channels (two input vectors, one 16-byte
+// code vector; ep_cast.h) instead of copying a vector.  Tiles of NL units
+// (64 where the last 128-unit tile would be at most half full, or the row
+// has at most 64 units), groups of kRanksPerGroup ranks; the first lane of
+// each 8-lane block stores the block's scale (fp32, or the UE8M0 byte) to
+// the scale row of each receiving rank.  Units past the row end read zeros
+// and store nothing (whole blocks lie on one side of it).
+template <int FMT, int SM, int NL>
+__global__ __launch_bounds__(NL)
+void dispatch_ranked_fp8_tile_kernel(const uint4* __restrict__ x, int nvec,
+                                     const int64_t* __restrict__ idx, const float* __restrict__ w,
+                                     int k, int E, int El, int G, const int32_t* __restrict__ s2d,
+                                     int64_t dest_rows, RankPtrs dq, RankPtrs ds, RankPtrs dw,
+                                     bool with_weights, int tpr, int64_t num_tiles, int groups)
+{
+    int64_t tile;
+    int g;
+    if (!xcd_tile(blockIdx.x, groups, num_tiles, tile, g)) return;
+    const int64_t t = tile / tpr;
+    const int pt = (int)(tile - t * tpr);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int d0 = g * kRanksPerGroup;
+    int32_t p = lane < G ? s2d[t * G + lane] : -1;
+    if (p >= dest_rows) p = -1;
+
+    if (with_weights && pt == 0 && tid < 64)
+        ranked_token_weights(idx, w, t, k, E, El, p, d0, min(G, d0 + kRanksPerGroup), dw);
+
+    int32_t r[kRanksPerGroup];
+#pragma unroll
+    for (int q = 0; q < kRanksPerGroup; ++q)
+        r[q] = d0 + q < G ? __builtin_amdgcn_readlane(p, d0 + q) : -1;
+    const int units = nvec >> 1;
+    const int nb = units / kLanesPerBlock;
+    const int unit = pt * NL + tid;
+    const __amdgpu_buffer_rsrc_t xs = buffer_rsrc(x + t * nvec, nvec * 16);
+    const uint4 lo = load_row16<0>(xs, unit * 32);
+    const uint4 hi = load_row16<0>(xs, unit * 32 + 16);
+    uint32_t sb;
+    const uint4 code = quantise16<FMT, SM>(lo, hi, sb);
+    const int bk = unit / kLanesPerBlock;
+    const bool scale_lane = (lane & (kLanesPerBlock - 1)) == 0 && bk < nb;
+#pragma unroll
+    for (int q = 0; q < kRanksPerGroup; ++q) {
+        if (r[q] < 0) continue;
+        if (unit < units)
+            store_row16(buffer_rsrc(static_cast<uint4*>(dq.p[d0 + q]) + (int64_t)r[q] * units,
+                                    units * 16),
+                        unit * 16, code);
+        if (scale_lane) {
+            const int64_t at = (int64_t)r[q] * nb + bk;
+            if (SM == kScaleUe8m0)
+                static_cast<uint8_t*>(ds.p[d0 + q])[at] = (uint8_t)sb;
+            else
+                static_cast<uint32_t*>(ds.p[d0 + q])[at] = sb;
+        }
+    }
 }
 
 // ------------------------------------------------ receive side, fused permute
@@ -828,8 +883,6 @@ void dispatch_fused_permute_kernel(RankPtrs src_x, RankPtrs src_s, RankPtrs src_
 
 // ---------------------------------------------------------------- combine
 
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
@@ -1131,6 +1184,60 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     default: EP_DR(128, 8); break;
     }
 #undef EP_DR
+    return hipGetLastError();
+}
+
+static int ranked_fp8_lanes(int units)
+{
+    return units <= 64 || narrow_tiles(units) ? kTileLanes / 2 : kTileLanes;
+}
+
+int64_t ranked_fp8_blocks(int64_t num_tokens, int hidden, int num_ranks)
+{
+    const int units = hidden / 16;
+    const int lanes = ranked_fp8_lanes(units);
+    const int64_t num_tiles = num_tokens * ((units + lanes - 1) / lanes);
+    const int groups = (num_ranks + kRanksPerGroup - 1) / kRanksPerGroup;
+    return (num_tiles + 7) / 8 * 8 * groups;
+}
+
+hipError_t launch_dispatch_ranked_fp8(const void* x, const int64_t* topk_idx,
+                                      const float* topk_weights, int64_t num_tokens, int hidden,
+                                      int num_topk, int num_experts, int num_ranks,
+                                      const int32_t* s2d, int format, int scale_mode,
+                                      const RankPtrs& dest_q, const RankPtrs& dest_scales,
+                                      const RankPtrs& dest_w, bool with_weights, int64_t dest_rows,
+                                      hipStream_t stream)
+{
+    if (num_tokens == 0) return hipSuccess;
+    const int nvec = hidden / 8;
+    const int units = hidden / 16;
+    const int lanes = ranked_fp8_lanes(units);
+    const int tpr = (units + lanes - 1) / lanes;
+    const int groups = (num_ranks + kRanksPerGroup - 1) / kRanksPerGroup;
+    const int64_t num_tiles = num_tokens * tpr;
+    const int64_t blocks = ranked_fp8_blocks(num_tokens, hidden, num_ranks);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int El = num_experts / num_ranks;
+    const uint4* xx = static_cast<const uint4*>(x);
+#define EP_RF8(F, M, NL)                                                                        \
+    hipLaunchKernelGGL((dispatch_ranked_fp8_tile_kernel<F, M, NL>), dim3((unsigned)blocks),       \
+                       dim3(NL), 0, stream, xx, nvec, topk_idx, topk_weights, num_topk,            \
+                       num_experts, El, num_ranks, s2d, dest_rows, dest_q, dest_scales, dest_w,    \
+                       with_weights, tpr, num_tiles, groups)
+#define EP_RF8_MODE(F, M)                                                                       \
+    if (lanes == kTileLanes) EP_RF8(F, M, kTileLanes); else EP_RF8(F, M, kTileLanes / 2)
+    if (format == kE5M2) {
+        if (scale_mode == kScalePow2) EP_RF8_MODE(kE5M2, kScalePow2);
+        else if (scale_mode == kScaleUe8m0) EP_RF8_MODE(kE5M2, kScaleUe8m0);
+        else EP_RF8_MODE(kE5M2, kScaleFp32);
+    } else {
+        if (scale_mode == kScalePow2) EP_RF8_MODE(kE4M3, kScalePow2);
+        else if (scale_mode == kScaleUe8m0) EP_RF8_MODE(kE4M3, kScaleUe8m0);
+        else EP_RF8_MODE(kE4M3, kScaleFp32);
+    }
+#undef EP_RF8_MODE
+#undef EP_RF8
     return hipGetLastError();
 }
 

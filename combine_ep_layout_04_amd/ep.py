@@ -49,7 +49,7 @@ SYMBOLS = ("ep_version", "ep_status_string", "ep_last_error", "ep_layout_workspa
            "ep_dispatch_prequantized", "ep_combine",
            "ep_combine_backward", "ep_dispatch_backward", "ep_routing_map",
            "ep_rank_layout_workspace_size", "ep_rank_layout", "ep_dispatch_ranked",
-           "ep_dispatch_ranked_prequantized", "ep_dispatch_fused_permute",
+           "ep_dispatch_ranked_prequantized", "ep_dispatch_ranked_fp8", "ep_dispatch_fused_permute",
            "ep_dispatch_fused_permute_prequantized", "ep_combine_ranked",
            "ep_dispatch_ranked_backward", "ep_dispatch_colmajor_workspace_size",
            "ep_dispatch_colmajor_scales", "ep_dispatch_prequantized_colmajor")
@@ -120,6 +120,9 @@ def lib() -> ctypes.CDLL:
         L.ep_dispatch_ranked_prequantized.argtypes = [P, P, P, P, i64, i32, i32, i32, i32, P, P, P,
                                                       P, i64, P]
         L.ep_dispatch_ranked_prequantized.restype = i32
+        L.ep_dispatch_ranked_fp8.argtypes = [P, P, P, i64, i32, i32, i32, i32, P, i32, i32, P, P,
+                                             P, i64, P]
+        L.ep_dispatch_ranked_fp8.restype = i32
         L.ep_dispatch_fused_permute.argtypes = [P, P, P, i64, i32, i32, i32, i32, i32, P, P, P, P,
                                                 i64, P, P, P]
         L.ep_dispatch_fused_permute.restype = i32
@@ -756,6 +759,58 @@ def ep_dispatch_ranked_prequantized(x_q: torch.Tensor, x_scales: torch.Tensor,
                                                _stream(stream))
     _check(st, "ep_dispatch_ranked_prequantized")
     return dest_q, dest_scales, dest_weights
+
+
+def ep_dispatch_ranked_fp8(x: torch.Tensor, sparse_to_dense: torch.Tensor, dest_q, dest_scales,
+                           num_experts: int, *, fmt: str = "e4m3", scale: str = "fp32",
+                           topk_idx: Optional[torch.Tensor] = None,
+                           topk_weights: Optional[torch.Tensor] = None, dest_weights=None,
+                           stream=None):
+    """Once-per-rank dispatch with the 8-bit cast on the way: ``x`` bf16
+    [T, H] (H a multiple of 128) is cast as ep_dispatch casts it (``fmt``
+    "e4m3" / "e5m2", ``scale`` "fp32" / "pow2" / "ue8m0") and each token's
+    codes and scales go to the G ranks' ``dest_q`` (uint8 [rows_d, H]) and
+    ``dest_scales`` ([rows_d, H/128], fp32, or uint8 for "ue8m0"); weights as
+    ep_dispatch_ranked.  Rows at or past the smallest rows_d are not
+    written."""
+    _need(x, "x", torch.bfloat16)
+    _need(sparse_to_dense, "sparse_to_dense", torch.int32)
+    if x.dim() != 2 or sparse_to_dense.dim() != 2 or sparse_to_dense.shape[0] != x.shape[0]:
+        raise ValueError("x must be [T, H] and sparse_to_dense [T, G]")
+    T, H = x.shape
+    nb = H // 128
+    G = sparse_to_dense.shape[1]
+    sdt = torch.uint8 if scale == "ue8m0" else torch.float32
+    if len(dest_q) != G or len(dest_scales) != G:
+        raise ValueError("one code and one scale buffer per rank")
+    for d in range(G):
+        _need(dest_q[d], f"dest_q[{d}]", torch.uint8)
+        if dest_q[d].dim() != 2 or dest_q[d].shape[1] != H:
+            raise ValueError(f"dest_q[{d}] must be [rows, {H}]")
+    rows = min(int(t.shape[0]) for t in dest_q)
+    for d in range(G):
+        _need(dest_scales[d], f"dest_scales[{d}]", sdt, rows * nb)
+    k = 1
+    if topk_idx is not None:
+        _need(topk_idx, "topk_idx", torch.int64)
+        k = topk_idx.shape[1]
+    if topk_weights is not None:
+        _need(topk_weights, "topk_weights", torch.float32, T * k)
+    wtab = None
+    if dest_weights is not None:
+        if topk_idx is None or len(dest_weights) != G:
+            raise ValueError("dest_weights needs topk_idx and one buffer (or None) per rank")
+        for d, t in enumerate(dest_weights):
+            if t is not None:
+                _need(t, f"dest_weights[{d}]", torch.float32, rows * k)
+        wtab = _ptr_table(dest_weights)
+    qtab = _ptr_table(dest_q)
+    stab = _ptr_table(dest_scales)
+    st = lib().ep_dispatch_ranked_fp8(_ptr(x), _ptr(topk_idx), _ptr(topk_weights), T, H, k,
+                                      int(num_experts), G, _ptr(sparse_to_dense), _FORMATS[fmt],
+                                      _SCALES[scale], qtab[1], stab[1],
+                                      None if wtab is None else wtab[1], rows, _stream(stream))
+    _check(st, "ep_dispatch_ranked_fp8")
 
 
 def _fused_permute_tables(G, T, k, R, src_topk_idx, src_topk_weights, recv_weights):

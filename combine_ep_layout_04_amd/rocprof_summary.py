@@ -198,6 +198,7 @@ KERNEL_KEYS = {
     # scales (448 vectors: 64 lanes) through the per-token one
     "dispatch_ranked": r"dispatch_ranked_tile_kernel",
     "dispatch_ranked_prequantized": r"dispatch_ranked_kernel<64, 7, 4>",
+    "dispatch_ranked_fp8": r"dispatch_ranked_fp8_tile_kernel<0, 0, 64>",
     "combine_ranked": r"combine_ranked_tile_kernel<128>",
     # the combine over ranks of the row gradients (the same kernel and bytes
     # as combine_ranked) and the weight-gradient gather

@@ -557,6 +557,42 @@ ep_status_t ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scal
                                             int64_t dest_rows, void *stream);
 
 /*
+ * ep_dispatch_ranked_fp8 -- ep_dispatch_ranked with the 8-bit cast of
+ * ep_dispatch_ex done on the way: each token is cast once (per 128-channel
+ * block: amax, scale, codes) and its code row and scale row go to every
+ * destination rank that receives it.  The same bytes as ep_dispatch_ex of
+ * the token followed by ep_dispatch_ranked_prequantized, without the
+ * intermediate buffers.
+ *
+ * Passages: NCCL EP page, ncclEpDispatch (fp8 output with hidden/128 fp32
+ * scales per token, scale block 128) and its high-throughput branch (a token
+ * travels once per rank); DeepEP page, low_latency_dispatch() (the cast
+ * inside the dispatch; round_scale, use_ue8m0).
+ *
+ * In:  x bf16 [num_tokens, hidden] (16-byte aligned); topk_idx,
+ *      topk_weights, sparse_to_dense_map as ep_dispatch_ranked.
+ *      out_dtype   EP_OUT_FP8_E4M3 or EP_OUT_FP8_E5M2.
+ *      scale_format  as ep_dispatch_ex.
+ * Out: dest_q      HOST array of G device pointers: codes [dest_rows, hidden]
+ *                  (16-byte aligned).
+ *      dest_scales HOST array of G device pointers: [dest_rows, hidden/128],
+ *                  fp32 (4-byte aligned) or, for EP_SCALE_UE8M0, bytes.
+ *      dest_weights as ep_dispatch_ranked (may be NULL).
+ *      Row sparse_to_dense_map[t, d] (when >= 0 and < dest_rows) of rank d's
+ *      buffers gets token t's codes and scales, exactly as ep_dispatch_ex
+ *      casts them.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN;
+ * EP_UNSUPPORTED when the launch would need 2^31 workgroups or more (one per
+ * token, tile of 64 or 128 units of 16 channels, and group of 8 ranks).
+ */
+ep_status_t ep_dispatch_ranked_fp8(const void *x, const int64_t *topk_idx, const float *topk_weights,
+                                   int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                   int num_ranks, const int32_t *sparse_to_dense_map,
+                                   int out_dtype, int scale_format, void *const *dest_q,
+                                   void *const *dest_scales, float *const *dest_weights,
+                                   int64_t dest_rows, void *stream);
+
+/*
  * ep_dispatch_fused_permute -- the receiving rank's dispatch with the
  * permute fused in: every token it receives is read once from the sending
  * rank's rows and written to each of its local-expert rows, so the rows come

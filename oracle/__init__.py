@@ -602,3 +602,27 @@ def dispatch_ranked_prequant(xq: np.ndarray, xs: np.ndarray, topk_idx: np.ndarra
                                           G, _ptr(s2d), _ptr_array(dq), _ptr_array(ds),
                                           None if dw is None else _ptr_array(dw))
     return dq, ds, dw
+
+
+def dispatch_ranked_quant(x_bits: np.ndarray, topk_idx: np.ndarray,
+                          topk_weights: Optional[np.ndarray], E: int, G: int,
+                          sparse_to_dense: np.ndarray, rows, fmt: str = "e4m3",
+                          scale: str = "fp32", with_weights: bool = True):
+    """The 8-bit cast sent once per rank (NCCL EP page, ncclEpDispatch: fp8
+    output with per-128-channel scales, and its high-throughput branch, one
+    copy per rank), by its definition: each token cast once as
+    oracle_dispatch_quant casts it, then its code and scale rows sent by
+    oracle_dispatch_ranked_prequant.  UE8M0 scale bytes travel through that
+    copy as the fp32 values 0..255, which it moves unchanged.  Returns
+    (dest_q list of G uint8 [rows_d, H], dest_s list of G [rows_d, H/128]
+    float32 or uint8, dest_w list of G float32 [rows_d, k] or None)."""
+    x = _c(x_bits, np.uint16)
+    T = x.shape[0]
+    q_tok, s_tok, _ = dispatch_quant(x, np.arange(T, dtype=np.int32)[:, None], fmt=fmt,
+                                     scale=scale)
+    dq, ds, dw = dispatch_ranked_prequant(q_tok, s_tok.astype(np.float32), topk_idx,
+                                          topk_weights, E, G, sparse_to_dense, rows,
+                                          with_weights)
+    if scale == "ue8m0":
+        ds = [v.astype(np.uint8) for v in ds]
+    return dq, ds, dw

@@ -480,6 +480,38 @@ def test_dispatch_ranked_prequantized_rejects(over, code):
 
 
 @no_gpu
+@pytest.mark.parametrize("over,code", [
+    (dict(fmt=0), 1), (dict(fmt=3), 1), (dict(sc=3), 1), (dict(H=200), 1), (dict(k=0), 1),
+    (dict(G=65, E=130), 1), (dict(E=9), 1), (dict(rows=-1), 1), (dict(dq="none"), 1),
+    (dict(ds="none"), 1), (dict(dq=(FAKE, FAKE + 8)), 1), (dict(ds=(FAKE, FAKE + 2)), 1),
+    (dict(ds=(FAKE, None)), 1), (dict(dw=(FAKE, FAKE + 2)), 1), (dict(x=None), 1),
+    (dict(s2d=None), 1), (dict(x=FAKE + 8), 1), (dict(dw=(FAKE, FAKE), idx=None), 1),
+    (dict(T=1 << 28, k=8), 2),
+    # 2^28 tokens of 7168 channels to 16 ranks: 7 tiles x 2 rank groups each
+    (dict(T=1 << 28, k=1, H=7168, G=16, E=16, dq=(FAKE,) * 16, ds=(FAKE,) * 16), 2),
+])
+def test_dispatch_ranked_fp8_rejects(over, code):
+    a = dict(x=FAKE, idx=FAKE, w=None, T=4, H=256, k=2, E=8, G=2, s2d=FAKE, fmt=1, sc=0,
+             dq=(FAKE, FAKE), ds=(FAKE, FAKE), dw=None, rows=16)
+    a.update(over)
+    tabs = {n: (None if a[n] in (None, "none") else _table(*a[n])) for n in ("dq", "ds", "dw")}
+    st = ep.lib().ep_dispatch_ranked_fp8(
+        a["x"], a["idx"], a["w"], a["T"], a["H"], a["k"], a["E"], a["G"], a["s2d"], a["fmt"],
+        a["sc"], *[None if tabs[n] is None else ctypes.addressof(tabs[n]) for n in ("dq", "ds", "dw")],
+        a["rows"], None)
+    assert st == code, ep.last_error()
+    assert ep.last_error()
+
+
+def test_dispatch_ranked_fp8_zero_tokens_is_a_noop():
+    dq = _table(FAKE, FAKE)
+    assert ep.lib().ep_dispatch_ranked_fp8(None, None, None, 0, 256, 2, 8, 2, None, 1, 2,
+                                           ctypes.addressof(dq), ctypes.addressof(dq), None, 0,
+                                           None) == 0
+    assert ep.last_error() == ""
+
+
+@no_gpu
 def test_colmajor_workspace_size():
     lib = ep.lib()
     assert lib.ep_dispatch_colmajor_workspace_size(8192, 7168, 0) == 8192 * 56 * 4

@@ -199,7 +199,8 @@ def test_variants_and_backward_graph():
     # every other entry point in one captured step: aligned and fixed-stride
     # layouts, the 8-bit cast variants (row- and column-major scales), the
     # pre-quantized copy, both backward passes, the routing map, the rank
-    # layout, the pre-quantized once-per-rank copy and the fused permute.
+    # layout, the pre-quantized and the casting once-per-rank copies, and the
+    # fused permutes (bf16 and 8-bit rows).
     # All outputs start as the 0x55 sentinel, so rows a call does not write
     # keep it in the eager run and in every replay alike.
     T, H, E, k, G = 1024, 2560, 64, 8, 4
@@ -264,8 +265,12 @@ def test_variants_and_backward_graph():
     dq = [torch.empty((RG, H), **u8) for _ in range(G)]
     ds = [torch.empty((RG, nb), **f32) for _ in range(G)]
     dw = [torch.empty((RG, k), **f32) for _ in range(G)]
+    fq = [torch.empty((RG, H), **u8) for _ in range(G)]
+    fs = [torch.empty((RG, nb), **u8) for _ in range(G)]
+    fw = [torch.empty((RG, k), **f32) for _ in range(G)]
     for d in range(G):
         o[f"dq{d}"], o[f"ds{d}"], o[f"dw{d}"] = dq[d], ds[d], dw[d]
+        o[f"fq{d}"], o[f"fs{d}"], o[f"fw{d}"] = fq[d], fs[d], fw[d]
     ws = torch.empty(max(ep.layout_workspace_size(T, k, E), 256), **u8)
     cmws = torch.empty(max(ep.ep_dispatch_colmajor_workspace_size(T, H, "fp32"), 256), **u8)
     pws = torch.empty(max(ep.layout_workspace_size(RG, k, El), 256), **u8)
@@ -301,6 +306,8 @@ def test_variants_and_backward_graph():
         ep.ep_rank_layout(o["gmap"], T, E, G, 0, k, out=lay, workspace=rws)
         ep.ep_dispatch_ranked_prequantized(xq, xs, o["s2d"], dq, ds, E, topk_idx=idx, topk_weights=w,
                                            dest_weights=dw)
+        ep.ep_dispatch_ranked_fp8(x, o["s2d"], fq, fs, E, fmt="e5m2", scale="ue8m0", topk_idx=idx,
+                                  topk_weights=w, dest_weights=fw)
         ep.ep_layout(o["rti"], El, counts=o["p_counts"], offsets=o["p_offsets"], slot=o["p_slot"],
                      want_src=False, want_invalid=False, workspace=pws)
         ep.ep_dispatch_fused_permute(x_all, o["rsrc"], o["rti"], o["p_slot"], E, 0, rows=RG * k,

@@ -409,6 +409,52 @@ def test_dispatch_ranked_prequant(seed, G, E, k):
         np.testing.assert_array_equal(dw[d], dw_ref[d])
 
 
+@pytest.mark.parametrize("seed,G,E,k,fmt,scale", [
+    (0, 2, 8, 3, "e4m3", "fp32"), (1, 4, 16, 5, "e5m2", "pow2"), (2, 8, 64, 8, "e4m3", "ue8m0"),
+    (3, 3, 9, 9, "e5m2", "fp32"),
+])
+def test_dispatch_ranked_quant_pins(seed, G, E, k, fmt, scale):
+    # the row a rank receives for token t is the expanded 8-bit dispatch's
+    # row for any of t's slots whose expert that rank owns (same codes, same
+    # scales: the cast depends on the token alone), rows no token maps to
+    # stay zero, and the weight rows are the bf16 once-per-rank dispatch's
+    T, H = 33, 384
+    El = E // G
+    inp = make_random_case(seed + 40, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    inp.x_bits[1, :128] = 0          # a zero block: scale 0, codes 0
+    maps = [oracle.routing_map(make_random_case(seed + 50 + s, T, 8, E, k).topk_idx, E)[0]
+            for s in range(G)]
+    maps[0] = oracle.routing_map(inp.topk_idx, E)[0]
+    L = oracle.rank_layout(np.concatenate(maps), T, E, G, 0, k)
+    rows = T + 2
+    dq, ds, dw = oracle.dispatch_ranked_quant(inp.x_bits, inp.topk_idx, inp.topk_weights, E, G,
+                                              L.sparse_to_dense, rows, fmt=fmt, scale=scale)
+    La = oracle.layout(inp.topk_idx, E)
+    eq, es, _ = oracle.dispatch_quant(inp.x_bits, La.slot, fmt=fmt, scale=scale,
+                                      rows=max(La.n, 1))
+    _, dw_ref = oracle.dispatch_ranked(inp.x_bits, inp.topk_idx, inp.topk_weights, E, G,
+                                       L.sparse_to_dense, rows)
+    want_dt = np.uint8 if scale == "ue8m0" else np.float32
+    received = 0
+    for d in range(G):
+        assert ds[d].dtype == want_dt
+        p = L.sparse_to_dense[:, d]
+        hit = np.zeros(rows, bool)
+        for t in range(T):
+            if p[t] < 0:
+                continue
+            js = [j for j in range(k) if d * El <= inp.topk_idx[t, j] < (d + 1) * El]
+            assert js, "the rank layout sends only tokens with a slot on the rank"
+            r = La.slot[t, js[0]]
+            np.testing.assert_array_equal(dq[d][p[t]], eq[r])
+            np.testing.assert_array_equal(ds[d][p[t]].view(np.uint8), es[r].view(np.uint8))
+            hit[p[t]] = True
+            received += 1
+        assert not dq[d][~hit].any() and not ds[d][~hit].any()
+        np.testing.assert_array_equal(dw[d], dw_ref[d])
+    assert received > T
+
+
 # ---- backward of the once-per-rank dispatch (weight gradients back to [T, k])
 
 def ranked_world(seed, G, T, E, k, dup=0.0, mask=0.2, invalid=0.0):

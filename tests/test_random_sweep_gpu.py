@@ -8,7 +8,7 @@ dedicated tests:
 
 * layout, dispatch copies, 8-bit codes and scales (row-major, and
   column-major through the two-pass cast), the rank layout, the per-rank
-  copies and the fused permute (bf16 rows, and 8-bit code rows with their
+  copies (bf16, and with the 8-bit cast) and the fused permute (bf16 rows, and 8-bit code rows with their
   scale rows) bounded by the device-side received count:
   bit-exact, with sentinel-filled outputs;
 * combine, combine backward, dispatch backward and the combine over ranks:
@@ -226,6 +226,31 @@ def test_random_case(seed):
         pr = pr[pr >= 0]
         np.testing.assert_array_equal(bf16_bits(dx[d])[pr], ox[d][pr])
         np.testing.assert_array_equal(host(dwt[d])[pr].view(np.uint32), ow[d][pr].view(np.uint32))
+    if c["fp8"]:
+        # the same sends with the case's 8-bit cast on the way
+        nb = H // 128
+        sdt = torch.uint8 if c["scale"] == "ue8m0" else torch.float32
+        fq = [torch.full((rows_r, H), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+        fs = [torch.zeros((rows_r, nb), dtype=sdt, device=DEV) for _ in range(G)]
+        fw = [torch.full((rows_r, k), float("nan"), dtype=torch.float32, device=DEV)
+              for _ in range(G)]
+        ep.ep_dispatch_ranked_fp8(x_dev(inp.x_bits), lay.sparse_to_dense, fq, fs, E, fmt=c["fmt"],
+                                  scale=c["scale"], topk_idx=dev(inp.topk_idx),
+                                  topk_weights=dev(inp.topk_weights), dest_weights=fw)
+        torch.cuda.synchronize()
+        oq8, os8, ow8 = oracle.dispatch_ranked_quant(inp.x_bits, inp.topk_idx, inp.topk_weights, E,
+                                                     G, RL.sparse_to_dense, rows_r, fmt=c["fmt"],
+                                                     scale=c["scale"])
+        for d in range(G):
+            pr = RL.sparse_to_dense[:, d]
+            pr = pr[pr >= 0]
+            np.testing.assert_array_equal(host(fq[d])[pr], oq8[d][pr])
+            np.testing.assert_array_equal(host(fs[d])[pr].view(np.uint8), os8[d][pr].view(np.uint8))
+            np.testing.assert_array_equal(host(fw[d])[pr].view(np.uint32),
+                                          ow8[d][pr].view(np.uint32))
+            rest = np.ones(rows_r, bool)
+            rest[pr] = False
+            assert np.all(host(fq[d])[rest] == 0xEE)
     ys = [make_gradient(rows_r, H, 9000 + seed * 10 + d) for d in range(G)]
     o = ep.ep_combine_ranked([x_dev(v) for v in ys], lay.sparse_to_dense)
     torch.cuda.synchronize()

@@ -509,6 +509,92 @@ def test_dispatch_ranked_prequantized_headline():
     check_ranked_prequant(xq, xs, inp.topk_idx, inp.topk_weights, w.E, G, L.sparse_to_dense, w.T)
 
 
+def check_ranked_fp8(x_bits, idx, w, E, G, s2d, rows, fmt, scale, with_weights=True):
+    T, H = x_bits.shape
+    k = idx.shape[1]
+    nb = H // 128
+    ue8m0 = scale == "ue8m0"
+    dq = [torch.full((rows, H), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+    if ue8m0:
+        ds = [torch.full((rows, nb), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+    else:
+        ds = [torch.full((rows, nb), 0x7FBADBAD, dtype=torch.int32, device=DEV).view(torch.float32)
+              for _ in range(G)]
+    dw = ([torch.full((rows, k), float("nan"), dtype=torch.float32, device=DEV) for _ in range(G)]
+          if with_weights else None)
+    ep.ep_dispatch_ranked_fp8(x_dev(x_bits), dev(s2d), dq, ds, E, fmt=fmt, scale=scale,
+                              topk_idx=dev(idx), topk_weights=None if w is None else dev(w),
+                              dest_weights=dw)
+    torch.cuda.synchronize()
+    oq, os_, ow = oracle.dispatch_ranked_quant(x_bits, idx, w, E, G,
+                                               np.where(s2d < rows, s2d, -1), rows, fmt=fmt,
+                                               scale=scale, with_weights=with_weights)
+    sent = 0
+    for d in range(G):
+        written = np.zeros(rows, bool)
+        p = s2d[:, d]
+        written[p[(p >= 0) & (p < rows)]] = True
+        sent += int(written.sum())
+        gq, gs = host(dq[d]), host(ds[d]).view(np.uint8)
+        np.testing.assert_array_equal(gq[written], oq[d][written])
+        np.testing.assert_array_equal(gs[written], os_[d][written].view(np.uint8))
+        assert np.all(gq[~written] == 0xEE), "a code row past the sent rows was written"
+        if ue8m0:
+            assert np.all(gs[~written] == 0xEE)
+        else:
+            assert np.all(gs[~written].view(np.uint32) == 0x7FBADBAD)
+        if with_weights:
+            gw = host(dw[d])
+            np.testing.assert_array_equal(gw[written].view(np.uint32),
+                                          ow[d][written].view(np.uint32))
+            assert np.all(np.isnan(gw[~written]))
+    return sent
+
+
+@pytest.mark.parametrize("G,T,H,E,k,fmt,scale", [
+    (1, 3, 128, 2, 1, "e4m3", "fp32"),        # 8 units: one 64-lane tile
+    (2, 37, 256, 8, 3, "e5m2", "pow2"),
+    (4, 200, 2048, 16, 5, "e4m3", "ue8m0"),   # 128 units: one 128-lane tile
+    (3, 90, 2176, 9, 9, "e5m2", "ue8m0"),     # 136 units: 64-lane tiles, k = 9
+    (8, 130, 7168, 64, 8, "e4m3", "fp32"),    # 448 units: 7 tiles of 64
+    (10, 40, 4224, 40, 8, "e4m3", "pow2"),    # 264 units, two groups of ranks (8 + 2)
+    (64, 10, 1024, 64, 64, "e4m3", "fp32"),   # G = EP_MAX_RANKS, k = EP_MAX_TOPK
+])
+def test_dispatch_ranked_fp8(G, T, H, E, k, fmt, scale):
+    inp = make_random_case(G * 5 + H, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
+    x = inp.x_bits.copy()
+    x[0, :128] = 0                                      # a zero block
+    if T > 2:
+        x[2, 128:256] = (x[2, 128:256].astype(np.uint32) + 0x0C00).astype(np.uint16)  # x 2^24
+    others = rank_cases(G + 11, G, T, 8, E, k, mask_frac=0.2)
+    maps = [oracle.routing_map(c.topk_idx, E)[0] for c in others]
+    rank = G // 2
+    maps[rank] = oracle.routing_map(inp.topk_idx, E)[0]
+    L = oracle.rank_layout(np.concatenate(maps), T, E, G, rank, k)
+    print(f"\n[ranked] 8-bit cast sent once per rank G={G} T={T} H={H} E={E} k={k} "
+          f"{fmt}/{scale}", flush=True)
+    assert check_ranked_fp8(x, inp.topk_idx, inp.topk_weights, E, G, L.sparse_to_dense, G * T,
+                            fmt, scale) > 0
+    # rows past a short destination buffer are not written; no weights
+    check_ranked_fp8(x, inp.topk_idx, None, E, G, L.sparse_to_dense, max(1, T // 2), fmt, scale,
+                     with_weights=False)
+
+
+def test_dispatch_ranked_fp8_headline():
+    # the 8-bit workload (T=8192, H=7168, E=256, k=8, 1% of rows x100) sent
+    # to 8 ranks
+    w = WORKLOADS["fp8"]
+    G = 8
+    inp = make_inputs(w)
+    idx = headline_global_map(G)
+    idx[0] = inp.topk_idx
+    gmap = np.concatenate([oracle.routing_map(i, w.E)[0] for i in idx])
+    L = oracle.rank_layout(gmap, w.T, w.E, G, 0, w.k)
+    print("\n[ranked] 8-bit cast sent once per rank, fp8 workload, G=8", flush=True)
+    assert check_ranked_fp8(inp.x_bits, inp.topk_idx, inp.topk_weights, w.E, G,
+                            L.sparse_to_dense, w.T, "e4m3", "fp32") > w.T
+
+
 def code_rows(seed, G, T, H):
     """G ranks' code rows and scale rows; the scales hold a few special
     values (infinities, a NaN payload, -0, a subnormal) that a bit copy keeps."""
