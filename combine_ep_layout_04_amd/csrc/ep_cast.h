@@ -3,8 +3,9 @@
 // by the expanded dispatch and the once-per-rank dispatch.
 //
 // Passages: NCCL EP page, ncclEpDispatch (fp8 output with hidden/128 fp32
-// scales per token, scale block 128); DeepEP page, dispatch() and
-// low_latency_dispatch() (round_scale, use_ue8m0).
+// scales per token, scale block 128; the low-latency branch casts inside
+// the dispatch, with round_scale and use_ue8m0); DeepEP page, ElasticBuffer
+// (use_fp8_dispatch).
 //
 // Each lane casts one "unit" of 16 channels (two 16-byte loads in, one
 // 16-byte store out), so 8 aligned lanes hold a block and its amax is an

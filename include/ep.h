@@ -564,10 +564,11 @@ ep_status_t ep_dispatch_ranked_prequantized(const void *x_q, const float *x_scal
  * the token followed by ep_dispatch_ranked_prequantized, without the
  * intermediate buffers.
  *
- * Passages: NCCL EP page, ncclEpDispatch (fp8 output with hidden/128 fp32
- * scales per token, scale block 128) and its high-throughput branch (a token
- * travels once per rank); DeepEP page, low_latency_dispatch() (the cast
- * inside the dispatch; round_scale, use_ue8m0).
+ * Passages: NCCL EP page, ncclEpDispatch: its low-latency branch casts
+ * inside the dispatch (fp8 output with hidden/128 fp32 scales per token,
+ * scale block 128; round_scale, use_ue8m0) and its high-throughput branch
+ * sends a token once per rank; DeepEP page, ElasticBuffer
+ * (use_fp8_dispatch).
  *
  * In:  x bf16 [num_tokens, hidden] (16-byte aligned); topk_idx,
  *      topk_weights, sparse_to_dense_map as ep_dispatch_ranked.
@@ -646,9 +647,10 @@ ep_status_t ep_dispatch_fused_permute(const void *const *src_x, const int64_t *c
  * (hidden bytes) and its scale row (hidden/128 fp32) are read once and
  * written, bit for bit, to each of the token's local-expert rows.
  *
- * Passages: NeMo fused_a2a page, HybridEPDispatch (fp8_dispatch together
- * with fuse_permute); NCCL EP page, ncclEpDispatch high-throughput branch
- * (FP8 tokens travel with a 2-D fp32 scales tensor).
+ * Passages: NeMo fused_a2a page, init_hybrid_ep_buffer (fp8_dispatch: FP8
+ * communication in the dispatch phase) and HybridEPDispatch (fuse_permute);
+ * NCCL EP page, ncclEpDispatch high-throughput branch (FP8 tokens travel
+ * with a 2-D fp32 scales tensor).
  *
  * In:  src_q       HOST array of G device pointers: rank s's code rows,
  *                  bytes [tokens_per_rank, hidden] (16-byte aligned).

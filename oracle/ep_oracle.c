@@ -880,9 +880,10 @@ void oracle_dispatch_fused_permute(const uint16_t *const *src_x, const int64_t *
 
 /*
  * The same receive-side dispatch for tokens already cast to 8 bits (NeMo
- * fused_a2a page: fp8_dispatch, FP8 communication in the dispatch phase,
- * with fuse_permute; NCCL EP page, ncclEpDispatch high-throughput branch:
- * FP8 tokens come with a 2-D fp32 scales tensor).  Each received token's
+ * fused_a2a page: init_hybrid_ep_buffer's fp8_dispatch, FP8 communication
+ * in the dispatch phase, and HybridEPDispatch's fuse_permute; NCCL EP page,
+ * ncclEpDispatch high-throughput branch: FP8 tokens come with a 2-D fp32
+ * scales tensor).  Each received token's
  * code row (H bytes) and scale row (H/128 fp32) are copied from the sending
  * rank to each of this rank's local-expert rows:
  *   recv_q[slot[i, j]] = src_q[s][t],  recv_s[slot[i, j]] = src_s[s][t]
