@@ -770,8 +770,9 @@ def test_ranked_calls_with_no_tokens():
 
 
 def test_ranked_path_at_max_hidden():
-    # hidden = EP_MAX_HIDDEN through the once-per-rank dispatch (bf16 and
-    # 8-bit), the fused permute and the combine over ranks
+    # hidden = EP_MAX_HIDDEN through the once-per-rank dispatch (bf16,
+    # pre-quantized and cast on the way), both fused permutes and the
+    # combine over ranks
     G, T, H, E, k = 2, 6, 65536, 4, 2
     cases = rank_cases(61, G, T, H, E, k, mask_frac=0.1)
     xs = [c.x_bits for c in cases]
@@ -788,6 +789,13 @@ def test_ranked_path_at_max_hidden():
     check_fused_permute(xs, idx, ws, E, G, 1)
     ys = [make_gradient(G * T, H, 70 + d) for d in range(G)]
     check_combine(ys, L.sparse_to_dense)
+    # the 8-bit forms: the cast sent once per rank (4096 units, 32 tiles of
+    # 128), and the 8-bit fused permute (512 scales per row, four passes of
+    # the scale loop)
+    for fmt, scale in (("e4m3", "fp32"), ("e5m2", "ue8m0")):
+        check_ranked_fp8(xs[0], idx[0], ws[0], E, G, L.sparse_to_dense, G * T, fmt, scale)
+    qs, ss = code_rows(63, G, T, H)
+    check_fused_permute_prequant(qs, ss, idx, ws, E, G, 1)
 
 
 # ---- backward of the once-per-rank dispatch

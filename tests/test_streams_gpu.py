@@ -1,6 +1,7 @@
-"""Concurrent calls: the library keeps no state between calls (the layout
-arrays and the caller's workspace are the only memory it touches), so
-independent pipelines on different streams can overlap.
+"""Concurrent calls: apart from the no-allocation layout's scratch, which
+these pipelines do not use, the library keeps no state between calls (the
+layout arrays and the caller's workspace are the only memory it touches),
+so independent pipelines on different streams can overlap.
 
 Two forward steps (layout -> bf16 and 8-bit dispatch, the 8-bit cast with
 column-major scales through each pipeline's own workspace -> combine) with
