@@ -19,7 +19,7 @@ import torch
 import oracle
 from combine_ep_layout_04_amd import ep
 from combine_ep_layout_04_amd.inputs import (
-    WORKLOADS, float32_from_bf16_bits, make_gradient, make_inputs, make_random_case,
+    WORKLOADS, bf16_bits_from_float32, float32_from_bf16_bits, make_gradient, make_inputs, make_random_case,
 )
 
 from gpu_util import DEV, bf16_bits, bf16_ulp, dev, host, x_dev
@@ -344,6 +344,62 @@ def test_ranked_round_trip_pipeline():
         # the rounding of the final sum
         tol = combine_tol(o_partial, OL[s].sparse_to_dense, ref) * 3
         assert np.all(np.abs(got - want) <= tol)
+
+
+def test_fused_permute_round_trip():
+    """The per-rank path with the permute fused in, G = 4 ranks on one
+    device: every receiver's fused permute from all senders -> an expert
+    stand-in built on the host (each expert row times its weight, rounded
+    to bf16) -> the unweighted combine over the receiver's layout -> the
+    combine over ranks at every sender.  Each stage against the oracle run
+    through the same steps on the same bytes."""
+    G, T, H, E, k = 4, 300, 256, 32, 4
+    El = E // G
+    cases = rank_cases(19, G, T, H, E, k, mask_frac=0.1, dup_frac=0.3)
+    xs = [make_gradient(T, H, 80 + s) for s in range(G)]
+    idx = [c.topk_idx for c in cases]
+    ws = [c.topk_weights for c in cases]
+    print("\n[ranked] fused permute round trip G=4", flush=True)
+    gmap = np.concatenate([oracle.routing_map(i, E)[0] for i in idx])
+    OL = [oracle.rank_layout(gmap, T, E, G, d, k) for d in range(G)]
+    parts, parts_ref, ys = [], [], []
+    for d in range(G):
+        Ld = oracle.layout(OL[d].recv_topk_idx, El)
+        rows = max(Ld.n, 1)
+        px, pw = ep.ep_dispatch_fused_permute(
+            [x_dev(x) for x in xs], dev(OL[d].recv_src), dev(OL[d].recv_topk_idx), dev(Ld.slot), E,
+            d, rows=rows, src_topk_idx=[dev(i) for i in idx], src_topk_weights=[dev(w) for w in ws],
+            want_weights=True)
+        torch.cuda.synchronize()
+        ox, ow = oracle.dispatch_fused_permute(xs, idx, ws, E, d, OL[d].recv_src,
+                                               OL[d].recv_topk_idx, Ld.slot, rows)
+        n = Ld.n
+        np.testing.assert_array_equal(bf16_bits(px)[:n], ox[:n])
+        np.testing.assert_array_equal(host(pw)[:n].view(np.uint32), ow[:n].view(np.uint32))
+        y = bf16_bits_from_float32(float32_from_bf16_bits(ox) * ow[:, None])
+        ys.append(y)
+        parts.append(ep.ep_combine(x_dev(y), dev(Ld.slot), None, rows=rows))
+        parts_ref.append(oracle.combine(y, Ld.slot, None))
+    torch.cuda.synchronize()
+    for d in range(G):
+        Ld = oracle.layout(OL[d].recv_topk_idx, El)
+        got = float32_from_bf16_bits(bf16_bits(parts[d])).astype(np.float64)
+        want = float32_from_bf16_bits(parts_ref[d]).astype(np.float64)
+        mag = np.zeros_like(want)
+        for j in range(k):
+            ok = Ld.slot[:, j] >= 0
+            mag[ok] += np.abs(float32_from_bf16_bits(ys[d][Ld.slot[ok, j]]).astype(np.float64))
+        assert np.all(np.abs(got - want) <= bf16_ulp(want) + k * 2.0 ** -24 * mag), f"receiver {d}"
+    for s in range(G):
+        out = ep.ep_combine_ranked(parts, dev(OL[s].sparse_to_dense))
+        torch.cuda.synchronize()
+        ref = oracle.combine_ranked(parts_ref, OL[s].sparse_to_dense)
+        got = float32_from_bf16_bits(bf16_bits(out)).astype(np.float64)
+        want = float32_from_bf16_bits(ref).astype(np.float64)
+        # the receivers' rows may differ by the tolerance above; allow that
+        # plus the rounding of the sum over ranks
+        tol = combine_tol(parts_ref, OL[s].sparse_to_dense, ref) * 3
+        assert np.all(np.abs(got - want) <= tol), f"sender {s}"
 
 
 def test_rank_layout_deterministic_and_on_a_side_stream():
