@@ -47,7 +47,8 @@
 //   fused permute: the receiving rank's dispatch with the permute folded
 //                 in: one workgroup per received token reads the sender's
 //                 row once and stores it to each of the rank's local-expert
-//                 rows, with the weights.
+//                 rows, with the weights; 8-bit code rows carry their scale
+//                 rows along.
 //   combine:      one workgroup per (token, 2 KiB tile; 1 KiB where the
 //                 last 2 KiB tile would be at most half full) gathers its vectors from the G buffers
 //                 through buffer resources (an unrouted rank gets a 0-byte
