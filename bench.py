@@ -224,6 +224,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the tiny / mid / skewed timings (profiling runs: the skewed config "
                          "shares the headline kernels)")
@@ -313,19 +315,51 @@ def main():
     n = int(offsets[E].item())
 
     # K steps, each after a cache flush; a step's time runs from its layout
-    # launch to the end of its combine (HIP events on the launch stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # launch to the end of its combine (HIP events on the launch stream, one
+    # before the layout and one after the combine: an event recorded between
+    # two launches adds a gap between them)
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         flush()
-        step(evs[i])
+        sev[i][0].record(stream)
+        step()
+        sev[i][1].record(stream)
     stream.synchronize()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms_step = (t1 - t0) * 1e3 / args.steps
-    ms_step = statistics.fmean([e[0].elapsed_time(e[3]) for e in evs])
+    ms_step = statistics.fmean([e[0].elapsed_time(e[1]) for e in sev])
+    # the same K steps again with events between the three launches, for
+    # the per-kernel times
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps with per-kernel events")
+    for i in range(args.steps):
+        flush()
+        step(evs[i])
+    stream.synchronize()
+    ms_step_staged = statistics.fmean([e[0].elapsed_time(e[3]) for e in evs])
+    # context: the same step captured once in a HIP graph and replayed after
+    # each flush
+    graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        stream.synchronize()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                flush()
+                gev[i][0].record(stream)
+                g.replay()
+                gev[i][1].record(stream)
+        stream.synchronize()
+        graph = {"ms_per_step": round(statistics.fmean([e[0].elapsed_time(e[1]) for e in gev]), 4)}
+        del g
 
     warm = None
     if args.warm:
@@ -826,6 +860,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_with_kernel_events": round(ms_step_staged, 4),
+        "graph_replay": graph,
         "wall_ms_per_step_incl_cache_flush": round(wall_ms_step, 4),
         "caches": "a 1 GiB scratch read before every timed launch and step (outside its events)",
         "higher_is_better": True,
