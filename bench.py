@@ -345,21 +345,26 @@ def main():
     # each flush
     graph = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        stream.synchronize()
-        with torch.cuda.graph(g, stream=stream):
-            step()
-        stream.synchronize()
-        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        with torch.cuda.stream(stream):
-            for i in range(args.steps):
-                flush()
-                gev[i][0].record(stream)
-                g.replay()
-                gev[i][1].record(stream)
-        stream.synchronize()
-        graph = {"ms_per_step": round(statistics.fmean([e[0].elapsed_time(e[1]) for e in gev]), 4)}
-        del g
+        try:
+            g = torch.cuda.CUDAGraph()
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                step()
+            stream.synchronize()
+            gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in range(args.steps)]
+            with torch.cuda.stream(stream):
+                for i in range(args.steps):
+                    flush()
+                    gev[i][0].record(stream)
+                    g.replay()
+                    gev[i][1].record(stream)
+            stream.synchronize()
+            graph = {"ms_per_step": round(statistics.fmean([e[0].elapsed_time(e[1]) for e in gev]), 4)}
+            del g
+        except RuntimeError as e:   # context only: the step itself is timed above
+            torch.cuda.synchronize()
+            graph = {"error": str(e)[:200]}
 
     warm = None
     if args.warm:
