@@ -669,6 +669,7 @@ static ep_status_t fused_permute_args(const void* const* src_x, const float* con
     if (rank < 0 || rank >= num_ranks)
         return fail(EP_INVALID_ARGUMENT, "rank %d outside [0, %d)", rank, num_ranks);
     if (rows < 0) return fail(EP_INVALID_ARGUMENT, "rows < 0");
+    if (tokens_per_rank == 0) return EP_SUCCESS;   // nothing is read or written
     if (!src_x) return fail(EP_INVALID_ARGUMENT, "src_x (a host array of pointers) is required");
     if (scales && !src_s)
         return fail(EP_INVALID_ARGUMENT, "src_scales (a host array of pointers) is required");

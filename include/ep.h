@@ -631,7 +631,8 @@ ep_status_t ep_dispatch_ranked_fp8(const void *x, const int64_t *topk_idx, const
  *      Rows past `rows` are never written; rows nothing maps to are not.
  *      A received row whose recv_src is not in [0, G*T), or past num_recv,
  *      is skipped.
- * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.
+ * hidden must be a positive multiple of 8, at most EP_MAX_HIDDEN.  With
+ * tokens_per_rank = 0 nothing is read or written and no pointer is checked.
  */
 ep_status_t ep_dispatch_fused_permute(const void *const *src_x, const int64_t *const *src_topk_idx,
                                       const float *const *src_topk_weights, int64_t tokens_per_rank,
@@ -662,7 +663,8 @@ ep_status_t ep_dispatch_fused_permute(const void *const *src_x, const int64_t *c
  *      gets received row i's code and scale rows;
  *      recv_weights as ep_dispatch_fused_permute.
  *      Rows past `rows` are never written; rows nothing maps to are not.
- * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.
+ * hidden must be a positive multiple of 128, at most EP_MAX_HIDDEN.  With
+ * tokens_per_rank = 0 nothing is read or written and no pointer is checked.
  */
 ep_status_t ep_dispatch_fused_permute_prequantized(
     const void *const *src_q, const float *const *src_scales, const int64_t *const *src_topk_idx,

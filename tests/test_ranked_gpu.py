@@ -817,12 +817,30 @@ def test_ranked_calls_with_no_tokens():
     dest = [torch.full((4, 256), 1.0, dtype=torch.bfloat16, device=DEV) for _ in range(G)]
     ep.ep_dispatch_ranked(x, s2d, dest, E, topk_idx=idx)
     o = ep.ep_combine_ranked(dest, s2d)
+    # the 8-bit forms: the cast sent once per rank, and both fused permutes
+    # of zero tokens per rank
+    dq = [torch.full((4, 256), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+    ds = [torch.full((4, 2), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(G)]
+    ep.ep_dispatch_ranked_fp8(x, s2d, dq, ds, E, scale="ue8m0", topk_idx=idx)
+    px = torch.full((4, 256), 1.0, dtype=torch.bfloat16, device=DEV)
+    empty_rows = [torch.empty((0, 256), dtype=torch.bfloat16, device=DEV) for _ in range(G)]
+    slot0 = torch.empty((0, k), **i32)
+    ep.ep_dispatch_fused_permute(empty_rows, out.recv_src, out.recv_topk_idx, slot0, E, 2,
+                                 rows=4, recv_x=px)
+    pq = torch.full((4, 256), 0xEE, dtype=torch.uint8, device=DEV)
+    psc = torch.full((4, 2), 5.0, dtype=torch.float32, device=DEV)
+    ep.ep_dispatch_fused_permute_prequantized(
+        [torch.empty((0, 256), dtype=torch.uint8, device=DEV) for _ in range(G)],
+        [torch.empty((0, 2), dtype=torch.float32, device=DEV) for _ in range(G)], out.recv_src,
+        out.recv_topk_idx, slot0, E, 2, rows=4, recv_q=pq, recv_scales=psc)
     torch.cuda.synchronize()
     assert int(bad.item()) == 0
     assert int(out.num_recv.item()) == 0 and int(out.num_overflow.item()) == 0
     assert torch.all(out.expert_counts == 0)
     assert o.shape == (0, 256)
     assert all(torch.all(d == 1.0) for d in dest)
+    assert all(torch.all(d == 0xEE) for d in dq + ds)
+    assert torch.all(px == 1.0) and torch.all(pq == 0xEE) and torch.all(psc == 5.0)
 
 
 def test_ranked_path_at_max_hidden():
