@@ -40,9 +40,10 @@
 //                 streaming stores, to each rank of the group that receives
 //                 the token (a table of G row pointers passed by value);
 //                 tile 0 also writes the token's weights for those ranks'
-//                 experts.  Rows under 512 vectors, and 8-bit rows with
-//                 their scales, take one workgroup per token that holds the
-//                 row in registers.  The 8-bit cast sent once per rank is
+//                 experts.  bf16 rows of 257-511 vectors whose last tile
+//                 would be at most half full take 64-lane tiles; other rows
+//                 under 512 vectors, and 8-bit rows with their scales, take
+//                 one workgroup per token that holds the row in registers.  The 8-bit cast sent once per rank is
 //                 tiled the same way, each lane casting 16 channels.
 //   fused permute: the receiving rank's dispatch with the permute folded
 //                 in: one workgroup per received token reads the sender's
@@ -576,7 +577,8 @@ __device__ __forceinline__ void ranked_token_weights(const int64_t* __restrict__
 // and 88.6 against 100.2 us at 16 (T=8192 per rank, interleaved A/B;
 // groups of 2 were as fast at 8 ranks but 10% slower at 16); for bf16 rows
 // of 448 vectors (hidden 3584) 76.4 against 82.9 us and 85.4 against
-// 98.1 us.  At 384 vectors and below groups were 2% faster to 41% slower.
+// 98.1 us (such rows now take 64-lane tiles, below).  At 384 vectors and
+// below groups were 2% faster to 41% slower.
 template <int NT, int VPT, int RG>
 __global__ __launch_bounds__(NT)
 void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t* __restrict__ idx,
@@ -645,10 +647,17 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
     }
 }
 
-// Tiled form (token rows of at least 512 vectors, no scale rows): workgroup
-// b maps (XCD-aware) to tile = (token t, tile pt of its row) and a group of
-// kRanksPerGroup destination ranks; the tile's loads after the first hit
-// the XCD's L2.  Tile 0's workgroups also write the group's weight rows.
+// Tiled form (no scale rows; token rows of at least 512 vectors, and rows
+// of 257-511 vectors whose last 128-lane tile would be at most half full, in
+// tiles of NL = 64 lanes): workgroup b maps (XCD-aware) to tile = (token t,
+// tile pt of its row) and a group of kRanksPerGroup destination ranks; the
+// tile's loads after the first hit the XCD's L2.  Tile 0's workgroups also
+// write the group's weight rows.  64-lane tiles against one workgroup per
+// token (8 ranks, T=8192 per rank, interleaved A/B): 77.7 against 82.8 us at
+// hidden 2560 and 95.5 against 99.8 us at 3584.  8-bit rows with their
+// scale rows stay per token: tiled (tile 0 copying the scales) they took
+// 99.0 against 98.3 us at hidden 7168 and were 13-35% slower at 8192 and
+// 16384.
 // The expanded dispatch's tiling, with groups of 8 ranks: a token reaches
 // only some of a group's ranks (5.3 of 8 on average with 8 ranks, k=8), so
 // a group of 8 stores about as many rows as the expanded dispatch's group
@@ -657,7 +666,8 @@ void dispatch_ranked_kernel(const uint4* __restrict__ x, int nvec, const int64_t
 // at 16 ranks, the same at 4; groups of 2 and 3 were 12-43% slower.
 constexpr int kRanksPerGroup = 8;
 
-__global__ __launch_bounds__(kTileLanes)
+template <int NL>
+__global__ __launch_bounds__(NL)
 void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
                                  const int64_t* __restrict__ idx, const float* __restrict__ w,
                                  int k, int E, int El, int G, const int32_t* __restrict__ s2d,
@@ -682,7 +692,7 @@ void dispatch_ranked_tile_kernel(const uint4* __restrict__ x, int nvec,
 #pragma unroll
     for (int q = 0; q < kRanksPerGroup; ++q)
         r[q] = d0 + q < G ? __builtin_amdgcn_readlane(p, d0 + q) : -1;
-    const int v = pt * kTileLanes + tid;    // past the row end: reads 0, stores nothing
+    const int v = pt * NL + tid;    // past the row end: reads 0, stores nothing
     uint4 val = load_row16<0>(buffer_rsrc(x + t * nvec, nvec * 16), v * 16);
     keep(val);
 #pragma unroll
@@ -1117,15 +1127,23 @@ hipError_t launch_dispatch_ranked(const void* x, const int64_t* topk_idx, const 
     const dim3 grid((unsigned)num_tokens);
     const uint4* xx = static_cast<const uint4*>(x);
     const int El = num_experts / num_ranks;
-    const int tpr = tiles_per_row(nvec);
+    const bool narrow = nvec > 2 * kTileLanes && nvec < kMinTiledDispatchVectors && narrow_tiles(nvec);
+    const int lanes = narrow ? kTileLanes / 2 : kTileLanes;
+    const int tpr = (nvec + lanes - 1) / lanes;
     const int groups = (num_ranks + kRanksPerGroup - 1) / kRanksPerGroup;
     const int64_t num_tiles = num_tokens * tpr;
     const int64_t blocks = (num_tiles + 7) / 8 * 8 * groups;
-    if (x_scales == nullptr && nvec >= kMinTiledDispatchVectors && blocks <= INT32_MAX) {
-        hipLaunchKernelGGL(dispatch_ranked_tile_kernel, dim3((unsigned)blocks), dim3(kTileLanes), 0,
-                           stream, xx, nvec, topk_idx, topk_weights, num_topk, num_experts, El,
-                           num_ranks, s2d, dest_rows, dest_x, dest_w, with_weights, tpr, num_tiles,
-                           groups);
+    if (x_scales == nullptr && (narrow || nvec >= kMinTiledDispatchVectors) && blocks <= INT32_MAX) {
+#define EP_RT(NL)                                                                               \
+    hipLaunchKernelGGL((dispatch_ranked_tile_kernel<NL>), dim3((unsigned)blocks), dim3(NL), 0,      \
+                       stream, xx, nvec, topk_idx, topk_weights, num_topk, num_experts, El,        \
+                       num_ranks, s2d, dest_rows, dest_x, dest_w, with_weights, tpr, num_tiles,    \
+                       groups)
+        if (narrow)
+            EP_RT(kTileLanes / 2);
+        else
+            EP_RT(kTileLanes);
+#undef EP_RT
         return hipGetLastError();
     }
     // rows of more than kRankGroupVectors vectors: one workgroup per

@@ -178,7 +178,10 @@ def check_dispatch(x_bits, idx, w, E, G, s2d, rows, with_weights=True):
     (64, 10, 256, 64, 64, True),      # k = EP_MAX_TOPK, G = EP_MAX_RANKS
     (64, 20, 4104, 64, 8, True),      # tiled rows (513 vectors), 8 groups of 8 ranks
     (12, 40, 4096, 48, 8, True),      # tiled rows, a full and a partial group of ranks
-    (10, 40, 3584, 40, 8, True),      # 448 vectors, per token: groups of 4 ranks, the last of 2
+    (10, 40, 3584, 40, 8, True),      # 448 vectors: 7 tiles of 64 lanes, a full and a partial group
+    (8, 100, 2560, 64, 8, True),      # 320 vectors: 5 tiles of 64 lanes
+    (12, 50, 3080, 48, 6, False),     # 385 vectors: 7 tiles of 64, the last of one vector
+    (10, 40, 3720, 40, 8, True),      # 465 vectors, per token: groups of 4 ranks, the last of 2
 ])
 def test_dispatch_ranked_small(G, T, H, E, k, weights):
     inp = make_random_case(G * 7 + H, T, H, E, k, mask_frac=0.2, dup_frac=1.0, invalid_frac=0.05)
