@@ -13,6 +13,14 @@
  *   ep_combine   gather the expert-output rows back and reduce them per
  *                token, weighted by topk_weights, in fp32, in top-k order.
  *
+ * Around them: ep_layout_ex (aligned segments, fixed capacity),
+ * ep_layout_noalloc (no workspace argument), ep_dispatch_ex and the
+ * pre-quantized / column-major-scale forms (8-bit variants), the two
+ * backward passes, and the per-(token, rank) path (ep_routing_map,
+ * ep_rank_layout, ep_dispatch_ranked and its 8-bit forms, the fused
+ * permutes, ep_combine_ranked, ep_dispatch_ranked_backward), each declared
+ * below with the passage it follows.
+ *
  * The operations follow the pages' problem statement:
  *   - NCCL EP (nccl_ep.cc): ncclEpCreateHandle (topk_idx is a 2-D int64
  *     tensor; "Step 3" metadata preprocessing gives per-expert counts),
@@ -31,7 +39,8 @@
  *   - All array arguments are device pointers (memory the GPU can read and
  *     write: hipMalloc'd, or torch CUDA tensors).  The caller owns them; the
  *     library never frees, keeps or allocates memory and holds no state
- *     between calls, so the layout outputs themselves are the "handle" that
+ *     between calls (apart from ep_layout_noalloc's fixed per-device
+ *     scratch), so the layout outputs themselves are the "handle" that
  *     dispatch and combine take.
  *   - bf16 / fp8 / fp32 row buffers must be 16-byte aligned.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
