@@ -16,7 +16,14 @@
  *   - every dispatched row equals its source token, bit for bit;
  *   - combine of the dispatched rows (identity experts) with weights
  *     summing to 1 returns x (by value: a -0 element comes back +0);
- *   - ep_layout_noalloc writes the same counts, offsets, slots and sources.
+ *   - ep_layout_noalloc writes the same counts, offsets, slots and sources;
+ *   - the per-(token, rank) path over 4 simulated ranks (when E is a
+ *     multiple of 4; rank s routes each slot to expert (e + s) mod E):
+ *     ep_routing_map for every rank, ep_rank_layout for rank 0, then rank
+ *     0's tokens sent once per destination rank (ep_dispatch_ranked, a host
+ *     array of 4 device pointers) and gathered back (ep_combine_ranked):
+ *     a token reaches rank d exactly when one of its experts is d's, every
+ *     sent row equals its token, and the gather of n copies is bf16(n * x).
  * It prints one line and exits 0 when all hold, 1 otherwise.
  */
 #include <stdint.h>
@@ -62,6 +69,14 @@ static float bf16_value(uint16_t b)
     float f;
     memcpy(&f, &u, sizeof f);
     return f;
+}
+
+/* bf16 bits of a finite float, round to nearest even */
+static uint16_t bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)((u + 0x7FFFU + ((u >> 16) & 1U)) >> 16);
 }
 
 static void *dev_alloc(size_t bytes)
@@ -196,12 +211,71 @@ int main(int argc, char **argv)
                            memcmp(offsets, offsets2, (E + 1) * sizeof *offsets) == 0 &&
                            memcmp(slot, slot2, P * sizeof *slot) == 0 &&
                            memcmp(src, src2, (size_t)live * sizeof *src) == 0;
-    const int ok = layout_ok && rows_ok && bad == 0 && noalloc_ok;
+
+    /* the per-(token, rank) path, rank 0 of 4 */
+    enum { G = 4 };
+    const char *ranked = "skipped (E not a multiple of 4)";
+    int ranked_ok = 1;
+    if (E % G == 0) {
+        const int W = (E + 7) / 8, El = E / G;
+        uint8_t *d_gmap = dev_alloc((size_t)G * T * W);
+        int64_t *idx_s = malloc(P * sizeof *idx_s);
+        int64_t *d_idx_s = dev_alloc(P * sizeof *d_idx_s);
+        for (int r = 0; r < G; ++r) {
+            for (int64_t i = 0; i < P; ++i) idx_s[i] = idx[i] < 0 ? -1 : (idx[i] + r) % E;
+            HIP_OK(hipMemcpy(d_idx_s, idx_s, P * sizeof *idx_s, hipMemcpyHostToDevice));
+            EP_OK(ep_routing_map(d_idx_s, T, k, E, d_gmap + (size_t)r * T * W, NULL, NULL));
+            HIP_OK(hipDeviceSynchronize());
+        }
+        const size_t rws_bytes = ep_rank_layout_workspace_size(T, E, G);
+        int32_t *d_s2d = dev_alloc((size_t)T * G * sizeof(int32_t));
+        uint8_t *d_lm = dev_alloc((size_t)G * T * El);
+        int32_t *d_rsrc = dev_alloc((size_t)G * T * sizeof(int32_t));
+        int64_t *d_rti = dev_alloc((size_t)G * T * k * sizeof(int64_t));
+        int32_t *d_ecnt = dev_alloc(El * sizeof(int32_t));
+        int32_t *d_nrecv = dev_alloc(sizeof(int32_t));
+        int32_t *d_novf = dev_alloc(sizeof(int32_t));
+        void *d_rws = dev_alloc(rws_bytes);
+        EP_OK(ep_rank_layout(d_gmap, T, E, G, 0, k, d_s2d, d_lm, d_rsrc, d_rti, d_ecnt, d_nrecv,
+                             d_novf, d_rws, rws_bytes, NULL));
+        /* rank 0 sends first, so its rows in every buffer are below T */
+        void *dest[G];
+        for (int d = 0; d < G; ++d) dest[d] = dev_alloc((size_t)T * H * 2);
+        uint16_t *d_out_r = dev_alloc((size_t)T * H * 2);
+        EP_OK(ep_dispatch_ranked(d_x, d_idx, d_w, T, H, k, E, G, d_s2d, dest, NULL, T, NULL));
+        EP_OK(ep_combine_ranked((const void *const *)dest, T, d_s2d, T, H, G, d_out_r, NULL));
+        HIP_OK(hipDeviceSynchronize());
+        int32_t *s2d = malloc((size_t)T * G * sizeof *s2d);
+        uint16_t *rows = malloc((size_t)T * H * 2);
+        HIP_OK(hipMemcpy(s2d, d_s2d, (size_t)T * G * sizeof *s2d, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(out, d_out_r, (size_t)T * H * 2, hipMemcpyDeviceToHost));
+        for (int d = 0; d < G && ranked_ok; ++d) {
+            HIP_OK(hipMemcpy(rows, dest[d], (size_t)T * H * 2, hipMemcpyDeviceToHost));
+            for (int64_t t = 0; t < T && ranked_ok; ++t) {
+                int reaches = 0;
+                for (int j = 0; j < k; ++j)
+                    reaches |= idx[t * k + j] >= (int64_t)d * El && idx[t * k + j] < (int64_t)(d + 1) * El;
+                const int32_t r = s2d[t * G + d];
+                ranked_ok = (r >= 0) == reaches && r < T &&
+                            (r < 0 || memcmp(rows + (size_t)r * H, x + (size_t)t * H, (size_t)H * 2) == 0);
+            }
+        }
+        for (int64_t t = 0; t < T && ranked_ok; ++t) {
+            int n = 0;
+            for (int d = 0; d < G; ++d) n += s2d[t * G + d] >= 0;
+            for (int c = 0; c < H && ranked_ok; ++c) {
+                const uint16_t want = n ? bf16_rne((float)n * bf16_value(x[t * H + c])) : 0;
+                ranked_ok = out[t * H + c] == want;
+            }
+        }
+        ranked = ranked_ok ? "ok" : "WRONG";
+    }
+    const int ok = layout_ok && rows_ok && bad == 0 && noalloc_ok && ranked_ok;
 
     printf("c_abi_demo T=%lld H=%d E=%d k=%d: %lld of %lld pairs routed; layout %s, rows %s, "
-           "combine %s (%lld elements off), noalloc %s\n",
+           "combine %s (%lld elements off), noalloc %s, ranked %s\n",
            (long long)T, H, E, k, (long long)live, (long long)P, layout_ok ? "ok" : "WRONG",
            rows_ok ? "ok" : "WRONG", bad == 0 ? "ok" : "WRONG", (long long)bad,
-           noalloc_ok ? "ok" : "WRONG");
+           noalloc_ok ? "ok" : "WRONG", ranked);
     return ok ? 0 : 1;
 }

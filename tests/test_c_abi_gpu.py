@@ -1,8 +1,10 @@
 """The C ABI from plain C: examples/c_abi_demo (built by build() with gcc
 against include/ep.h and libep.so, no Python or PyTorch in the process)
-runs layout, bf16 dispatch and combine on hipMalloc'd buffers, and the
-no-allocation layout beside the layout, and checks the invariants its header
-comment lists; it exits 0 when they all hold."""
+runs layout, bf16 dispatch and combine on hipMalloc'd buffers, the
+no-allocation layout beside the layout, and the per-rank path over 4
+simulated ranks (routing maps, rank layout, once-per-rank dispatch through a
+host array of device pointers, combine over ranks), and checks the
+invariants its header comment lists; it exits 0 when they all hold."""
 
 import os
 import subprocess
@@ -29,3 +31,4 @@ def test_c_demo(T, H, E, k):
     assert r.returncode == 0, r.stdout + r.stderr
     assert "layout ok, rows ok, combine ok" in r.stdout
     assert "noalloc ok" in r.stdout
+    assert ("ranked ok" if E % 4 == 0 else "ranked skipped") in r.stdout
